@@ -1,0 +1,254 @@
+/*
+ * tq.h - C ABI of libtq, an MI355X (gfx950) implementation of the hot path
+ * of a TurboQuant-style KV-cache codec: normalise-rotate-quantise encoding
+ * with a one-bit QJL sketch of the residual, and decode-time attention
+ * computed straight from the packed records.
+ *
+ * Sources (by page title and section):
+ *   FibQuant summary ("FibQuant: Quantizacao Vetorial Universal para
+ *     Compressao de KV-Cache de Acesso Aleatorio"), section 1: a deployable
+ *     cache codec stores fixed-rate records at fixed addresses so any token
+ *     decodes on its own; the interface stores the norm, applies one shared
+ *     random rotation and quantises each rotated coordinate with a scalar
+ *     Lloyd-Max table.  Section 2.1: one offline table serves every layer,
+ *     head and input.  Section 2.3: decoding looks up codes, applies the
+ *     inverse rotation and scales by the norm.
+ *   iaemfoco post ("TurboQuant: Compressao Avancada da Google para Cache KV
+ *     ..."), section "TurboQuant: Uma Nova Abordagem": a randomized Hadamard
+ *     rotation, then a quantized Johnson-Lindenstrauss step that makes inner
+ *     products unbiased.
+ *   itstec post ("Compressao KV eficaz com TurboQuant"), section "Por dentro
+ *     do processo de compressao KV": the residual's JL projection is kept as
+ *     sign bits only.
+ *   TurboESM summary, technical section 2: RoPE before the rotation; a fused
+ *     decode kernel (dequantisation, residual correction, online softmax)
+ *     with no intermediate dequantised copy.
+ *   tambur post ("Google acelera LLMs em 8 vezes"): attention logits
+ *     computed from quantised keys.
+ *
+ * Conventions for every entry point
+ *   - Device pointers are HIP device memory owned by the caller; host
+ *     pointers are ordinary host memory owned by the caller.  The library
+ *     owns only a codebook's tables (tq_codebook_init / tq_codebook_destroy)
+ *     and never allocates in encode, logits or decode calls: scratch space is
+ *     the caller's workspace, sized by tq_workspace_bytes().
+ *   - Arguments are validated on the host before anything is launched; an
+ *     invalid call returns an error code and launches nothing.  Work is
+ *     enqueued on `stream` (a hipStream_t; NULL = the default stream) and
+ *     the call returns without synchronising.  A failed launch returns
+ *     TQ_EHIP.  tq_last_error() gives a message for the calling thread's
+ *     last failure.
+ *   - Outputs must not alias inputs.  Calls that write the same buffers
+ *     must be ordered by the caller (same stream or events).
+ *   - Non-finite inputs give unspecified (but bounded, non-faulting) output.
+ *
+ * Packed record (one set of planes per tensor; vector index
+ * n = (seq * h_kv + head) * L_cap + token):
+ *   norm [n]          float    nu = ||x||_2 (after RoPE for keys)
+ *   rnorm[n]          float    gamma = ||y - t[c]||_2 (absent when m == 0)
+ *   codes[n][b*d/32]  uint32   coordinate i's code is bits [b*i, b*i+b) of
+ *                              the LSB-first bit string of the words (bit k
+ *                              is bit k%32 of word k/32); code 0 is the most
+ *                              negative level
+ *   signs[n][m/32]    uint32   bit l (bit l%32 of word l/32) is 1 iff
+ *                              (S e)_l >= 0
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t tq_status;
+enum {
+    TQ_OK = 0,
+    TQ_EINVAL = -1,        /* bad argument (null pointer, size, stride, alignment) */
+    TQ_EUNSUPPORTED = -2,  /* valid spec this build has no kernel for */
+    TQ_ENOMEM = -3,        /* device allocation failed (codebook init only) */
+    TQ_EHIP = -4           /* a HIP runtime call or kernel launch failed */
+};
+
+enum { TQ_F32 = 0, TQ_BF16 = 1 };                                  /* element types */
+enum { TQ_ROT_AUTO = 0, TQ_ROT_HADAMARD = 1, TQ_ROT_DENSE = 2 };   /* rotation forms */
+enum { TQ_OP_ENCODE = 0, TQ_OP_LOGITS = 1, TQ_OP_DECODE = 2 };     /* workspace queries */
+
+/*
+ * Codebook specification.
+ *   d        vector dimension.  Hadamard form: 64 or 128.  Dense form: a
+ *            multiple of 64 up to 4096.
+ *   bits     Lloyd-Max bits per coordinate, 1..4 (K = 2^bits levels);
+ *            bits*d must be a multiple of 32.
+ *   m        QJL sketch rows: 0 (no sketch, no rnorm plane) or a multiple of
+ *            32 up to 4096; the Hadamard form has kernels for m = 0, d/2, d.
+ *   rotation TQ_ROT_AUTO (Hadamard iff d is a power of two), _HADAMARD, _DENSE.
+ *   seed     draws sigma, the rotation Gaussians and S when no tq_draws are
+ *            given (SplitMix64 streams, Box-Muller Gaussians).
+ */
+typedef struct {
+    int32_t d, bits, m, rotation;
+    uint64_t seed;
+} tq_spec;
+
+/*
+ * Explicit random draws (host memory, read during the call only).  Any
+ * field may be NULL; NULL fields are derived from spec->seed.
+ *   sigma     [d] int8 +1/-1   Hadamard form: Pi = H diag(sigma) / sqrt(d)
+ *   rot_gauss [d*d] double     dense form: Pi = Q of rot_gauss = Q R with
+ *                              diag(R) > 0, stored as float32 (row-major,
+ *                              y = Pi u)
+ *   sketch    [m*d] float      S, row-major
+ */
+typedef struct {
+    const int8_t* sigma;
+    const double* rot_gauss;
+    const float* sketch;
+} tq_draws;
+
+typedef struct tq_codebook tq_codebook;  /* opaque; immutable after init */
+
+/* Caller-owned planes of one packed tensor (device memory); n = capacity in
+ * records.  rnorm and signs may be NULL when the codebook has m == 0. */
+typedef struct {
+    float* norm;
+    float* rnorm;
+    uint32_t* codes;
+    uint32_t* signs;
+    int64_t n;
+} tq_packed;
+
+/*
+ * tq_codebook_tables (host only, no GPU): computes the tables a codebook
+ * holds, into caller host buffers (any may be NULL to skip):
+ *   levels [K], thresholds [K-1]    float32 Lloyd-Max table for the density
+ *       of one coordinate of a uniform point on S^{d-1} (FibQuant summary,
+ *       section 2.1; itstec post, "Por dentro do processo": a Beta law),
+ *       levels at the conditional means, thresholds at the midpoints
+ *   rotation  Hadamard: [d] sigma as +-1.0f; dense: [d*d] Pi row-major
+ *   sketch    [m*d] S row-major
+ * Returns TQ_EINVAL / TQ_EUNSUPPORTED for a bad spec.
+ */
+tq_status tq_codebook_tables(const tq_spec* spec, const tq_draws* draws, float* levels,
+                             float* thresholds, float* rotation, float* sketch);
+
+/*
+ * tq_codebook_init: builds the tables (as tq_codebook_tables) and uploads
+ * them to the current HIP device on `stream` (the only host-to-device copy
+ * the library makes).  *out receives a handle owned by the library.
+ * Errors: TQ_EINVAL (null out/spec, bad spec), TQ_EUNSUPPORTED,
+ * TQ_ENOMEM, TQ_EHIP.  On error *out is set to NULL.
+ */
+tq_status tq_codebook_init(const tq_spec* spec, const tq_draws* draws, void* stream,
+                           tq_codebook** out);
+
+/* Frees a codebook's device tables.  The caller guarantees no enqueued
+ * work still uses it (synchronise first).  NULL is accepted. */
+tq_status tq_codebook_destroy(tq_codebook* cb);
+
+/* Copies the spec the codebook was built with. */
+tq_status tq_codebook_get_spec(const tq_codebook* cb, tq_spec* out);
+
+/* Host copies of the codebook's tables (same layout as tq_codebook_tables). */
+tq_status tq_codebook_export(const tq_codebook* cb, float* levels, float* thresholds,
+                             float* rotation, float* sketch);
+
+/*
+ * tq_encode_kv: encodes keys and/or values into packed records (FibQuant
+ * summary, sections 1 and 2.3; iaemfoco post, "Uma Nova Abordagem"; itstec
+ * post, "Por dentro do processo"; TurboESM summary, technical section 2 for
+ * RoPE first).  Per vector: RoPE (keys only, if tables are given) -> nu ->
+ * y = Pi (x / nu) -> codes -> residual e = y - t[c], gamma = ||e|| ->
+ * sign bits of S e.
+ *   ck, k, kout   key codebook, input and planes (k may be NULL: no keys)
+ *   cv, v, vout   value codebook, input and planes (v may be NULL)
+ *   dtype         TQ_F32 or TQ_BF16 for both inputs
+ *   n_seq, n_tok, h_kv   input shape [n_seq][n_tok][h_kv][d]; d contiguous
+ *   k_stride, v_stride   host int64[3]: element strides of seq, tok, head;
+ *                 each a multiple of 4 (f32) or 8 (bf16), base pointers
+ *                 16-byte aligned
+ *   tok_offset    cache slot (and RoPE position) of token 0
+ *   L_cap         cache capacity per (seq, head); tok_offset + n_tok <= L_cap
+ *   rope_cos, rope_sin   device float [rope_npos][d/2] (see tq_rope_table)
+ *                 or both NULL for no RoPE; tok_offset + n_tok <= rope_npos
+ *   ws, ws_bytes  device workspace, at least tq_workspace_bytes(ck, cv,
+ *                 TQ_OP_ENCODE, n_seq*n_tok*h_kv, ...) (0 for Hadamard codebooks)
+ * n_seq*n_tok*h_kv == 0 is a no-op returning TQ_OK.
+ */
+tq_status tq_encode_kv(const tq_codebook* ck, const tq_codebook* cv, const void* k, const void* v,
+                       int32_t dtype, int32_t n_seq, int32_t n_tok, int32_t h_kv,
+                       const int64_t* k_stride, const int64_t* v_stride, int32_t tok_offset,
+                       int32_t L_cap, const float* rope_cos, const float* rope_sin,
+                       int32_t rope_npos, const tq_packed* kout, const tq_packed* vout, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/*
+ * tq_attn_logits: attention logits from packed keys (tambur post; iaemfoco
+ * post, "Uma Nova Abordagem" for the unbiased QJL correction):
+ *   logit[b][h][t] = nu_t ( <q'_h, t[c_t]> + sqrt(pi/2)/m gamma_t <s_h, z_t> )
+ * with q'_h = Pi RoPE(q_h, seq_len[b]), s_h = S q'_h, z in {-1,+1}.
+ *   q             device [B][Hq][d], dtype TQ_F32 or TQ_BF16
+ *   k             packed keys, capacity >= B*h_kv*L_cap
+ *   B, Hq, h_kv   Hq a multiple of h_kv; query head h reads KV head h/(Hq/h_kv)
+ *   seq_len       device int32 [B]; keys t < seq_len[b] are scored (values
+ *                 above L_cap are clamped to L_cap); also the query's RoPE
+ *                 position
+ *   rope_*        as tq_encode_kv (rope_npos > L_cap) or NULL
+ *   top_k = 0     out = device float [B][Hq][L_cap]; entries t >= seq_len[b]
+ *                 are left untouched
+ *   top_k = 1..16 out = device float [B][Hq][top_k] best logits in
+ *                 descending order (ties to the smaller index), topk_idx =
+ *                 device int32 [B][Hq][top_k] (-1 / -inf when fewer keys)
+ *   ws, ws_bytes  device workspace >= tq_workspace_bytes(ck, NULL,
+ *                 TQ_OP_LOGITS, B, Hq, h_kv, L_cap, top_k)
+ */
+tq_status tq_attn_logits(const tq_codebook* ck, const void* q, int32_t q_dtype, const tq_packed* k,
+                         int32_t B, int32_t Hq, int32_t h_kv, int32_t L_cap, const int32_t* seq_len,
+                         const float* rope_cos, const float* rope_sin, int32_t rope_npos,
+                         int32_t top_k, float* out, int32_t* topk_idx, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/*
+ * tq_attn_decode: fused decode attention over packed K and V (TurboESM
+ * summary, technical section 2, fused kernel; FibQuant summary, section 2.3
+ * for value reconstruction):
+ *   out[b][h] = sum_t p_t nu^v_t Pi_v^T (t_v[c^v_t] + sqrt(pi/2)/m_v gamma^v_t S_v^T z^v_t),
+ *   p = softmax over t < seq_len[b] of scale * logit[b][h][t].
+ * Split over the key axis with an online softmax and a log-sum-exp merge.
+ *   scale         0 means 1/sqrt(d)
+ *   out           device float [B][Hq][d]; zeros where seq_len[b] == 0
+ *   other arguments as tq_attn_logits; ws >= tq_workspace_bytes(ck, cv,
+ *   TQ_OP_DECODE, B, Hq, h_kv, L_cap, 0)
+ */
+tq_status tq_attn_decode(const tq_codebook* ck, const tq_codebook* cv, const void* q, int32_t q_dtype,
+                         const tq_packed* k, const tq_packed* v, int32_t B, int32_t Hq, int32_t h_kv,
+                         int32_t L_cap, const int32_t* seq_len, const float* rope_cos,
+                         const float* rope_sin, int32_t rope_npos, float scale, float* out,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for an op.  For TQ_OP_ENCODE pass the vector count in B
+ * (other sizes ignored).  Returns 0 on a bad argument. */
+size_t tq_workspace_bytes(const tq_codebook* ck, const tq_codebook* cv, int32_t op, int64_t B,
+                          int32_t Hq, int32_t h_kv, int32_t L_cap, int32_t top_k);
+
+/* uint32 words per record of a plane: plane 0 = codes (bits*d/32),
+ * plane 1 = signs (m/32).  -1 on a bad spec. */
+int64_t tq_plane_words(const tq_spec* spec, int32_t plane);
+
+/* Host RoPE table: cos/sin[pos][i] = cos/sin(pos * base^(-2i/d)), angles in
+ * double, stored as float (i < d/2, pos < n_pos).  Half-split pairing: RoPE
+ * rotates (x_i, x_{i+d/2}).  cos_out and sin_out are host float[n_pos*d/2]. */
+tq_status tq_rope_table(double base, int32_t d, int32_t n_pos, float* cos_out, float* sin_out);
+
+/* Message for the calling thread's last failed call ("" if none). */
+const char* tq_last_error(void);
+
+/* Library version string. */
+const char* tq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TQ_H */

@@ -1,0 +1,283 @@
+"""Python binding of libtq: an MI355X (gfx950) TurboQuant-style KV codec.
+
+Thin marshalling over the C ABI in include/tq.h: tensors in, tensors out,
+launched on torch's current HIP stream.  Every step of encoding, logit
+scanning and decoding runs in the library's HIP kernels; PyTorch only
+provides device memory and the stream.  There is no CPU fallback: the calls
+raise if libtq.so is missing or no GPU is present.
+
+    ck = Codebook(d=128, bits=3, m=64, seed=0)          # keys
+    cv = Codebook(d=128, bits=3, m=64, seed=1)          # values
+    kp, vp = Packed(ck, n), Packed(cv, n)               # n = B * h_kv * L_cap
+    encode_kv(ck, cv, k, v, kp, vp, L_cap=L, rope=rope)
+    logits = attn_logits(ck, q, kp, h_kv, L, seq_len, rope=rope)
+    out = attn_decode(ck, cv, q, kp, vp, h_kv, L, seq_len, rope=rope)
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+import numpy as np
+
+from . import _lib
+from ._lib import (TQError, TQ_F32, TQ_BF16, TQ_ROT_AUTO, TQ_ROT_HADAMARD, TQ_ROT_DENSE, TQ_OP_ENCODE,
+                   TQ_OP_LOGITS, TQ_OP_DECODE, check, lib, tq_draws, tq_packed, tq_spec)
+
+__all__ = ["Codebook", "Packed", "encode_kv", "attn_logits", "attn_decode", "rope_table", "codebook_tables",
+           "plane_words", "workspace_bytes", "TQError", "lib"]
+
+_ROT = {"auto": TQ_ROT_AUTO, "hadamard": TQ_ROT_HADAMARD, "dense": TQ_ROT_DENSE}
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    torch = _torch()
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return TQ_F32
+    if t.dtype == torch.bfloat16:
+        return TQ_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _spec(d, bits, m, rotation="auto", seed=0):
+    return tq_spec(int(d), int(bits), int(m), _ROT[rotation] if isinstance(rotation, str) else int(rotation),
+                   int(seed) & 0xFFFFFFFFFFFFFFFF)
+
+
+def _draws(sigma=None, rot_gauss=None, sketch=None):
+    keep = []
+    dr = tq_draws()
+    if sigma is not None:
+        a = np.ascontiguousarray(sigma, dtype=np.int8)
+        keep.append(a)
+        dr.sigma = a.ctypes.data
+    if rot_gauss is not None:
+        a = np.ascontiguousarray(rot_gauss, dtype=np.float64)
+        keep.append(a)
+        dr.rot_gauss = a.ctypes.data
+    if sketch is not None:
+        a = np.ascontiguousarray(sketch, dtype=np.float32)
+        keep.append(a)
+        dr.sketch = a.ctypes.data
+    return dr, keep
+
+
+def plane_words(d, bits, m, rotation="auto"):
+    """(code words, sign words) per record."""
+    sp = _spec(d, bits, m, rotation)
+    cw = lib().tq_plane_words(C.byref(sp), 0)
+    sw = lib().tq_plane_words(C.byref(sp), 1)
+    if cw < 0:
+        raise TQError(-1, lib().tq_last_error().decode())
+    return int(cw), int(sw)
+
+
+def codebook_tables(d, bits, m, rotation="auto", seed=0, sigma=None, rot_gauss=None, sketch=None):
+    """Host-only table construction (no GPU): dict of levels, thresholds,
+    rotation (sigma as +-1 or the dense matrix) and sketch."""
+    sp = _spec(d, bits, m, rotation, seed)
+    dr, keep = _draws(sigma, rot_gauss, sketch)
+    K = 1 << bits
+    lv = np.zeros(K, np.float32)
+    th = np.zeros(K - 1, np.float32)
+    dense = (rotation == "dense") or (rotation == "auto" and (d & (d - 1)) != 0) or rotation == TQ_ROT_DENSE
+    rot = np.zeros(d * d if dense else d, np.float32)
+    sk = np.zeros(m * d, np.float32)
+    check(lib().tq_codebook_tables(C.byref(sp), C.byref(dr), lv.ctypes.data, th.ctypes.data, rot.ctypes.data,
+                                   sk.ctypes.data))
+    return {"levels": lv, "thresholds": th, "rotation": rot.reshape(d, d) if dense else rot,
+            "sketch": sk.reshape(m, d), "dense": dense}
+
+
+class Codebook:
+    """A codebook (Lloyd-Max table, rotation, sketch) resident on the current
+    GPU.  Draws default to the library's seeded generator; pass sigma /
+    rot_gauss / sketch (host arrays) to supply them."""
+
+    def __init__(self, d, bits, m, rotation="auto", seed=0, sigma=None, rot_gauss=None, sketch=None):
+        self.d, self.bits, self.m = int(d), int(bits), int(m)
+        sp = _spec(d, bits, m, rotation, seed)
+        dr, keep = _draws(sigma, rot_gauss, sketch)
+        h = C.c_void_p()
+        check(lib().tq_codebook_init(C.byref(sp), C.byref(dr), _stream(), C.byref(h)))
+        self._h = h
+        out = tq_spec()
+        check(lib().tq_codebook_get_spec(h, C.byref(out)))
+        self.rotation = out.rotation
+        self.dense = (out.rotation == TQ_ROT_DENSE) or (out.rotation == TQ_ROT_AUTO and (self.d & (self.d - 1)) != 0)
+        self.code_words = self.bits * self.d // 32
+        self.sign_words = self.m // 32
+
+    @property
+    def handle(self):
+        return self._h
+
+    def export(self):
+        K = 1 << self.bits
+        lv = np.zeros(K, np.float32)
+        th = np.zeros(K - 1, np.float32)
+        rot = np.zeros(self.d * self.d if self.dense else self.d, np.float32)
+        sk = np.zeros(self.m * self.d, np.float32)
+        check(lib().tq_codebook_export(self._h, lv.ctypes.data, th.ctypes.data, rot.ctypes.data, sk.ctypes.data))
+        return {"levels": lv, "thresholds": th,
+                "rotation": rot.reshape(self.d, self.d) if self.dense else rot,
+                "sketch": sk.reshape(self.m, self.d)}
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _torch().cuda.synchronize()
+            lib().tq_codebook_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            if getattr(self, "_h", None):
+                lib().tq_codebook_destroy(self._h)
+                self._h = None
+        except Exception:
+            pass
+
+
+class Packed:
+    """Device planes for n records of one codebook (torch tensors)."""
+
+    def __init__(self, cb: Codebook, n: int, device="cuda"):
+        torch = _torch()
+        self.n = int(n)
+        self.norm = torch.zeros(self.n, dtype=torch.float32, device=device)
+        self.rnorm = torch.zeros(self.n if cb.m else 0, dtype=torch.float32, device=device)
+        self.codes = torch.zeros((self.n, cb.code_words), dtype=torch.int32, device=device)
+        self.signs = torch.zeros((self.n, cb.sign_words), dtype=torch.int32, device=device)
+        self.m = cb.m
+
+    @classmethod
+    def from_arrays(cls, cb, norm, rnorm, codes, signs, device="cuda"):
+        torch = _torch()
+        p = cls.__new__(cls)
+        p.n = int(len(norm))
+        p.m = cb.m
+        p.norm = torch.as_tensor(np.asarray(norm, np.float32), device=device)
+        p.rnorm = torch.as_tensor(np.asarray(rnorm if cb.m else np.zeros(0), np.float32), device=device)
+        p.codes = torch.as_tensor(np.asarray(codes, np.uint32).view(np.int32), device=device)
+        p.signs = torch.as_tensor(np.asarray(signs if cb.m else np.zeros((p.n, 0)), np.uint32).view(np.int32),
+                                  device=device)
+        return p
+
+    def struct(self):
+        return tq_packed(self.norm.data_ptr(), self.rnorm.data_ptr() if self.m else None, self.codes.data_ptr(),
+                         self.signs.data_ptr() if self.m else None, self.n)
+
+    def numpy(self):
+        """(norm, rnorm, codes uint32, signs uint32) on the host."""
+        return (self.norm.cpu().numpy(), self.rnorm.cpu().numpy(),
+                self.codes.cpu().numpy().view(np.uint32), self.signs.cpu().numpy().view(np.uint32))
+
+
+def workspace_bytes(ck, cv, op, B, Hq=0, h_kv=1, L_cap=0, top_k=0):
+    return int(lib().tq_workspace_bytes(ck.handle, cv.handle if cv else None, op, int(B), int(Hq), int(h_kv),
+                                        int(L_cap), int(top_k)))
+
+
+def _workspace(nbytes):
+    torch = _torch()
+    if nbytes == 0:
+        return None, 0
+    return torch.empty(nbytes, dtype=torch.uint8, device="cuda"), nbytes
+
+
+def rope_table(base, d, n_pos, device="cuda"):
+    """(cos, sin) float32 [n_pos, d/2] from the library's host builder, on
+    ``device`` (or numpy arrays if device is None)."""
+    cs = np.zeros((n_pos, d // 2), np.float32)
+    sn = np.zeros((n_pos, d // 2), np.float32)
+    check(lib().tq_rope_table(float(base), int(d), int(n_pos), cs.ctypes.data, sn.ctypes.data))
+    if device is None:
+        return cs, sn
+    torch = _torch()
+    return torch.as_tensor(cs, device=device), torch.as_tensor(sn, device=device)
+
+
+def _strides(t):
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("inputs are [n_seq, n_tok, h_kv, d] with d contiguous")
+    return (C.c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2))
+
+
+def encode_kv(ck, cv, k, v, kout=None, vout=None, tok_offset=0, L_cap=None, rope=None, workspace=None):
+    """Encode k and/or v ([n_seq, n_tok, h_kv, d], float32 or bfloat16) into
+    Packed planes at cache slots tok_offset.. of each (seq, head)."""
+    x = k if k is not None else v
+    n_seq, n_tok, h_kv, _ = x.shape
+    L_cap = n_tok + tok_offset if L_cap is None else int(L_cap)
+    dt = _dtype_code(x)
+    ks = _strides(k) if k is not None else None
+    vs = _strides(v) if v is not None else None
+    need = workspace_bytes(ck if k is not None else cv, cv if (k is not None and v is not None) else None,
+                           TQ_OP_ENCODE, n_seq * n_tok * h_kv)
+    ws, wsb = (workspace, workspace.numel()) if workspace is not None else _workspace(need)
+    cos, sin = (None, None) if rope is None else rope
+    npos = 0 if rope is None else int(cos.shape[0])
+    kst = kout.struct() if kout is not None else None
+    vst = vout.struct() if vout is not None else None
+    check(lib().tq_encode_kv(ck.handle if ck else None, cv.handle if cv else None, _ptr(k), _ptr(v), dt,
+                             n_seq, n_tok, h_kv, ks, vs, int(tok_offset), L_cap, _ptr(cos), _ptr(sin), npos,
+                             C.byref(kst) if kst is not None else None, C.byref(vst) if vst is not None else None,
+                             _ptr(ws), wsb, _stream()))
+    return kout, vout
+
+
+def attn_logits(ck, q, kp, h_kv, L_cap, seq_len, rope=None, top_k=0, out=None, workspace=None):
+    """Logits [B, Hq, L_cap] (top_k = 0) or (values, indices) [B, Hq, top_k]
+    for queries q [B, Hq, d] against packed keys.  seq_len: int32 [B] on the
+    GPU."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    cos, sin = (None, None) if rope is None else rope
+    npos = 0 if rope is None else int(cos.shape[0])
+    need = workspace_bytes(ck, None, TQ_OP_LOGITS, B, Hq, h_kv, L_cap, top_k)
+    ws, wsb = (workspace, workspace.numel()) if workspace is not None else _workspace(need)
+    idx = None
+    if top_k:
+        out = torch.empty((B, Hq, top_k), dtype=torch.float32, device=q.device) if out is None else out
+        idx = torch.empty((B, Hq, top_k), dtype=torch.int32, device=q.device)
+    elif out is None:
+        out = torch.zeros((B, Hq, L_cap), dtype=torch.float32, device=q.device)
+    kst = kp.struct()
+    check(lib().tq_attn_logits(ck.handle, _ptr(q), _dtype_code(q), C.byref(kst), B, Hq, int(h_kv), int(L_cap),
+                               _ptr(seq_len), _ptr(cos), _ptr(sin), npos, int(top_k), _ptr(out), _ptr(idx),
+                               _ptr(ws), wsb, _stream()))
+    return (out, idx) if top_k else out
+
+
+def attn_decode(ck, cv, q, kp, vp, h_kv, L_cap, seq_len, rope=None, scale=0.0, out=None, workspace=None):
+    """Decode attention output [B, Hq, d] float32 over packed K and V."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    cos, sin = (None, None) if rope is None else rope
+    npos = 0 if rope is None else int(cos.shape[0])
+    need = workspace_bytes(ck, cv, TQ_OP_DECODE, B, Hq, h_kv, L_cap, 0)
+    ws, wsb = (workspace, workspace.numel()) if workspace is not None else _workspace(need)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    kst, vst = kp.struct(), vp.struct()
+    check(lib().tq_attn_decode(ck.handle, cv.handle, _ptr(q), _dtype_code(q), C.byref(kst), C.byref(vst), B, Hq,
+                               int(h_kv), int(L_cap), _ptr(seq_len), _ptr(cos), _ptr(sin), npos, float(scale),
+                               _ptr(out), _ptr(ws), wsb, _stream()))
+    return out

@@ -1,0 +1,951 @@
+// Decode-side kernels: attention logits from packed keys and the fused
+// decode (softmax times values) from packed keys and values.
+//
+// Estimator (iaemfoco post, "TurboQuant: Uma Nova Abordagem"; itstec post,
+// "Por dentro do processo de compressao KV"; tambur post for logits straight
+// from quantised keys): with q' = Pi RoPE(q) and s = S q',
+//     logit = nu ( <q', t[c]> + sqrt(pi/2)/m * gamma * <s, z> ),  z in {-1,+1}^m.
+// Fused decode (TurboESM summary, technical section 2: dequantisation,
+// residual correction and online softmax in one kernel, no dequantised copy
+// of the cache): each workgroup owns a split of the key axis for one group
+// of queries sharing a KV head, keeps a running max and sum, and accumulates
+// p nu_v t[c_v] (d values, rotated domain) and p nu_v gamma_v z_v (m values,
+// sketch domain).  A merge kernel combines the splits by log-sum-exp and
+// returns to the original domain once per query:
+//     out = Pi_v^T (A_y + sqrt(pi/2)/m_v S_v^T A_z) / l
+// (FibQuant summary, section 2.3: lookup, inverse rotation, norm scale).
+//
+// Work layout: Hadamard codebooks (d = 64, 128) use one thread per key for
+// the logit (codes unpacked in registers, the queries' q' and s broadcast
+// from LDS, GT queries per pass) and, in the decode kernel, one thread per
+// output coordinate for the value accumulation over keys staged in LDS.
+// Dense (Haar) codebooks score by an MFMA GEMM over a dequantised chunk.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+constexpr float kQjl = 1.2533141373155003f;  // sqrt(pi / 2)
+constexpr int kTopKMax = 16;
+
+__device__ __forceinline__ float load_q(const void* q, int bf16, int64_t i) {
+    if (bf16) return __uint_as_float((uint32_t) static_cast<const uint16_t*>(q)[i] << 16);
+    return static_cast<const float*>(q)[i];
+}
+
+__device__ __forceinline__ int clamp_len(const int32_t* seq_len, int b, int L_cap) {
+    int s = seq_len[b];
+    return s < 0 ? 0 : (s > L_cap ? L_cap : s);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// ------------------------------------------------------------ query prep
+struct QPrep {
+    const void* q;
+    int32_t bf16, Hq, L_cap, d, m;
+    const int32_t* seq_len;
+    const float* rope_cos;
+    const float* rope_sin;
+    const float* sigma;
+    const float* sketch;
+    float* qp;  // [B*Hq][d]
+    float* s;   // [B*Hq][m]
+};
+
+// q' = H (sigma * RoPE(q)) / sqrt(d), s = S q'; one workgroup per query head
+template <int D>
+__global__ __launch_bounds__(256) void qprep_rht_kernel(QPrep p) {
+    __shared__ float xs[D];
+    const int t = threadIdx.x;
+    const int64_t bh = blockIdx.x;
+    const int b = (int)(bh / p.Hq);
+    if (t < D) xs[t] = load_q(p.q, p.bf16, bh * D + t);
+    __syncthreads();
+    if (p.rope_cos) {
+        const int pos = clamp_len(p.seq_len, b, p.L_cap);
+        float lo = 0.f, hi = 0.f;
+        if (t < D / 2) {
+            const float c = p.rope_cos[(int64_t)pos * (D / 2) + t];
+            const float sn = p.rope_sin[(int64_t)pos * (D / 2) + t];
+            const float a = xs[t], bb = xs[t + D / 2];
+            lo = a * c - bb * sn;
+            hi = bb * c + a * sn;
+        }
+        __syncthreads();
+        if (t < D / 2) {
+            xs[t] = lo;
+            xs[t + D / 2] = hi;
+        }
+        __syncthreads();
+    }
+    if (t < D) xs[t] *= p.sigma[t];
+    __syncthreads();
+    for (int s = 1; s < D; s <<= 1) {
+        if (t < D / 2) {
+            const int i = (t / s) * 2 * s + (t % s);
+            const float a = xs[i], bb = xs[i + s];
+            xs[i] = a + bb;
+            xs[i + s] = a - bb;
+        }
+        __syncthreads();
+    }
+    const float inv = 1.0f / sqrtf((float)D);
+    if (t < D) {
+        xs[t] *= inv;
+        p.qp[bh * D + t] = xs[t];
+    }
+    __syncthreads();
+    for (int l = t; l < p.m; l += blockDim.x) {
+        const float* row = p.sketch + (int64_t)l * D;
+        float acc = 0.f;
+        for (int i = 0; i < D; ++i) acc = fmaf(row[i], xs[i], acc);
+        p.s[bh * p.m + l] = acc;
+    }
+}
+
+// RoPE'd query rows (fp32) for the dense path: out[bh][d]
+__global__ __launch_bounds__(256) void qrope_kernel(QPrep p, float* out) {
+    const int64_t bh = blockIdx.x;
+    const int b = (int)(bh / p.Hq);
+    const int half = p.d / 2;
+    for (int i = threadIdx.x; i < half; i += blockDim.x) {
+        float a = load_q(p.q, p.bf16, bh * p.d + i);
+        float bb = load_q(p.q, p.bf16, bh * p.d + i + half);
+        if (p.rope_cos) {
+            const int pos = clamp_len(p.seq_len, b, p.L_cap);
+            const float c = p.rope_cos[(int64_t)pos * half + i];
+            const float sn = p.rope_sin[(int64_t)pos * half + i];
+            const float a2 = a * c - bb * sn;
+            const float b2 = bb * c + a * sn;
+            a = a2;
+            bb = b2;
+        }
+        out[bh * p.d + i] = a;
+        out[bh * p.d + i + half] = bb;
+    }
+}
+
+// -------------------------------------------------------- logit scan (RHT)
+struct LogK {
+    const float* qp;
+    const float* s;
+    const float* levels;
+    const float* norm;
+    const float* rnorm;
+    const uint32_t* codes;
+    const uint32_t* signs;
+    const int32_t* seq_len;
+    int32_t Hq, h_kv, L_cap, m, ngroups;
+    int32_t k0, klen;   // keys [k0, k0 + klen) of each (b, kh)
+    float* out;         // row (b*Hq + head), column (key - col0)
+    int64_t ld;
+    int32_t col0;
+};
+
+template <int D, int BITS>
+__device__ __forceinline__ uint32_t code_at(const uint32_t* cw, int i) {
+    const int bp = BITS * i;
+    uint32_t c = cw[bp >> 5] >> (bp & 31);
+    if ((bp & 31) + BITS > 32) c |= cw[(bp >> 5) + 1] << (32 - (bp & 31));
+    return c & ((1u << BITS) - 1u);
+}
+
+template <int D, int BITS, int GT>
+__global__ __launch_bounds__(256) void logits_rht_kernel(LogK p) {
+    constexpr int CW = BITS * D / 32;
+    __shared__ float qs[GT * D];
+    __shared__ float ss[GT * D];  // m <= d for Hadamard codebooks
+    __shared__ float lvl[16];
+    const int t = threadIdx.x;
+    const int grp = blockIdx.x % p.ngroups;
+    const int64_t bk = blockIdx.x / p.ngroups;
+    const int b = (int)(bk / p.h_kv);
+    const int kh = (int)(bk % p.h_kv);
+    const int G = p.Hq / p.h_kv;
+    const int g0 = grp * GT;
+    for (int idx = t; idx < GT * D; idx += 256) {
+        const int g = idx / D, i = idx % D;
+        const int64_t row = (int64_t)b * p.Hq + kh * G + g0 + g;
+        qs[idx] = (g0 + g < G) ? p.qp[row * D + i] : 0.f;
+    }
+    for (int idx = t; idx < GT * p.m; idx += 256) {
+        const int g = idx / p.m, l = idx % p.m;
+        const int64_t row = (int64_t)b * p.Hq + kh * G + g0 + g;
+        ss[g * D + l] = (g0 + g < G) ? p.s[row * p.m + l] : 0.f;
+    }
+    if (t < 16) lvl[t] = p.levels[t];
+    __syncthreads();
+    const int sl = clamp_len(p.seq_len, b, p.L_cap);
+    const int j = p.k0 + blockIdx.y * 256 + t;
+    if (j >= sl || j >= p.k0 + p.klen) return;
+    const int64_t n = bk * p.L_cap + j;
+    uint32_t cw[CW];
+    const uint32_t* src = p.codes + n * CW;
+#pragma unroll
+    for (int w = 0; w < CW; ++w) cw[w] = src[w];
+    float acc[GT];
+#pragma unroll
+    for (int g = 0; g < GT; ++g) acc[g] = 0.f;
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+        const float y = lvl[code_at<D, BITS>(cw, i)];
+#pragma unroll
+        for (int g = 0; g < GT; ++g) acc[g] = fmaf(qs[g * D + i], y, acc[g]);
+    }
+    float accs[GT];
+#pragma unroll
+    for (int g = 0; g < GT; ++g) accs[g] = 0.f;
+    const int mw = p.m >> 5;
+    for (int w = 0; w < mw; ++w) {
+        const uint32_t word = p.signs[n * mw + w];
+#pragma unroll
+        for (int bit = 0; bit < 32; ++bit) {
+            const float z = ((word >> bit) & 1u) ? 1.0f : -1.0f;
+#pragma unroll
+            for (int g = 0; g < GT; ++g) accs[g] = fmaf(ss[g * D + w * 32 + bit], z, accs[g]);
+        }
+    }
+    const float nu = p.norm[n];
+    const float cg = p.m ? (kQjl / (float)p.m) * p.rnorm[n] : 0.f;
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+        if (g0 + g < G) {
+            const int64_t row = (int64_t)b * p.Hq + kh * G + g0 + g;
+            p.out[row * p.ld + (j - p.col0)] = nu * (acc[g] + cg * accs[g]);
+        }
+    }
+}
+
+// ----------------------------------------------------------------- top-k
+struct TopK {
+    const float* scores;  // [rows][ld] relative to row0, column c holds key col0 + c
+    int64_t ld;
+    int64_t row0;         // absolute row (b*Hq + head) of workgroup 0
+    int32_t col0, cnt;    // keys [col0, col0 + cnt)
+    int32_t Hq, L_cap, k, first;
+    const int32_t* seq_len;
+    float* out_val;       // [rows][k]
+    int32_t* out_idx;
+};
+
+__device__ __forceinline__ bool better(float a, int ia, float b, int ib) {
+    return a > b || (a == b && ia < ib);
+}
+
+// one workgroup per row: thread-local sorted lists, then k rounds of a
+// block-wide argmax; the running list of earlier chunks seeds thread 0
+__global__ __launch_bounds__(256) void topk_merge_kernel(TopK p) {
+    __shared__ float rv[4];
+    __shared__ int ri[4];
+    __shared__ int rt[4];
+    __shared__ int winner;
+    const int t = threadIdx.x;
+    const int64_t rel = blockIdx.x;
+    const int64_t row = p.row0 + rel;
+    const int b = (int)(row / p.Hq);
+    const int sl = clamp_len(p.seq_len, b, p.L_cap);
+    float vals[kTopKMax];
+    int idx[kTopKMax];
+#pragma unroll
+    for (int s = 0; s < kTopKMax; ++s) {
+        vals[s] = -INFINITY;
+        idx[s] = 0x7fffffff;
+    }
+    auto insert = [&](float x, int id) {
+        if (!(x == x)) return;  // NaN is never kept
+#pragma unroll
+        for (int s = 0; s < kTopKMax; ++s) {
+            if (s < p.k && better(x, id, vals[s], idx[s])) {
+                const float tv = vals[s];
+                const int ti = idx[s];
+                vals[s] = x;
+                idx[s] = id;
+                x = tv;
+                id = ti;
+            }
+        }
+    };
+    if (t == 0 && !p.first) {
+        for (int s = 0; s < p.k; ++s) {
+            const int id = p.out_idx[row * p.k + s];
+            if (id >= 0) insert(p.out_val[row * p.k + s], id);
+        }
+    }
+    const int hi = min(p.col0 + p.cnt, sl);
+    for (int key = p.col0 + t; key < hi; key += 256) insert(p.scores[rel * p.ld + (key - p.col0)], key);
+    int head = 0;
+    for (int r = 0; r < p.k; ++r) {
+        float bv = -INFINITY;
+        int bi = 0x7fffffff;
+        if (head < p.k) {
+#pragma unroll
+            for (int s = 0; s < kTopKMax; ++s)
+                if (s == head) {
+                    bv = vals[s];
+                    bi = idx[s];
+                }
+        }
+        int bt = t;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const float ov = __shfl_xor(bv, o);
+            const int oi = __shfl_xor(bi, o);
+            const int ot = __shfl_xor(bt, o);
+            if (better(ov, oi, bv, bi)) {
+                bv = ov;
+                bi = oi;
+                bt = ot;
+            }
+        }
+        if ((t & 63) == 0) {
+            rv[t >> 6] = bv;
+            ri[t >> 6] = bi;
+            rt[t >> 6] = bt;
+        }
+        __syncthreads();
+        if (t == 0) {
+            float v = rv[0];
+            int i = ri[0], w = rt[0];
+            for (int q = 1; q < 4; ++q)
+                if (better(rv[q], ri[q], v, i)) {
+                    v = rv[q];
+                    i = ri[q];
+                    w = rt[q];
+                }
+            const bool ok = i != 0x7fffffff;
+            p.out_val[row * p.k + r] = ok ? v : -INFINITY;
+            p.out_idx[row * p.k + r] = ok ? i : -1;
+            winner = ok ? w : -1;
+        }
+        __syncthreads();
+        if (t == winner) ++head;
+        __syncthreads();
+    }
+}
+
+// ------------------------------------------------- dense (Haar) scoring
+struct DenseScan {
+    const float* levels;
+    const float* norm;
+    const float* rnorm;
+    const uint32_t* codes;
+    const uint32_t* signs;
+    int32_t d, m, bits;
+    int64_t rec0;   // record index of key 0 of this (b, kh)
+    int32_t k0, cnt;
+    float* aug;     // [cnt][d + m]: t[c], then sqrt(pi/2)/m gamma z
+};
+
+__global__ __launch_bounds__(256) void dense_dequant_kernel(DenseScan p) {
+    const int width = p.d + p.m;
+    const int cw = p.bits * p.d / 32, mw = p.m / 32;
+    const uint32_t mask = (1u << p.bits) - 1u;
+    const float cq = p.m ? kQjl / (float)p.m : 0.f;
+    for (int64_t r = blockIdx.x; r < p.cnt; r += gridDim.x) {
+        const int64_t n = p.rec0 + p.k0 + r;
+        const uint32_t* c = p.codes + n * cw;
+        float* dst = p.aug + r * width;
+        for (int i = threadIdx.x; i < p.d; i += blockDim.x) {
+            const int bp = p.bits * i;
+            uint32_t v = c[bp >> 5] >> (bp & 31);
+            if ((bp & 31) + p.bits > 32) v |= c[(bp >> 5) + 1] << (32 - (bp & 31));
+            dst[i] = p.levels[v & mask];
+        }
+        if (p.m) {
+            const float g = cq * p.rnorm[n];
+            const uint32_t* sg = p.signs + n * mw;
+            for (int l = threadIdx.x; l < p.m; l += blockDim.x)
+                dst[p.d + l] = ((sg[l >> 5] >> (l & 31)) & 1u) ? g : -g;
+        }
+    }
+}
+
+// scores[g][c] *= nu of key k0 + c for keys below seq_len; with `out`
+// given, those scores are also copied to out[g][k0 + c] (row stride out_ld)
+__global__ __launch_bounds__(256) void finalize_scores_kernel(float* scores, int64_t ld, int rows, int cnt,
+                                                              const float* norm, int64_t rec0, int k0,
+                                                              const int32_t* seq_len, int b, int L_cap,
+                                                              float* out, int64_t out_ld) {
+    const int sl = clamp_len(seq_len, b, L_cap);
+    const int64_t total = (int64_t)rows * cnt;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+        const int64_t g = e / cnt;
+        const int c = (int)(e % cnt);
+        if (k0 + c >= sl) continue;
+        const float v = scores[g * ld + c] * norm[rec0 + k0 + c];
+        scores[g * ld + c] = v;
+        if (out) out[g * out_ld + k0 + c] = v;
+    }
+}
+
+// ------------------------------------------------------------- decode
+struct DecK {
+    const float* qp;
+    const float* s;
+    const float* lv_k;
+    const float* lv_v;
+    const float* k_norm;
+    const float* k_rnorm;
+    const uint32_t* k_codes;
+    const uint32_t* k_signs;
+    const float* v_norm;
+    const float* v_rnorm;
+    const uint32_t* v_codes;
+    const uint32_t* v_signs;
+    const int32_t* seq_len;
+    int32_t Hq, h_kv, L_cap, m, ngroups, nsplit, chunk;
+    float scale;
+    float* part;  // [B*Hq][nsplit][2 + d + m]
+};
+
+template <int D, int BITS, int GT>
+__global__ __launch_bounds__(256) void decode_split_kernel(DecK p) {
+    constexpr int CW = BITS * D / 32;
+    extern __shared__ float lds[];
+    const int m = p.m, mw = m >> 5;
+    float* qs = lds;                      // [GT][D]
+    float* ss = qs + GT * D;              // [GT][D]   (m <= D)
+    float* lvk = ss + GT * D;             // [16]
+    float* lvv = lvk + 16;                // [16]
+    float* pv = lvv + 16;                 // [256][GT]  p * nu_v
+    float* pz = pv + 256 * GT;            // [256][GT]  p * nu_v * gamma_v
+    float* red = pz + 256 * GT;           // [4][GT]
+    float* mrun = red + 4 * GT;           // [GT]
+    float* lrun = mrun + GT;              // [GT]
+    float* alpha = lrun + GT;             // [GT]
+    uint32_t* vc = reinterpret_cast<uint32_t*>(alpha + GT);  // [256][CW]
+    uint32_t* vs = vc + 256 * CW;                            // [256][mw]
+
+    const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
+    const int grp = blockIdx.x % p.ngroups;
+    const int64_t bk = blockIdx.x / p.ngroups;
+    const int b = (int)(bk / p.h_kv);
+    const int kh = (int)(bk % p.h_kv);
+    const int G = p.Hq / p.h_kv;
+    const int g0 = grp * GT;
+    const int split = blockIdx.y;
+    for (int idx = t; idx < GT * D; idx += 256) {
+        const int g = idx / D, i = idx % D;
+        const int64_t row = (int64_t)b * p.Hq + kh * G + g0 + g;
+        qs[idx] = (g0 + g < G) ? p.qp[row * D + i] : 0.f;
+        ss[idx] = (g0 + g < G && i < m) ? p.s[row * m + i] : 0.f;
+    }
+    if (t < 16) {
+        lvk[t] = p.lv_k[t];
+        lvv[t] = p.lv_v[t];
+    }
+    if (t < GT) {
+        mrun[t] = -INFINITY;
+        lrun[t] = 0.f;
+    }
+    __syncthreads();
+
+    const int sl = clamp_len(p.seq_len, b, p.L_cap);
+    const int c0 = split * p.chunk;
+    const int c1 = min(c0 + p.chunk, sl);
+    const float cqk = m ? kQjl / (float)m : 0.f;
+
+    // coordinate role of this thread in the value accumulation
+    const bool ycoord = t < D;
+    const bool zcoord = !ycoord && t < D + m;
+    const int bp = BITS * (ycoord ? t : 0);
+    const int cwi = bp >> 5, cof = bp & 31;
+    const bool straddle = cof + BITS > 32;
+    const int zl = t - D;
+    float acc[GT];
+#pragma unroll
+    for (int g = 0; g < GT; ++g) acc[g] = 0.f;
+
+    for (int base = c0; base < c1; base += 256) {
+        const int j = base + t;
+        const bool valid = j < c1;
+        const int64_t n = bk * p.L_cap + j;
+        float a[GT];
+        float nu_v = 0.f, gm_v = 0.f;
+        if (valid) {
+            uint32_t cw[CW];
+            const uint32_t* src = p.k_codes + n * CW;
+#pragma unroll
+            for (int w = 0; w < CW; ++w) cw[w] = src[w];
+            float ay[GT], az[GT];
+#pragma unroll
+            for (int g = 0; g < GT; ++g) ay[g] = az[g] = 0.f;
+#pragma unroll
+            for (int i = 0; i < D; ++i) {
+                const float y = lvk[code_at<D, BITS>(cw, i)];
+#pragma unroll
+                for (int g = 0; g < GT; ++g) ay[g] = fmaf(qs[g * D + i], y, ay[g]);
+            }
+            for (int w = 0; w < mw; ++w) {
+                const uint32_t word = p.k_signs[n * mw + w];
+#pragma unroll
+                for (int bit = 0; bit < 32; ++bit) {
+                    const float z = ((word >> bit) & 1u) ? 1.0f : -1.0f;
+#pragma unroll
+                    for (int g = 0; g < GT; ++g) az[g] = fmaf(ss[g * D + w * 32 + bit], z, az[g]);
+                }
+            }
+            const float nu = p.k_norm[n];
+            const float cg = m ? cqk * p.k_rnorm[n] : 0.f;
+#pragma unroll
+            for (int g = 0; g < GT; ++g) a[g] = p.scale * (nu * (ay[g] + cg * az[g]));
+            // stage the value record of key j
+            const uint32_t* vsrc = p.v_codes + n * CW;
+#pragma unroll
+            for (int w = 0; w < CW; ++w) vc[t * CW + w] = vsrc[w];
+            for (int w = 0; w < mw; ++w) vs[t * mw + w] = p.v_signs[n * mw + w];
+            nu_v = p.v_norm[n];
+            gm_v = m ? p.v_rnorm[n] : 0.f;
+        } else {
+#pragma unroll
+            for (int g = 0; g < GT; ++g) a[g] = -INFINITY;
+        }
+        // block max of this sub-block, new running max and rescale factor
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+            const float wm = wave_max(a[g]);
+            if (lane == 0) red[wave * GT + g] = wm;
+        }
+        __syncthreads();
+        if (t < GT) {
+            const float bm = fmaxf(fmaxf(red[t], red[GT + t]), fmaxf(red[2 * GT + t], red[3 * GT + t]));
+            const float mo = mrun[t];
+            const float mn = fmaxf(mo, bm);
+            alpha[t] = (mn == -INFINITY) ? 1.0f : expf(mo - mn);
+            mrun[t] = mn;
+        }
+        __syncthreads();
+        float psum[GT];
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+            const float pj = valid ? expf(a[g] - mrun[g]) : 0.f;
+            psum[g] = pj;
+            pv[t * GT + g] = pj * nu_v;
+            pz[t * GT + g] = pj * nu_v * gm_v;
+        }
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+            const float ws = wave_sum(psum[g]);
+            if (lane == 0) red[wave * GT + g] = ws;
+        }
+        __syncthreads();
+        if (t < GT) lrun[t] = lrun[t] * alpha[t] + (red[t] + red[GT + t] + red[2 * GT + t] + red[3 * GT + t]);
+#pragma unroll
+        for (int g = 0; g < GT; ++g) acc[g] *= alpha[g];
+        const int cnt = min(256, c1 - base);
+        if (ycoord) {
+            for (int jj = 0; jj < cnt; ++jj) {
+                uint32_t c = vc[jj * CW + cwi] >> cof;
+                if (straddle) c |= vc[jj * CW + cwi + 1] << (32 - cof);
+                const float y = lvv[c & ((1u << BITS) - 1u)];
+#pragma unroll
+                for (int g = 0; g < GT; ++g) acc[g] = fmaf(pv[jj * GT + g], y, acc[g]);
+            }
+        } else if (zcoord) {
+            for (int jj = 0; jj < cnt; ++jj) {
+                const float z = ((vs[jj * mw + (zl >> 5)] >> (zl & 31)) & 1u) ? 1.0f : -1.0f;
+#pragma unroll
+                for (int g = 0; g < GT; ++g) acc[g] = fmaf(pz[jj * GT + g], z, acc[g]);
+            }
+        }
+        __syncthreads();
+    }
+    const int width = 2 + D + m;
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+        if (g0 + g >= G) continue;
+        const int64_t row = (int64_t)b * p.Hq + kh * G + g0 + g;
+        float* dst = p.part + (row * p.nsplit + split) * width;
+        if (t == 0) {
+            dst[0] = mrun[g];
+            dst[1] = lrun[g];
+        }
+        if (t < D + m) dst[2 + t] = acc[g];
+    }
+}
+
+struct MergeK {
+    const float* part;
+    int32_t nsplit, d, m;
+    const float* sigma;   // Hadamard form
+    const float* sketch;  // [m][d]
+    float* out;           // [B*Hq][d]
+};
+
+// log-sum-exp merge of the splits, then back to the original domain:
+// out = sigma * H (A_y + sqrt(pi/2)/m S^T A_z) / (sqrt(d) l)
+template <int D>
+__global__ __launch_bounds__(256) void decode_merge_kernel(MergeK p) {
+    __shared__ float w[D];
+    __shared__ float az[D];
+    const int t = threadIdx.x;
+    const int64_t row = blockIdx.x;
+    const int width = 2 + D + p.m;
+    const float* base = p.part + row * p.nsplit * width;
+    float mx = -INFINITY;
+    for (int s = 0; s < p.nsplit; ++s) mx = fmaxf(mx, base[s * width]);
+    float l = 0.f, ay = 0.f, z = 0.f;
+    if (mx != -INFINITY) {
+        for (int s = 0; s < p.nsplit; ++s) {
+            const float ms = base[s * width];
+            if (ms == -INFINITY) continue;
+            const float f = expf(ms - mx);
+            l += f * base[s * width + 1];
+            if (t < D) ay += f * base[s * width + 2 + t];
+            if (t < p.m) z += f * base[s * width + 2 + D + t];
+        }
+    }
+    if (t < p.m) az[t] = z;
+    __syncthreads();
+    if (t < D) {
+        float corr = 0.f;
+        for (int k = 0; k < p.m; ++k) corr = fmaf(p.sketch[(int64_t)k * D + t], az[k], corr);
+        w[t] = ay + (p.m ? kQjl / (float)p.m : 0.f) * corr;
+    }
+    __syncthreads();
+    for (int s = 1; s < D; s <<= 1) {
+        if (t < D / 2) {
+            const int i = (t / s) * 2 * s + (t % s);
+            const float a = w[i], bb = w[i + s];
+            w[i] = a + bb;
+            w[i + s] = a - bb;
+        }
+        __syncthreads();
+    }
+    if (t < D) {
+        const float o = (l > 0.f) ? p.sigma[t] * w[t] / (sqrtf((float)D) * l) : 0.f;
+        p.out[row * D + t] = o;
+    }
+}
+
+// ------------------------------------------------------------ dispatch
+using LogFn = void (*)(LogK);
+using DecFn = void (*)(DecK);
+
+template <int D, int BITS>
+LogFn pick_log_gt(int gt) {
+    return gt == 8 ? logits_rht_kernel<D, BITS, 8> : logits_rht_kernel<D, BITS, 4>;
+}
+template <int D>
+LogFn pick_log_bits(int bits, int gt) {
+    switch (bits) {
+        case 1: return pick_log_gt<D, 1>(gt);
+        case 2: return pick_log_gt<D, 2>(gt);
+        case 3: return pick_log_gt<D, 3>(gt);
+        case 4: return pick_log_gt<D, 4>(gt);
+    }
+    return nullptr;
+}
+LogFn pick_logits(int d, int bits, int gt) {
+    if (d == 64) return pick_log_bits<64>(bits, gt);
+    if (d == 128) return pick_log_bits<128>(bits, gt);
+    return nullptr;
+}
+template <int D, int BITS>
+DecFn pick_dec_gt(int gt) {
+    return gt == 8 ? decode_split_kernel<D, BITS, 8> : decode_split_kernel<D, BITS, 4>;
+}
+template <int D>
+DecFn pick_dec_bits(int bits, int gt) {
+    switch (bits) {
+        case 1: return pick_dec_gt<D, 1>(gt);
+        case 2: return pick_dec_gt<D, 2>(gt);
+        case 3: return pick_dec_gt<D, 3>(gt);
+        case 4: return pick_dec_gt<D, 4>(gt);
+    }
+    return nullptr;
+}
+DecFn pick_decode(int d, int bits, int gt) {
+    if (d == 64) return pick_dec_bits<64>(bits, gt);
+    if (d == 128) return pick_dec_bits<128>(bits, gt);
+    return nullptr;
+}
+
+int group_tile(int G) { return G >= 8 ? 8 : 4; }
+
+constexpr int kScanChunk = 65536;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int decode_nsplit(int64_t bkg, int L_cap) {
+    int64_t want = (2048 + bkg - 1) / bkg;
+    int64_t maxs = (L_cap + 255) / 256;
+    if (want > maxs) want = maxs;
+    if (want < 1) want = 1;
+    return (int)want;
+}
+
+int decode_chunk(int L_cap, int nsplit) {
+    int c = (L_cap + nsplit - 1) / nsplit;
+    return ((c + 255) / 256) * 256;
+}
+
+QPrep make_qprep(const tq_codebook* ck, const AttnArgs& a, float* qp, float* s) {
+    QPrep q{};
+    q.q = a.q;
+    q.bf16 = a.bf16;
+    q.Hq = a.Hq;
+    q.L_cap = a.L_cap;
+    q.d = ck->spec.d;
+    q.m = ck->spec.m;
+    q.seq_len = a.seq_len;
+    q.rope_cos = a.rope_cos;
+    q.rope_sin = a.rope_sin;
+    q.sigma = ck->dev.sigma;
+    q.sketch = ck->dev.sketch;
+    q.qp = qp;
+    q.s = s;
+    return q;
+}
+
+hipError_t launch_qprep_rht(const tq_codebook* ck, const AttnArgs& a, float* qp, float* s,
+                            hipStream_t stream) {
+    QPrep q = make_qprep(ck, a, qp, s);
+    const unsigned grid = (unsigned)((int64_t)a.B * a.Hq);
+    if (ck->spec.d == 64) hipLaunchKernelGGL(qprep_rht_kernel<64>, dim3(grid), dim3(256), 0, stream, q);
+    else if (ck->spec.d == 128) hipLaunchKernelGGL(qprep_rht_kernel<128>, dim3(grid), dim3(256), 0, stream, q);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t logits_workspace_bytes(const tq_codebook* ck, int64_t B, int Hq, int h_kv, int L_cap, int top_k) {
+    const size_t d = ck->spec.d, m = ck->spec.m;
+    const size_t rows = (size_t)B * Hq;
+    const size_t chunk = (size_t)std::min(L_cap, kScanChunk);
+    if (!ck->dense) {
+        size_t bytes = align256(rows * (d + m) * 4);
+        if (top_k) bytes += align256(rows * chunk * 4);
+        return bytes;
+    }
+    const int G = h_kv > 0 ? Hq / h_kv : 0;
+    size_t bytes = align256(rows * d * 4) + align256(rows * (d + m) * 4);  // rope'd q, [q' | s]
+    bytes += align256(chunk * (d + m) * 4);                                // dequantised keys
+    bytes += align256((size_t)G * chunk * 4);                              // scores
+    (void)top_k;
+    return bytes;
+}
+
+size_t decode_workspace_bytes(const tq_codebook* ck, const tq_codebook* cv, int64_t B, int Hq, int h_kv,
+                              int L_cap) {
+    const size_t d = ck->spec.d, mk = ck->spec.m, mv = cv->spec.m;
+    const size_t rows = (size_t)B * Hq;
+    const int G = h_kv > 0 ? Hq / h_kv : 1;
+    const int gt = group_tile(G);
+    const int64_t bkg = (int64_t)B * h_kv * ((G + gt - 1) / gt);
+    const int ns = decode_nsplit(bkg > 0 ? bkg : 1, L_cap);
+    return align256(rows * (d + mk) * 4) + align256(rows * ns * (2 + d + mv) * 4);
+}
+
+hipError_t launch_logits(const tq_codebook* ck, const tq_packed& k, const AttnArgs& a, hipStream_t stream) {
+    const int d = ck->spec.d, m = ck->spec.m, bits = ck->spec.bits;
+    const int G = a.Hq / a.h_kv;
+    const int64_t rows = (int64_t)a.B * a.Hq;
+    char* ws = static_cast<char*>(a.ws);
+    const int chunk = std::min(a.L_cap, kScanChunk);
+    if (!ck->dense) {
+        float* qp = reinterpret_cast<float*>(ws);
+        float* s = qp + rows * d;
+        float* scores = reinterpret_cast<float*>(ws + align256(rows * (d + m) * 4));
+        hipError_t e = launch_qprep_rht(ck, a, qp, s, stream);
+        if (e != hipSuccess) return e;
+        const int gt = group_tile(G);
+        LogFn fn = pick_logits(d, bits, gt);
+        if (!fn) return hipErrorInvalidValue;
+        LogK p{};
+        p.qp = qp;
+        p.s = s;
+        p.levels = ck->dev.levels;
+        p.norm = k.norm;
+        p.rnorm = k.rnorm;
+        p.codes = k.codes;
+        p.signs = k.signs;
+        p.seq_len = a.seq_len;
+        p.Hq = a.Hq;
+        p.h_kv = a.h_kv;
+        p.L_cap = a.L_cap;
+        p.m = m;
+        p.ngroups = (G + gt - 1) / gt;
+        const unsigned gx = (unsigned)((int64_t)a.B * a.h_kv * p.ngroups);
+        if (a.top_k == 0) {
+            p.k0 = 0;
+            p.klen = a.L_cap;
+            p.out = a.out;
+            p.ld = a.L_cap;
+            p.col0 = 0;
+            hipLaunchKernelGGL(fn, dim3(gx, (a.L_cap + 255) / 256), dim3(256), 0, stream, p);
+            return hipGetLastError();
+        }
+        for (int k0 = 0; k0 < a.L_cap; k0 += chunk) {
+            const int cnt = std::min(chunk, a.L_cap - k0);
+            p.k0 = k0;
+            p.klen = cnt;
+            p.out = scores;
+            p.ld = chunk;
+            p.col0 = k0;
+            hipLaunchKernelGGL(fn, dim3(gx, (cnt + 255) / 256), dim3(256), 0, stream, p);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            TopK tk{};
+            tk.scores = scores;
+            tk.ld = chunk;
+            tk.col0 = k0;
+            tk.cnt = cnt;
+            tk.Hq = a.Hq;
+            tk.L_cap = a.L_cap;
+            tk.k = a.top_k;
+            tk.first = k0 == 0;
+            tk.seq_len = a.seq_len;
+            tk.out_val = a.out;
+            tk.out_idx = a.topk_idx;
+            hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)rows), dim3(256), 0, stream, tk);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    // dense rotation: q' and s by GEMM, keys dequantised per chunk, scores by GEMM
+    float* qr = reinterpret_cast<float*>(ws);
+    float* qaug = reinterpret_cast<float*>(ws + align256(rows * d * 4));
+    float* aug = reinterpret_cast<float*>(ws + align256(rows * d * 4) + align256(rows * (d + m) * 4));
+    float* scores = reinterpret_cast<float*>(ws + align256(rows * d * 4) + align256(rows * (d + m) * 4) +
+                                             align256((size_t)chunk * (d + m) * 4));
+    QPrep q = make_qprep(ck, a, nullptr, nullptr);
+    hipLaunchKernelGGL(qrope_kernel, dim3((unsigned)rows), dim3(256), 0, stream, q, qr);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_gemm_nt(qr, d, ck->dev.rot, d, qaug, d + m, (int)rows, d, d, stream);
+    if (e != hipSuccess) return e;
+    if (m) {
+        e = launch_gemm_nt(qaug, d + m, ck->dev.sketch, d, qaug + d, d + m, (int)rows, m, d, stream);
+        if (e != hipSuccess) return e;
+    }
+    for (int b = 0; b < a.B; ++b)
+        for (int kh = 0; kh < a.h_kv; ++kh) {
+            const int64_t rec0 = ((int64_t)b * a.h_kv + kh) * a.L_cap;
+            const int64_t row0 = (int64_t)b * a.Hq + (int64_t)kh * G;
+            for (int k0 = 0; k0 < a.L_cap; k0 += chunk) {
+                const int cnt = std::min(chunk, a.L_cap - k0);
+                DenseScan ds{};
+                ds.levels = ck->dev.levels;
+                ds.norm = k.norm;
+                ds.rnorm = k.rnorm;
+                ds.codes = k.codes;
+                ds.signs = k.signs;
+                ds.d = d;
+                ds.m = m;
+                ds.bits = bits;
+                ds.rec0 = rec0;
+                ds.k0 = k0;
+                ds.cnt = cnt;
+                ds.aug = aug;
+                hipLaunchKernelGGL(dense_dequant_kernel, dim3((unsigned)std::min(cnt, 8192)), dim3(256), 0, stream, ds);
+                e = hipGetLastError();
+                if (e != hipSuccess) return e;
+                e = launch_gemm_nt(qaug + row0 * (d + m), d + m, aug, d + m, scores, chunk, G, cnt, d + m, stream);
+                if (e != hipSuccess) return e;
+                const int64_t tot = (int64_t)G * cnt;
+                const unsigned sg = (unsigned)std::min<int64_t>((tot + 255) / 256, 65536);
+                hipLaunchKernelGGL(finalize_scores_kernel, dim3(sg), dim3(256), 0, stream, scores, (int64_t)chunk, G,
+                                   cnt, k.norm, rec0, k0, a.seq_len, b, a.L_cap,
+                                   a.top_k ? nullptr : a.out + row0 * a.L_cap, (int64_t)a.L_cap);
+                e = hipGetLastError();
+                if (e != hipSuccess) return e;
+                if (a.top_k) {
+                    TopK tk{};
+                    tk.scores = scores;
+                    tk.ld = chunk;
+                    tk.col0 = k0;
+                    tk.cnt = cnt;
+                    tk.Hq = a.Hq;
+                    tk.L_cap = a.L_cap;
+                    tk.k = a.top_k;
+                    tk.first = k0 == 0;
+                    tk.seq_len = a.seq_len;
+                    tk.row0 = row0;
+                    tk.out_val = a.out;
+                    tk.out_idx = a.topk_idx;
+                    hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)G), dim3(256), 0, stream, tk);
+                    e = hipGetLastError();
+                    if (e != hipSuccess) return e;
+                }
+            }
+        }
+    return hipSuccess;
+}
+
+hipError_t launch_decode(const tq_codebook* ck, const tq_codebook* cv, const tq_packed& k, const tq_packed& v,
+                         const AttnArgs& a, hipStream_t stream) {
+    const int d = ck->spec.d, m = ck->spec.m, bits = ck->spec.bits;
+    if (ck->dense || cv->dense || cv->spec.bits != bits || cv->spec.m != m) return hipErrorInvalidValue;
+    const int G = a.Hq / a.h_kv;
+    const int64_t rows = (int64_t)a.B * a.Hq;
+    char* ws = static_cast<char*>(a.ws);
+    float* qp = reinterpret_cast<float*>(ws);
+    float* s = qp + rows * d;
+    float* part = reinterpret_cast<float*>(ws + align256(rows * (d + m) * 4));
+    hipError_t e = launch_qprep_rht(ck, a, qp, s, stream);
+    if (e != hipSuccess) return e;
+    const int gt = group_tile(G);
+    DecFn fn = pick_decode(d, bits, gt);
+    if (!fn) return hipErrorInvalidValue;
+    DecK p{};
+    p.qp = qp;
+    p.s = s;
+    p.lv_k = ck->dev.levels;
+    p.lv_v = cv->dev.levels;
+    p.k_norm = k.norm;
+    p.k_rnorm = k.rnorm;
+    p.k_codes = k.codes;
+    p.k_signs = k.signs;
+    p.v_norm = v.norm;
+    p.v_rnorm = v.rnorm;
+    p.v_codes = v.codes;
+    p.v_signs = v.signs;
+    p.seq_len = a.seq_len;
+    p.Hq = a.Hq;
+    p.h_kv = a.h_kv;
+    p.L_cap = a.L_cap;
+    p.m = m;
+    p.ngroups = (G + gt - 1) / gt;
+    const int64_t bkg = (int64_t)a.B * a.h_kv * p.ngroups;
+    p.nsplit = decode_nsplit(bkg, a.L_cap);
+    p.chunk = decode_chunk(a.L_cap, p.nsplit);
+    p.scale = a.scale;
+    p.part = part;
+    const int cw = bits * d / 32;
+    const size_t lds = (size_t)(2 * gt * d + 32 + 2 * 256 * gt + 4 * gt + 3 * gt) * 4 + (size_t)256 * (cw + m / 32) * 4;
+    hipLaunchKernelGGL(fn, dim3((unsigned)bkg, (unsigned)p.nsplit), dim3(256), lds, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    MergeK mk{};
+    mk.part = part;
+    mk.nsplit = p.nsplit;
+    mk.d = d;
+    mk.m = m;
+    mk.sigma = cv->dev.sigma;
+    mk.sketch = cv->dev.sketch;
+    mk.out = a.out;
+    if (d == 64) hipLaunchKernelGGL(decode_merge_kernel<64>, dim3((unsigned)rows), dim3(256), 0, stream, mk);
+    else hipLaunchKernelGGL(decode_merge_kernel<128>, dim3((unsigned)rows), dim3(256), 0, stream, mk);
+    return hipGetLastError();
+}
+
+}  // namespace tq

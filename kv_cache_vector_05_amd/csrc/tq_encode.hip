@@ -1,0 +1,531 @@
+// Encoder kernels (FibQuant summary, sections 1 and 2.3; iaemfoco post,
+// "TurboQuant: Uma Nova Abordagem"; itstec post, "Por dentro do processo de
+// compressao KV"; TurboESM summary, technical section 2 for RoPE first).
+//
+// Hadamard form (d = 64 or 128): one wave64 encodes a tile of 32 consecutive
+// tokens of one (sequence, head).  Lane l holds vector l % 32, half
+// h = l / 32 of its coordinates ([h*d/2, (h+1)*d/2)), so
+//   * each lane reads one contiguous run of d/2 elements,
+//   * RoPE's pair (i, i + d/2) and the last butterfly stage of the
+//     Walsh-Hadamard transform are one cross-half swap (lane l <-> l ^ 32),
+//     every other stage stays in registers,
+//   * the codes of a half are a whole number of 32-bit words, written by that
+//     lane alone,
+//   * the residual already sits in the B-operand layout of
+//     v_mfma_f32_32x32x2f32 (B[k][j]: k = l / 32, j = l % 32), so the sketch
+//     S e of all 32 vectors is m/32 row blocks of d/2 MFMA steps each, with S
+//     read from LDS in the matching A-operand order.
+// Blocks are persistent (grid-stride over tiles) so each block stages the
+// sketch table in LDS once; consecutive tiles of a block walk the heads of
+// the same tokens, so RoPE table rows are reused from cache.
+//
+// Dense form (any d that is a multiple of 64): per-vector norm, then
+// Y = U Pi^T and Z = E S^T as MFMA GEMMs over chunks of vectors in the
+// caller's workspace, with per-vector quantise and sign-pack kernels between.
+#include <hip/hip_runtime.h>
+
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+struct EncK {
+    const void* x;
+    int64_t s_seq, s_tok, s_head;
+    int32_t n_seq, n_tok, h_kv, tok_offset, L_cap, tok_blocks;
+    int64_t n_tiles;
+    const float* rope_cos;
+    const float* rope_sin;
+    const float* sigma;
+    const float* levels;
+    const float* thresholds;
+    const float* sketch_mfma;
+    float* norm;
+    float* rnorm;
+    uint32_t* codes;
+    uint32_t* signs;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+template <int D, int BITS, int M, bool BF16>
+__global__ __launch_bounds__(256) void encode_rht_kernel(EncK p) {
+    constexpr int HALF = D / 2;
+    constexpr int K = 1 << BITS;
+    constexpr int CW = BITS * D / 32;     // code words per record
+    constexpr int WH = BITS * HALF / 32;  // code words per half
+    constexpr int NRB = M / 32;           // sketch row blocks (= sign words)
+    constexpr int SKN = M > 0 ? M * D : 1;
+    __shared__ float s_sk[SKN];
+
+    if constexpr (M > 0) {
+        for (int i = threadIdx.x; i < M * D; i += blockDim.x) s_sk[i] = p.sketch_mfma[i];
+    }
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63;
+    const int v = lane & 31;
+    const int h = lane >> 5;
+
+    // Hadamard signs of this lane's half as a bit mask (bit j: flip coordinate h*HALF + j)
+    uint32_t flip[HALF / 32];
+#pragma unroll
+    for (int w = 0; w < HALF / 32; ++w) {
+        uint32_t mask = 0;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) mask |= (p.sigma[h * HALF + w * 32 + j] < 0.0f ? 1u : 0u) << j;
+        flip[w] = mask;
+    }
+    float lv[K], th[K - 1];
+#pragma unroll
+    for (int k = 0; k < K; ++k) lv[k] = p.levels[k];
+#pragma unroll
+    for (int k = 0; k < K - 1; ++k) th[k] = p.thresholds[k];
+    const float inv_sqrt_d = 1.0f / sqrtf((float)D);
+
+    const int64_t wave_stride = (int64_t)gridDim.x * (blockDim.x >> 6);
+    for (int64_t tile = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); tile < p.n_tiles;
+         tile += wave_stride) {
+        const int head = (int)(tile % p.h_kv);
+        const int64_t r = tile / p.h_kv;
+        const int tb = (int)(r % p.tok_blocks);
+        const int seq = (int)(r / p.tok_blocks);
+        const int token = tb * 32 + v;
+        const bool valid = token < p.n_tok;
+
+        float x[HALF];
+        if (valid) {
+            const int64_t off = (int64_t)seq * p.s_seq + (int64_t)token * p.s_tok +
+                                (int64_t)head * p.s_head + h * HALF;
+            if constexpr (BF16) {
+                const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.x) + off);
+#pragma unroll
+                for (int c = 0; c < HALF / 8; ++c) {
+                    const uint4 w = src[c];
+                    x[8 * c + 0] = bf16_lo(w.x);
+                    x[8 * c + 1] = bf16_hi(w.x);
+                    x[8 * c + 2] = bf16_lo(w.y);
+                    x[8 * c + 3] = bf16_hi(w.y);
+                    x[8 * c + 4] = bf16_lo(w.z);
+                    x[8 * c + 5] = bf16_hi(w.z);
+                    x[8 * c + 6] = bf16_lo(w.w);
+                    x[8 * c + 7] = bf16_hi(w.w);
+                }
+            } else {
+                const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(p.x) + off);
+#pragma unroll
+                for (int c = 0; c < HALF / 4; ++c) {
+                    const float4 w = src[c];
+                    x[4 * c + 0] = w.x;
+                    x[4 * c + 1] = w.y;
+                    x[4 * c + 2] = w.z;
+                    x[4 * c + 3] = w.w;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < HALF; ++j) x[j] = 0.0f;
+        }
+
+        // RoPE (keys): pair (i, i + D/2) is (lane half 0, lane half 1) at the same j
+        if (p.rope_cos) {
+            const int pos = p.tok_offset + (valid ? token : 0);
+            const float4* cp = reinterpret_cast<const float4*>(p.rope_cos + (int64_t)pos * HALF);
+            const float4* sp = reinterpret_cast<const float4*>(p.rope_sin + (int64_t)pos * HALF);
+            const float sgn = h ? 1.0f : -1.0f;
+#pragma unroll
+            for (int c = 0; c < HALF / 4; ++c) {
+                const float4 cc = cp[c];
+                const float4 ss = sp[c];
+                const float cs[4] = {cc.x, cc.y, cc.z, cc.w};
+                const float sn[4] = {ss.x, ss.y, ss.z, ss.w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int j = 4 * c + u;
+                    const float other = __shfl_xor(x[j], 32);
+                    x[j] = x[j] * cs[u] + sgn * (other * sn[u]);
+                }
+            }
+        }
+
+        // norm nu and the scale that maps H(sigma*x) to y = Pi (x / nu)
+        float ss = 0.0f;
+#pragma unroll
+        for (int j = 0; j < HALF; ++j) ss = fmaf(x[j], x[j], ss);
+        ss += __shfl_xor(ss, 32);
+        const float nu = sqrtf(ss);
+        const float scale = nu > 0.0f ? inv_sqrt_d / nu : 0.0f;
+
+        // sign flips, then the Walsh-Hadamard butterflies (Sylvester order)
+#pragma unroll
+        for (int j = 0; j < HALF; ++j)
+            x[j] = __uint_as_float(__float_as_uint(x[j]) ^ (((flip[j >> 5] >> (j & 31)) & 1u) << 31));
+#pragma unroll
+        for (int s = 1; s < HALF; s <<= 1) {
+#pragma unroll
+            for (int j = 0; j < HALF; ++j) {
+                if (!(j & s)) {
+                    const float a = x[j], b = x[j + s];
+                    x[j] = a + b;
+                    x[j + s] = a - b;
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < HALF; ++j) {
+            const float o = __shfl_xor(x[j], 32);
+            x[j] = h ? (o - x[j]) : (x[j] + o);
+        }
+
+        // quantise (c = #{k : y >= tau_k}), residual, pack
+        uint32_t cw[WH];
+#pragma unroll
+        for (int w = 0; w < WH; ++w) cw[w] = 0u;
+        float gg = 0.0f;
+#pragma unroll
+        for (int j = 0; j < HALF; ++j) {
+            const float y = x[j] * scale;
+            uint32_t c = 0;
+            float yh = lv[0];
+#pragma unroll
+            for (int k = 0; k < K - 1; ++k) {
+                const bool ge = y >= th[k];
+                c = ge ? (uint32_t)(k + 1) : c;
+                yh = ge ? lv[k + 1] : yh;
+            }
+            const float e = y - yh;
+            x[j] = e;
+            gg = fmaf(e, e, gg);
+            const int bp = BITS * j;
+            cw[bp >> 5] |= c << (bp & 31);
+            if ((bp & 31) + BITS > 32) cw[(bp >> 5) + 1] |= c >> (32 - (bp & 31));
+        }
+        gg += __shfl_xor(gg, 32);
+        const float gamma = sqrtf(gg);
+
+        const int64_t n = ((int64_t)seq * p.h_kv + head) * p.L_cap + p.tok_offset + token;
+        if (valid) {
+            uint32_t* dst = p.codes + n * CW + h * WH;
+#pragma unroll
+            for (int w = 0; w < WH; ++w) dst[w] = cw[w];
+            if (h == 0) p.norm[n] = nu;
+            else if (M > 0) p.rnorm[n] = gamma;
+        }
+
+        if constexpr (M > 0) {
+            // S e for the 32 vectors of the tile: A = S (row block rb), B = e
+            floatx16 acc[NRB];
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[rb][r] = 0.0f;
+#pragma unroll
+            for (int pp = 0; pp < HALF; ++pp) {
+#pragma unroll
+                for (int rb = 0; rb < NRB; ++rb)
+                    acc[rb] = __builtin_amdgcn_mfma_f32_32x32x2f32(s_sk[(rb * HALF + pp) * 64 + lane], x[pp],
+                                                                   acc[rb], 0, 0, 0);
+            }
+            // D[i][j]: j = lane % 32, i = 8*(r/4) + 4*(lane/32) + r%4
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb) {
+                uint32_t wb = 0;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) wb |= (acc[rb][r] >= 0.0f ? 1u : 0u) << (8 * (r >> 2) + (r & 3));
+                wb <<= 4 * h;
+                wb |= __shfl_xor(wb, 32);
+                if (valid && (rb & 1) == h) p.signs[n * NRB + rb] = wb;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- dense form
+struct DenseK {
+    const void* x;
+    int64_t s_seq, s_tok, s_head;
+    int32_t n_tok, h_kv, tok_offset, L_cap, d, m, bits;
+    int64_t start, count;
+    int32_t bf16;
+    const float* rope_cos;
+    const float* rope_sin;
+    const float* levels;
+    const float* thresholds;
+    float* U;  // [count][d]  unit vectors, later residuals
+    float* Y;  // [count][d]  rotated
+    float* Z;  // [count][m]  sketch values
+    float* norm;
+    float* rnorm;
+    uint32_t* codes;
+    uint32_t* signs;
+};
+
+__device__ __forceinline__ int64_t dense_record(const DenseK& p, int64_t vi, int64_t* src_off, int* tok) {
+    const int head = (int)(vi % p.h_kv);
+    const int64_t r = vi / p.h_kv;
+    const int t = (int)(r % p.n_tok);
+    const int64_t seq = r / p.n_tok;
+    *tok = t;
+    *src_off = seq * p.s_seq + (int64_t)t * p.s_tok + (int64_t)head * p.s_head;
+    return (seq * p.h_kv + head) * p.L_cap + p.tok_offset + t;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// one wave per vector: RoPE (if tables), nu, u = x / nu into U
+__global__ __launch_bounds__(256) void dense_prep_kernel(DenseK p) {
+    const int lane = threadIdx.x & 63;
+    const int64_t stride = (int64_t)gridDim.x * 4;
+    const int half = p.d / 2;
+    for (int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); i < p.count; i += stride) {
+        int64_t off;
+        int tok;
+        const int64_t n = dense_record(p, p.start + i, &off, &tok);
+        float ss = 0.0f;
+        float* u = p.U + i * p.d;
+        for (int c = lane; c < half; c += 64) {
+            float a, b;
+            if (p.bf16) {
+                const uint16_t* s = static_cast<const uint16_t*>(p.x) + off;
+                a = __uint_as_float((uint32_t)s[c] << 16);
+                b = __uint_as_float((uint32_t)s[c + half] << 16);
+            } else {
+                const float* s = static_cast<const float*>(p.x) + off;
+                a = s[c];
+                b = s[c + half];
+            }
+            if (p.rope_cos) {
+                const int64_t pos = p.tok_offset + tok;
+                const float cs = p.rope_cos[pos * half + c], sn = p.rope_sin[pos * half + c];
+                const float a2 = a * cs - b * sn;
+                const float b2 = b * cs + a * sn;
+                a = a2;
+                b = b2;
+            }
+            u[c] = a;
+            u[c + half] = b;
+            ss = fmaf(a, a, fmaf(b, b, ss));
+        }
+        ss = wave_sum(ss);
+        const float nu = sqrtf(ss);
+        const float inv = nu > 0.0f ? 1.0f / nu : 0.0f;
+        for (int c = lane; c < p.d; c += 64) u[c] = u[c] * inv;
+        if (lane == 0) p.norm[n] = nu;
+    }
+}
+
+// one wave per vector: codes from Y (assembled in LDS), residual into U, gamma
+constexpr int kMaxCodeWords = 4 * 4096 / 32;
+__global__ __launch_bounds__(256) void dense_quant_kernel(DenseK p) {
+    __shared__ uint32_t words[4][kMaxCodeWords];
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int K = 1 << p.bits;
+    const int cw = p.bits * p.d / 32;
+    float lv[16], th[15];
+    for (int k = 0; k < 16; ++k) lv[k] = k < K ? p.levels[k] : 0.0f;
+    for (int k = 0; k < 15; ++k) th[k] = k < K - 1 ? p.thresholds[k] : INFINITY;
+    const int64_t stride = (int64_t)gridDim.x * 4;
+    // the loop bound is the same for every wave of the block, so the block
+    // barriers below are reached by all of its threads
+    for (int64_t i0 = (int64_t)blockIdx.x * 4; i0 < p.count; i0 += stride) {
+        const int64_t i = i0 + wv;
+        const bool active = i < p.count;
+        for (int w = lane; w < cw; w += 64) words[wv][w] = 0u;
+        __syncthreads();
+        float gg = 0.0f;
+        if (active) {
+            for (int c = lane; c < p.d; c += 64) {
+                const float y = p.Y[i * p.d + c];
+                uint32_t code = 0;
+                float yh = lv[0];
+                for (int k = 0; k < 15; ++k) {
+                    const bool ge = y >= th[k];
+                    code = ge ? (uint32_t)(k + 1) : code;
+                    yh = ge ? lv[k + 1] : yh;
+                }
+                const float e = y - yh;
+                p.U[i * p.d + c] = e;
+                gg = fmaf(e, e, gg);
+                const int bp = p.bits * c;
+                atomicOr(&words[wv][bp >> 5], code << (bp & 31));
+                if ((bp & 31) + p.bits > 32) atomicOr(&words[wv][(bp >> 5) + 1], code >> (32 - (bp & 31)));
+            }
+        }
+        gg = wave_sum(gg);
+        __syncthreads();
+        if (active) {
+            int64_t off;
+            int tok;
+            const int64_t n = dense_record(p, p.start + i, &off, &tok);
+            for (int w = lane; w < cw; w += 64) p.codes[n * cw + w] = words[wv][w];
+            if (lane == 0 && p.m > 0) p.rnorm[n] = sqrtf(gg);
+        }
+        __syncthreads();
+    }
+}
+
+// one wave per vector: sign bits of Z
+__global__ __launch_bounds__(256) void dense_signs_kernel(DenseK p) {
+    const int lane = threadIdx.x & 63;
+    const int64_t stride = (int64_t)gridDim.x * 4;
+    const int mw = p.m / 32;
+    for (int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); i < p.count; i += stride) {
+        int64_t off;
+        int tok;
+        const int64_t n = dense_record(p, p.start + i, &off, &tok);
+        for (int c = 0; c < p.m; c += 64) {
+            const int l = c + lane;
+            const bool bit = l < p.m && p.Z[i * p.m + l] >= 0.0f;
+            const uint64_t ball = __ballot(bit);
+            if (lane == 0) p.signs[n * mw + c / 32] = (uint32_t)ball;
+            if (lane == 32 && c / 32 + 1 < mw) p.signs[n * mw + c / 32 + 1] = (uint32_t)(ball >> 32);
+        }
+    }
+}
+
+int64_t dense_chunk(int64_t nvec) { return nvec < 65536 ? nvec : 65536; }
+
+using EncFn = void (*)(EncK);
+
+template <int D, int BITS, int M>
+EncFn pick_dtype(bool bf16) {
+    return bf16 ? encode_rht_kernel<D, BITS, M, true> : encode_rht_kernel<D, BITS, M, false>;
+}
+
+template <int D, int BITS>
+EncFn pick_m(int m, bool bf16) {
+    if (m == 0) return pick_dtype<D, BITS, 0>(bf16);
+    if (m == D / 2) return pick_dtype<D, BITS, D / 2>(bf16);
+    if (m == D) return pick_dtype<D, BITS, D>(bf16);
+    return nullptr;
+}
+
+template <int D>
+EncFn pick_bits(int bits, int m, bool bf16) {
+    switch (bits) {
+        case 1: return pick_m<D, 1>(m, bf16);
+        case 2: return pick_m<D, 2>(m, bf16);
+        case 3: return pick_m<D, 3>(m, bf16);
+        case 4: return pick_m<D, 4>(m, bf16);
+    }
+    return nullptr;
+}
+
+EncFn pick_encode(int d, int bits, int m, bool bf16) {
+    if (d == 64) return pick_bits<64>(bits, m, bf16);
+    if (d == 128) return pick_bits<128>(bits, m, bf16);
+    return nullptr;
+}
+
+int g_num_cus = 0;
+
+}  // namespace
+
+size_t encode_workspace_bytes(const tq_codebook* cb, int64_t n_vectors) {
+    if (!cb->dense) return 0;
+    const int64_t c = dense_chunk(n_vectors);
+    return (size_t)c * (2 * (size_t)cb->spec.d + (size_t)cb->spec.m) * sizeof(float);
+}
+
+hipError_t launch_encode(const tq_codebook* cb, const EncodeArgs& a, hipStream_t stream) {
+    const int d = cb->spec.d, bits = cb->spec.bits, m = cb->spec.m;
+    if (!g_num_cus) {
+        int dev = 0;
+        hipDeviceProp_t prop;
+        if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) return hipErrorUnknown;
+        g_num_cus = prop.multiProcessorCount;
+    }
+    if (!cb->dense) {
+        EncFn fn = pick_encode(d, bits, m, a.bf16 != 0);
+        if (!fn) return hipErrorInvalidValue;
+        EncK p{};
+        p.x = a.x;
+        p.s_seq = a.s_seq;
+        p.s_tok = a.s_tok;
+        p.s_head = a.s_head;
+        p.n_seq = a.n_seq;
+        p.n_tok = a.n_tok;
+        p.h_kv = a.h_kv;
+        p.tok_offset = a.tok_offset;
+        p.L_cap = a.L_cap;
+        p.tok_blocks = (a.n_tok + 31) / 32;
+        p.n_tiles = (int64_t)a.n_seq * p.tok_blocks * a.h_kv;
+        p.rope_cos = a.rope_cos;
+        p.rope_sin = a.rope_sin;
+        p.sigma = cb->dev.sigma;
+        p.levels = cb->dev.levels;
+        p.thresholds = cb->dev.thresholds;
+        p.sketch_mfma = cb->dev.sketch_mfma;
+        p.norm = a.out.norm;
+        p.rnorm = a.out.rnorm;
+        p.codes = a.out.codes;
+        p.signs = a.out.signs;
+        const int64_t blocks_needed = (p.n_tiles + 3) / 4;
+        const int64_t cap = (int64_t)g_num_cus * 8;
+        const int grid = (int)(blocks_needed < cap ? blocks_needed : cap);
+        hipLaunchKernelGGL(fn, dim3(grid), dim3(256), 0, stream, p);
+        return hipGetLastError();
+    }
+    // dense form, chunk by chunk
+    const int64_t nvec = (int64_t)a.n_seq * a.n_tok * a.h_kv;
+    const int64_t chunk = dense_chunk(nvec);
+    float* U = static_cast<float*>(a.ws);
+    float* Y = U + chunk * d;
+    float* Z = Y + chunk * d;
+    for (int64_t start = 0; start < nvec; start += chunk) {
+        const int64_t cnt = (nvec - start) < chunk ? (nvec - start) : chunk;
+        DenseK p{};
+        p.x = a.x;
+        p.s_seq = a.s_seq;
+        p.s_tok = a.s_tok;
+        p.s_head = a.s_head;
+        p.n_tok = a.n_tok;
+        p.h_kv = a.h_kv;
+        p.tok_offset = a.tok_offset;
+        p.L_cap = a.L_cap;
+        p.d = d;
+        p.m = m;
+        p.bits = bits;
+        p.start = start;
+        p.count = cnt;
+        p.bf16 = a.bf16;
+        p.rope_cos = a.rope_cos;
+        p.rope_sin = a.rope_sin;
+        p.levels = cb->dev.levels;
+        p.thresholds = cb->dev.thresholds;
+        p.U = U;
+        p.Y = Y;
+        p.Z = Z;
+        p.norm = a.out.norm;
+        p.rnorm = a.out.rnorm;
+        p.codes = a.out.codes;
+        p.signs = a.out.signs;
+        const int grid = (int)((cnt + 3) / 4 < (int64_t)g_num_cus * 8 ? (cnt + 3) / 4 : (int64_t)g_num_cus * 8);
+        hipLaunchKernelGGL(dense_prep_kernel, dim3(grid), dim3(256), 0, stream, p);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        e = launch_gemm_nt(U, d, cb->dev.rot, d, Y, d, (int)cnt, d, d, stream);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(dense_quant_kernel, dim3(grid), dim3(256), 0, stream, p);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        if (m > 0) {
+            e = launch_gemm_nt(U, d, cb->dev.sketch, d, Z, m, (int)cnt, m, d, stream);
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL(dense_signs_kernel, dim3(grid), dim3(256), 0, stream, p);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+    }
+    return hipSuccess;
+}
+
+}  // namespace tq

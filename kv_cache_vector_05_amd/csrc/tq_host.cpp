@@ -1,0 +1,635 @@
+// Host side of libtq: argument validation, codebook table construction
+// (Lloyd-Max solver, seeded draws, Haar rotation, RoPE table) and the C ABI
+// entry points, which validate and then enqueue the HIP kernels.
+//
+// Table construction follows the FibQuant summary, sections 1 and 2.1
+// (normalise, shared Haar rotation, scalar Lloyd-Max table for the
+// spherical-Beta marginal; one offline table for all inputs) and the
+// iaemfoco post, "TurboQuant: Uma Nova Abordagem" (randomized Hadamard
+// rotation; Johnson-Lindenstrauss sketch).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "tq_internal.h"
+
+namespace tq {
+
+static thread_local std::string g_last_error;
+
+tq_status fail(tq_status code, const std::string& msg) {
+    g_last_error = msg;
+    return code;
+}
+
+tq_status hip_fail(hipError_t e, const char* what) {
+    g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+    return TQ_EHIP;
+}
+
+static bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+tq_status check_spec(const tq_spec& s, bool* dense) {
+    if (s.bits < 1 || s.bits > 4) return fail(TQ_EINVAL, "bits must be 1..4");
+    if (s.d < 3 || s.d > 4096) return fail(TQ_EINVAL, "d must be 3..4096");
+    if ((s.bits * s.d) % 32) return fail(TQ_EINVAL, "bits*d must be a multiple of 32");
+    if (s.m < 0 || s.m > 4096 || (s.m % 32)) return fail(TQ_EINVAL, "m must be 0 or a multiple of 32 up to 4096");
+    bool dn;
+    if (s.rotation == TQ_ROT_AUTO) dn = !is_pow2(s.d);
+    else if (s.rotation == TQ_ROT_HADAMARD) dn = false;
+    else if (s.rotation == TQ_ROT_DENSE) dn = true;
+    else return fail(TQ_EINVAL, "unknown rotation");
+    if (!dn) {
+        if (!is_pow2(s.d)) return fail(TQ_EINVAL, "Hadamard rotation needs a power-of-two d");
+        if (s.d != 64 && s.d != 128) return fail(TQ_EUNSUPPORTED, "Hadamard kernels exist for d = 64 and 128");
+        if (s.m != 0 && s.m != s.d / 2 && s.m != s.d)
+            return fail(TQ_EUNSUPPORTED, "Hadamard kernels exist for m = 0, d/2 and d");
+    } else {
+        if (s.d % 64) return fail(TQ_EUNSUPPORTED, "dense kernels need d a multiple of 64");
+    }
+    if (dense) *dense = dn;
+    return TQ_OK;
+}
+
+// ------------------------------------------------------------------------
+// Lloyd-Max table for one coordinate of a uniform point on S^{d-1}.
+// Density f(y) proportional to (1 - y^2)^((d-3)/2).  With y = sin(theta),
+// f(y) dy is proportional to cos(theta)^(d-2) dtheta, smooth on
+// [-pi/2, pi/2] for every d >= 3, so composite Gauss-Legendre quadrature in
+// theta converges fast even where the y-density has an endpoint
+// singularity (small d).  The normalising constant cancels in the level
+// (a ratio of two integrals), so it is never formed.
+// ------------------------------------------------------------------------
+namespace {
+
+struct GaussLegendre {
+    std::vector<double> x, w;  // nodes and weights on [-1, 1]
+    explicit GaussLegendre(int n) : x(n), w(n) {
+        // Newton's method on P_n from the usual cosine starting points
+        auto legendre = [n](double z, double* dp) {
+            double p0 = 1.0, p1 = 0.0;
+            for (int k = 1; k <= n; ++k) {
+                const double p2 = p1;
+                p1 = p0;
+                p0 = ((2.0 * k - 1.0) * z * p1 - (k - 1.0) * p2) / k;
+            }
+            *dp = n * (z * p0 - p1) / (z * z - 1.0);
+            return p0;
+        };
+        for (int i = 0; i < n; ++i) {
+            double z = std::cos(M_PI * (i + 0.75) / (n + 0.5));
+            double dp = 0.0;
+            for (int it = 0; it < 100; ++it) {
+                const double pz = legendre(z, &dp);
+                const double dz = pz / dp;
+                z -= dz;
+                if (std::fabs(dz) < 1e-16) break;
+            }
+            legendre(z, &dp);
+            x[i] = z;
+            w[i] = 2.0 / ((1.0 - z * z) * dp * dp);
+        }
+    }
+};
+
+// (mass, first moment) of cos^(d-2) over [ta, tb] in theta (unnormalised).
+void cell_integrals(const GaussLegendre& gl, int d, double ta, double tb, double* mass,
+                    double* mom) {
+    const double width = 1.0 / std::sqrt((double)d);
+    // beyond ~60 widths the integrand is below exp(-1800): skip it
+    const double lim = std::min(M_PI / 2, 60.0 * width);
+    ta = std::max(ta, -lim);
+    tb = std::min(tb, lim);
+    *mass = 0.0;
+    *mom = 0.0;
+    if (tb <= ta) return;
+    const double h = std::min(0.05, 0.25 * width);
+    const int panels = std::max(1, (int)std::ceil((tb - ta) / h));
+    const double hp = (tb - ta) / panels;
+    for (int p = 0; p < panels; ++p) {
+        const double a = ta + p * hp, c = a + 0.5 * hp;
+        for (size_t k = 0; k < gl.x.size(); ++k) {
+            const double th = c + 0.5 * hp * gl.x[k];
+            const double ct = std::cos(th);
+            const double f = ct > 0 ? std::exp((d - 2) * std::log(ct)) : 0.0;
+            const double wk = 0.5 * hp * gl.w[k];
+            *mass += wk * f;
+            *mom += wk * f * std::sin(th);
+        }
+    }
+}
+
+}  // namespace
+
+void lloyd_max_table(int d, int bits, std::vector<double>* levels, std::vector<double>* thr) {
+    static const GaussLegendre gl(24);
+    const int K = 1 << bits, half = K / 2;
+    std::vector<double> t(K), tau(K - 1), tn(K);
+    // start: K evenly spread levels inside +-3 standard deviations
+    const double sd = 1.0 / std::sqrt((double)d);
+    for (int j = 0; j < K; ++j) t[j] = std::min(0.9, 3.0 * sd) * (2.0 * (j + 0.5) / K - 1.0);
+    double prev = INFINITY;
+    for (int it = 0; it < 2000000; ++it) {
+        for (int j = 0; j + 1 < K; ++j) tau[j] = 0.5 * (t[j] + t[j + 1]);
+        // upper-half cells [tau_{K/2-1} (= 0), ...), mirrored below (f is even)
+        for (int j = half; j < K; ++j) {
+            const double lo = tau[j - 1];
+            const double hi = (j + 1 < K) ? tau[j] : 1.0;
+            double mass, mom;
+            cell_integrals(gl, d, std::asin(std::max(-1.0, std::min(1.0, lo))),
+                           std::asin(std::max(-1.0, std::min(1.0, hi))), &mass, &mom);
+            tn[j] = mom / mass;
+            tn[K - 1 - j] = -tn[j];
+        }
+        double step = 0.0, big = 0.0;
+        for (int j = 0; j < K; ++j) {
+            step = std::max(step, std::fabs(tn[j] - t[j]));
+            big = std::max(big, std::fabs(tn[j]));
+        }
+        step /= big;
+        t = tn;
+        if (step <= 1e-14 || (step <= 1e-12 && step >= prev)) break;
+        prev = step;
+    }
+    for (int j = 0; j + 1 < K; ++j) tau[j] = 0.5 * (t[j] + t[j + 1]);
+    *levels = t;
+    *thr = tau;
+}
+
+// ------------------------------------------------------------------------
+// Seeded draws: SplitMix64 (Steele, Lea and Flood, OOPSLA 2014) streams,
+// Box-Muller (1958) Gaussians.  Purpose p (1 signs, 2 rotation, 3 sketch)
+// starts from output p of a SplitMix64 seeded with the codebook seed.
+// ------------------------------------------------------------------------
+namespace {
+constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
+inline uint64_t mix64(uint64_t z) {
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+inline uint64_t stream_start(uint64_t seed, int purpose) {
+    return mix64(seed + (uint64_t)purpose * kGamma);
+}
+}  // namespace
+
+void splitmix_gaussians(uint64_t seed, int purpose, size_t n, double* out) {
+    uint64_t s = stream_start(seed, purpose);
+    for (size_t i = 0; i < n; i += 2) {
+        s += kGamma;
+        const double u1 = (double)(mix64(s) >> 11) * 0x1.0p-53;
+        s += kGamma;
+        const double u2 = (double)(mix64(s) >> 11) * 0x1.0p-53;
+        const double r = std::sqrt(-2.0 * std::log(1.0 - u1));
+        const double a = 2.0 * M_PI * u2;
+        out[i] = r * std::cos(a);
+        if (i + 1 < n) out[i + 1] = r * std::sin(a);
+    }
+}
+
+void splitmix_signs(uint64_t seed, size_t n, int8_t* out) {
+    uint64_t s = stream_start(seed, 1);
+    for (size_t i = 0; i < n; ++i) {
+        s += kGamma;
+        out[i] = (mix64(s) >> 63) ? -1 : 1;
+    }
+}
+
+// ------------------------------------------------------------------------
+// Haar rotation: Householder QR of a d x d Gaussian matrix G = Q R, with the
+// columns of Q multiplied by sign(R_jj) so that diag(R) > 0.  Works on a
+// column-major copy; returns Q row-major.
+// ------------------------------------------------------------------------
+void haar_from_gaussians(int d, const double* g, std::vector<double>* qout) {
+    const size_t n = (size_t)d;
+    std::vector<double> a(n * n);  // column-major: a[j*n + i] = G[i][j]
+    for (size_t i = 0; i < n; ++i)
+        for (size_t j = 0; j < n; ++j) a[j * n + i] = g[i * n + j];
+    std::vector<double> vs(n * n, 0.0);  // Householder vectors, column k in vs[k*n ...]
+    std::vector<double> rdiag(n);
+    for (size_t k = 0; k < n; ++k) {
+        double* col = &a[k * n];
+        double norm2 = 0.0;
+        for (size_t i = k; i < n; ++i) norm2 += col[i] * col[i];
+        const double nrm = std::sqrt(norm2);
+        const double alpha = col[k] >= 0 ? -nrm : nrm;
+        double* v = &vs[k * n];
+        for (size_t i = k; i < n; ++i) v[i] = col[i];
+        v[k] -= alpha;
+        double vn2 = 0.0;
+        for (size_t i = k; i < n; ++i) vn2 += v[i] * v[i];
+        rdiag[k] = alpha;
+        if (vn2 == 0.0) continue;
+        const double inv = 1.0 / std::sqrt(vn2);
+        for (size_t i = k; i < n; ++i) v[i] *= inv;
+        for (size_t j = k; j < n; ++j) {
+            double* cj = &a[j * n];
+            double dot = 0.0;
+            for (size_t i = k; i < n; ++i) dot += v[i] * cj[i];
+            dot *= 2.0;
+            for (size_t i = k; i < n; ++i) cj[i] -= dot * v[i];
+        }
+    }
+    // Q = H_0 H_1 ... H_{n-1} I, accumulated from the right (column-major).
+    std::vector<double> q(n * n, 0.0);
+    for (size_t i = 0; i < n; ++i) q[i * n + i] = 1.0;
+    for (size_t kk = n; kk-- > 0;) {
+        const double* v = &vs[kk * n];
+        for (size_t j = kk; j < n; ++j) {
+            double* cj = &q[j * n];
+            double dot = 0.0;
+            for (size_t i = kk; i < n; ++i) dot += v[i] * cj[i];
+            dot *= 2.0;
+            if (dot != 0.0)
+                for (size_t i = kk; i < n; ++i) cj[i] -= dot * v[i];
+        }
+    }
+    qout->assign(n * n, 0.0);
+    for (size_t i = 0; i < n; ++i)
+        for (size_t j = 0; j < n; ++j) {
+            const double sgn = rdiag[j] < 0 ? -1.0 : 1.0;  // R_jj = rdiag[j]
+            (*qout)[i * n + j] = q[j * n + i] * sgn;
+        }
+}
+
+// Builds every host table of a codebook.
+static tq_status build_tables(const tq_spec& s, const tq_draws* dr, bool dense,
+                              std::vector<float>* levels, std::vector<float>* thr,
+                              std::vector<float>* rot, std::vector<float>* sk) {
+    std::vector<double> t, tau;
+    lloyd_max_table(s.d, s.bits, &t, &tau);
+    levels->assign(t.begin(), t.end());
+    thr->assign(tau.begin(), tau.end());
+    const size_t d = (size_t)s.d;
+    if (dense) {
+        std::vector<double> g;
+        const double* gp = dr ? dr->rot_gauss : nullptr;
+        if (!gp) {
+            g.resize(d * d);
+            splitmix_gaussians(s.seed, 2, d * d, g.data());
+            gp = g.data();
+        }
+        std::vector<double> q;
+        haar_from_gaussians(s.d, gp, &q);
+        rot->assign(q.begin(), q.end());
+    } else {
+        std::vector<int8_t> sg(d);
+        if (dr && dr->sigma) {
+            for (size_t i = 0; i < d; ++i) {
+                if (dr->sigma[i] != 1 && dr->sigma[i] != -1) return fail(TQ_EINVAL, "sigma entries must be +1 or -1");
+                sg[i] = dr->sigma[i];
+            }
+        } else {
+            splitmix_signs(s.seed, d, sg.data());
+        }
+        rot->resize(d);
+        for (size_t i = 0; i < d; ++i) (*rot)[i] = (float)sg[i];
+    }
+    const size_t md = (size_t)s.m * d;
+    sk->resize(md);
+    if (md) {
+        if (dr && dr->sketch) {
+            std::memcpy(sk->data(), dr->sketch, md * sizeof(float));
+        } else {
+            std::vector<double> g(md);
+            splitmix_gaussians(s.seed, 3, md, g.data());
+            for (size_t i = 0; i < md; ++i) (*sk)[i] = (float)g[i];
+        }
+    }
+    return TQ_OK;
+}
+
+}  // namespace tq
+
+using namespace tq;
+
+extern "C" {
+
+const char* tq_last_error(void) { return g_last_error.c_str(); }
+
+const char* tq_version(void) { return "libtq 0.1 (gfx950)"; }
+
+int64_t tq_plane_words(const tq_spec* spec, int32_t plane) {
+    if (!spec || check_spec(*spec, nullptr) != TQ_OK) return -1;
+    if (plane == 0) return (int64_t)spec->bits * spec->d / 32;
+    if (plane == 1) return spec->m / 32;
+    return -1;
+}
+
+tq_status tq_rope_table(double base, int32_t d, int32_t n_pos, float* cos_out, float* sin_out) {
+    if (!cos_out || !sin_out) return fail(TQ_EINVAL, "null output");
+    if (d <= 0 || (d & 1) || n_pos < 0 || !(base > 0)) return fail(TQ_EINVAL, "bad RoPE size or base");
+    const int half = d / 2;
+    std::vector<double> theta(half);
+    for (int i = 0; i < half; ++i) theta[i] = std::pow(base, -2.0 * i / d);
+    for (int64_t p = 0; p < n_pos; ++p)
+        for (int i = 0; i < half; ++i) {
+            const double ang = (double)p * theta[i];
+            cos_out[p * half + i] = (float)std::cos(ang);
+            sin_out[p * half + i] = (float)std::sin(ang);
+        }
+    return TQ_OK;
+}
+
+tq_status tq_codebook_tables(const tq_spec* spec, const tq_draws* draws, float* levels,
+                             float* thresholds, float* rotation, float* sketch) {
+    if (!spec) return fail(TQ_EINVAL, "null spec");
+    bool dense;
+    tq_status st = check_spec(*spec, &dense);
+    if (st) return st;
+    std::vector<float> lv, th, rot, sk;
+    st = build_tables(*spec, draws, dense, &lv, &th, &rot, &sk);
+    if (st) return st;
+    if (levels) std::memcpy(levels, lv.data(), lv.size() * sizeof(float));
+    if (thresholds) std::memcpy(thresholds, th.data(), th.size() * sizeof(float));
+    if (rotation) std::memcpy(rotation, rot.data(), rot.size() * sizeof(float));
+    if (sketch && !sk.empty()) std::memcpy(sketch, sk.data(), sk.size() * sizeof(float));
+    return TQ_OK;
+}
+
+tq_status tq_codebook_init(const tq_spec* spec, const tq_draws* draws, void* stream,
+                           tq_codebook** out) {
+    if (!out) return fail(TQ_EINVAL, "null out");
+    *out = nullptr;
+    if (!spec) return fail(TQ_EINVAL, "null spec");
+    bool dense;
+    tq_status st = check_spec(*spec, &dense);
+    if (st) return st;
+    tq_codebook* cb = new tq_codebook();
+    cb->spec = *spec;
+    cb->dense = dense;
+    cb->K = 1 << spec->bits;
+    st = build_tables(*spec, draws, dense, &cb->levels, &cb->thresholds, &cb->rotation, &cb->sketch);
+    if (st) {
+        delete cb;
+        return st;
+    }
+    const int d = spec->d, m = spec->m;
+    // the encode kernel's sketch operand order (Hadamard form): for row block
+    // rb, step p and lane l: S[rb*32 + l%32][(l/32)*(d/2) + p]
+    std::vector<float> sk_mfma((size_t)m * d);
+    if (!dense && m) {
+        const int half = d / 2;
+        for (int rb = 0; rb < m / 32; ++rb)
+            for (int p = 0; p < half; ++p)
+                for (int l = 0; l < 64; ++l)
+                    sk_mfma[((size_t)rb * half + p) * 64 + l] =
+                        cb->sketch[(size_t)(rb * 32 + (l & 31)) * d + (l >> 5) * half + p];
+    }
+    // one device block: levels[16] | thresholds[16] | sigma[d] or rot[d*d] | sketch | sketch_mfma
+    const size_t n_lv = 16, n_th = 16;
+    const size_t n_rot = dense ? (size_t)d * d : (size_t)d;
+    const size_t n_sk = (size_t)m * d;
+    const size_t total = n_lv + n_th + n_rot + 2 * n_sk;
+    std::vector<float> host(total, 0.0f);
+    std::memcpy(host.data(), cb->levels.data(), cb->levels.size() * 4);
+    std::memcpy(host.data() + n_lv, cb->thresholds.data(), cb->thresholds.size() * 4);
+    std::memcpy(host.data() + n_lv + n_th, cb->rotation.data(), n_rot * 4);
+    if (n_sk) {
+        std::memcpy(host.data() + n_lv + n_th + n_rot, cb->sketch.data(), n_sk * 4);
+        std::memcpy(host.data() + n_lv + n_th + n_rot + n_sk, sk_mfma.data(), n_sk * 4);
+    }
+    if (const char* f = std::getenv("TQ_TEST_FAIL_ALLOC"); f && std::atoi(f) == 1) {
+        delete cb;
+        return fail(TQ_ENOMEM, "allocation failure forced by TQ_TEST_FAIL_ALLOC");
+    }
+    hipError_t e = hipGetDevice(&cb->device);
+    if (e != hipSuccess) {
+        delete cb;
+        return hip_fail(e, "hipGetDevice");
+    }
+    e = hipMalloc(&cb->block, total * sizeof(float));
+    if (e != hipSuccess) {
+        delete cb;
+        (void)hipGetLastError();
+        return e == hipErrorOutOfMemory ? fail(TQ_ENOMEM, "hipMalloc of codebook tables failed")
+                                        : hip_fail(e, "hipMalloc");
+    }
+    float* base = (float*)cb->block;
+    cb->dev.levels = base;
+    cb->dev.thresholds = base + n_lv;
+    if (dense) cb->dev.rot = base + n_lv + n_th;
+    else cb->dev.sigma = base + n_lv + n_th;
+    if (n_sk) {
+        cb->dev.sketch = base + n_lv + n_th + n_rot;
+        cb->dev.sketch_mfma = base + n_lv + n_th + n_rot + n_sk;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    e = hipMemcpyAsync(cb->block, host.data(), total * sizeof(float), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);  // host staging buffer is local
+    if (e != hipSuccess) {
+        (void)hipFree(cb->block);
+        delete cb;
+        return hip_fail(e, "uploading codebook tables");
+    }
+    *out = cb;
+    return TQ_OK;
+}
+
+tq_status tq_codebook_destroy(tq_codebook* cb) {
+    if (!cb) return TQ_OK;
+    hipError_t e = hipSuccess;
+    if (cb->block) e = hipFree(cb->block);
+    delete cb;
+    return e == hipSuccess ? TQ_OK : hip_fail(e, "hipFree");
+}
+
+tq_status tq_codebook_get_spec(const tq_codebook* cb, tq_spec* out) {
+    if (!cb || !out) return fail(TQ_EINVAL, "null argument");
+    *out = cb->spec;
+    return TQ_OK;
+}
+
+tq_status tq_codebook_export(const tq_codebook* cb, float* levels, float* thresholds,
+                             float* rotation, float* sketch) {
+    if (!cb) return fail(TQ_EINVAL, "null codebook");
+    if (levels) std::memcpy(levels, cb->levels.data(), cb->levels.size() * 4);
+    if (thresholds) std::memcpy(thresholds, cb->thresholds.data(), cb->thresholds.size() * 4);
+    if (rotation) std::memcpy(rotation, cb->rotation.data(), cb->rotation.size() * 4);
+    if (sketch && !cb->sketch.empty()) std::memcpy(sketch, cb->sketch.data(), cb->sketch.size() * 4);
+    return TQ_OK;
+}
+
+static tq_status check_packed(const tq_codebook* cb, const tq_packed* p, int64_t need,
+                              const char* what) {
+    if (!p) return fail(TQ_EINVAL, std::string("null packed planes: ") + what);
+    if (!p->norm || !p->codes) return fail(TQ_EINVAL, std::string("null norm/codes plane: ") + what);
+    if (cb->spec.m && (!p->rnorm || !p->signs))
+        return fail(TQ_EINVAL, std::string("null rnorm/signs plane with m > 0: ") + what);
+    if (p->n < need) return fail(TQ_EINVAL, std::string("packed capacity too small: ") + what);
+    return TQ_OK;
+}
+
+tq_status tq_encode_kv(const tq_codebook* ck, const tq_codebook* cv, const void* k, const void* v,
+                       int32_t dtype, int32_t n_seq, int32_t n_tok, int32_t h_kv,
+                       const int64_t* k_stride, const int64_t* v_stride, int32_t tok_offset,
+                       int32_t L_cap, const float* rope_cos, const float* rope_sin,
+                       int32_t rope_npos, const tq_packed* kout, const tq_packed* vout, void* ws,
+                       size_t ws_bytes, void* stream) {
+    if (dtype != TQ_F32 && dtype != TQ_BF16) return fail(TQ_EINVAL, "dtype must be TQ_F32 or TQ_BF16");
+    if (n_seq < 0 || n_tok < 0 || h_kv < 0 || tok_offset < 0 || L_cap < 0)
+        return fail(TQ_EINVAL, "negative size");
+    if ((int64_t)tok_offset + n_tok > L_cap) return fail(TQ_EINVAL, "tok_offset + n_tok exceeds L_cap");
+    if (!k && !v) return fail(TQ_EINVAL, "neither k nor v given");
+    if ((rope_cos == nullptr) != (rope_sin == nullptr)) return fail(TQ_EINVAL, "give both RoPE tables or neither");
+    const int64_t nvec = (int64_t)n_seq * n_tok * h_kv;
+    const int64_t need = (int64_t)n_seq * h_kv * L_cap;
+    const int esz = dtype == TQ_F32 ? 4 : 2;
+    const int align = dtype == TQ_F32 ? 4 : 8;
+    struct Side { const tq_codebook* cb; const void* x; const int64_t* st; const tq_packed* o; bool rope; };
+    Side sides[2] = {{ck, k, k_stride, kout, rope_cos != nullptr}, {cv, v, v_stride, vout, false}};
+    for (auto& sd : sides) {
+        if (!sd.x) continue;
+        if (!sd.cb) return fail(TQ_EINVAL, "tensor given without a codebook");
+        if (!sd.st) return fail(TQ_EINVAL, "null strides");
+        for (int i = 0; i < 3; ++i)
+            if (sd.st[i] < 0 || sd.st[i] % align) return fail(TQ_EINVAL, "strides must be non-negative multiples of 16 bytes");
+        if (((uintptr_t)sd.x) % 16) return fail(TQ_EINVAL, "input must be 16-byte aligned");
+        tq_status st = check_packed(sd.cb, sd.o, need, sd.x == k ? "k" : "v");
+        if (st) return st;
+        if (sd.rope) {
+            if (rope_npos < tok_offset + n_tok) return fail(TQ_EINVAL, "RoPE table shorter than the last position");
+            if (sd.cb->spec.d % 2) return fail(TQ_EINVAL, "RoPE needs an even d");
+        }
+        if (sd.cb->dense && nvec > 0) {
+            const size_t wsn = encode_workspace_bytes(sd.cb, nvec);
+            if (!ws || ws_bytes < wsn) return fail(TQ_EINVAL, "workspace too small for the dense encoder");
+        }
+    }
+    (void)esz;
+    if (nvec == 0) return TQ_OK;
+    for (auto& sd : sides) {
+        if (!sd.x) continue;
+        EncodeArgs a{};
+        a.x = sd.x;
+        a.s_seq = sd.st[0];
+        a.s_tok = sd.st[1];
+        a.s_head = sd.st[2];
+        a.n_seq = n_seq;
+        a.n_tok = n_tok;
+        a.h_kv = h_kv;
+        a.tok_offset = tok_offset;
+        a.L_cap = L_cap;
+        a.bf16 = dtype == TQ_BF16;
+        a.rope_cos = sd.rope ? rope_cos : nullptr;
+        a.rope_sin = sd.rope ? rope_sin : nullptr;
+        a.out = *sd.o;
+        a.ws = ws;
+        a.ws_bytes = ws_bytes;
+        hipError_t e = launch_encode(sd.cb, a, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "encode launch");
+    }
+    return TQ_OK;
+}
+
+static tq_status check_attn(const tq_codebook* ck, const void* q, int32_t q_dtype, int32_t B,
+                            int32_t Hq, int32_t h_kv, int32_t L_cap, const int32_t* seq_len,
+                            const float* rope_cos, const float* rope_sin, int32_t rope_npos) {
+    if (!ck) return fail(TQ_EINVAL, "null key codebook");
+    if (!q || !seq_len) return fail(TQ_EINVAL, "null q or seq_len");
+    if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return fail(TQ_EINVAL, "q dtype must be TQ_F32 or TQ_BF16");
+    if (B < 0 || Hq < 0 || h_kv <= 0 || L_cap < 0) return fail(TQ_EINVAL, "bad sizes");
+    if (Hq % h_kv) return fail(TQ_EINVAL, "Hq must be a multiple of h_kv");
+    if ((rope_cos == nullptr) != (rope_sin == nullptr)) return fail(TQ_EINVAL, "give both RoPE tables or neither");
+    if (rope_cos && rope_npos <= L_cap) return fail(TQ_EINVAL, "RoPE table must cover position L_cap");
+    if (((uintptr_t)q) % 16) return fail(TQ_EINVAL, "q must be 16-byte aligned");
+    return TQ_OK;
+}
+
+tq_status tq_attn_logits(const tq_codebook* ck, const void* q, int32_t q_dtype, const tq_packed* k,
+                         int32_t B, int32_t Hq, int32_t h_kv, int32_t L_cap, const int32_t* seq_len,
+                         const float* rope_cos, const float* rope_sin, int32_t rope_npos,
+                         int32_t top_k, float* out, int32_t* topk_idx, void* ws, size_t ws_bytes,
+                         void* stream) {
+    tq_status st = check_attn(ck, q, q_dtype, B, Hq, h_kv, L_cap, seq_len, rope_cos, rope_sin, rope_npos);
+    if (st) return st;
+    if (top_k < 0 || top_k > 16) return fail(TQ_EINVAL, "top_k must be 0..16");
+    if (!out || (top_k && !topk_idx)) return fail(TQ_EINVAL, "null output");
+    st = check_packed(ck, k, (int64_t)B * h_kv * L_cap, "k");
+    if (st) return st;
+    if ((int64_t)B * Hq == 0 || (L_cap == 0 && top_k == 0)) return TQ_OK;
+    const size_t need = logits_workspace_bytes(ck, B, Hq, h_kv, L_cap, top_k);
+    if (ws_bytes < need || (need && !ws)) return fail(TQ_EINVAL, "workspace too small");
+    AttnArgs a{};
+    a.q = q;
+    a.bf16 = q_dtype == TQ_BF16;
+    a.B = B;
+    a.Hq = Hq;
+    a.h_kv = h_kv;
+    a.L_cap = L_cap;
+    a.seq_len = seq_len;
+    a.rope_cos = rope_cos;
+    a.rope_sin = rope_sin;
+    a.top_k = top_k;
+    a.out = out;
+    a.topk_idx = topk_idx;
+    a.ws = ws;
+    a.ws_bytes = ws_bytes;
+    hipError_t e = launch_logits(ck, *k, a, (hipStream_t)stream);
+    return e == hipSuccess ? TQ_OK : hip_fail(e, "logits launch");
+}
+
+tq_status tq_attn_decode(const tq_codebook* ck, const tq_codebook* cv, const void* q, int32_t q_dtype,
+                         const tq_packed* k, const tq_packed* v, int32_t B, int32_t Hq, int32_t h_kv,
+                         int32_t L_cap, const int32_t* seq_len, const float* rope_cos,
+                         const float* rope_sin, int32_t rope_npos, float scale, float* out,
+                         void* ws, size_t ws_bytes, void* stream) {
+    tq_status st = check_attn(ck, q, q_dtype, B, Hq, h_kv, L_cap, seq_len, rope_cos, rope_sin, rope_npos);
+    if (st) return st;
+    if (!cv) return fail(TQ_EINVAL, "null value codebook");
+    if (!out) return fail(TQ_EINVAL, "null output");
+    if (!(scale >= 0.0f) || std::isinf(scale)) return fail(TQ_EINVAL, "scale must be finite and >= 0");
+    if (ck->spec.d != cv->spec.d) return fail(TQ_EINVAL, "key and value dimensions differ");
+    st = check_packed(ck, k, (int64_t)B * h_kv * L_cap, "k");
+    if (st) return st;
+    st = check_packed(cv, v, (int64_t)B * h_kv * L_cap, "v");
+    if (st) return st;
+    if ((int64_t)B * Hq == 0) return TQ_OK;
+    const size_t need = decode_workspace_bytes(ck, cv, B, Hq, h_kv, L_cap);
+    if (ws_bytes < need || (need && !ws)) return fail(TQ_EINVAL, "workspace too small");
+    AttnArgs a{};
+    a.q = q;
+    a.bf16 = q_dtype == TQ_BF16;
+    a.B = B;
+    a.Hq = Hq;
+    a.h_kv = h_kv;
+    a.L_cap = L_cap;
+    a.seq_len = seq_len;
+    a.rope_cos = rope_cos;
+    a.rope_sin = rope_sin;
+    a.scale = scale > 0 ? scale : 1.0f / std::sqrt((float)ck->spec.d);
+    a.out = out;
+    a.ws = ws;
+    a.ws_bytes = ws_bytes;
+    hipError_t e = launch_decode(ck, cv, *k, *v, a, (hipStream_t)stream);
+    return e == hipSuccess ? TQ_OK : hip_fail(e, "decode launch");
+}
+
+size_t tq_workspace_bytes(const tq_codebook* ck, const tq_codebook* cv, int32_t op, int64_t B,
+                          int32_t Hq, int32_t h_kv, int32_t L_cap, int32_t top_k) {
+    if (!ck || B < 0) return 0;
+    switch (op) {
+        case TQ_OP_ENCODE: {
+            size_t a = encode_workspace_bytes(ck, B);
+            size_t b = cv ? encode_workspace_bytes(cv, B) : 0;
+            return std::max(a, b);
+        }
+        case TQ_OP_LOGITS:
+            if (h_kv <= 0 || Hq < 0 || L_cap < 0) return 0;
+            return logits_workspace_bytes(ck, B, Hq, h_kv, L_cap, top_k);
+        case TQ_OP_DECODE:
+            if (!cv || h_kv <= 0 || Hq < 0 || L_cap < 0) return 0;
+            return decode_workspace_bytes(ck, cv, B, Hq, h_kv, L_cap);
+        default:
+            return 0;
+    }
+}
+
+}  // extern "C"

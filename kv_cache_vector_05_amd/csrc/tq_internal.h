@@ -1,0 +1,94 @@
+// Internal declarations shared by the host side of libtq (argument checks,
+// table construction, launch orchestration) and the HIP kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/tq.h"
+
+namespace tq {
+
+constexpr int kMaxLevels = 16;  // 2^bits for bits <= 4
+
+struct DeviceTables {
+    float* levels = nullptr;      // [16]   float32 Lloyd-Max levels (first K used)
+    float* thresholds = nullptr;  // [16]   float32 thresholds (first K-1 used)
+    float* sigma = nullptr;       // [d]    Hadamard signs as +-1.0f
+    float* rot = nullptr;         // [d*d]  dense Pi, row-major (y = Pi u)
+    float* sketch = nullptr;      // [m*d]  S, row-major
+    float* sketch_mfma = nullptr; // [m*d]  S in the encode kernel's MFMA operand order
+};
+
+}  // namespace tq
+
+struct tq_codebook {
+    tq_spec spec;
+    bool dense;
+    int K;
+    int device;
+    std::vector<float> levels, thresholds, rotation, sketch;  // host mirrors
+    void* block = nullptr;                                    // one device allocation
+    tq::DeviceTables dev;
+};
+
+namespace tq {
+
+// ---- error reporting (thread-local message, see tq_last_error) ----
+tq_status fail(tq_status code, const std::string& msg);
+tq_status hip_fail(hipError_t e, const char* what);
+
+// ---- host math (tq_host.cpp) ----
+tq_status check_spec(const tq_spec& s, bool* dense);
+void lloyd_max_table(int d, int bits, std::vector<double>* levels, std::vector<double>* thr);
+void splitmix_gaussians(uint64_t seed, int purpose, size_t n, double* out);
+void splitmix_signs(uint64_t seed, size_t n, int8_t* out);
+void haar_from_gaussians(int d, const double* g, std::vector<double>* q);  // row-major
+
+// ---- kernel launchers (tq_encode.hip, tq_attn.hip, tq_gemm.hip) ----
+struct EncodeArgs {
+    const void* x;
+    int64_t s_seq, s_tok, s_head;
+    int32_t n_seq, n_tok, h_kv, tok_offset, L_cap;
+    int32_t bf16;
+    const float* rope_cos;  // nullptr: no RoPE
+    const float* rope_sin;
+    tq_packed out;
+    void* ws;  // dense form only
+    size_t ws_bytes;
+};
+hipError_t launch_encode(const tq_codebook* cb, const EncodeArgs& a, hipStream_t stream);
+size_t encode_workspace_bytes(const tq_codebook* cb, int64_t n_vectors);
+
+struct AttnArgs {
+    const void* q;
+    int32_t bf16;
+    int32_t B, Hq, h_kv, L_cap;
+    const int32_t* seq_len;
+    const float* rope_cos;
+    const float* rope_sin;
+    float scale;
+    int32_t top_k;
+    float* out;
+    int32_t* topk_idx;
+    void* ws;
+    size_t ws_bytes;
+};
+hipError_t launch_logits(const tq_codebook* ck, const tq_packed& k, const AttnArgs& a,
+                         hipStream_t stream);
+hipError_t launch_decode(const tq_codebook* ck, const tq_codebook* cv, const tq_packed& k,
+                         const tq_packed& v, const AttnArgs& a, hipStream_t stream);
+size_t logits_workspace_bytes(const tq_codebook* ck, int64_t B, int Hq, int h_kv, int L_cap,
+                              int top_k);
+size_t decode_workspace_bytes(const tq_codebook* ck, const tq_codebook* cv, int64_t B, int Hq,
+                              int h_kv, int L_cap);
+
+// C[M][N] = A[M][K] * B[N][K]^T (+ per-column scale if col_scale != nullptr),
+// fp32, row-major with leading dimensions lda/ldb/ldc (elements).
+hipError_t launch_gemm_nt(const float* A, int64_t lda, const float* B, int64_t ldb, float* C,
+                          int64_t ldc, int M, int N, int K, hipStream_t stream);
+
+}  // namespace tq
