@@ -1,0 +1,325 @@
+"""Benchmark of the KV codec's hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama8b]
+
+A step is one pass of the whole hot path over one batch of synthetic input
+that is already resident in HBM: encode K and V into packed records, score
+every cached key for every query head (attention logits), and run the fused
+decode (softmax times values).  The default workload is one
+Llama-3.1-8B-shaped layer: batch 8, 32 query heads over 8 KV heads, head dim
+128, context 32768, bf16 K/V with one percent of channels scaled x100, RoPE
+base 5e5, 3-bit Lloyd-Max codes plus a 64-row QJL sketch.
+
+Printed: one JSON line.  `value` is whole-step key throughput (cached keys
+encoded, scored and attended per second); per-kernel times come from HIP
+events on the launch stream inside the timed region, and `roofline` relates
+the dominant kernel's algorithmic bytes per launch to its measured duration.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode attn-logit keys/sec + % of HBM peak; KV encode tokens/sec (1 MI355X)"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama8b", choices=["llama8b", "llama70b", "esm650m", "vsearch", "tiny"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=0, help="keys in the oracle's sample (0: default)")
+    return ap.parse_args()
+
+
+class Timer:
+    """HIP events on the launch stream around individual API calls."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.spans = {}
+
+    def call(self, name, fn):
+        t = self.torch
+        s = t.cuda.Event(enable_timing=True)
+        e = t.cuda.Event(enable_timing=True)
+        stream = t.cuda.current_stream()
+        s.record(stream)
+        fn()
+        e.record(stream)
+        self.spans.setdefault(name, []).append((s, e))
+
+    def mean_ms(self, name):
+        v = [s.elapsed_time(e) for s, e in self.spans[name]]
+        return float(np.mean(v)), len(v)
+
+
+def bf16_dev(torch, bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+# ------------------------------------------------------------ llama-shaped
+def setup_llama(torch, tq, synth, kind):
+    if kind == "llama8b":
+        B, Hq, H, L, d, bits, m, rope_base = 8, 32, 8, 32768, 128, 3, 64, 5e5
+    else:
+        B, Hq, H, L, d, bits, m, rope_base = 1, 64, 8, 131072, 128, 3, 128, 0.0
+    K, V = synth.llama_kv_inputs(kind, seed=0, batch=B, ctx=L, hkv=H, d=d)
+    Q = synth.llama_q_inputs(seed=100, batch=B, hq=Hq, d=d)
+    st = {"B": B, "Hq": Hq, "H": H, "L": L, "d": d, "bits": bits, "m": m, "rope_base": rope_base}
+    st["K"], st["V"], st["Q"] = bf16_dev(torch, K), bf16_dev(torch, V), bf16_dev(torch, Q)
+    st["host"] = (K, V, Q)
+    st["ck"] = tq.Codebook(d, bits, m, "hadamard", seed=synth.K_SEED)
+    st["cv"] = tq.Codebook(d, bits, m, "hadamard", seed=synth.V_SEED)
+    st["kp"] = tq.Packed(st["ck"], B * H * L)
+    st["vp"] = tq.Packed(st["cv"], B * H * L)
+    st["rope"] = tq.rope_table(rope_base, d, L + 1) if rope_base else None
+    st["sl"] = torch.full((B,), L, dtype=torch.int32, device="cuda")
+    st["logits"] = torch.empty((B, Hq, L), dtype=torch.float32, device="cuda")
+    st["out"] = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    st["ws_l"] = torch.empty(max(1, tq.workspace_bytes(st["ck"], None, tq.TQ_OP_LOGITS, B, Hq, H, L, 0)),
+                             dtype=torch.uint8, device="cuda")
+    st["ws_d"] = torch.empty(max(1, tq.workspace_bytes(st["ck"], st["cv"], tq.TQ_OP_DECODE, B, Hq, H, L, 0)),
+                             dtype=torch.uint8, device="cuda")
+    return st
+
+
+def step_llama(st, tq, timer):
+    timer.call("encode_k", lambda: tq.encode_kv(st["ck"], None, st["K"], None, st["kp"], None, L_cap=st["L"],
+                                               rope=st["rope"]))
+    timer.call("encode_v", lambda: tq.encode_kv(None, st["cv"], None, st["V"], None, st["vp"], L_cap=st["L"]))
+    timer.call("logits", lambda: tq.attn_logits(st["ck"], st["Q"], st["kp"], st["H"], st["L"], st["sl"],
+                                                rope=st["rope"], out=st["logits"], workspace=st["ws_l"]))
+    timer.call("decode", lambda: tq.attn_decode(st["ck"], st["cv"], st["Q"], st["kp"], st["vp"], st["H"], st["L"],
+                                                st["sl"], rope=st["rope"], out=st["out"], workspace=st["ws_d"]))
+
+
+def llama_report(st, timer, ms_step):
+    B, Hq, H, L, d, bits, m = (st[k] for k in ("B", "Hq", "H", "L", "d", "bits", "m"))
+    G = Hq // H
+    keys = B * H * L
+    rec = 4 + (4 if m else 0) + bits * d // 8 + m // 8
+    in_bytes = 2 * d  # bf16
+    enc_ms, n_enc = timer.mean_ms("encode_k")
+    encv_ms, _ = timer.mean_ms("encode_v")
+    log_ms, _ = timer.mean_ms("logits")
+    dec_ms, _ = timer.mean_ms("decode")
+    kern = {
+        "encode_k": {"ms": enc_ms, "launches": n_enc, "alg_bytes": keys * (in_bytes + rec),
+                     "unit": "vectors", "units": keys},
+        "encode_v": {"ms": encv_ms, "alg_bytes": keys * (in_bytes + rec), "units": keys},
+        "logits": {"ms": log_ms, "alg_bytes": keys * (rec + 4 * G), "units": keys},
+        "decode": {"ms": dec_ms, "alg_bytes": keys * 2 * rec, "units": keys},
+    }
+    for k in kern.values():
+        k["GBps"] = k["alg_bytes"] / (k["ms"] * 1e-3) / 1e9
+        k["hbm_frac"] = k["GBps"] / HBM_PEAK_GBS
+    dom = max(("encode_k", "encode_v", "logits", "decode"), key=lambda k: kern[k]["ms"])
+    extra = {
+        "logit_keys_per_s": keys / (log_ms * 1e-3),
+        "logit_hbm_frac": kern["logits"]["hbm_frac"],
+        "decode_keys_per_s": keys / (dec_ms * 1e-3),
+        "encode_tokens_per_s": B * L / ((enc_ms + encv_ms) * 1e-3),
+        "encode_vectors_per_s": 2 * keys / ((enc_ms + encv_ms) * 1e-3),
+    }
+    cfg = {"workload": f"{'Llama-3.1-8B' if L == 32768 else 'Llama-70B'}-shaped decode layer", "batch": B,
+           "q_heads": Hq, "kv_heads": H, "head_dim": d, "context": L, "bits": bits, "qjl_rows": m,
+           "input_dtype": "bf16", "rope_base": st["rope_base"], "record_bytes": rec}
+    return keys / (ms_step * 1e-3), "keys/s", kern, dom, extra, cfg
+
+
+def cpu_baseline_llama(st, sample_keys):
+    """The oracle on a sample: encode sample_keys keys and values of one
+    (sequence, KV head), score them for its G query heads, and decode."""
+    import synth
+    from oracle import codec, estimator, rope as orope
+    K, V, Q = st["host"]
+    B, Hq, H, L, d, bits, m = (st[k] for k in ("B", "Hq", "H", "L", "d", "bits", "m"))
+    G = Hq // H
+    n = min(sample_keys, L)
+    t0 = time.perf_counter()
+    ock = codec.make_codebook(d, bits, m, False, seed=synth.K_SEED)
+    ocv = codec.make_codebook(d, bits, m, False, seed=synth.V_SEED)
+    t_setup = time.perf_counter() - t0
+    rope = orope.rope_table(st["rope_base"], d, L + 1) if st["rope_base"] else None
+    kx = synth.bf16_bits_to_f32(K[0, :n, 0])
+    vx = synth.bf16_bits_to_f32(V[0, :n, 0])
+    q = synth.bf16_bits_to_f32(Q[0, :G])
+    t0 = time.perf_counter()
+    ek = codec.encode(ock, kx, pos=np.arange(n), rope=rope)
+    ev = codec.encode(ocv, vx)
+    qp, s = estimator.prep_query(ock, q, n, rope)
+    estimator.logits(ock, qp, s, ek)
+    estimator.attention(ock, ocv, qp, s, ek, ev, n, 1 / math.sqrt(d))
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "keys/s", "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"{n} keys+values of one (sequence, KV head): oracle encode (RoPE for keys), logits for "
+                      f"its {G} query heads and fused decode; {dt:.1f} s on the host "
+                      f"(codebook tables built once beforehand, {t_setup:.1f} s)"}
+
+
+# ------------------------------------------------------------ ESM-2 prefill
+def setup_esm(torch, tq, synth):
+    S, T, H, d, layers, bits, m = 32, 1024, 20, 64, 33, 3, 64
+    tok = torch.from_numpy(synth.esm_tokens(0, S, T)).cuda()
+    Ks, Vs = [], []
+    for layer in range(layers):
+        pk, pv = synth.esm_layer_tables(layer)
+        Ks.append(torch.from_numpy(pk).cuda()[tok].view(S, T, H, d))
+        Vs.append(torch.from_numpy(pv).cuda()[tok].view(S, T, H, d))
+    st = {"S": S, "T": T, "H": H, "d": d, "layers": layers, "bits": bits, "m": m, "K": Ks, "V": Vs}
+    st["ck"] = tq.Codebook(d, bits, m, "hadamard", seed=synth.K_SEED)
+    st["cv"] = tq.Codebook(d, bits, m, "hadamard", seed=synth.V_SEED)
+    st["kp"] = [tq.Packed(st["ck"], S * H * T) for _ in range(layers)]
+    st["vp"] = [tq.Packed(st["cv"], S * H * T) for _ in range(layers)]
+    st["rope"] = tq.rope_table(1e4, d, T)
+    return st
+
+
+def step_esm(st, tq, timer):
+    for layer in range(st["layers"]):
+        timer.call("encode_k", lambda: tq.encode_kv(st["ck"], None, st["K"][layer], None, st["kp"][layer], None,
+                                                   L_cap=st["T"], rope=st["rope"]))
+        timer.call("encode_v", lambda: tq.encode_kv(None, st["cv"], None, st["V"][layer], None, st["vp"][layer],
+                                                   L_cap=st["T"]))
+
+
+def esm_report(st, timer, ms_step):
+    S, T, H, d, layers, bits, m = (st[k] for k in ("S", "T", "H", "d", "layers", "bits", "m"))
+    vec = S * T * H
+    rec = 4 + 4 + bits * d // 8 + m // 8
+    enc_ms, n = timer.mean_ms("encode_k")
+    encv_ms, _ = timer.mean_ms("encode_v")
+    kern = {"encode_k": {"ms": enc_ms, "launches": n, "alg_bytes": vec * (4 * d + rec), "units": vec},
+            "encode_v": {"ms": encv_ms, "alg_bytes": vec * (4 * d + rec), "units": vec}}
+    for k in kern.values():
+        k["GBps"] = k["alg_bytes"] / (k["ms"] * 1e-3) / 1e9
+        k["hbm_frac"] = k["GBps"] / HBM_PEAK_GBS
+    extra = {"encode_tokens_per_s": S * T / (ms_step * 1e-3), "encode_vectors_per_s": 2 * layers * vec / (ms_step * 1e-3)}
+    cfg = {"workload": "ESM-2-650M-shaped prefill encode", "layers": layers, "heads": H, "head_dim": d,
+           "sequences": S, "length": T, "bits": bits, "qjl_rows": m, "input_dtype": "f32", "rope_base": 1e4,
+           "record_bytes": rec}
+    return S * T / (ms_step * 1e-3), "tokens/s", kern, "encode_k", extra, cfg
+
+
+# ------------------------------------------------------------ vector search
+def setup_vsearch(torch, tq, synth):
+    n, nq, d, bits, m = 1_000_000, 1024, 1536, 2, 1536
+    X = torch.empty((n, d), dtype=torch.float32, device="cuda")
+    step = 65536
+    for s0 in range(0, n, step):
+        c = min(step, n - s0)
+        X[s0:s0 + c] = torch.from_numpy(synth.vsearch_rows(0, s0, c)).cuda()
+    Qh = synth.vsearch_rows(1, 0, nq)
+    st = {"n": n, "nq": nq, "d": d, "bits": bits, "m": m, "X": X.view(1, n, 1, d),
+          "Q": torch.from_numpy(Qh).cuda()[None], "Qh": Qh}
+    st["ck"] = tq.Codebook(d, bits, m, "dense", seed=synth.K_SEED)
+    st["kp"] = tq.Packed(st["ck"], n)
+    st["ws_e"] = torch.empty(tq.workspace_bytes(st["ck"], None, tq.TQ_OP_ENCODE, n), dtype=torch.uint8, device="cuda")
+    st["ws_l"] = torch.empty(tq.workspace_bytes(st["ck"], None, tq.TQ_OP_LOGITS, 1, nq, 1, n, 10), dtype=torch.uint8,
+                             device="cuda")
+    st["sl"] = torch.tensor([n], dtype=torch.int32, device="cuda")
+    return st
+
+
+def step_vsearch(st, tq, timer):
+    timer.call("encode_k", lambda: tq.encode_kv(st["ck"], None, st["X"], None, st["kp"], None, L_cap=st["n"],
+                                               workspace=st["ws_e"]))
+    timer.call("scan_topk", lambda: tq.attn_logits(st["ck"], st["Q"], st["kp"], 1, st["n"], st["sl"], top_k=10,
+                                                   workspace=st["ws_l"]))
+
+
+def vsearch_report(st, timer, ms_step):
+    n, nq, d, bits, m = (st[k] for k in ("n", "nq", "d", "bits", "m"))
+    rec = 8 + bits * d // 8 + m // 8
+    enc_ms, k = timer.mean_ms("encode_k")
+    scan_ms, _ = timer.mean_ms("scan_topk")
+    kern = {"encode_k": {"ms": enc_ms, "launches": k, "alg_bytes": n * (4 * d + rec), "units": n,
+                         "alg_tflop": 2.0 * n * d * (d + m) / 1e12},
+            "scan_topk": {"ms": scan_ms, "alg_bytes": n * rec, "units": n * nq,
+                          "alg_tflop": 2.0 * n * nq * (d + m) / 1e12}}
+    for kk in kern.values():
+        kk["GBps"] = kk["alg_bytes"] / (kk["ms"] * 1e-3) / 1e9
+        kk["hbm_frac"] = kk["GBps"] / HBM_PEAK_GBS
+        kk["TFLOPs"] = kk["alg_tflop"] / (kk["ms"] * 1e-3)
+    extra = {"scan_scores_per_s": n * nq / (scan_ms * 1e-3), "index_vectors_per_s": n / (enc_ms * 1e-3)}
+    cfg = {"workload": "vector search, 1e6 x 1536 unit vectors, 1024 queries, top-10", "bits": bits, "qjl_rows": m,
+           "rotation": "dense Haar", "record_bytes": rec}
+    return n / (ms_step * 1e-3), "vectors/s", kern, max(kern, key=lambda x: kern[x]["ms"]), extra, cfg
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        return 2
+    import torch
+    import kv_cache_vector_05_amd as tq
+    import synth
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    wl = args.workload
+    print(f"[bench] setting up {wl}", file=sys.stderr, flush=True)
+    if wl in ("llama8b", "llama70b"):
+        st = setup_llama(torch, tq, synth, wl)
+        step, report = (lambda t: step_llama(st, tq, t)), (lambda t, ms: llama_report(st, t, ms))
+    elif wl == "esm650m":
+        st = setup_esm(torch, tq, synth)
+        step, report = (lambda t: step_esm(st, tq, t)), (lambda t, ms: esm_report(st, t, ms))
+    elif wl == "vsearch":
+        st = setup_vsearch(torch, tq, synth)
+        step, report = (lambda t: step_vsearch(st, tq, t)), (lambda t, ms: vsearch_report(st, t, ms))
+    else:
+        raise SystemExit("tiny is a parity case, not a benchmark workload")
+    torch.cuda.synchronize()
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step(Timer(torch))
+    torch.cuda.synchronize()
+    timer = Timer(torch)
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(timer)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    value, unit, kern, dom, extra, cfg = report(timer, ms_step)
+    dk = kern[dom]
+    if "TFLOPs" in dk and dom == "scan_topk":
+        roof = {"bound": "mfma", "achieved": dk["TFLOPs"], "peak": 157.3, "unit": "TFLOP/s",
+                "frac": dk["TFLOPs"] / 157.3, "traffic": None, "kernel": dom}
+    else:
+        roof = {"bound": "hbm", "achieved": dk["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": dk["GBps"] / HBM_PEAK_GBS, "traffic": None, "kernel": dom}
+    line = {"metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f32", "data": "synthetic", "config": cfg, "roofline": roof,
+            "kernels": kern, **extra}
+    if not args.no_cpu_baseline and wl in ("llama8b", "llama70b"):
+        print("[bench] cpu baseline (oracle on a sample)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline_llama(st, args.cpu_sample or 65536)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -477,6 +477,7 @@ tq_status tq_encode_kv(const tq_codebook* ck, const tq_codebook* cv, const void*
     if (n_seq < 0 || n_tok < 0 || h_kv < 0 || tok_offset < 0 || L_cap < 0)
         return fail(TQ_EINVAL, "negative size");
     if ((int64_t)tok_offset + n_tok > L_cap) return fail(TQ_EINVAL, "tok_offset + n_tok exceeds L_cap");
+    if ((int64_t)n_seq * n_tok * h_kv == 0) return TQ_OK;  // nothing to encode
     if (!k && !v) return fail(TQ_EINVAL, "neither k nor v given");
     if ((rope_cos == nullptr) != (rope_sin == nullptr)) return fail(TQ_EINVAL, "give both RoPE tables or neither");
     const int64_t nvec = (int64_t)n_seq * n_tok * h_kv;
