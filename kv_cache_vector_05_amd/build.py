@@ -25,7 +25,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libtq.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["tq_host.cpp", "tq_gemm.hip", "tq_encode.hip", "tq_attn.hip"]
+SOURCES = ["tq_host.cpp", "tq_gemm.hip", "tq_encode.hip", "tq_attn.hip", "tq_logits.hip"]
 ARCH = "gfx950"
 
 
@@ -47,6 +47,9 @@ def _compile(src: str, verbose: bool) -> str:
     cmd = [hipcc()] + common_flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd += ["-ffp-contract=off"]
+    if src == "tq_logits.hip":
+        # keep MFMA accumulators in architectural VGPRs (no AGPR copies in the loop)
+        cmd += ["-mllvm", "--amdgpu-mfma-vgpr-form"]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

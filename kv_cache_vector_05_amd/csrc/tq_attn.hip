@@ -731,7 +731,8 @@ size_t logits_workspace_bytes(const tq_codebook* ck, int64_t B, int Hq, int h_kv
     const size_t rows = (size_t)B * Hq;
     const size_t chunk = (size_t)std::min(L_cap, kScanChunk);
     if (!ck->dense) {
-        size_t bytes = align256(rows * (d + m) * 4);
+        size_t bytes = logits_mfma_supported(ck) ? align256(qdigits_workspace_bytes(ck, (int64_t)rows))
+                                                 : align256(rows * (d + m) * 4);
         if (top_k) bytes += align256(rows * chunk * 4);
         return bytes;
     }
@@ -760,6 +761,35 @@ hipError_t launch_logits(const tq_codebook* ck, const tq_packed& k, const AttnAr
     const int64_t rows = (int64_t)a.B * a.Hq;
     char* ws = static_cast<char*>(a.ws);
     const int chunk = std::min(a.L_cap, kScanChunk);
+    if (!ck->dense && logits_mfma_supported(ck)) {
+        const QDigits qd = carve_qdigits(ck, ws, rows);
+        float* scores = reinterpret_cast<float*>(ws + align256(qdigits_workspace_bytes(ck, rows)));
+        hipError_t e = launch_qdigits(ck, a, qd, stream);
+        if (e != hipSuccess) return e;
+        if (a.top_k == 0) return launch_logits_mfma(ck, k, a, qd, 0, a.L_cap, a.out, a.L_cap, 0, stream);
+        for (int k0 = 0; k0 < a.L_cap; k0 += chunk) {
+            const int cnt = std::min(chunk, a.L_cap - k0);
+            e = launch_logits_mfma(ck, k, a, qd, k0, cnt, scores, chunk, k0, stream);
+            if (e != hipSuccess) return e;
+            TopK tk{};
+            tk.scores = scores;
+            tk.ld = chunk;
+            tk.row0 = 0;
+            tk.col0 = k0;
+            tk.cnt = cnt;
+            tk.Hq = a.Hq;
+            tk.L_cap = a.L_cap;
+            tk.k = a.top_k;
+            tk.first = k0 == 0;
+            tk.seq_len = a.seq_len;
+            tk.out_val = a.out;
+            tk.out_idx = a.topk_idx;
+            hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)rows), dim3(256), 0, stream, tk);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
     if (!ck->dense) {
         float* qp = reinterpret_cast<float*>(ws);
         float* s = qp + rows * d;

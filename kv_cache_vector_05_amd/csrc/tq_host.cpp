@@ -259,6 +259,34 @@ void haar_from_gaussians(int d, const double* g, std::vector<double>* qout) {
         }
 }
 
+// Levels as 24-bit fixed-point integers T_k ~= t_k * 2^shift split into three
+// balanced base-256 digits, each in [-128, 127]: T = e0*2^16 + e1*2^8 + e2.
+// The shift puts max|T| just under 127.5 * 2^16 so the top digit fits.
+void level_digits(const std::vector<float>& levels, uint32_t words[8], int* shift) {
+    double mx = 0.0;
+    for (float v : levels) mx = std::max(mx, (double)std::fabs(v));
+    int e = 0;
+    std::frexp(mx, &e);  // mx = f * 2^e, f in [0.5, 1)
+    int sh = 23 - e;
+    if (std::ldexp(mx, sh) > 127.0 * 65536.0) --sh;
+    *shift = sh;
+    for (int w = 0; w < 8; ++w) words[w] = 0u;
+    for (size_t c = 0; c < levels.size() && c < 8; ++c) {
+        long long T = std::llround(std::ldexp((double)levels[c], sh));
+        int dig[3];
+        for (int k = 2; k >= 1; --k) {
+            const long long r = ((T + 128) % 256 + 256) % 256 - 128;
+            dig[k] = (int)r;
+            T = (T - r) / 256;
+        }
+        dig[0] = (int)T;
+        for (int b = 0; b < 3; ++b) {
+            const uint32_t byte = (uint32_t)(uint8_t)(int8_t)dig[b];
+            words[2 * b + (c >> 2)] |= byte << (8 * (c & 3));
+        }
+    }
+}
+
 // Builds every host table of a codebook.
 static tq_status build_tables(const tq_spec& s, const tq_draws* dr, bool dense,
                               std::vector<float>* levels, std::vector<float>* thr,
@@ -371,6 +399,7 @@ tq_status tq_codebook_init(const tq_spec* spec, const tq_draws* draws, void* str
         delete cb;
         return st;
     }
+    if (cb->K <= 8) level_digits(cb->levels, cb->lvl_digits, &cb->lvl_shift);
     const int d = spec->d, m = spec->m;
     // the encode kernel's sketch operand order (Hadamard form): for row block
     // rb, step p and lane l: S[rb*32 + l%32][(l/32)*(d/2) + p]

@@ -33,6 +33,11 @@ struct tq_codebook {
     std::vector<float> levels, thresholds, rotation, sketch;  // host mirrors
     void* block = nullptr;                                    // one device allocation
     tq::DeviceTables dev;
+    // levels in 24-bit fixed point, t_k ~= T_k * 2^-lvl_shift, as three balanced
+    // base-256 int8 digits (digit 0 most significant); word 2b holds digit b
+    // of codes 0..3, word 2b+1 of codes 4..7 (byte tables for v_perm)
+    uint32_t lvl_digits[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int lvl_shift = 0;
 };
 
 namespace tq {
@@ -47,6 +52,7 @@ void lloyd_max_table(int d, int bits, std::vector<double>* levels, std::vector<d
 void splitmix_gaussians(uint64_t seed, int purpose, size_t n, double* out);
 void splitmix_signs(uint64_t seed, size_t n, int8_t* out);
 void haar_from_gaussians(int d, const double* g, std::vector<double>* q);  // row-major
+void level_digits(const std::vector<float>& levels, uint32_t words[8], int* shift);
 
 // ---- kernel launchers (tq_encode.hip, tq_attn.hip, tq_gemm.hip) ----
 struct EncodeArgs {
@@ -85,6 +91,22 @@ size_t logits_workspace_bytes(const tq_codebook* ck, int64_t B, int Hq, int h_kv
                               int top_k);
 size_t decode_workspace_bytes(const tq_codebook* ck, const tq_codebook* cv, int64_t B, int Hq,
                               int h_kv, int L_cap);
+
+// Fixed-point digit form of prepared queries (tq_logits.hip).
+struct QDigits {
+    float* qp;      // [rows][d]   q' = Pi RoPE(q)
+    float* s;       // [rows][m]   s = S q'
+    int8_t* qd;     // [rows*4][d] balanced base-128 digits of q' (most significant first)
+    int8_t* sd;     // [rows*4][sdw] digits of s in MFMA slot order
+    float* scale;   // [rows][3]   shift(q'), shift(s) (x ~= X * 2^-shift), fixed-point sum of s
+    int sdw, ncs;
+};
+bool logits_mfma_supported(const tq_codebook* ck);
+size_t qdigits_workspace_bytes(const tq_codebook* ck, int64_t rows);
+QDigits carve_qdigits(const tq_codebook* ck, void* ws, int64_t rows);
+hipError_t launch_qdigits(const tq_codebook* ck, const AttnArgs& a, const QDigits& q, hipStream_t stream);
+hipError_t launch_logits_mfma(const tq_codebook* ck, const tq_packed& k, const AttnArgs& a, const QDigits& q,
+                              int k0, int klen, float* out, int64_t ld, int col0, hipStream_t stream);
 
 // C[M][N] = A[M][K] * B[N][K]^T (+ per-column scale if col_scale != nullptr),
 // fp32, row-major with leading dimensions lda/ldb/ldc (elements).

@@ -1,0 +1,523 @@
+// Attention-logit scan from packed keys on the integer matrix cores
+// (tambur post: logits straight from quantised keys; iaemfoco post, "TurboQuant:
+// Uma Nova Abordagem" and itstec post, "Por dentro do processo de compressao
+// KV": the unbiased one-bit QJL correction):
+//     logit = nu ( <q', t[c]> + sqrt(pi/2)/m * gamma * <s, z> ),  q' = Pi RoPE(q), s = S q'.
+//
+// Exact integer formulation.  Every float that enters a product is turned
+// into a fixed-point integer split into balanced int8 digits: q' and s once
+// per query (here, in the query-prep kernel) as 28 bits in four base-128
+// digits, the levels t_k once per codebook (on the host) as 24 bits in three
+// base-256 digits, each with its own power-of-two scale.  The products of digits are summed exactly in int32 by
+// v_mfma_i32_16x16x64_i8, the digit sums are combined in int32 and fp64 and
+// only the final value is rounded to fp32; the residual error is the
+// rounding of q', s (2^-27 of their largest entry) and t (2^-24 of the
+// largest level) to fixed point, below an fp32 dot product's own error.
+//
+// MFMA shape: rows = (query, digit of q') - four digits of four queries fill
+// the 16 rows, so a GQA group of 4 wastes nothing - columns = 16 keys, K = 64
+// coordinates.  Lane l of the wave owns key l % 16 and the coordinate quarter
+// l / 16 ([q*d/4, (q+1)*d/4)), which for d = 128, b = 3 is exactly three whole
+// code words; its 16 K-slots per MFMA are 16 consecutive coordinates.  The B
+// operand (digit b of t[c] for the 16 coordinates) is built with one v_perm
+// per 4 coordinates from an 8-byte digit table.  After the MFMAs, lane l holds
+// all 12 digit products of (query l/16, key l%16): rows 4(l/16)+r = digit r.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+typedef int intx4 __attribute__((ext_vector_type(4)));
+
+constexpr double kQjlD = 1.2533141373155003;  // sqrt(pi / 2)
+
+__device__ __forceinline__ int clamp_len2(const int32_t* seq_len, int b, int L_cap) {
+    int s = seq_len[b];
+    return s < 0 ? 0 : (s > L_cap ? L_cap : s);
+}
+
+// block-wide max of |v| and sum of v over 256 threads
+__device__ __forceinline__ void block_absmax_sum(float v, float* red, float* amax, float* sum) {
+    float a = fabsf(v), s = v;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        a = fmaxf(a, __shfl_xor(a, o));
+        s += __shfl_xor(s, o);
+    }
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) {
+        red[threadIdx.x >> 6] = a;
+        red[4 + (threadIdx.x >> 6)] = s;
+    }
+    __syncthreads();
+    *amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    *sum = (red[4] + red[5]) + (red[6] + red[7]);
+}
+
+// Fixed point with four balanced base-128 digits: returns the shift sh with
+// x ~= X * 2^-sh, |X| <= 2^26, and writes the digits (most significant first).
+__device__ __forceinline__ int fixed_shift(float amax) {
+    if (!(amax > 0.0f)) return 0;
+    int e;
+    frexpf(amax, &e);
+    return 26 - e;
+}
+__device__ __forceinline__ long long to_fixed(float x, int sh) { return llrint(ldexp((double)x, sh)); }
+__device__ __forceinline__ void digits4(long long X, int8_t d[4]) {
+#pragma unroll
+    for (int k = 3; k >= 1; --k) {
+        long long r = ((X + 64) & 127) - 64;
+        d[k] = (int8_t)r;
+        X = (X - r) >> 7;
+    }
+    d[0] = (int8_t)X;
+}
+
+struct QDig {
+    const void* q;
+    int32_t bf16, Hq, L_cap, m, sdw, ncs;
+    const int32_t* seq_len;
+    const float* rope_cos;
+    const float* rope_sin;
+    const float* sigma;
+    const float* sketch;
+    float* qp;       // [rows][D]    q' (fp32)
+    float* s;        // [rows][m]    s = S q' (fp32)
+    int8_t* qd;      // [rows*4][D]  digits of q' (digit rows 4*row + a)
+    int8_t* sd;      // [rows*4][sdw] digits of s in MFMA slot order
+    float* scale;    // [rows][3]    shift(q'), shift(s), sum of the fixed-point s values
+};
+
+// One workgroup per query head: RoPE, sign flips, Walsh-Hadamard, 1/sqrt(d),
+// s = S q', then the fixed-point digit rows.
+template <int D>
+__global__ __launch_bounds__(256) void qprep_digits_kernel(QDig p) {
+    __shared__ float xs[D];
+    __shared__ float sv[D];
+    __shared__ float red[8];
+    const int t = threadIdx.x;
+    const int64_t bh = blockIdx.x;
+    const int b = (int)(bh / p.Hq);
+    if (t < D) {
+        xs[t] = p.bf16 ? __uint_as_float((uint32_t) static_cast<const uint16_t*>(p.q)[bh * D + t] << 16)
+                       : static_cast<const float*>(p.q)[bh * D + t];
+    }
+    __syncthreads();
+    if (p.rope_cos) {
+        const int pos = clamp_len2(p.seq_len, b, p.L_cap);
+        float lo = 0.f, hi = 0.f;
+        if (t < D / 2) {
+            const float c = p.rope_cos[(int64_t)pos * (D / 2) + t];
+            const float sn = p.rope_sin[(int64_t)pos * (D / 2) + t];
+            const float a = xs[t], bb = xs[t + D / 2];
+            lo = a * c - bb * sn;
+            hi = bb * c + a * sn;
+        }
+        __syncthreads();
+        if (t < D / 2) {
+            xs[t] = lo;
+            xs[t + D / 2] = hi;
+        }
+        __syncthreads();
+    }
+    if (t < D) xs[t] *= p.sigma[t];
+    __syncthreads();
+    for (int s = 1; s < D; s <<= 1) {
+        if (t < D / 2) {
+            const int i = (t / s) * 2 * s + (t % s);
+            const float a = xs[i], bb = xs[i + s];
+            xs[i] = a + bb;
+            xs[i + s] = a - bb;
+        }
+        __syncthreads();
+    }
+    const float inv = 1.0f / sqrtf((float)D);
+    float qv = 0.f;
+    if (t < D) {
+        qv = xs[t] * inv;
+        xs[t] = qv;
+        p.qp[bh * D + t] = qv;
+    }
+    __syncthreads();
+    float sval = 0.f;
+    if (t < p.m) {
+        const float* row = p.sketch + (int64_t)t * D;
+        for (int i = 0; i < D; ++i) sval = fmaf(row[i], xs[i], sval);
+        sv[t] = sval;
+        p.s[bh * p.m + t] = sval;
+    }
+    float qmax, qsum, smax, ssum;
+    block_absmax_sum(qv, red, &qmax, &qsum);
+    block_absmax_sum(sval, red, &smax, &ssum);
+    const int shq = fixed_shift(qmax);
+    const int shs = fixed_shift(smax);
+    if (t < D) {
+        int8_t d[4];
+        digits4(to_fixed(qv, shq), d);
+        for (int a = 0; a < 4; ++a) p.qd[(bh * 4 + a) * D + t] = d[a];
+    }
+    // sketch digits in MFMA slot order: byte (qk*ncs + cs)*16 + j holds
+    // sketch row qk*(m/4) + 16*cs + j (zero where that slot is past m/4)
+    long long sfix = 0;
+    if (t < p.m) sfix = to_fixed(sval, shs);
+    __syncthreads();
+    if (p.m) {
+        for (int off = t; off < p.sdw; off += blockDim.x) {
+            const int qk = off / (16 * p.ncs), rem = off % (16 * p.ncs);
+            const int cs = rem / 16, j = rem % 16;
+            const int l = qk * (p.m / 4) + 16 * cs + j;
+            int8_t d[4] = {0, 0, 0, 0};
+            if (16 * cs + j < p.m / 4) digits4(to_fixed(sv[l], shs), d);
+            for (int a = 0; a < 4; ++a) p.sd[(bh * 4 + a) * p.sdw + off] = d[a];
+        }
+    }
+    // sum of the fixed-point s values (exact integer), for sum_l s_l z_l = 2 sum_l s_l bit_l - sum_l s_l
+    double sf = (double)sfix;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sf += __shfl_xor(sf, o);
+    __syncthreads();
+    __shared__ double dred[4];
+    if ((t & 63) == 0) dred[t >> 6] = sf;
+    __syncthreads();
+    if (t == 0) {
+        p.scale[bh * 3 + 0] = (float)shq;  // shifts are small integers, exact in fp32
+        p.scale[bh * 3 + 1] = (float)shs;
+        p.scale[bh * 3 + 2] = (float)ldexp((dred[0] + dred[1]) + (dred[2] + dred[3]), -shs);
+    }
+}
+
+struct LogM {
+    const int8_t* qd;
+    const int8_t* sd;
+    const float* scale;
+    const float* norm;
+    const float* rnorm;
+    const uint32_t* codes;
+    const uint32_t* signs;
+    const int32_t* seq_len;
+    int32_t Hq, h_kv, L_cap, m, sdw, ngroups, tiles_per_wave;
+    int32_t k0, klen;
+    float* out;
+    int64_t ld;
+    int32_t col0;
+    uint32_t tdig[8];
+    int32_t lvl_shift;
+};
+
+// digit b of the levels of the 4 codes in the bytes of sel
+__device__ __forceinline__ uint32_t lut4(const uint32_t* tdig, int b, uint32_t sel) {
+    return __builtin_amdgcn_perm(tdig[2 * b + 1], tdig[2 * b], sel);
+}
+
+// v_perm selector for the 4 codes in the low 4*BITS bits of w: byte k = code k
+template <int BITS>
+__device__ __forceinline__ uint32_t code_sel(uint32_t w) {
+    if constexpr (BITS == 3) {
+        // even codes (bits 0-2, 6-8) and odd codes (3-5, 9-11) spread by
+        // multiplication; the partial products never overlap
+        return (((w & 0x1C7u) * 0x401u) & 0x70007u) | (((w & 0xE38u) * 0x8020u) & 0x7000700u);
+    } else if constexpr (BITS == 2) {
+        return (((w & 0x33u) * 0x1001u) & 0x30003u) | (((w & 0xCCu) * 0x40040u) & 0x3000300u);
+    } else {
+        return ((w & 0xFu) * 0x204081u) & 0x01010101u;
+    }
+}
+
+// bytes 0..3 of the result = bits 0..3 of x (as 0/1)
+__device__ __forceinline__ uint32_t spread4(uint32_t x) { return ((x & 0xFu) * 0x204081u) & 0x01010101u; }
+
+template <int D, int BITS, int NRT, int NCS>
+__global__ __launch_bounds__(256) void logits_mfma_kernel(LogM p) {
+    constexpr int LPG = D / 4;              // coordinates per lane group
+    constexpr int NC = LPG / 16;            // K=64 chunks over the coordinates
+    constexpr int CW = BITS * D / 32;       // code words per record
+    constexpr int BPG = BITS * LPG;         // code bits per lane group
+    constexpr bool ALIGNED = (BPG % 32) == 0;
+    constexpr int NW = ALIGNED ? BPG / 32 : (BPG + 31) / 32 + 1;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int n = lane & 15;
+    const int qk = lane >> 4;
+    const int grp = blockIdx.x % p.ngroups;
+    const int64_t bk = blockIdx.x / p.ngroups;
+    const int b = (int)(bk / p.h_kv);
+    const int kh = (int)(bk % p.h_kv);
+    const int G = p.Hq / p.h_kv;
+    const int64_t rowbase = (int64_t)b * p.Hq + (int64_t)kh * G;
+    const int gq0 = grp * 4 * NRT;
+
+    // A operands: row (lane % 16) = (query (lane%16)/4, digit lane%4)
+    intx4 aq[NRT][NC];
+    intx4 as[NRT][NCS > 0 ? NCS : 1];
+    {
+        const int a = lane & 3;
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+            const int g = gq0 + 4 * rt + ((lane & 15) >> 2);
+            const bool ok = g < G;
+            const int64_t drow = (rowbase + (ok ? g : 0)) * 4 + a;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const intx4 v = *reinterpret_cast<const intx4*>(p.qd + drow * D + qk * LPG + 16 * c);
+                aq[rt][c] = ok ? v : intx4{0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int cs = 0; cs < NCS; ++cs) {
+                const intx4 v = *reinterpret_cast<const intx4*>(p.sd + drow * p.sdw + (qk * NCS + cs) * 16);
+                as[rt][cs] = ok ? v : intx4{0, 0, 0, 0};
+            }
+        }
+    }
+    // output side: lane owns query gq0 + 4*rt + qk of each row tile
+    double qscale[NRT], sscale[NRT], ssum[NRT];
+    const double tscale = ldexp(1.0, -p.lvl_shift);
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+        const int g = gq0 + 4 * rt + qk;
+        const int64_t row = rowbase + (g < G ? g : 0);
+        qscale[rt] = ldexp(tscale, -(int)p.scale[row * 3 + 0]);
+        sscale[rt] = ldexp(1.0, -(int)p.scale[row * 3 + 1]);
+        ssum[rt] = (double)p.scale[row * 3 + 2];
+    }
+    const double cq = NCS > 0 ? kQjlD / (double)p.m : 0.0;
+    uint32_t tdig[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tdig[i] = p.tdig[i];
+
+    const int sl = clamp_len2(p.seq_len, b, p.L_cap);
+    const int kend = min(sl, p.k0 + p.klen);
+    const int kbeg = p.k0 + (blockIdx.y * (blockDim.x >> 6) + wave) * p.tiles_per_wave * 16;
+    // per-lane bases at the wave's first key; a tile advances them by 16 records
+    const int64_t rec0 = bk * p.L_cap + kbeg;
+    const uint32_t* cbase = p.codes + rec0 * CW + ((BPG * qk) >> 5);
+    const int mw = p.m >> 5;
+    const int per = p.m >> 2;  // sketch rows per lane group (8, 16, 32, ...)
+    const uint32_t* sbase = p.signs + rec0 * mw + ((qk * per) >> 5);
+    const float* nbase = p.norm + rec0;
+    const float* gbase = p.rnorm + rec0;
+    for (int tile = 0; tile < p.tiles_per_wave; ++tile) {
+        const int key0 = kbeg + tile * 16;
+        if (key0 >= kend) break;  // the same for the whole wave
+        const int key = key0 + n;
+        const bool kv = key < kend;
+        const int kk = min(key, kend - 1) - kbeg;  // record offset of this lane's key from kbeg
+
+        // this lane's code bits: [BPG*qk, BPG*(qk+1)) of the record
+        uint32_t W[NW];
+        {
+            const uint32_t* cp = cbase + kk * CW;
+            if constexpr (ALIGNED) {
+#pragma unroll
+                for (int i = 0; i < NW; ++i) W[i] = cp[i];
+            } else {
+                const int w0 = (BPG * qk) >> 5;
+#pragma unroll
+                for (int i = 0; i < NW; ++i) W[i] = cp[min(i, CW - 1 - w0)];
+                const int sh = (BPG * qk) & 31;
+#pragma unroll
+                for (int i = 0; i + 1 < NW; ++i) W[i] = __builtin_amdgcn_alignbit(W[i + 1], W[i], sh);
+            }
+        }
+        // B operands: digit b of t[c] for the lane's 16 coordinates of chunk c
+        intx4 bd[NC][3];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+#pragma unroll
+            for (int sg = 0; sg < 4; ++sg) {
+                const int o = BITS * (16 * c + 4 * sg);  // bit offset of the 4 codes
+                const uint32_t lo = W[o >> 5];
+                const uint32_t hi = ((o >> 5) + 1 < NW) ? W[(o >> 5) + 1] : 0u;
+                const uint32_t w = __builtin_amdgcn_alignbit(hi, lo, o & 31);
+                const uint32_t sel = code_sel<BITS>(w);
+#pragma unroll
+                for (int bb = 0; bb < 3; ++bb) bd[c][bb][sg] = (int)lut4(tdig, bb, sel);
+            }
+        }
+        // sign bits as 0/1 bytes: lane group qk holds sketch rows [qk*m/4, (qk+1)*m/4)
+        intx4 bz[NCS > 0 ? NCS : 1];
+        if constexpr (NCS > 0) {
+#pragma unroll
+            for (int cs = 0; cs < NCS; ++cs) {
+                const int bit0 = qk * per + 16 * cs;
+                uint32_t x = sbase[kk * mw + ((bit0 >> 5) - ((qk * per) >> 5))] >> (bit0 & 31);
+                if (per - 16 * cs < 16) x &= (1u << (per - 16 * cs)) - 1u;  // fewer than 16 rows left
+                bz[cs][0] = (int)spread4(x);
+                bz[cs][1] = (int)spread4(x >> 4);
+                bz[cs][2] = (int)spread4(x >> 8);
+                bz[cs][3] = (int)spread4(x >> 12);
+            }
+        }
+        const float nu = nbase[kk];
+        const float gm = NCS > 0 ? gbase[kk] : 0.0f;
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+            intx4 acc[3];
+#pragma unroll
+            for (int bb = 0; bb < 3; ++bb) acc[bb] = intx4{0, 0, 0, 0};
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+#pragma unroll
+                for (int bb = 0; bb < 3; ++bb)
+                    acc[bb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[rt][c], bd[c][bb], acc[bb], 0, 0, 0);
+            intx4 accz = intx4{0, 0, 0, 0};
+#pragma unroll
+            for (int cs = 0; cs < NCS; ++cs)
+                accz = __builtin_amdgcn_mfma_i32_16x16x64_i8(as[rt][cs], bz[cs], accz, 0, 0, 0);
+            // acc[b][a]: digit a of q' (weight 2^(7(3-a))) times digit b of t
+            // (weight 2^(8(2-b))); |acc| <= 128 * 64 * 128 = 2^20
+            double V = 0.0;
+#pragma unroll
+            for (int bb = 0; bb < 3; ++bb) {
+                const double h = (double)(acc[bb][0] * 128 + acc[bb][1]);  // |.| < 2^28: exact in int32
+                const double l = (double)(acc[bb][2] * 128 + acc[bb][3]);
+                V = V * 256.0 + (h * 16384.0 + l);
+            }
+            double logit = V * qscale[rt];
+            if constexpr (NCS > 0) {
+                const double Z = ((double)accz[0] * 2097152.0 + (double)accz[1] * 16384.0) +
+                                 ((double)accz[2] * 128.0 + (double)accz[3]);
+                logit += cq * (double)gm * (2.0 * Z * sscale[rt] - ssum[rt]);
+            }
+            const int g = gq0 + 4 * rt + qk;
+            if (kv && g < G) p.out[(rowbase + g) * p.ld + (key - p.col0)] = (float)((double)nu * logit);
+        }
+    }
+}
+
+using LogMFn = void (*)(LogM);
+
+template <int D, int BITS, int NRT>
+LogMFn pick_ncs(int m) {
+    const int ncs = m == 0 ? 0 : std::max(1, m / 64);
+    switch (ncs) {
+        case 0: return logits_mfma_kernel<D, BITS, NRT, 0>;
+        case 1: return logits_mfma_kernel<D, BITS, NRT, 1>;
+        case 2: return logits_mfma_kernel<D, BITS, NRT, 2>;
+    }
+    return nullptr;
+}
+template <int D, int BITS>
+LogMFn pick_nrt(int nrt, int m) {
+    if (nrt == 1) return pick_ncs<D, BITS, 1>(m);
+    if (nrt == 2) return pick_ncs<D, BITS, 2>(m);
+    if (nrt == 4) return pick_ncs<D, BITS, 4>(m);
+    return nullptr;
+}
+template <int D>
+LogMFn pick_bits_m(int bits, int nrt, int m) {
+    switch (bits) {
+        case 1: return pick_nrt<D, 1>(nrt, m);
+        case 2: return pick_nrt<D, 2>(nrt, m);
+        case 3: return pick_nrt<D, 3>(nrt, m);
+    }
+    return nullptr;
+}
+
+size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+bool logits_mfma_supported(const tq_codebook* ck) {
+    return !ck->dense && ck->spec.bits <= 3 && (ck->spec.d == 64 || ck->spec.d == 128) && ck->spec.m <= 128;
+}
+
+size_t qdigits_workspace_bytes(const tq_codebook* ck, int64_t rows) {
+    const size_t d = ck->spec.d, m = ck->spec.m;
+    const size_t ncs = m == 0 ? 0 : std::max<size_t>(1, m / 64);
+    const size_t sdw = 64 * ncs;
+    return al256(rows * d * 4) + al256(rows * (m ? m : 1) * 4) + al256(rows * 4 * d) + al256(rows * 4 * (sdw ? sdw : 1)) +
+           al256(rows * 3 * 4);
+}
+
+QDigits carve_qdigits(const tq_codebook* ck, void* ws, int64_t rows) {
+    const size_t d = ck->spec.d, m = ck->spec.m;
+    const size_t ncs = m == 0 ? 0 : std::max<size_t>(1, m / 64);
+    const size_t sdw = 64 * ncs;
+    char* p = static_cast<char*>(ws);
+    QDigits q;
+    q.qp = reinterpret_cast<float*>(p);
+    p += al256(rows * d * 4);
+    q.s = reinterpret_cast<float*>(p);
+    p += al256(rows * (m ? m : 1) * 4);
+    q.qd = reinterpret_cast<int8_t*>(p);
+    p += al256(rows * 4 * d);
+    q.sd = reinterpret_cast<int8_t*>(p);
+    p += al256(rows * 4 * (sdw ? sdw : 1));
+    q.scale = reinterpret_cast<float*>(p);
+    q.sdw = (int)sdw;
+    q.ncs = (int)ncs;
+    return q;
+}
+
+hipError_t launch_qdigits(const tq_codebook* ck, const AttnArgs& a, const QDigits& q, hipStream_t stream) {
+    QDig p{};
+    p.q = a.q;
+    p.bf16 = a.bf16;
+    p.Hq = a.Hq;
+    p.L_cap = a.L_cap;
+    p.m = ck->spec.m;
+    p.sdw = q.sdw;
+    p.ncs = q.ncs;
+    p.seq_len = a.seq_len;
+    p.rope_cos = a.rope_cos;
+    p.rope_sin = a.rope_sin;
+    p.sigma = ck->dev.sigma;
+    p.sketch = ck->dev.sketch;
+    p.qp = q.qp;
+    p.s = q.s;
+    p.qd = q.qd;
+    p.sd = q.sd;
+    p.scale = q.scale;
+    const unsigned grid = (unsigned)((int64_t)a.B * a.Hq);
+    if (ck->spec.d == 64) hipLaunchKernelGGL(qprep_digits_kernel<64>, dim3(grid), dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL(qprep_digits_kernel<128>, dim3(grid), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_logits_mfma(const tq_codebook* ck, const tq_packed& k, const AttnArgs& a, const QDigits& q,
+                              int k0, int klen, float* out, int64_t ld, int col0, hipStream_t stream) {
+    const int G = a.Hq / a.h_kv;
+    const int nrt = G <= 4 ? 1 : (G <= 8 ? 2 : 4);
+    const int ngroups = (G + 4 * nrt - 1) / (4 * nrt);
+    LogMFn fn = nullptr;
+    if (ck->spec.d == 64) fn = pick_bits_m<64>(ck->spec.bits, nrt, ck->spec.m);
+    else if (ck->spec.d == 128) fn = pick_bits_m<128>(ck->spec.bits, nrt, ck->spec.m);
+    if (!fn) return hipErrorInvalidValue;
+    LogM p{};
+    p.qd = q.qd;
+    p.sd = q.sd;
+    p.scale = q.scale;
+    p.norm = k.norm;
+    p.rnorm = k.rnorm;
+    p.codes = k.codes;
+    p.signs = k.signs;
+    p.seq_len = a.seq_len;
+    p.Hq = a.Hq;
+    p.h_kv = a.h_kv;
+    p.L_cap = a.L_cap;
+    p.m = ck->spec.m;
+    p.sdw = q.sdw;
+    p.ngroups = ngroups;
+    p.tiles_per_wave = 8;
+    p.k0 = k0;
+    p.klen = klen;
+    p.out = out;
+    p.ld = ld;
+    p.col0 = col0;
+    for (int i = 0; i < 8; ++i) p.tdig[i] = ck->lvl_digits[i];
+    p.lvl_shift = ck->lvl_shift;
+    const int keys_per_block = 4 * p.tiles_per_wave * 16;
+    const unsigned gx = (unsigned)((int64_t)a.B * a.h_kv * ngroups);
+    const unsigned gy = (unsigned)((klen + keys_per_block - 1) / keys_per_block);
+    if (gx == 0 || gy == 0) return hipSuccess;
+    hipLaunchKernelGGL(fn, dim3(gx, gy), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace tq
