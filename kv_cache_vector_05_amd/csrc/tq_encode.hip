@@ -51,6 +51,76 @@ struct EncK {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+
+// lanes l and l ^ 32 exchange v (v_permlane32_swap): returns {own half's r0, r1}
+// where for lanes < 32 r0 = own and r1 = partner, and for lanes >= 32 r0 =
+// partner and r1 = own.
+struct Swap {
+    float r0, r1;
+};
+__device__ __forceinline__ Swap swap32(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
+// branch-free select of a or b by a lane mask (all ones or all zeros)
+__device__ __forceinline__ float msel(uint32_t m, float a, float b) {
+    return __uint_as_float((__float_as_uint(a) & m) | (__float_as_uint(b) & ~m));
+}
+__device__ __forceinline__ uint32_t mask_of(bool c) { return c ? 0xFFFFFFFFu : 0u; }
+
+// c = #{j : y >= tau_j} by binary search over the sorted thresholds, and
+// the matching level.  th/lv hold the thresholds and levels (uniform).
+template <int BITS>
+__device__ __forceinline__ uint32_t quantise(float y, const float* th, const float* lv, float* level) {
+    if constexpr (BITS == 1) {
+        const bool c0 = y >= th[0];
+        *level = c0 ? lv[1] : lv[0];
+        return c0 ? 1u : 0u;
+    } else if constexpr (BITS == 2) {
+        const uint32_t m1 = mask_of(y >= th[1]);
+        const uint32_t m0 = mask_of(y >= msel(m1, th[2], th[0]));
+        *level = msel(m0, msel(m1, lv[3], lv[1]), msel(m1, lv[2], lv[0]));
+        return (m1 & 2u) | (m0 & 1u);
+    } else if constexpr (BITS == 3) {
+        const uint32_t m2 = mask_of(y >= th[3]);
+        const uint32_t m1 = mask_of(y >= msel(m2, th[5], th[1]));
+        const float tb = msel(m1, msel(m2, th[6], th[2]), msel(m2, th[4], th[0]));
+        const uint32_t m0 = mask_of(y >= tb);
+        *level = 0.0f;  // looked up four at a time by the caller
+        return (m2 & 4u) | (m1 & 2u) | (m0 & 1u);
+    } else {
+        uint32_t c = 0;
+        float l = lv[0];
+#pragma unroll
+        for (int k = 0; k < 15; ++k) {
+            const bool ge = y >= th[k];
+            c = ge ? (uint32_t)(k + 1) : c;
+            l = ge ? lv[k + 1] : l;
+        }
+        *level = l;
+        return c;
+    }
+}
+
+// fp32 levels of 4 codes (selector bytes) from byte-plane tables: plane k
+// holds byte k of the 8 levels (two words per plane)
+__device__ __forceinline__ void levels4(const uint32_t* bp, uint32_t sel, float out[4]) {
+    const uint32_t p0 = __builtin_amdgcn_perm(bp[1], bp[0], sel);
+    const uint32_t p1 = __builtin_amdgcn_perm(bp[3], bp[2], sel);
+    const uint32_t p2 = __builtin_amdgcn_perm(bp[5], bp[4], sel);
+    const uint32_t p3 = __builtin_amdgcn_perm(bp[7], bp[6], sel);
+    const uint32_t a01 = __builtin_amdgcn_perm(p1, p0, 0x05010400u);  // L0.b0 L0.b1 L1.b0 L1.b1
+    const uint32_t a23 = __builtin_amdgcn_perm(p3, p2, 0x05010400u);  // L0.b2 L0.b3 L1.b2 L1.b3
+    const uint32_t b01 = __builtin_amdgcn_perm(p1, p0, 0x07030602u);  // L2.b0 L2.b1 L3.b0 L3.b1
+    const uint32_t b23 = __builtin_amdgcn_perm(p3, p2, 0x07030602u);
+    out[0] = __uint_as_float(__builtin_amdgcn_perm(a23, a01, 0x05040100u));
+    out[1] = __uint_as_float(__builtin_amdgcn_perm(a23, a01, 0x07060302u));
+    out[2] = __uint_as_float(__builtin_amdgcn_perm(b23, b01, 0x05040100u));
+    out[3] = __uint_as_float(__builtin_amdgcn_perm(b23, b01, 0x07060302u));
+}
+
 template <int D, int BITS, int M, bool BF16>
 __global__ __launch_bounds__(256) void encode_rht_kernel(EncK p) {
     constexpr int HALF = D / 2;
@@ -58,33 +128,55 @@ __global__ __launch_bounds__(256) void encode_rht_kernel(EncK p) {
     constexpr int CW = BITS * D / 32;     // code words per record
     constexpr int WH = BITS * HALF / 32;  // code words per half
     constexpr int NRB = M / 32;           // sketch row blocks (= sign words)
-    constexpr int SKN = M > 0 ? M * D : 1;
-    __shared__ float s_sk[SKN];
+    constexpr int NP = HALF / 8;          // MFMA K-steps (8 coordinates per lane half)
+    constexpr int SKN = M > 0 ? NRB * NP * 2 * 64 : 1;
+    // residuals enter the sketch scaled by 2^8 so their fp16 low parts stay normal
+    constexpr float ESCALE = 256.0f;
+    __shared__ half8 s_sk[SKN];
 
     if constexpr (M > 0) {
-        for (int i = threadIdx.x; i < M * D; i += blockDim.x) s_sk[i] = p.sketch_mfma[i];
+        const half8* src = reinterpret_cast<const half8*>(p.sketch_mfma);
+        for (int i = threadIdx.x; i < SKN; i += blockDim.x) s_sk[i] = src[i];
     }
     __syncthreads();
 
     const int lane = threadIdx.x & 63;
     const int v = lane & 31;
     const int h = lane >> 5;
+    const float hs = h ? -1.0f : 1.0f;  // last butterfly: h = 0 keeps a + b, h = 1 keeps a - b
 
-    // Hadamard signs of this lane's half as a bit mask (bit j: flip coordinate h*HALF + j)
-    uint32_t flip[HALF / 32];
-#pragma unroll
-    for (int w = 0; w < HALF / 32; ++w) {
+    // Hadamard sign masks, bit j of word w flips coordinate h*HALF + 32w + j.
+    // Kept in LDS and re-read per tile: held in registers, the compiler would
+    // hoist one expanded mask per coordinate out of the tile loop.
+    __shared__ uint32_t s_flip[2 * (HALF / 32)];
+    if (threadIdx.x < 2 * (HALF / 32)) {
+        const int hh = threadIdx.x / (HALF / 32), w = threadIdx.x % (HALF / 32);
         uint32_t mask = 0;
-#pragma unroll
-        for (int j = 0; j < 32; ++j) mask |= (p.sigma[h * HALF + w * 32 + j] < 0.0f ? 1u : 0u) << j;
-        flip[w] = mask;
+        for (int j = 0; j < 32; ++j) mask |= (p.sigma[hh * HALF + w * 32 + j] < 0.0f ? 1u : 0u) << j;
+        s_flip[threadIdx.x] = mask;
     }
+    __syncthreads();
     float lv[K], th[K - 1];
 #pragma unroll
-    for (int k = 0; k < K; ++k) lv[k] = p.levels[k];
+    for (int k = 0; k < K; ++k) lv[k] = p.levels[k] * ESCALE;
 #pragma unroll
-    for (int k = 0; k < K - 1; ++k) th[k] = p.thresholds[k];
-    const float inv_sqrt_d = 1.0f / sqrtf((float)D);
+    for (int k = 0; k < K - 1; ++k) th[k] = p.thresholds[k] * ESCALE;
+    // byte planes of the (scaled) levels for four-at-a-time lookups (3 bits)
+    uint32_t bp[8];
+    if constexpr (BITS == 3) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                w0 |= ((__float_as_uint(lv[c]) >> (8 * k)) & 0xFFu) << (8 * c);
+                w1 |= ((__float_as_uint(lv[c + 4]) >> (8 * k)) & 0xFFu) << (8 * c);
+            }
+            bp[2 * k] = w0;
+            bp[2 * k + 1] = w1;
+        }
+    }
+    const float yscale = ESCALE / sqrtf((float)D);
 
     const int64_t wave_stride = (int64_t)gridDim.x * (blockDim.x >> 6);
     for (int64_t tile = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); tile < p.n_tiles;
@@ -98,8 +190,7 @@ __global__ __launch_bounds__(256) void encode_rht_kernel(EncK p) {
 
         float x[HALF];
         if (valid) {
-            const int64_t off = (int64_t)seq * p.s_seq + (int64_t)token * p.s_tok +
-                                (int64_t)head * p.s_head + h * HALF;
+            const int64_t off = (int64_t)seq * p.s_seq + (int64_t)token * p.s_tok + (int64_t)head * p.s_head + h * HALF;
             if constexpr (BF16) {
                 const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.x) + off);
 #pragma unroll
@@ -130,12 +221,12 @@ __global__ __launch_bounds__(256) void encode_rht_kernel(EncK p) {
             for (int j = 0; j < HALF; ++j) x[j] = 0.0f;
         }
 
+        __builtin_amdgcn_sched_barrier(0);
         // RoPE (keys): pair (i, i + D/2) is (lane half 0, lane half 1) at the same j
         if (p.rope_cos) {
             const int pos = p.tok_offset + (valid ? token : 0);
             const float4* cp = reinterpret_cast<const float4*>(p.rope_cos + (int64_t)pos * HALF);
             const float4* sp = reinterpret_cast<const float4*>(p.rope_sin + (int64_t)pos * HALF);
-            const float sgn = h ? 1.0f : -1.0f;
 #pragma unroll
             for (int c = 0; c < HALF / 4; ++c) {
                 const float4 cc = cp[c];
@@ -145,24 +236,33 @@ __global__ __launch_bounds__(256) void encode_rht_kernel(EncK p) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int j = 4 * c + u;
-                    const float other = __shfl_xor(x[j], 32);
-                    x[j] = x[j] * cs[u] + sgn * (other * sn[u]);
+                    const Swap sw = swap32(x[j]);
+                    const float other = h ? sw.r0 : sw.r1;
+                    x[j] = fmaf(x[j], cs[u], -hs * (other * sn[u]));
                 }
+                // four table entries at a time: bounded live ranges
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
 
-        // norm nu and the scale that maps H(sigma*x) to y = Pi (x / nu)
+        // norm nu and the scale that maps H(sigma*x) to 2^8 * Pi (x / nu)
         float ss = 0.0f;
 #pragma unroll
         for (int j = 0; j < HALF; ++j) ss = fmaf(x[j], x[j], ss);
-        ss += __shfl_xor(ss, 32);
+        {
+            const Swap sw = swap32(ss);
+            ss = sw.r0 + sw.r1;
+        }
         const float nu = sqrtf(ss);
-        const float scale = nu > 0.0f ? inv_sqrt_d / nu : 0.0f;
+        const float scale = nu > 0.0f ? yscale / nu : 0.0f;
 
         // sign flips, then the Walsh-Hadamard butterflies (Sylvester order)
+        uint32_t flip[HALF / 32];
+#pragma unroll
+        for (int w = 0; w < HALF / 32; ++w) flip[w] = s_flip[h * (HALF / 32) + w];
 #pragma unroll
         for (int j = 0; j < HALF; ++j)
-            x[j] = __uint_as_float(__float_as_uint(x[j]) ^ (((flip[j >> 5] >> (j & 31)) & 1u) << 31));
+            x[j] = __uint_as_float(__float_as_uint(x[j]) ^ ((flip[j >> 5] << (31 - (j & 31))) & 0x80000000u));
 #pragma unroll
         for (int s = 1; s < HALF; s <<= 1) {
 #pragma unroll
@@ -176,35 +276,83 @@ __global__ __launch_bounds__(256) void encode_rht_kernel(EncK p) {
         }
 #pragma unroll
         for (int j = 0; j < HALF; ++j) {
-            const float o = __shfl_xor(x[j], 32);
-            x[j] = h ? (o - x[j]) : (x[j] + o);
+            const Swap sw = swap32(x[j]);
+            x[j] = fmaf(hs, sw.r1, sw.r0);
         }
 
-        // quantise (c = #{k : y >= tau_k}), residual, pack
+        __builtin_amdgcn_sched_barrier(0);
+        // per 8-coordinate chunk: quantise, residual, pack, and feed the
+        // residual's fp16 hi/lo parts to the sketch MFMAs
         uint32_t cw[WH];
 #pragma unroll
         for (int w = 0; w < WH; ++w) cw[w] = 0u;
         float gg = 0.0f;
+        floatx16 acc[NRB > 0 ? NRB : 1];
 #pragma unroll
-        for (int j = 0; j < HALF; ++j) {
-            const float y = x[j] * scale;
-            uint32_t c = 0;
-            float yh = lv[0];
+        for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-            for (int k = 0; k < K - 1; ++k) {
-                const bool ge = y >= th[k];
-                c = ge ? (uint32_t)(k + 1) : c;
-                yh = ge ? lv[k + 1] : yh;
+            for (int q = 0; q < 16; ++q) acc[rb][q] = 0.0f;
+#pragma unroll
+        for (int pc = 0; pc < NP; ++pc) {
+            float e[8];
+            uint32_t code[8];
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                const float y = x[8 * pc + jj] * scale;
+                float level;
+                code[jj] = quantise<BITS>(y, th, lv, &level);
+                e[jj] = y - level;  // levels of 3-bit codes are subtracted below
             }
-            const float e = y - yh;
-            x[j] = e;
-            gg = fmaf(e, e, gg);
-            const int bp = BITS * j;
-            cw[bp >> 5] |= c << (bp & 31);
-            if ((bp & 31) + BITS > 32) cw[(bp >> 5) + 1] |= c >> (32 - (bp & 31));
+            if constexpr (BITS == 3) {
+#pragma unroll
+                for (int g4 = 0; g4 < 2; ++g4) {
+                    const uint32_t sel = code[4 * g4] | (code[4 * g4 + 1] << 8) | (code[4 * g4 + 2] << 16) |
+                                         (code[4 * g4 + 3] << 24);
+                    float l4[4];
+                    levels4(bp, sel, l4);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) e[4 * g4 + u] -= l4[u];
+                }
+            }
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                gg = fmaf(e[jj], e[jj], gg);
+                const int bpos = BITS * (8 * pc + jj);
+                cw[bpos >> 5] |= code[jj] << (bpos & 31);
+                if ((bpos & 31) + BITS > 32) cw[(bpos >> 5) + 1] |= code[jj] >> (32 - (bpos & 31));
+            }
+            if constexpr (M > 0) {
+                half8 ehi, elo;
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    const _Float16 hi = (_Float16)e[jj];
+                    ehi[jj] = hi;
+                    elo[jj] = (_Float16)(e[jj] - (float)hi);
+                }
+#pragma unroll
+                for (int rb = 0; rb < NRB; ++rb) {
+                    const half8 shi = s_sk[((rb * NP + pc) * 2 + 0) * 64 + lane];
+                    acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(shi, ehi, acc[rb], 0, 0, 0);
+                }
+#pragma unroll
+                for (int rb = 0; rb < NRB; ++rb) {
+                    const half8 shi = s_sk[((rb * NP + pc) * 2 + 0) * 64 + lane];
+                    acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(shi, elo, acc[rb], 0, 0, 0);
+                }
+#pragma unroll
+                for (int rb = 0; rb < NRB; ++rb) {
+                    const half8 slo = s_sk[((rb * NP + pc) * 2 + 1) * 64 + lane];
+                    acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(slo, ehi, acc[rb], 0, 0, 0);
+                }
+            }
+            // keep each chunk's operand reads next to its MFMAs (bounded live ranges)
+            __builtin_amdgcn_sched_barrier(0);
         }
-        gg += __shfl_xor(gg, 32);
-        const float gamma = sqrtf(gg);
+        {
+            const Swap sw = swap32(gg);
+            gg = sw.r0 + sw.r1;
+        }
+        const float gamma = sqrtf(gg) * (1.0f / ESCALE);
 
         const int64_t n = ((int64_t)seq * p.h_kv + head) * p.L_cap + p.tok_offset + token;
         if (valid) {
@@ -216,27 +364,15 @@ __global__ __launch_bounds__(256) void encode_rht_kernel(EncK p) {
         }
 
         if constexpr (M > 0) {
-            // S e for the 32 vectors of the tile: A = S (row block rb), B = e
-            floatx16 acc[NRB];
-#pragma unroll
-            for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[rb][r] = 0.0f;
-#pragma unroll
-            for (int pp = 0; pp < HALF; ++pp) {
-#pragma unroll
-                for (int rb = 0; rb < NRB; ++rb)
-                    acc[rb] = __builtin_amdgcn_mfma_f32_32x32x2f32(s_sk[(rb * HALF + pp) * 64 + lane], x[pp],
-                                                                   acc[rb], 0, 0, 0);
-            }
-            // D[i][j]: j = lane % 32, i = 8*(r/4) + 4*(lane/32) + r%4
+            // D[i][j]: j = lane % 32 (vector), i = 8*(r/4) + 4*(lane/32) + r%4 (sketch row)
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb) {
                 uint32_t wb = 0;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) wb |= (acc[rb][r] >= 0.0f ? 1u : 0u) << (8 * (r >> 2) + (r & 3));
+                for (int q = 0; q < 16; ++q) wb |= (acc[rb][q] >= 0.0f ? 1u : 0u) << (8 * (q >> 2) + (q & 3));
                 wb <<= 4 * h;
-                wb |= __shfl_xor(wb, 32);
+                const Swap sw = swap32(__uint_as_float(wb));
+                wb = __float_as_uint(sw.r0) | __float_as_uint(sw.r1);
                 if (valid && (rb & 1) == h) p.signs[n * NRB + rb] = wb;
             }
         }

@@ -287,6 +287,44 @@ void level_digits(const std::vector<float>& levels, uint32_t words[8], int* shif
     }
 }
 
+// IEEE binary16 conversions (round to nearest even), for the MFMA tables.
+uint16_t f32_to_f16(float f) {
+    uint32_t x;
+    std::memcpy(&x, &f, 4);
+    const uint32_t sign = (x >> 16) & 0x8000u;
+    const int32_t exp = (int32_t)((x >> 23) & 0xFF) - 127 + 15;
+    uint32_t man = x & 0x7FFFFFu;
+    if (((x >> 23) & 0xFF) == 0xFF) return (uint16_t)(sign | 0x7C00u | (man ? 0x200u : 0u));
+    if (exp >= 31) return (uint16_t)(sign | 0x7C00u);
+    if (exp <= 0) {
+        if (exp < -10) return (uint16_t)sign;
+        man |= 0x800000u;
+        const int shift = 14 - exp;
+        uint32_t h = man >> shift;
+        const uint32_t rem = man & ((1u << shift) - 1u), halfway = 1u << (shift - 1);
+        if (rem > halfway || (rem == halfway && (h & 1u))) ++h;
+        return (uint16_t)(sign | h);
+    }
+    uint32_t h = ((uint32_t)exp << 10) | (man >> 13);
+    const uint32_t rem = man & 0x1FFFu;
+    if (rem > 0x1000u || (rem == 0x1000u && (h & 1u))) ++h;
+    return (uint16_t)(sign | h);
+}
+
+float f16_to_f32(uint16_t h) {
+    const uint32_t sign = (uint32_t)(h & 0x8000u) << 16;
+    const uint32_t exp = (h >> 10) & 0x1F, man = h & 0x3FFu;
+    float v;
+    if (exp == 0) v = std::ldexp((float)man, -24);
+    else if (exp == 31) v = man ? NAN : INFINITY;
+    else v = std::ldexp((float)(man | 0x400u), (int)exp - 25);
+    uint32_t bits;
+    std::memcpy(&bits, &v, 4);
+    bits |= sign;
+    std::memcpy(&v, &bits, 4);
+    return v;
+}
+
 // Builds every host table of a codebook.
 static tq_status build_tables(const tq_spec& s, const tq_draws* dr, bool dense,
                               std::vector<float>* levels, std::vector<float>* thr,
@@ -401,16 +439,25 @@ tq_status tq_codebook_init(const tq_spec* spec, const tq_draws* draws, void* str
     }
     if (cb->K <= 8) level_digits(cb->levels, cb->lvl_digits, &cb->lvl_shift);
     const int d = spec->d, m = spec->m;
-    // the encode kernel's sketch operand order (Hadamard form): for row block
-    // rb, step p and lane l: S[rb*32 + l%32][(l/32)*(d/2) + p]
+    // the encode kernel's sketch operand (Hadamard form): S split into fp16
+    // hi + lo parts in the A-operand order of v_mfma_f32_32x32x16_f16:
+    // entry [(rb*(d/16) + p)*2 + piece][lane][s] = part `piece` of
+    // S[rb*32 + lane%32][(lane/32)*(d/2) + 8p + s]   (s = 0..7)
     std::vector<float> sk_mfma((size_t)m * d);
     if (!dense && m) {
-        const int half = d / 2;
+        const int half = d / 2, np = d / 16;
+        uint16_t* out = reinterpret_cast<uint16_t*>(sk_mfma.data());
         for (int rb = 0; rb < m / 32; ++rb)
-            for (int p = 0; p < half; ++p)
+            for (int p = 0; p < np; ++p)
                 for (int l = 0; l < 64; ++l)
-                    sk_mfma[((size_t)rb * half + p) * 64 + l] =
-                        cb->sketch[(size_t)(rb * 32 + (l & 31)) * d + (l >> 5) * half + p];
+                    for (int sidx = 0; sidx < 8; ++sidx) {
+                        const float v = cb->sketch[(size_t)(rb * 32 + (l & 31)) * d + (l >> 5) * half + 8 * p + sidx];
+                        const uint16_t hi = f32_to_f16(v);
+                        const uint16_t lo = f32_to_f16(v - f16_to_f32(hi));
+                        const size_t base = ((((size_t)rb * np + p) * 2) * 64 + l) * 8 + sidx;
+                        out[base] = hi;
+                        out[base + 64 * 8] = lo;
+                    }
     }
     // one device block: levels[16] | thresholds[16] | sigma[d] or rot[d*d] | sketch | sketch_mfma
     const size_t n_lv = 16, n_th = 16;

@@ -20,7 +20,7 @@ struct DeviceTables {
     float* sigma = nullptr;       // [d]    Hadamard signs as +-1.0f
     float* rot = nullptr;         // [d*d]  dense Pi, row-major (y = Pi u)
     float* sketch = nullptr;      // [m*d]  S, row-major
-    float* sketch_mfma = nullptr; // [m*d]  S in the encode kernel's MFMA operand order
+    float* sketch_mfma = nullptr; // [m*d]  S as fp16 hi/lo pairs in the encode kernel's MFMA operand order
 };
 
 }  // namespace tq
@@ -53,6 +53,8 @@ void splitmix_gaussians(uint64_t seed, int purpose, size_t n, double* out);
 void splitmix_signs(uint64_t seed, size_t n, int8_t* out);
 void haar_from_gaussians(int d, const double* g, std::vector<double>* q);  // row-major
 void level_digits(const std::vector<float>& levels, uint32_t words[8], int* shift);
+uint16_t f32_to_f16(float f);
+float f16_to_f32(uint16_t h);
 
 // ---- kernel launchers (tq_encode.hip, tq_attn.hip, tq_gemm.hip) ----
 struct EncodeArgs {
