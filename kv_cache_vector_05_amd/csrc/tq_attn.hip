@@ -751,6 +751,11 @@ size_t decode_workspace_bytes(const tq_codebook* ck, const tq_codebook* cv, int6
     const int G = h_kv > 0 ? Hq / h_kv : 1;
     const int gt = group_tile(G);
     const int64_t bkg = (int64_t)B * h_kv * ((G + gt - 1) / gt);
+    if (decode_mfma_supported(ck, cv)) {
+        int nsplit = 1, split_len = 0;
+        decode_mfma_plan(B, Hq, h_kv, L_cap, &nsplit, &split_len);
+        return align256(qdigits_workspace_bytes(ck, (int64_t)rows)) + align256(rows * nsplit * (2 + d + mv) * 4);
+    }
     const int ns = decode_nsplit(bkg > 0 ? bkg : 1, L_cap);
     return align256(rows * (d + mk) * 4) + align256(rows * ns * (2 + d + mv) * 4);
 }
@@ -928,6 +933,27 @@ hipError_t launch_decode(const tq_codebook* ck, const tq_codebook* cv, const tq_
     const int G = a.Hq / a.h_kv;
     const int64_t rows = (int64_t)a.B * a.Hq;
     char* ws = static_cast<char*>(a.ws);
+    MergeK mk{};
+    mk.d = d;
+    mk.m = m;
+    mk.sigma = cv->dev.sigma;
+    mk.sketch = cv->dev.sketch;
+    mk.out = a.out;
+    if (decode_mfma_supported(ck, cv)) {
+        int nsplit = 1, split_len = 0;
+        decode_mfma_plan(a.B, a.Hq, a.h_kv, a.L_cap, &nsplit, &split_len);
+        const QDigits qd = carve_qdigits(ck, ws, rows);
+        float* part = reinterpret_cast<float*>(ws + align256(qdigits_workspace_bytes(ck, rows)));
+        hipError_t e = launch_qdigits(ck, a, qd, stream);
+        if (e != hipSuccess) return e;
+        e = launch_decode_mfma(ck, cv, k, v, a, qd, part, nsplit, split_len, stream);
+        if (e != hipSuccess) return e;
+        mk.part = part;
+        mk.nsplit = nsplit;
+        if (d == 64) hipLaunchKernelGGL(decode_merge_kernel<64>, dim3((unsigned)rows), dim3(256), 0, stream, mk);
+        else hipLaunchKernelGGL(decode_merge_kernel<128>, dim3((unsigned)rows), dim3(256), 0, stream, mk);
+        return hipGetLastError();
+    }
     float* qp = reinterpret_cast<float*>(ws);
     float* s = qp + rows * d;
     float* part = reinterpret_cast<float*>(ws + align256(rows * (d + m) * 4));
@@ -965,14 +991,8 @@ hipError_t launch_decode(const tq_codebook* ck, const tq_codebook* cv, const tq_
     hipLaunchKernelGGL(fn, dim3((unsigned)bkg, (unsigned)p.nsplit), dim3(256), lds, stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    MergeK mk{};
     mk.part = part;
     mk.nsplit = p.nsplit;
-    mk.d = d;
-    mk.m = m;
-    mk.sigma = cv->dev.sigma;
-    mk.sketch = cv->dev.sketch;
-    mk.out = a.out;
     if (d == 64) hipLaunchKernelGGL(decode_merge_kernel<64>, dim3((unsigned)rows), dim3(256), 0, stream, mk);
     else hipLaunchKernelGGL(decode_merge_kernel<128>, dim3((unsigned)rows), dim3(256), 0, stream, mk);
     return hipGetLastError();

@@ -110,6 +110,14 @@ hipError_t launch_qdigits(const tq_codebook* ck, const AttnArgs& a, const QDigit
 hipError_t launch_logits_mfma(const tq_codebook* ck, const tq_packed& k, const AttnArgs& a, const QDigits& q,
                               int k0, int klen, float* out, int64_t ld, int col0, hipStream_t stream);
 
+// Fused decode on the integer matrix cores (tq_decode.hip): partials of
+// [B*Hq][nsplit][2 + d + m] floats (max, sum, A_y, A_z) for the merge kernel.
+bool decode_mfma_supported(const tq_codebook* ck, const tq_codebook* cv);
+void decode_mfma_plan(int64_t B, int Hq, int h_kv, int L_cap, int* nsplit, int* split_len);
+hipError_t launch_decode_mfma(const tq_codebook* ck, const tq_codebook* cv, const tq_packed& k, const tq_packed& v,
+                              const AttnArgs& a, const QDigits& q, float* part, int nsplit, int split_len,
+                              hipStream_t stream);
+
 // C[M][N] = A[M][K] * B[N][K]^T (+ per-column scale if col_scale != nullptr),
 // fp32, row-major with leading dimensions lda/ldb/ldc (elements).
 hipError_t launch_gemm_nt(const float* A, int64_t lda, const float* B, int64_t ldb, float* C,

@@ -27,14 +27,11 @@
 #include <algorithm>
 #include <cmath>
 
+#include "tq_device.h"
 #include "tq_internal.h"
 
 namespace tq {
 namespace {
-
-typedef int intx4 __attribute__((ext_vector_type(4)));
-
-constexpr double kQjlD = 1.2533141373155003;  // sqrt(pi / 2)
 
 __device__ __forceinline__ int clamp_len2(const int32_t* seq_len, int b, int L_cap) {
     int s = seq_len[b];
@@ -209,37 +206,10 @@ struct LogM {
     int32_t lvl_shift;
 };
 
-// digit b of the levels of the 4 codes in the bytes of sel
-__device__ __forceinline__ uint32_t lut4(const uint32_t* tdig, int b, uint32_t sel) {
-    return __builtin_amdgcn_perm(tdig[2 * b + 1], tdig[2 * b], sel);
-}
-
-// v_perm selector for the 4 codes in the low 4*BITS bits of w: byte k = code k
-template <int BITS>
-__device__ __forceinline__ uint32_t code_sel(uint32_t w) {
-    if constexpr (BITS == 3) {
-        // even codes (bits 0-2, 6-8) and odd codes (3-5, 9-11) spread by
-        // multiplication; the partial products never overlap
-        return (((w & 0x1C7u) * 0x401u) & 0x70007u) | (((w & 0xE38u) * 0x8020u) & 0x7000700u);
-    } else if constexpr (BITS == 2) {
-        return (((w & 0x33u) * 0x1001u) & 0x30003u) | (((w & 0xCCu) * 0x40040u) & 0x3000300u);
-    } else {
-        return ((w & 0xFu) * 0x204081u) & 0x01010101u;
-    }
-}
-
-// bytes 0..3 of the result = bits 0..3 of x (as 0/1)
-__device__ __forceinline__ uint32_t spread4(uint32_t x) { return ((x & 0xFu) * 0x204081u) & 0x01010101u; }
-
 template <int D, int BITS, int NRT, int NCS>
 __global__ __launch_bounds__(256) void logits_mfma_kernel(LogM p) {
-    constexpr int LPG = D / 4;              // coordinates per lane group
-    constexpr int NC = LPG / 16;            // K=64 chunks over the coordinates
-    constexpr int CW = BITS * D / 32;       // code words per record
-    constexpr int BPG = BITS * LPG;         // code bits per lane group
-    constexpr bool ALIGNED = (BPG % 32) == 0;
-    constexpr int NW = ALIGNED ? BPG / 32 : (BPG + 31) / 32 + 1;
-
+    using T = dev::TileLogit<D, BITS, NRT, NCS>;
+    using Q = typename T::Q;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int n = lane & 15;
@@ -252,53 +222,18 @@ __global__ __launch_bounds__(256) void logits_mfma_kernel(LogM p) {
     const int64_t rowbase = (int64_t)b * p.Hq + (int64_t)kh * G;
     const int gq0 = grp * 4 * NRT;
 
-    // A operands: row (lane % 16) = (query (lane%16)/4, digit lane%4)
-    intx4 aq[NRT][NC];
-    intx4 as[NRT][NCS > 0 ? NCS : 1];
-    {
-        const int a = lane & 3;
-#pragma unroll
-        for (int rt = 0; rt < NRT; ++rt) {
-            const int g = gq0 + 4 * rt + ((lane & 15) >> 2);
-            const bool ok = g < G;
-            const int64_t drow = (rowbase + (ok ? g : 0)) * 4 + a;
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const intx4 v = *reinterpret_cast<const intx4*>(p.qd + drow * D + qk * LPG + 16 * c);
-                aq[rt][c] = ok ? v : intx4{0, 0, 0, 0};
-            }
-#pragma unroll
-            for (int cs = 0; cs < NCS; ++cs) {
-                const intx4 v = *reinterpret_cast<const intx4*>(p.sd + drow * p.sdw + (qk * NCS + cs) * 16);
-                as[rt][cs] = ok ? v : intx4{0, 0, 0, 0};
-            }
-        }
-    }
-    // output side: lane owns query gq0 + 4*rt + qk of each row tile
-    double qscale[NRT], sscale[NRT], ssum[NRT];
-    const double tscale = ldexp(1.0, -p.lvl_shift);
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-        const int g = gq0 + 4 * rt + qk;
-        const int64_t row = rowbase + (g < G ? g : 0);
-        qscale[rt] = ldexp(tscale, -(int)p.scale[row * 3 + 0]);
-        sscale[rt] = ldexp(1.0, -(int)p.scale[row * 3 + 1]);
-        ssum[rt] = (double)p.scale[row * 3 + 2];
-    }
-    const double cq = NCS > 0 ? kQjlD / (double)p.m : 0.0;
-    uint32_t tdig[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) tdig[i] = p.tdig[i];
+    T tl;
+    tl.init(p.qd, p.sd, p.scale, p.sdw, p.m, rowbase, gq0, G, p.tdig, p.lvl_shift, lane);
 
     const int sl = clamp_len2(p.seq_len, b, p.L_cap);
     const int kend = min(sl, p.k0 + p.klen);
     const int kbeg = p.k0 + (blockIdx.y * (blockDim.x >> 6) + wave) * p.tiles_per_wave * 16;
     // per-lane bases at the wave's first key; a tile advances them by 16 records
     const int64_t rec0 = bk * p.L_cap + kbeg;
-    const uint32_t* cbase = p.codes + rec0 * CW + ((BPG * qk) >> 5);
+    const uint32_t* cbase = p.codes + rec0 * Q::CW + Q::word0(qk);
     const int mw = p.m >> 5;
     const int per = p.m >> 2;  // sketch rows per lane group (8, 16, 32, ...)
-    const uint32_t* sbase = p.signs + rec0 * mw + ((qk * per) >> 5);
+    const uint32_t* sbase = p.signs + rec0 * mw;
     const float* nbase = p.norm + rec0;
     const float* gbase = p.rnorm + rec0;
     for (int tile = 0; tile < p.tiles_per_wave; ++tile) {
@@ -307,85 +242,14 @@ __global__ __launch_bounds__(256) void logits_mfma_kernel(LogM p) {
         const int key = key0 + n;
         const bool kv = key < kend;
         const int kk = min(key, kend - 1) - kbeg;  // record offset of this lane's key from kbeg
-
-        // this lane's code bits: [BPG*qk, BPG*(qk+1)) of the record
-        uint32_t W[NW];
-        {
-            const uint32_t* cp = cbase + kk * CW;
-            if constexpr (ALIGNED) {
-#pragma unroll
-                for (int i = 0; i < NW; ++i) W[i] = cp[i];
-            } else {
-                const int w0 = (BPG * qk) >> 5;
-#pragma unroll
-                for (int i = 0; i < NW; ++i) W[i] = cp[min(i, CW - 1 - w0)];
-                const int sh = (BPG * qk) & 31;
-#pragma unroll
-                for (int i = 0; i + 1 < NW; ++i) W[i] = __builtin_amdgcn_alignbit(W[i + 1], W[i], sh);
-            }
-        }
-        // B operands: digit b of t[c] for the lane's 16 coordinates of chunk c
-        intx4 bd[NC][3];
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-#pragma unroll
-            for (int sg = 0; sg < 4; ++sg) {
-                const int o = BITS * (16 * c + 4 * sg);  // bit offset of the 4 codes
-                const uint32_t lo = W[o >> 5];
-                const uint32_t hi = ((o >> 5) + 1 < NW) ? W[(o >> 5) + 1] : 0u;
-                const uint32_t w = __builtin_amdgcn_alignbit(hi, lo, o & 31);
-                const uint32_t sel = code_sel<BITS>(w);
-#pragma unroll
-                for (int bb = 0; bb < 3; ++bb) bd[c][bb][sg] = (int)lut4(tdig, bb, sel);
-            }
-        }
-        // sign bits as 0/1 bytes: lane group qk holds sketch rows [qk*m/4, (qk+1)*m/4)
-        intx4 bz[NCS > 0 ? NCS : 1];
-        if constexpr (NCS > 0) {
-#pragma unroll
-            for (int cs = 0; cs < NCS; ++cs) {
-                const int bit0 = qk * per + 16 * cs;
-                uint32_t x = sbase[kk * mw + ((bit0 >> 5) - ((qk * per) >> 5))] >> (bit0 & 31);
-                if (per - 16 * cs < 16) x &= (1u << (per - 16 * cs)) - 1u;  // fewer than 16 rows left
-                bz[cs][0] = (int)spread4(x);
-                bz[cs][1] = (int)spread4(x >> 4);
-                bz[cs][2] = (int)spread4(x >> 8);
-                bz[cs][3] = (int)spread4(x >> 12);
-            }
-        }
         const float nu = nbase[kk];
         const float gm = NCS > 0 ? gbase[kk] : 0.0f;
+        double lg[NRT];
+        tl.compute(cbase + kk * Q::CW, sbase + kk * mw, gm, per, lane, lg);
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
-            intx4 acc[3];
-#pragma unroll
-            for (int bb = 0; bb < 3; ++bb) acc[bb] = intx4{0, 0, 0, 0};
-#pragma unroll
-            for (int c = 0; c < NC; ++c)
-#pragma unroll
-                for (int bb = 0; bb < 3; ++bb)
-                    acc[bb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[rt][c], bd[c][bb], acc[bb], 0, 0, 0);
-            intx4 accz = intx4{0, 0, 0, 0};
-#pragma unroll
-            for (int cs = 0; cs < NCS; ++cs)
-                accz = __builtin_amdgcn_mfma_i32_16x16x64_i8(as[rt][cs], bz[cs], accz, 0, 0, 0);
-            // acc[b][a]: digit a of q' (weight 2^(7(3-a))) times digit b of t
-            // (weight 2^(8(2-b))); |acc| <= 128 * 64 * 128 = 2^20
-            double V = 0.0;
-#pragma unroll
-            for (int bb = 0; bb < 3; ++bb) {
-                const double h = (double)(acc[bb][0] * 128 + acc[bb][1]);  // |.| < 2^28: exact in int32
-                const double l = (double)(acc[bb][2] * 128 + acc[bb][3]);
-                V = V * 256.0 + (h * 16384.0 + l);
-            }
-            double logit = V * qscale[rt];
-            if constexpr (NCS > 0) {
-                const double Z = ((double)accz[0] * 2097152.0 + (double)accz[1] * 16384.0) +
-                                 ((double)accz[2] * 128.0 + (double)accz[3]);
-                logit += cq * (double)gm * (2.0 * Z * sscale[rt] - ssum[rt]);
-            }
             const int g = gq0 + 4 * rt + qk;
-            if (kv && g < G) p.out[(rowbase + g) * p.ld + (key - p.col0)] = (float)((double)nu * logit);
+            if (kv && g < G) p.out[(rowbase + g) * p.ld + (key - p.col0)] = (float)((double)nu * lg[rt]);
         }
     }
 }
