@@ -25,6 +25,7 @@
 #include <algorithm>
 #include <cmath>
 
+#include "tq_device.h"
 #include "tq_internal.h"
 
 namespace tq {
@@ -159,10 +160,7 @@ struct LogK {
 
 template <int D, int BITS>
 __device__ __forceinline__ uint32_t code_at(const uint32_t* cw, int i) {
-    const int bp = BITS * i;
-    uint32_t c = cw[bp >> 5] >> (bp & 31);
-    if ((bp & 31) + BITS > 32) c |= cw[(bp >> 5) + 1] << (32 - (bp & 31));
-    return c & ((1u << BITS) - 1u);
+    return dev::code_get(cw, dev::code_loc(i, BITS), BITS);
 }
 
 template <int D, int BITS, int GT>
@@ -360,12 +358,8 @@ __global__ __launch_bounds__(256) void dense_dequant_kernel(DenseScan p) {
         const int64_t n = p.rec0 + p.k0 + r;
         const uint32_t* c = p.codes + n * cw;
         float* dst = p.aug + r * width;
-        for (int i = threadIdx.x; i < p.d; i += blockDim.x) {
-            const int bp = p.bits * i;
-            uint32_t v = c[bp >> 5] >> (bp & 31);
-            if ((bp & 31) + p.bits > 32) v |= c[(bp >> 5) + 1] << (32 - (bp & 31));
-            dst[i] = p.levels[v & mask];
-        }
+        for (int i = threadIdx.x; i < p.d; i += blockDim.x)
+            dst[i] = p.levels[dev::code_get(c, dev::code_loc(i, p.bits), p.bits) & mask];
         if (p.m) {
             const float g = cq * p.rnorm[n];
             const uint32_t* sg = p.signs + n * mw;
@@ -464,9 +458,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecK p) {
     // coordinate role of this thread in the value accumulation
     const bool ycoord = t < D;
     const bool zcoord = !ycoord && t < D + m;
-    const int bp = BITS * (ycoord ? t : 0);
-    const int cwi = bp >> 5, cof = bp & 31;
-    const bool straddle = cof + BITS > 32;
+    const dev::CodeLoc cl = dev::code_loc(ycoord ? t : 0, BITS);
     const int zl = t - D;
     float acc[GT];
 #pragma unroll
@@ -551,9 +543,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecK p) {
         const int cnt = min(256, c1 - base);
         if (ycoord) {
             for (int jj = 0; jj < cnt; ++jj) {
-                uint32_t c = vc[jj * CW + cwi] >> cof;
-                if (straddle) c |= vc[jj * CW + cwi + 1] << (32 - cof);
-                const float y = lvv[c & ((1u << BITS) - 1u)];
+                const float y = lvv[dev::code_get(vc + jj * CW, cl, BITS)];
 #pragma unroll
                 for (int g = 0; g < GT; ++g) acc[g] = fmaf(pv[jj * GT + g], y, acc[g]);
             }
@@ -590,33 +580,62 @@ struct MergeK {
 
 // log-sum-exp merge of the splits, then back to the original domain:
 // out = sigma * H (A_y + sqrt(pi/2)/m S^T A_z) / (sqrt(d) l)
+// The split maxima are read by all threads at once (one round trip), the
+// column sums are unrolled so their loads are in flight together.
 template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(MergeK p) {
+    __shared__ float fw[256];  // exp(M_s - M) of the current batch of splits
+    __shared__ float red[8];
     __shared__ float w[D];
     __shared__ float az[D];
     const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
     const int64_t row = blockIdx.x;
     const int width = 2 + D + p.m;
     const float* base = p.part + row * p.nsplit * width;
     float mx = -INFINITY;
-    for (int s = 0; s < p.nsplit; ++s) mx = fmaxf(mx, base[s * width]);
-    float l = 0.f, ay = 0.f, z = 0.f;
-    if (mx != -INFINITY) {
-        for (int s = 0; s < p.nsplit; ++s) {
-            const float ms = base[s * width];
-            if (ms == -INFINITY) continue;
-            const float f = expf(ms - mx);
-            l += f * base[s * width + 1];
-            if (t < D) ay += f * base[s * width + 2 + t];
-            if (t < p.m) z += f * base[s * width + 2 + D + t];
+    for (int s = t; s < p.nsplit; s += 256) mx = fmaxf(mx, base[(int64_t)s * width]);
+    mx = wave_max(mx);
+    if (lane == 0) red[wave] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    float l = 0.f, acc = 0.f;
+    const bool col = t < D + p.m;
+    for (int s0 = 0; s0 < p.nsplit; s0 += 256) {
+        const int cnt = min(256, p.nsplit - s0);
+        float lw = 0.f;
+        if (t < cnt) {
+            const float ms = base[(int64_t)(s0 + t) * width];
+            const float f = (ms == -INFINITY || mx == -INFINITY) ? 0.f : expf(ms - mx);
+            fw[t] = f;
+            lw = f * base[(int64_t)(s0 + t) * width + 1];
         }
+        lw = wave_sum(lw);
+        if (lane == 0) red[4 + wave] = lw;
+        __syncthreads();
+        l += (red[4] + red[5]) + (red[6] + red[7]);
+        if (col) {
+            const float* src = base + (int64_t)s0 * width + 2 + t;
+            int s = 0;
+            for (; s + 8 <= cnt; s += 8) {
+                float v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v[u] = src[(int64_t)(s + u) * width];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) acc = fmaf(fw[s + u], v[u], acc);
+            }
+            for (; s < cnt; ++s) acc = fmaf(fw[s], src[(int64_t)s * width], acc);
+        }
+        __syncthreads();
     }
-    if (t < p.m) az[t] = z;
+    // (empty splits have weight 0 and all-zero columns, written by the split kernels)
+    if (t >= D && col) az[t - D] = acc;
     __syncthreads();
     if (t < D) {
         float corr = 0.f;
         for (int k = 0; k < p.m; ++k) corr = fmaf(p.sketch[(int64_t)k * D + t], az[k], corr);
-        w[t] = ay + (p.m ? kQjl / (float)p.m : 0.f) * corr;
+        w[t] = acc + (p.m ? kQjl / (float)p.m : 0.f) * corr;
     }
     __syncthreads();
     for (int s = 1; s < D; s <<= 1) {

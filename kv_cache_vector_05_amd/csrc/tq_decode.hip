@@ -136,14 +136,10 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
     const int sl = dev::clamp_len(p.seq_len, b, p.L_cap);
     const int c0 = split * p.split_len;
     const int c1 = min(c0 + p.split_len, sl);
-    if (c0 >= c1) {  // empty split: the merge skips it
-        if (threadIdx.x < 4 * NRT) {
-            const int g = gq0 + threadIdx.x;
-            if (g < G) {
-                float* dst = p.part + ((rowbase + g) * p.nsplit + split) * width;
-                dst[0] = -INFINITY;
-                dst[1] = 0.f;
-            }
+    if (c0 >= c1) {  // empty split: weight 0 in the merge, all-zero columns
+        for (int i = threadIdx.x; i < 4 * NRT * width; i += blockDim.x) {
+            const int g = gq0 + i / width, c = i % width;
+            if (g < G) p.part[((rowbase + g) * p.nsplit + split) * width + c] = c == 0 ? -INFINITY : 0.f;
         }
         return;
     }
@@ -167,8 +163,10 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
                 const int64_t rec = rec_base + min(key, c1 - 1);
                 const float nu = p.k_norm[rec];
                 const float gm = M > 0 ? p.k_rnorm[rec] : 0.f;
+                typename TL::Raw raw;
+                TL::load(p.k_codes + rec * Q::CW + Q::word0(qk), p.k_signs + rec * MW, PER, lane, raw);
                 double lg[NRT];
-                tl.compute(p.k_codes + rec * Q::CW + Q::word0(qk), p.k_signs + rec * MW, gm, PER, lane, lg);
+                tl.compute(raw, gm, PER, lane, lg);
 #pragma unroll
                 for (int rt = 0; rt < NRT; ++rt)
                     a[rt] = valid ? (float)((double)p.scale * (double)nu * lg[rt]) : -INFINITY;
@@ -263,7 +261,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
         for (int j = 0; j < CBW; ++j) {
             uint32_t sel[4];
 #pragma unroll
-            for (int sg = 0; sg < 4; ++sg) sel[sg] = Q::sel(W, 4 * j + sg);
+            for (int sg = 0; sg < 4; ++sg) sel[sg] = Q::sel(W, 4 * j + sg, qk);
 #pragma unroll
             for (int bb = 0; bb < 3; ++bb) {
                 intx4 v;

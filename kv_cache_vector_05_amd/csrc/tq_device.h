@@ -48,6 +48,38 @@ __device__ __forceinline__ uint32_t code_sel(uint32_t w) {
     }
 }
 
+// Where coordinate i's code sits in a record's code words: its low n0 bits
+// at word w0 from bit s0, the rest (if n0 < bits) at word w1 from bit s1.
+//  * 1, 2 and 4 bits: bits [b*i, b*i+b) of the LSB-first bit string.
+//  * 3 bits: groups of 32 coordinates in three words W0..W2.  Coordinate
+//    j < 24 of a group takes bits 8(j%4) + 3((j%8)/4) .. +2 of W_{j/8} (two
+//    whole codes per byte); for j = 24 + r the low two bits sit at bit
+//    8(r%4) + 6 of W_{r/4} and the high bit at bit 8(r%4) + 6 + r/4 of W2.
+//    A byte-wise mask then yields four codes at once (see Quarter::sel).
+struct CodeLoc {
+    int w0, s0, n0, w1, s1;
+};
+__host__ __device__ constexpr CodeLoc code_loc(int i, int bits) {
+    if (bits == 3) {
+        const int g = i >> 5, j = i & 31;
+        if (j < 24) return CodeLoc{3 * g + (j >> 3), 8 * (j & 3) + 3 * ((j & 7) >> 2), 3, 0, 0};
+        const int r = j - 24;
+        return CodeLoc{3 * g + (r >> 2), 8 * (r & 3) + 6, 2, 3 * g + 2, 8 * (r & 3) + 6 + (r >> 2)};
+    }
+    const int bp = bits * i, s0 = bp & 31;
+    return CodeLoc{bp >> 5, s0, (32 - s0) < bits ? (32 - s0) : bits, (bp >> 5) + 1, 0};
+}
+__host__ __device__ inline uint32_t code_get(const uint32_t* cw, const CodeLoc& L, int bits) {
+    uint32_t c = (cw[L.w0] >> L.s0) & ((1u << L.n0) - 1u);
+    if (L.n0 < bits) c |= ((cw[L.w1] >> L.s1) & ((1u << (bits - L.n0)) - 1u)) << L.n0;
+    return c;
+}
+// ORs code c (< 2^bits) into zero-initialised words
+__host__ __device__ inline void code_put(uint32_t* cw, const CodeLoc& L, int bits, uint32_t c) {
+    cw[L.w0] |= (L.n0 == bits ? c : (c & ((1u << L.n0) - 1u))) << L.s0;
+    if (L.n0 < bits) cw[L.w1] |= (c >> L.n0) << L.s1;
+}
+
 // bytes 0..3 of the result = bits 0..3 of x (as 0/1)
 __device__ __forceinline__ uint32_t spread4(uint32_t x) { return ((x & 0xFu) * 0x204081u) & 0x01010101u; }
 
@@ -55,21 +87,26 @@ __device__ __forceinline__ uint32_t spread4(uint32_t x) { return ((x & 0xFu) * 0
 __device__ __forceinline__ uint32_t spread4_pm(uint32_t x) { return 0xFFFFFFFFu ^ (spread4(x) * 0xFEu); }
 
 // Code bits of one lane's coordinate quarter [qk*D/4, (qk+1)*D/4) of a
-// record, shifted so that coordinate qk*D/4 starts at bit 0 of W[0].
+// record, and the v_perm selectors (byte u = code of coordinate 4g + u of
+// the quarter) built from them.
 template <int D, int BITS>
 struct Quarter {
-    static constexpr int LPG = D / 4;           // coordinates per quarter
-    static constexpr int CW = BITS * D / 32;    // code words per record
-    static constexpr int BPG = BITS * LPG;      // code bits per quarter
+    static constexpr int LPG = D / 4;         // coordinates per quarter
+    static constexpr int CW = BITS * D / 32;  // code words per record
+    static constexpr int BPG = BITS * LPG;    // code bits per quarter
     static constexpr bool ALIGNED = (BPG % 32) == 0;
-    static constexpr int NW = ALIGNED ? BPG / 32 : (BPG + 31) / 32 + 1;
+    // 3 bits: the whole 32-coordinate group holding the quarter
+    static constexpr int NW = BITS == 3 ? 3 : (ALIGNED ? BPG / 32 : (BPG + 31) / 32 + 1);
 
-    // offset (words) of the quarter's first word within a record
-    __device__ static int word0(int qk) { return (BPG * qk) >> 5; }
+    // offset (words) of the first word the lane loads
+    __device__ static int word0(int qk) {
+        if constexpr (BITS == 3) return 3 * ((LPG * qk) >> 5);
+        return (BPG * qk) >> 5;
+    }
 
     // cp points at word word0(qk) of the record
     __device__ static void load(const uint32_t* cp, int qk, uint32_t W[NW]) {
-        if constexpr (ALIGNED) {
+        if constexpr (BITS == 3 || ALIGNED) {
 #pragma unroll
             for (int i = 0; i < NW; ++i) W[i] = cp[i];
         } else {
@@ -82,12 +119,34 @@ struct Quarter {
         }
     }
 
-    // v_perm selector of coordinates 4*g .. 4*g+3 of the quarter
-    __device__ static uint32_t sel(const uint32_t W[NW], int g) {
-        const int o = BITS * 4 * g;
-        const uint32_t lo = W[o >> 5];
-        const uint32_t hi = ((o >> 5) + 1 < NW) ? W[(o >> 5) + 1] : 0u;
-        return code_sel<BITS>(__builtin_amdgcn_alignbit(hi, lo, o & 31));
+    // selector t (0..7) of a 3-bit group: codes of coordinates 4t .. 4t+3
+    __device__ static uint32_t group_sel(const uint32_t W[3], int t) {
+        constexpr uint32_t M3 = 0x07070707u, M2 = 0x03030303u, M1 = 0x04040404u;
+        switch (t) {
+            case 0: return W[0] & M3;
+            case 1: return (W[0] >> 3) & M3;
+            case 2: return W[1] & M3;
+            case 3: return (W[1] >> 3) & M3;
+            case 4: return W[2] & M3;
+            case 5: return (W[2] >> 3) & M3;
+            case 6: return ((W[0] >> 6) & M2) | ((W[2] >> 4) & M1);
+            default: return ((W[1] >> 6) & M2) | ((W[2] >> 5) & M1);
+        }
+    }
+
+    // v_perm selector of coordinates 4g .. 4g+3 of the quarter
+    __device__ static uint32_t sel(const uint32_t W[NW], int g, int qk) {
+        if constexpr (BITS == 3) {
+            if constexpr (LPG == 32) return group_sel(W, g);
+            // half a group: quarters with odd qk hold coordinates 16..31
+            const uint32_t lo = group_sel(W, g), hi = group_sel(W, 4 + g);
+            return (qk & 1) ? hi : lo;
+        } else {
+            const int o = BITS * 4 * g;
+            const uint32_t lo = W[o >> 5];
+            const uint32_t hi = ((o >> 5) + 1 < NW) ? W[(o >> 5) + 1] : 0u;
+            return code_sel<BITS>(__builtin_amdgcn_alignbit(hi, lo, o & 31));
+        }
     }
 };
 
@@ -175,19 +234,30 @@ struct TileLogit {
         for (int i = 0; i < 8; ++i) tdig[i] = lvl_digits[i];
     }
 
-    // cp: the lane's code words (word Q::word0(qk) of its key's record);
-    // sp: the key's sign words; per = m / 4 sketch rows per lane group;
-    // out[rt] = <q', t[c]> + sqrt(pi/2)/m gamma <s, z>  (not yet times nu)
-    __device__ void compute(const uint32_t* cp, const uint32_t* sp, float gm, int per, int lane, double out[NRT]) const {
-        const int qk = lane >> 4;
+    // The lane's share of one key record, loaded ahead of its use so that a
+    // tile's loads can be in flight while the previous tile computes.
+    struct Raw {
         uint32_t W[Q::NW];
-        Q::load(cp, qk, W);
+        uint32_t sg;  // the sign word holding the lane's sketch rows (m <= 128)
+    };
+
+    // cp: word Q::word0(qk) of the key's code words; sp: the key's sign words;
+    // per = m / 4 sketch rows per lane group
+    __device__ static void load(const uint32_t* cp, const uint32_t* sp, int per, int lane, Raw& r) {
+        const int qk = lane >> 4;
+        Q::load(cp, qk, r.W);
+        r.sg = NCS > 0 ? sp[(qk * per) >> 5] : 0u;
+    }
+
+    // out[rt] = <q', t[c]> + sqrt(pi/2)/m gamma <s, z>  (not yet times nu)
+    __device__ void compute(const Raw& r, float gm, int per, int lane, double out[NRT]) const {
+        const int qk = lane >> 4;
         intx4 bd[NC][3];
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
 #pragma unroll
             for (int sg = 0; sg < 4; ++sg) {
-                const uint32_t sel = Q::sel(W, 4 * c + sg);
+                const uint32_t sel = Q::sel(r.W, 4 * c + sg, qk);
 #pragma unroll
                 for (int bb = 0; bb < 3; ++bb) bd[c][bb][sg] = (int)lut4(tdig, bb, sel);
             }
@@ -196,8 +266,8 @@ struct TileLogit {
         if constexpr (NCS > 0) {
 #pragma unroll
             for (int cs = 0; cs < NCS; ++cs) {
-                const int bit0 = qk * per + 16 * cs;
-                uint32_t x = sp[bit0 >> 5] >> (bit0 & 31);
+                const int bit0 = qk * per + 16 * cs;  // within the word loaded into r.sg
+                uint32_t x = r.sg >> (bit0 & 31);
                 if (per - 16 * cs < 16) x &= (1u << (per - 16 * cs)) - 1u;  // fewer than 16 rows left
                 bz[cs][0] = (int)spread4(x);
                 bz[cs][1] = (int)spread4(x >> 4);

@@ -24,6 +24,7 @@
 // caller's workspace, with per-vector quantise and sign-pack kernels between.
 #include <hip/hip_runtime.h>
 
+#include "tq_device.h"
 #include "tq_internal.h"
 
 namespace tq {
@@ -64,67 +65,73 @@ __device__ __forceinline__ Swap swap32(float v) {
     return {__uint_as_float(r[0]), __uint_as_float(r[1])};
 }
 
-// branch-free select of a or b by a lane mask (all ones or all zeros)
-__device__ __forceinline__ float msel(uint32_t m, float a, float b) {
-    return __uint_as_float((__float_as_uint(a) & m) | (__float_as_uint(b) & ~m));
+// lanes l and l ^ 32 trade one register each (v_permlane32_swap): afterwards
+// the lower lanes hold (own a, upper partner's a) and the upper lanes (lower
+// partner's b, own b) - a 2x2 transpose between the lane half and the
+// register pair (a, b)
+__device__ __forceinline__ void xchg(float& a, float& b) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
 }
-__device__ __forceinline__ uint32_t mask_of(bool c) { return c ? 0xFFFFFFFFu : 0u; }
 
-// c = #{j : y >= tau_j} by binary search over the sorted thresholds, and
-// the matching level.  th/lv hold the thresholds and levels (uniform).
+// Quantiser for a symmetric table (t_{K-1-k} = -t_k, tau_{K-2-k} = -tau_k,
+// tau_{K/2-1} = 0; the host builds the upper half and mirrors it, so this
+// holds exactly).  c = #{j : y >= tau_j} is found as the code c' of |y| among
+// the upper thresholds, mirrored for y < 0 (there a tie |y| = tau goes to
+// the other side, a decision within rounding of the boundary).  Returns the
+// code and the residual e = y - t_c = sign(y) (|y| - t_{K/2+c'}).
+// pt: the K/2-1 upper thresholds, pl: the K/2 upper levels (scaled).
+//
+// Comparisons of non-negative floats are made on their bit patterns as
+// integers (same order), giving all-ones/all-zeros lane masks in vector
+// registers: no compare masks pile up in scalar registers.
+__device__ __forceinline__ uint32_t below(float a, float t) {  // a < t ? ~0 : 0, for a, t >= 0
+    return (uint32_t)(((int32_t)__float_as_uint(a) - (int32_t)__float_as_uint(t)) >> 31);
+}
+__device__ __forceinline__ float pick(uint32_t m, float if_set, float if_clear) {
+    return __uint_as_float((__float_as_uint(if_set) & m) | (__float_as_uint(if_clear) & ~m));
+}
+
 template <int BITS>
-__device__ __forceinline__ uint32_t quantise(float y, const float* th, const float* lv, float* level) {
+__device__ __forceinline__ uint32_t quantise(float y, const float* pt, const float* pl, float* e) {
+    constexpr uint32_t K1 = (1u << BITS) - 1u;
+    const float a = fabsf(y);
+    uint32_t lowbits;  // bits of c' cleared (all-ones mask bits of "below")
+    float lv;
     if constexpr (BITS == 1) {
-        const bool c0 = y >= th[0];
-        *level = c0 ? lv[1] : lv[0];
-        return c0 ? 1u : 0u;
+        lowbits = 0u;
+        lv = pl[0];
     } else if constexpr (BITS == 2) {
-        const uint32_t m1 = mask_of(y >= th[1]);
-        const uint32_t m0 = mask_of(y >= msel(m1, th[2], th[0]));
-        *level = msel(m0, msel(m1, lv[3], lv[1]), msel(m1, lv[2], lv[0]));
-        return (m1 & 2u) | (m0 & 1u);
+        const uint32_t n0 = below(a, pt[0]);
+        lowbits = n0 & 1u;
+        lv = pick(n0, pl[0], pl[1]);
     } else if constexpr (BITS == 3) {
-        const uint32_t m2 = mask_of(y >= th[3]);
-        const uint32_t m1 = mask_of(y >= msel(m2, th[5], th[1]));
-        const float tb = msel(m1, msel(m2, th[6], th[2]), msel(m2, th[4], th[0]));
-        const uint32_t m0 = mask_of(y >= tb);
-        *level = 0.0f;  // looked up four at a time by the caller
-        return (m2 & 4u) | (m1 & 2u) | (m0 & 1u);
+        const uint32_t n1 = below(a, pt[1]);
+        const uint32_t n0 = below(a, pick(n1, pt[0], pt[2]));
+        lowbits = (n1 & 2u) | (n0 & 1u);
+        lv = pick(n0, pick(n1, pl[0], pl[2]), pick(n1, pl[1], pl[3]));
     } else {
-        uint32_t c = 0;
-        float l = lv[0];
-#pragma unroll
-        for (int k = 0; k < 15; ++k) {
-            const bool ge = y >= th[k];
-            c = ge ? (uint32_t)(k + 1) : c;
-            l = ge ? lv[k + 1] : l;
-        }
-        *level = l;
-        return c;
+        const uint32_t n2 = below(a, pt[3]);
+        const uint32_t n1 = below(a, pick(n2, pt[1], pt[5]));
+        const uint32_t n0 = below(a, pick(n1, pick(n2, pt[0], pt[4]), pick(n2, pt[2], pt[6])));
+        lowbits = (n2 & 4u) | (n1 & 2u) | (n0 & 1u);
+        const float q0 = pick(n2, pl[0], pl[4]), q1 = pick(n2, pl[1], pl[5]);
+        const float q2 = pick(n2, pl[2], pl[6]), q3 = pick(n2, pl[3], pl[7]);
+        lv = pick(n0, pick(n1, q0, q2), pick(n1, q1, q3));
     }
-}
-
-// fp32 levels of 4 codes (selector bytes) from byte-plane tables: plane k
-// holds byte k of the 8 levels (two words per plane)
-__device__ __forceinline__ void levels4(const uint32_t* bp, uint32_t sel, float out[4]) {
-    const uint32_t p0 = __builtin_amdgcn_perm(bp[1], bp[0], sel);
-    const uint32_t p1 = __builtin_amdgcn_perm(bp[3], bp[2], sel);
-    const uint32_t p2 = __builtin_amdgcn_perm(bp[5], bp[4], sel);
-    const uint32_t p3 = __builtin_amdgcn_perm(bp[7], bp[6], sel);
-    const uint32_t a01 = __builtin_amdgcn_perm(p1, p0, 0x05010400u);  // L0.b0 L0.b1 L1.b0 L1.b1
-    const uint32_t a23 = __builtin_amdgcn_perm(p3, p2, 0x05010400u);  // L0.b2 L0.b3 L1.b2 L1.b3
-    const uint32_t b01 = __builtin_amdgcn_perm(p1, p0, 0x07030602u);  // L2.b0 L2.b1 L3.b0 L3.b1
-    const uint32_t b23 = __builtin_amdgcn_perm(p3, p2, 0x07030602u);
-    out[0] = __uint_as_float(__builtin_amdgcn_perm(a23, a01, 0x05040100u));
-    out[1] = __uint_as_float(__builtin_amdgcn_perm(a23, a01, 0x07060302u));
-    out[2] = __uint_as_float(__builtin_amdgcn_perm(b23, b01, 0x05040100u));
-    out[3] = __uint_as_float(__builtin_amdgcn_perm(b23, b01, 0x07060302u));
+    const uint32_t yb = __float_as_uint(y);
+    const uint32_t neg = (uint32_t)((int32_t)yb >> 31);
+    *e = __uint_as_float(__float_as_uint(a - lv) ^ (yb & 0x80000000u));
+    // y >= 0: K/2 + c' = K1 ^ lowbits;  y < 0: K/2 - 1 - c' = lowbits
+    return lowbits ^ (~neg & K1);
 }
 
 template <int D, int BITS, int M, bool BF16>
 __global__ __launch_bounds__(256) void encode_rht_kernel(EncK p) {
     constexpr int HALF = D / 2;
-    constexpr int K = 1 << BITS;
+    constexpr int QTR = D / 4;
+    constexpr int KH = 1 << (BITS - 1);
     constexpr int CW = BITS * D / 32;     // code words per record
     constexpr int WH = BITS * HALF / 32;  // code words per half
     constexpr int NRB = M / 32;           // sketch row blocks (= sign words)
@@ -133,49 +140,32 @@ __global__ __launch_bounds__(256) void encode_rht_kernel(EncK p) {
     // residuals enter the sketch scaled by 2^8 so their fp16 low parts stay normal
     constexpr float ESCALE = 256.0f;
     __shared__ half8 s_sk[SKN];
+    // Hadamard sign flips as sign-bit masks, in the register order that
+    // follows the first lane exchange: lane half hh, register a*QTR + t holds
+    // coordinate a*HALF + hh*QTR + t
+    __shared__ uint4 s_flip[2 * HALF / 4];
 
     if constexpr (M > 0) {
         const half8* src = reinterpret_cast<const half8*>(p.sketch_mfma);
         for (int i = threadIdx.x; i < SKN; i += blockDim.x) s_sk[i] = src[i];
+    }
+    for (int i = threadIdx.x; i < 2 * HALF; i += blockDim.x) {
+        const int hh = i / HALF, r = i % HALF;
+        const int coord = (r / QTR) * HALF + hh * QTR + (r % QTR);
+        reinterpret_cast<uint32_t*>(s_flip)[i] = p.sigma[coord] < 0.0f ? 0x80000000u : 0u;
     }
     __syncthreads();
 
     const int lane = threadIdx.x & 63;
     const int v = lane & 31;
     const int h = lane >> 5;
-    const float hs = h ? -1.0f : 1.0f;  // last butterfly: h = 0 keeps a + b, h = 1 keeps a - b
 
-    // Hadamard sign masks, bit j of word w flips coordinate h*HALF + 32w + j.
-    // Kept in LDS and re-read per tile: held in registers, the compiler would
-    // hoist one expanded mask per coordinate out of the tile loop.
-    __shared__ uint32_t s_flip[2 * (HALF / 32)];
-    if (threadIdx.x < 2 * (HALF / 32)) {
-        const int hh = threadIdx.x / (HALF / 32), w = threadIdx.x % (HALF / 32);
-        uint32_t mask = 0;
-        for (int j = 0; j < 32; ++j) mask |= (p.sigma[hh * HALF + w * 32 + j] < 0.0f ? 1u : 0u) << j;
-        s_flip[threadIdx.x] = mask;
-    }
-    __syncthreads();
-    float lv[K], th[K - 1];
+    // upper halves of the symmetric tables, scaled
+    float pt[KH > 1 ? KH - 1 : 1], pl[KH];
 #pragma unroll
-    for (int k = 0; k < K; ++k) lv[k] = p.levels[k] * ESCALE;
+    for (int k = 0; k + 1 < KH; ++k) pt[k] = p.thresholds[KH + k] * ESCALE;
 #pragma unroll
-    for (int k = 0; k < K - 1; ++k) th[k] = p.thresholds[k] * ESCALE;
-    // byte planes of the (scaled) levels for four-at-a-time lookups (3 bits)
-    uint32_t bp[8];
-    if constexpr (BITS == 3) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                w0 |= ((__float_as_uint(lv[c]) >> (8 * k)) & 0xFFu) << (8 * c);
-                w1 |= ((__float_as_uint(lv[c + 4]) >> (8 * k)) & 0xFFu) << (8 * c);
-            }
-            bp[2 * k] = w0;
-            bp[2 * k + 1] = w1;
-        }
-    }
+    for (int k = 0; k < KH; ++k) pl[k] = p.levels[KH + k] * ESCALE;
     const float yscale = ESCALE / sqrtf((float)D);
 
     const int64_t wave_stride = (int64_t)gridDim.x * (blockDim.x >> 6);
@@ -188,6 +178,7 @@ __global__ __launch_bounds__(256) void encode_rht_kernel(EncK p) {
         const int token = tb * 32 + v;
         const bool valid = token < p.n_tok;
 
+        // lane half h reads coordinates [h*HALF, (h+1)*HALF): register j = coordinate h*HALF + j
         float x[HALF];
         if (valid) {
             const int64_t off = (int64_t)seq * p.s_seq + (int64_t)token * p.s_tok + (int64_t)head * p.s_head + h * HALF;
@@ -222,23 +213,29 @@ __global__ __launch_bounds__(256) void encode_rht_kernel(EncK p) {
         }
 
         __builtin_amdgcn_sched_barrier(0);
-        // RoPE (keys): pair (i, i + D/2) is (lane half 0, lane half 1) at the same j
+        // exchange the upper quarter of each lane half: register a*QTR + t of
+        // lane half h now holds coordinate a*HALF + h*QTR + t, so the RoPE pair
+        // (i, i + D/2) and coordinate bit log2(HALF) are within a lane
+#pragma unroll
+        for (int t = 0; t < QTR; ++t) xchg(x[t], x[t + QTR]);
+
+        // RoPE (keys): pair (i, i + D/2), i = h*QTR + t, is registers (t, t + QTR)
         if (p.rope_cos) {
             const int pos = p.tok_offset + (valid ? token : 0);
-            const float4* cp = reinterpret_cast<const float4*>(p.rope_cos + (int64_t)pos * HALF);
-            const float4* sp = reinterpret_cast<const float4*>(p.rope_sin + (int64_t)pos * HALF);
+            const float4* cp = reinterpret_cast<const float4*>(p.rope_cos + (int64_t)pos * HALF + h * QTR);
+            const float4* sp = reinterpret_cast<const float4*>(p.rope_sin + (int64_t)pos * HALF + h * QTR);
 #pragma unroll
-            for (int c = 0; c < HALF / 4; ++c) {
+            for (int c = 0; c < QTR / 4; ++c) {
                 const float4 cc = cp[c];
                 const float4 ss = sp[c];
                 const float cs[4] = {cc.x, cc.y, cc.z, cc.w};
                 const float sn[4] = {ss.x, ss.y, ss.z, ss.w};
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const int j = 4 * c + u;
-                    const Swap sw = swap32(x[j]);
-                    const float other = h ? sw.r0 : sw.r1;
-                    x[j] = fmaf(x[j], cs[u], -hs * (other * sn[u]));
+                    const int t = 4 * c + u;
+                    const float lo = x[t], hi = x[t + QTR];
+                    x[t] = fmaf(lo, cs[u], -(hi * sn[u]));
+                    x[t + QTR] = fmaf(hi, cs[u], lo * sn[u]);
                 }
                 // four table entries at a time: bounded live ranges
                 __builtin_amdgcn_sched_barrier(0);
@@ -256,13 +253,22 @@ __global__ __launch_bounds__(256) void encode_rht_kernel(EncK p) {
         const float nu = sqrtf(ss);
         const float scale = nu > 0.0f ? yscale / nu : 0.0f;
 
-        // sign flips, then the Walsh-Hadamard butterflies (Sylvester order)
-        uint32_t flip[HALF / 32];
+        // sign flips (masks re-read from LDS per tile: the opaque pointer keeps
+        // the compiler from holding 64 mask registers across the tile loop)
+        {
+            const uint4* fl = s_flip + h * (HALF / 4);
+            asm volatile("" : "+v"(fl));
 #pragma unroll
-        for (int w = 0; w < HALF / 32; ++w) flip[w] = s_flip[h * (HALF / 32) + w];
-#pragma unroll
-        for (int j = 0; j < HALF; ++j)
-            x[j] = __uint_as_float(__float_as_uint(x[j]) ^ ((flip[j >> 5] << (31 - (j & 31))) & 0x80000000u));
+            for (int c = 0; c < HALF / 4; ++c) {
+                const uint4 mk = fl[c];
+                x[4 * c + 0] = __uint_as_float(__float_as_uint(x[4 * c + 0]) ^ mk.x);
+                x[4 * c + 1] = __uint_as_float(__float_as_uint(x[4 * c + 1]) ^ mk.y);
+                x[4 * c + 2] = __uint_as_float(__float_as_uint(x[4 * c + 2]) ^ mk.z);
+                x[4 * c + 3] = __uint_as_float(__float_as_uint(x[4 * c + 3]) ^ mk.w);
+            }
+        }
+        // Walsh-Hadamard butterflies (Sylvester order) over every coordinate
+        // bit held in registers; the stages commute
 #pragma unroll
         for (int s = 1; s < HALF; s <<= 1) {
 #pragma unroll
@@ -274,10 +280,15 @@ __global__ __launch_bounds__(256) void encode_rht_kernel(EncK p) {
                 }
             }
         }
+        // exchange back (register j of lane half h = coordinate h*HALF + j);
+        // the remaining coordinate bit log2(QTR) is now registers (t, t + QTR)
 #pragma unroll
-        for (int j = 0; j < HALF; ++j) {
-            const Swap sw = swap32(x[j]);
-            x[j] = fmaf(hs, sw.r1, sw.r0);
+        for (int t = 0; t < QTR; ++t) xchg(x[t], x[t + QTR]);
+#pragma unroll
+        for (int t = 0; t < QTR; ++t) {
+            const float a = x[t], b = x[t + QTR];
+            x[t] = a + b;
+            x[t + QTR] = a - b;
         }
 
         __builtin_amdgcn_sched_barrier(0);
@@ -295,31 +306,14 @@ __global__ __launch_bounds__(256) void encode_rht_kernel(EncK p) {
 #pragma unroll
         for (int pc = 0; pc < NP; ++pc) {
             float e[8];
-            uint32_t code[8];
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) {
-                const float y = x[8 * pc + jj] * scale;
-                float level;
-                code[jj] = quantise<BITS>(y, th, lv, &level);
-                e[jj] = y - level;  // levels of 3-bit codes are subtracted below
-            }
-            if constexpr (BITS == 3) {
-#pragma unroll
-                for (int g4 = 0; g4 < 2; ++g4) {
-                    const uint32_t sel = code[4 * g4] | (code[4 * g4 + 1] << 8) | (code[4 * g4 + 2] << 16) |
-                                         (code[4 * g4 + 3] << 24);
-                    float l4[4];
-                    levels4(bp, sel, l4);
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) e[4 * g4 + u] -= l4[u];
-                }
-            }
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
+                // + 0: a zero vector's -0 coordinates count as +0 (code of y = 0)
+                const float y = fmaf(x[8 * pc + jj], scale, 0.0f);
+                const uint32_t code = quantise<BITS>(y, pt, pl, &e[jj]);
                 gg = fmaf(e[jj], e[jj], gg);
-                const int bpos = BITS * (8 * pc + jj);
-                cw[bpos >> 5] |= code[jj] << (bpos & 31);
-                if ((bpos & 31) + BITS > 32) cw[(bpos >> 5) + 1] |= code[jj] >> (32 - (bpos & 31));
+                // the half starts on a word (and, for 3 bits, a 32-code group) boundary
+                dev::code_put(cw, dev::code_loc(8 * pc + jj, BITS), BITS, code);
             }
             if constexpr (M > 0) {
                 half8 ehi, elo;
@@ -345,6 +339,10 @@ __global__ __launch_bounds__(256) void encode_rht_kernel(EncK p) {
                     acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(slo, ehi, acc[rb], 0, 0, 0);
                 }
             }
+            // the chunk's codes are merged into the words here, not at the
+            // final store (which would keep every compare mask alive)
+#pragma unroll
+            for (int w = 0; w < WH; ++w) asm volatile("" : "+v"(cw[w]));
             // keep each chunk's operand reads next to its MFMAs (bounded live ranges)
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -490,9 +488,9 @@ __global__ __launch_bounds__(256) void dense_quant_kernel(DenseK p) {
                 const float e = y - yh;
                 p.U[i * p.d + c] = e;
                 gg = fmaf(e, e, gg);
-                const int bp = p.bits * c;
-                atomicOr(&words[wv][bp >> 5], code << (bp & 31));
-                if ((bp & 31) + p.bits > 32) atomicOr(&words[wv][(bp >> 5) + 1], code >> (32 - (bp & 31)));
+                const dev::CodeLoc L = dev::code_loc(c, p.bits);
+                atomicOr(&words[wv][L.w0], (code & ((1u << L.n0) - 1u)) << L.s0);
+                if (L.n0 < p.bits) atomicOr(&words[wv][L.w1], (code >> L.n0) << L.s1);
             }
         }
         gg = wave_sum(gg);

@@ -236,21 +236,35 @@ __global__ __launch_bounds__(256) void logits_mfma_kernel(LogM p) {
     const uint32_t* sbase = p.signs + rec0 * mw;
     const float* nbase = p.norm + rec0;
     const float* gbase = p.rnorm + rec0;
-    for (int tile = 0; tile < p.tiles_per_wave; ++tile) {
-        const int key0 = kbeg + tile * 16;
-        if (key0 >= kend) break;  // the same for the whole wave
-        const int key = key0 + n;
-        const bool kv = key < kend;
-        const int kk = min(key, kend - 1) - kbeg;  // record offset of this lane's key from kbeg
-        const float nu = nbase[kk];
-        const float gm = NCS > 0 ? gbase[kk] : 0.0f;
+    // software pipeline: the record words of the next two tiles are in
+    // flight while a tile computes; three register slots in rotation, the
+    // loop unrolled by three so that no slot is ever copied
+    const int ntile = min(p.tiles_per_wave, (kend - kbeg + 15) / 16);  // <= 0: nothing to do
+    typename T::Raw rs[3];
+    float nus[3] = {0.f, 0.f, 0.f}, gms[3] = {0.f, 0.f, 0.f};
+    auto fetch = [&](int tile, int slot) {
+        const int kk = min(kbeg + tile * 16 + n, kend - 1) - kbeg;
+        T::load(cbase + kk * Q::CW, sbase + kk * mw, per, lane, rs[slot]);
+        nus[slot] = nbase[kk];
+        gms[slot] = NCS > 0 ? gbase[kk] : 0.0f;
+    };
+    auto step = [&](int tile, int slot) {
+        if (tile + 2 < ntile) fetch(tile + 2, (slot + 2) % 3);
+        const int key = kbeg + tile * 16 + n;
         double lg[NRT];
-        tl.compute(cbase + kk * Q::CW, sbase + kk * mw, gm, per, lane, lg);
+        tl.compute(rs[slot], gms[slot], per, lane, lg);
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
             const int g = gq0 + 4 * rt + qk;
-            if (kv && g < G) p.out[(rowbase + g) * p.ld + (key - p.col0)] = (float)((double)nu * lg[rt]);
+            if (key < kend && g < G) p.out[(rowbase + g) * p.ld + (key - p.col0)] = (float)((double)nus[slot] * lg[rt]);
         }
+    };
+    if (ntile > 0) fetch(0, 0);
+    if (ntile > 1) fetch(1, 1);
+    for (int tile = 0; tile < ntile; tile += 3) {
+        step(tile, 0);
+        if (tile + 1 < ntile) step(tile + 1, 1);
+        if (tile + 2 < ntile) step(tile + 2, 2);
     }
 }
 
@@ -284,6 +298,21 @@ LogMFn pick_bits_m(int bits, int nrt, int m) {
 }
 
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// workgroups of 256 threads of kernel fn that fit on the device at once
+int64_t resident_blocks(const void* fn) {
+    static thread_local const void* last_fn = nullptr;
+    static thread_local int64_t last = 0;
+    if (fn == last_fn) return last;
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, 0) != hipSuccess || per_cu < 1)
+        return 1024;
+    last_fn = fn;
+    last = (int64_t)cus * per_cu;
+    return last;
+}
 
 }  // namespace
 
@@ -368,7 +397,6 @@ hipError_t launch_logits_mfma(const tq_codebook* ck, const tq_packed& k, const A
     p.m = ck->spec.m;
     p.sdw = q.sdw;
     p.ngroups = ngroups;
-    p.tiles_per_wave = 8;
     p.k0 = k0;
     p.klen = klen;
     p.out = out;
@@ -376,11 +404,16 @@ hipError_t launch_logits_mfma(const tq_codebook* ck, const tq_packed& k, const A
     p.col0 = col0;
     for (int i = 0; i < 8; ++i) p.tdig[i] = ck->lvl_digits[i];
     p.lvl_shift = ck->lvl_shift;
-    const int keys_per_block = 4 * p.tiles_per_wave * 16;
-    const unsigned gx = (unsigned)((int64_t)a.B * a.h_kv * ngroups);
-    const unsigned gy = (unsigned)((klen + keys_per_block - 1) / keys_per_block);
-    if (gx == 0 || gy == 0) return hipSuccess;
-    hipLaunchKernelGGL(fn, dim3(gx, gy), dim3(256), 0, stream, p);
+    // Size the work per wave so that the whole grid is resident at once (one
+    // round of workgroups, no partly idle last round).
+    const int64_t gx = (int64_t)a.B * a.h_kv * ngroups;
+    const int64_t tiles_row = (klen + 15) / 16;  // 16-key tiles per (sequence, KV head)
+    if (gx == 0 || tiles_row == 0) return hipSuccess;
+    const int64_t resident = resident_blocks((const void*)fn);
+    const int64_t gy_want = std::max<int64_t>(1, (resident + gx - 1) / gx);
+    p.tiles_per_wave = (int)std::max<int64_t>(1, (tiles_row + 4 * gy_want - 1) / (4 * gy_want));
+    const int64_t gy = (tiles_row + 4 * (int64_t)p.tiles_per_wave - 1) / (4 * (int64_t)p.tiles_per_wave);
+    hipLaunchKernelGGL(fn, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

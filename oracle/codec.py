@@ -23,9 +23,17 @@ is rounded to float32 and compared with the float32 thresholds.
 
 Fixed-address record (FibQuant summary, section 1): per vector n, planes
 norm[n] f32, rnorm[n] f32 (absent when m = 0), codes[n][b*d/32] u32 and
-signs[n][m/32] u32.  Coordinate i's code is bits [b*i, b*i+b) of the
-LSB-first bit string of its code words (bit k is bit k%32 of word k//32);
-sketch bit l is bit l%32 of sign word l//32.
+signs[n][m/32] u32.  Sketch bit l is bit l%32 of sign word l//32.  Code bit
+positions (bit k is bit k%32 of word k//32 of the record's code words):
+
+* b = 1, 2, 4: coordinate i's code is bits [b*i, b*i+b), LSB first.
+* b = 3: coordinates go in groups of 32 (96 bits, words 3g..3g+2, called
+  W0, W1, W2).  Coordinate j < 24 of a group takes bits [8(j%4) + 3((j%8)//4),
+  +3) of word W_{j//8}: every byte holds two whole codes.  For j = 24 + r,
+  the low two bits sit at bits 8(r%4) + 6, +7 of W_{r//4} and the high bit
+  at bit 8(r%4) + 6 + r//4 of W2.  The pages fix only that records have
+  fixed addresses; this order lets a byte-wise mask recover four codes at
+  once.
 """
 from __future__ import annotations
 
@@ -75,6 +83,23 @@ def make_codebook(d: int, bits: int, m: int, dense: bool, sigma=None, rot_gauss=
 
 
 # -------------------------------------------------------------- packing --
+def code_bit_position(i: int, k: int, bits: int) -> int:
+    """Position (in the record's code-word bit string) of bit k of
+    coordinate i's code, per the layout in the module docstring."""
+    if bits != 3:
+        return bits * i + k
+    g, j = divmod(i, 32)
+    if j < 24:
+        word, pos = j // 8, 8 * (j % 4) + 3 * ((j % 8) // 4) + k
+    else:
+        r = j - 24
+        if k < 2:
+            word, pos = r // 4, 8 * (r % 4) + 6 + k
+        else:
+            word, pos = 2, 8 * (r % 4) + 6 + r // 4
+    return 96 * g + 32 * word + pos
+
+
 def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
     n, d = codes.shape
     nw = (bits * d + 31) // 32
@@ -82,7 +107,7 @@ def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
     c = codes.astype(np.uint64)
     for i in range(d):
         for k in range(bits):
-            pos = bits * i + k
+            pos = code_bit_position(i, k, bits)
             words[:, pos // 32] |= ((c[:, i] >> np.uint64(k)) & np.uint64(1)) << np.uint64(pos % 32)
     return words.astype(np.uint32)
 
@@ -93,7 +118,7 @@ def unpack_codes(words: np.ndarray, bits: int, d: int) -> np.ndarray:
     codes = np.zeros((n, d), dtype=np.int64)
     for i in range(d):
         for k in range(bits):
-            pos = bits * i + k
+            pos = code_bit_position(i, k, bits)
             codes[:, i] |= (((w[:, pos // 32] >> np.uint64(pos % 32)) & np.uint64(1)).astype(np.int64)) << k
     return codes
 

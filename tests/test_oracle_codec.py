@@ -24,15 +24,25 @@ def test_pack_unpack_round_trip(bits, d):
 
 
 def test_packing_matches_hand_derived_words():
-    """The LSB-first layout, worked by hand:
-    b=2, codes 0,1,2,3 repeated: each byte is 0b11100100 = 0xE4.
-    b=3, codes 0..7 repeated: each 24-bit group is sum c_k 2^(3k) = 0xFAC688,
-    so the words cycle through 0x88FAC688, 0xC688FAC6, 0xFAC688FA.
+    """The layouts, worked by hand:
+    b=2 (LSB first), codes 0,1,2,3 repeated: each byte is 0b11100100 = 0xE4.
+    b=3 (groups of 32), codes j % 8: byte k of W0 holds c_k = k (bits 0-2),
+    c_{4+k} = 4+k (bits 3-5) and the low bits of c_{24+k} = k (bits 6-7):
+    bytes 0x20, 0x69, 0xB2, 0xFB; W1 is the same (c_{8+k}, c_{12+k}, low bits
+    of c_{28+k} = 4+k); byte k of W2 holds c_{16+k} = k, c_{20+k} = 4+k, bit
+    2 of c_{24+k} (0) at bit 6 and bit 2 of c_{28+k} (1) at bit 7: bytes
+    0xA0, 0xA9, 0xB2, 0xBB.
+    b=3, single codes: c_26 = 7 puts 0b11 at W0 bits 22-23 and 1 at W2 bit 22;
+    c_30 = 5 puts 0b01 at W1 bit 22 and 1 at W2 bit 23; c_13 = 6 (0b110) sits
+    at W1 bits 11-13.
     Sketch bits 1,0,0,...,0,1 (bit 0 and bit 31 set) give 0x80000001."""
     c2 = np.tile(np.arange(4), 32)[None]
     assert list(codec.pack_codes(c2, 2)[0]) == [0xE4E4E4E4] * 8
     c3 = np.tile(np.arange(8), 16)[None]
-    assert list(codec.pack_codes(c3, 3)[0]) == [0x88FAC688, 0xC688FAC6, 0xFAC688FA] * 4
+    assert list(codec.pack_codes(c3, 3)[0]) == [0xFBB26920, 0xFBB26920, 0xBBB2A9A0] * 4
+    c3 = np.zeros((1, 64), np.int64)
+    c3[0, 26], c3[0, 30], c3[0, 13] = 7, 5, 6
+    assert list(codec.pack_codes(c3, 3)[0]) == [0x00C00000, 0x00403000, 0x00C00000, 0, 0, 0]
     s = np.zeros((1, 64), np.int64)
     s[0, 0] = s[0, 31] = 1
     s[0, 32 + 4] = 1
