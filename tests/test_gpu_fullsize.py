@@ -1,0 +1,171 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times (its own setup and step functions).
+
+The oracle cannot redo whole steps at these sizes, so each output is checked
+on a seeded sample it can compute one by one:
+* encode: sampled vectors re-encoded by the oracle (its own seeded codebook),
+  compared by the code/sign/norm protocol of tests/parity.py;
+* logits: sampled (query, key) entries recomputed from the GPU's own packed
+  records (both sides read the same cache);
+* decode: whole query groups of sampled KV heads, over every record of the
+  head;
+* top-10 (vector search): returned scores equal the oracle's scores of the
+  returned rows, and no sampled other row beats the 10th score by more than
+  the tolerance.
+"""
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import codec, estimator, rope as orope
+
+import parity
+
+torch = pytest.importorskip("torch")
+tq = pytest.importorskip("kv_cache_vector_05_amd")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def records(planes, idx):
+    """Encoded view of the GPU records at indices idx (nu, gamma as stored)."""
+    norm, rnorm, codes, signs = planes
+    rn = rnorm[idx].astype(np.float64) if rnorm is not None and len(rnorm) else np.zeros(len(idx))
+    sg = signs[idx] if signs is not None and len(signs) else np.zeros((len(idx), 0), np.uint32)
+    return codec.Encoded(norm[idx].astype(np.float64), rn, codes[idx], sg)
+
+
+def gpu_planes(packed):
+    norm, rnorm, codes, signs = packed.numpy()
+    return norm, rnorm, codes, signs
+
+
+def check_llama(kind, n_enc=192, n_logit=1024, n_decode_heads=2):
+    st = bench.setup_llama(torch, tq, synth, kind)
+    bench.step_llama(st, tq, bench.Timer(torch))
+    torch.cuda.synchronize()
+    B, Hq, H, L, d, bits, m = (st[k] for k in ("B", "Hq", "H", "L", "d", "bits", "m"))
+    G = Hq // H
+    K, V, Q = st["host"]
+    ock = codec.make_codebook(d, bits, m, False, seed=synth.K_SEED)
+    ocv = codec.make_codebook(d, bits, m, False, seed=synth.V_SEED)
+    rope_o = orope.rope_table(st["rope_base"], d, L + 1) if st["rope_base"] else None
+    kpl, vpl = gpu_planes(st["kp"]), gpu_planes(st["vp"])
+    g = np.random.default_rng(1234)
+
+    # encode: sampled vectors (record n = (b*H + kh)*L + t)
+    b_s = g.integers(0, B, n_enc)
+    kh_s = g.integers(0, H, n_enc)
+    t_s = np.concatenate([g.integers(0, L, n_enc - 2), [0, L - 1]])
+    n_s = (b_s * H + kh_s) * L + t_s
+    kx = synth.bf16_bits_to_f32(K[b_s, t_s, kh_s])
+    vx = synth.bf16_bits_to_f32(V[b_s, t_s, kh_s])
+    ek = codec.encode(ock, kx, pos=t_s, rope=rope_o)
+    ev = codec.encode(ocv, vx)
+    parity.compare_encoded(ock, ek, tuple(p[n_s] for p in kpl), f"{kind} K (full size, sampled)")
+    parity.compare_encoded(ocv, ev, tuple(p[n_s] for p in vpl), f"{kind} V (full size, sampled)")
+
+    # logits: sampled (b, h, t) entries from the GPU's records, query at position L
+    qf = synth.bf16_bits_to_f32(Q)
+    lg = st["logits"].cpu().numpy()
+    prep = {b: estimator.prep_query(ock, qf[b], L, rope_o) for b in range(B)}
+    b_l = g.integers(0, B, n_logit)
+    h_l = g.integers(0, Hq, n_logit)
+    t_l = g.integers(0, L, n_logit)
+    ref = np.empty(n_logit)
+    for i in range(n_logit):
+        qp, s = prep[b_l[i]]
+        n = (b_l[i] * H + h_l[i] // G) * L + t_l[i]
+        ref[i] = estimator.logits(ock, qp[h_l[i]:h_l[i] + 1], s[h_l[i]:h_l[i] + 1], records(kpl, [n]))[0, 0]
+    parity.assert_close(lg[b_l, h_l, t_l], ref, f"{kind} logits (full size, sampled)")
+
+    # decode: whole query groups of sampled KV heads
+    out = st["out"].cpu().numpy()
+    for _ in range(n_decode_heads):
+        b, kh = int(g.integers(0, B)), int(g.integers(0, H))
+        idx = np.arange((b * H + kh) * L, (b * H + kh + 1) * L)
+        qp, s = prep[b]
+        gs = slice(kh * G, (kh + 1) * G)
+        ref_o = estimator.attention(ock, ocv, qp[gs], s[gs], records(kpl, idx), records(vpl, idx), L,
+                                    1.0 / math.sqrt(d))
+        parity.assert_close(out[b, gs], ref_o, f"{kind} decode b={b} kh={kh} (full size)")
+
+
+@pytest.mark.timeout(900)
+def test_llama8b_full_size():
+    """Batch 8, 32/8 heads, context 32768, bf16, RoPE 5e5, b=3 + m=64."""
+    check_llama("llama8b")
+
+
+@pytest.mark.timeout(900)
+def test_llama70b_full_size():
+    """Batch 1, 64/8 heads, context 131072, Student-t(3) channel scales, b=3 + m=128."""
+    check_llama("llama70b", n_decode_heads=1)
+
+
+@pytest.mark.timeout(900)
+def test_esm650m_full_size():
+    """33 layers x 20 heads x 32 x 1024 tokens, d=64, RoPE 1e4, b=3 + m=64:
+    sampled vectors of the first and last layer."""
+    st = bench.setup_esm(torch, tq, synth)
+    bench.step_esm(st, tq, bench.Timer(torch))
+    torch.cuda.synchronize()
+    S, T, H, d, bits, m = (st[k] for k in ("S", "T", "H", "d", "bits", "m"))
+    ock = codec.make_codebook(d, bits, m, False, seed=synth.K_SEED)
+    ocv = codec.make_codebook(d, bits, m, False, seed=synth.V_SEED)
+    rope_o = orope.rope_table(1e4, d, T)
+    tok = synth.esm_tokens(0, S, T)
+    g = np.random.default_rng(99)
+    for layer in (0, st["layers"] - 1):
+        pk, pv = synth.esm_layer_tables(layer)
+        s_i, t_i, h_i = g.integers(0, S, 160), g.integers(0, T, 160), g.integers(0, H, 160)
+        n_s = (s_i * H + h_i) * T + t_i
+        kx = pk[tok[s_i, t_i]].reshape(-1, H, d)[np.arange(160), h_i]
+        vx = pv[tok[s_i, t_i]].reshape(-1, H, d)[np.arange(160), h_i]
+        ek = codec.encode(ock, kx, pos=t_i, rope=rope_o)
+        ev = codec.encode(ocv, vx)
+        parity.compare_encoded(ock, ek, tuple(p[n_s] for p in gpu_planes(st["kp"][layer])), f"esm K layer {layer}")
+        parity.compare_encoded(ocv, ev, tuple(p[n_s] for p in gpu_planes(st["vp"][layer])), f"esm V layer {layer}")
+
+
+@pytest.mark.timeout(1200)
+def test_vector_search_full_size():
+    """10^6 x 1536 unit vectors, dense Haar, b=2 + m=1536, 1024 queries, top-10."""
+    st = bench.setup_vsearch(torch, tq, synth)
+    bench.step_vsearch(st, tq, bench.Timer(torch))
+    vals, idx = tq.attn_logits(st["ck"], st["Q"], st["kp"], 1, st["n"], st["sl"], top_k=10, workspace=st["ws_l"])
+    torch.cuda.synchronize()
+    n, d, bits, m = st["n"], st["d"], st["bits"], st["m"]
+    vals, idx = vals.cpu().numpy()[0], idx.cpu().numpy()[0]
+    ock = codec.make_codebook(d, bits, m, True, seed=synth.K_SEED)
+    planes = gpu_planes(st["kp"])
+    g = np.random.default_rng(7)
+    # encode: sampled rows
+    # (rows from the first and the last 65536-row chunk: each chunk is generated whole)
+    last0 = (n - 1) // 65536 * 65536
+    first, last = synth.vsearch_rows(0, 0, 65536), synth.vsearch_rows(0, last0, n - last0)
+    ra, rb = g.integers(0, 65536, 31), np.concatenate([g.integers(last0, n, 32), [n - 1]])
+    rows_i = np.concatenate([ra, rb])
+    X = np.concatenate([first[ra], last[rb - last0]])
+    parity.compare_encoded(ock, codec.encode(ock, X), tuple(p[rows_i] for p in planes), "vsearch index (sampled)")
+    # top-10 of sampled queries
+    others = g.choice(n, 20000, replace=False)
+    for qi in g.choice(st["nq"], 6, replace=False):
+        qp, s = estimator.prep_query(ock, st["Qh"][qi:qi + 1])
+        assert len(set(idx[qi].tolist())) == 10 and np.all(np.diff(vals[qi]) <= 0)
+        ref_top = estimator.logits(ock, qp, s, records(planes, idx[qi]))[0]
+        parity.assert_close(vals[qi], ref_top, f"vsearch top-10 values, query {qi}")
+        ref_oth = estimator.logits(ock, qp, s, records(planes, others))[0]
+        kth = vals[qi, -1]
+        mask = ~np.isin(others, idx[qi])
+        assert np.all(ref_oth[mask] <= kth + parity.ATOL + parity.RTOL * abs(kth)), \
+            f"vsearch query {qi}: a sampled row beats the returned 10th score"
