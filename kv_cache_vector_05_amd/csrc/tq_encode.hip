@@ -37,6 +37,7 @@ struct EncK {
     int64_t s_seq, s_tok, s_head;
     int32_t n_seq, n_tok, h_kv, tok_offset, L_cap, tok_blocks;
     int64_t n_tiles;
+    int32_t rope_stage;  // the block's four waves share their tokens: RoPE rows staged in LDS
     const float* rope_cos;
     const float* rope_sin;
     const float* sigma;
@@ -127,6 +128,28 @@ __device__ __forceinline__ uint32_t quantise(float y, const float* pt, const flo
     return lowbits ^ (~neg & K1);
 }
 
+// RoPE rows of the 32 tokens of the tile step at `base` (table entries of
+// this thread's staging slots), and their store into the LDS buffer
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int HALF, int NQ>
+__device__ __forceinline__ void rope_stage_load(const EncK& p, int64_t base, const int (&tab)[NQ],
+                                                const int (&row)[NQ], const int (&c4)[NQ], f32x4 (&pre)[NQ]) {
+    const int tb0 = (int)((base / p.h_kv) % p.tok_blocks);
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+        const int pos = p.tok_offset + min(tb0 * 32 + row[j], p.n_tok - 1);
+        const float* src = (tab[j] ? p.rope_sin : p.rope_cos) + (int64_t)pos * HALF + 4 * c4[j];
+        pre[j] = *reinterpret_cast<const f32x4*>(src);
+    }
+}
+template <int RS, int NQ>
+__device__ __forceinline__ void rope_stage_store(f32x4* lds, const int (&tab)[NQ], const int (&row)[NQ],
+                                                 const int (&c4)[NQ], const f32x4 (&pre)[NQ]) {
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) lds[((tab[j] * 32 + row[j]) * RS) / 4 + c4[j]] = pre[j];
+}
+
 template <int D, int BITS, int M, bool BF16>
 __global__ __launch_bounds__(256) void encode_rht_kernel(EncK p) {
     constexpr int HALF = D / 2;
@@ -168,9 +191,40 @@ __global__ __launch_bounds__(256) void encode_rht_kernel(EncK p) {
     for (int k = 0; k < KH; ++k) pl[k] = p.levels[KH + k] * ESCALE;
     const float yscale = ESCALE / sqrtf((float)D);
 
-    const int64_t wave_stride = (int64_t)gridDim.x * (blockDim.x >> 6);
-    for (int64_t tile = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); tile < p.n_tiles;
-         tile += wave_stride) {
+    // RoPE rows of the block's 32 tokens, staged in LDS when the block's four
+    // waves encode four heads of the same tokens (h_kv a multiple of 4): the
+    // rows of the next tile step are loaded into registers while the current
+    // one computes, then written to LDS between two barriers.
+    constexpr int RS = HALF + 4;         // padded row stride (floats): conflict-free b128 reads
+    constexpr int NQ = 2 * 32 * (HALF / 4) / 256;  // float4 per thread per stage (cos and sin)
+    extern __shared__ f32x4 s_rope4[];  // [cos, sin][32 tokens][RS / 4]
+    float* s_rope = reinterpret_cast<float*>(s_rope4);
+    const bool stage = p.rope_cos != nullptr && p.rope_stage;
+    // staging slot j of this thread: table (0 cos, 1 sin), token row, float4 column
+    int st_table[NQ], st_row[NQ], st_c4[NQ];
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+        const int q = threadIdx.x + 256 * j;
+        st_table[j] = q / (32 * (HALF / 4));
+        const int rem = q % (32 * (HALF / 4));
+        st_row[j] = rem / (HALF / 4);
+        st_c4[j] = rem % (HALF / 4);
+    }
+    const int64_t blk_stride = (int64_t)gridDim.x * 4;
+    int64_t base = (int64_t)blockIdx.x * 4;
+    if (stage && base < p.n_tiles) {
+        f32x4 pre[NQ];
+        rope_stage_load<HALF, NQ>(p, base, st_table, st_row, st_c4, pre);
+        rope_stage_store<RS, NQ>(s_rope4, st_table, st_row, st_c4, pre);
+    }
+    __syncthreads();
+    // the loop bound is the same for the whole block (barriers inside)
+    for (; base < p.n_tiles; base += blk_stride) {
+      const int64_t tile = base + (threadIdx.x >> 6);
+      f32x4 pre[NQ];  // the next step's rows, in flight during this step
+      if (stage && base + blk_stride < p.n_tiles)
+          rope_stage_load<HALF, NQ>(p, base + blk_stride, st_table, st_row, st_c4, pre);
+      if (tile < p.n_tiles) {
         const int head = (int)(tile % p.h_kv);
         const int64_t r = tile / p.h_kv;
         const int tb = (int)(r % p.tok_blocks);
@@ -221,15 +275,29 @@ __global__ __launch_bounds__(256) void encode_rht_kernel(EncK p) {
 
         // RoPE (keys): pair (i, i + D/2), i = h*QTR + t, is registers (t, t + QTR)
         if (p.rope_cos) {
-            const int pos = p.tok_offset + (valid ? token : 0);
-            const float4* cp = reinterpret_cast<const float4*>(p.rope_cos + (int64_t)pos * HALF + h * QTR);
-            const float4* sp = reinterpret_cast<const float4*>(p.rope_sin + (int64_t)pos * HALF + h * QTR);
+            // all table reads in flight at once (LDS reads when staged, kept
+            // apart from the global path so they stay LDS instructions)
+            f32x4 cc[QTR / 4], ss[QTR / 4];
+            if (stage) {
+#pragma unroll
+                for (int c = 0; c < QTR / 4; ++c) {
+                    cc[c] = s_rope4[(v * RS + h * QTR) / 4 + c];
+                    ss[c] = s_rope4[((32 + v) * RS + h * QTR) / 4 + c];
+                }
+            } else {
+                const int64_t ro = (int64_t)(p.tok_offset + (valid ? token : 0)) * HALF + h * QTR;
+                const f32x4* cp = reinterpret_cast<const f32x4*>(p.rope_cos + ro);
+                const f32x4* sp = reinterpret_cast<const f32x4*>(p.rope_sin + ro);
+#pragma unroll
+                for (int c = 0; c < QTR / 4; ++c) {
+                    cc[c] = cp[c];
+                    ss[c] = sp[c];
+                }
+            }
 #pragma unroll
             for (int c = 0; c < QTR / 4; ++c) {
-                const float4 cc = cp[c];
-                const float4 ss = sp[c];
-                const float cs[4] = {cc.x, cc.y, cc.z, cc.w};
-                const float sn[4] = {ss.x, ss.y, ss.z, ss.w};
+                const float cs[4] = {cc[c][0], cc[c][1], cc[c][2], cc[c][3]};
+                const float sn[4] = {ss[c][0], ss[c][1], ss[c][2], ss[c][3]};
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int t = 4 * c + u;
@@ -237,8 +305,6 @@ __global__ __launch_bounds__(256) void encode_rht_kernel(EncK p) {
                     x[t] = fmaf(lo, cs[u], -(hi * sn[u]));
                     x[t + QTR] = fmaf(hi, cs[u], lo * sn[u]);
                 }
-                // four table entries at a time: bounded live ranges
-                __builtin_amdgcn_sched_barrier(0);
             }
         }
 
@@ -374,6 +440,12 @@ __global__ __launch_bounds__(256) void encode_rht_kernel(EncK p) {
                 if (valid && (rb & 1) == h) p.signs[n * NRB + rb] = wb;
             }
         }
+      }
+      if (stage) {
+          __syncthreads();  // every wave is done with the current rows
+          if (base + blk_stride < p.n_tiles) rope_stage_store<RS, NQ>(s_rope4, st_table, st_row, st_c4, pre);
+          __syncthreads();
+      }
     }
 }
 
@@ -605,7 +677,9 @@ hipError_t launch_encode(const tq_codebook* cb, const EncodeArgs& a, hipStream_t
         const int64_t blocks_needed = (p.n_tiles + 3) / 4;
         const int64_t cap = (int64_t)g_num_cus * 8;
         const int grid = (int)(blocks_needed < cap ? blocks_needed : cap);
-        hipLaunchKernelGGL(fn, dim3(grid), dim3(256), 0, stream, p);
+        p.rope_stage = (a.rope_cos != nullptr && a.h_kv % 4 == 0) ? 1 : 0;
+        const size_t lds = p.rope_stage ? (size_t)2 * 32 * (d / 2 + 4) * sizeof(float) : 0;
+        hipLaunchKernelGGL(fn, dim3(grid), dim3(256), lds, stream, p);
         return hipGetLastError();
     }
     // dense form, chunk by chunk
