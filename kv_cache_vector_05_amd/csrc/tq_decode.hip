@@ -11,8 +11,8 @@
 // "TurboQuant: Uma Nova Abordagem", the QJL dequantiser; FibQuant summary,
 // section 2.3: lookup, inverse rotation, norm scale).
 //
-// A workgroup (four waves) owns one split of one KV head (at most 1024 keys
-// for up to four queries, 512 for up to eight) and makes two passes over it:
+// A workgroup (four waves) owns one split of one KV head (at most 512 keys
+// for up to four queries, 256 for up to eight) and makes two passes over it:
 //  1. the logit of every key with the exact int8-MFMA tile of the scan (one
 //     16-key tile per wave per 64 keys), kept in LDS, plus the split's max
 //     logit per query and the max of nu and nu*gamma over its values;
@@ -63,7 +63,7 @@ struct DecM {
 
 template <int NRT>
 constexpr int split_max() {
-    return NRT == 1 ? 1024 : 512;
+    return NRT == 1 ? 512 : 256;
 }
 
 typedef __attribute__((address_space(3))) intx2* lds_intx2_ptr;
@@ -154,27 +154,35 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
     {
         TL tl;
         tl.init(p.qd, p.sd, p.qscale, p.sdw, M, rowbase, gq0, G, p.tdig_k, p.shift_k, lane);
+        // the key record (and the value norms) of the next chunk's tile are
+        // loaded before the current tile computes
+        struct Rec1 {
+            typename TL::Raw raw;
+            float nu, gm, vn, vg;
+        } cur, nxt;
+        auto fetch1 = [&](int c, Rec1& r) {
+            const int64_t rec = rec_base + min(c0 + 64 * c + 16 * wave + n, c1 - 1);
+            TL::load(p.k_codes + rec * Q::CW + Q::word0(qk), p.k_signs + rec * MW, PER, lane, r.raw);
+            r.nu = p.k_norm[rec];
+            r.gm = M > 0 ? p.k_rnorm[rec] : 0.f;
+            r.vn = p.v_norm[rec];
+            r.vg = M > 0 ? p.v_rnorm[rec] : 0.f;
+        };
+        if (c0 + 16 * wave < c1) fetch1(0, cur);
         for (int c = 0; c < nch; ++c) {
             const int key0 = c0 + 64 * c + 16 * wave;
+            if (key0 + 64 < c1) fetch1(c + 1, nxt);  // the same for the whole wave
             float a[NRT];
             if (key0 < c1) {  // the same for the whole wave
-                const int key = key0 + n;
-                const bool valid = key < c1;
-                const int64_t rec = rec_base + min(key, c1 - 1);
-                const float nu = p.k_norm[rec];
-                const float gm = M > 0 ? p.k_rnorm[rec] : 0.f;
-                typename TL::Raw raw;
-                TL::load(p.k_codes + rec * Q::CW + Q::word0(qk), p.k_signs + rec * MW, PER, lane, raw);
+                const bool valid = key0 + n < c1;
                 double lg[NRT];
-                tl.compute(raw, gm, PER, lane, lg);
+                tl.compute(cur.raw, cur.gm, PER, lane, lg);
 #pragma unroll
                 for (int rt = 0; rt < NRT; ++rt)
-                    a[rt] = valid ? (float)((double)p.scale * (double)nu * lg[rt]) : -INFINITY;
-                const float vn = p.v_norm[rec];
-                const float vg = M > 0 ? p.v_rnorm[rec] : 0.f;
+                    a[rt] = valid ? (float)((double)p.scale * (double)cur.nu * lg[rt]) : -INFINITY;
                 if (valid) {
-                    numax = fmaxf(numax, vn);
-                    ngmax = fmaxf(ngmax, vn * vg);
+                    numax = fmaxf(numax, cur.vn);
+                    ngmax = fmaxf(ngmax, cur.vn * cur.vg);
                 }
             } else {
 #pragma unroll
@@ -185,6 +193,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
                 lgs[((wave * NCH + c) * NRT + rt) * 64 + lane] = a[rt];
                 mx[rt] = fmaxf(mx[rt], a[rt]);
             }
+            cur = nxt;
         }
     }
 #pragma unroll
@@ -233,15 +242,26 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
     for (int i = 0; i < 8; ++i) tdv[i] = p.tdig_v[i];
     const int row = 16 * wave + n;  // this lane's key row within a 64-key chunk
 
-    for (int c = 0; c < nch; ++c) {
-        const int key = c0 + 64 * c + row;
-        const int64_t rec = rec_base + min(key, c1 - 1);
-        // value record of the lane's key (a clamped, valid record past the end;
-        // its weight is zero)
+    // value record of the lane's key (a clamped, valid record past the end;
+    // its weight is zero), loaded one chunk ahead
+    struct Rec2 {
         uint32_t W[Q::NW];
-        Q::load(p.v_codes + rec * Q::CW + Q::word0(qk), qk, W);
-        const float vn = p.v_norm[rec];
-        const float vg = M > 0 ? p.v_rnorm[rec] : 0.f;
+        uint32_t sg;  // the sign word holding sketch rows [qk*PER, (qk+1)*PER)
+        float vn, vg;
+    } vcur, vnxt;
+    auto fetch2 = [&](int c, Rec2& r) {
+        const int64_t rec = rec_base + min(c0 + 64 * c + row, c1 - 1);
+        Q::load(p.v_codes + rec * Q::CW + Q::word0(qk), qk, r.W);
+        r.sg = M > 0 ? p.v_signs[rec * MW + ((qk * PER) >> 5)] : 0u;
+        r.vn = p.v_norm[rec];
+        r.vg = M > 0 ? p.v_rnorm[rec] : 0.f;
+    };
+    fetch2(0, vcur);
+    for (int c = 0; c < nch; ++c) {
+        if (c + 1 < nch) fetch2(c + 1, vnxt);
+        const uint32_t* W = vcur.W;
+        const float vn = vcur.vn;
+        const float vg = vcur.vg;
         // weights in fixed point, digits in the A-operand rows 4 qk + digit
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
@@ -272,12 +292,11 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
         }
         // sign bits of sketch rows [qk*PER, (qk+1)*PER) as +-1 bytes
         if constexpr (M > 0) {
-            const uint32_t* sp = p.v_signs + rec * MW;
             if constexpr (PER >= 16) {
 #pragma unroll
                 for (int k = 0; k < PER / 16; ++k) {
                     const int bit0 = qk * PER + 16 * k;
-                    const uint32_t x = sp[bit0 >> 5] >> (bit0 & 31);
+                    const uint32_t x = vcur.sg >> (bit0 & 31);
                     intx4 v;
 #pragma unroll
                     for (int s4 = 0; s4 < 4; ++s4) v[s4] = (int)dev::spread4_pm(x >> (4 * s4));
@@ -285,7 +304,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
                 }
             } else {
                 const int bit0 = qk * PER;
-                const uint32_t x = sp[bit0 >> 5] >> (bit0 & 31);
+                const uint32_t x = vcur.sg >> (bit0 & 31);
                 intx2 v;
                 v[0] = (int)dev::spread4_pm(x);
                 v[1] = (int)dev::spread4_pm(x >> 4);
@@ -323,6 +342,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
             }
         }
         __syncthreads();
+        vcur = vnxt;
     }
 
     // ---------------- partial results of the split
