@@ -150,7 +150,7 @@ __device__ __forceinline__ void rope_stage_store(f32x4* lds, const int (&tab)[NQ
     for (int j = 0; j < NQ; ++j) lds[((tab[j] * 32 + row[j]) * RS) / 4 + c4[j]] = pre[j];
 }
 
-template <int D, int BITS, int M, bool BF16>
+template <int D, int BITS, int M, bool BF16, bool ROPE>
 __global__ __launch_bounds__(256) void encode_rht_kernel(EncK p) {
     constexpr int HALF = D / 2;
     constexpr int QTR = D / 4;
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(256) void encode_rht_kernel(EncK p) {
     constexpr int NQ = 2 * 32 * (HALF / 4) / 256;  // float4 per thread per stage (cos and sin)
     extern __shared__ f32x4 s_rope4[];  // [cos, sin][32 tokens][RS / 4]
     float* s_rope = reinterpret_cast<float*>(s_rope4);
-    const bool stage = p.rope_cos != nullptr && p.rope_stage;
+    const bool stage = ROPE && p.rope_stage;
     // staging slot j of this thread: table (0 cos, 1 sin), token row, float4 column
     int st_table[NQ], st_row[NQ], st_c4[NQ];
 #pragma unroll
@@ -274,7 +274,7 @@ __global__ __launch_bounds__(256) void encode_rht_kernel(EncK p) {
         for (int t = 0; t < QTR; ++t) xchg(x[t], x[t + QTR]);
 
         // RoPE (keys): pair (i, i + D/2), i = h*QTR + t, is registers (t, t + QTR)
-        if (p.rope_cos) {
+        if constexpr (ROPE) {
             // all table reads in flight at once (LDS reads when staged, kept
             // apart from the global path so they stay LDS instructions)
             f32x4 cc[QTR / 4], ss[QTR / 4];
@@ -602,32 +602,33 @@ int64_t dense_chunk(int64_t nvec) { return nvec < 65536 ? nvec : 65536; }
 using EncFn = void (*)(EncK);
 
 template <int D, int BITS, int M>
-EncFn pick_dtype(bool bf16) {
-    return bf16 ? encode_rht_kernel<D, BITS, M, true> : encode_rht_kernel<D, BITS, M, false>;
+EncFn pick_dtype(bool bf16, bool rope) {
+    if (rope) return bf16 ? encode_rht_kernel<D, BITS, M, true, true> : encode_rht_kernel<D, BITS, M, false, true>;
+    return bf16 ? encode_rht_kernel<D, BITS, M, true, false> : encode_rht_kernel<D, BITS, M, false, false>;
 }
 
 template <int D, int BITS>
-EncFn pick_m(int m, bool bf16) {
-    if (m == 0) return pick_dtype<D, BITS, 0>(bf16);
-    if (m == D / 2) return pick_dtype<D, BITS, D / 2>(bf16);
-    if (m == D) return pick_dtype<D, BITS, D>(bf16);
+EncFn pick_m(int m, bool bf16, bool rope) {
+    if (m == 0) return pick_dtype<D, BITS, 0>(bf16, rope);
+    if (m == D / 2) return pick_dtype<D, BITS, D / 2>(bf16, rope);
+    if (m == D) return pick_dtype<D, BITS, D>(bf16, rope);
     return nullptr;
 }
 
 template <int D>
-EncFn pick_bits(int bits, int m, bool bf16) {
+EncFn pick_bits(int bits, int m, bool bf16, bool rope) {
     switch (bits) {
-        case 1: return pick_m<D, 1>(m, bf16);
-        case 2: return pick_m<D, 2>(m, bf16);
-        case 3: return pick_m<D, 3>(m, bf16);
-        case 4: return pick_m<D, 4>(m, bf16);
+        case 1: return pick_m<D, 1>(m, bf16, rope);
+        case 2: return pick_m<D, 2>(m, bf16, rope);
+        case 3: return pick_m<D, 3>(m, bf16, rope);
+        case 4: return pick_m<D, 4>(m, bf16, rope);
     }
     return nullptr;
 }
 
-EncFn pick_encode(int d, int bits, int m, bool bf16) {
-    if (d == 64) return pick_bits<64>(bits, m, bf16);
-    if (d == 128) return pick_bits<128>(bits, m, bf16);
+EncFn pick_encode(int d, int bits, int m, bool bf16, bool rope) {
+    if (d == 64) return pick_bits<64>(bits, m, bf16, rope);
+    if (d == 128) return pick_bits<128>(bits, m, bf16, rope);
     return nullptr;
 }
 
@@ -650,7 +651,7 @@ hipError_t launch_encode(const tq_codebook* cb, const EncodeArgs& a, hipStream_t
         g_num_cus = prop.multiProcessorCount;
     }
     if (!cb->dense) {
-        EncFn fn = pick_encode(d, bits, m, a.bf16 != 0);
+        EncFn fn = pick_encode(d, bits, m, a.bf16 != 0, a.rope_cos != nullptr);
         if (!fn) return hipErrorInvalidValue;
         EncK p{};
         p.x = a.x;
