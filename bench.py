@@ -33,6 +33,38 @@ if ROOT not in sys.path:
 
 METRIC = "decode attn-logit keys/sec + % of HBM peak; KV encode tokens/sec (1 MI355X)"
 HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def device_code_digest() -> str:
+    """sha256 over the library's device sources and build script: counter
+    figures taken for another version of the kernels no longer apply."""
+    import hashlib
+    pkg = os.path.join(ROOT, "kv_cache_vector_05_amd")
+    csrc = os.path.join(pkg, "csrc")
+    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc) if f.endswith((".hip", ".h", ".cpp")))
+    files.append(os.path.join(pkg, "build.py"))
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, call: str):
+    """HBM bytes per call from rocprofv3 FETCH_SIZE / WRITE_SIZE passes
+    (profiles/hbm_traffic.json), or None when absent or taken for other
+    device code."""
+    import json as _json
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = _json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("device_code_sha256") != device_code_digest():
+        return None
+    return t.get("calls", {}).get(workload, {}).get(call, {}).get("traffic_bytes")
 
 
 def parse():
@@ -304,12 +336,14 @@ def main():
     ms_step = wall * 1e3 / args.steps
     value, unit, kern, dom, extra, cfg = report(timer, ms_step)
     dk = kern[dom]
+    for name, k in kern.items():
+        k["traffic_bytes"] = measured_traffic(wl, name)
     if "TFLOPs" in dk and dom == "scan_topk":
         roof = {"bound": "mfma", "achieved": dk["TFLOPs"], "peak": 157.3, "unit": "TFLOP/s",
-                "frac": dk["TFLOPs"] / 157.3, "traffic": None, "kernel": dom}
+                "frac": dk["TFLOPs"] / 157.3, "traffic": dk["traffic_bytes"], "kernel": dom}
     else:
         roof = {"bound": "hbm", "achieved": dk["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": dk["GBps"] / HBM_PEAK_GBS, "traffic": None, "kernel": dom}
+                "frac": dk["GBps"] / HBM_PEAK_GBS, "traffic": dk["traffic_bytes"], "kernel": dom}
     line = {"metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "f32", "data": "synthetic", "config": cfg, "roofline": roof,
