@@ -633,8 +633,15 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeK p) {
     if (t >= D && col) az[t - D] = acc;
     __syncthreads();
     if (t < D) {
+        // S^T A_z: sixteen sketch rows' loads in flight at a time (m is a multiple of 32)
         float corr = 0.f;
-        for (int k = 0; k < p.m; ++k) corr = fmaf(p.sketch[(int64_t)k * D + t], az[k], corr);
+        for (int k0 = 0; k0 < p.m; k0 += 16) {
+            float sv[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) sv[u] = p.sketch[(int64_t)(k0 + u) * D + t];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) corr = fmaf(sv[u], az[k0 + u], corr);
+        }
         w[t] = acc + (p.m ? kQjl / (float)p.m : 0.f) * corr;
     }
     __syncthreads();
@@ -650,6 +657,48 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeK p) {
     if (t < D) {
         const float o = (l > 0.f) ? p.sigma[t] * w[t] / (sqrtf((float)D) * l) : 0.f;
         p.out[row * D + t] = o;
+    }
+}
+
+// First merge stage for many splits: workgroup (row, g) combines splits
+// [32 g, 32 g + 32) of the row by log-sum-exp into one partial of the same
+// form (max, sum, A_y, A_z), so the final merge reads few partials.
+constexpr int kMergeGroup = 32;
+__global__ __launch_bounds__(256) void decode_merge_group_kernel(const float* part, int nsplit, int width,
+                                                                 float* out, int ngroup) {
+    __shared__ float fw[kMergeGroup];
+    __shared__ float red[2];
+    const int t = threadIdx.x;
+    const int64_t row = blockIdx.x;
+    const int g = blockIdx.y;
+    const int s0 = g * kMergeGroup, cnt = min(kMergeGroup, nsplit - s0);
+    const float* base = part + (row * nsplit + s0) * (int64_t)width;
+    if (t < 64) {
+        const float ms = t < cnt ? base[(int64_t)t * width] : -INFINITY;
+        const float mx = wave_max(ms);
+        const float f = (ms == -INFINITY) ? 0.f : expf(ms - mx);
+        if (t < kMergeGroup) fw[t] = f;
+        const float lw = wave_sum(t < cnt ? f * base[(int64_t)t * width + 1] : 0.f);
+        if (t == 0) {
+            red[0] = mx;
+            red[1] = lw;
+        }
+    }
+    __syncthreads();
+    float* dst = out + (row * ngroup + g) * (int64_t)width;
+    for (int c = t; c < width; c += blockDim.x) {
+        float v;
+        if (c == 0) v = red[0];
+        else if (c == 1) v = red[1];
+        else {
+            float x[kMergeGroup];
+#pragma unroll
+            for (int s = 0; s < kMergeGroup; ++s) x[s] = s < cnt ? base[(int64_t)s * width + c] : 0.f;
+            v = 0.f;
+#pragma unroll
+            for (int s = 0; s < kMergeGroup; ++s) v = fmaf(s < cnt ? fw[s] : 0.f, x[s], v);
+        }
+        dst[c] = v;
     }
 }
 
@@ -773,7 +822,9 @@ size_t decode_workspace_bytes(const tq_codebook* ck, const tq_codebook* cv, int6
     if (decode_mfma_supported(ck, cv)) {
         int nsplit = 1, split_len = 0;
         decode_mfma_plan(B, Hq, h_kv, L_cap, &nsplit, &split_len);
-        return align256(qdigits_workspace_bytes(ck, (int64_t)rows)) + align256(rows * nsplit * (2 + d + mv) * 4);
+        const size_t ngroup = (size_t)(nsplit + kMergeGroup - 1) / kMergeGroup;
+        return align256(qdigits_workspace_bytes(ck, (int64_t)rows)) + align256(rows * nsplit * (2 + d + mv) * 4) +
+               align256(rows * ngroup * (2 + d + mv) * 4);
     }
     const int ns = decode_nsplit(bkg > 0 ? bkg : 1, L_cap);
     return align256(rows * (d + mk) * 4) + align256(rows * ns * (2 + d + mv) * 4);
@@ -969,6 +1020,17 @@ hipError_t launch_decode(const tq_codebook* ck, const tq_codebook* cv, const tq_
         if (e != hipSuccess) return e;
         mk.part = part;
         mk.nsplit = nsplit;
+        if (nsplit > 2 * kMergeGroup) {
+            // many splits: a first stage reduces groups of 32 in parallel
+            const int ngroup = (nsplit + kMergeGroup - 1) / kMergeGroup;
+            float* part2 = part + align256(rows * nsplit * (2 + d + m) * 4) / 4;
+            hipLaunchKernelGGL(decode_merge_group_kernel, dim3((unsigned)rows, (unsigned)ngroup), dim3(256), 0, stream,
+                               part, nsplit, 2 + d + m, part2, ngroup);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            mk.part = part2;
+            mk.nsplit = ngroup;
+        }
         if (d == 64) hipLaunchKernelGGL(decode_merge_kernel<64>, dim3((unsigned)rows), dim3(256), 0, stream, mk);
         else hipLaunchKernelGGL(decode_merge_kernel<128>, dim3((unsigned)rows), dim3(256), 0, stream, mk);
         return hipGetLastError();

@@ -11,8 +11,8 @@
 // "TurboQuant: Uma Nova Abordagem", the QJL dequantiser; FibQuant summary,
 // section 2.3: lookup, inverse rotation, norm scale).
 //
-// A workgroup (four waves) owns one split of one KV head (at most 512 keys
-// for up to four queries, 256 for up to eight) and makes two passes over it:
+// A workgroup (four waves) owns one split of at most 512 keys of one KV head
+// and makes two passes over it:
 //  1. the logit of every key with the exact int8-MFMA tile of the scan (one
 //     16-key tile per wave per 64 keys), kept in LDS, plus the split's max
 //     logit per query and the max of nu and nu*gamma over its values;
@@ -63,7 +63,7 @@ struct DecM {
 
 template <int NRT>
 constexpr int split_max() {
-    return NRT == 1 ? 512 : 256;
+    return 512;
 }
 
 typedef __attribute__((address_space(3))) intx2* lds_intx2_ptr;

@@ -249,8 +249,13 @@ struct TileLogit {
         r.sg = NCS > 0 ? sp[(qk * per) >> 5] : 0u;
     }
 
-    // out[rt] = <q', t[c]> + sqrt(pi/2)/m gamma <s, z>  (not yet times nu)
-    __device__ void compute(const Raw& r, float gm, int per, int lane, double out[NRT]) const {
+    // integer digit sums of one tile (before their combination)
+    struct Acc {
+        intx4 y[NRT][3];
+        intx4 z[NRT];
+    };
+
+    __device__ void mma(const Raw& r, int per, int lane, Acc& A) const {
         const int qk = lane >> 4;
         intx4 bd[NC][3];
 #pragma unroll
@@ -277,32 +282,45 @@ struct TileLogit {
         }
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
-            intx4 acc[3];
 #pragma unroll
-            for (int bb = 0; bb < 3; ++bb) acc[bb] = intx4{0, 0, 0, 0};
+            for (int bb = 0; bb < 3; ++bb) A.y[rt][bb] = intx4{0, 0, 0, 0};
 #pragma unroll
             for (int c = 0; c < NC; ++c)
 #pragma unroll
                 for (int bb = 0; bb < 3; ++bb)
-                    acc[bb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[rt][c], bd[c][bb], acc[bb], 0, 0, 0);
-            intx4 accz = intx4{0, 0, 0, 0};
+                    A.y[rt][bb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[rt][c], bd[c][bb], A.y[rt][bb], 0, 0, 0);
+            A.z[rt] = intx4{0, 0, 0, 0};
 #pragma unroll
             for (int cs = 0; cs < NCS; ++cs)
-                accz = __builtin_amdgcn_mfma_i32_16x16x64_i8(as[rt][cs], bz[cs], accz, 0, 0, 0);
-            // acc[b][a]: digit a of q' (weight 2^(7(3-a))) times digit b of t
-            // (weight 2^(8(2-b))); |acc| <= 128 * 64 * 128 = 2^20
+                A.z[rt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(as[rt][cs], bz[cs], A.z[rt], 0, 0, 0);
+        }
+    }
+
+    // out[rt] = <q', t[c]> + sqrt(pi/2)/m gamma <s, z>  (not yet times nu)
+    __device__ void finish(const Acc& A, float gm, double out[NRT]) const {
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+            // y[b][a]: digit a of q' (weight 2^(7(3-a))) times digit b of t
+            // (weight 2^(8(2-b))); |y| <= 128 * 64 * 128 = 2^20
             double V = 0.0;
 #pragma unroll
-            for (int bb = 0; bb < 3; ++bb) V = V * 256.0 + digits4_value(acc[bb]);
+            for (int bb = 0; bb < 3; ++bb) V = V * 256.0 + digits4_value(A.y[rt][bb]);
             double logit = V * qscale[rt];
             if constexpr (NCS > 0) {
                 // sum_l s_l z_l = 2 sum_l s_l bit_l - sum_l s_l
-                const double Z = ((double)accz[0] * 2097152.0 + (double)accz[1] * 16384.0) +
-                                 ((double)accz[2] * 128.0 + (double)accz[3]);
+                const intx4& z = A.z[rt];
+                const double Z = ((double)z[0] * 2097152.0 + (double)z[1] * 16384.0) +
+                                 ((double)z[2] * 128.0 + (double)z[3]);
                 logit += cq * (double)gm * (2.0 * Z * sscale[rt] - ssum[rt]);
             }
             out[rt] = logit;
         }
+    }
+
+    __device__ void compute(const Raw& r, float gm, int per, int lane, double out[NRT]) const {
+        Acc A;
+        mma(r, per, lane, A);
+        finish(A, gm, out);
     }
 };
 

@@ -228,43 +228,67 @@ __global__ __launch_bounds__(256) void logits_mfma_kernel(LogM p) {
     const int sl = clamp_len2(p.seq_len, b, p.L_cap);
     const int kend = min(sl, p.k0 + p.klen);
     const int kbeg = p.k0 + (blockIdx.y * (blockDim.x >> 6) + wave) * p.tiles_per_wave * 16;
-    // per-lane bases at the wave's first key; a tile advances them by 16 records
-    const int64_t rec0 = bk * p.L_cap + kbeg;
-    const uint32_t* cbase = p.codes + rec0 * Q::CW + Q::word0(qk);
+    const int ntile = min(p.tiles_per_wave, (kend - kbeg + 15) / 16);  // <= 0: nothing to do
+    if (ntile <= 0) return;
+    const int nfull = min(p.tiles_per_wave, (kend - kbeg) / 16);  // tiles with all 16 keys below kend
     const int mw = p.m >> 5;
     const int per = p.m >> 2;  // sketch rows per lane group (8, 16, 32, ...)
-    const uint32_t* sbase = p.signs + rec0 * mw;
-    const float* nbase = p.norm + rec0;
-    const float* gbase = p.rnorm + rec0;
-    // software pipeline: the record words of the next two tiles are in
-    // flight while a tile computes; three register slots in rotation, the
-    // loop unrolled by three so that no slot is ever copied
-    const int ntile = min(p.tiles_per_wave, (kend - kbeg + 15) / 16);  // <= 0: nothing to do
-    typename T::Raw rs[3];
-    float nus[3] = {0.f, 0.f, 0.f}, gms[3] = {0.f, 0.f, 0.f};
+    // per-lane pointers at the lane's key of the wave's first tile; a tile
+    // advances them by 16 records
+    const int64_t rec0 = bk * p.L_cap + kbeg + n;
+    const uint32_t* cptr = p.codes + rec0 * Q::CW + Q::word0(qk);
+    const uint32_t* sptr = p.signs + rec0 * mw;
+    const float* nptr = p.norm + rec0;
+    const float* gptr = p.rnorm + rec0;
+    const int g_lane = gq0 + qk;  // the lane's query in row tile 0
+    float* optr = p.out + (rowbase + g_lane) * p.ld + (kbeg + n - p.col0);
+    const int64_t ort = 4 * p.ld;  // next row tile
+    const bool rows_full = gq0 + 4 * NRT <= G;
+
+    // Tiles go in pairs: both tiles' MFMAs are issued before either is
+    // combined, so one tile's operand building and digit combination overlap
+    // the other's matrix work.  The records of the next pair are loaded while
+    // a pair computes (four register slots, the loop unrolled by two pairs so
+    // that no slot is copied).  Full tiles take a path without key guards.
+    typename T::Raw rs[4];
+    float nus[4], gms[4];
     auto fetch = [&](int tile, int slot) {
-        const int kk = min(kbeg + tile * 16 + n, kend - 1) - kbeg;
-        T::load(cbase + kk * Q::CW, sbase + kk * mw, per, lane, rs[slot]);
-        nus[slot] = nbase[kk];
-        gms[slot] = NCS > 0 ? gbase[kk] : 0.0f;
+        // a partial last tile reads the record of its last valid key instead
+        const int off = tile < nfull ? tile * 16 : min(tile * 16, kend - 1 - kbeg - n);
+        T::load(cptr + off * Q::CW, sptr + off * mw, per, lane, rs[slot]);
+        nus[slot] = nptr[off];
+        gms[slot] = NCS > 0 ? gptr[off] : 0.0f;
     };
-    auto step = [&](int tile, int slot) {
-        if (tile + 2 < ntile) fetch(tile + 2, (slot + 2) % 3);
-        const int key = kbeg + tile * 16 + n;
-        double lg[NRT];
-        tl.compute(rs[slot], gms[slot], per, lane, lg);
+    auto store = [&](int tile, int slot, const double* lg) {
+        const bool ok = tile < nfull || kbeg + tile * 16 + n < kend;
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
-            const int g = gq0 + 4 * rt + qk;
-            if (key < kend && g < G) p.out[(rowbase + g) * p.ld + (key - p.col0)] = (float)((double)nus[slot] * lg[rt]);
+            const float v = (float)((double)nus[slot] * lg[rt]);
+            if (rows_full && tile < nfull) optr[rt * ort + tile * 16] = v;
+            else if (ok && g_lane + 4 * rt < G) optr[rt * ort + tile * 16] = v;
         }
     };
-    if (ntile > 0) fetch(0, 0);
+    auto pair = [&](int tile, int s0) {
+        const int s2 = s0 ^ 2;
+        if (tile + 2 < ntile) fetch(tile + 2, s2);
+        if (tile + 3 < ntile) fetch(tile + 3, s2 + 1);
+        typename T::Acc a0, a1;
+        tl.mma(rs[s0], per, lane, a0);
+        const bool two = tile + 1 < ntile;
+        if (two) tl.mma(rs[s0 + 1], per, lane, a1);
+        double lg[NRT];
+        tl.finish(a0, gms[s0], lg);
+        store(tile, s0, lg);
+        if (two) {
+            tl.finish(a1, gms[s0 + 1], lg);
+            store(tile + 1, s0 + 1, lg);
+        }
+    };
+    fetch(0, 0);
     if (ntile > 1) fetch(1, 1);
-    for (int tile = 0; tile < ntile; tile += 3) {
-        step(tile, 0);
-        if (tile + 1 < ntile) step(tile + 1, 1);
-        if (tile + 2 < ntile) step(tile + 2, 2);
+    for (int tile = 0; tile < ntile; tile += 4) {
+        pair(tile, 0);
+        if (tile + 2 < ntile) pair(tile + 2, 2);
     }
 }
 
