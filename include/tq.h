@@ -46,10 +46,15 @@
  * n = (seq * h_kv + head) * L_cap + token):
  *   norm [n]          float    nu = ||x||_2 (after RoPE for keys)
  *   rnorm[n]          float    gamma = ||y - t[c]||_2 (absent when m == 0)
- *   codes[n][b*d/32]  uint32   coordinate i's code is bits [b*i, b*i+b) of
- *                              the LSB-first bit string of the words (bit k
- *                              is bit k%32 of word k/32); code 0 is the most
- *                              negative level
+ *   codes[n][b*d/32]  uint32   code 0 is the most negative level; bit k of
+ *                              the words' bit string is bit k%32 of word k/32.
+ *                              b = 1, 2, 4: coordinate i's code is bits
+ *                              [b*i, b*i+b).  b = 3: coordinates in groups of
+ *                              32 take words 3g..3g+2 (W0..W2); coordinate
+ *                              j < 24 of a group is bits 8(j%4) + 3((j%8)/4)
+ *                              .. +2 of W_{j/8}; for j = 24 + r the low two
+ *                              bits are bits 8(r%4)+6, +7 of W_{r/4} and the
+ *                              high bit is bit 8(r%4) + 6 + r/4 of W2
  *   signs[n][m/32]    uint32   bit l (bit l%32 of word l/32) is 1 iff
  *                              (S e)_l >= 0
  */
@@ -175,7 +180,9 @@ tq_status tq_codebook_export(const tq_codebook* cb, float* levels, float* thresh
  *                 or both NULL for no RoPE; tok_offset + n_tok <= rope_npos
  *   ws, ws_bytes  device workspace, at least tq_workspace_bytes(ck, cv,
  *                 TQ_OP_ENCODE, n_seq*n_tok*h_kv, ...) (0 for Hadamard codebooks)
- * n_seq*n_tok*h_kv == 0 is a no-op returning TQ_OK.
+ * n_seq*n_tok*h_kv == 0 is a no-op returning TQ_OK.  Hadamard codebooks
+ * take at most 2^31 - 1 tiles of 32 tokens x 1 head per call
+ * (TQ_EUNSUPPORTED beyond).
  */
 tq_status tq_encode_kv(const tq_codebook* ck, const tq_codebook* cv, const void* k, const void* v,
                        int32_t dtype, int32_t n_seq, int32_t n_tok, int32_t h_kv,

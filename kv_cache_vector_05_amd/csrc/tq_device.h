@@ -29,6 +29,21 @@ __device__ __forceinline__ int clamp_len(const int32_t* seq_len, int b, int L_ca
     return s < 0 ? 0 : (s > L_cap ? L_cap : s);
 }
 
+// Division by a run-time constant d >= 1 for dividends below 2^31, by a
+// multiply-high and a shift (Granlund and Montgomery, PLDI 1994): with
+// s = ceil(log2 d) and m = floor(2^32 (2^s - d) / d) + 1,
+// n / d = (mulhi(n, m) + n) >> s.  Set up on the host.
+struct FastDiv {
+    uint32_t d, m, s;
+    __host__ __device__ FastDiv() : d(1), m(0), s(0) {}
+    __host__ explicit FastDiv(uint32_t div) : d(div) {
+        s = 0;
+        while ((1ull << s) < div) ++s;
+        m = (uint32_t)(((1ull << 32) * ((1ull << s) - div)) / div + 1);
+    }
+    __device__ uint32_t div(uint32_t n) const { return (__umulhi(n, m) + n) >> s; }
+};
+
 // digit b of the levels of the 4 codes in the bytes of sel
 __device__ __forceinline__ uint32_t lut4(const uint32_t* tdig, int b, uint32_t sel) {
     return __builtin_amdgcn_perm(tdig[2 * b + 1], tdig[2 * b], sel);

@@ -38,6 +38,7 @@ struct EncK {
     int32_t n_seq, n_tok, h_kv, tok_offset, L_cap, tok_blocks;
     int64_t n_tiles;
     int32_t rope_stage;  // the block's four waves share their tokens: RoPE rows staged in LDS
+    dev::FastDiv div_h, div_tb;  // by h_kv and by tok_blocks (tile indices are below 2^31)
     const float* rope_cos;
     const float* rope_sin;
     const float* sigma;
@@ -83,49 +84,44 @@ __device__ __forceinline__ void xchg(float& a, float& b) {
 // the other side, a decision within rounding of the boundary).  Returns the
 // code and the residual e = y - t_c = sign(y) (|y| - t_{K/2+c'}).
 // pt: the K/2-1 upper thresholds, pl: the K/2 upper levels (scaled).
-//
-// Comparisons of non-negative floats are made on their bit patterns as
-// integers (same order), giving all-ones/all-zeros lane masks in vector
-// registers: no compare masks pile up in scalar registers.
-__device__ __forceinline__ uint32_t below(float a, float t) {  // a < t ? ~0 : 0, for a, t >= 0
-    return (uint32_t)(((int32_t)__float_as_uint(a) - (int32_t)__float_as_uint(t)) >> 31);
-}
-__device__ __forceinline__ float pick(uint32_t m, float if_set, float if_clear) {
-    return __uint_as_float((__float_as_uint(if_set) & m) | (__float_as_uint(if_clear) & ~m));
-}
 
 template <int BITS>
 __device__ __forceinline__ uint32_t quantise(float y, const float* pt, const float* pl, float* e) {
-    constexpr uint32_t K1 = (1u << BITS) - 1u;
+    constexpr uint32_t KH = 1u << (BITS - 1);
     const float a = fabsf(y);
-    uint32_t lowbits;  // bits of c' cleared (all-ones mask bits of "below")
+    uint32_t cp;  // code of |y| among the upper cells
     float lv;
     if constexpr (BITS == 1) {
-        lowbits = 0u;
+        cp = 0u;
         lv = pl[0];
     } else if constexpr (BITS == 2) {
-        const uint32_t n0 = below(a, pt[0]);
-        lowbits = n0 & 1u;
-        lv = pick(n0, pl[0], pl[1]);
+        const bool m0 = a >= pt[0];
+        cp = (uint32_t)m0;
+        lv = m0 ? pl[1] : pl[0];
     } else if constexpr (BITS == 3) {
-        const uint32_t n1 = below(a, pt[1]);
-        const uint32_t n0 = below(a, pick(n1, pt[0], pt[2]));
-        lowbits = (n1 & 2u) | (n0 & 1u);
-        lv = pick(n0, pick(n1, pl[0], pl[2]), pick(n1, pl[1], pl[3]));
+        const bool m1 = a >= pt[1];
+        const bool m0 = a >= (m1 ? pt[2] : pt[0]);
+        cp = (m1 ? 2u : 0u) + (uint32_t)m0;
+        const float l0 = m1 ? pl[2] : pl[0];
+        const float l1 = m1 ? pl[3] : pl[1];
+        lv = m0 ? l1 : l0;
     } else {
-        const uint32_t n2 = below(a, pt[3]);
-        const uint32_t n1 = below(a, pick(n2, pt[1], pt[5]));
-        const uint32_t n0 = below(a, pick(n1, pick(n2, pt[0], pt[4]), pick(n2, pt[2], pt[6])));
-        lowbits = (n2 & 4u) | (n1 & 2u) | (n0 & 1u);
-        const float q0 = pick(n2, pl[0], pl[4]), q1 = pick(n2, pl[1], pl[5]);
-        const float q2 = pick(n2, pl[2], pl[6]), q3 = pick(n2, pl[3], pl[7]);
-        lv = pick(n0, pick(n1, q0, q2), pick(n1, q1, q3));
+        const bool m2 = a >= pt[3];
+        const bool m1 = a >= (m2 ? pt[5] : pt[1]);
+        const float t0 = m2 ? pt[4] : pt[0];
+        const float t1 = m2 ? pt[6] : pt[2];
+        const bool m0 = a >= (m1 ? t1 : t0);
+        cp = (m2 ? 4u : 0u) + (m1 ? 2u : 0u) + (uint32_t)m0;
+        const float q0 = m2 ? pl[4] : pl[0], q1 = m2 ? pl[5] : pl[1];
+        const float q2 = m2 ? pl[6] : pl[2], q3 = m2 ? pl[7] : pl[3];
+        const float r0 = m1 ? q2 : q0, r1 = m1 ? q3 : q1;
+        lv = m0 ? r1 : r0;
     }
     const uint32_t yb = __float_as_uint(y);
     const uint32_t neg = (uint32_t)((int32_t)yb >> 31);
     *e = __uint_as_float(__float_as_uint(a - lv) ^ (yb & 0x80000000u));
-    // y >= 0: K/2 + c' = K1 ^ lowbits;  y < 0: K/2 - 1 - c' = lowbits
-    return lowbits ^ (~neg & K1);
+    // y >= 0: K/2 + c';  y < 0: K/2 - 1 - c' = (~c') + K/2
+    return (cp ^ neg) + KH;
 }
 
 // RoPE rows of the 32 tokens of the tile step at `base` (table entries of
@@ -135,7 +131,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 template <int HALF, int NQ>
 __device__ __forceinline__ void rope_stage_load(const EncK& p, int64_t base, const int (&tab)[NQ],
                                                 const int (&row)[NQ], const int (&c4)[NQ], f32x4 (&pre)[NQ]) {
-    const int tb0 = (int)((base / p.h_kv) % p.tok_blocks);
+    const uint32_t r0 = p.div_h.div((uint32_t)base);
+    const int tb0 = (int)(r0 - p.div_tb.div(r0) * (uint32_t)p.tok_blocks);
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
         const int pos = p.tok_offset + min(tb0 * 32 + row[j], p.n_tok - 1);
@@ -225,10 +222,11 @@ __global__ __launch_bounds__(256) void encode_rht_kernel(EncK p) {
       if (stage && base + blk_stride < p.n_tiles)
           rope_stage_load<HALF, NQ>(p, base + blk_stride, st_table, st_row, st_c4, pre);
       if (tile < p.n_tiles) {
-        const int head = (int)(tile % p.h_kv);
-        const int64_t r = tile / p.h_kv;
-        const int tb = (int)(r % p.tok_blocks);
-        const int seq = (int)(r / p.tok_blocks);
+        const uint32_t r = p.div_h.div((uint32_t)tile);
+        const int head = (int)((uint32_t)tile - r * (uint32_t)p.h_kv);
+        const uint32_t sq = p.div_tb.div(r);
+        const int tb = (int)(r - sq * (uint32_t)p.tok_blocks);
+        const int seq = (int)sq;
         const int token = tb * 32 + v;
         const bool valid = token < p.n_tok;
 
@@ -319,14 +317,14 @@ __global__ __launch_bounds__(256) void encode_rht_kernel(EncK p) {
         const float nu = sqrtf(ss);
         const float scale = nu > 0.0f ? yscale / nu : 0.0f;
 
-        // sign flips (masks re-read from LDS per tile: the opaque pointer keeps
+        // sign flips (masks re-read from LDS per tile: the opaque offset keeps
         // the compiler from holding 64 mask registers across the tile loop)
         {
-            const uint4* fl = s_flip + h * (HALF / 4);
-            asm volatile("" : "+v"(fl));
+            int fo = h * (HALF / 4);
+            asm volatile("" : "+v"(fo));
 #pragma unroll
             for (int c = 0; c < HALF / 4; ++c) {
-                const uint4 mk = fl[c];
+                const uint4 mk = s_flip[fo + c];
                 x[4 * c + 0] = __uint_as_float(__float_as_uint(x[4 * c + 0]) ^ mk.x);
                 x[4 * c + 1] = __uint_as_float(__float_as_uint(x[4 * c + 1]) ^ mk.y);
                 x[4 * c + 2] = __uint_as_float(__float_as_uint(x[4 * c + 2]) ^ mk.z);
@@ -679,6 +677,8 @@ hipError_t launch_encode(const tq_codebook* cb, const EncodeArgs& a, hipStream_t
         const int64_t cap = (int64_t)g_num_cus * 8;
         const int grid = (int)(blocks_needed < cap ? blocks_needed : cap);
         p.rope_stage = (a.rope_cos != nullptr && a.h_kv % 4 == 0) ? 1 : 0;
+        p.div_h = dev::FastDiv((uint32_t)a.h_kv);
+        p.div_tb = dev::FastDiv((uint32_t)p.tok_blocks);
         const size_t lds = p.rope_stage ? (size_t)2 * 32 * (d / 2 + 4) * sizeof(float) : 0;
         hipLaunchKernelGGL(fn, dim3(grid), dim3(256), lds, stream, p);
         return hipGetLastError();

@@ -575,6 +575,8 @@ tq_status tq_encode_kv(const tq_codebook* ck, const tq_codebook* cv, const void*
             if (rope_npos < tok_offset + n_tok) return fail(TQ_EINVAL, "RoPE table shorter than the last position");
             if (sd.cb->spec.d % 2) return fail(TQ_EINVAL, "RoPE needs an even d");
         }
+        if (!sd.cb->dense && (int64_t)n_seq * ((n_tok + 31) / 32) * h_kv >= (int64_t)1 << 31)
+            return fail(TQ_EUNSUPPORTED, "too many vectors in one encode call (split it)");
         if (sd.cb->dense && nvec > 0) {
             const size_t wsn = encode_workspace_bytes(sd.cb, nvec);
             if (!ws || ws_bytes < wsn) return fail(TQ_EINVAL, "workspace too small for the dense encoder");
