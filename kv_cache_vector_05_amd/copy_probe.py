@@ -29,6 +29,21 @@ def main(argv=None):
     for _ in range(args.reps):
         dst.copy_(src)
     torch.cuda.synchronize()
+    # event-timed read-and-write (copy), write-only (fill) and read-only (sum)
+    # rates, for context next to the kernels' algorithmic rates
+    nbytes = n * 4
+    for label, fn, moved in (("copy", lambda: dst.copy_(src), 2 * nbytes),
+                             ("fill", lambda: dst.fill_(2.0), nbytes),
+                             ("sum", lambda: src.sum(), nbytes)):
+        fn()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(args.reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / args.reps
+        print(f"{label}: {moved / ms / 1e6:.0f} GB/s ({ms * 1e3:.0f} us per {moved / 2**20:.0f} MiB)", flush=True)
     print(f"copied {args.mib} MiB x {args.reps}", flush=True)
     return 0
 

@@ -77,6 +77,12 @@ __device__ __forceinline__ intx4 tr_operand(const int8_t* blk, int lane) {
     return intx4{lo[0], lo[1], hi[0], hi[1]};
 }
 
+// four base-128 digits (0..127, most significant in byte 0) of 0 <= X < 2^28:
+// the weights are non-negative, so no balancing is needed
+__device__ __forceinline__ uint32_t digits4_unsigned(uint32_t X) {
+    return ((X >> 21) & 0x7Fu) | ((X >> 6) & 0x7F00u) | ((X << 9) & 0x7F0000u) | ((X << 24) & 0x7F000000u);
+}
+
 // value of four rows holding the base-128 digits of one operand (double: the
 // sums of a whole split can exceed the int32 range once scaled by 128)
 __device__ __forceinline__ double digit_rows(const intx4& a) {
@@ -220,8 +226,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
     // weights: w = p nu <= max nu, w gamma <= max nu gamma (p <= 1)
     const int sw = dev::fixed_shift(numax);
     const int sz = dev::fixed_shift(ngmax);
-    const double wscale = ldexp(1.0, sw);
-    const double zscale = ldexp(1.0, sz);
+    // 2^sw, 2^sz as floats (w * 2^sw < 2^26 is exact; tiny norms clamp the exponent)
+    const float wscale = ldexpf(1.0f, min(sw, 126));
+    const float zscale = ldexpf(1.0f, min(sz, 126));
 
     // ---------------- pass 2: weighted value sums on the matrix cores
     float lsum[NRT];
@@ -266,14 +273,14 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
             const float a = lgs[((wave * NCH + c) * NRT + rt) * 64 + lane];
-            const float pj = expf(a - mx[rt]);  // exp(-inf) = 0 past the end
+            const float pj = __expf(a - mx[rt]);  // exp(-inf) = 0 past the end
             lsum[rt] += pj;
             const float w = pj * vn;
-            const int Wi = (int)rint((double)w * wscale);
-            *reinterpret_cast<uint32_t*>(wd + ((0 * NRT + rt) * 64 + row) * 16 + 4 * qk) = dev::digits4_packed(Wi);
+            const uint32_t Wi = (uint32_t)rintf(w * wscale);
+            *reinterpret_cast<uint32_t*>(wd + ((0 * NRT + rt) * 64 + row) * 16 + 4 * qk) = digits4_unsigned(Wi);
             if constexpr (M > 0) {
-                const int Zi = (int)rint((double)(w * vg) * zscale);
-                *reinterpret_cast<uint32_t*>(wd + ((1 * NRT + rt) * 64 + row) * 16 + 4 * qk) = dev::digits4_packed(Zi);
+                const uint32_t Zi = (uint32_t)rintf((w * vg) * zscale);
+                *reinterpret_cast<uint32_t*>(wd + ((1 * NRT + rt) * 64 + row) * 16 + 4 * qk) = digits4_unsigned(Zi);
             }
         }
         // level digits of the lane's coordinate quarter: column blocks qk*CBW + j

@@ -228,9 +228,10 @@ __global__ __launch_bounds__(256) void logits_mfma_kernel(LogM p) {
     const int sl = clamp_len2(p.seq_len, b, p.L_cap);
     const int kend = min(sl, p.k0 + p.klen);
     const int kbeg = p.k0 + (blockIdx.y * (blockDim.x >> 6) + wave) * p.tiles_per_wave * 16;
-    const int ntile = min(p.tiles_per_wave, (kend - kbeg + 15) / 16);  // <= 0: nothing to do
+    // (tile counts are wave-uniform: kept in scalar registers for scalar branches)
+    const int ntile = __builtin_amdgcn_readfirstlane(min(p.tiles_per_wave, (kend - kbeg + 15) / 16));
     if (ntile <= 0) return;
-    const int nfull = min(p.tiles_per_wave, (kend - kbeg) / 16);  // tiles with all 16 keys below kend
+    const int nfull = __builtin_amdgcn_readfirstlane(min(p.tiles_per_wave, (kend - kbeg) / 16));
     const int mw = p.m >> 5;
     const int per = p.m >> 2;  // sketch rows per lane group (8, 16, 32, ...)
     // per-lane pointers at the lane's key of the wave's first tile; a tile
@@ -253,11 +254,17 @@ __global__ __launch_bounds__(256) void logits_mfma_kernel(LogM p) {
     typename T::Raw rs[4];
     float nus[4], gms[4];
     auto fetch = [&](int tile, int slot) {
-        // a partial last tile reads the record of its last valid key instead
-        const int off = tile < nfull ? tile * 16 : min(tile * 16, kend - 1 - kbeg - n);
-        T::load(cptr + off * Q::CW, sptr + off * mw, per, lane, rs[slot]);
-        nus[slot] = nptr[off];
-        gms[slot] = NCS > 0 ? gptr[off] : 0.0f;
+        if (tile < nfull) {  // uniform record offset
+            const int off = tile * 16;
+            T::load(cptr + off * Q::CW, sptr + off * mw, per, lane, rs[slot]);
+            nus[slot] = nptr[off];
+            gms[slot] = NCS > 0 ? gptr[off] : 0.0f;
+        } else {  // a partial last tile reads the record of its last valid key instead
+            const int off = min(tile * 16, kend - 1 - kbeg - n);
+            T::load(cptr + off * Q::CW, sptr + off * mw, per, lane, rs[slot]);
+            nus[slot] = nptr[off];
+            gms[slot] = NCS > 0 ? gptr[off] : 0.0f;
+        }
     };
     auto store = [&](int tile, int slot, const double* lg) {
         const bool ok = tile < nfull || kbeg + tile * 16 + n < kend;
