@@ -66,9 +66,11 @@ def lib():
     """The loaded library (raises if it has not been built)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(f"libtq.so is not built ({LIB_PATH}); run python -m kv_cache_vector_05_amd.build")
-        L = C.CDLL(LIB_PATH)
+        # TQ_LIBRARY names another build of the same ABI (side-by-side timing)
+        path = os.environ.get("TQ_LIBRARY", LIB_PATH)
+        if not os.path.exists(path):
+            raise ImportError(f"libtq.so is not built ({path}); run python -m kv_cache_vector_05_amd.build")
+        L = C.CDLL(path)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(L, name)
             fn.restype = res

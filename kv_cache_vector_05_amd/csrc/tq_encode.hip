@@ -117,11 +117,11 @@ __device__ __forceinline__ uint32_t quantise(float y, const float* pt, const flo
         const float r0 = m1 ? q2 : q0, r1 = m1 ? q3 : q1;
         lv = m0 ? r1 : r0;
     }
-    const uint32_t yb = __float_as_uint(y);
-    const uint32_t neg = (uint32_t)((int32_t)yb >> 31);
-    *e = __uint_as_float(__float_as_uint(a - lv) ^ (yb & 0x80000000u));
-    // y >= 0: K/2 + c';  y < 0: K/2 - 1 - c' = (~c') + K/2
-    return (cp ^ neg) + KH;
+    // e = y - t_c with t_c = sign(y) * lv (one bitfield insert and a subtract)
+    *e = y - __builtin_copysignf(lv, y);
+    // y >= 0: K/2 + c';  y < 0: K/2 - 1 - c' = (K/2 + c') ^ (K - 1)
+    const uint32_t neg = (uint32_t)((int32_t)__float_as_uint(y) >> 31);
+    return (KH | cp) ^ (neg & (2u * KH - 1u));
 }
 
 // RoPE rows of the 32 tokens of the tile step at `base` (table entries of
@@ -148,7 +148,7 @@ __device__ __forceinline__ void rope_stage_store(f32x4* lds, const int (&tab)[NQ
 }
 
 template <int D, int BITS, int M, bool BF16, bool ROPE>
-__global__ __launch_bounds__(256) void encode_rht_kernel(EncK p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ROPE ? 2 : 3))) void encode_rht_kernel(EncK p) {
     constexpr int HALF = D / 2;
     constexpr int QTR = D / 4;
     constexpr int KH = 1 << (BITS - 1);
