@@ -55,6 +55,8 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // lanes l and l ^ 32 exchange v (v_permlane32_swap): returns {own half's r0, r1}
 // where for lanes < 32 r0 = own and r1 = partner, and for lanes >= 32 r0 =
@@ -124,6 +126,47 @@ __device__ __forceinline__ uint32_t quantise(float y, const float* pt, const flo
     return (KH | cp) ^ (neg & (2u * KH - 1u));
 }
 
+// K/2 + c' where c' is the code of a = |y| among the upper cells of a
+// symmetric table (pt: the K/2-1 upper thresholds); y's code is this value for
+// y >= 0 and its complement in K - 1 bits for y < 0.
+template <int BITS>
+__device__ __forceinline__ uint32_t upper_code(float a, const float* pt) {
+    if constexpr (BITS == 3) {
+        const bool m1 = a >= pt[1];
+        const bool m0 = a >= (m1 ? pt[2] : pt[0]);
+        return (m1 ? 6u : 4u) + (m0 ? 1u : 0u);
+    } else {
+        static_assert(BITS == 4, "byte-packed codes are used for 3 and 4 bits");
+        const bool m2 = a >= pt[3];
+        const bool m1 = a >= (m2 ? pt[5] : pt[1]);
+        const float t0 = m2 ? pt[4] : pt[0];
+        const float t1 = m2 ? pt[6] : pt[2];
+        const bool m0 = a >= (m1 ? t1 : t0);
+        return (m2 ? 12u : 8u) + (m1 ? 2u : 0u) + (m0 ? 1u : 0u);
+    }
+}
+
+// x = hi + lo (fp16 parts: hi = x rounded to nearest, lo = the exact
+// remainder x - hi rounded to nearest): x to within 2^-22 |x| while lo stays
+// normal.  Per pair: one packed conversion and two mixed-precision FMAs that
+// form x - hi exactly before rounding.  The asm operands are the floats as
+// stored, so the split cannot be fused with the product that made them.
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
+    asm volatile("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(hi) : "v"(a), "v"(b));
+    asm volatile(
+        "v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mixhi_f16 %0, %1, -1.0, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+        : "=&v"(lo)
+        : "v"(hi), "v"(a), "v"(b));
+}
+__device__ __forceinline__ void split_f16(const float* x, half8& hi, half8& lo) {
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) split_pair(x[2 * q], x[2 * q + 1], h[q], l[q]);
+    hi = __builtin_bit_cast(half8, make_uint4(h[0], h[1], h[2], h[3]));
+    lo = __builtin_bit_cast(half8, make_uint4(l[0], l[1], l[2], l[3]));
+}
+
 // RoPE rows of the 32 tokens of the tile step at `base` (table entries of
 // this thread's staging slots), and their store into the LDS buffer
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -148,31 +191,47 @@ __device__ __forceinline__ void rope_stage_store(f32x4* lds, const int (&tab)[NQ
 }
 
 template <int D, int BITS, int M, bool BF16, bool ROPE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ROPE ? 2 : 3))) void encode_rht_kernel(EncK p) {
+__global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
     constexpr int HALF = D / 2;
-    constexpr int QTR = D / 4;
+    constexpr int NOB = D / 32;            // 32-coordinate output blocks of H
+    constexpr int NKB = D / 16;            // 16-coordinate input steps of the MFMA
+    constexpr bool EXACT = BF16 && !ROPE;  // raw bf16 inputs are the MFMA operand as loaded
     constexpr int KH = 1 << (BITS - 1);
-    constexpr int CW = BITS * D / 32;     // code words per record
-    constexpr int WH = BITS * HALF / 32;  // code words per half
-    constexpr int NRB = M / 32;           // sketch row blocks (= sign words)
-    constexpr int NP = HALF / 8;          // MFMA K-steps (8 coordinates per lane half)
+    constexpr int CW = BITS * D / 32;      // code words per record
+    constexpr int NRB = M / 32;            // sketch row blocks (= sign words)
+    constexpr int NP = D / 16;             // sketch K-steps: chunks of 8 values per lane
     constexpr int SKN = M > 0 ? NRB * NP * 2 * 64 : 1;
     // residuals enter the sketch scaled by 2^8 so their fp16 low parts stay normal
     constexpr float ESCALE = 256.0f;
     __shared__ half8 s_sk[SKN];
-    // Hadamard sign flips as sign-bit masks, in the register order that
-    // follows the first lane exchange: lane half hh, register a*QTR + t holds
-    // coordinate a*HALF + hh*QTR + t
-    __shared__ uint4 s_flip[2 * HALF / 4];
+    // A operands of the Hadamard MFMAs, sign flips folded in: entry [kb][lane]
+    // holds H32[lane%32][16(kb%2) + 8(lane/32) + t] * sigma[16kb + 8(lane/32) + t]
+    // for t = 0..7 as bf16 (raw bf16 inputs) or fp16 (split inputs) +-1
+    __shared__ uint4 s_had[NKB * 64];
+    // scaled levels, indexed by code (3 and 4 bits: looked up by K/2 + c')
+    __shared__ float s_lvl[16];
 
     if constexpr (M > 0) {
         const half8* src = reinterpret_cast<const half8*>(p.sketch_mfma);
         for (int i = threadIdx.x; i < SKN; i += blockDim.x) s_sk[i] = src[i];
     }
-    for (int i = threadIdx.x; i < 2 * HALF; i += blockDim.x) {
-        const int hh = i / HALF, r = i % HALF;
-        const int coord = (r / QTR) * HALF + hh * QTR + (r % QTR);
-        reinterpret_cast<uint32_t*>(s_flip)[i] = p.sigma[coord] < 0.0f ? 0x80000000u : 0u;
+    if (threadIdx.x < 16) s_lvl[threadIdx.x] = threadIdx.x < 2 * KH ? p.levels[threadIdx.x] * ESCALE : 0.0f;
+    for (int i = threadIdx.x; i < NKB * 64; i += blockDim.x) {
+        const int kb = i >> 6, row = i & 31, hh = (i >> 5) & 1;
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            uint32_t pair = 0;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int t = 2 * q + s;
+                const int col = 16 * (kb & 1) + 8 * hh + t;
+                const bool neg = ((__popc(row & col) & 1) != 0) != (p.sigma[16 * kb + 8 * hh + t] < 0.0f);
+                pair |= ((EXACT ? 0x3F80u : 0x3C00u) | (neg ? 0x8000u : 0u)) << (16 * s);
+            }
+            w[q] = pair;
+        }
+        s_had[i] = make_uint4(w[0], w[1], w[2], w[3]);
     }
     __syncthreads();
 
@@ -192,12 +251,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ROPE ? 2 : 
     // waves encode four heads of the same tokens (h_kv a multiple of 4): the
     // rows of the next tile step are loaded into registers while the current
     // one computes, then written to LDS between two barriers.
-    constexpr int RS = HALF + 4;         // padded row stride (floats): conflict-free b128 reads
+    constexpr int RS = HALF + 4;                   // padded row stride (floats)
     constexpr int NQ = 2 * 32 * (HALF / 4) / 256;  // float4 per thread per stage (cos and sin)
-    extern __shared__ f32x4 s_rope4[];  // [cos, sin][32 tokens][RS / 4]
-    float* s_rope = reinterpret_cast<float*>(s_rope4);
+    extern __shared__ f32x4 s_rope4[];             // [cos, sin][32 tokens][RS / 4]
     const bool stage = ROPE && p.rope_stage;
-    // staging slot j of this thread: table (0 cos, 1 sin), token row, float4 column
     int st_table[NQ], st_row[NQ], st_c4[NQ];
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
@@ -218,9 +275,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ROPE ? 2 : 
     // the loop bound is the same for the whole block (barriers inside)
     for (; base < p.n_tiles; base += blk_stride) {
       const int64_t tile = base + (threadIdx.x >> 6);
-      f32x4 pre[NQ];  // the next step's rows, in flight during this step
-      if (stage && base + blk_stride < p.n_tiles)
-          rope_stage_load<HALF, NQ>(p, base + blk_stride, st_table, st_row, st_c4, pre);
+      // the next step's rows, in flight during this step's quantiser (loaded
+      // once this tile's own input registers are free)
+      f32x4 pre[NQ];
+      const bool prefetch = stage && base + blk_stride < p.n_tiles;
+      if (tile >= p.n_tiles && prefetch) rope_stage_load<HALF, NQ>(p, base + blk_stride, st_table, st_row, st_c4, pre);
       if (tile < p.n_tiles) {
         const uint32_t r = p.div_h.div((uint32_t)tile);
         const int head = (int)((uint32_t)tile - r * (uint32_t)p.h_kv);
@@ -229,185 +288,253 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ROPE ? 2 : 
         const int seq = (int)sq;
         const int token = tb * 32 + v;
         const bool valid = token < p.n_tok;
+        // lanes past the last token read the last token instead: an MFMA
+        // column only feeds its own vector, and these vectors are not stored
+        const int64_t off = (int64_t)seq * p.s_seq + (int64_t)min(token, p.n_tok - 1) * p.s_tok +
+                            (int64_t)head * p.s_head;
 
-        // lane half h reads coordinates [h*HALF, (h+1)*HALF): register j = coordinate h*HALF + j
-        float x[HALF];
-        if (valid) {
-            const int64_t off = (int64_t)seq * p.s_seq + (int64_t)token * p.s_tok + (int64_t)head * p.s_head + h * HALF;
-            if constexpr (BF16) {
-                const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.x) + off);
+        // B operands: input step kb is coordinates 16kb + 8h + t (t = 0..7)
+        // of this lane's vector
+        uint4 raw[BF16 ? NKB : 1];
+        float xv[BF16 ? 1 : NKB][8];
+        float ss = 0.0f;
+        if constexpr (BF16) {
+            const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.x) + off);
 #pragma unroll
-                for (int c = 0; c < HALF / 8; ++c) {
-                    const uint4 w = src[c];
-                    x[8 * c + 0] = bf16_lo(w.x);
-                    x[8 * c + 1] = bf16_hi(w.x);
-                    x[8 * c + 2] = bf16_lo(w.y);
-                    x[8 * c + 3] = bf16_hi(w.y);
-                    x[8 * c + 4] = bf16_lo(w.z);
-                    x[8 * c + 5] = bf16_hi(w.z);
-                    x[8 * c + 6] = bf16_lo(w.w);
-                    x[8 * c + 7] = bf16_hi(w.w);
-                }
-            } else {
-                const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(p.x) + off);
+            for (int kb = 0; kb < NKB; ++kb) raw[kb] = src[2 * kb + h];
+            // nu^2 from the bf16 pairs (RoPE keeps the norm)
 #pragma unroll
-                for (int c = 0; c < HALF / 4; ++c) {
-                    const float4 w = src[c];
-                    x[4 * c + 0] = w.x;
-                    x[4 * c + 1] = w.y;
-                    x[4 * c + 2] = w.z;
-                    x[4 * c + 3] = w.w;
-                }
+            for (int kb = 0; kb < NKB; ++kb) {
+                ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, raw[kb].x),
+                                                     __builtin_bit_cast(bf16x2, raw[kb].x), ss, false);
+                ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, raw[kb].y),
+                                                     __builtin_bit_cast(bf16x2, raw[kb].y), ss, false);
+                ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, raw[kb].z),
+                                                     __builtin_bit_cast(bf16x2, raw[kb].z), ss, false);
+                ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, raw[kb].w),
+                                                     __builtin_bit_cast(bf16x2, raw[kb].w), ss, false);
             }
         } else {
+            const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(p.x) + off);
 #pragma unroll
-            for (int j = 0; j < HALF; ++j) x[j] = 0.0f;
-        }
-
-        __builtin_amdgcn_sched_barrier(0);
-        // exchange the upper quarter of each lane half: register a*QTR + t of
-        // lane half h now holds coordinate a*HALF + h*QTR + t, so the RoPE pair
-        // (i, i + D/2) and coordinate bit log2(HALF) are within a lane
-#pragma unroll
-        for (int t = 0; t < QTR; ++t) xchg(x[t], x[t + QTR]);
-
-        // RoPE (keys): pair (i, i + D/2), i = h*QTR + t, is registers (t, t + QTR)
-        if constexpr (ROPE) {
-            // all table reads in flight at once (LDS reads when staged, kept
-            // apart from the global path so they stay LDS instructions)
-            f32x4 cc[QTR / 4], ss[QTR / 4];
-            if (stage) {
-#pragma unroll
-                for (int c = 0; c < QTR / 4; ++c) {
-                    cc[c] = s_rope4[(v * RS + h * QTR) / 4 + c];
-                    ss[c] = s_rope4[((32 + v) * RS + h * QTR) / 4 + c];
-                }
-            } else {
-                const int64_t ro = (int64_t)(p.tok_offset + (valid ? token : 0)) * HALF + h * QTR;
-                const f32x4* cp = reinterpret_cast<const f32x4*>(p.rope_cos + ro);
-                const f32x4* sp = reinterpret_cast<const f32x4*>(p.rope_sin + ro);
-#pragma unroll
-                for (int c = 0; c < QTR / 4; ++c) {
-                    cc[c] = cp[c];
-                    ss[c] = sp[c];
-                }
-            }
-#pragma unroll
-            for (int c = 0; c < QTR / 4; ++c) {
-                const float cs[4] = {cc[c][0], cc[c][1], cc[c][2], cc[c][3]};
-                const float sn[4] = {ss[c][0], ss[c][1], ss[c][2], ss[c][3]};
+            for (int kb = 0; kb < NKB; ++kb) {
+                const f32x4 a = src[4 * kb + 2 * h];
+                const f32x4 b = src[4 * kb + 2 * h + 1];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const int t = 4 * c + u;
-                    const float lo = x[t], hi = x[t + QTR];
-                    x[t] = fmaf(lo, cs[u], -(hi * sn[u]));
-                    x[t + QTR] = fmaf(hi, cs[u], lo * sn[u]);
+                    xv[kb][u] = a[u];
+                    xv[kb][4 + u] = b[u];
                 }
             }
-        }
-
-        // norm nu and the scale that maps H(sigma*x) to 2^8 * Pi (x / nu)
-        float ss = 0.0f;
 #pragma unroll
-        for (int j = 0; j < HALF; ++j) ss = fmaf(x[j], x[j], ss);
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int t = 0; t < 8; ++t) ss = fmaf(xv[kb][t], xv[kb][t], ss);
+        }
         {
             const Swap sw = swap32(ss);
             ss = sw.r0 + sw.r1;
         }
         const float nu = sqrtf(ss);
+        // maps H(sigma * x) to 2^8 * Pi (x / nu)
         const float scale = nu > 0.0f ? yscale / nu : 0.0f;
 
-        // sign flips (masks re-read from LDS per tile: the opaque offset keeps
-        // the compiler from holding 64 mask registers across the tile loop)
-        {
-            int fo = h * (HALF / 4);
-            asm volatile("" : "+v"(fo));
+        // Walsh-Hadamard transform as MFMAs: H_D = H_{D/32} (x) H32, so output
+        // block ob takes input step kb with the sign H_{D/32}[ob][kb/2].
+        // Output block ob, register r of this lane = coordinate
+        // 32 ob + 8 (r/4) + 4 h + r%4.
+        floatx16 acc[NOB];
 #pragma unroll
-            for (int c = 0; c < HALF / 4; ++c) {
-                const uint4 mk = s_flip[fo + c];
-                x[4 * c + 0] = __uint_as_float(__float_as_uint(x[4 * c + 0]) ^ mk.x);
-                x[4 * c + 1] = __uint_as_float(__float_as_uint(x[4 * c + 1]) ^ mk.y);
-                x[4 * c + 2] = __uint_as_float(__float_as_uint(x[4 * c + 2]) ^ mk.z);
-                x[4 * c + 3] = __uint_as_float(__float_as_uint(x[4 * c + 3]) ^ mk.w);
-            }
-        }
-        // Walsh-Hadamard butterflies (Sylvester order) over every coordinate
-        // bit held in registers; the stages commute
+        for (int ob = 0; ob < NOB; ++ob)
 #pragma unroll
-        for (int s = 1; s < HALF; s <<= 1) {
+            for (int q = 0; q < 16; ++q) acc[ob][q] = 0.0f;
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (EXACT) {
 #pragma unroll
-            for (int j = 0; j < HALF; ++j) {
-                if (!(j & s)) {
-                    const float a = x[j], b = x[j + s];
-                    x[j] = a + b;
-                    x[j + s] = a - b;
+            for (int kb = 0; kb < NKB; ++kb) {
+                const uint4 ap = s_had[kb * 64 + lane];
+                const uint4 an = make_uint4(ap.x ^ 0x80008000u, ap.y ^ 0x80008000u, ap.z ^ 0x80008000u,
+                                            ap.w ^ 0x80008000u);
+#pragma unroll
+                for (int ob = 0; ob < NOB; ++ob) {
+                    const uint4 a = (__builtin_popcount(ob & (kb >> 1)) & 1) ? an : ap;
+                    acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                                     __builtin_bit_cast(bf16x8, raw[kb]), acc[ob], 0, 0, 0);
                 }
             }
-        }
-        // exchange back (register j of lane half h = coordinate h*HALF + j);
-        // the remaining coordinate bit log2(QTR) is now registers (t, t + QTR)
+        } else {
+            // split inputs, one RoPE pair of steps at a time (pair (i, i + D/2)
+            // is steps kb and kb + NKB/2 at the same t): RoPE, the scale, fp16
+            // hi + lo parts, then both parts through the MFMAs
 #pragma unroll
-        for (int t = 0; t < QTR; ++t) xchg(x[t], x[t + QTR]);
+            for (int kp = 0; kp < NKB / 2; ++kp) {
+                float xl[8], xh[8];
+                if constexpr (BF16) {
+                    const uint32_t wl[4] = {raw[kp].x, raw[kp].y, raw[kp].z, raw[kp].w};
+                    const uint4 rh = raw[kp + NKB / 2];
+                    const uint32_t wh[4] = {rh.x, rh.y, rh.z, rh.w};
 #pragma unroll
-        for (int t = 0; t < QTR; ++t) {
-            const float a = x[t], b = x[t + QTR];
-            x[t] = a + b;
-            x[t + QTR] = a - b;
+                    for (int q = 0; q < 4; ++q) {
+                        xl[2 * q] = bf16_lo(wl[q]);
+                        xl[2 * q + 1] = bf16_hi(wl[q]);
+                        xh[2 * q] = bf16_lo(wh[q]);
+                        xh[2 * q + 1] = bf16_hi(wh[q]);
+                    }
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        xl[t] = xv[kp][t];
+                        xh[t] = xv[kp + NKB / 2][t];
+                    }
+                }
+                if constexpr (ROPE) {
+                    f32x4 cc[2], sn[2];
+                    if (stage) {
+#pragma unroll
+                        for (int c = 0; c < 2; ++c) {
+                            cc[c] = s_rope4[(v * RS + 16 * kp + 8 * h) / 4 + c];
+                            sn[c] = s_rope4[((32 + v) * RS + 16 * kp + 8 * h) / 4 + c];
+                        }
+                    } else {
+                        const int64_t ro = (int64_t)(p.tok_offset + (valid ? token : 0)) * HALF + 16 * kp + 8 * h;
+                        const f32x4* cp = reinterpret_cast<const f32x4*>(p.rope_cos + ro);
+                        const f32x4* sp = reinterpret_cast<const f32x4*>(p.rope_sin + ro);
+#pragma unroll
+                        for (int c = 0; c < 2; ++c) {
+                            cc[c] = cp[c];
+                            sn[c] = sp[c];
+                        }
+                    }
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        const float cs = cc[t >> 2][t & 3] * scale, s = sn[t >> 2][t & 3] * scale;
+                        const float lo = xl[t], hi = xh[t];
+                        xl[t] = fmaf(lo, cs, -(hi * s));
+                        xh[t] = fmaf(hi, cs, lo * s);
+                    }
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        xl[t] *= scale;
+                        xh[t] *= scale;
+                    }
+                }
+#pragma unroll
+                for (int side = 0; side < 2; ++side) {
+                    const int kb = kp + side * (NKB / 2);
+                    const float* xs = side ? xh : xl;
+                    half8 bhi, blo;
+                    split_f16(xs, bhi, blo);
+                    const uint4 ap = s_had[kb * 64 + lane];
+                    const uint4 an = make_uint4(ap.x ^ 0x80008000u, ap.y ^ 0x80008000u, ap.z ^ 0x80008000u,
+                                                ap.w ^ 0x80008000u);
+#pragma unroll
+                    for (int ob = 0; ob < NOB; ++ob) {
+                        const half8 a = __builtin_bit_cast(half8, (__builtin_popcount(ob & (kb >> 1)) & 1) ? an : ap);
+                        acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bhi, acc[ob], 0, 0, 0);
+                        acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, blo, acc[ob], 0, 0, 0);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-
         __builtin_amdgcn_sched_barrier(0);
-        // per 8-coordinate chunk: quantise, residual, pack, and feed the
-        // residual's fp16 hi/lo parts to the sketch MFMAs
-        uint32_t cw[WH];
+        if (prefetch) rope_stage_load<HALF, NQ>(p, base + blk_stride, st_table, st_row, st_c4, pre);
+
+        // per 8-value chunk pc (block pc/2, registers 8(pc%2)..+7): quantise,
+        // residual, pack, and feed the residual's fp16 hi/lo parts to the
+        // sketch MFMAs.  Codes are packed at lane half 0's positions; lane
+        // half 1's are moved into place afterwards.
+        uint32_t cw[CW];
 #pragma unroll
-        for (int w = 0; w < WH; ++w) cw[w] = 0u;
+        for (int w = 0; w < CW; ++w) cw[w] = 0u;
         float gg = 0.0f;
-        floatx16 acc[NRB > 0 ? NRB : 1];
+        floatx16 sacc[NRB > 0 ? NRB : 1];
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-            for (int q = 0; q < 16; ++q) acc[rb][q] = 0.0f;
+            for (int q = 0; q < 16; ++q) sacc[rb][q] = 0.0f;
 #pragma unroll
         for (int pc = 0; pc < NP; ++pc) {
+            const int ob = pc >> 1, hf = pc & 1;
             float e[8];
+            if constexpr (BITS >= 3) {
+                // byte-packed codes: the four codes of a group (t = 4g..4g+3,
+                // one 8-coordinate row a = 2hf + g) as bytes of P, then the
+                // negative coordinates complemented at once through a byte
+                // mask built from the four sign bits (v_perm byte selects)
+                float yv[8];
+                uint32_t xu[8];
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                // + 0: a zero vector's -0 coordinates count as +0 (code of y = 0)
-                const float y = fmaf(x[8 * pc + jj], scale, 0.0f);
-                const uint32_t code = quantise<BITS>(y, pt, pl, &e[jj]);
-                gg = fmaf(e[jj], e[jj], gg);
-                // the half starts on a word (and, for 3 bits, a 32-code group) boundary
-                dev::code_put(cw, dev::code_loc(8 * pc + jj, BITS), BITS, code);
+                for (int t = 0; t < 8; ++t) {
+                    // + 0: a zero vector's -0 coordinates count as +0 (code of y = 0)
+                    yv[t] = EXACT ? fmaf(acc[ob][8 * hf + t], scale, 0.0f) : acc[ob][8 * hf + t];
+                    xu[t] = upper_code<BITS>(fabsf(yv[t]), pt);
+                }
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    e[t] = yv[t] - __builtin_copysignf(s_lvl[xu[t]], yv[t]);
+                    gg = fmaf(e[t], e[t], gg);
+                }
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    const int t0 = 4 * g, a = 2 * hf + g;
+                    const uint32_t P = xu[t0] | (xu[t0 + 1] << 8) | (xu[t0 + 2] << 16) | (xu[t0 + 3] << 24);
+                    const uint32_t Mk = __builtin_amdgcn_perm(__float_as_uint(yv[t0 + 1]), __float_as_uint(yv[t0]), 0x0C0C0B09u) |
+                                        __builtin_amdgcn_perm(__float_as_uint(yv[t0 + 3]), __float_as_uint(yv[t0 + 2]), 0x0B090C0Cu);
+                    const uint32_t C = P ^ (Mk & (0x01010101u * (2u * KH - 1u)));
+                    if constexpr (BITS == 3) {
+                        // lane half 0 positions: rows 0-2 fill bits 0-2 of every
+                        // byte of word a; row 3 puts its low bits at 6-7 of word 0
+                        // and its high bit at 6 of word 2
+                        if (a < 3) {
+                            cw[3 * ob + a] |= C;
+                        } else {
+                            cw[3 * ob] |= (C & 0x03030303u) << 6;
+                            cw[3 * ob + 2] |= (C & 0x04040404u) << 4;
+                        }
+                    } else {
+                        // nibble b of word 4 ob + a
+                        const uint32_t t2 = C | (C >> 4);
+                        cw[4 * ob + a] |= __builtin_amdgcn_perm(t2, t2, 0x0C0C0200u);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    // + 0: a zero vector's -0 coordinates count as +0 (code of y = 0)
+                    const float y = EXACT ? fmaf(acc[ob][8 * hf + t], scale, 0.0f) : acc[ob][8 * hf + t];
+                    const uint32_t code = quantise<BITS>(y, pt, pl, &e[t]);
+                    gg = fmaf(e[t], e[t], gg);
+                    dev::code_put(cw, dev::code_loc(32 * ob + 8 * (2 * hf + (t >> 2)) + (t & 3), BITS), BITS, code);
+                }
             }
             if constexpr (M > 0) {
                 half8 ehi, elo;
+                split_f16(e, ehi, elo);
 #pragma unroll
-                for (int jj = 0; jj < 8; ++jj) {
-                    const _Float16 hi = (_Float16)e[jj];
-                    ehi[jj] = hi;
-                    elo[jj] = (_Float16)(e[jj] - (float)hi);
+                for (int rb = 0; rb < NRB; ++rb) {
+                    const half8 shi = s_sk[((rb * NP + pc) * 2 + 0) * 64 + lane];
+                    sacc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(shi, ehi, sacc[rb], 0, 0, 0);
                 }
 #pragma unroll
                 for (int rb = 0; rb < NRB; ++rb) {
                     const half8 shi = s_sk[((rb * NP + pc) * 2 + 0) * 64 + lane];
-                    acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(shi, ehi, acc[rb], 0, 0, 0);
-                }
-#pragma unroll
-                for (int rb = 0; rb < NRB; ++rb) {
-                    const half8 shi = s_sk[((rb * NP + pc) * 2 + 0) * 64 + lane];
-                    acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(shi, elo, acc[rb], 0, 0, 0);
+                    sacc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(shi, elo, sacc[rb], 0, 0, 0);
                 }
 #pragma unroll
                 for (int rb = 0; rb < NRB; ++rb) {
                     const half8 slo = s_sk[((rb * NP + pc) * 2 + 1) * 64 + lane];
-                    acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(slo, ehi, acc[rb], 0, 0, 0);
+                    sacc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(slo, ehi, sacc[rb], 0, 0, 0);
                 }
             }
-            // the chunk's codes are merged into the words here, not at the
-            // final store (which would keep every compare mask alive)
+            // (per-coordinate packing: the chunk's codes are merged into the
+            // words here, not at the final store, which would keep every
+            // compare mask alive)
+            if constexpr (BITS < 3) {
 #pragma unroll
-            for (int w = 0; w < WH; ++w) asm volatile("" : "+v"(cw[w]));
-            // keep each chunk's operand reads next to its MFMAs (bounded live ranges)
+                for (int w = 0; w < CW; ++w) asm volatile("" : "+v"(cw[w]));
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
         {
@@ -416,11 +543,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ROPE ? 2 : 
         }
         const float gamma = sqrtf(gg) * (1.0f / ESCALE);
 
+        // lane half 1's coordinates are 4 above lane half 0's in every block of
+        // 8: for b = 1, 2, 4 its codes sit 4b bits higher in the same words.
+        // For b = 3 they sit 3 bits higher in each byte, except the group's
+        // last four, whose low bits go to word 1 (not 0) at the same place
+        // and whose high bit sits one bit higher in word 2.
+        if constexpr (BITS == 3) {
+#pragma unroll
+            for (int g = 0; g < NOB; ++g) {
+                const uint32_t w0 = cw[3 * g], w1 = cw[3 * g + 1], w2 = cw[3 * g + 2];
+                cw[3 * g] = h ? (w0 & 0x07070707u) << 3 : w0;
+                cw[3 * g + 1] = h ? (w1 << 3) | (w0 & 0xC0C0C0C0u) : w1;
+                cw[3 * g + 2] = h ? ((w2 & 0x07070707u) << 3) | ((w2 & 0x40404040u) << 1) : w2;
+            }
+        } else {
+            const int sh = h * 4 * BITS;
+#pragma unroll
+            for (int w = 0; w < CW; ++w) cw[w] <<= sh;
+        }
+        // merge the lane pair's bits: lane half h keeps words [h CW/2, (h+1) CW/2)
+#pragma unroll
+        for (int k = 0; k < CW / 2; ++k) {
+            float a = __uint_as_float(cw[k]), b = __uint_as_float(cw[k + CW / 2]);
+            xchg(a, b);
+            cw[k] = __float_as_uint(a) | __float_as_uint(b);
+        }
+
         const int64_t n = ((int64_t)seq * p.h_kv + head) * p.L_cap + p.tok_offset + token;
         if (valid) {
-            uint32_t* dst = p.codes + n * CW + h * WH;
+            uint32_t* dst = p.codes + n * CW + h * (CW / 2);
 #pragma unroll
-            for (int w = 0; w < WH; ++w) dst[w] = cw[w];
+            for (int k = 0; k < CW / 2; ++k) dst[k] = cw[k];
             if (h == 0) p.norm[n] = nu;
             else if (M > 0) p.rnorm[n] = gamma;
         }
@@ -431,7 +584,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ROPE ? 2 : 
             for (int rb = 0; rb < NRB; ++rb) {
                 uint32_t wb = 0;
 #pragma unroll
-                for (int q = 0; q < 16; ++q) wb |= (acc[rb][q] >= 0.0f ? 1u : 0u) << (8 * (q >> 2) + (q & 3));
+                for (int q = 0; q < 16; ++q) wb |= (sacc[rb][q] >= 0.0f ? 1u : 0u) << (8 * (q >> 2) + (q & 3));
                 wb <<= 4 * h;
                 const Swap sw = swap32(__uint_as_float(wb));
                 wb = __float_as_uint(sw.r0) | __float_as_uint(sw.r1);
@@ -601,8 +754,8 @@ using EncFn = void (*)(EncK);
 
 template <int D, int BITS, int M>
 EncFn pick_dtype(bool bf16, bool rope) {
-    if (rope) return bf16 ? encode_rht_kernel<D, BITS, M, true, true> : encode_rht_kernel<D, BITS, M, false, true>;
-    return bf16 ? encode_rht_kernel<D, BITS, M, true, false> : encode_rht_kernel<D, BITS, M, false, false>;
+    if (rope) return bf16 ? encode_had_kernel<D, BITS, M, true, true> : encode_had_kernel<D, BITS, M, false, true>;
+    return bf16 ? encode_had_kernel<D, BITS, M, true, false> : encode_had_kernel<D, BITS, M, false, false>;
 }
 
 template <int D, int BITS>

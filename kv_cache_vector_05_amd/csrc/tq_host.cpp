@@ -440,18 +440,20 @@ tq_status tq_codebook_init(const tq_spec* spec, const tq_draws* draws, void* str
     if (cb->K <= 8) level_digits(cb->levels, cb->lvl_digits, &cb->lvl_shift);
     const int d = spec->d, m = spec->m;
     // the encode kernel's sketch operand (Hadamard form): S split into fp16
-    // hi + lo parts in the A-operand order of v_mfma_f32_32x32x16_f16:
+    // hi + lo parts in the A-operand order of v_mfma_f32_32x32x16_f16, the
+    // columns in the order the kernel's Hadamard MFMAs leave the residual in:
     // entry [(rb*(d/16) + p)*2 + piece][lane][s] = part `piece` of
-    // S[rb*32 + lane%32][(lane/32)*(d/2) + 8p + s]   (s = 0..7)
+    // S[rb*32 + lane%32][c],  c = 32(p/2) + 8(2(p%2) + s/4) + 4(lane/32) + s%4
     std::vector<float> sk_mfma((size_t)m * d);
     if (!dense && m) {
-        const int half = d / 2, np = d / 16;
+        const int np = d / 16;
         uint16_t* out = reinterpret_cast<uint16_t*>(sk_mfma.data());
         for (int rb = 0; rb < m / 32; ++rb)
             for (int p = 0; p < np; ++p)
                 for (int l = 0; l < 64; ++l)
                     for (int sidx = 0; sidx < 8; ++sidx) {
-                        const float v = cb->sketch[(size_t)(rb * 32 + (l & 31)) * d + (l >> 5) * half + 8 * p + sidx];
+                        const int c = 32 * (p / 2) + 8 * (2 * (p % 2) + sidx / 4) + 4 * (l >> 5) + sidx % 4;
+                        const float v = cb->sketch[(size_t)(rb * 32 + (l & 31)) * d + c];
                         const uint16_t hi = f32_to_f16(v);
                         const uint16_t lo = f32_to_f16(v - f16_to_f32(hi));
                         const size_t base = ((((size_t)rb * np + p) * 2) * 64 + l) * 8 + sidx;
