@@ -129,12 +129,20 @@ __device__ __forceinline__ uint32_t quantise(float y, const float* pt, const flo
 // K/2 + c' where c' is the code of a = |y| among the upper cells of a
 // symmetric table (pt: the K/2-1 upper thresholds); y's code is this value for
 // y >= 0 and its complement in K - 1 bits for y < 0.
+// base + m in one carry-in add (the lane mask of m is the carry)
+__device__ __forceinline__ uint32_t add_bit(uint32_t base, bool m) {
+    uint32_t r;
+    uint64_t carry_out;
+    asm("v_addc_co_u32 %0, %1, %2, 0, %3" : "=v"(r), "=s"(carry_out) : "v"(base), "s"(__builtin_amdgcn_ballot_w64(m)));
+    return r;
+}
+
 template <int BITS>
 __device__ __forceinline__ uint32_t upper_code(float a, const float* pt) {
     if constexpr (BITS == 3) {
         const bool m1 = a >= pt[1];
         const bool m0 = a >= (m1 ? pt[2] : pt[0]);
-        return (m1 ? 6u : 4u) + (m0 ? 1u : 0u);
+        return add_bit(m1 ? 6u : 4u, m0);
     } else {
         static_assert(BITS == 4, "byte-packed codes are used for 3 and 4 bits");
         const bool m2 = a >= pt[3];
@@ -142,7 +150,7 @@ __device__ __forceinline__ uint32_t upper_code(float a, const float* pt) {
         const float t0 = m2 ? pt[4] : pt[0];
         const float t1 = m2 ? pt[6] : pt[2];
         const bool m0 = a >= (m1 ? t1 : t0);
-        return (m2 ? 12u : 8u) + (m1 ? 2u : 0u) + (m0 ? 1u : 0u);
+        return add_bit((m2 ? 12u : 8u) + (m1 ? 2u : 0u), m0);
     }
 }
 
@@ -207,7 +215,7 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
     // A operands of the Hadamard MFMAs, sign flips folded in: entry [kb][lane]
     // holds H32[lane%32][16(kb%2) + 8(lane/32) + t] * sigma[16kb + 8(lane/32) + t]
     // for t = 0..7 as bf16 (raw bf16 inputs) or fp16 (split inputs) +-1
-    __shared__ uint4 s_had[NKB * 64];
+    __shared__ uint4 s_had[2 * NKB * 64];  // [+A; -A]
     // scaled levels, indexed by code (3 and 4 bits: looked up by K/2 + c')
     __shared__ float s_lvl[16];
 
@@ -232,6 +240,7 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
             w[q] = pair;
         }
         s_had[i] = make_uint4(w[0], w[1], w[2], w[3]);
+        s_had[NKB * 64 + i] = make_uint4(w[0] ^ 0x80008000u, w[1] ^ 0x80008000u, w[2] ^ 0x80008000u, w[3] ^ 0x80008000u);
     }
     __syncthreads();
 
@@ -353,8 +362,7 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 const uint4 ap = s_had[kb * 64 + lane];
-                const uint4 an = make_uint4(ap.x ^ 0x80008000u, ap.y ^ 0x80008000u, ap.z ^ 0x80008000u,
-                                            ap.w ^ 0x80008000u);
+                const uint4 an = s_had[NKB * 64 + kb * 64 + lane];
 #pragma unroll
                 for (int ob = 0; ob < NOB; ++ob) {
                     const uint4 a = (__builtin_popcount(ob & (kb >> 1)) & 1) ? an : ap;
@@ -426,8 +434,7 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
                     half8 bhi, blo;
                     split_f16(xs, bhi, blo);
                     const uint4 ap = s_had[kb * 64 + lane];
-                    const uint4 an = make_uint4(ap.x ^ 0x80008000u, ap.y ^ 0x80008000u, ap.z ^ 0x80008000u,
-                                                ap.w ^ 0x80008000u);
+                    const uint4 an = s_had[NKB * 64 + kb * 64 + lane];
 #pragma unroll
                     for (int ob = 0; ob < NOB; ++ob) {
                         const half8 a = __builtin_bit_cast(half8, (__builtin_popcount(ob & (kb >> 1)) & 1) ? an : ap);
@@ -582,10 +589,21 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
             // D[i][j]: j = lane % 32 (vector), i = 8*(r/4) + 4*(lane/32) + r%4 (sketch row)
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb) {
+                // per byte b: the sign bits of rows 8b + 4h + 0..3 as 0xFF/0x00
+                // bytes (v_perm sign selects), one bit kept per byte, gathered
+                // into byte 3 by a multiply and moved to byte b; a set bit is
+                // a negative value, so the word is complemented at the end
                 uint32_t wb = 0;
 #pragma unroll
-                for (int q = 0; q < 16; ++q) wb |= (sacc[rb][q] >= 0.0f ? 1u : 0u) << (8 * (q >> 2) + (q & 3));
-                wb <<= 4 * h;
+                for (int b = 0; b < 4; ++b) {
+                    const uint32_t f0 = __float_as_uint(sacc[rb][4 * b]), f1 = __float_as_uint(sacc[rb][4 * b + 1]);
+                    const uint32_t f2 = __float_as_uint(sacc[rb][4 * b + 2]), f3 = __float_as_uint(sacc[rb][4 * b + 3]);
+                    const uint32_t sb = (__builtin_amdgcn_perm(f1, f0, 0x0C0C0B09u) | __builtin_amdgcn_perm(f3, f2, 0x0B090C0Cu)) &
+                                        0x08040201u;
+                    // byte 3 of the product = bits 0..3; v_perm puts it at byte b of wb
+                    wb = __builtin_amdgcn_perm(sb * 0x01010101u, wb, (0x03020100u & ~(0xFFu << (8 * b))) | (0x07u << (8 * b)));
+                }
+                wb = (~wb & 0x0F0F0F0Fu) << (4 * h);
                 const Swap sw = swap32(__uint_as_float(wb));
                 wb = __float_as_uint(sw.r0) | __float_as_uint(sw.r1);
                 if (valid && (rb & 1) == h) p.signs[n * NRB + rb] = wb;
@@ -785,6 +803,23 @@ EncFn pick_encode(int d, int bits, int m, bool bf16, bool rope) {
 
 int g_num_cus = 0;
 
+// resident 256-thread blocks per CU of an encode kernel at a dynamic LDS size
+int resident_per_cu(const void* fn, size_t lds) {
+    static thread_local const void* last_fn = nullptr;
+    static thread_local size_t last_lds = 0;
+    static thread_local int last = 0;
+    if (fn == last_fn && lds == last_lds) return last;
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, lds) != hipSuccess || per_cu < 1) {
+        (void)hipGetLastError();
+        return 8;
+    }
+    last_fn = fn;
+    last_lds = lds;
+    last = per_cu;
+    return per_cu;
+}
+
 }  // namespace
 
 size_t encode_workspace_bytes(const tq_codebook* cb, int64_t n_vectors) {
@@ -826,13 +861,15 @@ hipError_t launch_encode(const tq_codebook* cb, const EncodeArgs& a, hipStream_t
         p.rnorm = a.out.rnorm;
         p.codes = a.out.codes;
         p.signs = a.out.signs;
-        const int64_t blocks_needed = (p.n_tiles + 3) / 4;
-        const int64_t cap = (int64_t)g_num_cus * 8;
-        const int grid = (int)(blocks_needed < cap ? blocks_needed : cap);
         p.rope_stage = (a.rope_cos != nullptr && a.h_kv % 4 == 0) ? 1 : 0;
         p.div_h = dev::FastDiv((uint32_t)a.h_kv);
         p.div_tb = dev::FastDiv((uint32_t)p.tok_blocks);
         const size_t lds = p.rope_stage ? (size_t)2 * 32 * (d / 2 + 4) * sizeof(float) : 0;
+        // persistent blocks: as many as are resident at once, so that no
+        // partial last round of blocks leaves CUs idle
+        const int64_t blocks_needed = (p.n_tiles + 3) / 4;
+        const int64_t cap = (int64_t)g_num_cus * resident_per_cu((const void*)fn, lds);
+        const int grid = (int)(blocks_needed < cap ? blocks_needed : cap);
         hipLaunchKernelGGL(fn, dim3(grid), dim3(256), lds, stream, p);
         return hipGetLastError();
     }
