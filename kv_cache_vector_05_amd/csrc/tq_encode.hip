@@ -281,6 +281,28 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
         rope_stage_store<RS, NQ>(s_rope4, st_table, st_row, st_c4, pre);
     }
     __syncthreads();
+    // element offset of this lane's input vector in tile t; lanes past the
+    // last token read the last token instead (an MFMA column only feeds its
+    // own vector, and these vectors are not stored)
+    auto input_offset = [&](int64_t t) -> int64_t {
+        const uint32_t r = p.div_h.div((uint32_t)t);
+        const int hd = (int)((uint32_t)t - r * (uint32_t)p.h_kv);
+        const uint32_t sq = p.div_tb.div(r);
+        const int tbk = (int)(r - sq * (uint32_t)p.tok_blocks);
+        return (int64_t)sq * p.s_seq + (int64_t)min(tbk * 32 + v, p.n_tok - 1) * p.s_tok + (int64_t)hd * p.s_head;
+    };
+    // RoPE keys run at two waves per SIMD whatever their register count, so
+    // their next tile's bf16 inputs are loaded while this tile is quantised
+    constexpr bool PREFETCH = ROPE && BF16 && D == 128;
+    uint4 nxt[PREFETCH ? NKB : 1];
+    if constexpr (PREFETCH) {
+        const int64_t t0 = base + (threadIdx.x >> 6);
+        if (t0 < p.n_tiles) {
+            const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.x) + input_offset(t0));
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) nxt[kb] = src[2 * kb + h];
+        }
+    }
     // the loop bound is the same for the whole block (barriers inside)
     for (; base < p.n_tiles; base += blk_stride) {
       const int64_t tile = base + (threadIdx.x >> 6);
@@ -297,10 +319,6 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
         const int seq = (int)sq;
         const int token = tb * 32 + v;
         const bool valid = token < p.n_tok;
-        // lanes past the last token read the last token instead: an MFMA
-        // column only feeds its own vector, and these vectors are not stored
-        const int64_t off = (int64_t)seq * p.s_seq + (int64_t)min(token, p.n_tok - 1) * p.s_tok +
-                            (int64_t)head * p.s_head;
 
         // B operands: input step kb is coordinates 16kb + 8h + t (t = 0..7)
         // of this lane's vector
@@ -308,9 +326,14 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
         float xv[BF16 ? 1 : NKB][8];
         float ss = 0.0f;
         if constexpr (BF16) {
-            const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.x) + off);
+            if constexpr (PREFETCH) {
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) raw[kb] = src[2 * kb + h];
+                for (int kb = 0; kb < NKB; ++kb) raw[kb] = nxt[kb];
+            } else {
+                const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.x) + input_offset(tile));
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) raw[kb] = src[2 * kb + h];
+            }
             // nu^2 from the bf16 pairs (RoPE keeps the norm)
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
@@ -324,7 +347,7 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
                                                      __builtin_bit_cast(bf16x2, raw[kb].w), ss, false);
             }
         } else {
-            const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(p.x) + off);
+            const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(p.x) + input_offset(tile));
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 const f32x4 a = src[4 * kb + 2 * h];
@@ -447,6 +470,14 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
         }
         __builtin_amdgcn_sched_barrier(0);
         if (prefetch) rope_stage_load<HALF, NQ>(p, base + blk_stride, st_table, st_row, st_c4, pre);
+        if constexpr (PREFETCH) {
+            const int64_t tn = tile + blk_stride;
+            if (tn < p.n_tiles) {
+                const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.x) + input_offset(tn));
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) nxt[kb] = src[2 * kb + h];
+            }
+        }
 
         // per 8-value chunk pc (block pc/2, registers 8(pc%2)..+7): quantise,
         // residual, pack, and feed the residual's fp16 hi/lo parts to the
