@@ -47,7 +47,7 @@ def _compile(src: str, verbose: bool) -> str:
     cmd = [hipcc()] + common_flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd += ["-ffp-contract=off"]
-    if src in ("tq_logits.hip", "tq_encode.hip"):
+    if src in ("tq_logits.hip", "tq_encode.hip", "tq_decode.hip"):
         # keep MFMA accumulators in architectural VGPRs (no AGPR copies in the loop)
         cmd += ["-mllvm", "--amdgpu-mfma-vgpr-form"]
     if verbose:
