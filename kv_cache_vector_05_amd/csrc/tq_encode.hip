@@ -38,7 +38,9 @@ struct EncK {
     int32_t n_seq, n_tok, h_kv, tok_offset, L_cap, tok_blocks;
     int64_t n_tiles;
     int32_t rope_stage;  // the block's four waves share their tokens: RoPE rows staged in LDS
-    dev::FastDiv div_h, div_tb;  // by h_kv and by tok_blocks (tile indices are below 2^31)
+    // tile t = (token block * n_seq + seq) * h_kv + head: the tiles that share
+    // a token block's RoPE rows (every sequence and head) run close together
+    dev::FastDiv div_h, div_seq;  // by h_kv and by n_seq (tile indices are below 2^31)
     const float* rope_cos;
     const float* rope_sin;
     const float* sigma;
@@ -183,7 +185,7 @@ template <int HALF, int NQ>
 __device__ __forceinline__ void rope_stage_load(const EncK& p, int64_t base, const int (&tab)[NQ],
                                                 const int (&row)[NQ], const int (&c4)[NQ], f32x4 (&pre)[NQ]) {
     const uint32_t r0 = p.div_h.div((uint32_t)base);
-    const int tb0 = (int)(r0 - p.div_tb.div(r0) * (uint32_t)p.tok_blocks);
+    const int tb0 = (int)p.div_seq.div(r0);
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
         const int pos = p.tok_offset + min(tb0 * 32 + row[j], p.n_tok - 1);
@@ -287,8 +289,9 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
     auto input_offset = [&](int64_t t) -> int64_t {
         const uint32_t r = p.div_h.div((uint32_t)t);
         const int hd = (int)((uint32_t)t - r * (uint32_t)p.h_kv);
-        const uint32_t sq = p.div_tb.div(r);
-        const int tbk = (int)(r - sq * (uint32_t)p.tok_blocks);
+        const uint32_t tq_ = p.div_seq.div(r);
+        const uint32_t sq = r - tq_ * (uint32_t)p.n_seq;
+        const int tbk = (int)tq_;
         return (int64_t)sq * p.s_seq + (int64_t)min(tbk * 32 + v, p.n_tok - 1) * p.s_tok + (int64_t)hd * p.s_head;
     };
     // RoPE keys run at two waves per SIMD whatever their register count, so
@@ -314,8 +317,9 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
       if (tile < p.n_tiles) {
         const uint32_t r = p.div_h.div((uint32_t)tile);
         const int head = (int)((uint32_t)tile - r * (uint32_t)p.h_kv);
-        const uint32_t sq = p.div_tb.div(r);
-        const int tb = (int)(r - sq * (uint32_t)p.tok_blocks);
+        const uint32_t tbq = p.div_seq.div(r);
+        const uint32_t sq = r - tbq * (uint32_t)p.n_seq;
+        const int tb = (int)tbq;
         const int seq = (int)sq;
         const int token = tb * 32 + v;
         const bool valid = token < p.n_tok;
@@ -894,7 +898,7 @@ hipError_t launch_encode(const tq_codebook* cb, const EncodeArgs& a, hipStream_t
         p.signs = a.out.signs;
         p.rope_stage = (a.rope_cos != nullptr && a.h_kv % 4 == 0) ? 1 : 0;
         p.div_h = dev::FastDiv((uint32_t)a.h_kv);
-        p.div_tb = dev::FastDiv((uint32_t)p.tok_blocks);
+        p.div_seq = dev::FastDiv((uint32_t)a.n_seq);
         const size_t lds = p.rope_stage ? (size_t)2 * 32 * (d / 2 + 4) * sizeof(float) : 0;
         // persistent blocks: as many as are resident at once, so that no
         // partial last round of blocks leaves CUs idle
