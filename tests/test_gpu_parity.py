@@ -206,6 +206,52 @@ def test_bit_widths_and_sketch_sizes(d, bits, m):
                             L, [333, 45], None, None, f"d{d} b{bits} m{m}")
 
 
+@pytest.mark.parametrize("d,bits,m,dtype,rope,H", [
+    (128, 3, 64, "bf16", True, 3),    # bf16 RoPE keys, heads not a multiple of 4: rows read per wave
+    (128, 3, 64, "bf16", True, 4),    # bf16 RoPE keys, rows staged per block
+    (128, 4, 128, "bf16", True, 8),   # 4-bit byte-packed codes, full-width sketch
+    (128, 3, 64, "f32", True, 2),     # fp32 RoPE keys
+    (128, 3, 0, "bf16", False, 5),    # raw bf16 operands, no sketch
+    (128, 2, 128, "bf16", True, 1),   # per-coordinate packing with RoPE
+    (64, 3, 64, "bf16", True, 4),     # d = 64, bf16 RoPE, staged
+    (64, 4, 32, "bf16", False, 3),    # d = 64, 4-bit, one sketch row block
+])
+def test_encoder_paths(d, bits, m, dtype, rope, H):
+    """The Hadamard encoder's paths (raw bf16 or split fp16 operands, RoPE rows
+    staged or read per wave, 2/3/4-bit packing, sketch widths) at a token offset
+    in a larger cache, with a ragged last tile: records match the oracle and
+    every other slot keeps its sentinel."""
+    B, T, off, L = 2, 77, 3, 90
+    g = synth.rng(d + 7 * bits + m + 31 * H + (100 if rope else 0))
+    X = g.standard_normal((B, T, H, d)).astype(np.float32)
+    X[:, :, :, 5] *= np.float32(40.0)  # one outlier channel
+    if dtype == "bf16":
+        xb = synth.bf16_round_bits(X)
+        X = synth.bf16_bits_to_f32(xb)
+        x_dev = bf16_tensor(xb)
+    else:
+        x_dev = torch.from_numpy(X).cuda()
+    ock, gck = codebooks(d, bits, m, False, 11)
+    rope_g = tq.rope_table(1e4, d, L + 1) if rope else None
+    rope_o = orope.rope_table(1e4, d, L + 1) if rope else None
+    kp = tq.Packed(gck, B * H * L)
+    kp.norm.fill_(-3.0)
+    tq.encode_kv(gck, None, x_dev, None, kp, None, tok_offset=off, L_cap=L, rope=rope_g)
+    torch.cuda.synchronize()
+    got = kp.numpy()
+    nrm = got[0].reshape(B * H, L)
+    assert np.all(nrm[:, :off] == -3.0) and np.all(nrm[:, off + T:] == -3.0)
+    pos = np.tile(off + np.arange(T), B * H)
+    enc = codec.encode(ock, parity.oracle_rows(X), pos=pos if rope else None, rope=rope_o)
+    def window(a):  # the records of tokens off .. off+T-1 of every (sequence, head)
+        if a.size == 0:
+            return a
+        if a.ndim == 2:
+            return a.reshape(B * H, L, -1)[:, off:off + T].reshape(B * H * T, -1)
+        return a.reshape(B * H, L)[:, off:off + T].reshape(-1)
+    parity.compare_encoded(ock, enc, tuple(window(a) for a in got), f"encoder d{d} b{bits} m{m} {dtype} rope={rope} H={H}")
+
+
 def test_edge_cases_lengths_offsets_zero_vectors():
     """seq_len 0 (decode gives zeros, logits untouched), seq_len above L_cap
     (clamped), zero key vectors, and an append at a token offset that leaves
