@@ -5,8 +5,10 @@
 //
 // Tiling: 256 threads (4 wave64s) own a 128 x 128 tile of C; each wave owns a
 // 64 x 64 quarter as 2 x 2 blocks of v_mfma_f32_32x32x2f32.  K advances in
-// steps of 16 through LDS tiles padded to 17 floats per row so that the 32
-// rows an MFMA operand reads fall in distinct banks.
+// steps of 32 through LDS tiles padded to 33 floats per row so that the 32
+// rows an MFMA operand reads fall in distinct banks.  The next step's operands
+// are loaded into registers (float4 where rows are 16-byte aligned) while the
+// current step multiplies, so global latency overlaps the matrix work.
 #include <hip/hip_runtime.h>
 
 #include "tq_internal.h"
@@ -17,9 +19,44 @@ namespace {
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int kTile = 128;
-constexpr int kKt = 16;
+constexpr int kKt = 32;
 constexpr int kLd = kKt + 1;
+constexpr int kLoads = kTile * kKt / 4 / 256;  // float4 slots per thread per operand and step
 
+// rows m0 + idx/8 of X, columns k0 + 4 (idx % 8) .. + 3 for the thread's slots
+template <bool VEC>
+__device__ __forceinline__ void load_step(const float* __restrict__ X, int64_t ldx, int64_t r0, int rows, int k0,
+                                          int K, int tid, float4 (&v)[kLoads]) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+        const int idx = tid + 256 * i;
+        const int64_t r = r0 + (idx >> 3);
+        const int k = k0 + 4 * (idx & 7);
+        if constexpr (VEC) {
+            v[i] = (r < rows && k < K) ? *reinterpret_cast<const float4*>(X + r * ldx + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+        } else {
+            const bool ok = r < rows;
+            v[i].x = ok && k < K ? X[r * ldx + k] : 0.f;
+            v[i].y = ok && k + 1 < K ? X[r * ldx + k + 1] : 0.f;
+            v[i].z = ok && k + 2 < K ? X[r * ldx + k + 2] : 0.f;
+            v[i].w = ok && k + 3 < K ? X[r * ldx + k + 3] : 0.f;
+        }
+    }
+}
+
+__device__ __forceinline__ void store_step(float* S, int tid, const float4 (&v)[kLoads]) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+        const int idx = tid + 256 * i;
+        float* d = S + (idx >> 3) * kLd + 4 * (idx & 7);
+        d[0] = v[i].x;
+        d[1] = v[i].y;
+        d[2] = v[i].z;
+        d[3] = v[i].w;
+    }
+}
+
+template <bool VEC>
 __global__ __launch_bounds__(256) void gemm_nt_f32(const float* __restrict__ A, int64_t lda,
                                                    const float* __restrict__ B, int64_t ldb,
                                                    float* __restrict__ C, int64_t ldc, int M, int N,
@@ -39,21 +76,17 @@ __global__ __launch_bounds__(256) void gemm_nt_f32(const float* __restrict__ A, 
         for (int j = 0; j < 2; ++j)
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // each thread stages 8 floats of A and 8 of B per K step:
-    // rows (tid >> 2) and (tid >> 2) + 64, columns (tid & 3) * 4 .. + 3
-    const int lr = tid >> 2;
-    const int lc = (tid & 3) * 4;
+    float4 va[kLoads], vb[kLoads];
+    load_step<VEC>(A, lda, m0, M, 0, K, tid, va);
+    load_step<VEC>(B, ldb, n0, N, 0, K, tid, vb);
     for (int k0 = 0; k0 < K; k0 += kKt) {
-        for (int h = 0; h < 2; ++h) {
-            const int row = lr + 64 * h;
-            const int64_t ga = m0 + row, gb = n0 + row;
-            for (int c = 0; c < 4; ++c) {
-                const int kk = k0 + lc + c;
-                As[row * kLd + lc + c] = (ga < M && kk < K) ? A[ga * lda + kk] : 0.0f;
-                Bs[row * kLd + lc + c] = (gb < N && kk < K) ? B[gb * ldb + kk] : 0.0f;
-            }
-        }
+        store_step(As, tid, va);
+        store_step(Bs, tid, vb);
         __syncthreads();
+        if (k0 + kKt < K) {  // the next step's operands, in flight during this step
+            load_step<VEC>(A, lda, m0, M, k0 + kKt, K, tid, va);
+            load_step<VEC>(B, ldb, n0, N, k0 + kKt, K, tid, vb);
+        }
 #pragma unroll
         for (int kk = 0; kk < kKt; kk += 2) {
             const int kidx = kk + (lane >> 5);
@@ -83,7 +116,10 @@ hipError_t launch_gemm_nt(const float* A, int64_t lda, const float* B, int64_t l
                           int64_t ldc, int M, int N, int K, hipStream_t stream) {
     if (M <= 0 || N <= 0) return hipSuccess;
     dim3 grid((N + kTile - 1) / kTile, (M + kTile - 1) / kTile);
-    hipLaunchKernelGGL(gemm_nt_f32, grid, dim3(256), 0, stream, A, lda, B, ldb, C, ldc, M, N, K);
+    // float4 loads need 16-byte aligned rows
+    const bool vec = ((lda | ldb) & 3) == 0 && ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & 15) == 0;
+    if (vec) hipLaunchKernelGGL(gemm_nt_f32<true>, grid, dim3(256), 0, stream, A, lda, B, ldb, C, ldc, M, N, K);
+    else hipLaunchKernelGGL(gemm_nt_f32<false>, grid, dim3(256), 0, stream, A, lda, B, ldb, C, ldc, M, N, K);
     return hipGetLastError();
 }
 
