@@ -71,7 +71,9 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warmup steps (default: as many as fill about 0.3 s, at least 3: the "
+                         "GPU's clocks take some 100 ms of load to settle)")
     ap.add_argument("--workload", default="llama8b", choices=["llama8b", "llama70b", "esm650m", "vsearch", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="keys in the oracle's sample (0: default)")
@@ -335,8 +337,21 @@ def main():
     else:
         raise SystemExit("tiny is a parity case, not a benchmark workload")
     torch.cuda.synchronize()
+    if args.warmup is None:
+        # enough steps to cover the clock ramp under load (~0.3 s), at least 3,
+        # sized from the second step (the first carries one-time set-up)
+        step(Timer(torch))
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        step(Timer(torch))
+        torch.cuda.synchronize()
+        one = time.perf_counter() - t0
+        args.warmup = max(3, min(2000, int(0.3 / max(one, 1e-6))))
+        warm = args.warmup - 2
+    else:
+        warm = args.warmup
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
+    for _ in range(warm):
         step(Timer(torch))
     torch.cuda.synchronize()
     timer = Timer(torch)
