@@ -3,21 +3,26 @@
 // compressao KV"; TurboESM summary, technical section 2 for RoPE first).
 //
 // Hadamard form (d = 64 or 128): one wave64 encodes a tile of 32 consecutive
-// tokens of one (sequence, head).  Lane l holds vector l % 32, half
-// h = l / 32 of its coordinates ([h*d/2, (h+1)*d/2)), so
-//   * each lane reads one contiguous run of d/2 elements,
-//   * RoPE's pair (i, i + d/2) and the last butterfly stage of the
-//     Walsh-Hadamard transform are one cross-half swap (lane l <-> l ^ 32),
-//     every other stage stays in registers,
-//   * the codes of a half are a whole number of 32-bit words, written by that
-//     lane alone,
-//   * the residual already sits in the B-operand layout of
-//     v_mfma_f32_32x32x2f32 (B[k][j]: k = l / 32, j = l % 32), so the sketch
-//     S e of all 32 vectors is m/32 row blocks of d/2 MFMA steps each, with S
-//     read from LDS in the matching A-operand order.
-// Blocks are persistent (grid-stride over tiles) so each block stages the
-// sketch table in LDS once; consecutive tiles of a block walk the heads of
-// the same tokens, so RoPE table rows are reused from cache.
+// tokens of one (sequence, head); lane l serves vector l % 32 with lane half
+// h = l / 32.
+//   * Input step kb holds coordinates 16 kb + 8 h + t (t = 0..7) of the lane's
+//     vector: the B operand of a 32x32x16 MFMA.  Raw bf16 inputs are that
+//     operand as loaded; RoPE'd or fp32 inputs are scaled and split into fp16
+//     hi + lo parts.  RoPE's pair (i, i + d/2) is steps kb and kb + d/32 of
+//     the same lane.
+//   * The Walsh-Hadamard transform is H_d = H_{d/32} (x) H32: the A operands
+//     are the halves of H32 with the sign flips folded in (and their
+//     negations), built once per block in LDS, and output block ob takes
+//     step kb with the sign H_{d/32}[ob][kb/2].  Afterwards lane (v, h) holds
+//     coordinates 32 ob + 8 (r/4) + 4 h + r%4 in register r of block ob.
+//   * Quantiser, residual and packing run on those values; the residual's
+//     fp16 hi/lo parts are again a B operand, so the sketch S e of all 32
+//     vectors is m/32 row blocks of d/16 MFMA steps, with S read from LDS in
+//     the matching coordinate order (laid out by the host).
+// Blocks are persistent (one resident round, grid-stride over tiles) so each
+// block stages its tables in LDS once; tiles run token block, then sequence,
+// then head, so a block's four waves encode four heads of the same tokens and
+// every user of a token block's RoPE rows runs close together.
 //
 // Dense form (any d that is a multiple of 64): per-vector norm, then
 // Y = U Pi^T and Z = E S^T as MFMA GEMMs over chunks of vectors in the
@@ -81,45 +86,27 @@ __device__ __forceinline__ void xchg(float& a, float& b) {
     b = __uint_as_float(r[1]);
 }
 
-// Quantiser for a symmetric table (t_{K-1-k} = -t_k, tau_{K-2-k} = -tau_k,
-// tau_{K/2-1} = 0; the host builds the upper half and mirrors it, so this
-// holds exactly).  c = #{j : y >= tau_j} is found as the code c' of |y| among
-// the upper thresholds, mirrored for y < 0 (there a tie |y| = tau goes to
-// the other side, a decision within rounding of the boundary).  Returns the
-// code and the residual e = y - t_c = sign(y) (|y| - t_{K/2+c'}).
+// Per-coordinate quantiser for 1 and 2 bits, for a symmetric table
+// (t_{K-1-k} = -t_k, tau_{K-2-k} = -tau_k, tau_{K/2-1} = 0; the host builds
+// the upper half and mirrors it, so this holds exactly).  c = #{j : y >= tau_j}
+// is found as the code c' of |y| among the upper thresholds, mirrored for
+// y < 0 (there a tie |y| = tau goes to the other side, a decision within
+// rounding of the boundary).  Returns the code and the residual
+// e = y - t_c = y - sign(y) t_{K/2+c'}.
 // pt: the K/2-1 upper thresholds, pl: the K/2 upper levels (scaled).
-
 template <int BITS>
 __device__ __forceinline__ uint32_t quantise(float y, const float* pt, const float* pl, float* e) {
+    static_assert(BITS <= 2, "3 and 4 bits use the byte-packed path");
     constexpr uint32_t KH = 1u << (BITS - 1);
-    const float a = fabsf(y);
     uint32_t cp;  // code of |y| among the upper cells
     float lv;
     if constexpr (BITS == 1) {
         cp = 0u;
         lv = pl[0];
-    } else if constexpr (BITS == 2) {
-        const bool m0 = a >= pt[0];
+    } else {
+        const bool m0 = fabsf(y) >= pt[0];
         cp = (uint32_t)m0;
         lv = m0 ? pl[1] : pl[0];
-    } else if constexpr (BITS == 3) {
-        const bool m1 = a >= pt[1];
-        const bool m0 = a >= (m1 ? pt[2] : pt[0]);
-        cp = (m1 ? 2u : 0u) + (uint32_t)m0;
-        const float l0 = m1 ? pl[2] : pl[0];
-        const float l1 = m1 ? pl[3] : pl[1];
-        lv = m0 ? l1 : l0;
-    } else {
-        const bool m2 = a >= pt[3];
-        const bool m1 = a >= (m2 ? pt[5] : pt[1]);
-        const float t0 = m2 ? pt[4] : pt[0];
-        const float t1 = m2 ? pt[6] : pt[2];
-        const bool m0 = a >= (m1 ? t1 : t0);
-        cp = (m2 ? 4u : 0u) + (m1 ? 2u : 0u) + (uint32_t)m0;
-        const float q0 = m2 ? pl[4] : pl[0], q1 = m2 ? pl[5] : pl[1];
-        const float q2 = m2 ? pl[6] : pl[2], q3 = m2 ? pl[7] : pl[3];
-        const float r0 = m1 ? q2 : q0, r1 = m1 ? q3 : q1;
-        lv = m0 ? r1 : r0;
     }
     // e = y - t_c with t_c = sign(y) * lv (one bitfield insert and a subtract)
     *e = y - __builtin_copysignf(lv, y);
