@@ -204,7 +204,11 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
     // A operands of the Hadamard MFMAs, sign flips folded in: entry [kb][lane]
     // holds H32[lane%32][16(kb%2) + 8(lane/32) + t] * sigma[16kb + 8(lane/32) + t]
     // for t = 0..7 as bf16 (raw bf16 inputs) or fp16 (split inputs) +-1
-    __shared__ uint4 s_had[2 * NKB * 64];  // [+A; -A]
+    // [+A; -A].  With a full-width sketch at d = 128 only +A is kept (-A by
+    // sign flips per tile): the tables then stay below half of a CU's LDS, so
+    // two blocks fit per CU instead of one.
+    constexpr bool NEG_LDS = !(M == D && D == 128);
+    __shared__ uint4 s_had[(NEG_LDS ? 2 : 1) * NKB * 64];
     // scaled levels, indexed by code (3 and 4 bits: looked up by K/2 + c')
     __shared__ float s_lvl[16];
 
@@ -229,13 +233,19 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
             w[q] = pair;
         }
         s_had[i] = make_uint4(w[0], w[1], w[2], w[3]);
-        s_had[NKB * 64 + i] = make_uint4(w[0] ^ 0x80008000u, w[1] ^ 0x80008000u, w[2] ^ 0x80008000u, w[3] ^ 0x80008000u);
+        if constexpr (NEG_LDS)
+            s_had[NKB * 64 + i] = make_uint4(w[0] ^ 0x80008000u, w[1] ^ 0x80008000u, w[2] ^ 0x80008000u, w[3] ^ 0x80008000u);
     }
     __syncthreads();
 
     const int lane = threadIdx.x & 63;
     const int v = lane & 31;
     const int h = lane >> 5;
+    // -A of input step kb (ap = +A)
+    auto neg_operand = [&](const uint4& ap, int kb, int ln) -> uint4 {
+        if constexpr (NEG_LDS) return s_had[NKB * 64 + kb * 64 + ln];
+        return make_uint4(ap.x ^ 0x80008000u, ap.y ^ 0x80008000u, ap.z ^ 0x80008000u, ap.w ^ 0x80008000u);
+    };
 
     // upper halves of the symmetric tables, scaled
     float pt[KH > 1 ? KH - 1 : 1], pl[KH];
@@ -376,7 +386,7 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 const uint4 ap = s_had[kb * 64 + lane];
-                const uint4 an = s_had[NKB * 64 + kb * 64 + lane];
+                const uint4 an = neg_operand(ap, kb, lane);
 #pragma unroll
                 for (int ob = 0; ob < NOB; ++ob) {
                     const uint4 a = (__builtin_popcount(ob & (kb >> 1)) & 1) ? an : ap;
@@ -448,7 +458,7 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
                     half8 bhi, blo;
                     split_f16(xs, bhi, blo);
                     const uint4 ap = s_had[kb * 64 + lane];
-                    const uint4 an = s_had[NKB * 64 + kb * 64 + lane];
+                    const uint4 an = neg_operand(ap, kb, lane);
 #pragma unroll
                     for (int ob = 0; ob < NOB; ++ob) {
                         const half8 a = __builtin_bit_cast(half8, (__builtin_popcount(ob & (kb >> 1)) & 1) ? an : ap);
