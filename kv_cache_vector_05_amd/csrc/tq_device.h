@@ -209,8 +209,8 @@ struct TileLogit {
 
     intx4 aq[NRT][NC];
     intx4 as[NRT][NCS > 0 ? NCS : 1];
-    double qscale[NRT], sscale[NRT], ssum[NRT];
-    double cq;
+    // logit / nu = V qscale + gamma (Z zk - zc), Z the sign-digit sum
+    double qscale[NRT], zk[NRT], zc[NRT];
     uint32_t tdig[8];
 
     // qd/sd/scale: the prepared query digits; rowbase: first query row of the
@@ -241,10 +241,11 @@ struct TileLogit {
             const int g = gq0 + 4 * rt + qk;
             const int64_t row = rowbase + (g < G ? g : 0);
             qscale[rt] = ldexp(tscale, -(int)scale[row * 3 + 0]);
-            sscale[rt] = ldexp(1.0, -(int)scale[row * 3 + 1]);
-            ssum[rt] = (double)scale[row * 3 + 2];
+            // sqrt(pi/2)/m <s, z> with z = 2 bit - 1: (2 Z 2^-shift(s) - sum s) sqrt(pi/2)/m
+            const double cq = NCS > 0 ? kQjlD / (double)m : 0.0;
+            zk[rt] = 2.0 * cq * ldexp(1.0, -(int)scale[row * 3 + 1]);
+            zc[rt] = cq * (double)scale[row * 3 + 2];
         }
-        cq = NCS > 0 ? kQjlD / (double)m : 0.0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) tdig[i] = lvl_digits[i];
     }
@@ -322,11 +323,11 @@ struct TileLogit {
             for (int bb = 0; bb < 3; ++bb) V = V * 256.0 + digits4_value(A.y[rt][bb]);
             double logit = V * qscale[rt];
             if constexpr (NCS > 0) {
-                // sum_l s_l z_l = 2 sum_l s_l bit_l - sum_l s_l
+                // sum_l s_l z_l = 2 sum_l s_l bit_l - sum_l s_l; the digit rows
+                // are paired in int32 (|z| <= 64 * 64 per row)
                 const intx4& z = A.z[rt];
-                const double Z = ((double)z[0] * 2097152.0 + (double)z[1] * 16384.0) +
-                                 ((double)z[2] * 128.0 + (double)z[3]);
-                logit += cq * (double)gm * (2.0 * Z * sscale[rt] - ssum[rt]);
+                const double Z = digits4_value(z);
+                logit = fma((double)gm, fma(Z, zk[rt], -zc[rt]), logit);
             }
             out[rt] = logit;
         }

@@ -270,7 +270,7 @@ __global__ __launch_bounds__(256) void logits_mfma_kernel(LogM p) {
         const bool ok = tile < nfull || kbeg + tile * 16 + n < kend;
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
-            const float v = (float)((double)nus[slot] * lg[rt]);
+            const float v = (float)lg[rt] * nus[slot];
             if (rows_full && tile < nfull) optr[rt * ort + tile * 16] = v;
             else if (ok && g_lane + 4 * rt < G) optr[rt * ort + tile * 16] = v;
         }
