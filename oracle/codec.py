@@ -14,6 +14,14 @@ dentro do processo de compressao KV"; TurboESM summary, technical section 2):
   6. One-bit QJL sketch of the residual: bit_l = [(S e)_l >= 0] for an
      m x d Gaussian S.
 
+TurboESM variant (TurboESM summary, technical section 2, the dual lookup
+tables and the one-bit residual correction): ``correction = "sign"`` keeps
+one sign bit per residual coordinate instead of a Gaussian sketch (S is the
+identity, m = d): bit_i = [e_i >= 0].  No gamma is stored; the decoder adds a
+per-head calibrated mean residual magnitude mu along those signs.  The table
+may be a calibrated one (``levels``), and ``rotation = "none"`` leaves the
+vectors in their original coordinates (the value table of that section).
+
 Readings where the pages are silent (each is listed with its reason in the
 design notes): the sketch acts on the residual in the rotated domain; gamma
 is stored per vector as float32 next to nu; ties go to the upper code and a
@@ -42,6 +50,7 @@ import math
 import numpy as np
 
 from . import lloyd_max, rotation, rng as _rng
+from . import rotation as rotation_mod
 from .rope import apply_rope
 
 QJL_CONST = math.sqrt(math.pi / 2.0)
@@ -56,8 +65,15 @@ class Codebook:
     t32: np.ndarray          # [K] float32 levels
     tau32: np.ndarray        # [K-1] float32 thresholds
     pi: np.ndarray           # [d, d] float64 rotation as the codec applies it
-    sketch: np.ndarray       # [m, d] float32 (empty when m == 0)
+    sketch: np.ndarray       # [m, d] float32 (empty when m == 0; the identity for "sign")
     sigma: np.ndarray | None = None
+    correction: str = "qjl"  # "qjl": Gaussian sketch + gamma; "sign": per-coordinate signs + mu
+    mu: np.ndarray | None = None  # float32 [n_mu] mean residual magnitude per KV head ("sign")
+    rotation: str = "hadamard"    # "hadamard", "dense" or "none"
+
+    def mu_of(self, head: int) -> float:
+        """mu of a KV head (one shared value when n_mu = 1)."""
+        return float(self.mu[head if len(self.mu) > 1 else 0])
 
 
 def make_codebook(d: int, bits: int, m: int, dense: bool, sigma=None, rot_gauss=None,
@@ -79,7 +95,47 @@ def make_codebook(d: int, bits: int, m: int, dense: bool, sigma=None, rot_gauss=
     s = np.zeros((0, d), np.float32) if m == 0 else np.asarray(sketch, np.float32)
     assert s.shape == (m, d)
     return Codebook(d, bits, m, dense, t32, tau32, pi, s,
-                    None if sigma is None else np.asarray(sigma))
+                    None if sigma is None else np.asarray(sigma),
+                    rotation="dense" if dense else "hadamard")
+
+
+def thresholds_of(t32: np.ndarray) -> np.ndarray:
+    """float32 thresholds of a float32 table: midpoints of neighbouring
+    levels, formed in float64 and rounded once."""
+    t = np.asarray(t32, np.float32).astype(np.float64)
+    return (0.5 * (t[:-1] + t[1:])).astype(np.float32)
+
+
+def make_sign_codebook(d: int, bits: int, rotation: str = "hadamard", sigma=None, seed: int | None = None,
+                       levels=None, mu=None) -> Codebook:
+    """TurboESM variant (TurboESM summary, technical section 2): sign of each
+    residual coordinate, a per-head mean residual magnitude, its own table.
+
+    rotation: "hadamard" (Pi = H diag(sigma)/sqrt(d); sigma from ``seed``
+    when not given) or "none" (Pi = I: the vectors stay in their original
+    coordinates).  levels: a float32 symmetric table (calibrated), or None for
+    the Beta-law Lloyd-Max table.  mu: float32 [n_mu], or None for the
+    Beta-law mean residual magnitude of the table (lloyd_max.mean_abs_error)."""
+    if levels is None:
+        t32, tau32 = lloyd_max.table_f32(d, bits)
+    else:
+        t32 = np.asarray(levels, np.float32)
+        assert len(t32) == 1 << bits
+        tau32 = thresholds_of(t32)
+    if rotation == "hadamard":
+        if sigma is None:
+            sigma, _, _ = _rng.seeded_draws(d, 0, False, seed if seed is not None else 0)
+        sigma = np.asarray(sigma)
+        pi = rotation_mod.rht_matrix(sigma)
+    elif rotation == "none":
+        sigma = None
+        pi = np.eye(d)
+    else:
+        raise ValueError("the sign correction takes the Hadamard rotation or none")
+    if mu is None:
+        mu = np.array([lloyd_max.mean_abs_error(t32, tau32, d)], np.float32)
+    return Codebook(d, bits, d, False, t32, tau32, pi, np.eye(d, dtype=np.float32), sigma,
+                    correction="sign", mu=np.asarray(mu, np.float32).reshape(-1), rotation=rotation)
 
 
 # -------------------------------------------------------------- packing --
@@ -180,7 +236,13 @@ def encode(cb: Codebook, x: np.ndarray, pos: np.ndarray | None = None, rope=None
     u = np.where(nu[:, None] > 0, x / safe[:, None], 0.0)
     y = u @ cb.pi.T
     code_idx = quantise(cb, y)
-    e, gamma, se = residual_and_sketch(cb, y, code_idx)
+    if cb.correction == "sign":
+        # one bit per residual coordinate: bit_i = [e_i >= 0]
+        e = y - cb.t32.astype(np.float64)[code_idx]
+        gamma = np.sqrt((e * e).sum(1))
+        se = e
+    else:
+        e, gamma, se = residual_and_sketch(cb, y, code_idx)
     bits = (se.astype(np.float32) >= 0).astype(np.int64)
     signs = pack_signs(bits) if cb.m else np.zeros((len(x), 0), np.uint32)
     return Encoded(nu, gamma, pack_codes(code_idx, cb.bits), signs, y, code_idx, e, se)
@@ -194,17 +256,21 @@ def dequant(cb: Codebook, enc: Encoded):
     return yhat, z
 
 
-def reconstruct(cb: Codebook, enc: Encoded) -> np.ndarray:
+def reconstruct(cb: Codebook, enc: Encoded, head: int = 0) -> np.ndarray:
     """Unbiased vector estimate nu * Pi^T (yhat + sqrt(pi/2)/m gamma S^T z)
     (FibQuant summary, section 2.3: look up, inverse rotation, scale by the
-    norm; the sketch term makes it unbiased over S)."""
+    norm; the sketch term makes it unbiased over S).  Sign correction:
+    nu * Pi^T (yhat + mu z), with mu of the records' KV head."""
     yhat, z = dequant(cb, enc)
     w = yhat.copy()
-    if cb.m:
+    if cb.correction == "sign":
+        w += cb.mu_of(head) * z
+    elif cb.m:
         w += (QJL_CONST / cb.m) * np.asarray(enc.rnorm, np.float64)[:, None] * (z @ cb.sketch.astype(np.float64))
     return np.asarray(enc.norm, np.float64)[:, None] * (w @ cb.pi)
 
 
 def record_bytes(d: int, bits: int, m: int, with_rnorm: bool = True) -> int:
-    """Bytes of one fixed-address record."""
+    """Bytes of one fixed-address record (with_rnorm False: the sign
+    correction's record, which stores no gamma)."""
     return 4 + (4 if (m and with_rnorm) else 0) + bits * d // 8 + m // 8

@@ -18,6 +18,14 @@
   (FibQuant summary, section 2.3).  The oracle takes the softmax in two
   passes (max, then exp and sum); the GPU's online form computes the same
   function.
+* TurboESM variant (TurboESM summary, technical section 2): with one sign
+  bit per residual coordinate (S = I) and a per-head calibrated mean residual
+  magnitude mu, the key estimate is nu (yhat + mu z), so
+
+      logit = nu * ( sum_i q'_i t[c_i] + mu * sum_i q'_i z_i ),
+
+  and a value row is nu Pi_v^T (yhat_v + mu_v z_v) (Pi_v = I for a table in
+  the original coordinates).  mu is that of the records' KV head.
 * Vector search (tambur post; itstec post, introduction): a full scan of
   inner-product estimates and the k best per query; ties go to the smaller
   index.
@@ -45,20 +53,26 @@ def prep_query(cb: Codebook, q: np.ndarray, pos=None, rope=None):
     return qp, s
 
 
-def logits(cb: Codebook, qp: np.ndarray, s: np.ndarray, enc: Encoded) -> np.ndarray:
-    """[G, n] logits of G prepared queries against n key records."""
+def logits(cb: Codebook, qp: np.ndarray, s: np.ndarray, enc: Encoded, head: int = 0) -> np.ndarray:
+    """[G, n] logits of G prepared queries against n key records of KV head
+    ``head`` (used by the sign correction's mu)."""
     yhat, z = dequant(cb, enc)
     out = yhat @ qp.T                                       # [n, G]
-    if cb.m:
+    if cb.correction == "sign":
+        out = out + cb.mu_of(head) * (z @ qp.T)
+    elif cb.m:
         out = out + (QJL_CONST / cb.m) * np.asarray(enc.rnorm, np.float64)[:, None] * (z @ s.T)
     return (np.asarray(enc.norm, np.float64)[:, None] * out).T
 
 
-def value_rows(cbv: Codebook, enc: Encoded) -> np.ndarray:
-    """[n, d] value estimates nu Pi^T (yhat + sqrt(pi/2)/m gamma S^T z)."""
+def value_rows(cbv: Codebook, enc: Encoded, head: int = 0) -> np.ndarray:
+    """[n, d] value estimates nu Pi^T (yhat + sqrt(pi/2)/m gamma S^T z), or
+    nu Pi^T (yhat + mu z) with the sign correction."""
     yhat, z = dequant(cbv, enc)
     w = yhat
-    if cbv.m:
+    if cbv.correction == "sign":
+        w = w + cbv.mu_of(head) * z
+    elif cbv.m:
         w = w + (QJL_CONST / cbv.m) * np.asarray(enc.rnorm, np.float64)[:, None] * (z @ cbv.sketch.astype(np.float64))
     return np.asarray(enc.norm, np.float64)[:, None] * (w @ cbv.pi)
 
@@ -70,14 +84,15 @@ def softmax_rows(a: np.ndarray) -> np.ndarray:
 
 
 def attention(cbk: Codebook, cbv: Codebook, qp, s, enc_k: Encoded, enc_v: Encoded,
-              seq_len: int, scale: float) -> np.ndarray:
-    """[G, d] decode output over the first seq_len records (zeros if 0)."""
+              seq_len: int, scale: float, head: int = 0) -> np.ndarray:
+    """[G, d] decode output over the first seq_len records (zeros if 0) of
+    KV head ``head``."""
     G = qp.shape[0]
     if seq_len == 0:
         return np.zeros((G, cbv.d))
-    lg = logits(cbk, qp, s, enc_k)[:, :seq_len] * scale
+    lg = logits(cbk, qp, s, enc_k, head)[:, :seq_len] * scale
     p = softmax_rows(lg)
-    return p @ value_rows(cbv, enc_v)[:seq_len]
+    return p @ value_rows(cbv, enc_v, head)[:seq_len]
 
 
 def topk(scores: np.ndarray, k: int):
