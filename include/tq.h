@@ -25,6 +25,10 @@
  *     with no intermediate dequantised copy.
  *   tambur post ("Google acelera LLMs em 8 vezes"): attention logits
  *     computed from quantised keys.
+ *   TurboESM summary, technical section 2, also: separate 8-entry tables
+ *     for keys (rotated) and values (original coordinates), and a one-bit
+ *     sign per residual coordinate corrected by a calibrated mean residual
+ *     magnitude (the TQ_CORR_SIGN codebooks below).
  *
  * Conventions for every entry point
  *   - Device pointers are HIP device memory owned by the caller; host
@@ -45,7 +49,8 @@
  * Packed record (one set of planes per tensor; vector index
  * n = (seq * h_kv + head) * L_cap + token):
  *   norm [n]          float    nu = ||x||_2 (after RoPE for keys)
- *   rnorm[n]          float    gamma = ||y - t[c]||_2 (absent when m == 0)
+ *   rnorm[n]          float    gamma = ||y - t[c]||_2 (absent when m == 0
+ *                              and for TQ_CORR_SIGN codebooks)
  *   codes[n][b*d/32]  uint32   code 0 is the most negative level; bit k of
  *                              the words' bit string is bit k%32 of word k/32.
  *                              b = 1, 2, 4: coordinate i's code is bits
@@ -56,7 +61,9 @@
  *                              bits are bits 8(r%4)+6, +7 of W_{r/4} and the
  *                              high bit is bit 8(r%4) + 6 + r/4 of W2
  *   signs[n][m/32]    uint32   bit l (bit l%32 of word l/32) is 1 iff
- *                              (S e)_l >= 0
+ *                              (S e)_l >= 0; for TQ_CORR_SIGN (S = I,
+ *                              m = d) iff e_l >= 0
+ * A TQ_CORR_SIGN record at d = 64, b = 3 is 4 + 24 + 8 = 36 bytes.
  */
 #ifndef TQ_H
 #define TQ_H
@@ -78,7 +85,8 @@ enum {
 };
 
 enum { TQ_F32 = 0, TQ_BF16 = 1 };                                  /* element types */
-enum { TQ_ROT_AUTO = 0, TQ_ROT_HADAMARD = 1, TQ_ROT_DENSE = 2 };   /* rotation forms */
+enum { TQ_ROT_AUTO = 0, TQ_ROT_HADAMARD = 1, TQ_ROT_DENSE = 2, TQ_ROT_NONE = 3 };  /* rotation forms */
+enum { TQ_CORR_QJL = 0, TQ_CORR_SIGN = 1 };                        /* residual corrections */
 enum { TQ_OP_ENCODE = 0, TQ_OP_LOGITS = 1, TQ_OP_DECODE = 2 };     /* workspace queries */
 
 /*
@@ -89,13 +97,25 @@ enum { TQ_OP_ENCODE = 0, TQ_OP_LOGITS = 1, TQ_OP_DECODE = 2 };     /* workspace 
  *            bits*d must be a multiple of 32.
  *   m        QJL sketch rows: 0 (no sketch, no rnorm plane) or a multiple of
  *            32 up to 4096; the Hadamard form has kernels for m = 0, d/2, d.
- *   rotation TQ_ROT_AUTO (Hadamard iff d is a power of two), _HADAMARD, _DENSE.
+ *   rotation TQ_ROT_AUTO (Hadamard iff d is a power of two), _HADAMARD,
+ *            _DENSE, or _NONE (Pi = I: vectors quantised in their original
+ *            coordinates; TQ_CORR_SIGN codebooks only).
  *   seed     draws sigma, the rotation Gaussians and S when no tq_draws are
  *            given (SplitMix64 streams, Box-Muller Gaussians).
+ *   correction
+ *            TQ_CORR_QJL (0): S is an m x d Gaussian sketch, gamma is stored
+ *            and the correction is sqrt(pi/2)/m gamma S^T z.
+ *            TQ_CORR_SIGN (TurboESM summary, technical section 2): one sign
+ *            per residual coordinate (S = I, so m must equal d), no gamma
+ *            plane, and the correction is mu z with mu the codebook's mean
+ *            residual magnitude of the record's KV head.  Needs d = 64 or
+ *            128, bits 1..3, rotation Hadamard or none.
+ *   reserved must be 0.
  */
 typedef struct {
     int32_t d, bits, m, rotation;
     uint64_t seed;
+    int32_t correction, reserved;
 } tq_spec;
 
 /*
@@ -105,7 +125,9 @@ typedef struct {
  *   rot_gauss [d*d] double     dense form: Pi = Q of rot_gauss = Q R with
  *                              diag(R) > 0, stored as float32 (row-major,
  *                              y = Pi u)
- *   sketch    [m*d] float      S, row-major
+ *   sketch    [m*d] float      S, row-major (must be NULL for
+ *                              TQ_CORR_SIGN, whose S is the identity)
+ * TQ_ROT_NONE codebooks read no sigma.
  */
 typedef struct {
     const int8_t* sigma;
@@ -116,7 +138,8 @@ typedef struct {
 typedef struct tq_codebook tq_codebook;  /* opaque; immutable after init */
 
 /* Caller-owned planes of one packed tensor (device memory); n = capacity in
- * records.  rnorm and signs may be NULL when the codebook has m == 0. */
+ * records.  rnorm and signs may be NULL when the codebook has m == 0; rnorm
+ * may be NULL for TQ_CORR_SIGN codebooks (it is neither read nor written). */
 typedef struct {
     float* norm;
     float* rnorm;
@@ -132,8 +155,8 @@ typedef struct {
  *       of one coordinate of a uniform point on S^{d-1} (FibQuant summary,
  *       section 2.1; itstec post, "Por dentro do processo": a Beta law),
  *       levels at the conditional means, thresholds at the midpoints
- *   rotation  Hadamard: [d] sigma as +-1.0f; dense: [d*d] Pi row-major
- *   sketch    [m*d] S row-major
+ *   rotation  Hadamard: [d] sigma as +-1.0f; dense: [d*d] Pi row-major; none: not written
+ *   sketch    [m*d] S row-major (the identity for TQ_CORR_SIGN)
  * Returns TQ_EINVAL / TQ_EUNSUPPORTED for a bad spec.
  */
 tq_status tq_codebook_tables(const tq_spec* spec, const tq_draws* draws, float* levels,
@@ -148,6 +171,56 @@ tq_status tq_codebook_tables(const tq_spec* spec, const tq_draws* draws, float* 
  */
 tq_status tq_codebook_init(const tq_spec* spec, const tq_draws* draws, void* stream,
                            tq_codebook** out);
+
+/*
+ * tq_codebook_init_calibrated: as tq_codebook_init, with the table and (for
+ * TQ_CORR_SIGN) the mean residual magnitudes given instead of derived
+ * (TurboESM summary, technical section 2: per-tensor tables and a
+ * calibrated residual magnitude; see tq_calibrate).
+ *   levels   host float [2^bits], strictly increasing and symmetric
+ *            (levels[K-1-j] == -levels[j] exactly), or NULL for the
+ *            spherical-Beta Lloyd-Max table.  Thresholds are the midpoints
+ *            of neighbouring levels, formed in double and rounded to float.
+ *   mu, n_mu host float [n_mu], finite and >= 0: mu of KV head h is
+ *            mu[n_mu == 1 ? 0 : h]; calls on the codebook then need
+ *            h_kv == n_mu unless n_mu == 1.  NULL (n_mu 0) gives one shared
+ *            mu = E|Y - t[c(Y)]| under the spherical-Beta law of the table.
+ *            Must be NULL / 0 for TQ_CORR_QJL codebooks.
+ * Errors as tq_codebook_init, and TQ_EINVAL for a bad table or mu.
+ */
+tq_status tq_codebook_init_calibrated(const tq_spec* spec, const tq_draws* draws, const float* levels,
+                                      const float* mu, int32_t n_mu, void* stream, tq_codebook** out);
+
+/*
+ * tq_calibrate (host only, no GPU): fits a TQ_CORR_SIGN codebook's table
+ * and per-head mean residual magnitudes to a calibration batch (TurboESM
+ * summary, technical section 2).
+ *   x          host float [n_tok][h][d] (contiguous): vectors as the encoder
+ *              would receive them; token t sits at position tok_offset + t
+ *   rope_cos, rope_sin, rope_npos   host tables as tq_rope_table writes
+ *              them ([rope_npos][d/2]), or NULL for no RoPE; they must
+ *              cover position tok_offset + n_tok - 1
+ *   levels     out: host float [2^bits], the symmetric table: its upper
+ *              half is Lloyd's fixed point for |y| over every head's rotated
+ *              unit vectors (y = Pi RoPE(x) / nu, vectors with nu = 0 left
+ *              out), started from the order statistics
+ *              |y|_(floor((j + 1/2) N / (K/2))) of the N sorted values and
+ *              iterated until no value changes cell (a value on a boundary
+ *              goes to the upper cell; an empty cell keeps its level)
+ *   mu         out: host float [h], mean |y_i - t[c_i]| over head h's
+ *              vectors and coordinates, codes decided in float against the
+ *              float table (0 for a head with no non-zero vector)
+ * The rotation is the one spec/draws give (sigma for Hadamard, identity for
+ * TQ_ROT_NONE).  Errors: TQ_EINVAL (bad spec or sizes, no non-zero vector),
+ * TQ_EUNSUPPORTED.
+ */
+tq_status tq_calibrate(const tq_spec* spec, const tq_draws* draws, const float* x, int64_t n_tok,
+                       int32_t h, int32_t tok_offset, const float* rope_cos, const float* rope_sin,
+                       int32_t rope_npos, float* levels, float* mu);
+
+/* The codebook's mean residual magnitudes: *n_mu receives their count (0 for
+ * TQ_CORR_QJL), mu (host float [*n_mu], may be NULL) the values. */
+tq_status tq_codebook_get_mu(const tq_codebook* cb, float* mu, int32_t* n_mu);
 
 /* Frees a codebook's device tables.  The caller guarantees no enqueued
  * work still uses it (synchronise first).  NULL is accepted. */
@@ -195,7 +268,9 @@ tq_status tq_encode_kv(const tq_codebook* ck, const tq_codebook* cv, const void*
  * tq_attn_logits: attention logits from packed keys (tambur post; iaemfoco
  * post, "Uma Nova Abordagem" for the unbiased QJL correction):
  *   logit[b][h][t] = nu_t ( <q'_h, t[c_t]> + sqrt(pi/2)/m gamma_t <s_h, z_t> )
- * with q'_h = Pi RoPE(q_h, seq_len[b]), s_h = S q'_h, z in {-1,+1}.
+ * with q'_h = Pi RoPE(q_h, seq_len[b]), s_h = S q'_h, z in {-1,+1}; for a
+ * TQ_CORR_SIGN codebook the second term is mu_kv <q'_h, z_t> (TurboESM
+ * summary, technical section 2), kv = h / (Hq / h_kv).
  *   q             device [B][Hq][d], dtype TQ_F32 or TQ_BF16
  *   k             packed keys, capacity >= B*h_kv*L_cap
  *   B, Hq, h_kv   Hq a multiple of h_kv; query head h reads KV head h/(Hq/h_kv)
@@ -222,7 +297,10 @@ tq_status tq_attn_logits(const tq_codebook* ck, const void* q, int32_t q_dtype, 
  * summary, technical section 2, fused kernel; FibQuant summary, section 2.3
  * for value reconstruction):
  *   out[b][h] = sum_t p_t nu^v_t Pi_v^T (t_v[c^v_t] + sqrt(pi/2)/m_v gamma^v_t S_v^T z^v_t),
- *   p = softmax over t < seq_len[b] of scale * logit[b][h][t].
+ *   p = softmax over t < seq_len[b] of scale * logit[b][h][t];
+ * a TQ_CORR_SIGN value codebook takes mu_kv z^v_t as the correction term
+ * (and Pi_v = I for TQ_ROT_NONE).  Key and value codebooks need the same d,
+ * bits and m; TQ_CORR_SIGN codebooks are served for bits <= 3 only.
  * Split over the key axis with an online softmax and a log-sum-exp merge.
  *   scale         0 means 1/sqrt(d)
  *   out           device float [B][Hq][d]; zeros where seq_len[b] == 0

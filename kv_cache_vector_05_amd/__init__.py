@@ -8,6 +8,15 @@ raise if libtq.so is missing or no GPU is present.
 
     ck = Codebook(d=128, bits=3, m=64, seed=0)          # keys
     cv = Codebook(d=128, bits=3, m=64, seed=1)          # values
+
+TurboESM-style codebooks (one residual sign per coordinate, a calibrated
+mean residual magnitude per KV head, separate key/value tables, values in
+their original coordinates):
+
+    lk, mk = calibrate(128, 3, k_sample, seed=0, rope=rope_host)
+    lv, mv = calibrate(128, 3, v_sample, rotation="none")
+    ck = Codebook(128, 3, 128, seed=0, correction="sign", levels=lk, mu=mk)
+    cv = Codebook(128, 3, 128, rotation="none", correction="sign", levels=lv, mu=mv)
     kp, vp = Packed(ck, n), Packed(cv, n)               # n = B * h_kv * L_cap
     encode_kv(ck, cv, k, v, kp, vp, L_cap=L, rope=rope)
     logits = attn_logits(ck, q, kp, h_kv, L, seq_len, rope=rope)
@@ -20,13 +29,15 @@ import ctypes as C
 import numpy as np
 
 from . import _lib
-from ._lib import (TQError, TQ_F32, TQ_BF16, TQ_ROT_AUTO, TQ_ROT_HADAMARD, TQ_ROT_DENSE, TQ_OP_ENCODE,
-                   TQ_OP_LOGITS, TQ_OP_DECODE, check, lib, tq_draws, tq_packed, tq_spec)
+from ._lib import (TQError, TQ_F32, TQ_BF16, TQ_ROT_AUTO, TQ_ROT_HADAMARD, TQ_ROT_DENSE, TQ_ROT_NONE,
+                   TQ_CORR_QJL, TQ_CORR_SIGN, TQ_OP_ENCODE, TQ_OP_LOGITS, TQ_OP_DECODE, check, lib, tq_draws,
+                   tq_packed, tq_spec)
 
 __all__ = ["Codebook", "Packed", "encode_kv", "attn_logits", "attn_decode", "rope_table", "codebook_tables",
-           "plane_words", "workspace_bytes", "TQError", "lib"]
+           "plane_words", "workspace_bytes", "calibrate", "TQError", "lib"]
 
-_ROT = {"auto": TQ_ROT_AUTO, "hadamard": TQ_ROT_HADAMARD, "dense": TQ_ROT_DENSE}
+_ROT = {"auto": TQ_ROT_AUTO, "hadamard": TQ_ROT_HADAMARD, "dense": TQ_ROT_DENSE, "none": TQ_ROT_NONE}
+_CORR = {"qjl": TQ_CORR_QJL, "sign": TQ_CORR_SIGN}
 
 
 def _torch():
@@ -52,9 +63,10 @@ def _dtype_code(t):
     raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
 
 
-def _spec(d, bits, m, rotation="auto", seed=0):
+def _spec(d, bits, m, rotation="auto", seed=0, correction="qjl"):
     return tq_spec(int(d), int(bits), int(m), _ROT[rotation] if isinstance(rotation, str) else int(rotation),
-                   int(seed) & 0xFFFFFFFFFFFFFFFF)
+                   int(seed) & 0xFFFFFFFFFFFFFFFF,
+                   _CORR[correction] if isinstance(correction, str) else int(correction), 0)
 
 
 def _draws(sigma=None, rot_gauss=None, sketch=None):
@@ -75,9 +87,9 @@ def _draws(sigma=None, rot_gauss=None, sketch=None):
     return dr, keep
 
 
-def plane_words(d, bits, m, rotation="auto"):
+def plane_words(d, bits, m, rotation="auto", correction="qjl"):
     """(code words, sign words) per record."""
-    sp = _spec(d, bits, m, rotation)
+    sp = _spec(d, bits, m, rotation, 0, correction)
     cw = lib().tq_plane_words(C.byref(sp), 0)
     sw = lib().tq_plane_words(C.byref(sp), 1)
     if cw < 0:
@@ -85,10 +97,12 @@ def plane_words(d, bits, m, rotation="auto"):
     return int(cw), int(sw)
 
 
-def codebook_tables(d, bits, m, rotation="auto", seed=0, sigma=None, rot_gauss=None, sketch=None):
+def codebook_tables(d, bits, m, rotation="auto", seed=0, sigma=None, rot_gauss=None, sketch=None,
+                    correction="qjl"):
     """Host-only table construction (no GPU): dict of levels, thresholds,
-    rotation (sigma as +-1 or the dense matrix) and sketch."""
-    sp = _spec(d, bits, m, rotation, seed)
+    rotation (sigma as +-1 or the dense matrix; zeros for rotation "none")
+    and sketch."""
+    sp = _spec(d, bits, m, rotation, seed, correction)
     dr, keep = _draws(sigma, rot_gauss, sketch)
     K = 1 << bits
     lv = np.zeros(K, np.float32)
@@ -102,18 +116,53 @@ def codebook_tables(d, bits, m, rotation="auto", seed=0, sigma=None, rot_gauss=N
             "sketch": sk.reshape(m, d), "dense": dense}
 
 
+def calibrate(d, bits, x, rotation="hadamard", seed=0, sigma=None, tok_offset=0, rope=None,
+              correction="sign"):
+    """Host-only calibration (no GPU) of a table and per-head mean residual
+    magnitudes from x [n_tok, h, d] (numpy float32; rope = host (cos, sin)
+    tables from rope_table(..., device=None)).  Returns (levels [2^bits],
+    mu [h]) as float32 arrays."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    n_tok, h, dx = x.shape
+    if dx != d:
+        raise ValueError("x is [n_tok, h, d]")
+    sp = _spec(d, bits, d if correction == "sign" else 0, rotation, seed, correction)
+    dr, keep = _draws(sigma, None, None)
+    lv = np.zeros(1 << bits, np.float32)
+    mu = np.zeros(h, np.float32)
+    cs = sn = None
+    npos = 0
+    if rope is not None:
+        cs = np.ascontiguousarray(rope[0], np.float32)
+        sn = np.ascontiguousarray(rope[1], np.float32)
+        npos = cs.shape[0]
+    check(lib().tq_calibrate(C.byref(sp), C.byref(dr), x.ctypes.data, n_tok, h, int(tok_offset),
+                             None if cs is None else cs.ctypes.data, None if sn is None else sn.ctypes.data, npos,
+                             lv.ctypes.data, mu.ctypes.data))
+    return lv, mu
+
+
 class Codebook:
     """A codebook (Lloyd-Max table, rotation, sketch) resident on the current
     GPU.  Draws default to the library's seeded generator; pass sigma /
-    rot_gauss / sketch (host arrays) to supply them."""
+    rot_gauss / sketch (host arrays) to supply them.  correction="sign" makes
+    a TurboESM-style codebook (m must equal d); levels / mu give a calibrated
+    table and per-head mean residual magnitudes (see calibrate)."""
 
-    def __init__(self, d, bits, m, rotation="auto", seed=0, sigma=None, rot_gauss=None, sketch=None):
+    def __init__(self, d, bits, m, rotation="auto", seed=0, sigma=None, rot_gauss=None, sketch=None,
+                 correction="qjl", levels=None, mu=None):
         self.d, self.bits, self.m = int(d), int(bits), int(m)
-        sp = _spec(d, bits, m, rotation, seed)
+        sp = _spec(d, bits, m, rotation, seed, correction)
         dr, keep = _draws(sigma, rot_gauss, sketch)
+        lv = None if levels is None else np.ascontiguousarray(levels, np.float32)
+        mu_a = None if mu is None else np.ascontiguousarray(np.atleast_1d(mu), np.float32)
         h = C.c_void_p()
-        check(lib().tq_codebook_init(C.byref(sp), C.byref(dr), _stream(), C.byref(h)))
+        check(lib().tq_codebook_init_calibrated(C.byref(sp), C.byref(dr), None if lv is None else lv.ctypes.data,
+                                                None if mu_a is None else mu_a.ctypes.data,
+                                                0 if mu_a is None else len(mu_a), _stream(), C.byref(h)))
         self._h = h
+        self.correction = correction if isinstance(correction, str) else ("sign" if correction else "qjl")
+        self.has_rnorm = self.m > 0 and self.correction == "qjl"
         out = tq_spec()
         check(lib().tq_codebook_get_spec(h, C.byref(out)))
         self.rotation = out.rotation
@@ -124,6 +173,16 @@ class Codebook:
     @property
     def handle(self):
         return self._h
+
+    def mu(self):
+        """The mean residual magnitudes (float32 array; empty for the QJL
+        sketch)."""
+        n = C.c_int32()
+        check(lib().tq_codebook_get_mu(self._h, None, C.byref(n)))
+        out = np.zeros(n.value, np.float32)
+        if n.value:
+            check(lib().tq_codebook_get_mu(self._h, out.ctypes.data, C.byref(n)))
+        return out
 
     def export(self):
         K = 1 << self.bits
@@ -158,10 +217,11 @@ class Packed:
         torch = _torch()
         self.n = int(n)
         self.norm = torch.zeros(self.n, dtype=torch.float32, device=device)
-        self.rnorm = torch.zeros(self.n if cb.m else 0, dtype=torch.float32, device=device)
+        self.rnorm = torch.zeros(self.n if cb.has_rnorm else 0, dtype=torch.float32, device=device)
         self.codes = torch.zeros((self.n, cb.code_words), dtype=torch.int32, device=device)
         self.signs = torch.zeros((self.n, cb.sign_words), dtype=torch.int32, device=device)
         self.m = cb.m
+        self.has_rnorm = cb.has_rnorm
 
     @classmethod
     def from_arrays(cls, cb, norm, rnorm, codes, signs, device="cuda"):
@@ -169,15 +229,16 @@ class Packed:
         p = cls.__new__(cls)
         p.n = int(len(norm))
         p.m = cb.m
+        p.has_rnorm = cb.has_rnorm
         p.norm = torch.as_tensor(np.asarray(norm, np.float32), device=device)
-        p.rnorm = torch.as_tensor(np.asarray(rnorm if cb.m else np.zeros(0), np.float32), device=device)
+        p.rnorm = torch.as_tensor(np.asarray(rnorm if cb.has_rnorm else np.zeros(0), np.float32), device=device)
         p.codes = torch.as_tensor(np.asarray(codes, np.uint32).view(np.int32), device=device)
         p.signs = torch.as_tensor(np.asarray(signs if cb.m else np.zeros((p.n, 0)), np.uint32).view(np.int32),
                                   device=device)
         return p
 
     def struct(self):
-        return tq_packed(self.norm.data_ptr(), self.rnorm.data_ptr() if self.m else None, self.codes.data_ptr(),
+        return tq_packed(self.norm.data_ptr(), self.rnorm.data_ptr() if self.has_rnorm else None, self.codes.data_ptr(),
                          self.signs.data_ptr() if self.m else None, self.n)
 
     def numpy(self):

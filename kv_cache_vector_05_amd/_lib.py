@@ -12,13 +12,14 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtq.so")
 
 TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_ENOMEM, TQ_EHIP = 0, -1, -2, -3, -4
 TQ_F32, TQ_BF16 = 0, 1
-TQ_ROT_AUTO, TQ_ROT_HADAMARD, TQ_ROT_DENSE = 0, 1, 2
+TQ_ROT_AUTO, TQ_ROT_HADAMARD, TQ_ROT_DENSE, TQ_ROT_NONE = 0, 1, 2, 3
+TQ_CORR_QJL, TQ_CORR_SIGN = 0, 1
 TQ_OP_ENCODE, TQ_OP_LOGITS, TQ_OP_DECODE = 0, 1, 2
 
 
 class tq_spec(C.Structure):
     _fields_ = [("d", C.c_int32), ("bits", C.c_int32), ("m", C.c_int32), ("rotation", C.c_int32),
-                ("seed", C.c_uint64)]
+                ("seed", C.c_uint64), ("correction", C.c_int32), ("reserved", C.c_int32)]
 
 
 class tq_draws(C.Structure):
@@ -36,6 +37,11 @@ SIGNATURES = {
                                        C.c_void_p, C.c_void_p]),
     "tq_codebook_init": (C.c_int32, [C.POINTER(tq_spec), C.POINTER(tq_draws), C.c_void_p,
                                      C.POINTER(C.c_void_p)]),
+    "tq_codebook_init_calibrated": (C.c_int32, [C.POINTER(tq_spec), C.POINTER(tq_draws), C.c_void_p, C.c_void_p,
+                                                C.c_int32, C.c_void_p, C.POINTER(C.c_void_p)]),
+    "tq_calibrate": (C.c_int32, [C.POINTER(tq_spec), C.POINTER(tq_draws), C.c_void_p, C.c_int64, C.c_int32,
+                                 C.c_int32, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p]),
+    "tq_codebook_get_mu": (C.c_int32, [C.c_void_p, C.c_void_p, C.POINTER(C.c_int32)]),
     "tq_codebook_destroy": (C.c_int32, [C.c_void_p]),
     "tq_codebook_get_spec": (C.c_int32, [C.c_void_p, C.POINTER(tq_spec)]),
     "tq_codebook_export": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),

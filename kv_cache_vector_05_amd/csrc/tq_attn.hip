@@ -575,6 +575,9 @@ struct MergeK {
     int32_t nsplit, d, m;
     const float* sigma;   // Hadamard form
     const float* sketch;  // [m][d]
+    float corr;           // scale of the correction term (sqrt(pi/2)/m, or 1 for the sign correction)
+    int32_t s_ident;      // S = I (sign correction): S^T A_z = A_z
+    int32_t norot;        // Pi = I: no inverse rotation
     float* out;           // [B*Hq][d]
 };
 
@@ -633,18 +636,26 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeK p) {
     if (t >= D && col) az[t - D] = acc;
     __syncthreads();
     if (t < D) {
-        // S^T A_z: sixteen sketch rows' loads in flight at a time (m is a multiple of 32)
         float corr = 0.f;
-        for (int k0 = 0; k0 < p.m; k0 += 16) {
-            float sv[16];
+        if (p.s_ident) {
+            corr = p.m ? az[t] : 0.f;
+        } else {
+            // S^T A_z: sixteen sketch rows' loads in flight at a time (m is a multiple of 32)
+            for (int k0 = 0; k0 < p.m; k0 += 16) {
+                float sv[16];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) sv[u] = p.sketch[(int64_t)(k0 + u) * D + t];
+                for (int u = 0; u < 16; ++u) sv[u] = p.sketch[(int64_t)(k0 + u) * D + t];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) corr = fmaf(sv[u], az[k0 + u], corr);
+                for (int u = 0; u < 16; ++u) corr = fmaf(sv[u], az[k0 + u], corr);
+            }
         }
-        w[t] = acc + (p.m ? kQjl / (float)p.m : 0.f) * corr;
+        w[t] = acc + p.corr * corr;
     }
     __syncthreads();
+    if (p.norot) {
+        if (t < D) p.out[row * D + t] = (l > 0.f) ? w[t] / l : 0.f;
+        return;
+    }
     for (int s = 1; s < D; s <<= 1) {
         if (t < D / 2) {
             const int i = (t / s) * 2 * s + (t % s);
@@ -1008,6 +1019,9 @@ hipError_t launch_decode(const tq_codebook* ck, const tq_codebook* cv, const tq_
     mk.m = m;
     mk.sigma = cv->dev.sigma;
     mk.sketch = cv->dev.sketch;
+    mk.corr = (float)corr_scale(cv);
+    mk.s_ident = sign_corr(cv) ? 1 : 0;
+    mk.norot = no_rotation(cv) ? 1 : 0;
     mk.out = a.out;
     if (decode_mfma_supported(ck, cv)) {
         int nsplit = 1, split_len = 0;

@@ -5,7 +5,9 @@
 // correction and the softmax run in one kernel, with no dequantised copy of
 // the cache.  Per query, the split kernel returns for its share of the key
 // axis the max logit M, l = sum_j exp(a_j - M) and, in the rotated domain,
-//     A_y[i] = sum_j w_j t_v[c_ji],   A_z[r] = sum_j w_j gamma_j z_jr,   w_j = exp(a_j - M) nu_j;
+//     A_y[i] = sum_j w_j t_v[c_ji],   A_z[r] = sum_j w_j gamma_j z_jr,   w_j = exp(a_j - M) nu_j
+// (with the sign correction of the TurboESM summary, technical section 2,
+// gamma_j is the KV head's mu and S_v = I);
 // the merge kernel combines the splits by log-sum-exp and maps back once per
 // query: out = Pi_v^T (A_y + sqrt(pi/2)/m S_v^T A_z) / l  (iaemfoco post,
 // "TurboQuant: Uma Nova Abordagem", the QJL dequantiser; FibQuant summary,
@@ -58,6 +60,10 @@ struct DecM {
     int32_t shift_k;
     uint32_t tdig_v[8];
     int32_t shift_v;
+    double cq_k;                  // scale of the key correction term
+    const float* k_mu;            // sign correction: mu per KV head, else nullptr (gamma per key)
+    const float* v_mu;
+    int32_t k_mu_stride, v_mu_stride;
     float* part;  // [B*Hq][nsplit][2 + D + M]
 };
 
@@ -151,6 +157,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
     }
     const int nch = (c1 - c0 + 63) / 64;
     const int64_t rec_base = bk * p.L_cap;
+    // correction weights: gamma per record (QJL sketch) or the KV head's mu
+    const float k_head = p.k_mu ? p.k_mu[kh * p.k_mu_stride] : 0.f;
+    const float v_head = p.v_mu ? p.v_mu[kh * p.v_mu_stride] : 0.f;
 
     // ---------------- pass 1: logits, split max, value-norm bounds
     float mx[NRT];
@@ -159,7 +168,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
     float numax = 0.f, ngmax = 0.f;
     {
         TL tl;
-        tl.init(p.qd, p.sd, p.qscale, p.sdw, M, rowbase, gq0, G, p.tdig_k, p.shift_k, lane);
+        tl.init(p.qd, p.sd, p.qscale, p.sdw, p.cq_k, rowbase, gq0, G, p.tdig_k, p.shift_k, lane);
         // the key record (and the value norms) of the next chunk's tile are
         // loaded before the current tile computes
         struct Rec1 {
@@ -170,9 +179,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
             const int64_t rec = rec_base + min(c0 + 64 * c + 16 * wave + n, c1 - 1);
             TL::load(p.k_codes + rec * Q::CW + Q::word0(qk), p.k_signs + rec * MW, PER, lane, r.raw);
             r.nu = p.k_norm[rec];
-            r.gm = M > 0 ? p.k_rnorm[rec] : 0.f;
+            r.gm = M > 0 ? (p.k_mu ? k_head : p.k_rnorm[rec]) : 0.f;
             r.vn = p.v_norm[rec];
-            r.vg = M > 0 ? p.v_rnorm[rec] : 0.f;
+            r.vg = M > 0 ? (p.v_mu ? v_head : p.v_rnorm[rec]) : 0.f;
         };
         if (c0 + 16 * wave < c1) fetch1(0, cur);
         for (int c = 0; c < nch; ++c) {
@@ -261,7 +270,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
         Q::load(p.v_codes + rec * Q::CW + Q::word0(qk), qk, r.W);
         r.sg = M > 0 ? p.v_signs[rec * MW + ((qk * PER) >> 5)] : 0u;
         r.vn = p.v_norm[rec];
-        r.vg = M > 0 ? p.v_rnorm[rec] : 0.f;
+        r.vg = M > 0 ? (p.v_mu ? v_head : p.v_rnorm[rec]) : 0.f;
     };
     fetch2(0, vcur);
     for (int c = 0; c < nch; ++c) {
@@ -481,6 +490,12 @@ hipError_t launch_decode_mfma(const tq_codebook* ck, const tq_codebook* cv, cons
     }
     p.shift_k = ck->lvl_shift;
     p.shift_v = cv->lvl_shift;
+    p.cq_k = corr_scale(ck);
+    const MuRef mk = mu_ref(ck), mv = mu_ref(cv);
+    p.k_mu = mk.ptr;
+    p.k_mu_stride = mk.stride;
+    p.v_mu = mv.ptr;
+    p.v_mu_stride = mv.stride;
     p.part = part;
     const unsigned gx = (unsigned)((int64_t)a.B * a.h_kv * p.ngroups);
     if (gx == 0 || nsplit == 0) return hipSuccess;

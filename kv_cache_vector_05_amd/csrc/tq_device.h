@@ -213,9 +213,11 @@ struct TileLogit {
     double qscale[NRT], zk[NRT], zc[NRT];
     uint32_t tdig[8];
 
-    // qd/sd/scale: the prepared query digits; rowbase: first query row of the
-    // KV head; gq0: first query of this row-tile set; G: queries per KV head
-    __device__ void init(const int8_t* qd, const int8_t* sd, const float* scale, int sdw, int m, int64_t rowbase,
+    // qd/sd/scale: the prepared query digits; cq: scale of the correction
+    // term (sqrt(pi/2)/m for the QJL sketch, 1 for the sign correction);
+    // rowbase: first query row of the KV head; gq0: first query of this
+    // row-tile set; G: queries per KV head
+    __device__ void init(const int8_t* qd, const int8_t* sd, const float* scale, int sdw, double cq, int64_t rowbase,
                          int gq0, int G, const uint32_t* lvl_digits, int lvl_shift, int lane) {
         const int qk = lane >> 4;
         const int a = lane & 3;
@@ -241,10 +243,10 @@ struct TileLogit {
             const int g = gq0 + 4 * rt + qk;
             const int64_t row = rowbase + (g < G ? g : 0);
             qscale[rt] = ldexp(tscale, -(int)scale[row * 3 + 0]);
-            // sqrt(pi/2)/m <s, z> with z = 2 bit - 1: (2 Z 2^-shift(s) - sum s) sqrt(pi/2)/m
-            const double cq = NCS > 0 ? kQjlD / (double)m : 0.0;
-            zk[rt] = 2.0 * cq * ldexp(1.0, -(int)scale[row * 3 + 1]);
-            zc[rt] = cq * (double)scale[row * 3 + 2];
+            // cq <s, z> with z = 2 bit - 1: (2 Z 2^-shift(s) - sum s) cq
+            const double c = NCS > 0 ? cq : 0.0;
+            zk[rt] = 2.0 * c * ldexp(1.0, -(int)scale[row * 3 + 1]);
+            zc[rt] = c * (double)scale[row * 3 + 2];
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) tdig[i] = lvl_digits[i];
@@ -312,7 +314,8 @@ struct TileLogit {
         }
     }
 
-    // out[rt] = <q', t[c]> + sqrt(pi/2)/m gamma <s, z>  (not yet times nu)
+    // out[rt] = <q', t[c]> + cq gm <s, z>  (not yet times nu); gm is gamma
+    // for the QJL sketch, the KV head's mu for the sign correction
     __device__ void finish(const Acc& A, float gm, double out[NRT]) const {
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {

@@ -19,6 +19,11 @@
 //     fp16 hi/lo parts are again a B operand, so the sketch S e of all 32
 //     vectors is m/32 row blocks of d/16 MFMA steps, with S read from LDS in
 //     the matching coordinate order (laid out by the host).
+// Sign correction (TurboESM summary, technical section 2; MODE 1 and 2): the
+// sign of every residual coordinate is kept (S = I, m = d) and no gamma, so
+// the sketch MFMAs give way to byte-wise sign packing.  MODE 2 also skips the
+// rotation (values quantised in their original coordinates): the lane loads
+// its output coordinates straight from the input.
 // Blocks are persistent (one resident round, grid-stride over tiles) so each
 // block stages its tables in LDS once; tiles run token block, then sequence,
 // then head, so a block's four waves encode four heads of the same tokens and
@@ -187,17 +192,24 @@ __device__ __forceinline__ void rope_stage_store(f32x4* lds, const int (&tab)[NQ
     for (int j = 0; j < NQ; ++j) lds[((tab[j] * 32 + row[j]) * RS) / 4 + c4[j]] = pre[j];
 }
 
-template <int D, int BITS, int M, bool BF16, bool ROPE>
+// MODE 0: Hadamard rotation, Gaussian sketch of the residual and gamma;
+// 1: Hadamard rotation, sign of each residual coordinate; 2: no rotation,
+// sign of each residual coordinate.
+template <int D, int BITS, int M, bool BF16, bool ROPE, int MODE>
 __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
+    constexpr bool SGN = MODE != 0;
+    constexpr bool NOROT = MODE == 2;
+    static_assert(!SGN || M == D, "the sign correction keeps one bit per coordinate");
     constexpr int HALF = D / 2;
     constexpr int NOB = D / 32;            // 32-coordinate output blocks of H
     constexpr int NKB = D / 16;            // 16-coordinate input steps of the MFMA
-    constexpr bool EXACT = BF16 && !ROPE;  // raw bf16 inputs are the MFMA operand as loaded
+    constexpr bool EXACT = BF16 && !ROPE && !NOROT;  // raw bf16 inputs are the MFMA operand as loaded
     constexpr int KH = 1 << (BITS - 1);
     constexpr int CW = BITS * D / 32;      // code words per record
     constexpr int NRB = M / 32;            // sketch row blocks (= sign words)
     constexpr int NP = D / 16;             // sketch K-steps: chunks of 8 values per lane
-    constexpr int SKN = M > 0 ? NRB * NP * 2 * 64 : 1;
+    constexpr bool SKETCH = M > 0 && !SGN;  // Gaussian sketch on the matrix cores
+    constexpr int SKN = SKETCH ? NRB * NP * 2 * 64 : 1;
     // residuals enter the sketch scaled by 2^8 so their fp16 low parts stay normal
     constexpr float ESCALE = 256.0f;
     __shared__ half8 s_sk[SKN];
@@ -207,17 +219,17 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
     // [+A; -A].  With a full-width sketch at d = 128 only +A is kept (-A by
     // sign flips per tile): the tables then stay below half of a CU's LDS, so
     // two blocks fit per CU instead of one.
-    constexpr bool NEG_LDS = !(M == D && D == 128);
-    __shared__ uint4 s_had[(NEG_LDS ? 2 : 1) * NKB * 64];
+    constexpr bool NEG_LDS = !(M == D && D == 128) || SGN;
+    __shared__ uint4 s_had[NOROT ? 1 : (NEG_LDS ? 2 : 1) * NKB * 64];
     // scaled levels, indexed by code (3 and 4 bits: looked up by K/2 + c')
     __shared__ float s_lvl[16];
 
-    if constexpr (M > 0) {
+    if constexpr (SKETCH) {
         const half8* src = reinterpret_cast<const half8*>(p.sketch_mfma);
         for (int i = threadIdx.x; i < SKN; i += blockDim.x) s_sk[i] = src[i];
     }
     if (threadIdx.x < 16) s_lvl[threadIdx.x] = threadIdx.x < 2 * KH ? p.levels[threadIdx.x] * ESCALE : 0.0f;
-    for (int i = threadIdx.x; i < NKB * 64; i += blockDim.x) {
+    for (int i = threadIdx.x; i < (NOROT ? 0 : NKB * 64); i += blockDim.x) {
         const int kb = i >> 6, row = i & 31, hh = (i >> 5) & 1;
         uint32_t w[4];
 #pragma unroll
@@ -233,7 +245,7 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
             w[q] = pair;
         }
         s_had[i] = make_uint4(w[0], w[1], w[2], w[3]);
-        if constexpr (NEG_LDS)
+        if constexpr (NEG_LDS && !NOROT)
             s_had[NKB * 64 + i] = make_uint4(w[0] ^ 0x80008000u, w[1] ^ 0x80008000u, w[2] ^ 0x80008000u, w[3] ^ 0x80008000u);
     }
     __syncthreads();
@@ -243,7 +255,7 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
     const int h = lane >> 5;
     // -A of input step kb (ap = +A)
     auto neg_operand = [&](const uint4& ap, int kb, int ln) -> uint4 {
-        if constexpr (NEG_LDS) return s_had[NKB * 64 + kb * 64 + ln];
+        if constexpr (NEG_LDS && !NOROT) return s_had[NKB * 64 + kb * 64 + ln];
         return make_uint4(ap.x ^ 0x80008000u, ap.y ^ 0x80008000u, ap.z ^ 0x80008000u, ap.w ^ 0x80008000u);
     };
 
@@ -293,7 +305,7 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
     };
     // RoPE keys run at two waves per SIMD whatever their register count, so
     // their next tile's bf16 inputs are loaded while this tile is quantised
-    constexpr bool PREFETCH = ROPE && BF16 && D == 128;
+    constexpr bool PREFETCH = ROPE && BF16 && D == 128 && !NOROT;
     uint4 nxt[PREFETCH ? NKB : 1];
     if constexpr (PREFETCH) {
         const int64_t t0 = base + (threadIdx.x >> 6);
@@ -321,6 +333,74 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
         const int token = tb * 32 + v;
         const bool valid = token < p.n_tok;
 
+        floatx16 acc[NOB];
+        float nu, scale;
+        if constexpr (NOROT) {
+            // register r of block ob holds coordinate 32 ob + 8 (r/4) + 4 h + r%4
+            // (the layout the Hadamard MFMAs leave): four contiguous inputs per
+            // (ob, r/4), loaded as they are
+            float xs[NOB][16];
+            const int64_t off = input_offset(tile);
+#pragma unroll
+            for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int c0 = 32 * ob + 8 * g + 4 * h;
+                    if constexpr (BF16) {
+                        const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.x) + off + c0);
+                        xs[ob][4 * g] = bf16_lo(w.x);
+                        xs[ob][4 * g + 1] = bf16_hi(w.x);
+                        xs[ob][4 * g + 2] = bf16_lo(w.y);
+                        xs[ob][4 * g + 3] = bf16_hi(w.y);
+                    } else {
+                        const f32x4 w = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.x) + off + c0);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) xs[ob][4 * g + j] = w[j];
+                    }
+                }
+            float ss = 0.0f;
+#pragma unroll
+            for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) ss = fmaf(xs[ob][r], xs[ob][r], ss);
+            {
+                const Swap sw = swap32(ss);
+                ss = sw.r0 + sw.r1;
+            }
+            nu = sqrtf(ss);
+            scale = nu > 0.0f ? ESCALE / nu : 0.0f;
+            // y = 2^8 RoPE(x) / nu; + 0 turns a -0 into +0, whose code is that of 0
+            if constexpr (ROPE) {
+                // pair (i, i + D/2) is blocks ob and ob + NOB/2 at the same register
+#pragma unroll
+                for (int ob = 0; ob < NOB / 2; ++ob)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int c0 = 32 * ob + 8 * g + 4 * h;
+                        f32x4 cc, sn;
+                        if (stage) {
+                            cc = s_rope4[(v * RS + c0) / 4];
+                            sn = s_rope4[((32 + v) * RS + c0) / 4];
+                        } else {
+                            const int64_t ro = (int64_t)(p.tok_offset + (valid ? token : 0)) * HALF + c0;
+                            cc = *reinterpret_cast<const f32x4*>(p.rope_cos + ro);
+                            sn = *reinterpret_cast<const f32x4*>(p.rope_sin + ro);
+                        }
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const float cs = cc[j] * scale, sv = sn[j] * scale;
+                            const float lo = xs[ob][4 * g + j], hi = xs[ob + NOB / 2][4 * g + j];
+                            acc[ob][4 * g + j] = fmaf(lo, cs, -(hi * sv)) + 0.0f;
+                            acc[ob + NOB / 2][4 * g + j] = fmaf(hi, cs, lo * sv) + 0.0f;
+                        }
+                    }
+            } else {
+#pragma unroll
+                for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[ob][r] = fmaf(xs[ob][r], scale, 0.0f);
+            }
+        } else {
         // B operands: input step kb is coordinates 16kb + 8h + t (t = 0..7)
         // of this lane's vector
         uint4 raw[BF16 ? NKB : 1];
@@ -368,15 +448,14 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
             const Swap sw = swap32(ss);
             ss = sw.r0 + sw.r1;
         }
-        const float nu = sqrtf(ss);
+        nu = sqrtf(ss);
         // maps H(sigma * x) to 2^8 * Pi (x / nu)
-        const float scale = nu > 0.0f ? yscale / nu : 0.0f;
+        scale = nu > 0.0f ? yscale / nu : 0.0f;
 
         // Walsh-Hadamard transform as MFMAs: H_D = H_{D/32} (x) H32, so output
         // block ob takes input step kb with the sign H_{D/32}[ob][kb/2].
         // Output block ob, register r of this lane = coordinate
         // 32 ob + 8 (r/4) + 4 h + r%4.
-        floatx16 acc[NOB];
 #pragma unroll
         for (int ob = 0; ob < NOB; ++ob)
 #pragma unroll
@@ -469,6 +548,7 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+        }  // rotation
         __builtin_amdgcn_sched_barrier(0);
         if (prefetch) rope_stage_load<HALF, NQ>(p, base + blk_stride, st_table, st_row, st_c4, pre);
         if constexpr (PREFETCH) {
@@ -488,11 +568,16 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
 #pragma unroll
         for (int w = 0; w < CW; ++w) cw[w] = 0u;
         float gg = 0.0f;
-        floatx16 sacc[NRB > 0 ? NRB : 1];
+        floatx16 sacc[SKETCH ? NRB : 1];
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb)
+        for (int rb = 0; rb < (SKETCH ? NRB : 0); ++rb)
 #pragma unroll
             for (int q = 0; q < 16; ++q) sacc[rb][q] = 0.0f;
+        // sign correction: per block, the negative-residual flags of the lane's
+        // coordinates, byte a = coordinates 8a + 4h + 0..3 in bits 0..3
+        uint32_t wsg[SGN ? NOB : 1];
+#pragma unroll
+        for (int ob = 0; ob < (SGN ? NOB : 1); ++ob) wsg[ob] = 0u;
 #pragma unroll
         for (int pc = 0; pc < NP; ++pc) {
             const int ob = pc >> 1, hf = pc & 1;
@@ -513,7 +598,7 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
 #pragma unroll
                 for (int t = 0; t < 8; ++t) {
                     e[t] = yv[t] - __builtin_copysignf(s_lvl[xu[t]], yv[t]);
-                    gg = fmaf(e[t], e[t], gg);
+                    if constexpr (!SGN) gg = fmaf(e[t], e[t], gg);
                 }
 #pragma unroll
                 for (int g = 0; g < 2; ++g) {
@@ -544,11 +629,26 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
                     // + 0: a zero vector's -0 coordinates count as +0 (code of y = 0)
                     const float y = EXACT ? fmaf(acc[ob][8 * hf + t], scale, 0.0f) : acc[ob][8 * hf + t];
                     const uint32_t code = quantise<BITS>(y, pt, pl, &e[t]);
-                    gg = fmaf(e[t], e[t], gg);
+                    if constexpr (!SGN) gg = fmaf(e[t], e[t], gg);
                     dev::code_put(cw, dev::code_loc(32 * ob + 8 * (2 * hf + (t >> 2)) + (t & 3), BITS), BITS, code);
                 }
             }
-            if constexpr (M > 0) {
+            if constexpr (SGN) {
+                // the four flags of group g as bytes 0xFF / 0x00 (v_perm sign
+                // selects), one bit kept per byte, summed into byte 3 by a
+                // multiply and moved to byte a = 2 hf + g of the block's word
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    const int a = 2 * hf + g;
+                    const uint32_t f0 = __float_as_uint(e[4 * g]), f1 = __float_as_uint(e[4 * g + 1]);
+                    const uint32_t f2 = __float_as_uint(e[4 * g + 2]), f3 = __float_as_uint(e[4 * g + 3]);
+                    const uint32_t sb = (__builtin_amdgcn_perm(f1, f0, 0x0C0C0B09u) | __builtin_amdgcn_perm(f3, f2, 0x0B090C0Cu)) &
+                                        0x08040201u;
+                    wsg[ob] = __builtin_amdgcn_perm(sb * 0x01010101u, wsg[ob],
+                                                    (0x03020100u & ~(0xFFu << (8 * a))) | (0x07u << (8 * a)));
+                }
+            }
+            if constexpr (SKETCH) {
                 half8 ehi, elo;
                 split_f16(e, ehi, elo);
 #pragma unroll
@@ -614,10 +714,22 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
 #pragma unroll
             for (int k = 0; k < CW / 2; ++k) dst[k] = cw[k];
             if (h == 0) p.norm[n] = nu;
-            else if (M > 0) p.rnorm[n] = gamma;
+            else if (SKETCH) p.rnorm[n] = gamma;
         }
 
-        if constexpr (M > 0) {
+        if constexpr (SGN) {
+            // a set flag is a negative residual: complement, place lane half
+            // 1's nibbles 4 bits up, merge the pair; lane half h stores the
+            // blocks of its parity
+#pragma unroll
+            for (int ob = 0; ob < NOB; ++ob) {
+                uint32_t wb = (~wsg[ob] & 0x0F0F0F0Fu) << (4 * h);
+                const Swap sw = swap32(__uint_as_float(wb));
+                wb = __float_as_uint(sw.r0) | __float_as_uint(sw.r1);
+                if (valid && (ob & 1) == h) p.signs[n * NOB + ob] = wb;
+            }
+        }
+        if constexpr (SKETCH) {
             // D[i][j]: j = lane % 32 (vector), i = 8*(r/4) + 4*(lane/32) + r%4 (sketch row)
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb) {
@@ -802,34 +914,42 @@ int64_t dense_chunk(int64_t nvec) { return nvec < 65536 ? nvec : 65536; }
 
 using EncFn = void (*)(EncK);
 
-template <int D, int BITS, int M>
+template <int D, int BITS, int M, int MODE>
 EncFn pick_dtype(bool bf16, bool rope) {
-    if (rope) return bf16 ? encode_had_kernel<D, BITS, M, true, true> : encode_had_kernel<D, BITS, M, false, true>;
-    return bf16 ? encode_had_kernel<D, BITS, M, true, false> : encode_had_kernel<D, BITS, M, false, false>;
+    if (rope) return bf16 ? encode_had_kernel<D, BITS, M, true, true, MODE> : encode_had_kernel<D, BITS, M, false, true, MODE>;
+    return bf16 ? encode_had_kernel<D, BITS, M, true, false, MODE> : encode_had_kernel<D, BITS, M, false, false, MODE>;
 }
 
 template <int D, int BITS>
-EncFn pick_m(int m, bool bf16, bool rope) {
-    if (m == 0) return pick_dtype<D, BITS, 0>(bf16, rope);
-    if (m == D / 2) return pick_dtype<D, BITS, D / 2>(bf16, rope);
-    if (m == D) return pick_dtype<D, BITS, D>(bf16, rope);
+EncFn pick_m(int m, bool bf16, bool rope, int mode) {
+    if (mode != 0) {
+        if constexpr (BITS <= 3) {
+            if (m != D) return nullptr;
+            return mode == 1 ? pick_dtype<D, BITS, D, 1>(bf16, rope) : pick_dtype<D, BITS, D, 2>(bf16, rope);
+        }
+        return nullptr;
+    }
+    if (m == 0) return pick_dtype<D, BITS, 0, 0>(bf16, rope);
+    if (m == D / 2) return pick_dtype<D, BITS, D / 2, 0>(bf16, rope);
+    if (m == D) return pick_dtype<D, BITS, D, 0>(bf16, rope);
     return nullptr;
 }
 
 template <int D>
-EncFn pick_bits(int bits, int m, bool bf16, bool rope) {
+EncFn pick_bits(int bits, int m, bool bf16, bool rope, int mode) {
     switch (bits) {
-        case 1: return pick_m<D, 1>(m, bf16, rope);
-        case 2: return pick_m<D, 2>(m, bf16, rope);
-        case 3: return pick_m<D, 3>(m, bf16, rope);
-        case 4: return pick_m<D, 4>(m, bf16, rope);
+        case 1: return pick_m<D, 1>(m, bf16, rope, mode);
+        case 2: return pick_m<D, 2>(m, bf16, rope, mode);
+        case 3: return pick_m<D, 3>(m, bf16, rope, mode);
+        case 4: return pick_m<D, 4>(m, bf16, rope, mode);
     }
     return nullptr;
 }
 
-EncFn pick_encode(int d, int bits, int m, bool bf16, bool rope) {
-    if (d == 64) return pick_bits<64>(bits, m, bf16, rope);
-    if (d == 128) return pick_bits<128>(bits, m, bf16, rope);
+// mode: 0 QJL sketch, 1 sign correction, 2 sign correction without rotation
+EncFn pick_encode(int d, int bits, int m, bool bf16, bool rope, int mode) {
+    if (d == 64) return pick_bits<64>(bits, m, bf16, rope, mode);
+    if (d == 128) return pick_bits<128>(bits, m, bf16, rope, mode);
     return nullptr;
 }
 
@@ -869,7 +989,8 @@ hipError_t launch_encode(const tq_codebook* cb, const EncodeArgs& a, hipStream_t
         g_num_cus = prop.multiProcessorCount;
     }
     if (!cb->dense) {
-        EncFn fn = pick_encode(d, bits, m, a.bf16 != 0, a.rope_cos != nullptr);
+        const int mode = cb->spec.correction == TQ_CORR_SIGN ? (cb->spec.rotation == TQ_ROT_NONE ? 2 : 1) : 0;
+        EncFn fn = pick_encode(d, bits, m, a.bf16 != 0, a.rope_cos != nullptr, mode);
         if (!fn) return hipErrorInvalidValue;
         EncK p{};
         p.x = a.x;

@@ -41,11 +41,21 @@ tq_status check_spec(const tq_spec& s, bool* dense) {
     if (s.d < 3 || s.d > 4096) return fail(TQ_EINVAL, "d must be 3..4096");
     if ((s.bits * s.d) % 32) return fail(TQ_EINVAL, "bits*d must be a multiple of 32");
     if (s.m < 0 || s.m > 4096 || (s.m % 32)) return fail(TQ_EINVAL, "m must be 0 or a multiple of 32 up to 4096");
+    if (s.correction != TQ_CORR_QJL && s.correction != TQ_CORR_SIGN) return fail(TQ_EINVAL, "unknown correction");
+    if (s.reserved != 0) return fail(TQ_EINVAL, "reserved must be 0");
     bool dn;
     if (s.rotation == TQ_ROT_AUTO) dn = !is_pow2(s.d);
-    else if (s.rotation == TQ_ROT_HADAMARD) dn = false;
+    else if (s.rotation == TQ_ROT_HADAMARD || s.rotation == TQ_ROT_NONE) dn = false;
     else if (s.rotation == TQ_ROT_DENSE) dn = true;
     else return fail(TQ_EINVAL, "unknown rotation");
+    if (s.rotation == TQ_ROT_NONE && s.correction != TQ_CORR_SIGN)
+        return fail(TQ_EUNSUPPORTED, "rotation none is served with the sign correction only");
+    if (s.correction == TQ_CORR_SIGN) {
+        if (s.m != s.d) return fail(TQ_EINVAL, "the sign correction keeps one bit per coordinate: m must equal d");
+        if (dn || (s.d != 64 && s.d != 128))
+            return fail(TQ_EUNSUPPORTED, "the sign correction has kernels for d = 64 and 128, Hadamard or no rotation");
+        if (s.bits > 3) return fail(TQ_EUNSUPPORTED, "the sign correction has kernels for bits 1..3");
+    }
     if (!dn) {
         if (!is_pow2(s.d)) return fail(TQ_EINVAL, "Hadamard rotation needs a power-of-two d");
         if (s.d != 64 && s.d != 128) return fail(TQ_EUNSUPPORTED, "Hadamard kernels exist for d = 64 and 128");
@@ -161,6 +171,29 @@ void lloyd_max_table(int d, int bits, std::vector<double>* levels, std::vector<d
     for (int j = 0; j + 1 < K; ++j) tau[j] = 0.5 * (t[j] + t[j + 1]);
     *levels = t;
     *thr = tau;
+}
+
+// E|Y - t[c(Y)]| under the same density (the sign correction's mean residual
+// magnitude when no calibration is given): per cell, the integrals of
+// (t - y) f below the level and (y - t) f above it, from the cell's mass and
+// first moment in theta, over the total mass.
+double beta_mean_abs_error(int d, const std::vector<float>& levels, const std::vector<float>& thr) {
+    static const GaussLegendre gl(24);
+    const int K = (int)levels.size();
+    auto th = [](double y) { return std::asin(std::max(-1.0, std::min(1.0, y))); };
+    double mass = 0.0, acc = 0.0;
+    for (int j = 0; j < K; ++j) {
+        const double lo = j == 0 ? -1.0 : (double)thr[j - 1];
+        const double hi = j + 1 < K ? (double)thr[j] : 1.0;
+        const double t = levels[j];
+        const double tm = std::min(std::max(t, lo), hi);
+        double m1, s1, m2, s2;
+        cell_integrals(gl, d, th(lo), th(tm), &m1, &s1);
+        cell_integrals(gl, d, th(tm), th(hi), &m2, &s2);
+        acc += (t * m1 - s1) + (s2 - t * m2);
+        mass += m1 + m2;
+    }
+    return acc / mass;
 }
 
 // ------------------------------------------------------------------------
@@ -345,6 +378,8 @@ static tq_status build_tables(const tq_spec& s, const tq_draws* dr, bool dense,
         std::vector<double> q;
         haar_from_gaussians(s.d, gp, &q);
         rot->assign(q.begin(), q.end());
+    } else if (s.rotation == TQ_ROT_NONE) {
+        rot->assign(d, 1.0f);  // no rotation: the kernels read no sigma
     } else {
         std::vector<int8_t> sg(d);
         if (dr && dr->sigma) {
@@ -360,7 +395,12 @@ static tq_status build_tables(const tq_spec& s, const tq_draws* dr, bool dense,
     }
     const size_t md = (size_t)s.m * d;
     sk->resize(md);
-    if (md) {
+    if (s.correction == TQ_CORR_SIGN) {
+        // S = I: the sign of each residual coordinate
+        if (dr && dr->sketch) return fail(TQ_EINVAL, "the sign correction takes no sketch draws");
+        std::fill(sk->begin(), sk->end(), 0.0f);
+        for (size_t i = 0; i < d; ++i) (*sk)[i * d + i] = 1.0f;
+    } else if (md) {
         if (dr && dr->sketch) {
             std::memcpy(sk->data(), dr->sketch, md * sizeof(float));
         } else {
@@ -415,27 +455,52 @@ tq_status tq_codebook_tables(const tq_spec* spec, const tq_draws* draws, float* 
     if (st) return st;
     if (levels) std::memcpy(levels, lv.data(), lv.size() * sizeof(float));
     if (thresholds) std::memcpy(thresholds, th.data(), th.size() * sizeof(float));
-    if (rotation) std::memcpy(rotation, rot.data(), rot.size() * sizeof(float));
+    if (rotation && spec->rotation != TQ_ROT_NONE) std::memcpy(rotation, rot.data(), rot.size() * sizeof(float));
     if (sketch && !sk.empty()) std::memcpy(sketch, sk.data(), sk.size() * sizeof(float));
     return TQ_OK;
 }
 
-tq_status tq_codebook_init(const tq_spec* spec, const tq_draws* draws, void* stream,
-                           tq_codebook** out) {
+}  // extern "C"
+
+static tq_status codebook_create(const tq_spec* spec, const tq_draws* draws, const float* levels,
+                                 const float* mu, int32_t n_mu, void* stream, tq_codebook** out) {
     if (!out) return fail(TQ_EINVAL, "null out");
     *out = nullptr;
     if (!spec) return fail(TQ_EINVAL, "null spec");
     bool dense;
     tq_status st = check_spec(*spec, &dense);
     if (st) return st;
+    const int K = 1 << spec->bits;
+    if (levels) {
+        // a calibrated table: strictly increasing, exactly symmetric
+        for (int j = 0; j < K; ++j) {
+            if (!std::isfinite(levels[j])) return fail(TQ_EINVAL, "levels must be finite");
+            if (j && !(levels[j] > levels[j - 1])) return fail(TQ_EINVAL, "levels must be strictly increasing");
+            if (levels[K - 1 - j] != -levels[j]) return fail(TQ_EINVAL, "levels must be symmetric about 0");
+        }
+    }
+    const bool sign = spec->correction == TQ_CORR_SIGN;
+    if (!sign && (mu || n_mu)) return fail(TQ_EINVAL, "mu is given only for the sign correction");
+    if (mu && n_mu < 1) return fail(TQ_EINVAL, "n_mu must be >= 1 when mu is given");
+    if (!mu && n_mu) return fail(TQ_EINVAL, "n_mu without mu");
+    for (int32_t i = 0; mu && i < n_mu; ++i)
+        if (!std::isfinite(mu[i]) || mu[i] < 0.0f) return fail(TQ_EINVAL, "mu must be finite and >= 0");
     tq_codebook* cb = new tq_codebook();
     cb->spec = *spec;
     cb->dense = dense;
-    cb->K = 1 << spec->bits;
+    cb->K = K;
     st = build_tables(*spec, draws, dense, &cb->levels, &cb->thresholds, &cb->rotation, &cb->sketch);
     if (st) {
         delete cb;
         return st;
+    }
+    if (levels) {
+        cb->levels.assign(levels, levels + K);
+        for (int j = 0; j + 1 < K; ++j) cb->thresholds[j] = (float)(0.5 * ((double)levels[j] + (double)levels[j + 1]));
+    }
+    if (sign) {
+        if (mu) cb->mu.assign(mu, mu + n_mu);
+        else cb->mu.assign(1, (float)beta_mean_abs_error(spec->d, cb->levels, cb->thresholds));
     }
     if (cb->K <= 8) level_digits(cb->levels, cb->lvl_digits, &cb->lvl_shift);
     const int d = spec->d, m = spec->m;
@@ -445,7 +510,7 @@ tq_status tq_codebook_init(const tq_spec* spec, const tq_draws* draws, void* str
     // entry [(rb*(d/16) + p)*2 + piece][lane][s] = part `piece` of
     // S[rb*32 + lane%32][c],  c = 32(p/2) + 8(2(p%2) + s/4) + 4(lane/32) + s%4
     std::vector<float> sk_mfma((size_t)m * d);
-    if (!dense && m) {
+    if (!dense && m && !sign) {
         const int np = d / 16;
         uint16_t* out = reinterpret_cast<uint16_t*>(sk_mfma.data());
         for (int rb = 0; rb < m / 32; ++rb)
@@ -461,11 +526,13 @@ tq_status tq_codebook_init(const tq_spec* spec, const tq_draws* draws, void* str
                         out[base + 64 * 8] = lo;
                     }
     }
-    // one device block: levels[16] | thresholds[16] | sigma[d] or rot[d*d] | sketch | sketch_mfma
+    // one device block: levels[16] | thresholds[16] | sigma[d] or rot[d*d] | sketch | sketch_mfma | mu
+    // (the sign correction's S = I is never read on the device)
     const size_t n_lv = 16, n_th = 16;
     const size_t n_rot = dense ? (size_t)d * d : (size_t)d;
-    const size_t n_sk = (size_t)m * d;
-    const size_t total = n_lv + n_th + n_rot + 2 * n_sk;
+    const size_t n_sk = sign ? 0 : (size_t)m * d;
+    const size_t n_mu_dev = cb->mu.size();
+    const size_t total = n_lv + n_th + n_rot + 2 * n_sk + n_mu_dev;
     std::vector<float> host(total, 0.0f);
     std::memcpy(host.data(), cb->levels.data(), cb->levels.size() * 4);
     std::memcpy(host.data() + n_lv, cb->thresholds.data(), cb->thresholds.size() * 4);
@@ -474,6 +541,7 @@ tq_status tq_codebook_init(const tq_spec* spec, const tq_draws* draws, void* str
         std::memcpy(host.data() + n_lv + n_th + n_rot, cb->sketch.data(), n_sk * 4);
         std::memcpy(host.data() + n_lv + n_th + n_rot + n_sk, sk_mfma.data(), n_sk * 4);
     }
+    if (n_mu_dev) std::memcpy(host.data() + n_lv + n_th + n_rot + 2 * n_sk, cb->mu.data(), n_mu_dev * 4);
     if (const char* f = std::getenv("TQ_TEST_FAIL_ALLOC"); f && std::atoi(f) == 1) {
         delete cb;
         return fail(TQ_ENOMEM, "allocation failure forced by TQ_TEST_FAIL_ALLOC");
@@ -499,6 +567,7 @@ tq_status tq_codebook_init(const tq_spec* spec, const tq_draws* draws, void* str
         cb->dev.sketch = base + n_lv + n_th + n_rot;
         cb->dev.sketch_mfma = base + n_lv + n_th + n_rot + n_sk;
     }
+    if (n_mu_dev) cb->dev.mu = base + n_lv + n_th + n_rot + 2 * n_sk;
     hipStream_t s = (hipStream_t)stream;
     e = hipMemcpyAsync(cb->block, host.data(), total * sizeof(float), hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);  // host staging buffer is local
@@ -508,6 +577,154 @@ tq_status tq_codebook_init(const tq_spec* spec, const tq_draws* draws, void* str
         return hip_fail(e, "uploading codebook tables");
     }
     *out = cb;
+    return TQ_OK;
+}
+
+extern "C" {
+
+tq_status tq_codebook_init(const tq_spec* spec, const tq_draws* draws, void* stream,
+                           tq_codebook** out) {
+    return codebook_create(spec, draws, nullptr, nullptr, 0, stream, out);
+}
+
+tq_status tq_codebook_init_calibrated(const tq_spec* spec, const tq_draws* draws, const float* levels,
+                                      const float* mu, int32_t n_mu, void* stream, tq_codebook** out) {
+    return codebook_create(spec, draws, levels, mu, n_mu, stream, out);
+}
+
+// Calibration (TurboESM summary, technical section 2: per-tensor tables and a
+// calibrated mean residual magnitude).  Rotated unit vectors in double; the
+// symmetric table's upper half is Lloyd's fixed point for |y|, computed on
+// the sorted values with prefix sums (a cell's mean is a difference of two
+// sums); mu per head with the float table, as the encoder decides codes.
+tq_status tq_calibrate(const tq_spec* spec, const tq_draws* draws, const float* x, int64_t n_tok,
+                       int32_t h, int32_t tok_offset, const float* rope_cos, const float* rope_sin,
+                       int32_t rope_npos, float* levels, float* mu) {
+    if (!spec || !x || !levels || !mu) return fail(TQ_EINVAL, "null argument");
+    bool dense;
+    tq_status st = check_spec(*spec, &dense);
+    if (st) return st;
+    if (dense) return fail(TQ_EUNSUPPORTED, "calibration is served for Hadamard and unrotated codebooks");
+    if (n_tok <= 0 || h <= 0 || tok_offset < 0) return fail(TQ_EINVAL, "bad calibration sizes");
+    if ((rope_cos == nullptr) != (rope_sin == nullptr)) return fail(TQ_EINVAL, "give both RoPE tables or neither");
+    if (rope_cos && (int64_t)rope_npos < (int64_t)tok_offset + n_tok)
+        return fail(TQ_EINVAL, "RoPE table shorter than the last position");
+    const int d = spec->d, half_d = d / 2, K = 1 << spec->bits, half = K / 2;
+    std::vector<float> sig(d, 1.0f);
+    if (spec->rotation != TQ_ROT_NONE) {
+        std::vector<int8_t> sg(d);
+        if (draws && draws->sigma) {
+            for (int i = 0; i < d; ++i) {
+                if (draws->sigma[i] != 1 && draws->sigma[i] != -1) return fail(TQ_EINVAL, "sigma entries must be +1 or -1");
+                sg[i] = draws->sigma[i];
+            }
+        } else {
+            splitmix_signs(spec->seed, d, sg.data());
+        }
+        for (int i = 0; i < d; ++i) sig[i] = (float)sg[i];
+    }
+    const int64_t nvec = n_tok * h;
+    std::vector<double> y((size_t)nvec * d);
+    std::vector<char> keep((size_t)nvec, 0);
+    std::vector<double> v(d);
+    const double inv_sqrt_d = 1.0 / std::sqrt((double)d);
+    for (int64_t t = 0; t < n_tok; ++t)
+        for (int j = 0; j < h; ++j) {
+            const int64_t n = t * h + j;
+            const float* xr = x + n * d;
+            for (int i = 0; i < d; ++i) v[i] = xr[i];
+            if (rope_cos) {
+                const int64_t pos = tok_offset + t;
+                for (int i = 0; i < half_d; ++i) {
+                    const double c = rope_cos[pos * half_d + i], sn = rope_sin[pos * half_d + i];
+                    const double lo = v[i], hi = v[i + half_d];
+                    v[i] = lo * c - hi * sn;
+                    v[i + half_d] = hi * c + lo * sn;
+                }
+            }
+            double ss = 0.0;
+            for (int i = 0; i < d; ++i) ss += v[i] * v[i];
+            const double nu = std::sqrt(ss);
+            if (!(nu > 0.0)) continue;
+            keep[n] = 1;
+            double* yr = y.data() + n * d;
+            for (int i = 0; i < d; ++i) yr[i] = v[i] / nu * sig[i];
+            if (spec->rotation != TQ_ROT_NONE) {
+                // Walsh-Hadamard butterflies (Sylvester order), then 1/sqrt(d)
+                for (int len = 1; len < d; len <<= 1)
+                    for (int i = 0; i < d; i += 2 * len)
+                        for (int k = i; k < i + len; ++k) {
+                            const double a = yr[k], b = yr[k + len];
+                            yr[k] = a + b;
+                            yr[k + len] = a - b;
+                        }
+                for (int i = 0; i < d; ++i) yr[i] *= inv_sqrt_d;
+            }
+        }
+    std::vector<double> a;
+    a.reserve((size_t)nvec * d);
+    for (int64_t n = 0; n < nvec; ++n)
+        if (keep[n])
+            for (int i = 0; i < d; ++i) a.push_back(std::fabs(y[(size_t)n * d + i]));
+    if (a.empty()) return fail(TQ_EINVAL, "no non-zero calibration vector");
+    std::sort(a.begin(), a.end());
+    const size_t N = a.size();
+    std::vector<long double> pre(N + 1, 0.0L);
+    for (size_t i = 0; i < N; ++i) pre[i + 1] = pre[i] + (long double)a[i];
+    std::vector<double> lv(half);
+    for (int j = 0; j < half; ++j) {
+        size_t idx = (size_t)std::floor((j + 0.5) * (double)N / half);
+        lv[j] = a[std::min(idx, N - 1)];
+    }
+    std::vector<size_t> cut(half + 1), prev;
+    bool settled = false;
+    for (int it = 0; it < 100000; ++it) {
+        cut[0] = 0;
+        cut[half] = N;
+        for (int j = 1; j < half; ++j) {
+            const double b = 0.5 * (lv[j - 1] + lv[j]);
+            cut[j] = (size_t)(std::lower_bound(a.begin(), a.end(), b) - a.begin());  // ties go up
+        }
+        for (int j = 0; j < half; ++j)
+            if (cut[j + 1] > cut[j]) lv[j] = (double)((pre[cut[j + 1]] - pre[cut[j]]) / (long double)(cut[j + 1] - cut[j]));
+        if (!prev.empty() && prev == cut) {
+            settled = true;
+            break;
+        }
+        prev = cut;
+    }
+    if (!settled) return fail(TQ_EINVAL, "calibration did not settle");
+    std::vector<float> t32(K), tau32(K - 1);
+    for (int j = 0; j < half; ++j) {
+        t32[half + j] = (float)lv[j];
+        t32[half - 1 - j] = -(float)lv[j];
+    }
+    for (int j = 0; j + 1 < K; ++j) tau32[j] = (float)(0.5 * ((double)t32[j] + (double)t32[j + 1]));
+    for (int j = 0; j < h; ++j) {
+        double sum = 0.0;
+        int64_t cnt = 0;
+        for (int64_t t = 0; t < n_tok; ++t) {
+            const int64_t n = t * h + j;
+            if (!keep[n]) continue;
+            for (int i = 0; i < d; ++i) {
+                const double yy = y[(size_t)n * d + i];
+                const float y32 = (float)yy;
+                int c = 0;
+                for (int k = 0; k + 1 < K; ++k) c += y32 >= tau32[k];
+                sum += std::fabs(yy - (double)t32[c]);
+                ++cnt;
+            }
+        }
+        mu[j] = cnt ? (float)(sum / (double)cnt) : 0.0f;
+    }
+    std::memcpy(levels, t32.data(), K * sizeof(float));
+    return TQ_OK;
+}
+
+tq_status tq_codebook_get_mu(const tq_codebook* cb, float* mu, int32_t* n_mu) {
+    if (!cb || !n_mu) return fail(TQ_EINVAL, "null argument");
+    *n_mu = (int32_t)cb->mu.size();
+    if (mu && !cb->mu.empty()) std::memcpy(mu, cb->mu.data(), cb->mu.size() * 4);
     return TQ_OK;
 }
 
@@ -530,7 +747,7 @@ tq_status tq_codebook_export(const tq_codebook* cb, float* levels, float* thresh
     if (!cb) return fail(TQ_EINVAL, "null codebook");
     if (levels) std::memcpy(levels, cb->levels.data(), cb->levels.size() * 4);
     if (thresholds) std::memcpy(thresholds, cb->thresholds.data(), cb->thresholds.size() * 4);
-    if (rotation) std::memcpy(rotation, cb->rotation.data(), cb->rotation.size() * 4);
+    if (rotation && !no_rotation(cb)) std::memcpy(rotation, cb->rotation.data(), cb->rotation.size() * 4);
     if (sketch && !cb->sketch.empty()) std::memcpy(sketch, cb->sketch.data(), cb->sketch.size() * 4);
     return TQ_OK;
 }
@@ -539,8 +756,8 @@ static tq_status check_packed(const tq_codebook* cb, const tq_packed* p, int64_t
                               const char* what) {
     if (!p) return fail(TQ_EINVAL, std::string("null packed planes: ") + what);
     if (!p->norm || !p->codes) return fail(TQ_EINVAL, std::string("null norm/codes plane: ") + what);
-    if (cb->spec.m && (!p->rnorm || !p->signs))
-        return fail(TQ_EINVAL, std::string("null rnorm/signs plane with m > 0: ") + what);
+    if (cb->spec.m && !p->signs) return fail(TQ_EINVAL, std::string("null signs plane with m > 0: ") + what);
+    if (has_rnorm(cb) && !p->rnorm) return fail(TQ_EINVAL, std::string("null rnorm plane with m > 0: ") + what);
     if (p->n < need) return fail(TQ_EINVAL, std::string("packed capacity too small: ") + what);
     return TQ_OK;
 }
@@ -610,6 +827,13 @@ tq_status tq_encode_kv(const tq_codebook* ck, const tq_codebook* cv, const void*
     return TQ_OK;
 }
 
+// a sign-corrected codebook has one mu per KV head of the call, or one shared
+static tq_status check_mu(const tq_codebook* cb, int32_t h_kv) {
+    if (sign_corr(cb) && cb->mu.size() != 1 && (int64_t)cb->mu.size() != h_kv)
+        return fail(TQ_EINVAL, "the codebook's mu count matches neither 1 nor h_kv");
+    return TQ_OK;
+}
+
 static tq_status check_attn(const tq_codebook* ck, const void* q, int32_t q_dtype, int32_t B,
                             int32_t Hq, int32_t h_kv, int32_t L_cap, const int32_t* seq_len,
                             const float* rope_cos, const float* rope_sin, int32_t rope_npos) {
@@ -635,6 +859,9 @@ tq_status tq_attn_logits(const tq_codebook* ck, const void* q, int32_t q_dtype, 
     if (!out || (top_k && !topk_idx)) return fail(TQ_EINVAL, "null output");
     st = check_packed(ck, k, (int64_t)B * h_kv * L_cap, "k");
     if (st) return st;
+    st = check_mu(ck, h_kv);
+    if (st) return st;
+    if (sign_corr(ck) && !logits_mfma_supported(ck)) return fail(TQ_EUNSUPPORTED, "no logit kernel for this codebook");
     if ((int64_t)B * Hq == 0 || (L_cap == 0 && top_k == 0)) return TQ_OK;
     const size_t need = logits_workspace_bytes(ck, B, Hq, h_kv, L_cap, top_k);
     if (ws_bytes < need || (need && !ws)) return fail(TQ_EINVAL, "workspace too small");
@@ -672,6 +899,12 @@ tq_status tq_attn_decode(const tq_codebook* ck, const tq_codebook* cv, const voi
     if (st) return st;
     st = check_packed(cv, v, (int64_t)B * h_kv * L_cap, "v");
     if (st) return st;
+    st = check_mu(ck, h_kv);
+    if (st) return st;
+    st = check_mu(cv, h_kv);
+    if (st) return st;
+    if ((sign_corr(ck) || sign_corr(cv)) && !decode_mfma_supported(ck, cv))
+        return fail(TQ_EUNSUPPORTED, "sign-corrected codebooks need key and value tables of equal d, bits and m");
     if ((int64_t)B * Hq == 0) return TQ_OK;
     const size_t need = decode_workspace_bytes(ck, cv, B, Hq, h_kv, L_cap);
     if (ws_bytes < need || (need && !ws)) return fail(TQ_EINVAL, "workspace too small");

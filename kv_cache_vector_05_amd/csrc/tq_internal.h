@@ -21,6 +21,7 @@ struct DeviceTables {
     float* rot = nullptr;         // [d*d]  dense Pi, row-major (y = Pi u)
     float* sketch = nullptr;      // [m*d]  S, row-major
     float* sketch_mfma = nullptr; // [m*d]  S as fp16 hi/lo pairs in the encode kernel's MFMA operand order
+    float* mu = nullptr;          // [n_mu] mean residual magnitudes (sign correction)
 };
 
 }  // namespace tq
@@ -31,6 +32,7 @@ struct tq_codebook {
     int K;
     int device;
     std::vector<float> levels, thresholds, rotation, sketch;  // host mirrors
+    std::vector<float> mu;  // sign correction: per KV head (or one shared), else empty
     void* block = nullptr;                                    // one device allocation
     tq::DeviceTables dev;
     // levels in 24-bit fixed point, t_k ~= T_k * 2^-lvl_shift, as three balanced
@@ -42,6 +44,31 @@ struct tq_codebook {
 
 namespace tq {
 
+inline bool sign_corr(const tq_codebook* cb) { return cb->spec.correction == TQ_CORR_SIGN; }
+inline bool no_rotation(const tq_codebook* cb) { return cb->spec.rotation == TQ_ROT_NONE; }
+// scale of the correction term: sqrt(pi/2)/m for the QJL sketch, 1 for the
+// sign correction (whose mu is applied per KV head)
+inline double corr_scale(const tq_codebook* cb) {
+    if (sign_corr(cb)) return 1.0;
+    return cb->spec.m ? 1.2533141373155003 / (double)cb->spec.m : 0.0;
+}
+// planes a record of this codebook carries
+inline bool has_rnorm(const tq_codebook* cb) { return cb->spec.m > 0 && !sign_corr(cb); }
+// mu of KV head kh on the device (sign correction), else nullptr; the
+// stride is 0 for one shared value
+struct MuRef {
+    const float* ptr = nullptr;
+    int stride = 0;
+};
+inline MuRef mu_ref(const tq_codebook* cb) {
+    MuRef r;
+    if (sign_corr(cb)) {
+        r.ptr = cb->dev.mu;
+        r.stride = cb->mu.size() > 1 ? 1 : 0;
+    }
+    return r;
+}
+
 // ---- error reporting (thread-local message, see tq_last_error) ----
 tq_status fail(tq_status code, const std::string& msg);
 tq_status hip_fail(hipError_t e, const char* what);
@@ -49,6 +76,7 @@ tq_status hip_fail(hipError_t e, const char* what);
 // ---- host math (tq_host.cpp) ----
 tq_status check_spec(const tq_spec& s, bool* dense);
 void lloyd_max_table(int d, int bits, std::vector<double>* levels, std::vector<double>* thr);
+double beta_mean_abs_error(int d, const std::vector<float>& levels, const std::vector<float>& thr);
 void splitmix_gaussians(uint64_t seed, int purpose, size_t n, double* out);
 void splitmix_signs(uint64_t seed, size_t n, int8_t* out);
 void haar_from_gaussians(int d, const double* g, std::vector<double>* q);  // row-major

@@ -2,7 +2,9 @@
 // (tambur post: logits straight from quantised keys; iaemfoco post, "TurboQuant:
 // Uma Nova Abordagem" and itstec post, "Por dentro do processo de compressao
 // KV": the unbiased one-bit QJL correction):
-//     logit = nu ( <q', t[c]> + sqrt(pi/2)/m * gamma * <s, z> ),  q' = Pi RoPE(q), s = S q'.
+//     logit = nu ( <q', t[c]> + sqrt(pi/2)/m * gamma * <s, z> ),  q' = Pi RoPE(q), s = S q',
+// or, with the sign correction (TurboESM summary, technical section 2),
+//     logit = nu ( <q', t[c]> + mu_head <q', z> )  (S = I, so s = q').
 //
 // Exact integer formulation.  Every float that enters a product is turned
 // into a fixed-point integer split into balanced int8 digits: q' and s once
@@ -78,6 +80,8 @@ __device__ __forceinline__ void digits4(long long X, int8_t d[4]) {
 struct QDig {
     const void* q;
     int32_t bf16, Hq, L_cap, m, sdw, ncs;
+    int32_t norot;    // Pi = I: q' = RoPE(q)
+    int32_t s_ident;  // S = I (sign correction): s = q'
     const int32_t* seq_len;
     const float* rope_cos;
     const float* rope_sin;
@@ -122,18 +126,20 @@ __global__ __launch_bounds__(256) void qprep_digits_kernel(QDig p) {
         }
         __syncthreads();
     }
-    if (t < D) xs[t] *= p.sigma[t];
-    __syncthreads();
-    for (int s = 1; s < D; s <<= 1) {
-        if (t < D / 2) {
-            const int i = (t / s) * 2 * s + (t % s);
-            const float a = xs[i], bb = xs[i + s];
-            xs[i] = a + bb;
-            xs[i + s] = a - bb;
-        }
+    if (!p.norot) {
+        if (t < D) xs[t] *= p.sigma[t];
         __syncthreads();
+        for (int s = 1; s < D; s <<= 1) {
+            if (t < D / 2) {
+                const int i = (t / s) * 2 * s + (t % s);
+                const float a = xs[i], bb = xs[i + s];
+                xs[i] = a + bb;
+                xs[i + s] = a - bb;
+            }
+            __syncthreads();
+        }
     }
-    const float inv = 1.0f / sqrtf((float)D);
+    const float inv = p.norot ? 1.0f : 1.0f / sqrtf((float)D);
     float qv = 0.f;
     if (t < D) {
         qv = xs[t] * inv;
@@ -143,8 +149,12 @@ __global__ __launch_bounds__(256) void qprep_digits_kernel(QDig p) {
     __syncthreads();
     float sval = 0.f;
     if (t < p.m) {
-        const float* row = p.sketch + (int64_t)t * D;
-        for (int i = 0; i < D; ++i) sval = fmaf(row[i], xs[i], sval);
+        if (p.s_ident) {
+            sval = xs[t];
+        } else {
+            const float* row = p.sketch + (int64_t)t * D;
+            for (int i = 0; i < D; ++i) sval = fmaf(row[i], xs[i], sval);
+        }
         sv[t] = sval;
         p.s[bh * p.m + t] = sval;
     }
@@ -204,6 +214,9 @@ struct LogM {
     int32_t col0;
     uint32_t tdig[8];
     int32_t lvl_shift;
+    double cq;           // scale of the correction term
+    const float* mu;     // sign correction: mu per KV head (stride mu_stride), else nullptr
+    int32_t mu_stride;
 };
 
 template <int D, int BITS, int NRT, int NCS>
@@ -223,7 +236,10 @@ __global__ __launch_bounds__(256) void logits_mfma_kernel(LogM p) {
     const int gq0 = grp * 4 * NRT;
 
     T tl;
-    tl.init(p.qd, p.sd, p.scale, p.sdw, p.m, rowbase, gq0, G, p.tdig, p.lvl_shift, lane);
+    tl.init(p.qd, p.sd, p.scale, p.sdw, p.cq, rowbase, gq0, G, p.tdig, p.lvl_shift, lane);
+    // correction weight: gamma per key (QJL sketch) or the KV head's mu
+    const bool g_per_key = p.mu == nullptr;
+    const float g_head = g_per_key ? 0.0f : p.mu[kh * p.mu_stride];
 
     const int sl = clamp_len2(p.seq_len, b, p.L_cap);
     const int kend = min(sl, p.k0 + p.klen);
@@ -258,12 +274,12 @@ __global__ __launch_bounds__(256) void logits_mfma_kernel(LogM p) {
             const int off = tile * 16;
             T::load(cptr + off * Q::CW, sptr + off * mw, per, lane, rs[slot]);
             nus[slot] = nptr[off];
-            gms[slot] = NCS > 0 ? gptr[off] : 0.0f;
+            gms[slot] = NCS > 0 ? (g_per_key ? gptr[off] : g_head) : 0.0f;
         } else {  // a partial last tile reads the record of its last valid key instead
             const int off = min(tile * 16, kend - 1 - kbeg - n);
             T::load(cptr + off * Q::CW, sptr + off * mw, per, lane, rs[slot]);
             nus[slot] = nptr[off];
-            gms[slot] = NCS > 0 ? gptr[off] : 0.0f;
+            gms[slot] = NCS > 0 ? (g_per_key ? gptr[off] : g_head) : 0.0f;
         }
     };
     auto store = [&](int tile, int slot, const double* lg) {
@@ -393,6 +409,8 @@ hipError_t launch_qdigits(const tq_codebook* ck, const AttnArgs& a, const QDigit
     p.rope_sin = a.rope_sin;
     p.sigma = ck->dev.sigma;
     p.sketch = ck->dev.sketch;
+    p.norot = no_rotation(ck) ? 1 : 0;
+    p.s_ident = sign_corr(ck) ? 1 : 0;
     p.qp = q.qp;
     p.s = q.s;
     p.qd = q.qd;
@@ -435,6 +453,10 @@ hipError_t launch_logits_mfma(const tq_codebook* ck, const tq_packed& k, const A
     p.col0 = col0;
     for (int i = 0; i < 8; ++i) p.tdig[i] = ck->lvl_digits[i];
     p.lvl_shift = ck->lvl_shift;
+    p.cq = corr_scale(ck);
+    const MuRef mr = mu_ref(ck);
+    p.mu = mr.ptr;
+    p.mu_stride = mr.stride;
     // Size the work per wave so that the whole grid is resident at once (one
     // round of workgroups, no partly idle last round).
     const int64_t gx = (int64_t)a.B * a.h_kv * ngroups;

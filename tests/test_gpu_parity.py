@@ -59,12 +59,12 @@ def check_logits_and_decode(ock, gck, ocv, gcv, encK, encV, q_f32, q_dev, B, Hq,
             n0 = (b * H + kh) * L
             ek = rows(encK, n0, n0 + L)
             gsl = slice(kh * G, (kh + 1) * G)
-            ref = estimator.logits(ock, qp[gsl], s[gsl], ek)[:, :pos]
+            ref = estimator.logits(ock, qp[gsl], s[gsl], ek, kh)[:, :pos]
             parity.assert_close(lg[b, gsl, :pos], ref, f"{label} logits b={b} kh={kh}")
             assert np.all(np.isnan(lg[b, gsl, pos:])), f"{label}: logits past seq_len were written"
             if do_decode:
                 ev = rows(encV, n0, n0 + L)
-                ref_o = estimator.attention(ock, ocv, qp[gsl], s[gsl], ek, ev, pos, 1.0 / math.sqrt(ock.d))
+                ref_o = estimator.attention(ock, ocv, qp[gsl], s[gsl], ek, ev, pos, 1.0 / math.sqrt(ock.d), kh)
                 parity.assert_close(out[b, gsl], ref_o, f"{label} decode b={b} kh={kh}")
 
 
