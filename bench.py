@@ -74,7 +74,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed warmup steps (default: as many as fill about 0.3 s, at least 3: the "
                          "GPU's clocks take some 100 ms of load to settle)")
-    ap.add_argument("--workload", default="llama8b", choices=["llama8b", "llama70b", "esm650m", "vsearch", "tiny"])
+    ap.add_argument("--workload", default="llama8b",
+                    choices=["llama8b", "llama70b", "esm650m", "vsearch", "llama8b-turboesm", "esm650m-turboesm",
+                             "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="keys in the oracle's sample (0: default)")
     return ap.parse_args()
@@ -106,19 +108,43 @@ def bf16_dev(torch, bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
 
 
+# ------------------------------------------------------------ TurboESM tables
+CALIB_TOKENS = 256  # calibration batch: the first tokens of the first sequence
+
+
+def turboesm_codebooks(tq, synth, d, bits, k_sample, v_sample, rope_host):
+    """Key codebook (Hadamard, RoPE'd calibration) and value codebook (no
+    rotation), each with its own calibrated table and one mu per KV head
+    (TurboESM-style records: codes, one residual sign per coordinate, nu)."""
+    lk, mk = tq.calibrate(d, bits, k_sample, rotation="hadamard", seed=synth.K_SEED, rope=rope_host)
+    lv, mv = tq.calibrate(d, bits, v_sample, rotation="none")
+    ck = tq.Codebook(d, bits, d, "hadamard", seed=synth.K_SEED, correction="sign", levels=lk, mu=mk)
+    cv = tq.Codebook(d, bits, d, "none", correction="sign", levels=lv, mu=mv)
+    return ck, cv
+
+
 # ------------------------------------------------------------ llama-shaped
-def setup_llama(torch, tq, synth, kind):
+def setup_llama(torch, tq, synth, kind, variant="qjl"):
     if kind == "llama8b":
         B, Hq, H, L, d, bits, m, rope_base = 8, 32, 8, 32768, 128, 3, 64, 5e5
     else:
         B, Hq, H, L, d, bits, m, rope_base = 1, 64, 8, 131072, 128, 3, 128, 0.0
+    if variant == "turboesm":
+        m = d
     K, V = synth.llama_kv_inputs(kind, seed=0, batch=B, ctx=L, hkv=H, d=d)
     Q = synth.llama_q_inputs(seed=100, batch=B, hq=Hq, d=d)
-    st = {"B": B, "Hq": Hq, "H": H, "L": L, "d": d, "bits": bits, "m": m, "rope_base": rope_base}
+    st = {"B": B, "Hq": Hq, "H": H, "L": L, "d": d, "bits": bits, "m": m, "rope_base": rope_base,
+          "variant": variant}
     st["K"], st["V"], st["Q"] = bf16_dev(torch, K), bf16_dev(torch, V), bf16_dev(torch, Q)
     st["host"] = (K, V, Q)
-    st["ck"] = tq.Codebook(d, bits, m, "hadamard", seed=synth.K_SEED)
-    st["cv"] = tq.Codebook(d, bits, m, "hadamard", seed=synth.V_SEED)
+    if variant == "turboesm":
+        rope_host = tq.rope_table(rope_base, d, L + 1, device=None) if rope_base else None
+        st["ck"], st["cv"] = turboesm_codebooks(tq, synth, d, bits,
+                                                synth.bf16_bits_to_f32(K[0, :CALIB_TOKENS]),
+                                                synth.bf16_bits_to_f32(V[0, :CALIB_TOKENS]), rope_host)
+    else:
+        st["ck"] = tq.Codebook(d, bits, m, "hadamard", seed=synth.K_SEED)
+        st["cv"] = tq.Codebook(d, bits, m, "hadamard", seed=synth.V_SEED)
     st["kp"] = tq.Packed(st["ck"], B * H * L)
     st["vp"] = tq.Packed(st["cv"], B * H * L)
     st["rope"] = tq.rope_table(rope_base, d, L + 1) if rope_base else None
@@ -146,7 +172,8 @@ def llama_report(st, timer, ms_step):
     B, Hq, H, L, d, bits, m = (st[k] for k in ("B", "Hq", "H", "L", "d", "bits", "m"))
     G = Hq // H
     keys = B * H * L
-    rec = 4 + (4 if m else 0) + bits * d // 8 + m // 8
+    sign = st["variant"] == "turboesm"
+    rec = 4 + (4 if m and not sign else 0) + bits * d // 8 + m // 8
     in_bytes = 2 * d  # bf16
     enc_ms, n_enc = timer.mean_ms("encode_k")
     encv_ms, _ = timer.mean_ms("encode_v")
@@ -170,9 +197,15 @@ def llama_report(st, timer, ms_step):
         "encode_tokens_per_s": B * L / ((enc_ms + encv_ms) * 1e-3),
         "encode_vectors_per_s": 2 * keys / ((enc_ms + encv_ms) * 1e-3),
     }
-    cfg = {"workload": f"{'Llama-3.1-8B' if L == 32768 else 'Llama-70B'}-shaped decode layer", "batch": B,
-           "q_heads": Hq, "kv_heads": H, "head_dim": d, "context": L, "bits": bits, "qjl_rows": m,
+    name = f"{'Llama-3.1-8B' if L == 32768 else 'Llama-70B'}-shaped decode layer"
+    cfg = {"workload": name + (", TurboESM-style records" if sign else ""), "batch": B,
+           "q_heads": Hq, "kv_heads": H, "head_dim": d, "context": L, "bits": bits,
            "input_dtype": "bf16", "rope_base": st["rope_base"], "record_bytes": rec}
+    if sign:
+        cfg.update({"residual_signs": "one per coordinate, mu per KV head", "key_table": "calibrated, rotated",
+                    "value_table": "calibrated, original coordinates", "calibration_tokens": CALIB_TOKENS})
+    else:
+        cfg["qjl_rows"] = m
     return keys / (ms_step * 1e-3), "keys/s", kern, dom, extra, cfg
 
 
@@ -186,11 +219,15 @@ def cpu_baseline_llama(st, sample_keys, budget_s=12.0):
     K, V, Q = st["host"]
     B, Hq, H, L, d, bits, m = (st[k] for k in ("B", "Hq", "H", "L", "d", "bits", "m"))
     G = Hq // H
-    t0 = time.perf_counter()
-    ock = codec.make_codebook(d, bits, m, False, seed=synth.K_SEED)
-    ocv = codec.make_codebook(d, bits, m, False, seed=synth.V_SEED)
-    t_setup = time.perf_counter() - t0
     rope = orope.rope_table(st["rope_base"], d, L + 1) if st["rope_base"] else None
+    t0 = time.perf_counter()
+    if st["variant"] == "turboesm":
+        ock, ocv = oracle_turboesm_codebooks(synth, d, bits, synth.bf16_bits_to_f32(K[0, :CALIB_TOKENS]),
+                                             synth.bf16_bits_to_f32(V[0, :CALIB_TOKENS]), rope)
+    else:
+        ock = codec.make_codebook(d, bits, m, False, seed=synth.K_SEED)
+        ocv = codec.make_codebook(d, bits, m, False, seed=synth.V_SEED)
+    t_setup = time.perf_counter() - t0
     done, pairs, dt = 0, 0, 0.0
     for b in range(B):
         for kh in range(H):
@@ -204,8 +241,8 @@ def cpu_baseline_llama(st, sample_keys, budget_s=12.0):
             ek = codec.encode(ock, kx, pos=np.arange(n), rope=rope)
             ev = codec.encode(ocv, vx)
             qp, s = estimator.prep_query(ock, q, n, rope)
-            estimator.logits(ock, qp, s, ek)
-            estimator.attention(ock, ocv, qp, s, ek, ev, n, 1 / math.sqrt(d))
+            estimator.logits(ock, qp, s, ek, kh)
+            estimator.attention(ock, ocv, qp, s, ek, ev, n, 1 / math.sqrt(d), kh)
             dt += time.perf_counter() - t1
             done += n
             pairs += 1
@@ -220,36 +257,102 @@ def cpu_baseline_llama(st, sample_keys, budget_s=12.0):
                       f"{dt:.1f} s on the host (codebook tables built once beforehand, {t_setup:.1f} s)"}
 
 
+def oracle_turboesm_codebooks(synth, d, bits, k_sample, v_sample, rope):
+    """The oracle's own calibration and sign-corrected codebooks for the same
+    samples (the CPU baseline times the oracle as it stands)."""
+    from oracle import calibration, codec, rotation
+    sigma = synth.codec_draws(d, 0, False, synth.K_SEED)[0]
+    lk, mk = calibration.calibrate(rotation.rht_matrix(sigma), bits, k_sample, rope=rope)
+    lv, mv = calibration.calibrate(np.eye(d), bits, v_sample)
+    return (codec.make_sign_codebook(d, bits, "hadamard", sigma=sigma, levels=lk, mu=mk),
+            codec.make_sign_codebook(d, bits, "none", levels=lv, mu=mv))
+
+
 # ------------------------------------------------------------ ESM-2 prefill
-def setup_esm(torch, tq, synth):
+def setup_esm(torch, tq, synth, variant="qjl"):
     S, T, H, d, layers, bits, m = 32, 1024, 20, 64, 33, 3, 64
-    tok = torch.from_numpy(synth.esm_tokens(0, S, T)).cuda()
-    Ks, Vs = [], []
+    tok_h = synth.esm_tokens(0, S, T)
+    tok = torch.from_numpy(tok_h).cuda()
+    Ks, Vs, cks, cvs = [], [], [], []
+    rope_host = tq.rope_table(1e4, d, T, device=None)
     for layer in range(layers):
         pk, pv = synth.esm_layer_tables(layer)
         Ks.append(torch.from_numpy(pk).cuda()[tok].view(S, T, H, d))
         Vs.append(torch.from_numpy(pv).cuda()[tok].view(S, T, H, d))
-    st = {"S": S, "T": T, "H": H, "d": d, "layers": layers, "bits": bits, "m": m, "K": Ks, "V": Vs}
-    st["ck"] = tq.Codebook(d, bits, m, "hadamard", seed=synth.K_SEED)
-    st["cv"] = tq.Codebook(d, bits, m, "hadamard", seed=synth.V_SEED)
-    st["kp"] = [tq.Packed(st["ck"], S * H * T) for _ in range(layers)]
-    st["vp"] = [tq.Packed(st["cv"], S * H * T) for _ in range(layers)]
+        if variant == "turboesm":
+            # per layer: key and value tables, mu per head, from the first tokens of sequence 0
+            ck, cv = turboesm_codebooks(tq, synth, d, bits, pk[tok_h[0, :CALIB_TOKENS]].reshape(-1, H, d),
+                                        pv[tok_h[0, :CALIB_TOKENS]].reshape(-1, H, d), rope_host)
+            cks.append(ck)
+            cvs.append(cv)
+    st = {"S": S, "T": T, "H": H, "d": d, "layers": layers, "bits": bits, "m": m, "K": Ks, "V": Vs,
+          "variant": variant, "tok": tok_h}
+    if variant != "turboesm":
+        ck = tq.Codebook(d, bits, m, "hadamard", seed=synth.K_SEED)
+        cv = tq.Codebook(d, bits, m, "hadamard", seed=synth.V_SEED)
+        cks, cvs = [ck] * layers, [cv] * layers
+    st["ck"], st["cv"] = cks, cvs
+    st["kp"] = [tq.Packed(cks[i], S * H * T) for i in range(layers)]
+    st["vp"] = [tq.Packed(cvs[i], S * H * T) for i in range(layers)]
     st["rope"] = tq.rope_table(1e4, d, T)
     return st
 
 
 def step_esm(st, tq, timer):
     for layer in range(st["layers"]):
-        timer.call("encode_k", lambda: tq.encode_kv(st["ck"], None, st["K"][layer], None, st["kp"][layer], None,
-                                                   L_cap=st["T"], rope=st["rope"]))
-        timer.call("encode_v", lambda: tq.encode_kv(None, st["cv"], None, st["V"][layer], None, st["vp"][layer],
-                                                   L_cap=st["T"]))
+        timer.call("encode_k", lambda: tq.encode_kv(st["ck"][layer], None, st["K"][layer], None, st["kp"][layer],
+                                                   None, L_cap=st["T"], rope=st["rope"]))
+        timer.call("encode_v", lambda: tq.encode_kv(None, st["cv"][layer], None, st["V"][layer], None,
+                                                   st["vp"][layer], L_cap=st["T"]))
+
+
+def cpu_baseline_esm(st, budget_s=12.0):
+    """The oracle on a bounded sample: layer 0's keys (RoPE) and values of
+    whole (sequence, head) pairs in order, until about budget_s seconds of
+    host time; reported as tokens/s of the whole 33-layer encode."""
+    import synth
+    from oracle import codec, rope as orope
+    S, T, H, d, layers, bits, m = (st[k] for k in ("S", "T", "H", "d", "layers", "bits", "m"))
+    pk, pv = synth.esm_layer_tables(0)
+    rope = orope.rope_table(1e4, d, T)
+    t0 = time.perf_counter()
+    if st["variant"] == "turboesm":
+        tok0 = st["tok"][0, :CALIB_TOKENS]
+        ock, ocv = oracle_turboesm_codebooks(synth, d, bits, pk[tok0].reshape(-1, H, d), pv[tok0].reshape(-1, H, d),
+                                             rope)
+    else:
+        ock = codec.make_codebook(d, bits, m, False, seed=synth.K_SEED)
+        ocv = codec.make_codebook(d, bits, m, False, seed=synth.V_SEED)
+    t_setup = time.perf_counter() - t0
+    done, dt = 0, 0.0
+    for s in range(S):
+        for h in range(H):
+            if dt >= budget_s:
+                break
+            kx = pk[st["tok"][s]].reshape(T, H, d)[:, h]
+            vx = pv[st["tok"][s]].reshape(T, H, d)[:, h]
+            t1 = time.perf_counter()
+            codec.encode(ock, kx, pos=np.arange(T), rope=rope)
+            codec.encode(ocv, vx)
+            dt += time.perf_counter() - t1
+            done += T
+    try:
+        import threadpoolctl
+        threads = max(p["num_threads"] for p in threadpoolctl.threadpool_info()) or 1
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    # `done` key+value vector pairs of one layer; a token needs layers * H of them
+    return {"value": done / dt / (layers * H), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} key+value vector pairs of layer 0 ({done // T} (sequence, head) pairs of {T} tokens) "
+                      f"encoded by the oracle in {dt:.1f} s on the host, scaled to tokens of the {layers}-layer, "
+                      f"{H}-head encode (codebook tables built once beforehand, {t_setup:.1f} s)"}
 
 
 def esm_report(st, timer, ms_step):
     S, T, H, d, layers, bits, m = (st[k] for k in ("S", "T", "H", "d", "layers", "bits", "m"))
     vec = S * T * H
-    rec = 4 + 4 + bits * d // 8 + m // 8
+    sign = st["variant"] == "turboesm"
+    rec = 4 + (0 if sign else 4) + bits * d // 8 + m // 8
     enc_ms, n = timer.mean_ms("encode_k")
     encv_ms, _ = timer.mean_ms("encode_v")
     kern = {"encode_k": {"ms": enc_ms, "launches": n, "alg_bytes": vec * (4 * d + rec), "units": vec},
@@ -257,10 +360,18 @@ def esm_report(st, timer, ms_step):
     for k in kern.values():
         k["GBps"] = k["alg_bytes"] / (k["ms"] * 1e-3) / 1e9
         k["hbm_frac"] = k["GBps"] / HBM_PEAK_GBS
-    extra = {"encode_tokens_per_s": S * T / (ms_step * 1e-3), "encode_vectors_per_s": 2 * layers * vec / (ms_step * 1e-3)}
-    cfg = {"workload": "ESM-2-650M-shaped prefill encode", "layers": layers, "heads": H, "head_dim": d,
-           "sequences": S, "length": T, "bits": bits, "qjl_rows": m, "input_dtype": "f32", "rope_base": 1e4,
-           "record_bytes": rec}
+    extra = {"encode_tokens_per_s": S * T / (ms_step * 1e-3), "encode_vectors_per_s": 2 * layers * vec / (ms_step * 1e-3),
+             "kv_bytes_fp32_per_sequence": 2 * layers * T * H * d * 4,
+             "kv_bytes_packed_per_sequence": 2 * layers * T * H * rec,
+             "kv_reduction_vs_fp32": (4 * d) / rec}
+    cfg = {"workload": "ESM-2-650M-shaped prefill encode" + (", TurboESM-style records" if sign else ""),
+           "layers": layers, "heads": H, "head_dim": d, "sequences": S, "length": T, "bits": bits,
+           "input_dtype": "f32", "rope_base": 1e4, "record_bytes": rec}
+    if sign:
+        cfg.update({"residual_signs": "one per coordinate, mu per head", "key_table": "calibrated per layer, rotated",
+                    "value_table": "calibrated per layer, original coordinates", "calibration_tokens": CALIB_TOKENS})
+    else:
+        cfg["qjl_rows"] = m
     return S * T / (ms_step * 1e-3), "tokens/s", kern, "encode_k", extra, cfg
 
 
@@ -325,11 +436,11 @@ def main():
     torch.cuda.set_device(0)
     wl = args.workload
     print(f"[bench] setting up {wl}", file=sys.stderr, flush=True)
-    if wl in ("llama8b", "llama70b"):
-        st = setup_llama(torch, tq, synth, wl)
+    if wl in ("llama8b", "llama70b", "llama8b-turboesm"):
+        st = setup_llama(torch, tq, synth, wl.split("-")[0], "turboesm" if wl.endswith("turboesm") else "qjl")
         step, report = (lambda t: step_llama(st, tq, t)), (lambda t, ms: llama_report(st, t, ms))
-    elif wl == "esm650m":
-        st = setup_esm(torch, tq, synth)
+    elif wl in ("esm650m", "esm650m-turboesm"):
+        st = setup_esm(torch, tq, synth, "turboesm" if wl.endswith("turboesm") else "qjl")
         step, report = (lambda t: step_esm(st, tq, t)), (lambda t, ms: esm_report(st, t, ms))
     elif wl == "vsearch":
         st = setup_vsearch(torch, tq, synth)
@@ -377,9 +488,12 @@ def main():
             "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "f32", "data": "synthetic", "config": cfg, "roofline": roof,
             "kernels": kern, **extra}
-    if not args.no_cpu_baseline and wl in ("llama8b", "llama70b"):
+    if not args.no_cpu_baseline and wl in ("llama8b", "llama70b", "llama8b-turboesm"):
         print("[bench] cpu baseline (oracle on a sample)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline_llama(st, args.cpu_sample or 1 << 22)
+    elif not args.no_cpu_baseline and wl in ("esm650m", "esm650m-turboesm"):
+        print("[bench] cpu baseline (oracle on a sample)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline_esm(st)
     print(json.dumps(line), flush=True)
     return 0
 
