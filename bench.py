@@ -83,25 +83,39 @@ def parse():
 
 
 class Timer:
-    """HIP events on the launch stream around individual API calls."""
+    """HIP events on the launch stream around individual API calls (events
+    created up front, so that recording them costs the host little)."""
 
-    def __init__(self, torch):
+    def __init__(self, torch, events=0):
         self.torch = torch
         self.spans = {}
+        self.stream = torch.cuda.current_stream()
+        self.pool = [torch.cuda.Event(enable_timing=True) for _ in range(2 * events)]
+        self.used = 0
+
+    def _event(self):
+        if self.used < len(self.pool):
+            self.used += 1
+            return self.pool[self.used - 1]
+        return self.torch.cuda.Event(enable_timing=True)
 
     def call(self, name, fn):
-        t = self.torch
-        s = t.cuda.Event(enable_timing=True)
-        e = t.cuda.Event(enable_timing=True)
-        stream = t.cuda.current_stream()
-        s.record(stream)
+        s, e = self._event(), self._event()
+        s.record(self.stream)
         fn()
-        e.record(stream)
+        e.record(self.stream)
         self.spans.setdefault(name, []).append((s, e))
 
     def mean_ms(self, name):
         v = [s.elapsed_time(e) for s, e in self.spans[name]]
         return float(np.mean(v)), len(v)
+
+
+class NoTimer:
+    """Warmup steps: the calls only."""
+
+    def call(self, name, fn):
+        fn()
 
 
 def bf16_dev(torch, bits):
@@ -155,17 +169,22 @@ def setup_llama(torch, tq, synth, kind, variant="qjl"):
                              dtype=torch.uint8, device="cuda")
     st["ws_d"] = torch.empty(max(1, tq.workspace_bytes(st["ck"], st["cv"], tq.TQ_OP_DECODE, B, Hq, H, L, 0)),
                              dtype=torch.uint8, device="cuda")
+    # every call of the step with its arguments marshalled once
+    st["calls"] = [
+        ("encode_k", tq.encode_kv(st["ck"], None, st["K"], None, st["kp"], None, L_cap=L, rope=st["rope"],
+                                  prepare=True)),
+        ("encode_v", tq.encode_kv(None, st["cv"], None, st["V"], None, st["vp"], L_cap=L, prepare=True)),
+        ("logits", tq.attn_logits(st["ck"], st["Q"], st["kp"], H, L, st["sl"], rope=st["rope"], out=st["logits"],
+                                  workspace=st["ws_l"], prepare=True)[0]),
+        ("decode", tq.attn_decode(st["ck"], st["cv"], st["Q"], st["kp"], st["vp"], H, L, st["sl"], rope=st["rope"],
+                                  out=st["out"], workspace=st["ws_d"], prepare=True)[0]),
+    ]
     return st
 
 
-def step_llama(st, tq, timer):
-    timer.call("encode_k", lambda: tq.encode_kv(st["ck"], None, st["K"], None, st["kp"], None, L_cap=st["L"],
-                                               rope=st["rope"]))
-    timer.call("encode_v", lambda: tq.encode_kv(None, st["cv"], None, st["V"], None, st["vp"], L_cap=st["L"]))
-    timer.call("logits", lambda: tq.attn_logits(st["ck"], st["Q"], st["kp"], st["H"], st["L"], st["sl"],
-                                                rope=st["rope"], out=st["logits"], workspace=st["ws_l"]))
-    timer.call("decode", lambda: tq.attn_decode(st["ck"], st["cv"], st["Q"], st["kp"], st["vp"], st["H"], st["L"],
-                                                st["sl"], rope=st["rope"], out=st["out"], workspace=st["ws_d"]))
+def run_calls(st, timer):
+    for name, launch in st["calls"]:
+        timer.call(name, launch)
 
 
 def llama_report(st, timer, ms_step):
@@ -295,15 +314,13 @@ def setup_esm(torch, tq, synth, variant="qjl"):
     st["kp"] = [tq.Packed(cks[i], S * H * T) for i in range(layers)]
     st["vp"] = [tq.Packed(cvs[i], S * H * T) for i in range(layers)]
     st["rope"] = tq.rope_table(1e4, d, T)
+    st["calls"] = []
+    for layer in range(layers):
+        st["calls"].append(("encode_k", tq.encode_kv(cks[layer], None, Ks[layer], None, st["kp"][layer], None,
+                                                     L_cap=T, rope=st["rope"], prepare=True)))
+        st["calls"].append(("encode_v", tq.encode_kv(None, cvs[layer], None, Vs[layer], None, st["vp"][layer],
+                                                     L_cap=T, prepare=True)))
     return st
-
-
-def step_esm(st, tq, timer):
-    for layer in range(st["layers"]):
-        timer.call("encode_k", lambda: tq.encode_kv(st["ck"][layer], None, st["K"][layer], None, st["kp"][layer],
-                                                   None, L_cap=st["T"], rope=st["rope"]))
-        timer.call("encode_v", lambda: tq.encode_kv(None, st["cv"][layer], None, st["V"][layer], None,
-                                                   st["vp"][layer], L_cap=st["T"]))
 
 
 def cpu_baseline_esm(st, budget_s=12.0):
@@ -392,14 +409,13 @@ def setup_vsearch(torch, tq, synth):
     st["ws_l"] = torch.empty(tq.workspace_bytes(st["ck"], None, tq.TQ_OP_LOGITS, 1, nq, 1, n, 10), dtype=torch.uint8,
                              device="cuda")
     st["sl"] = torch.tensor([n], dtype=torch.int32, device="cuda")
+    st["calls"] = [
+        ("encode_k", tq.encode_kv(st["ck"], None, st["X"], None, st["kp"], None, L_cap=n, workspace=st["ws_e"],
+                                  prepare=True)),
+        ("scan_topk", tq.attn_logits(st["ck"], st["Q"], st["kp"], 1, n, st["sl"], top_k=10, workspace=st["ws_l"],
+                                     prepare=True)[0]),
+    ]
     return st
-
-
-def step_vsearch(st, tq, timer):
-    timer.call("encode_k", lambda: tq.encode_kv(st["ck"], None, st["X"], None, st["kp"], None, L_cap=st["n"],
-                                               workspace=st["ws_e"]))
-    timer.call("scan_topk", lambda: tq.attn_logits(st["ck"], st["Q"], st["kp"], 1, st["n"], st["sl"], top_k=10,
-                                                   workspace=st["ws_l"]))
 
 
 def vsearch_report(st, timer, ms_step):
@@ -438,23 +454,24 @@ def main():
     print(f"[bench] setting up {wl}", file=sys.stderr, flush=True)
     if wl in ("llama8b", "llama70b", "llama8b-turboesm"):
         st = setup_llama(torch, tq, synth, wl.split("-")[0], "turboesm" if wl.endswith("turboesm") else "qjl")
-        step, report = (lambda t: step_llama(st, tq, t)), (lambda t, ms: llama_report(st, t, ms))
+        report = lambda t, ms: llama_report(st, t, ms)
     elif wl in ("esm650m", "esm650m-turboesm"):
         st = setup_esm(torch, tq, synth, "turboesm" if wl.endswith("turboesm") else "qjl")
-        step, report = (lambda t: step_esm(st, tq, t)), (lambda t, ms: esm_report(st, t, ms))
+        report = lambda t, ms: esm_report(st, t, ms)
     elif wl == "vsearch":
         st = setup_vsearch(torch, tq, synth)
-        step, report = (lambda t: step_vsearch(st, tq, t)), (lambda t, ms: vsearch_report(st, t, ms))
+        report = lambda t, ms: vsearch_report(st, t, ms)
     else:
         raise SystemExit("tiny is a parity case, not a benchmark workload")
+    step = lambda t: run_calls(st, t)
     torch.cuda.synchronize()
     if args.warmup is None:
         # enough steps to cover the clock ramp under load (~0.3 s), at least 3,
         # sized from the second step (the first carries one-time set-up)
-        step(Timer(torch))
+        step(NoTimer())
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        step(Timer(torch))
+        step(NoTimer())
         torch.cuda.synchronize()
         one = time.perf_counter() - t0
         args.warmup = max(3, min(2000, int(0.3 / max(one, 1e-6))))
@@ -463,9 +480,9 @@ def main():
         warm = args.warmup
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(warm):
-        step(Timer(torch))
+        step(NoTimer())
     torch.cuda.synchronize()
-    timer = Timer(torch)
+    timer = Timer(torch, events=args.steps * len(st["calls"]))
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()

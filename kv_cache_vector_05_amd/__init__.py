@@ -33,8 +33,8 @@ from ._lib import (TQError, TQ_F32, TQ_BF16, TQ_ROT_AUTO, TQ_ROT_HADAMARD, TQ_RO
                    TQ_CORR_QJL, TQ_CORR_SIGN, TQ_OP_ENCODE, TQ_OP_LOGITS, TQ_OP_DECODE, check, lib, tq_draws,
                    tq_packed, tq_spec)
 
-__all__ = ["Codebook", "Packed", "encode_kv", "attn_logits", "attn_decode", "rope_table", "codebook_tables",
-           "plane_words", "workspace_bytes", "calibrate", "TQError", "lib"]
+__all__ = ["Codebook", "Packed", "Launch", "encode_kv", "attn_logits", "attn_decode", "rope_table",
+           "codebook_tables", "plane_words", "workspace_bytes", "calibrate", "TQError", "lib"]
 
 _ROT = {"auto": TQ_ROT_AUTO, "hadamard": TQ_ROT_HADAMARD, "dense": TQ_ROT_DENSE, "none": TQ_ROT_NONE}
 _CORR = {"qjl": TQ_CORR_QJL, "sign": TQ_CORR_SIGN}
@@ -247,6 +247,30 @@ class Packed:
                 self.codes.cpu().numpy().view(np.uint32), self.signs.cpu().numpy().view(np.uint32))
 
 
+class Launch:
+    """One library call with its arguments marshalled once: calling it
+    enqueues the same work again (same buffers, sizes and stream).  Loops that
+    repeat a call (a layer's encode, a decode step) pay the Python-side
+    argument handling once instead of per launch."""
+
+    def __init__(self, fn, args, keep):
+        self._fn = fn
+        self._args = args
+        self._keep = keep  # host objects the pointers in args refer to
+
+    def __call__(self):
+        code = self._fn(*self._args)
+        if code != 0:
+            raise TQError(code, lib().tq_last_error().decode())
+
+
+def _run(fn, args, keep, prepare):
+    if prepare:
+        return Launch(fn, tuple(args), keep)
+    check(fn(*args))
+    return None
+
+
 def workspace_bytes(ck, cv, op, B, Hq=0, h_kv=1, L_cap=0, top_k=0):
     return int(lib().tq_workspace_bytes(ck.handle, cv.handle if cv else None, op, int(B), int(Hq), int(h_kv),
                                         int(L_cap), int(top_k)))
@@ -277,9 +301,12 @@ def _strides(t):
     return (C.c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2))
 
 
-def encode_kv(ck, cv, k, v, kout=None, vout=None, tok_offset=0, L_cap=None, rope=None, workspace=None):
+def encode_kv(ck, cv, k, v, kout=None, vout=None, tok_offset=0, L_cap=None, rope=None, workspace=None,
+              prepare=False):
     """Encode k and/or v ([n_seq, n_tok, h_kv, d], float32 or bfloat16) into
-    Packed planes at cache slots tok_offset.. of each (seq, head)."""
+    Packed planes at cache slots tok_offset.. of each (seq, head).  With
+    prepare=True nothing runs: a Launch that enqueues this call is returned
+    (the tensors must stay alive and in place)."""
     x = k if k is not None else v
     n_seq, n_tok, h_kv, _ = x.shape
     L_cap = n_tok + tok_offset if L_cap is None else int(L_cap)
@@ -293,17 +320,17 @@ def encode_kv(ck, cv, k, v, kout=None, vout=None, tok_offset=0, L_cap=None, rope
     npos = 0 if rope is None else int(cos.shape[0])
     kst = kout.struct() if kout is not None else None
     vst = vout.struct() if vout is not None else None
-    check(lib().tq_encode_kv(ck.handle if ck else None, cv.handle if cv else None, _ptr(k), _ptr(v), dt,
-                             n_seq, n_tok, h_kv, ks, vs, int(tok_offset), L_cap, _ptr(cos), _ptr(sin), npos,
-                             C.byref(kst) if kst is not None else None, C.byref(vst) if vst is not None else None,
-                             _ptr(ws), wsb, _stream()))
-    return kout, vout
+    args = [ck.handle if ck else None, cv.handle if cv else None, _ptr(k), _ptr(v), dt, n_seq, n_tok, h_kv, ks, vs,
+            int(tok_offset), L_cap, _ptr(cos), _ptr(sin), npos, C.byref(kst) if kst is not None else None,
+            C.byref(vst) if vst is not None else None, _ptr(ws), wsb, _stream()]
+    launch = _run(lib().tq_encode_kv, args, (kst, vst, ks, vs, ws), prepare)
+    return launch if prepare else (kout, vout)
 
 
-def attn_logits(ck, q, kp, h_kv, L_cap, seq_len, rope=None, top_k=0, out=None, workspace=None):
+def attn_logits(ck, q, kp, h_kv, L_cap, seq_len, rope=None, top_k=0, out=None, workspace=None, prepare=False):
     """Logits [B, Hq, L_cap] (top_k = 0) or (values, indices) [B, Hq, top_k]
     for queries q [B, Hq, d] against packed keys.  seq_len: int32 [B] on the
-    GPU."""
+    GPU.  prepare=True returns (Launch, outputs) without running."""
     torch = _torch()
     B, Hq, d = q.shape
     if not q.is_contiguous():
@@ -319,14 +346,17 @@ def attn_logits(ck, q, kp, h_kv, L_cap, seq_len, rope=None, top_k=0, out=None, w
     elif out is None:
         out = torch.zeros((B, Hq, L_cap), dtype=torch.float32, device=q.device)
     kst = kp.struct()
-    check(lib().tq_attn_logits(ck.handle, _ptr(q), _dtype_code(q), C.byref(kst), B, Hq, int(h_kv), int(L_cap),
-                               _ptr(seq_len), _ptr(cos), _ptr(sin), npos, int(top_k), _ptr(out), _ptr(idx),
-                               _ptr(ws), wsb, _stream()))
-    return (out, idx) if top_k else out
+    args = [ck.handle, _ptr(q), _dtype_code(q), C.byref(kst), B, Hq, int(h_kv), int(L_cap), _ptr(seq_len), _ptr(cos),
+            _ptr(sin), npos, int(top_k), _ptr(out), _ptr(idx), _ptr(ws), wsb, _stream()]
+    launch = _run(lib().tq_attn_logits, args, (kst, ws, out, idx), prepare)
+    res = (out, idx) if top_k else out
+    return (launch, res) if prepare else res
 
 
-def attn_decode(ck, cv, q, kp, vp, h_kv, L_cap, seq_len, rope=None, scale=0.0, out=None, workspace=None):
-    """Decode attention output [B, Hq, d] float32 over packed K and V."""
+def attn_decode(ck, cv, q, kp, vp, h_kv, L_cap, seq_len, rope=None, scale=0.0, out=None, workspace=None,
+                prepare=False):
+    """Decode attention output [B, Hq, d] float32 over packed K and V.
+    prepare=True returns (Launch, out) without running."""
     torch = _torch()
     B, Hq, d = q.shape
     if not q.is_contiguous():
@@ -338,7 +368,7 @@ def attn_decode(ck, cv, q, kp, vp, h_kv, L_cap, seq_len, rope=None, scale=0.0, o
     if out is None:
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
     kst, vst = kp.struct(), vp.struct()
-    check(lib().tq_attn_decode(ck.handle, cv.handle, _ptr(q), _dtype_code(q), C.byref(kst), C.byref(vst), B, Hq,
-                               int(h_kv), int(L_cap), _ptr(seq_len), _ptr(cos), _ptr(sin), npos, float(scale),
-                               _ptr(out), _ptr(ws), wsb, _stream()))
-    return out
+    args = [ck.handle, cv.handle, _ptr(q), _dtype_code(q), C.byref(kst), C.byref(vst), B, Hq, int(h_kv), int(L_cap),
+            _ptr(seq_len), _ptr(cos), _ptr(sin), npos, float(scale), _ptr(out), _ptr(ws), wsb, _stream()]
+    launch = _run(lib().tq_attn_decode, args, (kst, vst, ws, out), prepare)
+    return (launch, out) if prepare else out

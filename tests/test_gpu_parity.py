@@ -328,3 +328,34 @@ def test_api_rejects_bad_calls_on_gpu():
         tq.encode_kv(gck, None, torch.zeros((1, 64, 1, d), device="cuda"), None, kp, None, tok_offset=10, L_cap=64)
     # empty input is a no-op
     tq.encode_kv(gck, None, torch.zeros((1, 0, 1, d), device="cuda"), None, kp, None, L_cap=64)
+
+
+def test_prepared_launches_match_eager_calls():
+    """A Launch (arguments marshalled once) enqueues the same work as the
+    eager call, and can be replayed."""
+    d, H, Hq, L = 128, 2, 8, 700
+    gck = codebooks(d, 3, 64, False, 0)[1]
+    gcv = codebooks(d, 3, 64, False, 1)[1]
+    g = synth.rng(12)
+    K = torch.from_numpy(g.standard_normal((1, L, H, d)).astype(np.float32)).cuda()
+    V = torch.from_numpy(g.standard_normal((1, L, H, d)).astype(np.float32)).cuda()
+    Q = torch.from_numpy(g.standard_normal((1, Hq, d)).astype(np.float32)).cuda()
+    sl = torch.tensor([L - 3], dtype=torch.int32, device="cuda")
+    kp, vp = tq.Packed(gck, H * L), tq.Packed(gcv, H * L)
+    tq.encode_kv(gck, gcv, K, V, kp, vp, L_cap=L)
+    lg = tq.attn_logits(gck, Q, kp, H, L, sl)
+    out = tq.attn_decode(gck, gcv, Q, kp, vp, H, L, sl)
+    kp2, vp2 = tq.Packed(gck, H * L), tq.Packed(gcv, H * L)
+    enc = tq.encode_kv(gck, gcv, K, V, kp2, vp2, L_cap=L, prepare=True)
+    run_l, lg2 = tq.attn_logits(gck, Q, kp2, H, L, sl, prepare=True)
+    run_d, out2 = tq.attn_decode(gck, gcv, Q, kp2, vp2, H, L, sl, prepare=True)
+    torch.cuda.synchronize()
+    assert not kp2.norm.any()  # nothing ran yet
+    for _ in range(2):
+        enc()
+        run_l()
+        run_d()
+        torch.cuda.synchronize()
+        for a, b in [(kp.codes, kp2.codes), (kp.signs, kp2.signs), (kp.norm, kp2.norm), (vp.codes, vp2.codes),
+                     (lg[..., :L - 3], lg2[..., :L - 3]), (out, out2)]:
+            assert torch.equal(a, b)
