@@ -279,8 +279,8 @@ def cpu_baseline_llama(st, sample_keys, budget_s=12.0):
 def oracle_turboesm_codebooks(synth, d, bits, k_sample, v_sample, rope):
     """The oracle's own calibration and sign-corrected codebooks for the same
     samples (the CPU baseline times the oracle as it stands)."""
-    from oracle import calibration, codec, rotation
-    sigma = synth.codec_draws(d, 0, False, synth.K_SEED)[0]
+    from oracle import calibration, codec, rng, rotation
+    sigma = rng.signs(synth.K_SEED, d)  # the seeded signs the library derives from the same seed
     lk, mk = calibration.calibrate(rotation.rht_matrix(sigma), bits, k_sample, rope=rope)
     lv, mv = calibration.calibrate(np.eye(d), bits, v_sample)
     return (codec.make_sign_codebook(d, bits, "hadamard", sigma=sigma, levels=lk, mu=mk),

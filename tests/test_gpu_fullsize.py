@@ -49,16 +49,27 @@ def gpu_planes(packed):
     return norm, rnorm, codes, signs
 
 
-def check_llama(kind, n_enc=192, n_logit=1024, n_decode_heads=2):
-    st = bench.setup_llama(torch, tq, synth, kind)
-    bench.step_llama(st, tq, bench.Timer(torch))
+def pick(planes, idx):
+    """The planes' rows at idx (a record without an rnorm plane keeps it empty)."""
+    return tuple(p[idx] if len(p) else p for p in planes)
+
+
+def check_llama(kind, n_enc=192, n_logit=1024, n_decode_heads=2, variant="qjl"):
+    st = bench.setup_llama(torch, tq, synth, kind, variant)
+    bench.run_calls(st, bench.NoTimer())
     torch.cuda.synchronize()
     B, Hq, H, L, d, bits, m = (st[k] for k in ("B", "Hq", "H", "L", "d", "bits", "m"))
     G = Hq // H
     K, V, Q = st["host"]
-    ock = codec.make_codebook(d, bits, m, False, seed=synth.K_SEED)
-    ocv = codec.make_codebook(d, bits, m, False, seed=synth.V_SEED)
     rope_o = orope.rope_table(st["rope_base"], d, L + 1) if st["rope_base"] else None
+    if variant == "turboesm":
+        # the oracle's own calibration on the same batch
+        ock, ocv = bench.oracle_turboesm_codebooks(synth, d, bits,
+                                                   synth.bf16_bits_to_f32(K[0, :bench.CALIB_TOKENS]),
+                                                   synth.bf16_bits_to_f32(V[0, :bench.CALIB_TOKENS]), rope_o)
+    else:
+        ock = codec.make_codebook(d, bits, m, False, seed=synth.K_SEED)
+        ocv = codec.make_codebook(d, bits, m, False, seed=synth.V_SEED)
     kpl, vpl = gpu_planes(st["kp"]), gpu_planes(st["vp"])
     g = np.random.default_rng(1234)
 
@@ -71,8 +82,8 @@ def check_llama(kind, n_enc=192, n_logit=1024, n_decode_heads=2):
     vx = synth.bf16_bits_to_f32(V[b_s, t_s, kh_s])
     ek = codec.encode(ock, kx, pos=t_s, rope=rope_o)
     ev = codec.encode(ocv, vx)
-    parity.compare_encoded(ock, ek, tuple(p[n_s] for p in kpl), f"{kind} K (full size, sampled)")
-    parity.compare_encoded(ocv, ev, tuple(p[n_s] for p in vpl), f"{kind} V (full size, sampled)")
+    parity.compare_encoded(ock, ek, pick(kpl, n_s), f"{kind} K (full size, sampled)")
+    parity.compare_encoded(ocv, ev, pick(vpl, n_s), f"{kind} V (full size, sampled)")
 
     # logits: sampled (b, h, t) entries from the GPU's records, query at position L
     qf = synth.bf16_bits_to_f32(Q)
@@ -85,7 +96,8 @@ def check_llama(kind, n_enc=192, n_logit=1024, n_decode_heads=2):
     for i in range(n_logit):
         qp, s = prep[b_l[i]]
         n = (b_l[i] * H + h_l[i] // G) * L + t_l[i]
-        ref[i] = estimator.logits(ock, qp[h_l[i]:h_l[i] + 1], s[h_l[i]:h_l[i] + 1], records(kpl, [n]))[0, 0]
+        ref[i] = estimator.logits(ock, qp[h_l[i]:h_l[i] + 1], s[h_l[i]:h_l[i] + 1], records(kpl, [n]),
+                                  h_l[i] // G)[0, 0]
     parity.assert_close(lg[b_l, h_l, t_l], ref, f"{kind} logits (full size, sampled)")
 
     # decode: whole query groups of sampled KV heads
@@ -96,7 +108,7 @@ def check_llama(kind, n_enc=192, n_logit=1024, n_decode_heads=2):
         qp, s = prep[b]
         gs = slice(kh * G, (kh + 1) * G)
         ref_o = estimator.attention(ock, ocv, qp[gs], s[gs], records(kpl, idx), records(vpl, idx), L,
-                                    1.0 / math.sqrt(d))
+                                    1.0 / math.sqrt(d), kh)
         parity.assert_close(out[b, gs], ref_o, f"{kind} decode b={b} kh={kh} (full size)")
 
 
@@ -113,35 +125,49 @@ def test_llama70b_full_size():
 
 
 @pytest.mark.timeout(900)
-def test_esm650m_full_size():
-    """33 layers x 20 heads x 32 x 1024 tokens, d=64, RoPE 1e4, b=3 + m=64:
+def test_llama8b_turboesm_full_size():
+    """The Llama-3.1-8B-shaped layer with TurboESM-style records: calibrated
+    key (rotated) and value (unrotated) tables, one mu per KV head."""
+    check_llama("llama8b", variant="turboesm")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("variant", ["qjl", "turboesm"])
+def test_esm650m_full_size(variant):
+    """33 layers x 20 heads x 32 x 1024 tokens, d=64, RoPE 1e4, b=3 (+ m=64
+    sketch, or TurboESM-style records with per-layer calibrated tables):
     sampled vectors of the first and last layer."""
-    st = bench.setup_esm(torch, tq, synth)
-    bench.step_esm(st, tq, bench.Timer(torch))
+    st = bench.setup_esm(torch, tq, synth, variant)
+    bench.run_calls(st, bench.NoTimer())
     torch.cuda.synchronize()
     S, T, H, d, bits, m = (st[k] for k in ("S", "T", "H", "d", "bits", "m"))
-    ock = codec.make_codebook(d, bits, m, False, seed=synth.K_SEED)
-    ocv = codec.make_codebook(d, bits, m, False, seed=synth.V_SEED)
     rope_o = orope.rope_table(1e4, d, T)
     tok = synth.esm_tokens(0, S, T)
     g = np.random.default_rng(99)
     for layer in (0, st["layers"] - 1):
         pk, pv = synth.esm_layer_tables(layer)
+        if variant == "turboesm":
+            t0 = tok[0, :bench.CALIB_TOKENS]
+            ock, ocv = bench.oracle_turboesm_codebooks(synth, d, bits, pk[t0].reshape(-1, H, d),
+                                                       pv[t0].reshape(-1, H, d), rope_o)
+        else:
+            ock = codec.make_codebook(d, bits, m, False, seed=synth.K_SEED)
+            ocv = codec.make_codebook(d, bits, m, False, seed=synth.V_SEED)
         s_i, t_i, h_i = g.integers(0, S, 160), g.integers(0, T, 160), g.integers(0, H, 160)
         n_s = (s_i * H + h_i) * T + t_i
         kx = pk[tok[s_i, t_i]].reshape(-1, H, d)[np.arange(160), h_i]
         vx = pv[tok[s_i, t_i]].reshape(-1, H, d)[np.arange(160), h_i]
         ek = codec.encode(ock, kx, pos=t_i, rope=rope_o)
         ev = codec.encode(ocv, vx)
-        parity.compare_encoded(ock, ek, tuple(p[n_s] for p in gpu_planes(st["kp"][layer])), f"esm K layer {layer}")
-        parity.compare_encoded(ocv, ev, tuple(p[n_s] for p in gpu_planes(st["vp"][layer])), f"esm V layer {layer}")
+        parity.compare_encoded(ock, ek, pick(gpu_planes(st["kp"][layer]), n_s), f"esm K layer {layer}")
+        parity.compare_encoded(ocv, ev, pick(gpu_planes(st["vp"][layer]), n_s), f"esm V layer {layer}")
 
 
 @pytest.mark.timeout(1200)
 def test_vector_search_full_size():
     """10^6 x 1536 unit vectors, dense Haar, b=2 + m=1536, 1024 queries, top-10."""
     st = bench.setup_vsearch(torch, tq, synth)
-    bench.step_vsearch(st, tq, bench.Timer(torch))
+    bench.run_calls(st, bench.NoTimer())
     vals, idx = tq.attn_logits(st["ck"], st["Q"], st["kp"], 1, st["n"], st["sl"], top_k=10, workspace=st["ws_l"])
     torch.cuda.synchronize()
     n, d, bits, m = st["n"], st["d"], st["bits"], st["m"]
@@ -156,7 +182,7 @@ def test_vector_search_full_size():
     ra, rb = g.integers(0, 65536, 31), np.concatenate([g.integers(last0, n, 32), [n - 1]])
     rows_i = np.concatenate([ra, rb])
     X = np.concatenate([first[ra], last[rb - last0]])
-    parity.compare_encoded(ock, codec.encode(ock, X), tuple(p[rows_i] for p in planes), "vsearch index (sampled)")
+    parity.compare_encoded(ock, codec.encode(ock, X), pick(planes, rows_i), "vsearch index (sampled)")
     # top-10 of sampled queries
     others = g.choice(n, 20000, replace=False)
     for qi in g.choice(st["nq"], 6, replace=False):

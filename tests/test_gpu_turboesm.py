@@ -92,13 +92,17 @@ def test_sign_encoder_paths(d, bits, dtype, rope, rot, H):
 
 
 def _calibrated(d, bits, rot, seed, sample, rope_host=None, tok_offset=0):
-    """Tables and per-head mu from the library's calibration (host); the same
-    values feed the oracle codebook (the calibration itself is pinned against
-    the oracle in the CPU tests)."""
-    lv, mu = tq.calibrate(d, bits, sample, rotation=rot, seed=0,
-                          sigma=synth.codec_draws(d, 0, False, seed)[0] if rot == "hadamard" else None,
-                          tok_offset=tok_offset, rope=rope_host)
-    return sign_codebooks(d, bits, rot, seed, levels=lv, mu=mu)
+    """(oracle, GPU) codebooks, each calibrated on the same batch by its own
+    side: the oracle's calibration (oracle.calibration) and the library's
+    (tq_calibrate), which agree to a unit or two in the last place."""
+    sigma = synth.codec_draws(d, 0, False, seed)[0] if rot == "hadamard" else None
+    lv, mu = tq.calibrate(d, bits, sample, rotation=rot, seed=0, sigma=sigma, tok_offset=tok_offset,
+                          rope=rope_host)
+    pi = orot.rht_matrix(sigma) if rot == "hadamard" else np.eye(d)
+    olv, omu = ocal.calibrate(pi, bits, sample, tok_offset=tok_offset, rope=rope_host)
+    o = codec.make_sign_codebook(d, bits, rot, sigma=sigma, levels=olv, mu=omu)
+    g = tq.Codebook(d, bits, d, rot, sigma=sigma, correction="sign", levels=lv, mu=mu)
+    return o, g
 
 
 def test_llama8b_shaped_sign_logits_and_decode():
