@@ -149,6 +149,28 @@ typedef struct {
 } tq_packed;
 
 /*
+ * Paged records (FibQuant summary, section 1: fixed addresses, any token
+ * decodable by address arithmetic; TurboESM summary, technical section 5:
+ * autoregressive generation).  A sequence's cache slots are cut into pages
+ * of page_size slots; pages[b * max_pages + j] is the physical page that
+ * holds logical page j of sequence b, and physical page p holds every KV
+ * head's slots: the record of (b, head, slot t) is
+ *     n = (pages[b][t / page_size] * h_kv + head) * page_size + t % page_size.
+ *   pages      device int32 [B][max_pages], owned by the caller
+ *   page_size  a positive multiple of 64
+ *   max_pages  row length; max_pages * page_size < 2^31 (the logical capacity)
+ *   n_pages    physical pages; record planes hold n_pages * h_kv * page_size
+ *              records.  Entries outside [0, n_pages) are never dereferenced:
+ *              encodes skip such slots, scans read page 0 or n_pages - 1
+ *              instead (the caller keeps every entry below seq_len valid).
+ */
+typedef struct {
+    const int32_t* pages;
+    int32_t page_size, max_pages;
+    int64_t n_pages;
+} tq_pages;
+
+/*
  * tq_codebook_tables (host only, no GPU): computes the tables a codebook
  * holds, into caller host buffers (any may be NULL to skip):
  *   levels [K], thresholds [K-1]    float32 Lloyd-Max table for the density
@@ -265,6 +287,42 @@ tq_status tq_encode_kv(const tq_codebook* ck, const tq_codebook* cv, const void*
                        size_t ws_bytes, void* stream);
 
 /*
+ * tq_encode_kv_paged: as tq_encode_kv, into paged records: slot
+ * tok_offset + t of sequence s goes through the page table (tok_offset +
+ * n_tok <= max_pages * page_size).  Hadamard and unrotated codebooks only
+ * (TQ_EUNSUPPORTED for dense ones); no workspace.
+ */
+tq_status tq_encode_kv_paged(const tq_codebook* ck, const tq_codebook* cv, const void* k, const void* v,
+                             int32_t dtype, int32_t n_seq, int32_t n_tok, int32_t h_kv, const int64_t* k_stride,
+                             const int64_t* v_stride, int32_t tok_offset, const tq_pages* pages,
+                             const float* rope_cos, const float* rope_sin, int32_t rope_npos,
+                             const tq_packed* kout, const tq_packed* vout, void* stream);
+
+/*
+ * tq_append_kv: one autoregressive step's keys and/or values, one token per
+ * (sequence, KV head), each sequence at its own slot (FibQuant summary,
+ * section 1: a record at a fixed address; TurboESM summary, technical
+ * section 5: autoregressive generation).  The token of sequence b goes to
+ * slot pos[b], which is also its RoPE position.
+ *   k, v          device [B][h_kv][d] (dtype as tq_encode_kv), strides
+ *                 host int64[2] (sequence, head) in elements, multiples of
+ *                 16 bytes
+ *   pos           device int32 [B]; a slot outside the cache (or behind a
+ *                 page entry outside the pool) is encoded but not stored
+ *   pages         paged records, or NULL for contiguous records of L_cap
+ *                 slots per (sequence, head)
+ *   rope_*        as tq_encode_kv; every pos[b] must be below rope_npos
+ *                 (a position beyond the table reads its last row)
+ * Hadamard and unrotated codebooks only.  Writes nothing but the records of
+ * the B * h_kv appended tokens.
+ */
+tq_status tq_append_kv(const tq_codebook* ck, const tq_codebook* cv, const void* k, const void* v, int32_t dtype,
+                       int32_t B, int32_t h_kv, const int64_t* k_stride, const int64_t* v_stride,
+                       const int32_t* pos, const tq_pages* pages, int32_t L_cap, const float* rope_cos,
+                       const float* rope_sin, int32_t rope_npos, const tq_packed* kout, const tq_packed* vout,
+                       void* stream);
+
+/*
  * tq_attn_logits: attention logits from packed keys (tambur post; iaemfoco
  * post, "Uma Nova Abordagem" for the unbiased QJL correction):
  *   logit[b][h][t] = nu_t ( <q'_h, t[c_t]> + sqrt(pi/2)/m gamma_t <s_h, z_t> )
@@ -312,6 +370,23 @@ tq_status tq_attn_decode(const tq_codebook* ck, const tq_codebook* cv, const voi
                          int32_t L_cap, const int32_t* seq_len, const float* rope_cos,
                          const float* rope_sin, int32_t rope_npos, float scale, float* out,
                          void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Paged forms of tq_attn_logits and tq_attn_decode: keys (and values) are
+ * read through the page table; the logical capacity max_pages * page_size
+ * takes the place of L_cap (logit rows are [max_pages * page_size] wide,
+ * workspaces are sized with it).  Bits <= 3 Hadamard or unrotated codebooks
+ * (TQ_EUNSUPPORTED otherwise).
+ */
+tq_status tq_attn_logits_paged(const tq_codebook* ck, const void* q, int32_t q_dtype, const tq_packed* k, int32_t B,
+                               int32_t Hq, int32_t h_kv, const int32_t* seq_len, const tq_pages* pages,
+                               const float* rope_cos, const float* rope_sin, int32_t rope_npos, int32_t top_k,
+                               float* out, int32_t* topk_idx, void* ws, size_t ws_bytes, void* stream);
+tq_status tq_attn_decode_paged(const tq_codebook* ck, const tq_codebook* cv, const void* q, int32_t q_dtype,
+                               const tq_packed* k, const tq_packed* v, int32_t B, int32_t Hq, int32_t h_kv,
+                               const int32_t* seq_len, const tq_pages* pages, const float* rope_cos,
+                               const float* rope_sin, int32_t rope_npos, float scale, float* out, void* ws,
+                               size_t ws_bytes, void* stream);
 
 /* Workspace bytes for an op.  For TQ_OP_ENCODE pass the vector count in B
  * (other sizes ignored).  Returns 0 on a bad argument. */

@@ -31,10 +31,10 @@ import numpy as np
 from . import _lib
 from ._lib import (TQError, TQ_F32, TQ_BF16, TQ_ROT_AUTO, TQ_ROT_HADAMARD, TQ_ROT_DENSE, TQ_ROT_NONE,
                    TQ_CORR_QJL, TQ_CORR_SIGN, TQ_OP_ENCODE, TQ_OP_LOGITS, TQ_OP_DECODE, check, lib, tq_draws,
-                   tq_packed, tq_spec)
+                   tq_packed, tq_pages, tq_spec)
 
-__all__ = ["Codebook", "Packed", "Launch", "encode_kv", "attn_logits", "attn_decode", "rope_table",
-           "codebook_tables", "plane_words", "workspace_bytes", "calibrate", "TQError", "lib"]
+__all__ = ["Codebook", "Packed", "Pages", "Launch", "encode_kv", "append_kv", "attn_logits", "attn_decode",
+           "rope_table", "codebook_tables", "plane_words", "workspace_bytes", "calibrate", "TQError", "lib"]
 
 _ROT = {"auto": TQ_ROT_AUTO, "hadamard": TQ_ROT_HADAMARD, "dense": TQ_ROT_DENSE, "none": TQ_ROT_NONE}
 _CORR = {"qjl": TQ_CORR_QJL, "sign": TQ_CORR_SIGN}
@@ -247,6 +247,33 @@ class Packed:
                 self.codes.cpu().numpy().view(np.uint32), self.signs.cpu().numpy().view(np.uint32))
 
 
+class Pages:
+    """A page table for paged records: table int32 [B, max_pages] on the GPU
+    (physical page of each sequence's logical page), pages of page_size
+    slots (a multiple of 64), n_pages physical pages in the pool.  Record
+    planes for it hold records(h_kv) records."""
+
+    def __init__(self, table, page_size, n_pages):
+        torch = _torch()
+        if table.dtype != torch.int32 or table.dim() != 2 or not table.is_contiguous():
+            raise ValueError("the page table is a contiguous int32 [B, max_pages] tensor")
+        self.table = table
+        self.page_size = int(page_size)
+        self.n_pages = int(n_pages)
+        self.max_pages = int(table.shape[1])
+
+    @property
+    def capacity(self):
+        """Logical slots per sequence."""
+        return self.max_pages * self.page_size
+
+    def records(self, h_kv):
+        return self.n_pages * int(h_kv) * self.page_size
+
+    def struct(self):
+        return tq_pages(self.table.data_ptr(), self.page_size, self.max_pages, self.n_pages)
+
+
 class Launch:
     """One library call with its arguments marshalled once: calling it
     enqueues the same work again (same buffers, sizes and stream).  Loops that
@@ -302,13 +329,27 @@ def _strides(t):
 
 
 def encode_kv(ck, cv, k, v, kout=None, vout=None, tok_offset=0, L_cap=None, rope=None, workspace=None,
-              prepare=False):
+              prepare=False, pages=None):
     """Encode k and/or v ([n_seq, n_tok, h_kv, d], float32 or bfloat16) into
-    Packed planes at cache slots tok_offset.. of each (seq, head).  With
-    prepare=True nothing runs: a Launch that enqueues this call is returned
-    (the tensors must stay alive and in place)."""
+    Packed planes at cache slots tok_offset.. of each (seq, head) (through
+    the page table when pages is a Pages).  With prepare=True nothing runs:
+    a Launch that enqueues this call is returned (the tensors must stay alive
+    and in place)."""
     x = k if k is not None else v
     n_seq, n_tok, h_kv, _ = x.shape
+    if pages is not None:
+        ks = _strides(k) if k is not None else None
+        vs = _strides(v) if v is not None else None
+        cos, sin = (None, None) if rope is None else rope
+        npos = 0 if rope is None else int(cos.shape[0])
+        pst = pages.struct()
+        kst = kout.struct() if kout is not None else None
+        vst = vout.struct() if vout is not None else None
+        args = [ck.handle if ck else None, cv.handle if cv else None, _ptr(k), _ptr(v), _dtype_code(x), n_seq, n_tok,
+                h_kv, ks, vs, int(tok_offset), C.byref(pst), _ptr(cos), _ptr(sin), npos,
+                C.byref(kst) if kst is not None else None, C.byref(vst) if vst is not None else None, _stream()]
+        launch = _run(lib().tq_encode_kv_paged, args, (kst, vst, ks, vs, pst), prepare)
+        return launch if prepare else (kout, vout)
     L_cap = n_tok + tok_offset if L_cap is None else int(L_cap)
     dt = _dtype_code(x)
     ks = _strides(k) if k is not None else None
@@ -327,12 +368,44 @@ def encode_kv(ck, cv, k, v, kout=None, vout=None, tok_offset=0, L_cap=None, rope
     return launch if prepare else (kout, vout)
 
 
-def attn_logits(ck, q, kp, h_kv, L_cap, seq_len, rope=None, top_k=0, out=None, workspace=None, prepare=False):
+def append_kv(ck, cv, k, v, kout, vout, pos, pages=None, L_cap=None, rope=None, prepare=False):
+    """One autoregressive step: k and/or v [B, h_kv, d] (float32 or bfloat16),
+    the token of sequence b written at slot pos[b] (int32 [B] on the GPU),
+    through the page table when pages is given, else into contiguous records
+    of L_cap slots."""
+    x = k if k is not None else v
+    B, h_kv, _ = x.shape
+
+    def strides(t):
+        if t is None:
+            return None
+        if t.dim() != 3 or t.stride(2) != 1:
+            raise ValueError("append inputs are [B, h_kv, d] with d contiguous")
+        return (C.c_int64 * 2)(t.stride(0), t.stride(1))
+    ks, vs = strides(k), strides(v)
+    cos, sin = (None, None) if rope is None else rope
+    npos = 0 if rope is None else int(cos.shape[0])
+    pst = pages.struct() if pages is not None else None
+    kst = kout.struct() if kout is not None else None
+    vst = vout.struct() if vout is not None else None
+    args = [ck.handle if ck else None, cv.handle if cv else None, _ptr(k), _ptr(v), _dtype_code(x), B, h_kv, ks, vs,
+            _ptr(pos), C.byref(pst) if pst is not None else None, 0 if L_cap is None else int(L_cap), _ptr(cos),
+            _ptr(sin), npos, C.byref(kst) if kst is not None else None, C.byref(vst) if vst is not None else None,
+            _stream()]
+    return _run(lib().tq_append_kv, args, (kst, vst, ks, vs, pst), prepare)
+
+
+def attn_logits(ck, q, kp, h_kv, L_cap, seq_len, rope=None, top_k=0, out=None, workspace=None, prepare=False,
+                pages=None):
     """Logits [B, Hq, L_cap] (top_k = 0) or (values, indices) [B, Hq, top_k]
     for queries q [B, Hq, d] against packed keys.  seq_len: int32 [B] on the
-    GPU.  prepare=True returns (Launch, outputs) without running."""
+    GPU.  With pages (a Pages), keys are read through the page table and
+    L_cap is its capacity.  prepare=True returns (Launch, outputs) without
+    running."""
     torch = _torch()
     B, Hq, d = q.shape
+    if pages is not None:
+        L_cap = pages.capacity
     if not q.is_contiguous():
         raise ValueError("q must be contiguous")
     cos, sin = (None, None) if rope is None else rope
@@ -346,19 +419,28 @@ def attn_logits(ck, q, kp, h_kv, L_cap, seq_len, rope=None, top_k=0, out=None, w
     elif out is None:
         out = torch.zeros((B, Hq, L_cap), dtype=torch.float32, device=q.device)
     kst = kp.struct()
-    args = [ck.handle, _ptr(q), _dtype_code(q), C.byref(kst), B, Hq, int(h_kv), int(L_cap), _ptr(seq_len), _ptr(cos),
-            _ptr(sin), npos, int(top_k), _ptr(out), _ptr(idx), _ptr(ws), wsb, _stream()]
-    launch = _run(lib().tq_attn_logits, args, (kst, ws, out, idx), prepare)
+    if pages is not None:
+        pst = pages.struct()
+        args = [ck.handle, _ptr(q), _dtype_code(q), C.byref(kst), B, Hq, int(h_kv), _ptr(seq_len), C.byref(pst),
+                _ptr(cos), _ptr(sin), npos, int(top_k), _ptr(out), _ptr(idx), _ptr(ws), wsb, _stream()]
+        launch = _run(lib().tq_attn_logits_paged, args, (kst, pst, ws, out, idx), prepare)
+    else:
+        args = [ck.handle, _ptr(q), _dtype_code(q), C.byref(kst), B, Hq, int(h_kv), int(L_cap), _ptr(seq_len),
+                _ptr(cos), _ptr(sin), npos, int(top_k), _ptr(out), _ptr(idx), _ptr(ws), wsb, _stream()]
+        launch = _run(lib().tq_attn_logits, args, (kst, ws, out, idx), prepare)
     res = (out, idx) if top_k else out
     return (launch, res) if prepare else res
 
 
 def attn_decode(ck, cv, q, kp, vp, h_kv, L_cap, seq_len, rope=None, scale=0.0, out=None, workspace=None,
-                prepare=False):
-    """Decode attention output [B, Hq, d] float32 over packed K and V.
+                prepare=False, pages=None):
+    """Decode attention output [B, Hq, d] float32 over packed K and V (read
+    through the page table when pages is given; L_cap is then its capacity).
     prepare=True returns (Launch, out) without running."""
     torch = _torch()
     B, Hq, d = q.shape
+    if pages is not None:
+        L_cap = pages.capacity
     if not q.is_contiguous():
         raise ValueError("q must be contiguous")
     cos, sin = (None, None) if rope is None else rope
@@ -368,7 +450,15 @@ def attn_decode(ck, cv, q, kp, vp, h_kv, L_cap, seq_len, rope=None, scale=0.0, o
     if out is None:
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
     kst, vst = kp.struct(), vp.struct()
-    args = [ck.handle, cv.handle, _ptr(q), _dtype_code(q), C.byref(kst), C.byref(vst), B, Hq, int(h_kv), int(L_cap),
-            _ptr(seq_len), _ptr(cos), _ptr(sin), npos, float(scale), _ptr(out), _ptr(ws), wsb, _stream()]
-    launch = _run(lib().tq_attn_decode, args, (kst, vst, ws, out), prepare)
+    if pages is not None:
+        pst = pages.struct()
+        args = [ck.handle, cv.handle, _ptr(q), _dtype_code(q), C.byref(kst), C.byref(vst), B, Hq, int(h_kv),
+                _ptr(seq_len), C.byref(pst), _ptr(cos), _ptr(sin), npos, float(scale), _ptr(out), _ptr(ws), wsb,
+                _stream()]
+        launch = _run(lib().tq_attn_decode_paged, args, (kst, vst, pst, ws, out), prepare)
+    else:
+        args = [ck.handle, cv.handle, _ptr(q), _dtype_code(q), C.byref(kst), C.byref(vst), B, Hq, int(h_kv),
+                int(L_cap), _ptr(seq_len), _ptr(cos), _ptr(sin), npos, float(scale), _ptr(out), _ptr(ws), wsb,
+                _stream()]
+        launch = _run(lib().tq_attn_decode, args, (kst, vst, ws, out), prepare)
     return (launch, out) if prepare else out

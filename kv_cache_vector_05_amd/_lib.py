@@ -31,6 +31,10 @@ class tq_packed(C.Structure):
                 ("n", C.c_int64)]
 
 
+class tq_pages(C.Structure):
+    _fields_ = [("pages", C.c_void_p), ("page_size", C.c_int32), ("max_pages", C.c_int32), ("n_pages", C.c_int64)]
+
+
 # exported symbols and their signatures (restype, argtypes)
 SIGNATURES = {
     "tq_codebook_tables": (C.c_int32, [C.POINTER(tq_spec), C.POINTER(tq_draws), C.c_void_p, C.c_void_p,
@@ -49,6 +53,22 @@ SIGNATURES = {
                                  C.c_int32, C.c_int32, C.POINTER(C.c_int64), C.POINTER(C.c_int64), C.c_int32,
                                  C.c_int32, C.c_void_p, C.c_void_p, C.c_int32, C.POINTER(tq_packed),
                                  C.POINTER(tq_packed), C.c_void_p, C.c_size_t, C.c_void_p]),
+    "tq_encode_kv_paged": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
+                                       C.c_int32, C.c_int32, C.POINTER(C.c_int64), C.POINTER(C.c_int64), C.c_int32,
+                                       C.POINTER(tq_pages), C.c_void_p, C.c_void_p, C.c_int32, C.POINTER(tq_packed),
+                                       C.POINTER(tq_packed), C.c_void_p]),
+    "tq_append_kv": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32,
+                                 C.POINTER(C.c_int64), C.POINTER(C.c_int64), C.c_void_p, C.POINTER(tq_pages),
+                                 C.c_int32, C.c_void_p, C.c_void_p, C.c_int32, C.POINTER(tq_packed),
+                                 C.POINTER(tq_packed), C.c_void_p]),
+    "tq_attn_logits_paged": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_int32, C.POINTER(tq_packed), C.c_int32,
+                                         C.c_int32, C.c_int32, C.c_void_p, C.POINTER(tq_pages), C.c_void_p,
+                                         C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
+                                         C.c_size_t, C.c_void_p]),
+    "tq_attn_decode_paged": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.POINTER(tq_packed),
+                                         C.POINTER(tq_packed), C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
+                                         C.POINTER(tq_pages), C.c_void_p, C.c_void_p, C.c_int32, C.c_float,
+                                         C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "tq_attn_logits": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_int32, C.POINTER(tq_packed), C.c_int32,
                                    C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
                                    C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,

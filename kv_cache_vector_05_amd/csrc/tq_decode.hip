@@ -64,6 +64,13 @@ struct DecM {
     const float* k_mu;            // sign correction: mu per KV head, else nullptr (gamma per key)
     const float* v_mu;
     int32_t k_mu_stride, v_mu_stride;
+    // paged records (pages != nullptr): page table [B][max_pages] of pages of
+    // page_size slots, a multiple of 64, so a 64-key chunk (splits start at
+    // multiples of 64) lies in one page; entries are clamped into [0, n_pages)
+    const int32_t* pages;
+    int32_t page_size, max_pages;
+    int64_t n_pages;
+    dev::FastDiv div_page;
     float* part;  // [B*Hq][nsplit][2 + D + M]
 };
 
@@ -111,7 +118,7 @@ __device__ __forceinline__ float max64(float v) {
     return v;
 }
 
-template <int D, int BITS, int NRT, int M>
+template <int D, int BITS, int NRT, int M, bool PAGED>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
     constexpr int NCS = M == 0 ? 0 : (M >= 64 ? M / 64 : 1);  // K=64 sketch chunks of the logit
     using TL = dev::TileLogit<D, BITS, NRT, NCS>;
@@ -157,6 +164,17 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
     }
     const int nch = (c1 - c0 + 63) / 64;
     const int64_t rec_base = bk * p.L_cap;
+    // record index of key c0 + 64 c + r (0 <= r < 64) of this (sequence, KV head)
+    auto record = [&](int c, int r) -> int64_t {
+        if constexpr (PAGED) {
+            const int key0 = __builtin_amdgcn_readfirstlane(c0 + 64 * c);
+            const uint32_t j = p.div_page.div((uint32_t)key0);
+            int64_t pg = p.pages[(int64_t)b * p.max_pages + j];
+            pg = pg < 0 ? 0 : (pg >= p.n_pages ? p.n_pages - 1 : pg);
+            return (pg * p.h_kv + kh) * p.page_size + (key0 - (int64_t)j * p.page_size) + r;
+        }
+        return rec_base + c0 + 64 * c + r;
+    };
     // correction weights: gamma per record (QJL sketch) or the KV head's mu
     const float k_head = p.k_mu ? p.k_mu[kh * p.k_mu_stride] : 0.f;
     const float v_head = p.v_mu ? p.v_mu[kh * p.v_mu_stride] : 0.f;
@@ -176,7 +194,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
             float nu, gm, vn, vg;
         } cur, nxt;
         auto fetch1 = [&](int c, Rec1& r) {
-            const int64_t rec = rec_base + min(c0 + 64 * c + 16 * wave + n, c1 - 1);
+            const int64_t rec = record(c, min(16 * wave + n, c1 - 1 - c0 - 64 * c));
             TL::load(p.k_codes + rec * Q::CW + Q::word0(qk), p.k_signs + rec * MW, PER, lane, r.raw);
             r.nu = p.k_norm[rec];
             r.gm = M > 0 ? (p.k_mu ? k_head : p.k_rnorm[rec]) : 0.f;
@@ -266,7 +284,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
         float vn, vg;
     } vcur, vnxt;
     auto fetch2 = [&](int c, Rec2& r) {
-        const int64_t rec = rec_base + min(c0 + 64 * c + row, c1 - 1);
+        const int64_t rec = record(c, min(row, c1 - 1 - c0 - 64 * c));
         Q::load(p.v_codes + rec * Q::CW + Q::word0(qk), qk, r.W);
         r.sg = M > 0 ? p.v_signs[rec * MW + ((qk * PER) >> 5)] : 0u;
         r.vn = p.v_norm[rec];
@@ -399,33 +417,33 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
 
 using DecMFn = void (*)(DecM);
 
-template <int D, int BITS, int NRT>
+template <int D, int BITS, int NRT, bool PG>
 DecMFn pick_m(int m) {
     if constexpr (D == 64) {
         switch (m) {
-            case 0: return decode_mfma_kernel<D, BITS, NRT, 0>;
-            case 32: return decode_mfma_kernel<D, BITS, NRT, 32>;
-            case 64: return decode_mfma_kernel<D, BITS, NRT, 64>;
+            case 0: return decode_mfma_kernel<D, BITS, NRT, 0, PG>;
+            case 32: return decode_mfma_kernel<D, BITS, NRT, 32, PG>;
+            case 64: return decode_mfma_kernel<D, BITS, NRT, 64, PG>;
         }
     } else {
         switch (m) {
-            case 0: return decode_mfma_kernel<D, BITS, NRT, 0>;
-            case 64: return decode_mfma_kernel<D, BITS, NRT, 64>;
-            case 128: return decode_mfma_kernel<D, BITS, NRT, 128>;
+            case 0: return decode_mfma_kernel<D, BITS, NRT, 0, PG>;
+            case 64: return decode_mfma_kernel<D, BITS, NRT, 64, PG>;
+            case 128: return decode_mfma_kernel<D, BITS, NRT, 128, PG>;
         }
     }
     return nullptr;
 }
-template <int D, int BITS>
+template <int D, int BITS, bool PG>
 DecMFn pick_nrt(int nrt, int m) {
-    return nrt == 1 ? pick_m<D, BITS, 1>(m) : pick_m<D, BITS, 2>(m);
+    return nrt == 1 ? pick_m<D, BITS, 1, PG>(m) : pick_m<D, BITS, 2, PG>(m);
 }
-template <int D>
+template <int D, bool PG>
 DecMFn pick_bits(int bits, int nrt, int m) {
     switch (bits) {
-        case 1: return pick_nrt<D, 1>(nrt, m);
-        case 2: return pick_nrt<D, 2>(nrt, m);
-        case 3: return pick_nrt<D, 3>(nrt, m);
+        case 1: return pick_nrt<D, 1, PG>(nrt, m);
+        case 2: return pick_nrt<D, 2, PG>(nrt, m);
+        case 3: return pick_nrt<D, 3, PG>(nrt, m);
     }
     return nullptr;
 }
@@ -460,8 +478,11 @@ hipError_t launch_decode_mfma(const tq_codebook* ck, const tq_codebook* cv, cons
     const int G = a.Hq / a.h_kv;
     const int nrt = decode_nrt(G);
     DecMFn fn = nullptr;
-    if (ck->spec.d == 64) fn = pick_bits<64>(ck->spec.bits, nrt, ck->spec.m);
-    else if (ck->spec.d == 128) fn = pick_bits<128>(ck->spec.bits, nrt, ck->spec.m);
+    const bool paged = a.pages.table != nullptr;
+    if (ck->spec.d == 64)
+        fn = paged ? pick_bits<64, true>(ck->spec.bits, nrt, ck->spec.m) : pick_bits<64, false>(ck->spec.bits, nrt, ck->spec.m);
+    else if (ck->spec.d == 128)
+        fn = paged ? pick_bits<128, true>(ck->spec.bits, nrt, ck->spec.m) : pick_bits<128, false>(ck->spec.bits, nrt, ck->spec.m);
     if (!fn) return hipErrorInvalidValue;
     DecM p{};
     p.qd = q.qd;
@@ -496,6 +517,11 @@ hipError_t launch_decode_mfma(const tq_codebook* ck, const tq_codebook* cv, cons
     p.k_mu_stride = mk.stride;
     p.v_mu = mv.ptr;
     p.v_mu_stride = mv.stride;
+    p.pages = a.pages.table;
+    p.page_size = a.pages.size;
+    p.max_pages = a.pages.max_pages;
+    p.n_pages = a.pages.n_pages;
+    p.div_page = dev::FastDiv((uint32_t)(a.pages.size > 0 ? a.pages.size : 1));
     p.part = part;
     const unsigned gx = (unsigned)((int64_t)a.B * a.h_kv * p.ngroups);
     if (gx == 0 || nsplit == 0) return hipSuccess;

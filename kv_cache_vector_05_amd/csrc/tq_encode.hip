@@ -51,6 +51,18 @@ struct EncK {
     // tile t = (token block * n_seq + seq) * h_kv + head: the tiles that share
     // a token block's RoPE rows (every sequence and head) run close together
     dev::FastDiv div_h, div_seq;  // by h_kv and by n_seq (tile indices are below 2^31)
+    // append = 1: one token per (sequence, head); tile t holds vectors
+    // [32 t, 32 t + 32) of the n_seq * h_kv list (sequence-major) and the
+    // token of sequence b goes to slot pos[b] (its RoPE position too)
+    int32_t append;
+    const int32_t* pos;
+    int32_t rope_npos;
+    // paged records (pages != nullptr): page table [n_seq][max_pages] of
+    // physical pages of page_size slots, each holding every head's slots
+    const int32_t* pages;
+    int32_t page_size, max_pages;
+    int64_t n_pages;
+    dev::FastDiv div_page;
     const float* rope_cos;
     const float* rope_sin;
     const float* sigma;
@@ -296,12 +308,31 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
     // last token read the last token instead (an MFMA column only feeds its
     // own vector, and these vectors are not stored)
     auto input_offset = [&](int64_t t) -> int64_t {
+        if (p.append) {
+            const int64_t idx = min(t * 32 + v, (int64_t)p.n_seq * p.h_kv - 1);
+            const uint32_t b = p.div_h.div((uint32_t)idx);
+            return (int64_t)b * p.s_seq + (int64_t)((uint32_t)idx - b * (uint32_t)p.h_kv) * p.s_head;
+        }
         const uint32_t r = p.div_h.div((uint32_t)t);
         const int hd = (int)((uint32_t)t - r * (uint32_t)p.h_kv);
         const uint32_t tq_ = p.div_seq.div(r);
         const uint32_t sq = r - tq_ * (uint32_t)p.n_seq;
         const int tbk = (int)tq_;
         return (int64_t)sq * p.s_seq + (int64_t)min(tbk * 32 + v, p.n_tok - 1) * p.s_tok + (int64_t)hd * p.s_head;
+    };
+    // record of slot t of (sequence b, head hd), or -1 for a slot outside the
+    // cache (or behind a page-table entry outside the pool): such a vector is
+    // encoded but not stored
+    auto record_of = [&](int b, int hd, int64_t t) -> int64_t {
+        if (p.pages) {
+            if (t < 0 || t >= (int64_t)p.max_pages * p.page_size) return -1;
+            const uint32_t j = p.div_page.div((uint32_t)t);
+            const int32_t pg = p.pages[(int64_t)b * p.max_pages + j];
+            if (pg < 0 || pg >= p.n_pages) return -1;
+            return ((int64_t)pg * p.h_kv + hd) * p.page_size + (t - (int64_t)j * p.page_size);
+        }
+        if (t < 0 || t >= p.L_cap) return -1;
+        return ((int64_t)b * p.h_kv + hd) * p.L_cap + t;
     };
     // RoPE keys run at two waves per SIMD whatever their register count, so
     // their next tile's bf16 inputs are loaded while this tile is quantised
@@ -324,14 +355,31 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
       const bool prefetch = stage && base + blk_stride < p.n_tiles;
       if (tile >= p.n_tiles && prefetch) rope_stage_load<HALF, NQ>(p, base + blk_stride, st_table, st_row, st_c4, pre);
       if (tile < p.n_tiles) {
-        const uint32_t r = p.div_h.div((uint32_t)tile);
-        const int head = (int)((uint32_t)tile - r * (uint32_t)p.h_kv);
-        const uint32_t tbq = p.div_seq.div(r);
-        const uint32_t sq = r - tbq * (uint32_t)p.n_seq;
-        const int tb = (int)tbq;
-        const int seq = (int)sq;
-        const int token = tb * 32 + v;
-        const bool valid = token < p.n_tok;
+        int head, seq;
+        int64_t slot;  // cache slot of the lane's vector
+        int rpos;      // its RoPE row (a valid table row for every lane)
+        bool valid;
+        if (p.append) {
+            const int64_t idx = tile * 32 + v;
+            const int64_t nv = (int64_t)p.n_seq * p.h_kv;
+            const uint32_t bq = p.div_h.div((uint32_t)min(idx, nv - 1));
+            seq = (int)bq;
+            head = (int)((uint32_t)min(idx, nv - 1) - bq * (uint32_t)p.h_kv);
+            slot = p.pos[seq];
+            valid = idx < nv;
+            rpos = (int)min(max(slot, (int64_t)0), (int64_t)max(p.rope_npos - 1, 0));
+        } else {
+            const uint32_t r = p.div_h.div((uint32_t)tile);
+            head = (int)((uint32_t)tile - r * (uint32_t)p.h_kv);
+            const uint32_t tbq = p.div_seq.div(r);
+            seq = (int)(r - tbq * (uint32_t)p.n_seq);
+            const int token = (int)tbq * 32 + v;
+            valid = token < p.n_tok;
+            slot = (int64_t)p.tok_offset + token;
+            rpos = p.tok_offset + (valid ? token : 0);
+        }
+        const int64_t n = record_of(seq, head, slot);
+        valid = valid && n >= 0;
 
         floatx16 acc[NOB];
         float nu, scale;
@@ -382,7 +430,7 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
                             cc = s_rope4[(v * RS + c0) / 4];
                             sn = s_rope4[((32 + v) * RS + c0) / 4];
                         } else {
-                            const int64_t ro = (int64_t)(p.tok_offset + (valid ? token : 0)) * HALF + c0;
+                            const int64_t ro = (int64_t)rpos * HALF + c0;
                             cc = *reinterpret_cast<const f32x4*>(p.rope_cos + ro);
                             sn = *reinterpret_cast<const f32x4*>(p.rope_sin + ro);
                         }
@@ -507,7 +555,7 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
                             sn[c] = s_rope4[((32 + v) * RS + 16 * kp + 8 * h) / 4 + c];
                         }
                     } else {
-                        const int64_t ro = (int64_t)(p.tok_offset + (valid ? token : 0)) * HALF + 16 * kp + 8 * h;
+                        const int64_t ro = (int64_t)rpos * HALF + 16 * kp + 8 * h;
                         const f32x4* cp = reinterpret_cast<const f32x4*>(p.rope_cos + ro);
                         const f32x4* sp = reinterpret_cast<const f32x4*>(p.rope_sin + ro);
 #pragma unroll
@@ -708,7 +756,6 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
             cw[k] = __float_as_uint(a) | __float_as_uint(b);
         }
 
-        const int64_t n = ((int64_t)seq * p.h_kv + head) * p.L_cap + p.tok_offset + token;
         if (valid) {
             uint32_t* dst = p.codes + n * CW + h * (CW / 2);
 #pragma unroll
@@ -1014,9 +1061,18 @@ hipError_t launch_encode(const tq_codebook* cb, const EncodeArgs& a, hipStream_t
         p.rnorm = a.out.rnorm;
         p.codes = a.out.codes;
         p.signs = a.out.signs;
-        p.rope_stage = (a.rope_cos != nullptr && a.h_kv % 4 == 0) ? 1 : 0;
+        p.rope_stage = (a.rope_cos != nullptr && a.h_kv % 4 == 0 && !a.append) ? 1 : 0;
         p.div_h = dev::FastDiv((uint32_t)a.h_kv);
         p.div_seq = dev::FastDiv((uint32_t)a.n_seq);
+        p.append = a.append;
+        p.pos = a.pos;
+        p.rope_npos = a.rope_npos;
+        p.pages = a.pages.table;
+        p.page_size = a.pages.size;
+        p.max_pages = a.pages.max_pages;
+        p.n_pages = a.pages.n_pages;
+        p.div_page = dev::FastDiv((uint32_t)(a.pages.size > 0 ? a.pages.size : 1));
+        if (a.append) p.n_tiles = ((int64_t)a.n_seq * a.h_kv + 31) / 32;
         const size_t lds = p.rope_stage ? (size_t)2 * 32 * (d / 2 + 4) * sizeof(float) : 0;
         // persistent blocks: as many as are resident at once, so that no
         // partial last round of blocks leaves CUs idle

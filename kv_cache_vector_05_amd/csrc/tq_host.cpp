@@ -762,25 +762,42 @@ static tq_status check_packed(const tq_codebook* cb, const tq_packed* p, int64_t
     return TQ_OK;
 }
 
-tq_status tq_encode_kv(const tq_codebook* ck, const tq_codebook* cv, const void* k, const void* v,
-                       int32_t dtype, int32_t n_seq, int32_t n_tok, int32_t h_kv,
-                       const int64_t* k_stride, const int64_t* v_stride, int32_t tok_offset,
-                       int32_t L_cap, const float* rope_cos, const float* rope_sin,
-                       int32_t rope_npos, const tq_packed* kout, const tq_packed* vout, void* ws,
-                       size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+// page table checks: page size a multiple of 64, logical capacity below 2^31
+static tq_status check_pages(const tq_pages* pg, PageRef* out) {
+    if (!pg || !pg->pages) return fail(TQ_EINVAL, "null page table");
+    if (pg->page_size <= 0 || pg->page_size % 64) return fail(TQ_EINVAL, "page_size must be a positive multiple of 64");
+    if (pg->max_pages <= 0 || pg->n_pages <= 0) return fail(TQ_EINVAL, "max_pages and n_pages must be positive");
+    if ((int64_t)pg->max_pages * pg->page_size >= ((int64_t)1 << 31))
+        return fail(TQ_EINVAL, "max_pages * page_size must be below 2^31");
+    out->table = pg->pages;
+    out->size = pg->page_size;
+    out->max_pages = pg->max_pages;
+    out->n_pages = pg->n_pages;
+    return TQ_OK;
+}
+
+// Shared body of the encode entry points.  pos != nullptr: one token per
+// (sequence, head) at slot pos[sequence] (append); pg.table != nullptr: paged
+// records.  cap_records: records the planes must hold.
+static tq_status encode_common(const tq_codebook* ck, const tq_codebook* cv, const void* k, const void* v,
+                               int32_t dtype, int32_t n_seq, int32_t n_tok, int32_t h_kv, const int64_t ks[3],
+                               const int64_t vs[3], int32_t tok_offset, int32_t L_cap, const PageRef& pg,
+                               const int32_t* pos, const float* rope_cos, const float* rope_sin, int32_t rope_npos,
+                               const tq_packed* kout, const tq_packed* vout, int64_t cap_records, void* ws,
+                               size_t ws_bytes, void* stream) {
     if (dtype != TQ_F32 && dtype != TQ_BF16) return fail(TQ_EINVAL, "dtype must be TQ_F32 or TQ_BF16");
-    if (n_seq < 0 || n_tok < 0 || h_kv < 0 || tok_offset < 0 || L_cap < 0)
-        return fail(TQ_EINVAL, "negative size");
-    if ((int64_t)tok_offset + n_tok > L_cap) return fail(TQ_EINVAL, "tok_offset + n_tok exceeds L_cap");
+    if (n_seq < 0 || n_tok < 0 || h_kv < 0 || tok_offset < 0 || L_cap < 0) return fail(TQ_EINVAL, "negative size");
+    const int64_t slots = pg.table ? (int64_t)pg.max_pages * pg.size : L_cap;
+    if (!pos && (int64_t)tok_offset + n_tok > slots) return fail(TQ_EINVAL, "tok_offset + n_tok exceeds the cache's slots");
     if ((int64_t)n_seq * n_tok * h_kv == 0) return TQ_OK;  // nothing to encode
     if (!k && !v) return fail(TQ_EINVAL, "neither k nor v given");
     if ((rope_cos == nullptr) != (rope_sin == nullptr)) return fail(TQ_EINVAL, "give both RoPE tables or neither");
     const int64_t nvec = (int64_t)n_seq * n_tok * h_kv;
-    const int64_t need = (int64_t)n_seq * h_kv * L_cap;
-    const int esz = dtype == TQ_F32 ? 4 : 2;
     const int align = dtype == TQ_F32 ? 4 : 8;
     struct Side { const tq_codebook* cb; const void* x; const int64_t* st; const tq_packed* o; bool rope; };
-    Side sides[2] = {{ck, k, k_stride, kout, rope_cos != nullptr}, {cv, v, v_stride, vout, false}};
+    Side sides[2] = {{ck, k, ks, kout, rope_cos != nullptr}, {cv, v, vs, vout, false}};
     for (auto& sd : sides) {
         if (!sd.x) continue;
         if (!sd.cb) return fail(TQ_EINVAL, "tensor given without a codebook");
@@ -788,12 +805,15 @@ tq_status tq_encode_kv(const tq_codebook* ck, const tq_codebook* cv, const void*
         for (int i = 0; i < 3; ++i)
             if (sd.st[i] < 0 || sd.st[i] % align) return fail(TQ_EINVAL, "strides must be non-negative multiples of 16 bytes");
         if (((uintptr_t)sd.x) % 16) return fail(TQ_EINVAL, "input must be 16-byte aligned");
-        tq_status st = check_packed(sd.cb, sd.o, need, sd.x == k ? "k" : "v");
+        tq_status st = check_packed(sd.cb, sd.o, cap_records, sd.x == k ? "k" : "v");
         if (st) return st;
         if (sd.rope) {
-            if (rope_npos < tok_offset + n_tok) return fail(TQ_EINVAL, "RoPE table shorter than the last position");
+            if (!pos && rope_npos < tok_offset + n_tok) return fail(TQ_EINVAL, "RoPE table shorter than the last position");
+            if (pos && rope_npos <= 0) return fail(TQ_EINVAL, "empty RoPE table");
             if (sd.cb->spec.d % 2) return fail(TQ_EINVAL, "RoPE needs an even d");
         }
+        if (sd.cb->dense && (pos || pg.table))
+            return fail(TQ_EUNSUPPORTED, "appends and paged records are served for Hadamard and unrotated codebooks");
         if (!sd.cb->dense && (int64_t)n_seq * ((n_tok + 31) / 32) * h_kv >= (int64_t)1 << 31)
             return fail(TQ_EUNSUPPORTED, "too many vectors in one encode call (split it)");
         if (sd.cb->dense && nvec > 0) {
@@ -801,8 +821,6 @@ tq_status tq_encode_kv(const tq_codebook* ck, const tq_codebook* cv, const void*
             if (!ws || ws_bytes < wsn) return fail(TQ_EINVAL, "workspace too small for the dense encoder");
         }
     }
-    (void)esz;
-    if (nvec == 0) return TQ_OK;
     for (auto& sd : sides) {
         if (!sd.x) continue;
         EncodeArgs a{};
@@ -818,9 +836,13 @@ tq_status tq_encode_kv(const tq_codebook* ck, const tq_codebook* cv, const void*
         a.bf16 = dtype == TQ_BF16;
         a.rope_cos = sd.rope ? rope_cos : nullptr;
         a.rope_sin = sd.rope ? rope_sin : nullptr;
+        a.rope_npos = rope_npos;
         a.out = *sd.o;
         a.ws = ws;
         a.ws_bytes = ws_bytes;
+        a.append = pos ? 1 : 0;
+        a.pos = pos;
+        a.pages = pg;
         hipError_t e = launch_encode(sd.cb, a, (hipStream_t)stream);
         if (e != hipSuccess) return hip_fail(e, "encode launch");
     }
@@ -848,20 +870,21 @@ static tq_status check_attn(const tq_codebook* ck, const void* q, int32_t q_dtyp
     return TQ_OK;
 }
 
-tq_status tq_attn_logits(const tq_codebook* ck, const void* q, int32_t q_dtype, const tq_packed* k,
-                         int32_t B, int32_t Hq, int32_t h_kv, int32_t L_cap, const int32_t* seq_len,
-                         const float* rope_cos, const float* rope_sin, int32_t rope_npos,
-                         int32_t top_k, float* out, int32_t* topk_idx, void* ws, size_t ws_bytes,
-                         void* stream) {
+static tq_status logits_common(const tq_codebook* ck, const void* q, int32_t q_dtype, const tq_packed* k, int32_t B,
+                               int32_t Hq, int32_t h_kv, int32_t L_cap, const int32_t* seq_len, const PageRef& pg,
+                               int64_t cap_records, const float* rope_cos, const float* rope_sin, int32_t rope_npos,
+                               int32_t top_k, float* out, int32_t* topk_idx, void* ws, size_t ws_bytes, void* stream) {
     tq_status st = check_attn(ck, q, q_dtype, B, Hq, h_kv, L_cap, seq_len, rope_cos, rope_sin, rope_npos);
     if (st) return st;
     if (top_k < 0 || top_k > 16) return fail(TQ_EINVAL, "top_k must be 0..16");
     if (!out || (top_k && !topk_idx)) return fail(TQ_EINVAL, "null output");
-    st = check_packed(ck, k, (int64_t)B * h_kv * L_cap, "k");
+    st = check_packed(ck, k, cap_records, "k");
     if (st) return st;
     st = check_mu(ck, h_kv);
     if (st) return st;
-    if (sign_corr(ck) && !logits_mfma_supported(ck)) return fail(TQ_EUNSUPPORTED, "no logit kernel for this codebook");
+    if ((sign_corr(ck) || pg.table) && !logits_mfma_supported(ck))
+        return fail(TQ_EUNSUPPORTED, "no logit kernel for this codebook (paged and sign-corrected scans need "
+                                     "a Hadamard or unrotated codebook with bits <= 3 and m <= 128)");
     if ((int64_t)B * Hq == 0 || (L_cap == 0 && top_k == 0)) return TQ_OK;
     const size_t need = logits_workspace_bytes(ck, B, Hq, h_kv, L_cap, top_k);
     if (ws_bytes < need || (need && !ws)) return fail(TQ_EINVAL, "workspace too small");
@@ -880,31 +903,33 @@ tq_status tq_attn_logits(const tq_codebook* ck, const void* q, int32_t q_dtype, 
     a.topk_idx = topk_idx;
     a.ws = ws;
     a.ws_bytes = ws_bytes;
+    a.pages = pg;
     hipError_t e = launch_logits(ck, *k, a, (hipStream_t)stream);
     return e == hipSuccess ? TQ_OK : hip_fail(e, "logits launch");
 }
 
-tq_status tq_attn_decode(const tq_codebook* ck, const tq_codebook* cv, const void* q, int32_t q_dtype,
-                         const tq_packed* k, const tq_packed* v, int32_t B, int32_t Hq, int32_t h_kv,
-                         int32_t L_cap, const int32_t* seq_len, const float* rope_cos,
-                         const float* rope_sin, int32_t rope_npos, float scale, float* out,
-                         void* ws, size_t ws_bytes, void* stream) {
+static tq_status decode_common(const tq_codebook* ck, const tq_codebook* cv, const void* q, int32_t q_dtype,
+                               const tq_packed* k, const tq_packed* v, int32_t B, int32_t Hq, int32_t h_kv,
+                               int32_t L_cap, const int32_t* seq_len, const PageRef& pg, int64_t cap_records,
+                               const float* rope_cos, const float* rope_sin, int32_t rope_npos, float scale,
+                               float* out, void* ws, size_t ws_bytes, void* stream) {
     tq_status st = check_attn(ck, q, q_dtype, B, Hq, h_kv, L_cap, seq_len, rope_cos, rope_sin, rope_npos);
     if (st) return st;
     if (!cv) return fail(TQ_EINVAL, "null value codebook");
     if (!out) return fail(TQ_EINVAL, "null output");
     if (!(scale >= 0.0f) || std::isinf(scale)) return fail(TQ_EINVAL, "scale must be finite and >= 0");
     if (ck->spec.d != cv->spec.d) return fail(TQ_EINVAL, "key and value dimensions differ");
-    st = check_packed(ck, k, (int64_t)B * h_kv * L_cap, "k");
+    st = check_packed(ck, k, cap_records, "k");
     if (st) return st;
-    st = check_packed(cv, v, (int64_t)B * h_kv * L_cap, "v");
+    st = check_packed(cv, v, cap_records, "v");
     if (st) return st;
     st = check_mu(ck, h_kv);
     if (st) return st;
     st = check_mu(cv, h_kv);
     if (st) return st;
-    if ((sign_corr(ck) || sign_corr(cv)) && !decode_mfma_supported(ck, cv))
-        return fail(TQ_EUNSUPPORTED, "sign-corrected codebooks need key and value tables of equal d, bits and m");
+    if ((sign_corr(ck) || sign_corr(cv) || pg.table) && !decode_mfma_supported(ck, cv))
+        return fail(TQ_EUNSUPPORTED, "paged and sign-corrected decodes need key and value tables of equal d, bits "
+                                     "and m (bits <= 3)");
     if ((int64_t)B * Hq == 0) return TQ_OK;
     const size_t need = decode_workspace_bytes(ck, cv, B, Hq, h_kv, L_cap);
     if (ws_bytes < need || (need && !ws)) return fail(TQ_EINVAL, "workspace too small");
@@ -922,8 +947,102 @@ tq_status tq_attn_decode(const tq_codebook* ck, const tq_codebook* cv, const voi
     a.out = out;
     a.ws = ws;
     a.ws_bytes = ws_bytes;
+    a.pages = pg;
     hipError_t e = launch_decode(ck, cv, *k, *v, a, (hipStream_t)stream);
     return e == hipSuccess ? TQ_OK : hip_fail(e, "decode launch");
+}
+
+extern "C" {
+
+tq_status tq_encode_kv(const tq_codebook* ck, const tq_codebook* cv, const void* k, const void* v,
+                       int32_t dtype, int32_t n_seq, int32_t n_tok, int32_t h_kv,
+                       const int64_t* k_stride, const int64_t* v_stride, int32_t tok_offset,
+                       int32_t L_cap, const float* rope_cos, const float* rope_sin,
+                       int32_t rope_npos, const tq_packed* kout, const tq_packed* vout, void* ws,
+                       size_t ws_bytes, void* stream) {
+    return encode_common(ck, cv, k, v, dtype, n_seq, n_tok, h_kv, k_stride, v_stride, tok_offset, L_cap, PageRef{},
+                         nullptr, rope_cos, rope_sin, rope_npos, kout, vout, (int64_t)n_seq * h_kv * L_cap, ws,
+                         ws_bytes, stream);
+}
+
+tq_status tq_encode_kv_paged(const tq_codebook* ck, const tq_codebook* cv, const void* k, const void* v,
+                             int32_t dtype, int32_t n_seq, int32_t n_tok, int32_t h_kv, const int64_t* k_stride,
+                             const int64_t* v_stride, int32_t tok_offset, const tq_pages* pages,
+                             const float* rope_cos, const float* rope_sin, int32_t rope_npos,
+                             const tq_packed* kout, const tq_packed* vout, void* stream) {
+    PageRef pg;
+    tq_status st = check_pages(pages, &pg);
+    if (st) return st;
+    return encode_common(ck, cv, k, v, dtype, n_seq, n_tok, h_kv, k_stride, v_stride, tok_offset, 0, pg, nullptr,
+                         rope_cos, rope_sin, rope_npos, kout, vout, pg.n_pages * h_kv * (int64_t)pg.size, nullptr, 0,
+                         stream);
+}
+
+tq_status tq_append_kv(const tq_codebook* ck, const tq_codebook* cv, const void* k, const void* v, int32_t dtype,
+                       int32_t B, int32_t h_kv, const int64_t* k_stride, const int64_t* v_stride,
+                       const int32_t* pos, const tq_pages* pages, int32_t L_cap, const float* rope_cos,
+                       const float* rope_sin, int32_t rope_npos, const tq_packed* kout, const tq_packed* vout,
+                       void* stream) {
+    if (!pos) return fail(TQ_EINVAL, "null pos");
+    PageRef pg;
+    int64_t cap = 0;
+    if (pages) {
+        tq_status st = check_pages(pages, &pg);
+        if (st) return st;
+        cap = pg.n_pages * h_kv * (int64_t)pg.size;
+        L_cap = 0;
+    } else {
+        if (L_cap <= 0) return fail(TQ_EINVAL, "L_cap must be positive without a page table");
+        cap = (int64_t)B * h_kv * L_cap;
+    }
+    if ((int64_t)B * h_kv >= ((int64_t)1 << 31)) return fail(TQ_EUNSUPPORTED, "too many vectors in one append");
+    const int64_t ks[3] = {k_stride ? k_stride[0] : 0, 0, k_stride ? k_stride[1] : 0};
+    const int64_t vs[3] = {v_stride ? v_stride[0] : 0, 0, v_stride ? v_stride[1] : 0};
+    return encode_common(ck, cv, k, v, dtype, B, 1, h_kv, k_stride ? ks : nullptr, v_stride ? vs : nullptr, 0, L_cap,
+                         pg, pos, rope_cos, rope_sin, rope_npos, kout, vout, cap, nullptr, 0, stream);
+}
+
+tq_status tq_attn_logits(const tq_codebook* ck, const void* q, int32_t q_dtype, const tq_packed* k,
+                         int32_t B, int32_t Hq, int32_t h_kv, int32_t L_cap, const int32_t* seq_len,
+                         const float* rope_cos, const float* rope_sin, int32_t rope_npos,
+                         int32_t top_k, float* out, int32_t* topk_idx, void* ws, size_t ws_bytes,
+                         void* stream) {
+    return logits_common(ck, q, q_dtype, k, B, Hq, h_kv, L_cap, seq_len, PageRef{}, (int64_t)B * h_kv * L_cap,
+                         rope_cos, rope_sin, rope_npos, top_k, out, topk_idx, ws, ws_bytes, stream);
+}
+
+tq_status tq_attn_logits_paged(const tq_codebook* ck, const void* q, int32_t q_dtype, const tq_packed* k, int32_t B,
+                               int32_t Hq, int32_t h_kv, const int32_t* seq_len, const tq_pages* pages,
+                               const float* rope_cos, const float* rope_sin, int32_t rope_npos, int32_t top_k,
+                               float* out, int32_t* topk_idx, void* ws, size_t ws_bytes, void* stream) {
+    PageRef pg;
+    tq_status st = check_pages(pages, &pg);
+    if (st) return st;
+    return logits_common(ck, q, q_dtype, k, B, Hq, h_kv, pg.max_pages * pg.size, seq_len, pg,
+                         pg.n_pages * h_kv * (int64_t)pg.size, rope_cos, rope_sin, rope_npos, top_k, out, topk_idx, ws,
+                         ws_bytes, stream);
+}
+
+tq_status tq_attn_decode(const tq_codebook* ck, const tq_codebook* cv, const void* q, int32_t q_dtype,
+                         const tq_packed* k, const tq_packed* v, int32_t B, int32_t Hq, int32_t h_kv,
+                         int32_t L_cap, const int32_t* seq_len, const float* rope_cos,
+                         const float* rope_sin, int32_t rope_npos, float scale, float* out,
+                         void* ws, size_t ws_bytes, void* stream) {
+    return decode_common(ck, cv, q, q_dtype, k, v, B, Hq, h_kv, L_cap, seq_len, PageRef{}, (int64_t)B * h_kv * L_cap,
+                         rope_cos, rope_sin, rope_npos, scale, out, ws, ws_bytes, stream);
+}
+
+tq_status tq_attn_decode_paged(const tq_codebook* ck, const tq_codebook* cv, const void* q, int32_t q_dtype,
+                               const tq_packed* k, const tq_packed* v, int32_t B, int32_t Hq, int32_t h_kv,
+                               const int32_t* seq_len, const tq_pages* pages, const float* rope_cos,
+                               const float* rope_sin, int32_t rope_npos, float scale, float* out, void* ws,
+                               size_t ws_bytes, void* stream) {
+    PageRef pg;
+    tq_status st = check_pages(pages, &pg);
+    if (st) return st;
+    return decode_common(ck, cv, q, q_dtype, k, v, B, Hq, h_kv, pg.max_pages * pg.size, seq_len, pg,
+                         pg.n_pages * h_kv * (int64_t)pg.size, rope_cos, rope_sin, rope_npos, scale, out, ws, ws_bytes,
+                         stream);
 }
 
 size_t tq_workspace_bytes(const tq_codebook* ck, const tq_codebook* cv, int32_t op, int64_t B,

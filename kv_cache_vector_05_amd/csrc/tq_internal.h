@@ -85,6 +85,13 @@ uint16_t f32_to_f16(float f);
 float f16_to_f32(uint16_t h);
 
 // ---- kernel launchers (tq_encode.hip, tq_attn.hip, tq_gemm.hip) ----
+// paged records: table [B][max_pages] of physical pages of `size` slots
+// (table == nullptr: contiguous records of L_cap slots per (sequence, head))
+struct PageRef {
+    const int32_t* table = nullptr;
+    int32_t size = 0, max_pages = 0;
+    int64_t n_pages = 0;
+};
 struct EncodeArgs {
     const void* x;
     int64_t s_seq, s_tok, s_head;
@@ -95,6 +102,10 @@ struct EncodeArgs {
     tq_packed out;
     void* ws;  // dense form only
     size_t ws_bytes;
+    int32_t append = 0;           // one token per (sequence, head) at slot pos[sequence]
+    const int32_t* pos = nullptr;
+    int32_t rope_npos = 0;
+    PageRef pages;
 };
 hipError_t launch_encode(const tq_codebook* cb, const EncodeArgs& a, hipStream_t stream);
 size_t encode_workspace_bytes(const tq_codebook* cb, int64_t n_vectors);
@@ -112,6 +123,7 @@ struct AttnArgs {
     int32_t* topk_idx;
     void* ws;
     size_t ws_bytes;
+    PageRef pages;
 };
 hipError_t launch_logits(const tq_codebook* ck, const tq_packed& k, const AttnArgs& a,
                          hipStream_t stream);

@@ -217,9 +217,26 @@ struct LogM {
     double cq;           // scale of the correction term
     const float* mu;     // sign correction: mu per KV head (stride mu_stride), else nullptr
     int32_t mu_stride;
+    // paged records: page table [B][max_pages] of pages of page_size slots
+    // (a multiple of 64); entries are clamped into [0, n_pages)
+    const int32_t* pages;
+    int32_t page_size, max_pages;
+    int64_t n_pages;
+    dev::FastDiv div_page;
 };
 
-template <int D, int BITS, int NRT, int NCS>
+// Record index of key `key` of (sequence b, KV head kh) through the page table
+// (key0: a wave-uniform key of the same page, from which the page is found).
+__device__ __forceinline__ int64_t paged_record(const int32_t* pages, int32_t page_size, int32_t max_pages,
+                                                int64_t n_pages, const dev::FastDiv& div_page, int h_kv, int b, int kh,
+                                                int key) {
+    const uint32_t j = div_page.div((uint32_t)key);
+    int64_t pg = pages[(int64_t)b * max_pages + j];
+    pg = pg < 0 ? 0 : (pg >= n_pages ? n_pages - 1 : pg);
+    return (pg * h_kv + kh) * page_size + (key - (int64_t)j * page_size);
+}
+
+template <int D, int BITS, int NRT, int NCS, bool PAGED>
 __global__ __launch_bounds__(256) void logits_mfma_kernel(LogM p) {
     using T = dev::TileLogit<D, BITS, NRT, NCS>;
     using Q = typename T::Q;
@@ -270,7 +287,21 @@ __global__ __launch_bounds__(256) void logits_mfma_kernel(LogM p) {
     typename T::Raw rs[4];
     float nus[4], gms[4];
     auto fetch = [&](int tile, int slot) {
-        if (tile < nfull) {  // uniform record offset
+        if constexpr (PAGED) {
+            // a full tile's 16 keys share one page (wave-uniform lookup); a
+            // partial last tile reads the record of its last valid key instead
+            int64_t rec;
+            if (tile < nfull) {
+                const int key0 = __builtin_amdgcn_readfirstlane(kbeg + tile * 16);
+                rec = paged_record(p.pages, p.page_size, p.max_pages, p.n_pages, p.div_page, p.h_kv, b, kh, key0) + n;
+            } else {
+                const int key = min(kbeg + tile * 16 + n, kend - 1);
+                rec = paged_record(p.pages, p.page_size, p.max_pages, p.n_pages, p.div_page, p.h_kv, b, kh, key);
+            }
+            T::load(p.codes + rec * Q::CW + Q::word0(qk), p.signs + rec * mw, per, lane, rs[slot]);
+            nus[slot] = p.norm[rec];
+            gms[slot] = NCS > 0 ? (g_per_key ? p.rnorm[rec] : g_head) : 0.0f;
+        } else if (tile < nfull) {  // uniform record offset
             const int off = tile * 16;
             T::load(cptr + off * Q::CW, sptr + off * mw, per, lane, rs[slot]);
             nus[slot] = nptr[off];
@@ -317,29 +348,29 @@ __global__ __launch_bounds__(256) void logits_mfma_kernel(LogM p) {
 
 using LogMFn = void (*)(LogM);
 
-template <int D, int BITS, int NRT>
+template <int D, int BITS, int NRT, bool PG>
 LogMFn pick_ncs(int m) {
     const int ncs = m == 0 ? 0 : std::max(1, m / 64);
     switch (ncs) {
-        case 0: return logits_mfma_kernel<D, BITS, NRT, 0>;
-        case 1: return logits_mfma_kernel<D, BITS, NRT, 1>;
-        case 2: return logits_mfma_kernel<D, BITS, NRT, 2>;
+        case 0: return logits_mfma_kernel<D, BITS, NRT, 0, PG>;
+        case 1: return logits_mfma_kernel<D, BITS, NRT, 1, PG>;
+        case 2: return logits_mfma_kernel<D, BITS, NRT, 2, PG>;
     }
     return nullptr;
 }
-template <int D, int BITS>
+template <int D, int BITS, bool PG>
 LogMFn pick_nrt(int nrt, int m) {
-    if (nrt == 1) return pick_ncs<D, BITS, 1>(m);
-    if (nrt == 2) return pick_ncs<D, BITS, 2>(m);
-    if (nrt == 4) return pick_ncs<D, BITS, 4>(m);
+    if (nrt == 1) return pick_ncs<D, BITS, 1, PG>(m);
+    if (nrt == 2) return pick_ncs<D, BITS, 2, PG>(m);
+    if (nrt == 4) return pick_ncs<D, BITS, 4, PG>(m);
     return nullptr;
 }
-template <int D>
+template <int D, bool PG>
 LogMFn pick_bits_m(int bits, int nrt, int m) {
     switch (bits) {
-        case 1: return pick_nrt<D, 1>(nrt, m);
-        case 2: return pick_nrt<D, 2>(nrt, m);
-        case 3: return pick_nrt<D, 3>(nrt, m);
+        case 1: return pick_nrt<D, 1, PG>(nrt, m);
+        case 2: return pick_nrt<D, 2, PG>(nrt, m);
+        case 3: return pick_nrt<D, 3, PG>(nrt, m);
     }
     return nullptr;
 }
@@ -428,8 +459,11 @@ hipError_t launch_logits_mfma(const tq_codebook* ck, const tq_packed& k, const A
     const int nrt = G <= 4 ? 1 : (G <= 8 ? 2 : 4);
     const int ngroups = (G + 4 * nrt - 1) / (4 * nrt);
     LogMFn fn = nullptr;
-    if (ck->spec.d == 64) fn = pick_bits_m<64>(ck->spec.bits, nrt, ck->spec.m);
-    else if (ck->spec.d == 128) fn = pick_bits_m<128>(ck->spec.bits, nrt, ck->spec.m);
+    const bool paged = a.pages.table != nullptr;
+    if (ck->spec.d == 64)
+        fn = paged ? pick_bits_m<64, true>(ck->spec.bits, nrt, ck->spec.m) : pick_bits_m<64, false>(ck->spec.bits, nrt, ck->spec.m);
+    else if (ck->spec.d == 128)
+        fn = paged ? pick_bits_m<128, true>(ck->spec.bits, nrt, ck->spec.m) : pick_bits_m<128, false>(ck->spec.bits, nrt, ck->spec.m);
     if (!fn) return hipErrorInvalidValue;
     LogM p{};
     p.qd = q.qd;
@@ -457,6 +491,11 @@ hipError_t launch_logits_mfma(const tq_codebook* ck, const tq_packed& k, const A
     const MuRef mr = mu_ref(ck);
     p.mu = mr.ptr;
     p.mu_stride = mr.stride;
+    p.pages = a.pages.table;
+    p.page_size = a.pages.size;
+    p.max_pages = a.pages.max_pages;
+    p.n_pages = a.pages.n_pages;
+    p.div_page = dev::FastDiv((uint32_t)(a.pages.size > 0 ? a.pages.size : 1));
     // Size the work per wave so that the whole grid is resident at once (one
     // round of workgroups, no partly idle last round).
     const int64_t gx = (int64_t)a.B * a.h_kv * ngroups;

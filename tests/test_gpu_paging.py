@@ -1,0 +1,219 @@
+"""GPU parity for the growing cache: paged records (encode, logits and
+decode through a page table), autoregressive appends (one token per
+(sequence, head) at per-sequence slots), against the oracle's layouts in
+oracle/paging.py."""
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import codec, estimator, paging, rope as orope
+
+import parity
+from test_gpu_parity import bf16_tensor, codebooks, stored
+
+torch = pytest.importorskip("torch")
+tq = pytest.importorskip("kv_cache_vector_05_amd")
+
+pytestmark = pytest.mark.gpu
+
+
+def make_codebooks(kind, d, bits):
+    if kind == "sign":
+        sk = synth.codec_draws(d, 0, False, 5)[0]
+        sv = synth.codec_draws(d, 0, False, 6)[0]
+        mu = np.array([0.011, 0.014], np.float32)
+        ock = codec.make_sign_codebook(d, bits, "hadamard", sigma=sk, mu=mu)
+        ocv = codec.make_sign_codebook(d, bits, "none", mu=mu[::-1].copy())
+        gck = tq.Codebook(d, bits, d, "hadamard", sigma=sk, correction="sign", mu=mu)
+        gcv = tq.Codebook(d, bits, d, "none", correction="sign", mu=mu[::-1].copy())
+        return ock, gck, ocv, gcv
+    ock, gck = codebooks(d, bits, 64, False, 5)
+    ocv, gcv = codebooks(d, bits, 64, False, 6)
+    return ock, gck, ocv, gcv
+
+
+def pool_packed(gcb, pool):
+    return tq.Packed.from_arrays(gcb, pool["norm"], pool["rnorm"], pool["codes"], pool["signs"])
+
+
+def page_table(g, B, max_pages, n_pages):
+    perm = g.permutation(n_pages)[:B * max_pages].astype(np.int32).reshape(B, max_pages)
+    return perm
+
+
+@pytest.mark.parametrize("kind", ["qjl", "sign"])
+def test_paged_logits_and_decode(kind):
+    """Records scattered over a shuffled pool of pages: paged logits and
+    decode equal the oracle's over each sequence's own tokens; page entries
+    past seq_len that point outside the pool are never dereferenced."""
+    B, H, Hq, d, bits, P, J = 3, 2, 8, 128, 3, 64, 10
+    n_pages = B * J + 6
+    lens = [300, 517, 64]
+    g = synth.rng(41)
+    ock, gck, ocv, gcv = make_codebooks(kind, d, bits)
+    pages = page_table(g, B, J, n_pages)
+    # entries beyond each sequence's last page: out of the pool (must not be read)
+    for b in range(B):
+        pages[b, (lens[b] + P - 1) // P:] = 10 ** 6
+    kpool, vpool = paging.empty_pool(ock, n_pages * H * P), paging.empty_pool(ocv, n_pages * H * P)
+    rope_o = orope.rope_table(5e5, d, J * P + 1)
+    for b in range(B):
+        for h in range(H):
+            t = np.arange(lens[b])
+            ek = codec.encode(ock, g.standard_normal((lens[b], d)), pos=t, rope=rope_o)
+            ev = codec.encode(ocv, g.standard_normal((lens[b], d)))
+            idx = paging.paged_index(pages, P, H, b, h, t)
+            paging.write(kpool, idx, stored(ek))
+            paging.write(vpool, idx, stored(ev))
+    pg = tq.Pages(torch.from_numpy(pages).cuda(), P, n_pages)
+    kp, vp = pool_packed(gck, kpool), pool_packed(gcv, vpool)
+    Q = g.standard_normal((B, Hq, d)).astype(np.float32)
+    qt = torch.from_numpy(Q).cuda()
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    rope_g = tq.rope_table(5e5, d, J * P + 1)
+    cap = J * P
+    lg = tq.attn_logits(gck, qt, kp, H, None, sl, rope=rope_g, pages=pg,
+                        out=torch.full((B, Hq, cap), float("nan"), device="cuda")).cpu().numpy()
+    out = tq.attn_decode(gck, gcv, qt, kp, vp, H, None, sl, rope=rope_g, pages=pg).cpu().numpy()
+    vals, tidx = tq.attn_logits(gck, qt, kp, H, None, sl, rope=rope_g, pages=pg, top_k=5)
+    vals, tidx = vals.cpu().numpy(), tidx.cpu().numpy()
+    G = Hq // H
+    for b in range(B):
+        qp, s = estimator.prep_query(ock, Q[b], lens[b], rope_o)
+        for h in range(H):
+            t = np.arange(lens[b])
+            ek = paging.gather(kpool, paging.paged_index(pages, P, H, b, h, t))
+            ev = paging.gather(vpool, paging.paged_index(pages, P, H, b, h, t))
+            gs = slice(h * G, (h + 1) * G)
+            ref = estimator.logits(ock, qp[gs], s[gs], ek, h)
+            parity.assert_close(lg[b, gs, :lens[b]], ref, f"paged {kind} logits b={b} h={h}")
+            assert np.all(np.isnan(lg[b, gs, lens[b]:]))
+            ref_o = estimator.attention(ock, ocv, qp[gs], s[gs], ek, ev, lens[b], 1.0 / math.sqrt(d), h)
+            parity.assert_close(out[b, gs], ref_o, f"paged {kind} decode b={b} h={h}")
+            for r in range(G):
+                parity.assert_close(vals[b, h * G + r], ref[r, tidx[b, h * G + r]], f"paged top-k b={b}")
+                kth = np.sort(ref[r])[::-1][4]
+                assert np.all(ref[r, tidx[b, h * G + r]] >= kth - (parity.ATOL + parity.RTOL * abs(kth)))
+
+
+@pytest.mark.parametrize("kind", ["qjl", "sign"])
+def test_paged_encode(kind):
+    """A bulk encode into paged records at a token offset (pages crossed
+    mid-tile): records equal the oracle's, every other slot keeps its
+    sentinel."""
+    B, T, H, d, bits, P, J, off = 2, 150, 4, 128, 3, 64, 4, 37
+    n_pages = B * J + 3
+    g = synth.rng(42)
+    ock, gck, _, _ = make_codebooks(kind, d, bits)
+    pages = page_table(g, B, J, n_pages)
+    X = g.standard_normal((B, T, H, d)).astype(np.float32)
+    xb = synth.bf16_round_bits(X)
+    X = synth.bf16_bits_to_f32(xb)
+    rope_g = tq.rope_table(1e4, d, J * P)
+    rope_o = orope.rope_table(1e4, d, J * P)
+    pg = tq.Pages(torch.from_numpy(pages).cuda(), P, n_pages)
+    kp = tq.Packed(gck, pg.records(H))
+    kp.norm.fill_(-5.0)
+    tq.encode_kv(gck, None, bf16_tensor(xb), None, kp, None, tok_offset=off, rope=rope_g, pages=pg)
+    torch.cuda.synchronize()
+    got = kp.numpy()
+    written = np.zeros(len(got[0]), bool)
+    for b in range(B):
+        for h in range(H):
+            t = off + np.arange(T)
+            idx = paging.paged_index(pages, P, H, b, h, t)
+            written[idx] = True
+            enc = codec.encode(ock, X[b, :, h], pos=t, rope=rope_o)
+            parity.compare_encoded(ock, enc, tuple(a[idx] if len(a) else a for a in got), f"paged encode b={b} h={h}")
+    assert np.all(got[0][~written] == -5.0)
+
+
+@pytest.mark.parametrize("kind", ["qjl", "sign"])
+def test_autoregressive_appends_through_pages(kind):
+    """150 steps of one token per (sequence, head), sequences starting at
+    different steps (negative slots are skipped), bf16 keys with RoPE at each
+    token's slot; every 30 steps a paged decode at each sequence's current
+    length; at the end every record equals the oracle's appends."""
+    B, H, Hq, d, bits, P, J, steps = 3, 2, 4, 128, 3, 64, 3, 150
+    n_pages = B * J + 3
+    start = np.array([0, 7, 40])
+    g = synth.rng(43)
+    ock, gck, ocv, gcv = make_codebooks(kind, d, bits)
+    pages = page_table(g, B, J, n_pages)
+    pg = tq.Pages(torch.from_numpy(pages).cuda(), P, n_pages)
+    kp, vp = tq.Packed(gck, pg.records(H)), tq.Packed(gcv, pg.records(H))
+    kpool, vpool = paging.empty_pool(ock, pg.records(H)), paging.empty_pool(ocv, pg.records(H))
+    rope_g = tq.rope_table(5e5, d, J * P + 1)
+    rope_o = orope.rope_table(5e5, d, J * P + 1)
+    K = synth.bf16_round_bits(g.standard_normal((steps, B, H, d)).astype(np.float32))
+    V = synth.bf16_round_bits(g.standard_normal((steps, B, H, d)).astype(np.float32))
+    Q = g.standard_normal((B, Hq, d)).astype(np.float32)
+    index_of = lambda b, h, t: paging.paged_index(pages, P, H, b, h, t)
+    G = Hq // H
+    for s in range(steps):
+        pos = (s - start).astype(np.int32)
+        tq.append_kv(gck, gcv, bf16_tensor(K[s]), bf16_tensor(V[s]), kp, vp,
+                     torch.from_numpy(pos).cuda(), pages=pg, rope=rope_g)
+        live = np.nonzero(pos >= 0)[0]
+        kf, vf = synth.bf16_bits_to_f32(K[s]), synth.bf16_bits_to_f32(V[s])
+        for b in live:
+            paging.append(ock, kpool, kf[b:b + 1], pos[b:b + 1], lambda bb, h, t: index_of(bb + b, h, t), rope=rope_o)
+            paging.append(ocv, vpool, vf[b:b + 1], pos[b:b + 1], lambda bb, h, t: index_of(bb + b, h, t))
+        if (s + 1) % 30 == 0:
+            lens = np.maximum(pos + 1, 0)
+            out = tq.attn_decode(gck, gcv, torch.from_numpy(Q).cuda(), kp, vp, H, None,
+                                 torch.from_numpy(lens.astype(np.int32)).cuda(), rope=rope_g, pages=pg).cpu().numpy()
+            # the decode reads the GPU's own records; compare with the oracle over them
+            gk, gv = kp.numpy(), vp.numpy()
+            for b in range(B):
+                qp, sq = estimator.prep_query(ock, Q[b], int(lens[b]), rope_o)
+                for h in range(H):
+                    idx = index_of(b, h, np.arange(lens[b]))
+                    ek = codec.Encoded(gk[0][idx].astype(np.float64), gk[1][idx].astype(np.float64) if len(gk[1]) else
+                                       np.zeros(len(idx)), gk[2][idx], gk[3][idx])
+                    ev = codec.Encoded(gv[0][idx].astype(np.float64), gv[1][idx].astype(np.float64) if len(gv[1]) else
+                                       np.zeros(len(idx)), gv[2][idx], gv[3][idx])
+                    ref = estimator.attention(ock, ocv, qp[h * G:(h + 1) * G], sq[h * G:(h + 1) * G], ek, ev,
+                                              int(lens[b]), 1.0 / math.sqrt(d), h)
+                    parity.assert_close(out[b, h * G:(h + 1) * G], ref, f"append {kind} step {s} b={b} h={h}")
+    torch.cuda.synchronize()
+    # every appended record against the oracle's encode of that sequence's
+    # tokens at their slots (codes and signs by the boundary protocol), and
+    # the oracle's own appends leave exactly those records
+    for name, gpk, pool, cb, X, rope in (("K", kp, kpool, ock, K, rope_o), ("V", vp, vpool, ocv, V, None)):
+        got = gpk.numpy()
+        for b in range(B):
+            t = np.arange(steps - start[b])
+            x = synth.bf16_bits_to_f32(X[start[b] + t, b])
+            for h in range(H):
+                idx = index_of(b, h, t)
+                enc = codec.encode(cb, x[:, h], pos=t if rope is not None else None, rope=rope)
+                parity.compare_encoded(cb, enc, tuple(a[idx] if len(a) else a for a in got), f"append {name} b={b}")
+                np.testing.assert_array_equal(pool["codes"][idx], enc.codes)
+
+
+def test_contiguous_appends_and_out_of_range_slots():
+    """Appends into contiguous records (no page table): each sequence's token
+    lands at its own slot; slots at or past L_cap and negative slots are
+    skipped without touching anything."""
+    B, H, d, L = 4, 3, 64, 100
+    g = synth.rng(44)
+    ock, gck = codebooks(d, 3, 64, False, 7)
+    kp = tq.Packed(gck, B * H * L)
+    kp.norm.fill_(-2.0)
+    X = g.standard_normal((B, H, d)).astype(np.float32)
+    pos = np.array([5, 99, 100, -3], np.int32)
+    tq.append_kv(gck, None, torch.from_numpy(X).cuda(), None, kp, None, torch.from_numpy(pos).cuda(), L_cap=L)
+    torch.cuda.synchronize()
+    got = kp.numpy()
+    nrm = got[0].reshape(B, H, L)
+    for b in range(2):
+        idx = paging.contiguous_index(b, np.arange(H), pos[b], H, L)
+        enc = codec.encode(ock, X[b])
+        parity.compare_encoded(ock, enc, tuple(a[idx] for a in got), f"contiguous append b={b}")
+        others = np.ones(L, bool)
+        others[pos[b]] = False
+        assert np.all(nrm[b][:, others] == -2.0)
+    assert np.all(nrm[2:] == -2.0)

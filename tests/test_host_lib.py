@@ -157,3 +157,23 @@ def test_forced_allocation_failure_reports_enomem(monkeypatch):
     h = C.c_void_p()
     assert tq.lib().tq_codebook_init(C.byref(sp), None, None, C.byref(h)) == _lib.TQ_ENOMEM
     assert not h.value
+
+
+def test_paged_and_append_calls_reject_bad_arguments_without_a_gpu():
+    """Page tables and appends are checked on the host before any launch."""
+    L = tq.lib()
+    sp = _lib.tq_spec(64, 2, 32, 0, 0)
+    for size, maxp, npg in [(48, 4, 8), (0, 4, 8), (64, 0, 8), (64, 4, 0), (64, 1 << 25, 8)]:
+        pg = _lib.tq_pages(1, size, maxp, npg)
+        assert L.tq_attn_logits_paged(None, None, 0, None, 1, 1, 1, None, C.byref(pg), None, None, 0, 0, None,
+                                      None, None, 0, None) == _lib.TQ_EINVAL
+    pg = _lib.tq_pages(None, 64, 4, 8)
+    assert L.tq_attn_decode_paged(None, None, None, 0, None, None, 1, 1, 1, None, C.byref(pg), None, None, 0, 0.0,
+                                  None, None, 0, None) == _lib.TQ_EINVAL
+    assert L.tq_encode_kv_paged(None, None, None, None, 0, 1, 1, 1, None, None, 0, None, None, None, 0, None, None,
+                                None) == _lib.TQ_EINVAL
+    # append: no positions, or no page table and no capacity
+    assert L.tq_append_kv(None, None, None, None, 0, 1, 1, None, None, None, None, 8, None, None, 0, None, None,
+                          None) == _lib.TQ_EINVAL
+    assert L.tq_append_kv(None, None, None, None, 0, 1, 1, None, None, C.c_void_p(16), None, 0, None, None, 0, None,
+                          None, None) == _lib.TQ_EINVAL
