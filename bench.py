@@ -76,7 +76,7 @@ def parse():
                          "GPU's clocks take some 100 ms of load to settle)")
     ap.add_argument("--workload", default="llama8b",
                     choices=["llama8b", "llama70b", "esm650m", "vsearch", "llama8b-turboesm", "esm650m-turboesm",
-                             "tiny"])
+                             "llama8b-serve", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="keys in the oracle's sample (0: default)")
     return ap.parse_args()
@@ -226,6 +226,113 @@ def llama_report(st, timer, ms_step):
     else:
         cfg["qjl_rows"] = m
     return keys / (ms_step * 1e-3), "keys/s", kern, dom, extra, cfg
+
+
+# ------------------------------------------------------------ serving step
+PAGE = 256  # slots per page of the paged cache
+
+
+def setup_serve(torch, tq, synth):
+    """One autoregressive step of the Llama-3.1-8B-shaped layer over a paged
+    cache: the cache holds L - 1 tokens per sequence, spread over a shuffled
+    pool of pages; a step appends token L - 1 (keys and values of every
+    (sequence, KV head)) and runs the fused decode over the L tokens."""
+    B, Hq, H, L, d, bits, m, rope_base = 8, 32, 8, 32768, 128, 3, 64, 5e5
+    K, V = synth.llama_kv_inputs("llama8b", seed=0, batch=B, ctx=L, hkv=H, d=d)
+    Q = synth.llama_q_inputs(seed=100, batch=B, hq=Hq, d=d)
+    st = {"B": B, "Hq": Hq, "H": H, "L": L, "d": d, "bits": bits, "m": m, "rope_base": rope_base,
+          "variant": "qjl", "host": (K, V, Q)}
+    J = L // PAGE
+    n_pages = B * J
+    table = synth.rng(3).permutation(n_pages).astype(np.int32).reshape(B, J)
+    st["pages"] = tq.Pages(torch.from_numpy(table).cuda(), PAGE, n_pages)
+    st["ck"] = tq.Codebook(d, bits, m, "hadamard", seed=synth.K_SEED)
+    st["cv"] = tq.Codebook(d, bits, m, "hadamard", seed=synth.V_SEED)
+    st["kp"] = tq.Packed(st["ck"], st["pages"].records(H))
+    st["vp"] = tq.Packed(st["cv"], st["pages"].records(H))
+    st["rope"] = tq.rope_table(rope_base, d, L + 1)
+    Kd, Vd = bf16_dev(torch, K), bf16_dev(torch, V)
+    # prefill: the first L - 1 tokens
+    tq.encode_kv(st["ck"], st["cv"], Kd[:, :L - 1], Vd[:, :L - 1], st["kp"], st["vp"], rope=st["rope"],
+                 pages=st["pages"])
+    st["K1"], st["V1"] = Kd[:, L - 1].contiguous(), Vd[:, L - 1].contiguous()
+    st["pos"] = torch.full((B,), L - 1, dtype=torch.int32, device="cuda")
+    st["sl"] = torch.full((B,), L, dtype=torch.int32, device="cuda")
+    st["Q"] = bf16_dev(torch, Q)
+    st["out"] = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    st["ws_d"] = torch.empty(max(1, tq.workspace_bytes(st["ck"], st["cv"], tq.TQ_OP_DECODE, B, Hq, H, L, 0)),
+                             dtype=torch.uint8, device="cuda")
+    st["calls"] = [
+        ("append", tq.append_kv(st["ck"], st["cv"], st["K1"], st["V1"], st["kp"], st["vp"], st["pos"],
+                                pages=st["pages"], rope=st["rope"], prepare=True)),
+        ("decode", tq.attn_decode(st["ck"], st["cv"], st["Q"], st["kp"], st["vp"], H, None, st["sl"], rope=st["rope"],
+                                  out=st["out"], workspace=st["ws_d"], prepare=True, pages=st["pages"])[0]),
+    ]
+    return st
+
+
+def serve_report(st, timer, ms_step):
+    B, Hq, H, L, d, bits, m = (st[k] for k in ("B", "Hq", "H", "L", "d", "bits", "m"))
+    keys = B * H * L
+    rec = 8 + bits * d // 8 + m // 8
+    app_ms, n = timer.mean_ms("append")
+    dec_ms, _ = timer.mean_ms("decode")
+    kern = {"append": {"ms": app_ms, "launches": n, "alg_bytes": 2 * B * H * (2 * d + rec), "units": 2 * B * H},
+            "decode": {"ms": dec_ms, "alg_bytes": keys * 2 * rec, "units": keys}}
+    for k in kern.values():
+        k["GBps"] = k["alg_bytes"] / (k["ms"] * 1e-3) / 1e9
+        k["hbm_frac"] = k["GBps"] / HBM_PEAK_GBS
+    extra = {"decode_keys_per_s": keys / (dec_ms * 1e-3), "append_us": app_ms * 1e3, "decode_us": dec_ms * 1e3,
+             "tokens_per_s": B / (ms_step * 1e-3)}
+    cfg = {"workload": "Llama-3.1-8B-shaped decode step over a paged cache (append + fused decode)", "batch": B,
+           "q_heads": Hq, "kv_heads": H, "head_dim": d, "context": L, "bits": bits, "qjl_rows": m,
+           "input_dtype": "bf16", "rope_base": st["rope_base"], "record_bytes": rec, "page_size": PAGE,
+           "pages": B * (L // PAGE), "page_order": "shuffled"}
+    return keys / (ms_step * 1e-3), "keys/s", kern, "decode", extra, cfg
+
+
+def cpu_baseline_serve(st, budget_s=8.0):
+    """The oracle on a bounded sample of the serving step: whole (sequence,
+    KV head) pairs in order, each cache encoded beforehand (untimed), then
+    timed: the append of the pair's new key and value and the decode of its
+    G query heads over all L keys, until about budget_s seconds."""
+    import synth
+    from oracle import codec, estimator, rope as orope
+    K, V, Q = st["host"]
+    B, Hq, H, L, d, bits, m = (st[k] for k in ("B", "Hq", "H", "L", "d", "bits", "m"))
+    G = Hq // H
+    ock = codec.make_codebook(d, bits, m, False, seed=synth.K_SEED)
+    ocv = codec.make_codebook(d, bits, m, False, seed=synth.V_SEED)
+    rope = orope.rope_table(st["rope_base"], d, L + 1)
+    done, pairs, dt = 0, 0, 0.0
+    for b in range(B):
+        for kh in range(H):
+            if dt >= budget_s:
+                break
+            kx = synth.bf16_bits_to_f32(K[b, :, kh])
+            vx = synth.bf16_bits_to_f32(V[b, :, kh])
+            ek = codec.encode(ock, kx[:L - 1], pos=np.arange(L - 1), rope=rope)
+            ev = codec.encode(ocv, vx[:L - 1])
+            q = synth.bf16_bits_to_f32(Q[b, kh * G:(kh + 1) * G])
+            t1 = time.perf_counter()
+            nk = codec.encode(ock, kx[L - 1:], pos=np.array([L - 1]), rope=rope)
+            nv = codec.encode(ocv, vx[L - 1:])
+            cat = lambda e, n: codec.Encoded(np.concatenate([e.norm, n.norm]), np.concatenate([e.rnorm, n.rnorm]),
+                                             np.concatenate([e.codes, n.codes]), np.concatenate([e.signs, n.signs]))
+            qp, s = estimator.prep_query(ock, q, L, rope)
+            estimator.attention(ock, ocv, qp, s, cat(ek, nk), cat(ev, nv), L, 1 / math.sqrt(d))
+            dt += time.perf_counter() - t1
+            done += L
+            pairs += 1
+    try:
+        import threadpoolctl
+        threads = max(p["num_threads"] for p in threadpoolctl.threadpool_info()) or 1
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    return {"value": done / dt, "unit": "keys/s", "cores": threads, "kind": "oracle",
+            "sample": f"{pairs} (sequence, KV head) pairs: the append of one key and value and the decode of "
+                      f"{G} query heads over {L} cached keys each, {dt:.1f} s on the host (the caches encoded "
+                      f"beforehand, untimed)"}
 
 
 def cpu_baseline_llama(st, sample_keys, budget_s=12.0):
@@ -461,6 +568,9 @@ def main():
     elif wl == "vsearch":
         st = setup_vsearch(torch, tq, synth)
         report = lambda t, ms: vsearch_report(st, t, ms)
+    elif wl == "llama8b-serve":
+        st = setup_serve(torch, tq, synth)
+        report = lambda t, ms: serve_report(st, t, ms)
     else:
         raise SystemExit("tiny is a parity case, not a benchmark workload")
     step = lambda t: run_calls(st, t)
@@ -505,7 +615,10 @@ def main():
             "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "f32", "data": "synthetic", "config": cfg, "roofline": roof,
             "kernels": kern, **extra}
-    if not args.no_cpu_baseline and wl in ("llama8b", "llama70b", "llama8b-turboesm"):
+    if not args.no_cpu_baseline and wl == "llama8b-serve":
+        print("[bench] cpu baseline (oracle on a sample)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline_serve(st)
+    elif not args.no_cpu_baseline and wl in ("llama8b", "llama70b", "llama8b-turboesm"):
         print("[bench] cpu baseline (oracle on a sample)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline_llama(st, args.cpu_sample or 1 << 22)
     elif not args.no_cpu_baseline and wl in ("esm650m", "esm650m-turboesm"):
