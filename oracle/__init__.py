@@ -37,5 +37,5 @@ Parity status of each function is stated in its docstring; every function is
 pinned by the CPU tests in ``tests/test_oracle_*.py`` except where a
 docstring says "parity unpinned".
 """
-from . import rng, lloyd_max, rotation, rope, codec, estimator, calibration, paging  # noqa: F401
+from . import rng, lloyd_max, rotation, rope, codec, estimator, calibration, paging, fibquant  # noqa: F401
 from .codec import Codebook, make_codebook, encode, dequant  # noqa: F401
