@@ -51,6 +51,8 @@
  *   norm [n]          float    nu = ||x||_2 (after RoPE for keys)
  *   rnorm[n]          float    gamma = ||y - t[c]||_2 (absent when m == 0
  *                              and for TQ_CORR_SIGN codebooks)
+ *   (vector codebooks: codes[n][ceil(bits * d / block / 32)], the index of
+ *   block j at bits [j*bits, (j+1)*bits) LSB first; no rnorm or signs)
  *   codes[n][b*d/32]  uint32   code 0 is the most negative level; bit k of
  *                              the words' bit string is bit k%32 of word k/32.
  *                              b = 1, 2, 4: coordinate i's code is bits
@@ -110,12 +112,21 @@ enum { TQ_OP_ENCODE = 0, TQ_OP_LOGITS = 1, TQ_OP_DECODE = 2 };     /* workspace 
  *            plane, and the correction is mu z with mu the codebook's mean
  *            residual magnitude of the record's KV head.  Needs d = 64 or
  *            128, bits 1..3, rotation Hadamard or none.
- *   reserved must be 0.
+ *   block    0 or 1: a scalar Lloyd-Max table per coordinate (the above).
+ *            2 or 3: a FibQuant vector codebook (FibQuant summary, section
+ *            2): N = 2^bits codewords (bits 1..8) for blocks of `block`
+ *            consecutive rotated coordinates, built offline for the
+ *            spherical-Beta law of such a block (Bennett-Gersho radii,
+ *            golden-spiral / Fibonacci-sphere directions, Lloyd-Max with
+ *            restarts); rate bits / block per coordinate.  m must be 0,
+ *            correction TQ_CORR_QJL (no residual correction) and d a multiple
+ *            of block.  Kernels exist for block 2 with the Hadamard rotation
+ *            (d = 64, 128); other vector codebooks build tables only.
  */
 typedef struct {
     int32_t d, bits, m, rotation;
     uint64_t seed;
-    int32_t correction, reserved;
+    int32_t correction, block;
 } tq_spec;
 
 /*
@@ -173,6 +184,8 @@ typedef struct {
 /*
  * tq_codebook_tables (host only, no GPU): computes the tables a codebook
  * holds, into caller host buffers (any may be NULL to skip):
+ *   (vector codebooks: levels receives the N x block codewords row-major,
+ *   thresholds nothing)
  *   levels [K], thresholds [K-1]    float32 Lloyd-Max table for the density
  *       of one coordinate of a uniform point on S^{d-1} (FibQuant summary,
  *       section 2.1; itstec post, "Por dentro do processo": a Beta law),
@@ -387,6 +400,16 @@ tq_status tq_attn_decode_paged(const tq_codebook* ck, const tq_codebook* cv, con
                                const int32_t* seq_len, const tq_pages* pages, const float* rope_cos,
                                const float* rope_sin, int32_t rope_npos, float scale, float* out, void* ws,
                                size_t ws_bytes, void* stream);
+
+/*
+ * tq_decode_vectors: the FibQuant decoder (FibQuant summary, section 2.3):
+ * records [first, first + count) of a vector-coded tensor rebuilt as
+ * out[i] = nu Pi^T (c[idx_0], c[idx_1], ...) (device float [count][d]).
+ * Vector codebooks with kernels only (TQ_EUNSUPPORTED otherwise).  The fused
+ * decode (tq_attn_decode) takes scalar codebooks.
+ */
+tq_status tq_decode_vectors(const tq_codebook* cb, const tq_packed* packed, int64_t first, int64_t count, float* out,
+                            void* stream);
 
 /* Workspace bytes for an op.  For TQ_OP_ENCODE pass the vector count in B
  * (other sizes ignored).  Returns 0 on a bad argument. */

@@ -34,7 +34,8 @@ from ._lib import (TQError, TQ_F32, TQ_BF16, TQ_ROT_AUTO, TQ_ROT_HADAMARD, TQ_RO
                    tq_packed, tq_pages, tq_spec)
 
 __all__ = ["Codebook", "Packed", "Pages", "Launch", "encode_kv", "append_kv", "attn_logits", "attn_decode",
-           "rope_table", "codebook_tables", "plane_words", "workspace_bytes", "calibrate", "TQError", "lib"]
+           "decode_vectors", "rope_table", "codebook_tables", "plane_words", "workspace_bytes", "calibrate",
+           "TQError", "lib"]
 
 _ROT = {"auto": TQ_ROT_AUTO, "hadamard": TQ_ROT_HADAMARD, "dense": TQ_ROT_DENSE, "none": TQ_ROT_NONE}
 _CORR = {"qjl": TQ_CORR_QJL, "sign": TQ_CORR_SIGN}
@@ -63,10 +64,10 @@ def _dtype_code(t):
     raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
 
 
-def _spec(d, bits, m, rotation="auto", seed=0, correction="qjl"):
+def _spec(d, bits, m, rotation="auto", seed=0, correction="qjl", block=0):
     return tq_spec(int(d), int(bits), int(m), _ROT[rotation] if isinstance(rotation, str) else int(rotation),
                    int(seed) & 0xFFFFFFFFFFFFFFFF,
-                   _CORR[correction] if isinstance(correction, str) else int(correction), 0)
+                   _CORR[correction] if isinstance(correction, str) else int(correction), int(block))
 
 
 def _draws(sigma=None, rot_gauss=None, sketch=None):
@@ -87,9 +88,9 @@ def _draws(sigma=None, rot_gauss=None, sketch=None):
     return dr, keep
 
 
-def plane_words(d, bits, m, rotation="auto", correction="qjl"):
+def plane_words(d, bits, m, rotation="auto", correction="qjl", block=0):
     """(code words, sign words) per record."""
-    sp = _spec(d, bits, m, rotation, 0, correction)
+    sp = _spec(d, bits, m, rotation, 0, correction, block)
     cw = lib().tq_plane_words(C.byref(sp), 0)
     sw = lib().tq_plane_words(C.byref(sp), 1)
     if cw < 0:
@@ -98,22 +99,22 @@ def plane_words(d, bits, m, rotation="auto", correction="qjl"):
 
 
 def codebook_tables(d, bits, m, rotation="auto", seed=0, sigma=None, rot_gauss=None, sketch=None,
-                    correction="qjl"):
-    """Host-only table construction (no GPU): dict of levels, thresholds,
-    rotation (sigma as +-1 or the dense matrix; zeros for rotation "none")
-    and sketch."""
-    sp = _spec(d, bits, m, rotation, seed, correction)
+                    correction="qjl", block=0):
+    """Host-only table construction (no GPU): dict of levels (for a vector
+    codebook, its codewords [2^bits, block]), thresholds, rotation (sigma as
+    +-1 or the dense matrix; zeros for rotation "none") and sketch."""
+    sp = _spec(d, bits, m, rotation, seed, correction, block)
     dr, keep = _draws(sigma, rot_gauss, sketch)
     K = 1 << bits
-    lv = np.zeros(K, np.float32)
+    lv = np.zeros(K * max(1, block), np.float32)
     th = np.zeros(K - 1, np.float32)
     dense = (rotation == "dense") or (rotation == "auto" and (d & (d - 1)) != 0) or rotation == TQ_ROT_DENSE
     rot = np.zeros(d * d if dense else d, np.float32)
     sk = np.zeros(m * d, np.float32)
     check(lib().tq_codebook_tables(C.byref(sp), C.byref(dr), lv.ctypes.data, th.ctypes.data, rot.ctypes.data,
                                    sk.ctypes.data))
-    return {"levels": lv, "thresholds": th, "rotation": rot.reshape(d, d) if dense else rot,
-            "sketch": sk.reshape(m, d), "dense": dense}
+    return {"levels": lv.reshape(K, block) if block >= 2 else lv, "thresholds": th,
+            "rotation": rot.reshape(d, d) if dense else rot, "sketch": sk.reshape(m, d), "dense": dense}
 
 
 def calibrate(d, bits, x, rotation="hadamard", seed=0, sigma=None, tok_offset=0, rope=None,
@@ -150,9 +151,9 @@ class Codebook:
     table and per-head mean residual magnitudes (see calibrate)."""
 
     def __init__(self, d, bits, m, rotation="auto", seed=0, sigma=None, rot_gauss=None, sketch=None,
-                 correction="qjl", levels=None, mu=None):
-        self.d, self.bits, self.m = int(d), int(bits), int(m)
-        sp = _spec(d, bits, m, rotation, seed, correction)
+                 correction="qjl", levels=None, mu=None, block=0):
+        self.d, self.bits, self.m, self.block = int(d), int(bits), int(m), int(block)
+        sp = _spec(d, bits, m, rotation, seed, correction, block)
         dr, keep = _draws(sigma, rot_gauss, sketch)
         lv = None if levels is None else np.ascontiguousarray(levels, np.float32)
         mu_a = None if mu is None else np.ascontiguousarray(np.atleast_1d(mu), np.float32)
@@ -167,7 +168,7 @@ class Codebook:
         check(lib().tq_codebook_get_spec(h, C.byref(out)))
         self.rotation = out.rotation
         self.dense = (out.rotation == TQ_ROT_DENSE) or (out.rotation == TQ_ROT_AUTO and (self.d & (self.d - 1)) != 0)
-        self.code_words = self.bits * self.d // 32
+        self.code_words = int(lib().tq_plane_words(C.byref(sp), 0))
         self.sign_words = self.m // 32
 
     @property
@@ -186,12 +187,12 @@ class Codebook:
 
     def export(self):
         K = 1 << self.bits
-        lv = np.zeros(K, np.float32)
+        lv = np.zeros(K * max(1, self.block), np.float32)
         th = np.zeros(K - 1, np.float32)
         rot = np.zeros(self.d * self.d if self.dense else self.d, np.float32)
         sk = np.zeros(self.m * self.d, np.float32)
         check(lib().tq_codebook_export(self._h, lv.ctypes.data, th.ctypes.data, rot.ctypes.data, sk.ctypes.data))
-        return {"levels": lv, "thresholds": th,
+        return {"levels": lv.reshape(K, self.block) if self.block >= 2 else lv, "thresholds": th,
                 "rotation": rot.reshape(self.d, self.d) if self.dense else rot,
                 "sketch": sk.reshape(self.m, self.d)}
 
@@ -296,6 +297,18 @@ def _run(fn, args, keep, prepare):
         return Launch(fn, tuple(args), keep)
     check(fn(*args))
     return None
+
+
+def decode_vectors(cb, packed, first=0, count=None, out=None):
+    """The vector codebook's decoder: records [first, first + count) rebuilt
+    as float32 [count, d] (nu Pi^T of the looked-up codewords)."""
+    torch = _torch()
+    count = packed.n - first if count is None else int(count)
+    if out is None:
+        out = torch.empty((count, cb.d), dtype=torch.float32, device="cuda")
+    pst = packed.struct()
+    check(lib().tq_decode_vectors(cb.handle, C.byref(pst), int(first), count, _ptr(out), _stream()))
+    return out
 
 
 def workspace_bytes(ck, cv, op, B, Hq=0, h_kv=1, L_cap=0, top_k=0):

@@ -19,7 +19,7 @@ TQ_OP_ENCODE, TQ_OP_LOGITS, TQ_OP_DECODE = 0, 1, 2
 
 class tq_spec(C.Structure):
     _fields_ = [("d", C.c_int32), ("bits", C.c_int32), ("m", C.c_int32), ("rotation", C.c_int32),
-                ("seed", C.c_uint64), ("correction", C.c_int32), ("reserved", C.c_int32)]
+                ("seed", C.c_uint64), ("correction", C.c_int32), ("block", C.c_int32)]
 
 
 class tq_draws(C.Structure):
@@ -46,6 +46,8 @@ SIGNATURES = {
     "tq_calibrate": (C.c_int32, [C.POINTER(tq_spec), C.POINTER(tq_draws), C.c_void_p, C.c_int64, C.c_int32,
                                  C.c_int32, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p]),
     "tq_codebook_get_mu": (C.c_int32, [C.c_void_p, C.c_void_p, C.POINTER(C.c_int32)]),
+    "tq_decode_vectors": (C.c_int32, [C.c_void_p, C.POINTER(tq_packed), C.c_int64, C.c_int64, C.c_void_p,
+                                      C.c_void_p]),
     "tq_codebook_destroy": (C.c_int32, [C.c_void_p]),
     "tq_codebook_get_spec": (C.c_int32, [C.c_void_p, C.POINTER(tq_spec)]),
     "tq_codebook_export": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),

@@ -25,7 +25,8 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libtq.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["tq_host.cpp", "tq_gemm.hip", "tq_encode.hip", "tq_attn.hip", "tq_logits.hip", "tq_decode.hip"]
+SOURCES = ["tq_host.cpp", "tq_gemm.hip", "tq_encode.hip", "tq_attn.hip", "tq_logits.hip", "tq_decode.hip",
+           "tq_vq.hip"]
 ARCH = "gfx950"
 
 

@@ -793,6 +793,8 @@ QPrep make_qprep(const tq_codebook* ck, const AttnArgs& a, float* qp, float* s) 
     return q;
 }
 
+}  // namespace
+
 hipError_t launch_qprep_rht(const tq_codebook* ck, const AttnArgs& a, float* qp, float* s,
                             hipStream_t stream) {
     QPrep q = make_qprep(ck, a, qp, s);
@@ -803,12 +805,36 @@ hipError_t launch_qprep_rht(const tq_codebook* ck, const AttnArgs& a, float* qp,
     return hipGetLastError();
 }
 
-}  // namespace
+// merge the scores of keys [col0, col0 + cnt) (rows row0.. of `scores`, ld
+// apart) into the running top-k of every query row
+hipError_t launch_topk(const AttnArgs& a, const float* scores, int64_t ld, int64_t row0, int col0, int cnt,
+                       bool first, hipStream_t stream) {
+    TopK tk{};
+    tk.scores = scores;
+    tk.ld = ld;
+    tk.row0 = row0;
+    tk.col0 = col0;
+    tk.cnt = cnt;
+    tk.Hq = a.Hq;
+    tk.L_cap = a.L_cap;
+    tk.k = a.top_k;
+    tk.first = first;
+    tk.seq_len = a.seq_len;
+    tk.out_val = a.out;
+    tk.out_idx = a.topk_idx;
+    hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)((int64_t)a.B * a.Hq)), dim3(256), 0, stream, tk);
+    return hipGetLastError();
+}
 
 size_t logits_workspace_bytes(const tq_codebook* ck, int64_t B, int Hq, int h_kv, int L_cap, int top_k) {
     const size_t d = ck->spec.d, m = ck->spec.m;
     const size_t rows = (size_t)B * Hq;
     const size_t chunk = (size_t)std::min(L_cap, kScanChunk);
+    if (ck->spec.block >= 2) {
+        size_t bytes = align256(rows * d * 4);
+        if (top_k) bytes += align256(rows * chunk * 4);
+        return bytes;
+    }
     if (!ck->dense) {
         size_t bytes = logits_mfma_supported(ck) ? align256(qdigits_workspace_bytes(ck, (int64_t)rows))
                                                  : align256(rows * (d + m) * 4);
@@ -847,6 +873,23 @@ hipError_t launch_logits(const tq_codebook* ck, const tq_packed& k, const AttnAr
     const int64_t rows = (int64_t)a.B * a.Hq;
     char* ws = static_cast<char*>(a.ws);
     const int chunk = std::min(a.L_cap, kScanChunk);
+    if (ck->spec.block >= 2) {
+        // vector codebook: q' = Pi RoPE(q), then codeword lookups fused into the dot products
+        if (!vq_supported(ck)) return hipErrorInvalidValue;
+        float* qp = reinterpret_cast<float*>(ws);
+        float* scores = reinterpret_cast<float*>(ws + align256((size_t)rows * d * 4));
+        hipError_t e = launch_qprep_rht(ck, a, qp, nullptr, stream);
+        if (e != hipSuccess) return e;
+        if (a.top_k == 0) return launch_vq_logits(ck, k, a, qp, 0, a.L_cap, a.out, a.L_cap, 0, stream);
+        for (int k0 = 0; k0 < a.L_cap; k0 += chunk) {
+            const int cnt = std::min(chunk, a.L_cap - k0);
+            e = launch_vq_logits(ck, k, a, qp, k0, cnt, scores, chunk, k0, stream);
+            if (e != hipSuccess) return e;
+            e = launch_topk(a, scores, chunk, 0, k0, cnt, k0 == 0, stream);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
     if (!ck->dense && logits_mfma_supported(ck)) {
         const QDigits qd = carve_qdigits(ck, ws, rows);
         float* scores = reinterpret_cast<float*>(ws + align256(qdigits_workspace_bytes(ck, rows)));

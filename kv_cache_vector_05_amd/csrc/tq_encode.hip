@@ -1035,6 +1035,7 @@ hipError_t launch_encode(const tq_codebook* cb, const EncodeArgs& a, hipStream_t
         if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) return hipErrorUnknown;
         g_num_cus = prop.multiProcessorCount;
     }
+    if (cb->spec.block >= 2) return vq_supported(cb) ? launch_vq_encode(cb, a, stream) : hipErrorInvalidValue;
     if (!cb->dense) {
         const int mode = cb->spec.correction == TQ_CORR_SIGN ? (cb->spec.rotation == TQ_ROT_NONE ? 2 : 1) : 0;
         EncFn fn = pick_encode(d, bits, m, a.bf16 != 0, a.rope_cos != nullptr, mode);

@@ -37,12 +37,28 @@ tq_status hip_fail(hipError_t e, const char* what) {
 static bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
 tq_status check_spec(const tq_spec& s, bool* dense) {
+    if (s.block < 0 || s.block > 3) return fail(TQ_EINVAL, "block must be 0..3");
+    if (s.block >= 2) {
+        // a FibQuant vector codebook: N = 2^bits codewords per block of `block` coordinates
+        if (s.bits < 1 || s.bits > 8) return fail(TQ_EINVAL, "a vector codebook has 1..8 index bits per block");
+        if (s.d < 3 || s.d > 4096 || s.d % s.block) return fail(TQ_EINVAL, "d must be a multiple of block");
+        if (s.m != 0 || s.correction != TQ_CORR_QJL)
+            return fail(TQ_EINVAL, "vector codebooks take no residual correction (m = 0)");
+        bool dn;
+        if (s.rotation == TQ_ROT_AUTO) dn = !is_pow2(s.d);
+        else if (s.rotation == TQ_ROT_HADAMARD) dn = false;
+        else if (s.rotation == TQ_ROT_DENSE) dn = true;
+        else return fail(TQ_EINVAL, "vector codebooks take the Hadamard or the dense rotation");
+        if (!dn && !is_pow2(s.d)) return fail(TQ_EINVAL, "Hadamard rotation needs a power-of-two d");
+        if (dn && s.d % 64) return fail(TQ_EUNSUPPORTED, "dense rotations need d a multiple of 64");
+        if (dense) *dense = dn;
+        return TQ_OK;
+    }
     if (s.bits < 1 || s.bits > 4) return fail(TQ_EINVAL, "bits must be 1..4");
     if (s.d < 3 || s.d > 4096) return fail(TQ_EINVAL, "d must be 3..4096");
     if ((s.bits * s.d) % 32) return fail(TQ_EINVAL, "bits*d must be a multiple of 32");
     if (s.m < 0 || s.m > 4096 || (s.m % 32)) return fail(TQ_EINVAL, "m must be 0 or a multiple of 32 up to 4096");
     if (s.correction != TQ_CORR_QJL && s.correction != TQ_CORR_SIGN) return fail(TQ_EINVAL, "unknown correction");
-    if (s.reserved != 0) return fail(TQ_EINVAL, "reserved must be 0");
     bool dn;
     if (s.rotation == TQ_ROT_AUTO) dn = !is_pow2(s.d);
     else if (s.rotation == TQ_ROT_HADAMARD || s.rotation == TQ_ROT_NONE) dn = false;
@@ -194,6 +210,201 @@ double beta_mean_abs_error(int d, const std::vector<float>& levels, const std::v
         mass += m1 + m2;
     }
     return acc / mass;
+}
+
+// ------------------------------------------------------------------------
+// FibQuant vector codebooks (FibQuant summary, section 2.2).  A block of k
+// coordinates of a uniform point on S^{d-1} has |x|^2 ~ Beta(k/2, (d-k)/2).
+// Initial codewords: Bennett-Gersho radii (point density proportional to
+// f^(k/(k+2)), whose |x|^2 is Beta(k/2, a + 1), a = k (d-k-2) / (2 (k+2)),
+// taken at the quantiles (n + 1/2) / N) with golden-angle directions (k = 2)
+// or a Fibonacci sphere (k = 3, radius quantile frac((n + 1/2) / phi)).
+// Refinement: Lloyd-Max on an equal-mass deterministic sample (64 radial
+// quantiles times 256 directions; for k = 3 a Fibonacci sphere and its
+// antipodes), several restarts rotated by 2 pi r / (R N).
+// ------------------------------------------------------------------------
+namespace {
+
+// continued fraction of the regularised incomplete beta function (DLMF
+// 8.17.22), evaluated by the modified Lentz method
+double ibeta_cf(double a, double b, double x) {
+    const double tiny = 1e-300;
+    double c = 1.0, dd = 1.0 - (a + b) * x / (a + 1.0);
+    if (std::fabs(dd) < tiny) dd = tiny;
+    dd = 1.0 / dd;
+    double f = dd;
+    for (int m = 1; m < 10000; ++m) {
+        // even step: m (b - m) x / ((a + 2m - 1)(a + 2m))
+        double num = m * (b - m) * x / ((a + 2.0 * m - 1.0) * (a + 2.0 * m));
+        dd = 1.0 + num * dd;
+        if (std::fabs(dd) < tiny) dd = tiny;
+        c = 1.0 + num / c;
+        if (std::fabs(c) < tiny) c = tiny;
+        dd = 1.0 / dd;
+        f *= dd * c;
+        // odd step: -(a + m)(a + b + m) x / ((a + 2m)(a + 2m + 1))
+        num = -(a + m) * (a + b + m) * x / ((a + 2.0 * m) * (a + 2.0 * m + 1.0));
+        dd = 1.0 + num * dd;
+        if (std::fabs(dd) < tiny) dd = tiny;
+        c = 1.0 + num / c;
+        if (std::fabs(c) < tiny) c = tiny;
+        dd = 1.0 / dd;
+        const double step = dd * c;
+        f *= step;
+        if (std::fabs(step - 1.0) < 1e-16) break;
+    }
+    return f;
+}
+
+// I_x(a, b)
+double ibeta(double a, double b, double x) {
+    if (x <= 0.0) return 0.0;
+    if (x >= 1.0) return 1.0;
+    const double lfront = std::lgamma(a + b) - std::lgamma(a) - std::lgamma(b) + a * std::log(x) + b * std::log1p(-x);
+    if (x < (a + 1.0) / (a + b + 2.0)) return std::exp(lfront) * ibeta_cf(a, b, x) / a;
+    return 1.0 - std::exp(lfront) * ibeta_cf(b, a, 1.0 - x) / b;
+}
+
+// the p-quantile of Beta(a, b), by bisection
+double ibeta_inv(double a, double b, double p) {
+    double lo = 0.0, hi = 1.0;
+    for (int it = 0; it < 200; ++it) {
+        const double mid = 0.5 * (lo + hi);
+        if (mid <= lo || mid >= hi) break;
+        if (ibeta(a, b, mid) < p) lo = mid;
+        else hi = mid;
+    }
+    return 0.5 * (lo + hi);
+}
+
+const double kPhi = 1.6180339887498949;  // (1 + sqrt 5) / 2
+
+void fibonacci_sphere(int n, std::vector<double>* out) {
+    const double ga = 2.0 * M_PI / (kPhi * kPhi);
+    out->resize((size_t)n * 3);
+    for (int i = 0; i < n; ++i) {
+        const double z = 1.0 - 2.0 * (i + 0.5) / n;
+        const double rho = std::sqrt(std::max(0.0, 1.0 - z * z));
+        const double th = i * ga;
+        (*out)[3 * i] = rho * std::cos(th);
+        (*out)[3 * i + 1] = rho * std::sin(th);
+        (*out)[3 * i + 2] = z;
+    }
+}
+
+// Lloyd-Max on equal-weight points (row-major [P][k]) from code [N][k];
+// returns the mean squared error
+double vq_lloyd(const std::vector<double>& pts, int k, std::vector<double>* code, int N) {
+    const size_t P = pts.size() / k;
+    std::vector<int> assign(P, -1), next(P);
+    std::vector<double> sum((size_t)N * k);
+    std::vector<long> cnt(N);
+    for (int it = 0; it < 5000; ++it) {
+        for (size_t p = 0; p < P; ++p) {
+            double best = 0.0;
+            int bi = 0;
+            for (int n = 0; n < N; ++n) {
+                double dist = 0.0;
+                for (int i = 0; i < k; ++i) {
+                    const double df = pts[p * k + i] - (*code)[(size_t)n * k + i];
+                    dist = dist + df * df;
+                }
+                if (n == 0 || dist < best) {
+                    best = dist;
+                    bi = n;
+                }
+            }
+            next[p] = bi;
+        }
+        if (next == assign) break;
+        assign = next;
+        std::fill(sum.begin(), sum.end(), 0.0);
+        std::fill(cnt.begin(), cnt.end(), 0);
+        for (size_t p = 0; p < P; ++p) {
+            ++cnt[assign[p]];
+            for (int i = 0; i < k; ++i) sum[(size_t)assign[p] * k + i] += pts[p * k + i];
+        }
+        for (int n = 0; n < N; ++n)
+            if (cnt[n])
+                for (int i = 0; i < k; ++i) (*code)[(size_t)n * k + i] = sum[(size_t)n * k + i] / (double)cnt[n];
+    }
+    double mse = 0.0;
+    for (size_t p = 0; p < P; ++p) {
+        double dist = 0.0;
+        for (int i = 0; i < k; ++i) {
+            const double df = pts[p * k + i] - (*code)[(size_t)assign[p] * k + i];
+            dist += df * df;
+        }
+        mse += dist;
+    }
+    return mse / (double)P;
+}
+
+}  // namespace
+
+void fibquant_codebook(int d, int k, int N, std::vector<double>* out) {
+    const int n_radii = 64, n_dirs = 256, restarts = 4;
+    // equal-mass sample of the block law
+    std::vector<double> r(n_radii), dirs;
+    for (int i = 0; i < n_radii; ++i) r[i] = std::sqrt(ibeta_inv(k / 2.0, (d - k) / 2.0, (i + 0.5) / n_radii));
+    int nd;
+    if (k == 2) {
+        nd = n_dirs;
+        dirs.resize((size_t)nd * 2);
+        for (int j = 0; j < nd; ++j) {
+            const double th = 2.0 * M_PI * (j + 0.5) / nd;
+            dirs[2 * j] = std::cos(th);
+            dirs[2 * j + 1] = std::sin(th);
+        }
+    } else {
+        std::vector<double> f;
+        fibonacci_sphere(n_dirs, &f);
+        nd = 2 * n_dirs;
+        dirs.resize((size_t)nd * 3);
+        for (size_t i = 0; i < f.size(); ++i) {
+            dirs[i] = f[i];
+            dirs[f.size() + i] = -f[i];
+        }
+    }
+    std::vector<double> pts((size_t)n_radii * nd * k);
+    for (int i = 0; i < n_radii; ++i)
+        for (int j = 0; j < nd; ++j)
+            for (int c = 0; c < k; ++c) pts[((size_t)i * nd + j) * k + c] = r[i] * dirs[(size_t)j * k + c];
+    // initial codebook
+    const double a = k * (d - k - 2) / (2.0 * (k + 2));
+    std::vector<double> init((size_t)N * k);
+    if (k == 2) {
+        const double ga = 2.0 * M_PI / (kPhi * kPhi);
+        for (int n = 0; n < N; ++n) {
+            const double rn = std::sqrt(ibeta_inv(1.0, a + 1.0, (n + 0.5) / N));
+            const double th = n * ga;
+            init[2 * n] = rn * std::cos(th);
+            init[2 * n + 1] = rn * std::sin(th);
+        }
+    } else {
+        std::vector<double> f;
+        fibonacci_sphere(N, &f);
+        for (int n = 0; n < N; ++n) {
+            const double lv = std::fmod((n + 0.5) / kPhi, 1.0);
+            const double rn = std::sqrt(ibeta_inv(1.5, a + 1.0, lv));
+            for (int c = 0; c < 3; ++c) init[3 * n + c] = rn * f[3 * n + c];
+        }
+    }
+    double best_mse = 0.0;
+    for (int rs = 0; rs < restarts; ++rs) {
+        const double ang = 2.0 * M_PI * rs / (restarts * (double)N);
+        const double ca = std::cos(ang), sa = std::sin(ang);
+        std::vector<double> c = init;
+        for (int n = 0; n < N; ++n) {
+            c[(size_t)n * k] = ca * init[(size_t)n * k] - sa * init[(size_t)n * k + 1];
+            c[(size_t)n * k + 1] = sa * init[(size_t)n * k] + ca * init[(size_t)n * k + 1];
+        }
+        const double mse = vq_lloyd(pts, k, &c, N);
+        if (rs == 0 || mse < best_mse * (1.0 - 1e-9)) {
+            best_mse = mse;
+            *out = c;
+        }
+    }
 }
 
 // ------------------------------------------------------------------------
@@ -362,10 +573,18 @@ float f16_to_f32(uint16_t h) {
 static tq_status build_tables(const tq_spec& s, const tq_draws* dr, bool dense,
                               std::vector<float>* levels, std::vector<float>* thr,
                               std::vector<float>* rot, std::vector<float>* sk) {
-    std::vector<double> t, tau;
-    lloyd_max_table(s.d, s.bits, &t, &tau);
-    levels->assign(t.begin(), t.end());
-    thr->assign(tau.begin(), tau.end());
+    if (s.block >= 2) {
+        // vector codebook: levels holds the N x block codewords
+        std::vector<double> code;
+        fibquant_codebook(s.d, s.block, 1 << s.bits, &code);
+        levels->assign(code.begin(), code.end());
+        thr->clear();
+    } else {
+        std::vector<double> t, tau;
+        lloyd_max_table(s.d, s.bits, &t, &tau);
+        levels->assign(t.begin(), t.end());
+        thr->assign(tau.begin(), tau.end());
+    }
     const size_t d = (size_t)s.d;
     if (dense) {
         std::vector<double> g;
@@ -424,6 +643,7 @@ const char* tq_version(void) { return "libtq 0.1 (gfx950)"; }
 
 int64_t tq_plane_words(const tq_spec* spec, int32_t plane) {
     if (!spec || check_spec(*spec, nullptr) != TQ_OK) return -1;
+    if (plane == 0 && spec->block >= 2) return ((int64_t)spec->bits * (spec->d / spec->block) + 31) / 32;
     if (plane == 0) return (int64_t)spec->bits * spec->d / 32;
     if (plane == 1) return spec->m / 32;
     return -1;
@@ -471,7 +691,12 @@ static tq_status codebook_create(const tq_spec* spec, const tq_draws* draws, con
     tq_status st = check_spec(*spec, &dense);
     if (st) return st;
     const int K = 1 << spec->bits;
-    if (levels) {
+    const bool vq = spec->block >= 2;
+    if (levels && vq) {
+        // explicit codewords of a vector codebook [N][block]
+        for (int j = 0; j < K * spec->block; ++j)
+            if (!std::isfinite(levels[j])) return fail(TQ_EINVAL, "codewords must be finite");
+    } else if (levels) {
         // a calibrated table: strictly increasing, exactly symmetric
         for (int j = 0; j < K; ++j) {
             if (!std::isfinite(levels[j])) return fail(TQ_EINVAL, "levels must be finite");
@@ -494,7 +719,9 @@ static tq_status codebook_create(const tq_spec* spec, const tq_draws* draws, con
         delete cb;
         return st;
     }
-    if (levels) {
+    if (levels && vq) {
+        cb->levels.assign(levels, levels + (size_t)K * spec->block);
+    } else if (levels) {
         cb->levels.assign(levels, levels + K);
         for (int j = 0; j + 1 < K; ++j) cb->thresholds[j] = (float)(0.5 * ((double)levels[j] + (double)levels[j + 1]));
     }
@@ -502,7 +729,7 @@ static tq_status codebook_create(const tq_spec* spec, const tq_draws* draws, con
         if (mu) cb->mu.assign(mu, mu + n_mu);
         else cb->mu.assign(1, (float)beta_mean_abs_error(spec->d, cb->levels, cb->thresholds));
     }
-    if (cb->K <= 8) level_digits(cb->levels, cb->lvl_digits, &cb->lvl_shift);
+    if (cb->K <= 8 && !vq) level_digits(cb->levels, cb->lvl_digits, &cb->lvl_shift);
     const int d = spec->d, m = spec->m;
     // the encode kernel's sketch operand (Hadamard form): S split into fp16
     // hi + lo parts in the A-operand order of v_mfma_f32_32x32x16_f16, the
@@ -528,7 +755,7 @@ static tq_status codebook_create(const tq_spec* spec, const tq_draws* draws, con
     }
     // one device block: levels[16] | thresholds[16] | sigma[d] or rot[d*d] | sketch | sketch_mfma | mu
     // (the sign correction's S = I is never read on the device)
-    const size_t n_lv = 16, n_th = 16;
+    const size_t n_lv = vq ? std::max<size_t>(16, cb->levels.size()) : 16, n_th = 16;
     const size_t n_rot = dense ? (size_t)d * d : (size_t)d;
     const size_t n_sk = sign ? 0 : (size_t)m * d;
     const size_t n_mu_dev = cb->mu.size();
@@ -814,6 +1041,11 @@ static tq_status encode_common(const tq_codebook* ck, const tq_codebook* cv, con
         }
         if (sd.cb->dense && (pos || pg.table))
             return fail(TQ_EUNSUPPORTED, "appends and paged records are served for Hadamard and unrotated codebooks");
+        if (sd.cb->spec.block >= 2) {
+            if (!vq_supported(sd.cb))
+                return fail(TQ_EUNSUPPORTED, "vector codebooks encode on the GPU for block 2, Hadamard, d = 64 or 128");
+            if (nvec >= ((int64_t)1 << 31)) return fail(TQ_EUNSUPPORTED, "too many vectors in one encode call (split it)");
+        }
         if (!sd.cb->dense && (int64_t)n_seq * ((n_tok + 31) / 32) * h_kv >= (int64_t)1 << 31)
             return fail(TQ_EUNSUPPORTED, "too many vectors in one encode call (split it)");
         if (sd.cb->dense && nvec > 0) {
@@ -882,9 +1114,12 @@ static tq_status logits_common(const tq_codebook* ck, const void* q, int32_t q_d
     if (st) return st;
     st = check_mu(ck, h_kv);
     if (st) return st;
-    if ((sign_corr(ck) || pg.table) && !logits_mfma_supported(ck))
+    if (ck->spec.block >= 2) {
+        if (!vq_supported(ck)) return fail(TQ_EUNSUPPORTED, "no logit kernel for this vector codebook");
+    } else if ((sign_corr(ck) || pg.table) && !logits_mfma_supported(ck)) {
         return fail(TQ_EUNSUPPORTED, "no logit kernel for this codebook (paged and sign-corrected scans need "
                                      "a Hadamard or unrotated codebook with bits <= 3 and m <= 128)");
+    }
     if ((int64_t)B * Hq == 0 || (L_cap == 0 && top_k == 0)) return TQ_OK;
     const size_t need = logits_workspace_bytes(ck, B, Hq, h_kv, L_cap, top_k);
     if (ws_bytes < need || (need && !ws)) return fail(TQ_EINVAL, "workspace too small");
@@ -919,6 +1154,9 @@ static tq_status decode_common(const tq_codebook* ck, const tq_codebook* cv, con
     if (!out) return fail(TQ_EINVAL, "null output");
     if (!(scale >= 0.0f) || std::isinf(scale)) return fail(TQ_EINVAL, "scale must be finite and >= 0");
     if (ck->spec.d != cv->spec.d) return fail(TQ_EINVAL, "key and value dimensions differ");
+    if (ck->spec.block >= 2 || cv->spec.block >= 2)
+        return fail(TQ_EUNSUPPORTED, "the fused decode takes scalar codebooks; rebuild vector-coded values with "
+                                     "tq_decode_vectors");
     st = check_packed(ck, k, cap_records, "k");
     if (st) return st;
     st = check_packed(cv, v, cap_records, "v");
@@ -1043,6 +1281,18 @@ tq_status tq_attn_decode_paged(const tq_codebook* ck, const tq_codebook* cv, con
     return decode_common(ck, cv, q, q_dtype, k, v, B, Hq, h_kv, pg.max_pages * pg.size, seq_len, pg,
                          pg.n_pages * h_kv * (int64_t)pg.size, rope_cos, rope_sin, rope_npos, scale, out, ws, ws_bytes,
                          stream);
+}
+
+tq_status tq_decode_vectors(const tq_codebook* cb, const tq_packed* packed, int64_t first, int64_t count, float* out,
+                            void* stream) {
+    if (!cb || !packed || !out) return fail(TQ_EINVAL, "null argument");
+    if (!packed->norm || !packed->codes) return fail(TQ_EINVAL, "null norm/codes plane");
+    if (first < 0 || count < 0 || first + count > packed->n) return fail(TQ_EINVAL, "records out of range");
+    if (cb->spec.block < 2 || !vq_supported(cb))
+        return fail(TQ_EUNSUPPORTED, "vectors are rebuilt for vector codebooks (block 2, Hadamard, d = 64 or 128)");
+    if (count == 0) return TQ_OK;
+    hipError_t e = launch_vq_decode(cb, *packed, first, count, out, (hipStream_t)stream);
+    return e == hipSuccess ? TQ_OK : hip_fail(e, "decode launch");
 }
 
 size_t tq_workspace_bytes(const tq_codebook* ck, const tq_codebook* cv, int32_t op, int64_t B,

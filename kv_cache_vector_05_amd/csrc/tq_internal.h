@@ -77,6 +77,7 @@ tq_status hip_fail(hipError_t e, const char* what);
 tq_status check_spec(const tq_spec& s, bool* dense);
 void lloyd_max_table(int d, int bits, std::vector<double>* levels, std::vector<double>* thr);
 double beta_mean_abs_error(int d, const std::vector<float>& levels, const std::vector<float>& thr);
+void fibquant_codebook(int d, int k, int N, std::vector<double>* code);  // [N][k] row-major
 void splitmix_gaussians(uint64_t seed, int purpose, size_t n, double* out);
 void splitmix_signs(uint64_t seed, size_t n, int8_t* out);
 void haar_from_gaussians(int d, const double* g, std::vector<double>* q);  // row-major
@@ -157,6 +158,17 @@ void decode_mfma_plan(int64_t B, int Hq, int h_kv, int L_cap, int* nsplit, int* 
 hipError_t launch_decode_mfma(const tq_codebook* ck, const tq_codebook* cv, const tq_packed& k, const tq_packed& v,
                               const AttnArgs& a, const QDigits& q, float* part, int nsplit, int split_len,
                               hipStream_t stream);
+
+// FibQuant vector codebooks (tq_vq.hip): block 2, Hadamard rotation, d = 64, 128
+bool vq_supported(const tq_codebook* cb);
+hipError_t launch_vq_encode(const tq_codebook* cb, const EncodeArgs& a, hipStream_t stream);
+hipError_t launch_vq_logits(const tq_codebook* ck, const tq_packed& k, const AttnArgs& a, const float* qp, int k0,
+                            int klen, float* out, int64_t ld, int col0, hipStream_t stream);
+hipError_t launch_vq_decode(const tq_codebook* cb, const tq_packed& k, int64_t first, int64_t count, float* out,
+                            hipStream_t stream);
+hipError_t launch_qprep_rht(const tq_codebook* ck, const AttnArgs& a, float* qp, float* s, hipStream_t stream);
+hipError_t launch_topk(const AttnArgs& a, const float* scores, int64_t ld, int64_t row0, int col0, int cnt,
+                       bool first, hipStream_t stream);
 
 // C[M][N] = A[M][K] * B[N][K]^T (+ per-column scale if col_scale != nullptr),
 // fp32, row-major with leading dimensions lda/ldb/ldc (elements).

@@ -395,7 +395,7 @@ int64_t resident_blocks(const void* fn) {
 }  // namespace
 
 bool logits_mfma_supported(const tq_codebook* ck) {
-    return !ck->dense && ck->spec.bits <= 3 && (ck->spec.d == 64 || ck->spec.d == 128) && ck->spec.m <= 128;
+    return !ck->dense && ck->spec.block < 2 && ck->spec.bits <= 3 && (ck->spec.d == 64 || ck->spec.d == 128) && ck->spec.m <= 128;
 }
 
 size_t qdigits_workspace_bytes(const tq_codebook* ck, int64_t rows) {

@@ -1,0 +1,169 @@
+"""GPU parity for FibQuant vector codebooks (FibQuant summary, sections
+2.1-2.3): the nearest-codeword encoder (bulk, appended and paged), the logit
+scan with codeword lookups (and top-k), and the decoder, through the C ABI
+against the oracle in oracle/fibquant.py.
+
+Protocol: a block's codeword index must equal the oracle's unless its two
+nearest codewords are within 1e-6 in squared distance (the GPU decides in
+float32 from a float32 rotation); at most a 1e-6 fraction of the other
+blocks may differ.  Norms within 1e-5 relative; logits and rebuilt vectors
+within 1e-4 + 1e-3 |ref| (both read the same records)."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import fibquant as F, estimator, paging, rope as orope
+
+import parity
+from test_gpu_parity import bf16_tensor
+
+torch = pytest.importorskip("torch")
+tq = pytest.importorskip("kv_cache_vector_05_amd")
+
+pytestmark = pytest.mark.gpu
+
+MARGIN = 1e-6
+
+
+def books(d, bits, seed):
+    """(oracle, GPU) codebooks: the same seeded signs; each side builds its own codewords."""
+    sigma = synth.codec_draws(d, 0, False, seed)[0]
+    g = tq.Codebook(d, bits, 0, "hadamard", sigma=sigma, block=2)
+    o = F.make_vq_codebook(d, 2, 1 << bits, sigma)
+    np.testing.assert_allclose(g.export()["levels"], o.code32, rtol=0, atol=1e-7)
+    return o, g
+
+
+def compare(o, enc, norm, codes, label):
+    g_idx = F.unpack_indices(codes, o.index_bits, o.d // 2)
+    near = enc.margin < MARGIN
+    bad = (g_idx != enc.idx) & ~near
+    assert bad.sum() <= int(1e-6 * (~near).sum()), f"{label}: {bad.sum()} index mismatches"
+    np.testing.assert_allclose(norm, enc.norm, rtol=1e-5, atol=1e-30, err_msg=f"{label}: norm")
+
+
+@pytest.mark.parametrize("d,bits,dtype,rope,H", [
+    (128, 4, "bf16", True, 8),     # rate 2 with RoPE keys
+    (128, 1, "f32", False, 3),     # rate 1/2: two codewords
+    (128, 5, "bf16", False, 2),    # rate 2.5: indices straddle words
+    (128, 8, "f32", True, 1),      # rate 4: 256 codewords
+    (64, 6, "bf16", True, 5),      # d = 64, rate 3, two vectors per wave
+    (64, 3, "f32", False, 4),      # rate 1.5
+])
+def test_vq_encode(d, bits, dtype, rope, H):
+    B, T, off, L = 2, 45, 7, 60
+    g = synth.rng(d + bits + H)
+    X = g.standard_normal((B, T, H, d)).astype(np.float32)
+    X[:, :, :, 3] *= np.float32(30.0)
+    X[0, 4] = 0.0
+    if dtype == "bf16":
+        xb = synth.bf16_round_bits(X)
+        X = synth.bf16_bits_to_f32(xb)
+        x_dev = bf16_tensor(xb)
+    else:
+        x_dev = torch.from_numpy(X).cuda()
+    o, gc = books(d, bits, 13)
+    rope_g = tq.rope_table(1e4, d, L) if rope else None
+    rope_o = orope.rope_table(1e4, d, L) if rope else None
+    kp = tq.Packed(gc, B * H * L)
+    kp.norm.fill_(-4.0)
+    tq.encode_kv(gc, None, x_dev, None, kp, None, tok_offset=off, L_cap=L, rope=rope_g)
+    torch.cuda.synchronize()
+    norm, _, codes, _ = kp.numpy()
+    nrm = norm.reshape(B * H, L)
+    assert np.all(nrm[:, :off] == -4.0) and np.all(nrm[:, off + T:] == -4.0)
+    idx = paging.contiguous_index(np.repeat(np.arange(B), H * T), np.tile(np.repeat(np.arange(H), T), B),
+                                  off + np.tile(np.arange(T), B * H), H, L)
+    enc = F.encode(o, parity.oracle_rows(X), pos=off + np.tile(np.arange(T), B * H) if rope else None, rope=rope_o)
+    compare(o, enc, norm[idx], codes[idx], f"vq encode d{d} b{bits} {dtype} rope={rope}")
+
+
+@pytest.mark.parametrize("d,bits", [(128, 4), (128, 7), (64, 2)])
+def test_vq_logits_topk_and_decoder(d, bits):
+    """Logits of GQA groups (12 queries per KV head: two blocks of up to 8),
+    a ragged length, top-k, and the decoder, over the oracle's records."""
+    B, Hq, H, L = 2, 24, 2, 700
+    g = synth.rng(50 + bits)
+    o, gc = books(d, bits, 21)
+    X = g.standard_normal((B * H * L, d))
+    enc = F.encode(o, X)
+    kp = tq.Packed.from_arrays(gc, enc.norm.astype(np.float32), np.zeros(0), enc.codes, np.zeros((len(X), 0)))
+    Q = g.standard_normal((B, Hq, d)).astype(np.float32)
+    qt = torch.from_numpy(Q).cuda()
+    lens = [700, 333]
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    lg = tq.attn_logits(gc, qt, kp, H, L, sl, out=torch.full((B, Hq, L), float("nan"), device="cuda")).cpu().numpy()
+    vals, tidx = tq.attn_logits(gc, qt, kp, H, L, sl, top_k=6)
+    vals, tidx = vals.cpu().numpy(), tidx.cpu().numpy()
+    norm32 = enc.norm.astype(np.float32).astype(np.float64)
+    G = Hq // H
+    for b in range(B):
+        for h in range(H):
+            rows = slice((b * H + h) * L, (b * H + h) * L + lens[b])
+            gs = slice(h * G, (h + 1) * G)
+            ref = F.logits(o, Q[b, gs] @ o.pi.T, norm32[rows], enc.codes[rows])
+            parity.assert_close(lg[b, gs, :lens[b]], ref, f"vq logits b={b} h={h}")
+            assert np.all(np.isnan(lg[b, gs, lens[b]:]))
+            for r in range(G):
+                parity.assert_close(vals[b, h * G + r], ref[r, tidx[b, h * G + r]], "vq top-k values")
+                kth = np.sort(ref[r])[::-1][5]
+                assert np.all(ref[r, tidx[b, h * G + r]] >= kth - (parity.ATOL + parity.RTOL * abs(kth)))
+    rec = tq.decode_vectors(gc, kp, first=100, count=900).cpu().numpy()
+    parity.assert_close(rec, F.reconstruct(o, norm32[100:1000], enc.codes[100:1000]), "vq decoder")
+
+
+def test_vq_appends_and_paged_scan():
+    """Autoregressive appends of vector-coded keys through a page table, then
+    the paged logit scan over them."""
+    B, H, Hq, d, bits, P, J, steps = 2, 2, 4, 128, 4, 64, 2, 90
+    g = synth.rng(60)
+    o, gc = books(d, bits, 23)
+    table = g.permutation(B * J + 2)[:B * J].astype(np.int32).reshape(B, J)
+    pg = tq.Pages(torch.from_numpy(table).cuda(), P, B * J + 2)
+    kp = tq.Packed(gc, pg.records(H))
+    rope_g = tq.rope_table(5e5, d, J * P + 1)
+    rope_o = orope.rope_table(5e5, d, J * P + 1)
+    K = synth.bf16_round_bits(g.standard_normal((steps, B, H, d)).astype(np.float32))
+    start = np.array([0, 17])
+    for s in range(steps):
+        pos = (s - start).astype(np.int32)
+        tq.append_kv(gc, None, bf16_tensor(K[s]), None, kp, None, torch.from_numpy(pos).cuda(), pages=pg, rope=rope_g)
+    torch.cuda.synchronize()
+    norm, _, codes, _ = kp.numpy()
+    Q = g.standard_normal((B, Hq, d)).astype(np.float32)
+    lens = steps - start
+    lg = tq.attn_logits(gc, torch.from_numpy(Q).cuda(), kp, H, None, torch.from_numpy(lens.astype(np.int32)).cuda(),
+                        rope=rope_g, pages=pg).cpu().numpy()
+    G = Hq // H
+    for b in range(B):
+        t = np.arange(lens[b])
+        x = synth.bf16_bits_to_f32(K[start[b] + t, b])
+        qp, _ = estimator.prep_query(o_as_scalar(o), Q[b], int(lens[b]), rope_o)
+        for h in range(H):
+            idx = paging.paged_index(table, P, H, b, h, t)
+            enc = F.encode(o, x[:, h], pos=t, rope=rope_o)
+            compare(o, enc, norm[idx], codes[idx], f"vq append b={b} h={h}")
+            ref = F.logits(o, qp[h * G:(h + 1) * G], norm[idx].astype(np.float64), codes[idx])
+            parity.assert_close(lg[b, h * G:(h + 1) * G, :lens[b]], ref, f"vq paged logits b={b} h={h}")
+
+
+def o_as_scalar(o):
+    """A view of the vector codebook with the attributes the query preparation
+    reads (rotation and an empty sketch)."""
+    class _Q:
+        pi = o.pi
+        sketch = np.zeros((0, o.d), np.float32)
+    return _Q()
+
+
+def test_vq_rejections():
+    o, gc = books(128, 4, 3)
+    kp = tq.Packed(gc, 64)
+    q = torch.zeros((1, 4, 128), device="cuda")
+    sl = torch.tensor([64], dtype=torch.int32, device="cuda")
+    with pytest.raises(tq.TQError) as ei:
+        tq.attn_decode(gc, gc, q, kp, kp, 1, 64, sl)
+    assert ei.value.code == -2
+    with pytest.raises(tq.TQError) as ei:
+        tq.decode_vectors(gc, kp, first=10, count=60)
+    assert ei.value.code == -1

@@ -122,8 +122,8 @@ def test_calibrated_init_rejects_bad_tables_before_any_gpu_work():
     assert init(None, [0.01], 0) == _lib.TQ_EINVAL                          # mu without a count
     qjl = _lib.tq_spec(64, 2, 32, _lib.TQ_ROT_HADAMARD, 0, _lib.TQ_CORR_QJL, 0)
     assert init(None, [0.01], 1, qjl) == _lib.TQ_EINVAL                     # mu for the QJL sketch
-    bad = _lib.tq_spec(64, 2, 64, _lib.TQ_ROT_HADAMARD, 0, _lib.TQ_CORR_SIGN, 1)
-    assert init(None, None, 0, bad) == _lib.TQ_EINVAL                       # reserved != 0
+    bad = _lib.tq_spec(64, 2, 64, _lib.TQ_ROT_HADAMARD, 0, _lib.TQ_CORR_SIGN, 2)
+    assert init(None, None, 0, bad) == _lib.TQ_EINVAL                       # a vector codebook with signs
     sk = np.zeros(64 * 64, np.float32)
     dr = _lib.tq_draws(None, None, sk.ctypes.data)
     assert L.tq_codebook_init_calibrated(C.byref(sp), C.byref(dr), None, None, 0, None,
