@@ -76,7 +76,7 @@ def parse():
                          "GPU's clocks take some 100 ms of load to settle)")
     ap.add_argument("--workload", default="llama8b",
                     choices=["llama8b", "llama70b", "esm650m", "vsearch", "llama8b-turboesm", "esm650m-turboesm",
-                             "llama8b-serve", "tiny"])
+                             "llama8b-serve", "llama8b-fib", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="keys in the oracle's sample (0: default)")
     return ap.parse_args()
@@ -226,6 +226,103 @@ def llama_report(st, timer, ms_step):
     else:
         cfg["qjl_rows"] = m
     return keys / (ms_step * 1e-3), "keys/s", kern, dom, extra, cfg
+
+
+# ------------------------------------------------------------ FibQuant codebooks
+FIB_BITS = 4  # 16 codewords per 2-coordinate block: 2 bits per coordinate
+
+
+def setup_fib(torch, tq, synth):
+    """The Llama-3.1-8B-shaped layer with FibQuant vector codebooks for keys
+    and values (k = 2, N = 16): encode K (RoPE), encode V, and the logit scan
+    of the 32 query heads over every cached key."""
+    B, Hq, H, L, d = 8, 32, 8, 32768, 128
+    K, V = synth.llama_kv_inputs("llama8b", seed=0, batch=B, ctx=L, hkv=H, d=d)
+    Q = synth.llama_q_inputs(seed=100, batch=B, hq=Hq, d=d)
+    st = {"B": B, "Hq": Hq, "H": H, "L": L, "d": d, "bits": FIB_BITS, "rope_base": 5e5, "host": (K, V, Q)}
+    st["K"], st["V"], st["Q"] = bf16_dev(torch, K), bf16_dev(torch, V), bf16_dev(torch, Q)
+    st["ck"] = tq.Codebook(d, FIB_BITS, 0, "hadamard", seed=synth.K_SEED, block=2)
+    st["cv"] = tq.Codebook(d, FIB_BITS, 0, "hadamard", seed=synth.V_SEED, block=2)
+    st["kp"], st["vp"] = tq.Packed(st["ck"], B * H * L), tq.Packed(st["cv"], B * H * L)
+    st["rope"] = tq.rope_table(5e5, d, L + 1)
+    st["sl"] = torch.full((B,), L, dtype=torch.int32, device="cuda")
+    st["logits"] = torch.empty((B, Hq, L), dtype=torch.float32, device="cuda")
+    st["ws_l"] = torch.empty(max(1, tq.workspace_bytes(st["ck"], None, tq.TQ_OP_LOGITS, B, Hq, H, L, 0)),
+                             dtype=torch.uint8, device="cuda")
+    st["calls"] = [
+        ("encode_k", tq.encode_kv(st["ck"], None, st["K"], None, st["kp"], None, L_cap=L, rope=st["rope"],
+                                  prepare=True)),
+        ("encode_v", tq.encode_kv(None, st["cv"], None, st["V"], None, st["vp"], L_cap=L, prepare=True)),
+        ("logits", tq.attn_logits(st["ck"], st["Q"], st["kp"], H, L, st["sl"], rope=st["rope"], out=st["logits"],
+                                  workspace=st["ws_l"], prepare=True)[0]),
+    ]
+    return st
+
+
+def fib_report(st, timer, ms_step):
+    B, Hq, H, L, d, bits = (st[k] for k in ("B", "Hq", "H", "L", "d", "bits"))
+    keys = B * H * L
+    rec = 4 + 4 * ((d // 2 * bits + 31) // 32)
+    enc_ms, n = timer.mean_ms("encode_k")
+    encv_ms, _ = timer.mean_ms("encode_v")
+    log_ms, _ = timer.mean_ms("logits")
+    kern = {"encode_k": {"ms": enc_ms, "launches": n, "alg_bytes": keys * (2 * d + rec), "units": keys},
+            "encode_v": {"ms": encv_ms, "alg_bytes": keys * (2 * d + rec), "units": keys},
+            "logits": {"ms": log_ms, "alg_bytes": keys * (rec + 4 * Hq // H), "units": keys}}
+    for k in kern.values():
+        k["GBps"] = k["alg_bytes"] / (k["ms"] * 1e-3) / 1e9
+        k["hbm_frac"] = k["GBps"] / HBM_PEAK_GBS
+    dom = max(kern, key=lambda x: kern[x]["ms"])
+    extra = {"logit_keys_per_s": keys / (log_ms * 1e-3), "logit_hbm_frac": kern["logits"]["hbm_frac"],
+             "encode_vectors_per_s": 2 * keys / ((enc_ms + encv_ms) * 1e-3)}
+    cfg = {"workload": "Llama-3.1-8B-shaped layer with FibQuant vector codebooks (encode K, V; logits)", "batch": B,
+           "q_heads": Hq, "kv_heads": H, "head_dim": d, "context": L, "block": 2, "codewords": 1 << bits,
+           "bits_per_coordinate": bits / 2, "input_dtype": "bf16", "rope_base": st["rope_base"],
+           "record_bytes": rec}
+    return keys / (ms_step * 1e-3), "keys/s", kern, dom, extra, cfg
+
+
+def cpu_baseline_fib(st, budget_s=10.0):
+    """The oracle on a bounded sample of the FibQuant step: (sequence, KV
+    head) pairs in order, keys (RoPE) and values encoded and the pair's 4
+    query heads scored, until about budget_s seconds."""
+    import synth
+    from oracle import fibquant as F, rng, rope as orope
+    K, V, Q = st["host"]
+    B, Hq, H, L, d, bits = (st[k] for k in ("B", "Hq", "H", "L", "d", "bits"))
+    G = Hq // H
+    t0 = time.perf_counter()
+    ock = F.make_vq_codebook(d, 2, 1 << bits, rng.signs(synth.K_SEED, d))
+    ocv = F.make_vq_codebook(d, 2, 1 << bits, rng.signs(synth.V_SEED, d), code=ock.code32)
+    t_setup = time.perf_counter() - t0
+    rope = orope.rope_table(st["rope_base"], d, L + 1)
+    from oracle.rope import apply_rope
+    done, pairs, dt = 0, 0, 0.0
+    n = 4096  # keys per pair in the sample (the oracle's nearest-codeword search is slow)
+    for b in range(B):
+        for kh in range(H):
+            if dt >= budget_s:
+                break
+            kx = synth.bf16_bits_to_f32(K[b, :n, kh])
+            vx = synth.bf16_bits_to_f32(V[b, :n, kh])
+            q = synth.bf16_bits_to_f32(Q[b, kh * G:(kh + 1) * G])
+            t1 = time.perf_counter()
+            ek = F.encode(ock, kx, pos=np.arange(n), rope=rope)
+            F.encode(ocv, vx)
+            qp = apply_rope(q, np.full(G, L), rope[0], rope[1]) @ ock.pi.T
+            F.logits(ock, qp, ek.norm, ek.codes)
+            dt += time.perf_counter() - t1
+            done += n
+            pairs += 1
+    try:
+        import threadpoolctl
+        threads = max(p["num_threads"] for p in threadpoolctl.threadpool_info()) or 1
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    return {"value": done / dt, "unit": "keys/s", "cores": threads, "kind": "oracle",
+            "sample": f"{pairs} (sequence, KV head) pairs, the first {n} keys and values of each encoded and scored "
+                      f"for {G} query heads by the oracle, {dt:.1f} s on the host (codebook built beforehand, "
+                      f"{t_setup:.1f} s)"}
 
 
 # ------------------------------------------------------------ serving step
@@ -571,6 +668,9 @@ def main():
     elif wl == "llama8b-serve":
         st = setup_serve(torch, tq, synth)
         report = lambda t, ms: serve_report(st, t, ms)
+    elif wl == "llama8b-fib":
+        st = setup_fib(torch, tq, synth)
+        report = lambda t, ms: fib_report(st, t, ms)
     else:
         raise SystemExit("tiny is a parity case, not a benchmark workload")
     step = lambda t: run_calls(st, t)
@@ -615,7 +715,10 @@ def main():
             "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "f32", "data": "synthetic", "config": cfg, "roofline": roof,
             "kernels": kern, **extra}
-    if not args.no_cpu_baseline and wl == "llama8b-serve":
+    if not args.no_cpu_baseline and wl == "llama8b-fib":
+        print("[bench] cpu baseline (oracle on a sample)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline_fib(st)
+    elif not args.no_cpu_baseline and wl == "llama8b-serve":
         print("[bench] cpu baseline (oracle on a sample)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline_serve(st)
     elif not args.no_cpu_baseline and wl in ("llama8b", "llama70b", "llama8b-turboesm"):

@@ -24,6 +24,13 @@
 // the sketch MFMAs give way to byte-wise sign packing.  MODE 2 also skips the
 // rotation (values quantised in their original coordinates): the lane loads
 // its output coordinates straight from the input.
+// Vector codebooks (FibQuant summary, sections 2.1-2.3; MODE 3): after the
+// rotation each lane holds 32 (d = 128) or 16 (d = 64) whole blocks of two
+// coordinates (registers r, r + 1 for even r), so the nearest codeword - the
+// largest <y, c> - |c|^2 / 2, ties to the smaller index - is a search over
+// the shared codebook (registers for N <= 16, LDS broadcast above) with no
+// data exchange; the indices are packed LSB first, lane half 1's moved up
+// by two blocks, and the pair's words merged.
 // Blocks are persistent (one resident round, grid-stride over tiles) so each
 // block stages its tables in LDS once; tiles run token block, then sequence,
 // then head, so a block's four waves encode four heads of the same tokens and
@@ -206,18 +213,21 @@ __device__ __forceinline__ void rope_stage_store(f32x4* lds, const int (&tab)[NQ
 
 // MODE 0: Hadamard rotation, Gaussian sketch of the residual and gamma;
 // 1: Hadamard rotation, sign of each residual coordinate; 2: no rotation,
-// sign of each residual coordinate.
+// sign of each residual coordinate; 3: Hadamard rotation, nearest codeword
+// of every two-coordinate block in a vector codebook of 2^BITS codewords.
 template <int D, int BITS, int M, bool BF16, bool ROPE, int MODE>
 __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
-    constexpr bool SGN = MODE != 0;
+    constexpr bool SGN = MODE == 1 || MODE == 2;
     constexpr bool NOROT = MODE == 2;
+    constexpr bool VQ = MODE == 3;
     static_assert(!SGN || M == D, "the sign correction keeps one bit per coordinate");
+    static_assert(!VQ || M == 0, "vector codebooks keep no sketch");
     constexpr int HALF = D / 2;
     constexpr int NOB = D / 32;            // 32-coordinate output blocks of H
     constexpr int NKB = D / 16;            // 16-coordinate input steps of the MFMA
     constexpr bool EXACT = BF16 && !ROPE && !NOROT;  // raw bf16 inputs are the MFMA operand as loaded
-    constexpr int KH = 1 << (BITS - 1);
-    constexpr int CW = BITS * D / 32;      // code words per record
+    constexpr int KH = VQ ? 1 : 1 << (BITS - 1);
+    constexpr int CW = VQ ? BITS * D / 64 : BITS * D / 32;  // code words per record
     constexpr int NRB = M / 32;            // sketch row blocks (= sign words)
     constexpr int NP = D / 16;             // sketch K-steps: chunks of 8 values per lane
     constexpr bool SKETCH = M > 0 && !SGN;  // Gaussian sketch on the matrix cores
@@ -235,12 +245,22 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
     __shared__ uint4 s_had[NOROT ? 1 : (NEG_LDS ? 2 : 1) * NKB * 64];
     // scaled levels, indexed by code (3 and 4 bits: looked up by K/2 + c')
     __shared__ float s_lvl[16];
+    // vector codebook, scaled: {c0, c1, -|c|^2 / 2} (LDS above 16 codewords)
+    constexpr int NV = VQ ? 1 << BITS : 1;
+    constexpr bool VQREG = VQ && NV <= 16;
+    __shared__ float4 s_vq[VQ && !VQREG ? NV : 1];
 
     if constexpr (SKETCH) {
         const half8* src = reinterpret_cast<const half8*>(p.sketch_mfma);
         for (int i = threadIdx.x; i < SKN; i += blockDim.x) s_sk[i] = src[i];
     }
-    if (threadIdx.x < 16) s_lvl[threadIdx.x] = threadIdx.x < 2 * KH ? p.levels[threadIdx.x] * ESCALE : 0.0f;
+    if (!VQ && threadIdx.x < 16) s_lvl[threadIdx.x] = threadIdx.x < 2 * KH ? p.levels[threadIdx.x] * ESCALE : 0.0f;
+    if constexpr (VQ && !VQREG) {
+        for (int i = threadIdx.x; i < NV; i += blockDim.x) {
+            const float c0 = p.levels[2 * i] * ESCALE, c1 = p.levels[2 * i + 1] * ESCALE;
+            s_vq[i] = make_float4(c0, c1, -0.5f * (c0 * c0 + c1 * c1), 0.0f);
+        }
+    }
     for (int i = threadIdx.x; i < (NOROT ? 0 : NKB * 64); i += blockDim.x) {
         const int kb = i >> 6, row = i & 31, hh = (i >> 5) & 1;
         uint32_t w[4];
@@ -273,10 +293,24 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
 
     // upper halves of the symmetric tables, scaled
     float pt[KH > 1 ? KH - 1 : 1], pl[KH];
+    if constexpr (!VQ) {
 #pragma unroll
-    for (int k = 0; k + 1 < KH; ++k) pt[k] = p.thresholds[KH + k] * ESCALE;
+        for (int k = 0; k + 1 < KH; ++k) pt[k] = p.thresholds[KH + k] * ESCALE;
 #pragma unroll
-    for (int k = 0; k < KH; ++k) pl[k] = p.levels[KH + k] * ESCALE;
+        for (int k = 0; k < KH; ++k) pl[k] = p.levels[KH + k] * ESCALE;
+    }
+    // small vector codebooks in registers, scaled: the coordinates in scalar
+    // registers (one scalar operand per FMA), -|c|^2 / 2 in vector registers
+    float vc0[VQREG ? NV : 1], vc1[VQREG ? NV : 1], vnh[VQREG ? NV : 1];
+    if constexpr (VQREG) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const float c0 = p.levels[2 * i] * ESCALE, c1 = p.levels[2 * i + 1] * ESCALE;
+            vc0[i] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, c0)));
+            vc1[i] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, c1)));
+            vnh[i] = -0.5f * (c0 * c0 + c1 * c1);
+        }
+    }
     const float yscale = ESCALE / sqrtf((float)D);
 
     // RoPE rows of the block's 32 tokens, staged in LDS when the block's four
@@ -608,196 +642,266 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
             }
         }
 
-        // per 8-value chunk pc (block pc/2, registers 8(pc%2)..+7): quantise,
-        // residual, pack, and feed the residual's fp16 hi/lo parts to the
-        // sketch MFMAs.  Codes are packed at lane half 0's positions; lane
-        // half 1's are moved into place afterwards.
-        uint32_t cw[CW];
+        if constexpr (VQ) {
+            // block j = 16 ob + 4 (r/4) + 2 h + (r%4)/2 is registers r, r + 1
+            // (r even); indices are packed at lane half 0's positions (h = 0)
+            uint32_t cw[CW];
 #pragma unroll
-        for (int w = 0; w < CW; ++w) cw[w] = 0u;
-        float gg = 0.0f;
-        floatx16 sacc[SKETCH ? NRB : 1];
+            for (int w = 0; w < CW; ++w) cw[w] = 0u;
 #pragma unroll
-        for (int rb = 0; rb < (SKETCH ? NRB : 0); ++rb)
+            for (int ob = 0; ob < NOB; ++ob)
 #pragma unroll
-            for (int q = 0; q < 16; ++q) sacc[rb][q] = 0.0f;
-        // sign correction: per block, the negative-residual flags of the lane's
-        // coordinates, byte a = coordinates 8a + 4h + 0..3 in bits 0..3
-        uint32_t wsg[SGN ? NOB : 1];
+                for (int r = 0; r < 16; r += 2) {
+                    const float y0 = EXACT ? fmaf(acc[ob][r], scale, 0.0f) : acc[ob][r];
+                    const float y1 = EXACT ? fmaf(acc[ob][r + 1], scale, 0.0f) : acc[ob][r + 1];
+                    float bs;
+                    uint32_t bi = 0u;
+                    if constexpr (VQREG) {
+                        bs = fmaf(vc0[0], y0, fmaf(vc1[0], y1, vnh[0]));
 #pragma unroll
-        for (int ob = 0; ob < (SGN ? NOB : 1); ++ob) wsg[ob] = 0u;
-#pragma unroll
-        for (int pc = 0; pc < NP; ++pc) {
-            const int ob = pc >> 1, hf = pc & 1;
-            float e[8];
-            if constexpr (BITS >= 3) {
-                // byte-packed codes: the four codes of a group (t = 4g..4g+3,
-                // one 8-coordinate row a = 2hf + g) as bytes of P, then the
-                // negative coordinates complemented at once through a byte
-                // mask built from the four sign bits (v_perm byte selects)
-                float yv[8];
-                uint32_t xu[8];
-#pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    // + 0: a zero vector's -0 coordinates count as +0 (code of y = 0)
-                    yv[t] = EXACT ? fmaf(acc[ob][8 * hf + t], scale, 0.0f) : acc[ob][8 * hf + t];
-                    xu[t] = upper_code<BITS>(fabsf(yv[t]), pt);
-                }
-#pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    e[t] = yv[t] - __builtin_copysignf(s_lvl[xu[t]], yv[t]);
-                    if constexpr (!SGN) gg = fmaf(e[t], e[t], gg);
-                }
-#pragma unroll
-                for (int g = 0; g < 2; ++g) {
-                    const int t0 = 4 * g, a = 2 * hf + g;
-                    const uint32_t P = xu[t0] | (xu[t0 + 1] << 8) | (xu[t0 + 2] << 16) | (xu[t0 + 3] << 24);
-                    const uint32_t Mk = __builtin_amdgcn_perm(__float_as_uint(yv[t0 + 1]), __float_as_uint(yv[t0]), 0x0C0C0B09u) |
-                                        __builtin_amdgcn_perm(__float_as_uint(yv[t0 + 3]), __float_as_uint(yv[t0 + 2]), 0x0B090C0Cu);
-                    const uint32_t C = P ^ (Mk & (0x01010101u * (2u * KH - 1u)));
-                    if constexpr (BITS == 3) {
-                        // lane half 0 positions: rows 0-2 fill bits 0-2 of every
-                        // byte of word a; row 3 puts its low bits at 6-7 of word 0
-                        // and its high bit at 6 of word 2
-                        if (a < 3) {
-                            cw[3 * ob + a] |= C;
-                        } else {
-                            cw[3 * ob] |= (C & 0x03030303u) << 6;
-                            cw[3 * ob + 2] |= (C & 0x04040404u) << 4;
+                        for (int c = 1; c < NV; ++c) {
+                            const float sc = fmaf(vc0[c], y0, fmaf(vc1[c], y1, vnh[c]));
+                            if (sc > bs) {
+                                bs = sc;
+                                bi = (uint32_t)c;
+                            }
                         }
                     } else {
-                        // nibble b of word 4 ob + a
-                        const uint32_t t2 = C | (C >> 4);
-                        cw[4 * ob + a] |= __builtin_amdgcn_perm(t2, t2, 0x0C0C0200u);
+                        bs = -INFINITY;
+#pragma unroll 2
+                        for (int c = 0; c < NV; ++c) {
+                            const float4 cv = s_vq[c];
+                            const float sc = fmaf(cv.x, y0, fmaf(cv.y, y1, cv.z));
+                            if (sc > bs) {
+                                bs = sc;
+                                bi = (uint32_t)c;
+                            }
+                        }
+                    }
+                    const int o = (16 * ob + 4 * (r / 4) + (r % 4) / 2) * BITS;
+                    cw[o >> 5] |= bi << (o & 31);
+                    if ((o & 31) + BITS > 32) cw[(o >> 5) + 1] |= bi >> (32 - (o & 31));
+                }
+            // lane half 1's blocks sit two blocks (2 BITS bits) higher
+            if (h) {
+#pragma unroll
+                for (int w = CW - 1; w > 0; --w) cw[w] = (cw[w] << (2 * BITS)) | (cw[w - 1] >> (32 - 2 * BITS));
+                cw[0] <<= 2 * BITS;
+            }
+            // merge the pair's bits; lane half h stores its share of the words
+            constexpr int HW = (CW + 1) / 2;
+#pragma unroll
+            for (int w = 0; w < CW; ++w) {
+                const Swap sw = swap32(__uint_as_float(cw[w]));
+                cw[w] = __float_as_uint(sw.r0) | __float_as_uint(sw.r1);
+            }
+            if (valid) {
+                uint32_t* dst = p.codes + n * CW;
+                if constexpr (CW % 8 == 0) {
+#pragma unroll
+                    for (int k = 0; k < HW / 4; ++k) {
+                        const int w0 = h * HW + 4 * k;
+                        reinterpret_cast<uint4*>(dst + h * HW)[k] = make_uint4(cw[w0], cw[w0 + 1], cw[w0 + 2], cw[w0 + 3]);
+                    }
+                } else {
+#pragma unroll
+                    for (int w = 0; w < CW; ++w)
+                        if ((w >= HW) == (h == 1)) dst[w] = cw[w];
+                }
+                if (h == 0) p.norm[n] = nu;
+            }
+        } else {
+            // per 8-value chunk pc (block pc/2, registers 8(pc%2)..+7): quantise,
+            // residual, pack, and feed the residual's fp16 hi/lo parts to the
+            // sketch MFMAs.  Codes are packed at lane half 0's positions; lane
+            // half 1's are moved into place afterwards.
+            uint32_t cw[CW];
+    #pragma unroll
+            for (int w = 0; w < CW; ++w) cw[w] = 0u;
+            float gg = 0.0f;
+            floatx16 sacc[SKETCH ? NRB : 1];
+    #pragma unroll
+            for (int rb = 0; rb < (SKETCH ? NRB : 0); ++rb)
+    #pragma unroll
+                for (int q = 0; q < 16; ++q) sacc[rb][q] = 0.0f;
+            // sign correction: per block, the negative-residual flags of the lane's
+            // coordinates, byte a = coordinates 8a + 4h + 0..3 in bits 0..3
+            uint32_t wsg[SGN ? NOB : 1];
+    #pragma unroll
+            for (int ob = 0; ob < (SGN ? NOB : 1); ++ob) wsg[ob] = 0u;
+    #pragma unroll
+            for (int pc = 0; pc < NP; ++pc) {
+                const int ob = pc >> 1, hf = pc & 1;
+                float e[8];
+                if constexpr (BITS >= 3) {
+                    // byte-packed codes: the four codes of a group (t = 4g..4g+3,
+                    // one 8-coordinate row a = 2hf + g) as bytes of P, then the
+                    // negative coordinates complemented at once through a byte
+                    // mask built from the four sign bits (v_perm byte selects)
+                    float yv[8];
+                    uint32_t xu[8];
+    #pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        // + 0: a zero vector's -0 coordinates count as +0 (code of y = 0)
+                        yv[t] = EXACT ? fmaf(acc[ob][8 * hf + t], scale, 0.0f) : acc[ob][8 * hf + t];
+                        xu[t] = upper_code<BITS>(fabsf(yv[t]), pt);
+                    }
+    #pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        e[t] = yv[t] - __builtin_copysignf(s_lvl[xu[t]], yv[t]);
+                        if constexpr (!SGN) gg = fmaf(e[t], e[t], gg);
+                    }
+    #pragma unroll
+                    for (int g = 0; g < 2; ++g) {
+                        const int t0 = 4 * g, a = 2 * hf + g;
+                        const uint32_t P = xu[t0] | (xu[t0 + 1] << 8) | (xu[t0 + 2] << 16) | (xu[t0 + 3] << 24);
+                        const uint32_t Mk = __builtin_amdgcn_perm(__float_as_uint(yv[t0 + 1]), __float_as_uint(yv[t0]), 0x0C0C0B09u) |
+                                            __builtin_amdgcn_perm(__float_as_uint(yv[t0 + 3]), __float_as_uint(yv[t0 + 2]), 0x0B090C0Cu);
+                        const uint32_t C = P ^ (Mk & (0x01010101u * (2u * KH - 1u)));
+                        if constexpr (BITS == 3) {
+                            // lane half 0 positions: rows 0-2 fill bits 0-2 of every
+                            // byte of word a; row 3 puts its low bits at 6-7 of word 0
+                            // and its high bit at 6 of word 2
+                            if (a < 3) {
+                                cw[3 * ob + a] |= C;
+                            } else {
+                                cw[3 * ob] |= (C & 0x03030303u) << 6;
+                                cw[3 * ob + 2] |= (C & 0x04040404u) << 4;
+                            }
+                        } else {
+                            // nibble b of word 4 ob + a
+                            const uint32_t t2 = C | (C >> 4);
+                            cw[4 * ob + a] |= __builtin_amdgcn_perm(t2, t2, 0x0C0C0200u);
+                        }
+                    }
+                } else {
+    #pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        // + 0: a zero vector's -0 coordinates count as +0 (code of y = 0)
+                        const float y = EXACT ? fmaf(acc[ob][8 * hf + t], scale, 0.0f) : acc[ob][8 * hf + t];
+                        const uint32_t code = quantise<BITS>(y, pt, pl, &e[t]);
+                        if constexpr (!SGN) gg = fmaf(e[t], e[t], gg);
+                        dev::code_put(cw, dev::code_loc(32 * ob + 8 * (2 * hf + (t >> 2)) + (t & 3), BITS), BITS, code);
                     }
                 }
-            } else {
-#pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    // + 0: a zero vector's -0 coordinates count as +0 (code of y = 0)
-                    const float y = EXACT ? fmaf(acc[ob][8 * hf + t], scale, 0.0f) : acc[ob][8 * hf + t];
-                    const uint32_t code = quantise<BITS>(y, pt, pl, &e[t]);
-                    if constexpr (!SGN) gg = fmaf(e[t], e[t], gg);
-                    dev::code_put(cw, dev::code_loc(32 * ob + 8 * (2 * hf + (t >> 2)) + (t & 3), BITS), BITS, code);
+                if constexpr (SGN) {
+                    // the four flags of group g as bytes 0xFF / 0x00 (v_perm sign
+                    // selects), one bit kept per byte, summed into byte 3 by a
+                    // multiply and moved to byte a = 2 hf + g of the block's word
+    #pragma unroll
+                    for (int g = 0; g < 2; ++g) {
+                        const int a = 2 * hf + g;
+                        const uint32_t f0 = __float_as_uint(e[4 * g]), f1 = __float_as_uint(e[4 * g + 1]);
+                        const uint32_t f2 = __float_as_uint(e[4 * g + 2]), f3 = __float_as_uint(e[4 * g + 3]);
+                        const uint32_t sb = (__builtin_amdgcn_perm(f1, f0, 0x0C0C0B09u) | __builtin_amdgcn_perm(f3, f2, 0x0B090C0Cu)) &
+                                            0x08040201u;
+                        wsg[ob] = __builtin_amdgcn_perm(sb * 0x01010101u, wsg[ob],
+                                                        (0x03020100u & ~(0xFFu << (8 * a))) | (0x07u << (8 * a)));
+                    }
                 }
+                if constexpr (SKETCH) {
+                    half8 ehi, elo;
+                    split_f16(e, ehi, elo);
+    #pragma unroll
+                    for (int rb = 0; rb < NRB; ++rb) {
+                        const half8 shi = s_sk[((rb * NP + pc) * 2 + 0) * 64 + lane];
+                        sacc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(shi, ehi, sacc[rb], 0, 0, 0);
+                    }
+    #pragma unroll
+                    for (int rb = 0; rb < NRB; ++rb) {
+                        const half8 shi = s_sk[((rb * NP + pc) * 2 + 0) * 64 + lane];
+                        sacc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(shi, elo, sacc[rb], 0, 0, 0);
+                    }
+    #pragma unroll
+                    for (int rb = 0; rb < NRB; ++rb) {
+                        const half8 slo = s_sk[((rb * NP + pc) * 2 + 1) * 64 + lane];
+                        sacc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(slo, ehi, sacc[rb], 0, 0, 0);
+                    }
+                }
+                // (per-coordinate packing: the chunk's codes are merged into the
+                // words here, not at the final store, which would keep every
+                // compare mask alive)
+                if constexpr (BITS < 3) {
+    #pragma unroll
+                    for (int w = 0; w < CW; ++w) asm volatile("" : "+v"(cw[w]));
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
+            {
+                const Swap sw = swap32(gg);
+                gg = sw.r0 + sw.r1;
+            }
+            const float gamma = sqrtf(gg) * (1.0f / ESCALE);
+
+            // lane half 1's coordinates are 4 above lane half 0's in every block of
+            // 8: for b = 1, 2, 4 its codes sit 4b bits higher in the same words.
+            // For b = 3 they sit 3 bits higher in each byte, except the group's
+            // last four, whose low bits go to word 1 (not 0) at the same place
+            // and whose high bit sits one bit higher in word 2.
+            if constexpr (BITS == 3) {
+    #pragma unroll
+                for (int g = 0; g < NOB; ++g) {
+                    const uint32_t w0 = cw[3 * g], w1 = cw[3 * g + 1], w2 = cw[3 * g + 2];
+                    cw[3 * g] = h ? (w0 & 0x07070707u) << 3 : w0;
+                    cw[3 * g + 1] = h ? (w1 << 3) | (w0 & 0xC0C0C0C0u) : w1;
+                    cw[3 * g + 2] = h ? ((w2 & 0x07070707u) << 3) | ((w2 & 0x40404040u) << 1) : w2;
+                }
+            } else {
+                const int sh = h * 4 * BITS;
+    #pragma unroll
+                for (int w = 0; w < CW; ++w) cw[w] <<= sh;
+            }
+            // merge the lane pair's bits: lane half h keeps words [h CW/2, (h+1) CW/2)
+    #pragma unroll
+            for (int k = 0; k < CW / 2; ++k) {
+                float a = __uint_as_float(cw[k]), b = __uint_as_float(cw[k + CW / 2]);
+                xchg(a, b);
+                cw[k] = __float_as_uint(a) | __float_as_uint(b);
+            }
+
+            if (valid) {
+                uint32_t* dst = p.codes + n * CW + h * (CW / 2);
+    #pragma unroll
+                for (int k = 0; k < CW / 2; ++k) dst[k] = cw[k];
+                if (h == 0) p.norm[n] = nu;
+                else if (SKETCH) p.rnorm[n] = gamma;
+            }
+
             if constexpr (SGN) {
-                // the four flags of group g as bytes 0xFF / 0x00 (v_perm sign
-                // selects), one bit kept per byte, summed into byte 3 by a
-                // multiply and moved to byte a = 2 hf + g of the block's word
-#pragma unroll
-                for (int g = 0; g < 2; ++g) {
-                    const int a = 2 * hf + g;
-                    const uint32_t f0 = __float_as_uint(e[4 * g]), f1 = __float_as_uint(e[4 * g + 1]);
-                    const uint32_t f2 = __float_as_uint(e[4 * g + 2]), f3 = __float_as_uint(e[4 * g + 3]);
-                    const uint32_t sb = (__builtin_amdgcn_perm(f1, f0, 0x0C0C0B09u) | __builtin_amdgcn_perm(f3, f2, 0x0B090C0Cu)) &
-                                        0x08040201u;
-                    wsg[ob] = __builtin_amdgcn_perm(sb * 0x01010101u, wsg[ob],
-                                                    (0x03020100u & ~(0xFFu << (8 * a))) | (0x07u << (8 * a)));
+                // a set flag is a negative residual: complement, place lane half
+                // 1's nibbles 4 bits up, merge the pair; lane half h stores the
+                // blocks of its parity
+    #pragma unroll
+                for (int ob = 0; ob < NOB; ++ob) {
+                    uint32_t wb = (~wsg[ob] & 0x0F0F0F0Fu) << (4 * h);
+                    const Swap sw = swap32(__uint_as_float(wb));
+                    wb = __float_as_uint(sw.r0) | __float_as_uint(sw.r1);
+                    if (valid && (ob & 1) == h) p.signs[n * NOB + ob] = wb;
                 }
             }
             if constexpr (SKETCH) {
-                half8 ehi, elo;
-                split_f16(e, ehi, elo);
-#pragma unroll
+                // D[i][j]: j = lane % 32 (vector), i = 8*(r/4) + 4*(lane/32) + r%4 (sketch row)
+    #pragma unroll
                 for (int rb = 0; rb < NRB; ++rb) {
-                    const half8 shi = s_sk[((rb * NP + pc) * 2 + 0) * 64 + lane];
-                    sacc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(shi, ehi, sacc[rb], 0, 0, 0);
+                    // per byte b: the sign bits of rows 8b + 4h + 0..3 as 0xFF/0x00
+                    // bytes (v_perm sign selects), one bit kept per byte, gathered
+                    // into byte 3 by a multiply and moved to byte b; a set bit is
+                    // a negative value, so the word is complemented at the end
+                    uint32_t wb = 0;
+    #pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        const uint32_t f0 = __float_as_uint(sacc[rb][4 * b]), f1 = __float_as_uint(sacc[rb][4 * b + 1]);
+                        const uint32_t f2 = __float_as_uint(sacc[rb][4 * b + 2]), f3 = __float_as_uint(sacc[rb][4 * b + 3]);
+                        const uint32_t sb = (__builtin_amdgcn_perm(f1, f0, 0x0C0C0B09u) | __builtin_amdgcn_perm(f3, f2, 0x0B090C0Cu)) &
+                                            0x08040201u;
+                        // byte 3 of the product = bits 0..3; v_perm puts it at byte b of wb
+                        wb = __builtin_amdgcn_perm(sb * 0x01010101u, wb, (0x03020100u & ~(0xFFu << (8 * b))) | (0x07u << (8 * b)));
+                    }
+                    wb = (~wb & 0x0F0F0F0Fu) << (4 * h);
+                    const Swap sw = swap32(__uint_as_float(wb));
+                    wb = __float_as_uint(sw.r0) | __float_as_uint(sw.r1);
+                    if (valid && (rb & 1) == h) p.signs[n * NRB + rb] = wb;
                 }
-#pragma unroll
-                for (int rb = 0; rb < NRB; ++rb) {
-                    const half8 shi = s_sk[((rb * NP + pc) * 2 + 0) * 64 + lane];
-                    sacc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(shi, elo, sacc[rb], 0, 0, 0);
-                }
-#pragma unroll
-                for (int rb = 0; rb < NRB; ++rb) {
-                    const half8 slo = s_sk[((rb * NP + pc) * 2 + 1) * 64 + lane];
-                    sacc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(slo, ehi, sacc[rb], 0, 0, 0);
-                }
-            }
-            // (per-coordinate packing: the chunk's codes are merged into the
-            // words here, not at the final store, which would keep every
-            // compare mask alive)
-            if constexpr (BITS < 3) {
-#pragma unroll
-                for (int w = 0; w < CW; ++w) asm volatile("" : "+v"(cw[w]));
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        {
-            const Swap sw = swap32(gg);
-            gg = sw.r0 + sw.r1;
-        }
-        const float gamma = sqrtf(gg) * (1.0f / ESCALE);
-
-        // lane half 1's coordinates are 4 above lane half 0's in every block of
-        // 8: for b = 1, 2, 4 its codes sit 4b bits higher in the same words.
-        // For b = 3 they sit 3 bits higher in each byte, except the group's
-        // last four, whose low bits go to word 1 (not 0) at the same place
-        // and whose high bit sits one bit higher in word 2.
-        if constexpr (BITS == 3) {
-#pragma unroll
-            for (int g = 0; g < NOB; ++g) {
-                const uint32_t w0 = cw[3 * g], w1 = cw[3 * g + 1], w2 = cw[3 * g + 2];
-                cw[3 * g] = h ? (w0 & 0x07070707u) << 3 : w0;
-                cw[3 * g + 1] = h ? (w1 << 3) | (w0 & 0xC0C0C0C0u) : w1;
-                cw[3 * g + 2] = h ? ((w2 & 0x07070707u) << 3) | ((w2 & 0x40404040u) << 1) : w2;
-            }
-        } else {
-            const int sh = h * 4 * BITS;
-#pragma unroll
-            for (int w = 0; w < CW; ++w) cw[w] <<= sh;
-        }
-        // merge the lane pair's bits: lane half h keeps words [h CW/2, (h+1) CW/2)
-#pragma unroll
-        for (int k = 0; k < CW / 2; ++k) {
-            float a = __uint_as_float(cw[k]), b = __uint_as_float(cw[k + CW / 2]);
-            xchg(a, b);
-            cw[k] = __float_as_uint(a) | __float_as_uint(b);
-        }
-
-        if (valid) {
-            uint32_t* dst = p.codes + n * CW + h * (CW / 2);
-#pragma unroll
-            for (int k = 0; k < CW / 2; ++k) dst[k] = cw[k];
-            if (h == 0) p.norm[n] = nu;
-            else if (SKETCH) p.rnorm[n] = gamma;
-        }
-
-        if constexpr (SGN) {
-            // a set flag is a negative residual: complement, place lane half
-            // 1's nibbles 4 bits up, merge the pair; lane half h stores the
-            // blocks of its parity
-#pragma unroll
-            for (int ob = 0; ob < NOB; ++ob) {
-                uint32_t wb = (~wsg[ob] & 0x0F0F0F0Fu) << (4 * h);
-                const Swap sw = swap32(__uint_as_float(wb));
-                wb = __float_as_uint(sw.r0) | __float_as_uint(sw.r1);
-                if (valid && (ob & 1) == h) p.signs[n * NOB + ob] = wb;
-            }
-        }
-        if constexpr (SKETCH) {
-            // D[i][j]: j = lane % 32 (vector), i = 8*(r/4) + 4*(lane/32) + r%4 (sketch row)
-#pragma unroll
-            for (int rb = 0; rb < NRB; ++rb) {
-                // per byte b: the sign bits of rows 8b + 4h + 0..3 as 0xFF/0x00
-                // bytes (v_perm sign selects), one bit kept per byte, gathered
-                // into byte 3 by a multiply and moved to byte b; a set bit is
-                // a negative value, so the word is complemented at the end
-                uint32_t wb = 0;
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const uint32_t f0 = __float_as_uint(sacc[rb][4 * b]), f1 = __float_as_uint(sacc[rb][4 * b + 1]);
-                    const uint32_t f2 = __float_as_uint(sacc[rb][4 * b + 2]), f3 = __float_as_uint(sacc[rb][4 * b + 3]);
-                    const uint32_t sb = (__builtin_amdgcn_perm(f1, f0, 0x0C0C0B09u) | __builtin_amdgcn_perm(f3, f2, 0x0B090C0Cu)) &
-                                        0x08040201u;
-                    // byte 3 of the product = bits 0..3; v_perm puts it at byte b of wb
-                    wb = __builtin_amdgcn_perm(sb * 0x01010101u, wb, (0x03020100u & ~(0xFFu << (8 * b))) | (0x07u << (8 * b)));
-                }
-                wb = (~wb & 0x0F0F0F0Fu) << (4 * h);
-                const Swap sw = swap32(__uint_as_float(wb));
-                wb = __float_as_uint(sw.r0) | __float_as_uint(sw.r1);
-                if (valid && (rb & 1) == h) p.signs[n * NRB + rb] = wb;
             }
         }
       }
@@ -993,8 +1097,29 @@ EncFn pick_bits(int bits, int m, bool bf16, bool rope, int mode) {
     return nullptr;
 }
 
-// mode: 0 QJL sketch, 1 sign correction, 2 sign correction without rotation
+template <int D>
+EncFn pick_vq_bits(int bits, bool bf16, bool rope) {
+    switch (bits) {
+        case 1: return pick_dtype<D, 1, 0, 3>(bf16, rope);
+        case 2: return pick_dtype<D, 2, 0, 3>(bf16, rope);
+        case 3: return pick_dtype<D, 3, 0, 3>(bf16, rope);
+        case 4: return pick_dtype<D, 4, 0, 3>(bf16, rope);
+        case 5: return pick_dtype<D, 5, 0, 3>(bf16, rope);
+        case 6: return pick_dtype<D, 6, 0, 3>(bf16, rope);
+        case 7: return pick_dtype<D, 7, 0, 3>(bf16, rope);
+        case 8: return pick_dtype<D, 8, 0, 3>(bf16, rope);
+    }
+    return nullptr;
+}
+
+// mode: 0 QJL sketch, 1 sign correction, 2 sign correction without rotation,
+// 3 vector codebook (bits = log2 of the codebook size)
 EncFn pick_encode(int d, int bits, int m, bool bf16, bool rope, int mode) {
+    if (mode == 3) {
+        if (d == 64) return pick_vq_bits<64>(bits, bf16, rope);
+        if (d == 128) return pick_vq_bits<128>(bits, bf16, rope);
+        return nullptr;
+    }
     if (d == 64) return pick_bits<64>(bits, m, bf16, rope, mode);
     if (d == 128) return pick_bits<128>(bits, m, bf16, rope, mode);
     return nullptr;
@@ -1035,9 +1160,11 @@ hipError_t launch_encode(const tq_codebook* cb, const EncodeArgs& a, hipStream_t
         if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) return hipErrorUnknown;
         g_num_cus = prop.multiProcessorCount;
     }
-    if (cb->spec.block >= 2) return vq_supported(cb) ? launch_vq_encode(cb, a, stream) : hipErrorInvalidValue;
+    if (cb->spec.block >= 2 && !vq_supported(cb)) return hipErrorInvalidValue;
     if (!cb->dense) {
-        const int mode = cb->spec.correction == TQ_CORR_SIGN ? (cb->spec.rotation == TQ_ROT_NONE ? 2 : 1) : 0;
+        const int mode = cb->spec.block >= 2                    ? 3
+                         : cb->spec.correction == TQ_CORR_SIGN ? (cb->spec.rotation == TQ_ROT_NONE ? 2 : 1)
+                                                               : 0;
         EncFn fn = pick_encode(d, bits, m, a.bf16 != 0, a.rope_cos != nullptr, mode);
         if (!fn) return hipErrorInvalidValue;
         EncK p{};

@@ -161,7 +161,6 @@ hipError_t launch_decode_mfma(const tq_codebook* ck, const tq_codebook* cv, cons
 
 // FibQuant vector codebooks (tq_vq.hip): block 2, Hadamard rotation, d = 64, 128
 bool vq_supported(const tq_codebook* cb);
-hipError_t launch_vq_encode(const tq_codebook* cb, const EncodeArgs& a, hipStream_t stream);
 hipError_t launch_vq_logits(const tq_codebook* ck, const tq_packed& k, const AttnArgs& a, const float* qp, int k0,
                             int klen, float* out, int64_t ld, int col0, hipStream_t stream);
 hipError_t launch_vq_decode(const tq_codebook* cb, const tq_packed& k, int64_t first, int64_t count, float* out,
