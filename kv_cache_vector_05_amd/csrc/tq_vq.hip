@@ -45,7 +45,8 @@ struct VqLog {
 };
 
 constexpr int kVqGroup = 8;  // queries per block of the gather form
-constexpr int kLutKeys = 4;  // keys per thread of the table form
+constexpr int kLutBatch = 4;  // keys per thread whose records are loaded together
+constexpr int kLutKeys = 8;   // keys per thread of the table form
 
 // the W code words of a record, with the widest loads its alignment allows
 template <int W>
@@ -112,49 +113,65 @@ __global__ __launch_bounds__(256) void vq_lut_logits_kernel(VqLog p) {
         s_q[g][i % D] = g < ng ? p.qp[(row0 + g) * D + i % D] : 0.0f;
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < SLOTS * NB * N; e += blockDim.x) {
-        const int sl = e / (NB * N), j = (e / N) % NB, n = e % N;
+    // entry (slot, j, n): thread e serves codeword n = e % N for every (slot, j)
+    // it meets (N divides the 256 threads)
+    {
+        const int n = threadIdx.x % N;
         const float c0 = p.code[2 * n], c1 = p.code[2 * n + 1];
-        float v[4];
+        for (int e = threadIdx.x; e < SLOTS * NB * N; e += blockDim.x) {
+            const int sl = e / (NB * N), j = (e / N) % NB;
+            float v[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = fmaf(s_q[4 * sl + i][2 * j + 1], c1, s_q[4 * sl + i][2 * j] * c0);
-        s_lut[sl][j][n] = make_float4(v[0], v[1], v[2], v[3]);
+            for (int i = 0; i < 4; ++i) v[i] = fmaf(s_q[4 * sl + i][2 * j + 1], c1, s_q[4 * sl + i][2 * j] * c0);
+            s_lut[sl][j][n] = make_float4(v[0], v[1], v[2], v[3]);
+        }
     }
     __syncthreads();
     const int sl_end = min(max(p.seq_len[b], 0), p.L_cap);
     const int t_end = min(sl_end, p.k0 + p.klen);
     const int tb = p.k0 + blockIdx.y * (256 * kLutKeys) + threadIdx.x;
-    for (int kk = 0; kk < kLutKeys; ++kk) {
-        const int t = tb + 256 * kk;
-        if (t >= t_end) break;
-        const int64_t rec = vq_record(p, bk, b, kh, t);
-        uint32_t w[W];
-        load_words<W>(p.codes + rec * W, w);
-        const float nu = p.norm[rec];
-        float acc[QB];
+    for (int k0 = 0; k0 < kLutKeys; k0 += kLutBatch) {
+        if (tb + 256 * k0 >= t_end) break;
+        // the batch's records in flight together (keys past the end re-read
+        // the last key and are not stored)
+        uint32_t w[kLutBatch][W];
+        float nu[kLutBatch];
 #pragma unroll
-        for (int g = 0; g < QB; ++g) acc[g] = 0.0f;
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const uint32_t idx = index_at<BITS, W>(w, j);
-#pragma unroll
-            for (int sl = 0; sl < SLOTS; ++sl) {
-                const float4 f = s_lut[sl][j][idx];
-                acc[4 * sl] += f.x;
-                acc[4 * sl + 1] += f.y;
-                acc[4 * sl + 2] += f.z;
-                acc[4 * sl + 3] += f.w;
-            }
-            // the sums are formed here (not sunk into the guarded stores
-            // below), so only a word's lookups are in flight at a time
-            if ((j & 7) == 7) {
-#pragma unroll
-                for (int g = 0; g < QB; ++g) asm volatile("" : "+v"(acc[g]));
-            }
+        for (int kk = 0; kk < kLutBatch; ++kk) {
+            const int64_t rec = vq_record(p, bk, b, kh, min(tb + 256 * (k0 + kk), t_end - 1));
+            load_words<W>(p.codes + rec * W, w[kk]);
+            nu[kk] = p.norm[rec];
         }
 #pragma unroll
-        for (int g = 0; g < QB; ++g)
-            if (g < ng) p.out[(row0 + g) * p.ld + (t - p.col0)] = acc[g] * nu;
+        for (int kk = 0; kk < kLutBatch; ++kk) {
+            const int t = tb + 256 * (k0 + kk);
+            float acc[QB];
+#pragma unroll
+            for (int g = 0; g < QB; ++g) acc[g] = 0.0f;
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const uint32_t idx = index_at<BITS, W>(w[kk], j);
+#pragma unroll
+                for (int sl = 0; sl < SLOTS; ++sl) {
+                    const float4 f = s_lut[sl][j][idx];
+                    acc[4 * sl] += f.x;
+                    acc[4 * sl + 1] += f.y;
+                    acc[4 * sl + 2] += f.z;
+                    acc[4 * sl + 3] += f.w;
+                }
+                // the sums are formed here (not sunk into the guarded stores
+                // below), so only a word's lookups are in flight at a time
+                if ((j & 7) == 7) {
+#pragma unroll
+                    for (int g = 0; g < QB; ++g) asm volatile("" : "+v"(acc[g]));
+                }
+            }
+            if (t < t_end) {
+#pragma unroll
+                for (int g = 0; g < QB; ++g)
+                    if (g < ng) p.out[(row0 + g) * p.ld + (t - p.col0)] = acc[g] * nu[kk];
+            }
+        }
     }
 }
 
