@@ -7,7 +7,7 @@ calibrated mean residual magnitude along each stored sign.  The pages
 calibrate on real protein activations; here every calibration sample is a
 seeded synthetic one.
 
-Readings where the pages are silent (listed in the design notes):
+Readings where the pages are silent:
 
 * The table is fitted to a calibration sample by Lloyd's algorithm with a
   mirror-symmetric constraint: its upper half is the Lloyd-Max quantiser of

@@ -22,8 +22,8 @@ per-head calibrated mean residual magnitude mu along those signs.  The table
 may be a calibrated one (``levels``), and ``rotation = "none"`` leaves the
 vectors in their original coordinates (the value table of that section).
 
-Readings where the pages are silent (each is listed with its reason in the
-design notes): the sketch acts on the residual in the rotated domain; gamma
+Readings where the pages are silent: the sketch acts on the residual in the
+rotated domain; gamma
 is stored per vector as float32 next to nu; ties go to the upper code and a
 zero sketch value gives bit 1.  Integer decisions (codes, sign bits) are
 taken in float32, the precision the GPU kernels decide in: the float64 value

@@ -18,7 +18,7 @@ Compressao de KV-Cache de Acesso Aleatorio").
   by nu.  The rate is b = log2(N) / k bits per coordinate, so fractional and
   below-one-bit rates exist.
 
-Readings where the page is silent (listed in the design notes):
+Readings where the page is silent:
 * f_{d,k}(x) is proportional to (1 - |x|^2)^((d-k-2)/2) on B^k, and |x|^2
   follows Beta(k/2, (d-k)/2).  Bennett-Gersho companding puts codewords with
   density proportional to f^(k/(k+2)); its radial law has |x|^2 ~

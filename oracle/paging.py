@@ -6,7 +6,7 @@ its own through simple address arithmetic; the cache grows with the context
 and is read at every decode step.  TurboESM summary, technical section 5:
 autoregressive generation, where keeping the context is the bottleneck.
 
-Readings (listed in the design notes):
+Readings:
 
 * Appending a token encodes it exactly as a bulk encode would (RoPE at its
   own position for keys) and writes its record at its slot, nothing else.
