@@ -121,7 +121,10 @@ enum { TQ_OP_ENCODE = 0, TQ_OP_LOGITS = 1, TQ_OP_DECODE = 2 };     /* workspace 
  *            restarts); rate bits / block per coordinate.  m must be 0,
  *            correction TQ_CORR_QJL (no residual correction) and d a multiple
  *            of block.  Kernels exist for block 2 with the Hadamard rotation
- *            (d = 64, 128); other vector codebooks build tables only.
+ *            (d = 64, 128), and for block 2 or 3 with a dense rotation (d a
+ *            multiple of 64: bulk encodes and contiguous scans; appends and
+ *            pages return TQ_EUNSUPPORTED); other vector codebooks build
+ *            tables only.
  */
 typedef struct {
     int32_t d, bits, m, rotation;

@@ -344,10 +344,31 @@ struct DenseScan {
     const uint32_t* codes;
     const uint32_t* signs;
     int32_t d, m, bits;
+    int32_t block;  // vector codebooks: levels holds the N x block codewords
     int64_t rec0;   // record index of key 0 of this (b, kh)
     int32_t k0, cnt;
     float* aug;     // [cnt][d + m]: t[c], then sqrt(pi/2)/m gamma z
 };
+
+// vector codebooks: aug[r] = the concatenated codewords of key k0 + r (the
+// rotated unit vector's estimate; FibQuant summary, section 2.3)
+__global__ __launch_bounds__(256) void dense_vq_dequant_kernel(DenseScan p) {
+    const int k = p.block, nb = p.d / k;
+    const int cw = (p.bits * nb + 31) / 32;
+    const uint32_t mask = (1u << p.bits) - 1u;
+    for (int64_t r = blockIdx.x; r < p.cnt; r += gridDim.x) {
+        const int64_t n = p.rec0 + p.k0 + r;
+        const uint32_t* c = p.codes + n * cw;
+        float* dst = p.aug + r * p.d;
+        for (int j = threadIdx.x; j < nb; j += blockDim.x) {
+            const int o = j * p.bits;
+            uint32_t idx = c[o >> 5] >> (o & 31);
+            if ((o & 31) + p.bits > 32) idx |= c[(o >> 5) + 1] << (32 - (o & 31));
+            idx &= mask;
+            for (int i = 0; i < k; ++i) dst[j * k + i] = p.levels[idx * k + i];
+        }
+    }
+}
 
 __global__ __launch_bounds__(256) void dense_dequant_kernel(DenseScan p) {
     const int width = p.d + p.m;
@@ -830,7 +851,7 @@ size_t logits_workspace_bytes(const tq_codebook* ck, int64_t B, int Hq, int h_kv
     const size_t d = ck->spec.d, m = ck->spec.m;
     const size_t rows = (size_t)B * Hq;
     const size_t chunk = (size_t)std::min(L_cap, kScanChunk);
-    if (ck->spec.block >= 2) {
+    if (ck->spec.block >= 2 && !ck->dense) {
         size_t bytes = align256(rows * d * 4);
         if (top_k) bytes += align256(rows * chunk * 4);
         return bytes;
@@ -873,7 +894,7 @@ hipError_t launch_logits(const tq_codebook* ck, const tq_packed& k, const AttnAr
     const int64_t rows = (int64_t)a.B * a.Hq;
     char* ws = static_cast<char*>(a.ws);
     const int chunk = std::min(a.L_cap, kScanChunk);
-    if (ck->spec.block >= 2) {
+    if (ck->spec.block >= 2 && !ck->dense) {
         // vector codebook: q' = Pi RoPE(q), then codeword lookups fused into the dot products
         if (!vq_supported(ck)) return hipErrorInvalidValue;
         float* qp = reinterpret_cast<float*>(ws);
@@ -1011,11 +1032,17 @@ hipError_t launch_logits(const tq_codebook* ck, const tq_packed& k, const AttnAr
                 ds.d = d;
                 ds.m = m;
                 ds.bits = bits;
+                ds.block = ck->spec.block;
                 ds.rec0 = rec0;
                 ds.k0 = k0;
                 ds.cnt = cnt;
                 ds.aug = aug;
-                hipLaunchKernelGGL(dense_dequant_kernel, dim3((unsigned)std::min(cnt, 8192)), dim3(256), 0, stream, ds);
+                if (ck->spec.block >= 2)
+                    hipLaunchKernelGGL(dense_vq_dequant_kernel, dim3((unsigned)std::min(cnt, 8192)), dim3(256), 0,
+                                       stream, ds);
+                else
+                    hipLaunchKernelGGL(dense_dequant_kernel, dim3((unsigned)std::min(cnt, 8192)), dim3(256), 0, stream,
+                                       ds);
                 e = hipGetLastError();
                 if (e != hipSuccess) return e;
                 e = launch_gemm_nt(qaug + row0 * (d + m), d + m, aug, d + m, scores, chunk, G, cnt, d + m, stream);

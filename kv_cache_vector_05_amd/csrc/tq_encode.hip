@@ -918,6 +918,7 @@ struct DenseK {
     const void* x;
     int64_t s_seq, s_tok, s_head;
     int32_t n_tok, h_kv, tok_offset, L_cap, d, m, bits;
+    int32_t block;  // vector codebooks: coordinates per block (levels holds the N x block codewords)
     int64_t start, count;
     int32_t bf16;
     const float* rope_cos;
@@ -1037,6 +1038,67 @@ __global__ __launch_bounds__(256) void dense_quant_kernel(DenseK p) {
             const int64_t n = dense_record(p, p.start + i, &off, &tok);
             for (int w = lane; w < cw; w += 64) p.codes[n * cw + w] = words[wv][w];
             if (lane == 0 && p.m > 0) p.rnorm[n] = sqrtf(gg);
+        }
+        __syncthreads();
+    }
+}
+
+// vector codebooks (FibQuant summary, section 2.3), one wave per vector: each
+// block of `block` rotated coordinates of Y takes its nearest codeword - the
+// largest <y, c> - |c|^2 / 2, ties to the smaller index - from the codebook
+// in LDS; index j goes to bits [j bits, (j+1) bits) of the record, assembled
+// in LDS
+constexpr int kMaxVqWords = 4096 * 8 / 2 / 32;
+__global__ __launch_bounds__(256) void dense_vq_kernel(DenseK p) {
+    __shared__ uint32_t words[4][kMaxVqWords];
+    __shared__ float s_code[256 * 4];  // {c_0 .. c_{k-1}, -|c|^2 / 2} per codeword
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int k = p.block, N = 1 << p.bits, nb = p.d / k;
+    const int cw = (p.bits * nb + 31) / 32;
+    for (int c = threadIdx.x; c < N; c += blockDim.x) {
+        float h = 0.0f;
+        for (int i = 0; i < k; ++i) {
+            const float v = p.levels[c * k + i];
+            s_code[4 * c + i] = v;
+            h = fmaf(v, v, h);
+        }
+        s_code[4 * c + 3] = -0.5f * h;
+    }
+    const int64_t stride = (int64_t)gridDim.x * 4;
+    // the loop bound is the same for every wave of the block, so the block
+    // barriers below are reached by all of its threads
+    for (int64_t i0 = (int64_t)blockIdx.x * 4; i0 < p.count; i0 += stride) {
+        const int64_t i = i0 + wv;
+        const bool active = i < p.count;
+        for (int w = lane; w < cw; w += 64) words[wv][w] = 0u;
+        __syncthreads();
+        if (active) {
+            for (int j = lane; j < nb; j += 64) {
+                const float* y = p.Y + i * p.d + (int64_t)j * k;
+                const float y0 = y[0], y1 = y[1], y2 = k == 3 ? y[2] : 0.0f;
+                float bs = -INFINITY;
+                uint32_t bi = 0;
+                for (int c = 0; c < N; ++c) {
+                    const float* cv = s_code + 4 * c;
+                    float sc = fmaf(cv[1], y1, fmaf(cv[0], y0, cv[3]));
+                    if (k == 3) sc = fmaf(cv[2], y2, sc);
+                    if (sc > bs) {
+                        bs = sc;
+                        bi = (uint32_t)c;
+                    }
+                }
+                const int o = j * p.bits;
+                atomicOr(&words[wv][o >> 5], bi << (o & 31));
+                if ((o & 31) + p.bits > 32) atomicOr(&words[wv][(o >> 5) + 1], bi >> (32 - (o & 31)));
+            }
+        }
+        __syncthreads();
+        if (active) {
+            int64_t off;
+            int tok;
+            const int64_t n = dense_record(p, p.start + i, &off, &tok);
+            for (int w = lane; w < cw; w += 64) p.codes[n * cw + w] = words[wv][w];
         }
         __syncthreads();
     }
@@ -1230,6 +1292,7 @@ hipError_t launch_encode(const tq_codebook* cb, const EncodeArgs& a, hipStream_t
         p.d = d;
         p.m = m;
         p.bits = bits;
+        p.block = cb->spec.block;
         p.start = start;
         p.count = cnt;
         p.bf16 = a.bf16;
@@ -1250,7 +1313,8 @@ hipError_t launch_encode(const tq_codebook* cb, const EncodeArgs& a, hipStream_t
         if (e != hipSuccess) return e;
         e = launch_gemm_nt(U, d, cb->dev.rot, d, Y, d, (int)cnt, d, d, stream);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(dense_quant_kernel, dim3(grid), dim3(256), 0, stream, p);
+        if (cb->spec.block >= 2) hipLaunchKernelGGL(dense_vq_kernel, dim3(grid), dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL(dense_quant_kernel, dim3(grid), dim3(256), 0, stream, p);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (m > 0) {

@@ -1043,7 +1043,9 @@ static tq_status encode_common(const tq_codebook* ck, const tq_codebook* cv, con
             return fail(TQ_EUNSUPPORTED, "appends and paged records are served for Hadamard and unrotated codebooks");
         if (sd.cb->spec.block >= 2) {
             if (!vq_supported(sd.cb))
-                return fail(TQ_EUNSUPPORTED, "vector codebooks encode on the GPU for block 2, Hadamard, d = 64 or 128");
+                return fail(TQ_EUNSUPPORTED,
+                            "vector codebooks encode on the GPU for block 2 with the Hadamard rotation at d = 64 or 128, "
+                            "or any block with a dense rotation");
             if (nvec >= ((int64_t)1 << 31)) return fail(TQ_EUNSUPPORTED, "too many vectors in one encode call (split it)");
         }
         if (!sd.cb->dense && (int64_t)n_seq * ((n_tok + 31) / 32) * h_kv >= (int64_t)1 << 31)
@@ -1116,6 +1118,7 @@ static tq_status logits_common(const tq_codebook* ck, const void* q, int32_t q_d
     if (st) return st;
     if (ck->spec.block >= 2) {
         if (!vq_supported(ck)) return fail(TQ_EUNSUPPORTED, "no logit kernel for this vector codebook");
+        if (ck->dense && pg.table) return fail(TQ_EUNSUPPORTED, "paged scans are served for Hadamard codebooks");
     } else if ((sign_corr(ck) || pg.table) && !logits_mfma_supported(ck)) {
         return fail(TQ_EUNSUPPORTED, "no logit kernel for this codebook (paged and sign-corrected scans need "
                                      "a Hadamard or unrotated codebook with bits <= 3 and m <= 128)");
@@ -1289,7 +1292,7 @@ tq_status tq_decode_vectors(const tq_codebook* cb, const tq_packed* packed, int6
     if (!packed->norm || !packed->codes) return fail(TQ_EINVAL, "null norm/codes plane");
     if (first < 0 || count < 0 || first + count > packed->n) return fail(TQ_EINVAL, "records out of range");
     if (cb->spec.block < 2 || !vq_supported(cb))
-        return fail(TQ_EUNSUPPORTED, "vectors are rebuilt for vector codebooks (block 2, Hadamard, d = 64 or 128)");
+        return fail(TQ_EUNSUPPORTED, "vectors are rebuilt for vector codebooks");
     if (count == 0) return TQ_OK;
     hipError_t e = launch_vq_decode(cb, *packed, first, count, out, (hipStream_t)stream);
     return e == hipSuccess ? TQ_OK : hip_fail(e, "decode launch");

@@ -16,7 +16,10 @@
 // free of bank conflicts.  Codebooks whose table does not fit in LDS use the
 // gather form: codewords looked up and multiplied by q' per key.
 // Decoder: codewords looked up, inverse Walsh-Hadamard transform and signs,
-// scaled by nu.
+// scaled by nu (dense rotations: the product with Pi^T per vector).  With a
+// dense rotation the encoder and the scan take the dense GEMM path (the
+// encoder's dense_vq_kernel, the scan's codeword dequantisation), for blocks
+// of 2 or 3 coordinates.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -269,6 +272,44 @@ __global__ __launch_bounds__(256) void vq_decode_kernel(VqDec p) {
     }
 }
 
+// dense rotation: x = nu Pi^T y_hat, one block per vector (grid-stride); the
+// concatenated codewords y_hat are staged in LDS, and thread c forms output
+// coordinate c from column c of Pi (rows read in order, coalesced)
+struct VqDenseDec {
+    const float* norm;
+    const uint32_t* codes;
+    const float* code;
+    const float* rot;  // Pi [d][d] row-major
+    int32_t d, block, bits, words;
+    int64_t first, count;
+    float* out;  // [count][d]
+};
+
+__global__ __launch_bounds__(256) void vq_dense_decode_kernel(VqDenseDec p) {
+    __shared__ float s_y[4096];
+    const int k = p.block, nb = p.d / k;
+    const uint32_t mask = (1u << p.bits) - 1u;
+    for (int64_t i = blockIdx.x; i < p.count; i += gridDim.x) {
+        const int64_t rec = p.first + i;
+        const uint32_t* c = p.codes + rec * p.words;
+        __syncthreads();  // the previous vector's reads of s_y are done
+        for (int j = threadIdx.x; j < nb; j += blockDim.x) {
+            const int o = j * p.bits;
+            uint32_t idx = c[o >> 5] >> (o & 31);
+            if ((o & 31) + p.bits > 32) idx |= c[(o >> 5) + 1] << (32 - (o & 31));
+            idx &= mask;
+            for (int t = 0; t < k; ++t) s_y[j * k + t] = p.code[idx * k + t];
+        }
+        __syncthreads();
+        const float nu = p.norm[rec];
+        for (int col = threadIdx.x; col < p.d; col += blockDim.x) {
+            float acc = 0.0f;
+            for (int r = 0; r < p.d; ++r) acc = fmaf(p.rot[(int64_t)r * p.d + col], s_y[r], acc);
+            p.out[i * p.d + col] = acc * nu;
+        }
+    }
+}
+
 using VqLogFn = void (*)(VqLog);
 
 // LDS of the table form: SLOTS * D/2 * N float4 entries (at most 48 KiB)
@@ -316,7 +357,10 @@ int vq_grid(int64_t waves_needed) {
 }  // namespace
 
 bool vq_supported(const tq_codebook* cb) {
-    return cb->spec.block == 2 && !cb->dense && (cb->spec.d == 64 || cb->spec.d == 128);
+    if (cb->spec.block < 2) return false;
+    // dense rotations (d a multiple of 64, any block) run on the dense GEMM path
+    if (cb->dense) return cb->spec.d <= 4096;
+    return cb->spec.block == 2 && (cb->spec.d == 64 || cb->spec.d == 128);
 }
 
 hipError_t launch_vq_logits(const tq_codebook* ck, const tq_packed& k, const AttnArgs& a, const float* qp, int k0,
@@ -363,6 +407,24 @@ hipError_t launch_vq_logits(const tq_codebook* ck, const tq_packed& k, const Att
 hipError_t launch_vq_decode(const tq_codebook* cb, const tq_packed& k, int64_t first, int64_t count, float* out,
                             hipStream_t stream) {
     const int d = cb->spec.d;
+    if (count == 0) return hipSuccess;
+    if (cb->dense) {
+        VqDenseDec p{};
+        p.norm = k.norm;
+        p.codes = k.codes;
+        p.code = cb->dev.levels;
+        p.rot = cb->dev.rot;
+        p.d = d;
+        p.block = cb->spec.block;
+        p.bits = cb->spec.bits;
+        p.words = (int)((cb->spec.bits * (d / cb->spec.block) + 31) / 32);
+        p.first = first;
+        p.count = count;
+        p.out = out;
+        const int grid = (int)std::min<int64_t>(count, 2048);
+        hipLaunchKernelGGL(vq_dense_decode_kernel, dim3(grid), dim3(256), 0, stream, p);
+        return hipGetLastError();
+    }
     VqDec p{};
     p.norm = k.norm;
     p.codes = k.codes;

@@ -1,7 +1,8 @@
 """GPU parity for FibQuant vector codebooks (FibQuant summary, sections
 2.1-2.3): the nearest-codeword encoder (bulk, appended and paged), the logit
 scan with codeword lookups (and top-k), and the decoder, through the C ABI
-against the oracle in oracle/fibquant.py.
+against the oracle in oracle/fibquant.py; blocks of two coordinates with the
+Hadamard rotation, and of two or three with a dense Haar rotation.
 
 Protocol: a block's codeword index must equal the oracle's unless its two
 nearest codewords are within 1e-6 in squared distance (the GPU decides in
@@ -12,7 +13,7 @@ import numpy as np
 import pytest
 
 import synth
-from oracle import fibquant as F, estimator, paging, rope as orope
+from oracle import fibquant as F, estimator, paging, rope as orope, rotation as orot
 
 import parity
 from test_gpu_parity import bf16_tensor
@@ -34,8 +35,19 @@ def books(d, bits, seed):
     return o, g
 
 
+def dense_books(d, k, bits, seed):
+    """(oracle, GPU) codebooks with a dense Haar rotation from the same seeded
+    Gaussian draws; each side builds its own codewords and its own QR."""
+    gauss = synth.codec_draws(d, 0, True, seed)[1]
+    g = tq.Codebook(d, bits, 0, "dense", rot_gauss=gauss, block=k)
+    code, _ = F.build_codebook(d, k, 1 << bits)
+    o = F.VQCodebook(d, k, 1 << bits, code.astype(np.float32), orot.haar_rotation(gauss))
+    np.testing.assert_allclose(g.export()["levels"], o.code32, rtol=0, atol=1e-7)
+    return o, g
+
+
 def compare(o, enc, norm, codes, label):
-    g_idx = F.unpack_indices(codes, o.index_bits, o.d // 2)
+    g_idx = F.unpack_indices(codes, o.index_bits, o.d // o.k)
     near = enc.margin < MARGIN
     bad = (g_idx != enc.idx) & ~near
     assert bad.sum() <= int(1e-6 * (~near).sum()), f"{label}: {bad.sum()} index mismatches"
@@ -154,6 +166,89 @@ def o_as_scalar(o):
         pi = o.pi
         sketch = np.zeros((0, o.d), np.float32)
     return _Q()
+
+
+@pytest.mark.parametrize("k,bits,dtype,rope", [
+    (3, 3, "f32", True),    # rate 1: 8 codewords per 3-coordinate block, RoPE keys
+    (3, 1, "bf16", False),  # rate 1/3
+    (3, 6, "f32", False),   # rate 2, indices straddle words
+    (2, 4, "bf16", True),   # a 2-coordinate code with the dense rotation
+])
+def test_vq_dense_encode(k, bits, dtype, rope):
+    d, B, T, H, off, L = 192, 2, 37, 3, 5, 50
+    g = synth.rng(300 + 10 * k + bits)
+    X = g.standard_normal((B, T, H, d)).astype(np.float32)
+    X[:, :, :, 7] *= np.float32(20.0)
+    X[1, 3] = 0.0
+    if dtype == "bf16":
+        xb = synth.bf16_round_bits(X)
+        X = synth.bf16_bits_to_f32(xb)
+        x_dev = bf16_tensor(xb)
+    else:
+        x_dev = torch.from_numpy(X).cuda()
+    o, gc = dense_books(d, k, bits, 31 + bits)
+    rope_g = tq.rope_table(1e4, d, L) if rope else None
+    rope_o = orope.rope_table(1e4, d, L) if rope else None
+    kp = tq.Packed(gc, B * H * L)
+    kp.norm.fill_(-4.0)
+    tq.encode_kv(gc, None, x_dev, None, kp, None, tok_offset=off, L_cap=L, rope=rope_g)
+    torch.cuda.synchronize()
+    norm, _, codes, _ = kp.numpy()
+    assert np.all(norm.reshape(B * H, L)[:, :off] == -4.0)
+    idx = paging.contiguous_index(np.repeat(np.arange(B), H * T), np.tile(np.repeat(np.arange(H), T), B),
+                                  off + np.tile(np.arange(T), B * H), H, L)
+    enc = F.encode(o, parity.oracle_rows(X), pos=off + np.tile(np.arange(T), B * H) if rope else None, rope=rope_o)
+    compare(o, enc, norm[idx], codes[idx], f"dense vq encode k{k} b{bits} {dtype} rope={rope}")
+
+
+@pytest.mark.parametrize("k,bits", [(3, 4), (2, 5)])
+def test_vq_dense_logits_topk_and_decoder(k, bits):
+    """The dense scan (codewords dequantised per chunk, scores by GEMM) with a
+    ragged length and top-k, and the dense decoder, over the oracle's records."""
+    d, B, Hq, H, L = 192, 2, 6, 2, 600
+    g = synth.rng(70 + k + bits)
+    o, gc = dense_books(d, k, bits, 41)
+    X = g.standard_normal((B * H * L, d))
+    enc = F.encode(o, X)
+    kp = tq.Packed.from_arrays(gc, enc.norm.astype(np.float32), np.zeros(0), enc.codes, np.zeros((len(X), 0)))
+    Q = g.standard_normal((B, Hq, d)).astype(np.float32)
+    qt = torch.from_numpy(Q).cuda()
+    lens = [600, 257]
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    lg = tq.attn_logits(gc, qt, kp, H, L, sl, out=torch.full((B, Hq, L), float("nan"), device="cuda")).cpu().numpy()
+    vals, tidx = tq.attn_logits(gc, qt, kp, H, L, sl, top_k=5)
+    vals, tidx = vals.cpu().numpy(), tidx.cpu().numpy()
+    norm32 = enc.norm.astype(np.float32).astype(np.float64)
+    G = Hq // H
+    for b in range(B):
+        for h in range(H):
+            rows = slice((b * H + h) * L, (b * H + h) * L + lens[b])
+            gs = slice(h * G, (h + 1) * G)
+            ref = F.logits(o, Q[b, gs] @ o.pi.T, norm32[rows], enc.codes[rows])
+            parity.assert_close(lg[b, gs, :lens[b]], ref, f"dense vq logits b={b} h={h}")
+            for r in range(G):
+                parity.assert_close(vals[b, h * G + r], ref[r, tidx[b, h * G + r]], "dense vq top-k values")
+                kth = np.sort(ref[r])[::-1][4]
+                assert np.all(ref[r, tidx[b, h * G + r]] >= kth - (parity.ATOL + parity.RTOL * abs(kth)))
+    rec = tq.decode_vectors(gc, kp, first=50, count=700).cpu().numpy()
+    parity.assert_close(rec, F.reconstruct(o, norm32[50:750], enc.codes[50:750]), "dense vq decoder")
+
+
+def test_vq_dense_rejections():
+    """Appends and pages are served for Hadamard codebooks only."""
+    o, gc = dense_books(192, 3, 2, 5)
+    B, H, P = 1, 1, 64
+    table = torch.zeros((B, 1), dtype=torch.int32, device="cuda")
+    pg = tq.Pages(table, P, 1)
+    kp = tq.Packed(gc, pg.records(H))
+    x = torch.zeros((B, H, 192), device="cuda")
+    with pytest.raises(tq.TQError) as ei:
+        tq.append_kv(gc, None, x, None, kp, None, torch.zeros(B, dtype=torch.int32, device="cuda"), pages=pg)
+    assert ei.value.code == -2
+    q = torch.zeros((B, 3, 192), device="cuda")
+    with pytest.raises(tq.TQError) as ei:
+        tq.attn_logits(gc, q, kp, H, None, torch.tensor([10], dtype=torch.int32, device="cuda"), pages=pg)
+    assert ei.value.code == -2
 
 
 def test_vq_rejections():
