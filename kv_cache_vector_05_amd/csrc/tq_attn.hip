@@ -877,6 +877,13 @@ size_t decode_workspace_bytes(const tq_codebook* ck, const tq_codebook* cv, int6
     const int G = h_kv > 0 ? Hq / h_kv : 1;
     const int gt = group_tile(G);
     const int64_t bkg = (int64_t)B * h_kv * ((G + gt - 1) / gt);
+    if (ck->spec.block >= 2) {
+        // q', split partials (M, l, A_y) and the merge's first stage
+        int nsplit = 1, split_len = 0;
+        vq_attn_plan(L_cap, &nsplit, &split_len);
+        const size_t ngroup = (size_t)(nsplit + kMergeGroup - 1) / kMergeGroup;
+        return align256(rows * d * 4) + align256(rows * nsplit * (2 + d) * 4) + align256(rows * ngroup * (2 + d) * 4);
+    }
     if (decode_mfma_supported(ck, cv)) {
         int nsplit = 1, split_len = 0;
         decode_mfma_plan(B, Hq, h_kv, L_cap, &nsplit, &split_len);
@@ -1080,10 +1087,47 @@ hipError_t launch_logits(const tq_codebook* ck, const tq_packed& k, const AttnAr
 hipError_t launch_decode(const tq_codebook* ck, const tq_codebook* cv, const tq_packed& k, const tq_packed& v,
                          const AttnArgs& a, hipStream_t stream) {
     const int d = ck->spec.d, m = ck->spec.m, bits = ck->spec.bits;
-    if (ck->dense || cv->dense || cv->spec.bits != bits || cv->spec.m != m) return hipErrorInvalidValue;
     const int G = a.Hq / a.h_kv;
     const int64_t rows = (int64_t)a.B * a.Hq;
     char* ws = static_cast<char*>(a.ws);
+    // the split merge: log-sum-exp over splits (a first stage over groups of
+    // 32 when there are many), then Pi_v^T and 1/l
+    auto merge = [&](MergeK mk, float* part, int nsplit, int width) -> hipError_t {
+        mk.part = part;
+        mk.nsplit = nsplit;
+        if (nsplit > 2 * kMergeGroup) {
+            const int ngroup = (nsplit + kMergeGroup - 1) / kMergeGroup;
+            float* part2 = part + align256(rows * nsplit * width * 4) / 4;
+            hipLaunchKernelGGL(decode_merge_group_kernel, dim3((unsigned)rows, (unsigned)ngroup), dim3(256), 0, stream,
+                               part, nsplit, width, part2, ngroup);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            mk.part = part2;
+            mk.nsplit = ngroup;
+        }
+        if (d == 64) hipLaunchKernelGGL(decode_merge_kernel<64>, dim3((unsigned)rows), dim3(256), 0, stream, mk);
+        else hipLaunchKernelGGL(decode_merge_kernel<128>, dim3((unsigned)rows), dim3(256), 0, stream, mk);
+        return hipGetLastError();
+    };
+    if (ck->spec.block >= 2) {
+        // vector codebooks: q' = Pi_k RoPE(q), split kernel, merge (no correction term)
+        if (!vq_attn_supported(ck, cv)) return hipErrorInvalidValue;
+        int nsplit = 1, split_len = 0;
+        vq_attn_plan(a.L_cap, &nsplit, &split_len);
+        float* qp = reinterpret_cast<float*>(ws);
+        float* part = reinterpret_cast<float*>(ws + align256(rows * d * 4));
+        hipError_t e = launch_qprep_rht(ck, a, qp, nullptr, stream);
+        if (e != hipSuccess) return e;
+        e = launch_vq_attn_split(ck, cv, k, v, a, qp, part, nsplit, split_len, stream);
+        if (e != hipSuccess) return e;
+        MergeK mk{};
+        mk.d = d;
+        mk.m = 0;
+        mk.sigma = cv->dev.sigma;
+        mk.out = a.out;
+        return merge(mk, part, nsplit, 2 + d);
+    }
+    if (ck->dense || cv->dense || cv->spec.bits != bits || cv->spec.m != m) return hipErrorInvalidValue;
     MergeK mk{};
     mk.d = d;
     mk.m = m;
@@ -1102,22 +1146,7 @@ hipError_t launch_decode(const tq_codebook* ck, const tq_codebook* cv, const tq_
         if (e != hipSuccess) return e;
         e = launch_decode_mfma(ck, cv, k, v, a, qd, part, nsplit, split_len, stream);
         if (e != hipSuccess) return e;
-        mk.part = part;
-        mk.nsplit = nsplit;
-        if (nsplit > 2 * kMergeGroup) {
-            // many splits: a first stage reduces groups of 32 in parallel
-            const int ngroup = (nsplit + kMergeGroup - 1) / kMergeGroup;
-            float* part2 = part + align256(rows * nsplit * (2 + d + m) * 4) / 4;
-            hipLaunchKernelGGL(decode_merge_group_kernel, dim3((unsigned)rows, (unsigned)ngroup), dim3(256), 0, stream,
-                               part, nsplit, 2 + d + m, part2, ngroup);
-            e = hipGetLastError();
-            if (e != hipSuccess) return e;
-            mk.part = part2;
-            mk.nsplit = ngroup;
-        }
-        if (d == 64) hipLaunchKernelGGL(decode_merge_kernel<64>, dim3((unsigned)rows), dim3(256), 0, stream, mk);
-        else hipLaunchKernelGGL(decode_merge_kernel<128>, dim3((unsigned)rows), dim3(256), 0, stream, mk);
-        return hipGetLastError();
+        return merge(mk, part, nsplit, 2 + d + m);
     }
     float* qp = reinterpret_cast<float*>(ws);
     float* s = qp + rows * d;

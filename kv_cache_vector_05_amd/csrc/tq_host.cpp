@@ -1157,9 +1157,11 @@ static tq_status decode_common(const tq_codebook* ck, const tq_codebook* cv, con
     if (!out) return fail(TQ_EINVAL, "null output");
     if (!(scale >= 0.0f) || std::isinf(scale)) return fail(TQ_EINVAL, "scale must be finite and >= 0");
     if (ck->spec.d != cv->spec.d) return fail(TQ_EINVAL, "key and value dimensions differ");
-    if (ck->spec.block >= 2 || cv->spec.block >= 2)
-        return fail(TQ_EUNSUPPORTED, "the fused decode takes scalar codebooks; rebuild vector-coded values with "
-                                     "tq_decode_vectors");
+    const bool vq = ck->spec.block >= 2 || cv->spec.block >= 2;
+    if (vq && !vq_attn_supported(ck, cv))
+        return fail(TQ_EUNSUPPORTED, "the fused decode takes vector codebooks for keys and values together (block 2, "
+                                     "Hadamard, d = 64 or 128, at most 5 key index bits at d = 128 and 6 at d = 64); "
+                                     "rebuild other vector-coded values with tq_decode_vectors");
     st = check_packed(ck, k, cap_records, "k");
     if (st) return st;
     st = check_packed(cv, v, cap_records, "v");
@@ -1168,7 +1170,7 @@ static tq_status decode_common(const tq_codebook* ck, const tq_codebook* cv, con
     if (st) return st;
     st = check_mu(cv, h_kv);
     if (st) return st;
-    if ((sign_corr(ck) || sign_corr(cv) || pg.table) && !decode_mfma_supported(ck, cv))
+    if (!vq && (sign_corr(ck) || sign_corr(cv) || pg.table) && !decode_mfma_supported(ck, cv))
         return fail(TQ_EUNSUPPORTED, "paged and sign-corrected decodes need key and value tables of equal d, bits "
                                      "and m (bits <= 3)");
     if ((int64_t)B * Hq == 0) return TQ_OK;

@@ -163,6 +163,13 @@ hipError_t launch_decode_mfma(const tq_codebook* ck, const tq_codebook* cv, cons
 bool vq_supported(const tq_codebook* cb);
 hipError_t launch_vq_logits(const tq_codebook* ck, const tq_packed& k, const AttnArgs& a, const float* qp, int k0,
                             int klen, float* out, int64_t ld, int col0, hipStream_t stream);
+// fused decode with vector-coded keys and values (Hadamard, d = 64 or 128):
+// the split kernel writes (M, l, A_y) partials for the split merge
+bool vq_attn_supported(const tq_codebook* ck, const tq_codebook* cv);
+void vq_attn_plan(int L_cap, int* nsplit, int* split_len);
+hipError_t launch_vq_attn_split(const tq_codebook* ck, const tq_codebook* cv, const tq_packed& k, const tq_packed& v,
+                                const AttnArgs& a, const float* qp, float* part, int nsplit, int split_len,
+                                hipStream_t stream);
 hipError_t launch_vq_decode(const tq_codebook* cb, const tq_packed& k, int64_t first, int64_t count, float* out,
                             hipStream_t stream);
 hipError_t launch_qprep_rht(const tq_codebook* ck, const AttnArgs& a, float* qp, float* s, hipStream_t stream);

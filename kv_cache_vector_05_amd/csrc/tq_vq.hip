@@ -86,8 +86,9 @@ __device__ __forceinline__ uint32_t index_at(const uint32_t (&w)[W], int j) {
 }
 
 // record of key t of (sequence b, KV head kh) (paged: page-table entries
-// clamped into the pool)
-__device__ __forceinline__ int64_t vq_record(const VqLog& p, int64_t bk, int b, int kh, int t) {
+// clamped into the pool); P carries the page table and the cache shape
+template <class P>
+__device__ __forceinline__ int64_t vq_record(const P& p, int64_t bk, int b, int kh, int t) {
     if (p.pages) {
         const uint32_t j = p.div_page.div((uint32_t)t);
         int64_t pg = p.pages[(int64_t)b * p.max_pages + j];
@@ -272,6 +273,241 @@ __global__ __launch_bounds__(256) void vq_decode_kernel(VqDec p) {
     }
 }
 
+// ---------------------------------------------------------------- fused decode
+// softmax(scale * logits) . V over one split of keys, for vector-coded keys
+// and values (FibQuant summary, sections 2.3 and 5: decompression fused into
+// attention).  Grid (B * h_kv * ngroups, nsplit); a block of 256 threads
+// serves QB = 4 SLOTS query heads of one KV head and up to kVqSplit keys.
+// Pass 1 scores the keys with the product-code table of the scan and keeps
+// the logits in LDS as [key][query].  Per query the split's max M and
+// l = sum exp(a - M) follow, and the weights w = exp(a - M) nu_v.  Pass 2: lane
+// j of a key stream owns value block j and accumulates sum_t w_t c_v[idx_j(t)]
+// for every query; stream s takes keys s, s + KS, ... (KS = 256 / (D/2)), and
+// the streams' sums are added through LDS.  The partials (M, l, A_y) per
+// (query row, split) go to the split merge, which applies Pi_v^T and divides
+// by l.
+constexpr int kVqSplit = 512;
+
+struct VqAttn {
+    const float* qp;  // [B*Hq][D] q' = Pi_k RoPE(q)
+    const float* knorm;
+    const uint32_t* kcodes;
+    const float* kcode;  // key codewords [NK][2]
+    const float* vnorm;
+    const uint32_t* vcodes;
+    const float* vcode;  // value codewords [NV][2]
+    const int32_t* seq_len;
+    int32_t Hq, h_kv, L_cap, ngroups, nsplit, split_len;
+    int32_t vbits, vwords, nv;
+    float scale;
+    const int32_t* pages;
+    int32_t page_size, max_pages;
+    int64_t n_pages;
+    dev::FastDiv div_page;
+    float* part;  // [B*Hq][nsplit][2 + D]
+};
+
+template <int D, int KB, int SLOTS>
+__global__ __launch_bounds__(256) void vq_attn_split_kernel(VqAttn p) {
+    constexpr int NB = D / 2, NK = 1 << KB, QB = 4 * SLOTS;
+    constexpr int KW = (NB * KB + 31) / 32;
+    constexpr int KS = 256 / NB;  // key streams of pass 2
+    constexpr int LUT_F = 4 * SLOTS * NB * NK;
+    constexpr int ACC_F = KS * QB * D;
+    constexpr int UNION_F = LUT_F > ACC_F ? LUT_F : ACC_F;
+    // the key table (pass 1), later the streams' sums (pass 2)
+    __shared__ float4 s_u4[UNION_F / 4];
+    __shared__ float s_q[QB][D];
+    __shared__ float4 s_w4[kVqSplit][SLOTS];  // [key][query]: logits, then weights
+    __shared__ float2 s_vc[256];
+    __shared__ float s_m[QB], s_l[QB];
+    float4* s_lut = s_u4;  // [SLOTS][NB][NK]
+    float* s_acc = reinterpret_cast<float*>(s_u4);  // [KS][QB][D]
+    float* s_w = reinterpret_cast<float*>(s_w4);
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int grp = blockIdx.x % p.ngroups;
+    const int64_t bk = blockIdx.x / p.ngroups;
+    const int b = (int)(bk / p.h_kv), kh = (int)(bk % p.h_kv);
+    const int G = p.Hq / p.h_kv;
+    const int g0 = grp * QB;
+    const int ng = min(QB, G - g0);
+    const int64_t row0 = (int64_t)b * p.Hq + (int64_t)kh * G + g0;
+    const int sl = min(max(p.seq_len[b], 0), p.L_cap);
+    const int t0 = blockIdx.y * p.split_len;
+    const int cnt = max(0, min(p.split_len, sl - t0));  // keys of this split below seq_len
+
+    for (int i = threadIdx.x; i < QB * D; i += blockDim.x) {
+        const int g = i / D;
+        s_q[g][i % D] = g < ng ? p.qp[(row0 + g) * D + i % D] : 0.0f;
+    }
+    for (int i = threadIdx.x; i < p.nv; i += blockDim.x) s_vc[i] = make_float2(p.vcode[2 * i], p.vcode[2 * i + 1]);
+    __syncthreads();
+    {
+        const int n = threadIdx.x % NK;
+        const float c0 = p.kcode[2 * n], c1 = p.kcode[2 * n + 1];
+        for (int e = threadIdx.x; e < SLOTS * NB * NK; e += blockDim.x) {
+            const int sl4 = e / (NB * NK), j = (e / NK) % NB;
+            float v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = fmaf(s_q[4 * sl4 + i][2 * j + 1], c1, s_q[4 * sl4 + i][2 * j] * c0);
+            s_lut[(sl4 * NB + j) * NK + n] = make_float4(v[0], v[1], v[2], v[3]);
+        }
+    }
+    __syncthreads();
+
+    // pass 1: scaled logits (keys past seq_len: -inf)
+    for (int i = threadIdx.x; i < p.split_len; i += blockDim.x) {
+        float acc[QB];
+#pragma unroll
+        for (int g = 0; g < QB; ++g) acc[g] = 0.0f;
+        if (i < cnt) {
+            const int64_t rec = vq_record(p, bk, b, kh, t0 + i);
+            uint32_t w[KW];
+            load_words<KW>(p.kcodes + rec * KW, w);
+            const float f = p.knorm[rec] * p.scale;
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const uint32_t idx = index_at<KB, KW>(w, j);
+#pragma unroll
+                for (int sl4 = 0; sl4 < SLOTS; ++sl4) {
+                    const float4 t = s_lut[(sl4 * NB + j) * NK + idx];
+                    acc[4 * sl4] += t.x;
+                    acc[4 * sl4 + 1] += t.y;
+                    acc[4 * sl4 + 2] += t.z;
+                    acc[4 * sl4 + 3] += t.w;
+                }
+                if ((j & 7) == 7) {
+#pragma unroll
+                    for (int g = 0; g < QB; ++g) asm volatile("" : "+v"(acc[g]));
+                }
+            }
+#pragma unroll
+            for (int g = 0; g < QB; ++g) acc[g] *= f;
+        } else {
+#pragma unroll
+            for (int g = 0; g < QB; ++g) acc[g] = -INFINITY;
+        }
+#pragma unroll
+        for (int sl4 = 0; sl4 < SLOTS; ++sl4)
+            s_w4[i][sl4] = make_float4(acc[4 * sl4], acc[4 * sl4 + 1], acc[4 * sl4 + 2], acc[4 * sl4 + 3]);
+    }
+    __syncthreads();
+    // softmax statistics per query (a split with no keys: M = -inf, l = 0)
+    for (int g = wave; g < QB; g += 4) {
+        float mx = -INFINITY;
+        for (int i = lane; i < cnt; i += 64) mx = fmaxf(mx, s_w[i * QB + g]);
+        for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        float l = 0.0f;
+        for (int i = lane; i < cnt; i += 64) {
+            const float e = expf(s_w[i * QB + g] - mx);
+            s_w[i * QB + g] = e;
+            l += e;
+        }
+        for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
+        if (lane == 0) {
+            s_m[g] = mx;
+            s_l[g] = l;
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < cnt; i += blockDim.x) {
+        const float nv = p.vnorm[vq_record(p, bk, b, kh, t0 + i)];
+#pragma unroll
+        for (int sl4 = 0; sl4 < SLOTS; ++sl4) {
+            float4 w = s_w4[i][sl4];
+            w.x *= nv;
+            w.y *= nv;
+            w.z *= nv;
+            w.w *= nv;
+            s_w4[i][sl4] = w;
+        }
+    }
+    __syncthreads();
+
+    // pass 2: lane j of stream st accumulates value block j
+    const int j = threadIdx.x % NB, st = threadIdx.x / NB;
+    const int o = j * p.vbits, wi = o >> 5, sh = o & 31;
+    const bool straddle = sh + p.vbits > 32;
+    const uint32_t vmask = (1u << p.vbits) - 1u;
+    float a0[QB], a1[QB];
+#pragma unroll
+    for (int g = 0; g < QB; ++g) a0[g] = a1[g] = 0.0f;
+#pragma unroll 4
+    for (int i = st; i < cnt; i += KS) {
+        const uint32_t* vw = p.vcodes + vq_record(p, bk, b, kh, t0 + i) * p.vwords;
+        uint32_t idx = vw[wi] >> sh;
+        if (straddle) idx |= vw[wi + 1] << (32 - sh);
+        const float2 c = s_vc[idx & vmask];
+#pragma unroll
+        for (int sl4 = 0; sl4 < SLOTS; ++sl4) {
+            const float4 w = s_w4[i][sl4];
+            a0[4 * sl4] = fmaf(w.x, c.x, a0[4 * sl4]);
+            a1[4 * sl4] = fmaf(w.x, c.y, a1[4 * sl4]);
+            a0[4 * sl4 + 1] = fmaf(w.y, c.x, a0[4 * sl4 + 1]);
+            a1[4 * sl4 + 1] = fmaf(w.y, c.y, a1[4 * sl4 + 1]);
+            a0[4 * sl4 + 2] = fmaf(w.z, c.x, a0[4 * sl4 + 2]);
+            a1[4 * sl4 + 2] = fmaf(w.z, c.y, a1[4 * sl4 + 2]);
+            a0[4 * sl4 + 3] = fmaf(w.w, c.x, a0[4 * sl4 + 3]);
+            a1[4 * sl4 + 3] = fmaf(w.w, c.y, a1[4 * sl4 + 3]);
+        }
+    }
+    // (the table is no longer read: every thread passed the barriers above)
+#pragma unroll
+    for (int g = 0; g < QB; ++g) {
+        s_acc[(st * QB + g) * D + 2 * j] = a0[g];
+        s_acc[(st * QB + g) * D + 2 * j + 1] = a1[g];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < QB * D; e += blockDim.x) {
+        const int g = e / D, c = e % D;
+        if (g >= ng) continue;
+        float sum = 0.0f;
+#pragma unroll
+        for (int q = 0; q < KS; ++q) sum += s_acc[(q * QB + g) * D + c];
+        p.part[((row0 + g) * p.nsplit + blockIdx.y) * (2 + D) + 2 + c] = sum;
+    }
+    if (threadIdx.x < ng) {
+        float* dst = p.part + ((row0 + threadIdx.x) * p.nsplit + blockIdx.y) * (2 + D);
+        dst[0] = s_m[threadIdx.x];
+        dst[1] = s_l[threadIdx.x];
+    }
+}
+
+using VqAttnFn = void (*)(VqAttn);
+
+// LDS of the decode's key table: at most 32 KiB
+constexpr bool attn_lut_fits(int d, int bits, int slots) { return (int64_t)slots * (d / 2) * (1 << bits) * 16 <= 32 * 1024; }
+
+template <int D, int KB>
+VqAttnFn pick_vq_attn_bits(int slots) {
+    if constexpr (attn_lut_fits(D, KB, 2)) {
+        if (slots == 2) return vq_attn_split_kernel<D, KB, 2>;
+    }
+    if constexpr (attn_lut_fits(D, KB, 1)) {
+        if (slots == 1) return vq_attn_split_kernel<D, KB, 1>;
+    }
+    return nullptr;
+}
+
+template <int D>
+VqAttnFn pick_vq_attn(int kbits, int slots) {
+    switch (kbits) {
+        case 1: return pick_vq_attn_bits<D, 1>(slots);
+        case 2: return pick_vq_attn_bits<D, 2>(slots);
+        case 3: return pick_vq_attn_bits<D, 3>(slots);
+        case 4: return pick_vq_attn_bits<D, 4>(slots);
+        case 5: return pick_vq_attn_bits<D, 5>(slots);
+        case 6: return pick_vq_attn_bits<D, 6>(slots);
+    }
+    return nullptr;
+}
+
+int vq_attn_slots(int d, int kbits, int G) {
+    if (G > 4 && attn_lut_fits(d, kbits, 2)) return 2;
+    return attn_lut_fits(d, kbits, 1) ? 1 : 0;
+}
+
 // dense rotation: x = nu Pi^T y_hat, one block per vector (grid-stride); the
 // concatenated codewords y_hat are staged in LDS, and thread c forms output
 // coordinate c from column c of Pi (rows read in order, coalesced)
@@ -401,6 +637,56 @@ hipError_t launch_vq_logits(const tq_codebook* ck, const tq_packed& k, const Att
     const int64_t gy = (klen + per_block - 1) / per_block;
     if (gx == 0 || gy == 0) return hipSuccess;
     hipLaunchKernelGGL(fn, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+bool vq_attn_supported(const tq_codebook* ck, const tq_codebook* cv) {
+    if (!vq_supported(ck) || !vq_supported(cv) || ck->dense || cv->dense) return false;
+    if (ck->spec.d != cv->spec.d) return false;
+    return vq_attn_slots(ck->spec.d, ck->spec.bits, 1) > 0;
+}
+
+void vq_attn_plan(int L_cap, int* nsplit, int* split_len) {
+    *split_len = kVqSplit;
+    *nsplit = std::max(1, (L_cap + kVqSplit - 1) / kVqSplit);
+}
+
+hipError_t launch_vq_attn_split(const tq_codebook* ck, const tq_codebook* cv, const tq_packed& k, const tq_packed& v,
+                                const AttnArgs& a, const float* qp, float* part, int nsplit, int split_len,
+                                hipStream_t stream) {
+    const int d = ck->spec.d;
+    const int G = a.Hq / a.h_kv;
+    const int slots = vq_attn_slots(d, ck->spec.bits, G);
+    VqAttnFn fn = d == 64 ? pick_vq_attn<64>(ck->spec.bits, slots) : pick_vq_attn<128>(ck->spec.bits, slots);
+    if (!fn) return hipErrorInvalidValue;
+    VqAttn p{};
+    p.qp = qp;
+    p.knorm = k.norm;
+    p.kcodes = k.codes;
+    p.kcode = ck->dev.levels;
+    p.vnorm = v.norm;
+    p.vcodes = v.codes;
+    p.vcode = cv->dev.levels;
+    p.seq_len = a.seq_len;
+    p.Hq = a.Hq;
+    p.h_kv = a.h_kv;
+    p.L_cap = a.L_cap;
+    p.ngroups = (G + 4 * slots - 1) / (4 * slots);
+    p.nsplit = nsplit;
+    p.split_len = split_len;
+    p.vbits = cv->spec.bits;
+    p.vwords = (int)((cv->spec.bits * (d / 2) + 31) / 32);
+    p.nv = cv->K;
+    p.scale = a.scale;
+    p.pages = a.pages.table;
+    p.page_size = a.pages.size;
+    p.max_pages = a.pages.max_pages;
+    p.n_pages = a.pages.n_pages;
+    p.div_page = dev::FastDiv((uint32_t)(a.pages.size > 0 ? a.pages.size : 1));
+    p.part = part;
+    const int64_t gx = (int64_t)a.B * a.h_kv * p.ngroups;
+    if (gx == 0) return hipSuccess;
+    hipLaunchKernelGGL(fn, dim3((unsigned)gx, (unsigned)nsplit), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

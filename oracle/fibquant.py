@@ -49,7 +49,8 @@ sphere and its exact second moment; N = 2 against the closed form +-E|Y|;
 Lloyd fixed points checked by brute-force nearest codewords; the vector
 code's distortion below the scalar Lloyd-Max table's at equal rate (the
 page's claim of strict dominance); the rate arithmetic; logits against the
-decoder's rebuilt vectors.
+decoder's rebuilt vectors; attention against textbook softmax attention over
+the rebuilt keys and values.
 """
 from __future__ import annotations
 
@@ -263,3 +264,20 @@ def logits(cb: VQCodebook, qp: np.ndarray, norm: np.ndarray, codes: np.ndarray) 
     idx = unpack_indices(codes, cb.index_bits, nb)
     yhat = cb.code32.astype(np.float64)[idx].reshape(len(idx), cb.d)
     return (np.asarray(norm, np.float64)[:, None] * (yhat @ np.asarray(qp, np.float64).T)).T
+
+
+def attention(ck: VQCodebook, cv: VQCodebook, qp: np.ndarray, knorm: np.ndarray, kcodes: np.ndarray,
+              vnorm: np.ndarray, vcodes: np.ndarray, scale: float) -> np.ndarray:
+    """Attention of prepared queries q' = Pi_k RoPE(q) [G, d] over n
+    vector-coded keys and values (float64 [G, d]): softmax over scale times
+    the logits, then the weighted sum of the decoded values (section 2.3's
+    decoder; section 5 asks for decompression fused with attention).  No keys
+    give zeros."""
+    qp = np.asarray(qp, np.float64)
+    if len(knorm) == 0:
+        return np.zeros((qp.shape[0], cv.d))
+    a = scale * logits(ck, qp, knorm, kcodes)
+    a = a - a.max(axis=1, keepdims=True)
+    w = np.exp(a)
+    w /= w.sum(axis=1, keepdims=True)
+    return w @ reconstruct(cv, vnorm, vcodes)

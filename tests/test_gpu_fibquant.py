@@ -251,13 +251,101 @@ def test_vq_dense_rejections():
     assert ei.value.code == -2
 
 
+def fused_case(d, kbits, vbits, B, H, L, seed):
+    """Oracle-encoded keys (RoPE at their slots) and values, as records for
+    both sides."""
+    g = synth.rng(seed)
+    ok, gk = books(d, kbits, seed + 1)
+    ov, gv = books(d, vbits, seed + 2)
+    rope_o = orope.rope_table(5e5, d, L + 1)
+    n = B * H * L
+    K = g.standard_normal((n, d)) * np.linspace(0.5, 3.0, d)
+    V = g.standard_normal((n, d))
+    ek = F.encode(ok, K, pos=np.tile(np.arange(L), B * H), rope=rope_o)
+    ev = F.encode(ov, V)
+    return g, (ok, gk, ek), (ov, gv, ev), rope_o
+
+
+def fused_reference(ok, ov, ek, ev, Q, lens, H, L, rope_o, rows_of):
+    """[B, Hq, d] oracle attention; rows_of(b, h, t) gives the records of
+    slots t of (sequence b, KV head h)."""
+    B, Hq, d = Q.shape
+    G = Hq // H
+    out = np.zeros((B, Hq, d))
+    kn = ek.norm.astype(np.float32).astype(np.float64)
+    vn = ev.norm.astype(np.float32).astype(np.float64)
+    for b in range(B):
+        qp, _ = estimator.prep_query(o_as_scalar(ok), Q[b], int(lens[b]), rope_o)
+        for h in range(H):
+            r = rows_of(b, h, np.arange(lens[b]))
+            out[b, h * G:(h + 1) * G] = F.attention(ok, ov, qp[h * G:(h + 1) * G], kn[r], ek.codes[r], vn[r],
+                                                    ev.codes[r], 1.0 / np.sqrt(d))
+    return out
+
+
+@pytest.mark.parametrize("d,kbits,vbits,Hq,H", [
+    (128, 4, 3, 8, 2),   # groups of 4: one table slot
+    (128, 4, 8, 12, 2),  # groups of 6: two slots, 256 value codewords
+    (128, 5, 2, 4, 1),   # 32 key codewords
+    (64, 6, 5, 6, 1),    # d = 64: eight key streams, indices straddling words
+])
+def test_vq_fused_decode(d, kbits, vbits, Hq, H):
+    """softmax . V over vector-coded keys and values, through the split merge:
+    lengths over several 512-key splits, a ragged tail and an empty sequence."""
+    B, L = 3, 1300
+    g, (ok, gk, ek), (ov, gv, ev), rope_o = fused_case(d, kbits, vbits, B, H, L, 80 + kbits + vbits)
+    z = np.zeros((B * H * L, 0))
+    kp = tq.Packed.from_arrays(gk, ek.norm.astype(np.float32), np.zeros(0), ek.codes, z)
+    vp = tq.Packed.from_arrays(gv, ev.norm.astype(np.float32), np.zeros(0), ev.codes, z)
+    Q = g.standard_normal((B, Hq, d)).astype(np.float32)
+    lens = np.array([1300, 777, 0], np.int32)
+    out = tq.attn_decode(gk, gv, torch.from_numpy(Q).cuda(), kp, vp, H, L, torch.from_numpy(lens).cuda(),
+                         rope=tq.rope_table(5e5, d, L + 1)).cpu().numpy()
+    ref = fused_reference(ok, ov, ek, ev, Q, lens, H, L, rope_o, lambda b, h, t: (b * H + h) * L + t)
+    parity.assert_close(out, ref, f"vq fused decode d{d} k{kbits} v{vbits} Hq{Hq}")
+    assert not np.any(out[2])
+
+
+def test_vq_fused_decode_paged():
+    """The same decode with records in shuffled pages of 64 slots."""
+    d, B, H, Hq, P, J = 128, 2, 2, 8, 64, 12
+    L = P * J
+    g, (ok, gk, ek), (ov, gv, ev), rope_o = fused_case(d, 4, 4, B, H, L, 120)
+    table = g.permutation(B * J + 3)[:B * J].astype(np.int32).reshape(B, J)
+    nrec = (B * J + 3) * H * P
+    cont = lambda b, h, t: (b * H + h) * L + t
+    dst = np.concatenate([paging.paged_index(table, P, H, b, h, np.arange(L)) for b in range(B) for h in range(H)])
+    src = np.concatenate([cont(b, h, np.arange(L)) for b in range(B) for h in range(H)])
+
+    def placed(enc):
+        norm = np.zeros(nrec, np.float32)
+        codes = np.zeros((nrec, enc.codes.shape[1]), np.uint32)
+        norm[dst], codes[dst] = enc.norm[src], enc.codes[src]
+        return norm, codes
+
+    kn, kc = placed(ek)
+    vn, vc = placed(ev)
+    z = np.zeros((nrec, 0))
+    kp = tq.Packed.from_arrays(gk, kn, np.zeros(0), kc, z)
+    vp = tq.Packed.from_arrays(gv, vn, np.zeros(0), vc, z)
+    pg = tq.Pages(torch.from_numpy(table).cuda(), P, B * J + 3)
+    Q = g.standard_normal((B, Hq, d)).astype(np.float32)
+    lens = np.array([L, 601], np.int32)
+    out = tq.attn_decode(gk, gv, torch.from_numpy(Q).cuda(), kp, vp, H, None, torch.from_numpy(lens).cuda(),
+                         rope=tq.rope_table(5e5, d, L + 1), pages=pg).cpu().numpy()
+    ref = fused_reference(ok, ov, ek, ev, Q, lens, H, L, rope_o, cont)
+    parity.assert_close(out, ref, "vq paged fused decode")
+
+
 def test_vq_rejections():
     o, gc = books(128, 4, 3)
     kp = tq.Packed(gc, 64)
     q = torch.zeros((1, 4, 128), device="cuda")
     sl = torch.tensor([64], dtype=torch.int32, device="cuda")
+    scalar = tq.Codebook(128, 3, 64, "hadamard", seed=1)
+    sp = tq.Packed(scalar, 64)
     with pytest.raises(tq.TQError) as ei:
-        tq.attn_decode(gc, gc, q, kp, kp, 1, 64, sl)
+        tq.attn_decode(scalar, gc, q, sp, kp, 1, 64, sl)  # scalar keys with vector-coded values
     assert ei.value.code == -2
     with pytest.raises(tq.TQError) as ei:
         tq.decode_vectors(gc, kp, first=10, count=60)

@@ -119,3 +119,31 @@ def test_encoder_is_nearest_codeword_and_logits_match_the_decoder():
     err = ((rec - x / enc.norm[:, None]) ** 2).mean()
     _, mse = F.build_codebook(d, k, N)
     assert abs(err - mse / k) < 0.25 * mse / k
+
+
+def test_attention_is_softmax_attention_over_decoded_keys_and_values():
+    """The fused decode's oracle equals textbook attention (scipy's softmax)
+    over the decoder's rebuilt keys and values, with RoPE applied to the
+    query before the rotation; no keys give zeros."""
+    from scipy.special import softmax
+    from oracle import rope as orope
+    d, n, G = 64, 300, 3
+    g = np.random.default_rng(9)
+    sk = np.where(g.integers(0, 2, d) == 1, 1, -1)
+    sv = np.where(g.integers(0, 2, d) == 1, 1, -1)
+    ck = F.make_vq_codebook(d, 2, 16, sk)
+    cv = F.make_vq_codebook(d, 2, 8, sv)
+    cs, sn = orope.rope_table(1e4, d, n + 1)
+    K, V = g.standard_normal((n, d)) * 2.0, g.standard_normal((n, d))
+    ek = F.encode(ck, K, pos=np.arange(n), rope=(cs, sn))
+    ev = F.encode(cv, V)
+    q = g.standard_normal((G, d))
+    q_rot = orope.apply_rope(q, np.full(G, n), cs, sn)
+    scale = 1.0 / math.sqrt(d)
+    out = F.attention(ck, cv, q_rot @ ck.pi.T, ek.norm, ek.codes, ev.norm, ev.codes, scale)
+    khat = F.reconstruct(ck, ek.norm, ek.codes)
+    vhat = F.reconstruct(cv, ev.norm, ev.codes)
+    ref = softmax(scale * (q_rot @ khat.T), axis=1) @ vhat
+    np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-12)
+    assert not np.any(F.attention(ck, cv, q_rot @ ck.pi.T, ek.norm[:0], ek.codes[:0], ev.norm[:0], ev.codes[:0],
+                                  scale))
