@@ -234,8 +234,8 @@ FIB_BITS = 4  # 16 codewords per 2-coordinate block: 2 bits per coordinate
 
 def setup_fib(torch, tq, synth):
     """The Llama-3.1-8B-shaped layer with FibQuant vector codebooks for keys
-    and values (k = 2, N = 16): encode K (RoPE), encode V, and the logit scan
-    of the 32 query heads over every cached key."""
+    and values (k = 2, N = 16): encode K (RoPE), encode V, the logit scan of
+    the 32 query heads over every cached key, and the fused decode."""
     B, Hq, H, L, d = 8, 32, 8, 32768, 128
     K, V = synth.llama_kv_inputs("llama8b", seed=0, batch=B, ctx=L, hkv=H, d=d)
     Q = synth.llama_q_inputs(seed=100, batch=B, hq=Hq, d=d)
@@ -249,12 +249,17 @@ def setup_fib(torch, tq, synth):
     st["logits"] = torch.empty((B, Hq, L), dtype=torch.float32, device="cuda")
     st["ws_l"] = torch.empty(max(1, tq.workspace_bytes(st["ck"], None, tq.TQ_OP_LOGITS, B, Hq, H, L, 0)),
                              dtype=torch.uint8, device="cuda")
+    st["out"] = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    st["ws_d"] = torch.empty(max(1, tq.workspace_bytes(st["ck"], st["cv"], tq.TQ_OP_DECODE, B, Hq, H, L, 0)),
+                             dtype=torch.uint8, device="cuda")
     st["calls"] = [
         ("encode_k", tq.encode_kv(st["ck"], None, st["K"], None, st["kp"], None, L_cap=L, rope=st["rope"],
                                   prepare=True)),
         ("encode_v", tq.encode_kv(None, st["cv"], None, st["V"], None, st["vp"], L_cap=L, prepare=True)),
         ("logits", tq.attn_logits(st["ck"], st["Q"], st["kp"], H, L, st["sl"], rope=st["rope"], out=st["logits"],
                                   workspace=st["ws_l"], prepare=True)[0]),
+        ("decode", tq.attn_decode(st["ck"], st["cv"], st["Q"], st["kp"], st["vp"], H, L, st["sl"], rope=st["rope"],
+                                  out=st["out"], workspace=st["ws_d"], prepare=True)[0]),
     ]
     return st
 
@@ -266,16 +271,20 @@ def fib_report(st, timer, ms_step):
     enc_ms, n = timer.mean_ms("encode_k")
     encv_ms, _ = timer.mean_ms("encode_v")
     log_ms, _ = timer.mean_ms("logits")
+    dec_ms, _ = timer.mean_ms("decode")
     kern = {"encode_k": {"ms": enc_ms, "launches": n, "alg_bytes": keys * (2 * d + rec), "units": keys},
             "encode_v": {"ms": encv_ms, "alg_bytes": keys * (2 * d + rec), "units": keys},
-            "logits": {"ms": log_ms, "alg_bytes": keys * (rec + 4 * Hq // H), "units": keys}}
+            "logits": {"ms": log_ms, "alg_bytes": keys * (rec + 4 * Hq // H), "units": keys},
+            "decode": {"ms": dec_ms, "alg_bytes": keys * 2 * rec, "units": keys}}
     for k in kern.values():
         k["GBps"] = k["alg_bytes"] / (k["ms"] * 1e-3) / 1e9
         k["hbm_frac"] = k["GBps"] / HBM_PEAK_GBS
     dom = max(kern, key=lambda x: kern[x]["ms"])
     extra = {"logit_keys_per_s": keys / (log_ms * 1e-3), "logit_hbm_frac": kern["logits"]["hbm_frac"],
+             "decode_keys_per_s": keys / (dec_ms * 1e-3),
              "encode_vectors_per_s": 2 * keys / ((enc_ms + encv_ms) * 1e-3)}
-    cfg = {"workload": "Llama-3.1-8B-shaped layer with FibQuant vector codebooks (encode K, V; logits)", "batch": B,
+    cfg = {"workload": "Llama-3.1-8B-shaped layer with FibQuant vector codebooks (encode K, V; logits; decode)",
+           "batch": B,
            "q_heads": Hq, "kv_heads": H, "head_dim": d, "context": L, "block": 2, "codewords": 1 << bits,
            "bits_per_coordinate": bits / 2, "input_dtype": "bf16", "rope_base": st["rope_base"],
            "record_bytes": rec}
@@ -308,9 +317,10 @@ def cpu_baseline_fib(st, budget_s=10.0):
             q = synth.bf16_bits_to_f32(Q[b, kh * G:(kh + 1) * G])
             t1 = time.perf_counter()
             ek = F.encode(ock, kx, pos=np.arange(n), rope=rope)
-            F.encode(ocv, vx)
+            ev = F.encode(ocv, vx)
             qp = apply_rope(q, np.full(G, L), rope[0], rope[1]) @ ock.pi.T
             F.logits(ock, qp, ek.norm, ek.codes)
+            F.attention(ock, ocv, qp, ek.norm, ek.codes, ev.norm, ev.codes, 1.0 / math.sqrt(d))
             dt += time.perf_counter() - t1
             done += n
             pairs += 1
@@ -320,8 +330,8 @@ def cpu_baseline_fib(st, budget_s=10.0):
     except Exception:
         threads = len(os.sched_getaffinity(0))
     return {"value": done / dt, "unit": "keys/s", "cores": threads, "kind": "oracle",
-            "sample": f"{pairs} (sequence, KV head) pairs, the first {n} keys and values of each encoded and scored "
-                      f"for {G} query heads by the oracle, {dt:.1f} s on the host (codebook built beforehand, "
+            "sample": f"{pairs} (sequence, KV head) pairs, the first {n} keys and values of each encoded, scored "
+                      f"and attended for {G} query heads by the oracle, {dt:.1f} s on the host (codebook built beforehand, "
                       f"{t_setup:.1f} s)"}
 
 

@@ -278,15 +278,16 @@ __global__ __launch_bounds__(256) void vq_decode_kernel(VqDec p) {
 // and values (FibQuant summary, sections 2.3 and 5: decompression fused into
 // attention).  Grid (B * h_kv * ngroups, nsplit); a block of 256 threads
 // serves QB = 4 SLOTS query heads of one KV head and up to kVqSplit keys.
-// Pass 1 scores the keys with the product-code table of the scan and keeps
-// the logits in LDS as [key][query].  Per query the split's max M and
+// Pass 1 (one key per thread) scores the keys with the product-code table of
+// the scan, keeps the logits in LDS as [key][query] and stages the keys'
+// value records and norms in LDS.  Per query the split's max M and
 // l = sum exp(a - M) follow, and the weights w = exp(a - M) nu_v.  Pass 2: lane
 // j of a key stream owns value block j and accumulates sum_t w_t c_v[idx_j(t)]
-// for every query; stream s takes keys s, s + KS, ... (KS = 256 / (D/2)), and
-// the streams' sums are added through LDS.  The partials (M, l, A_y) per
-// (query row, split) go to the split merge, which applies Pi_v^T and divides
-// by l.
-constexpr int kVqSplit = 512;
+// for every query from the staged records; stream s takes keys s, s + KS, ...
+// (KS = 256 / (D/2)), and the streams' sums are added through LDS.  The
+// partials (M, l, A_y) per (query row, split) go to the split merge, which
+// applies Pi_v^T and divides by l.
+constexpr int kVqSplit = 256;
 
 struct VqAttn {
     const float* qp;  // [B*Hq][D] q' = Pi_k RoPE(q)
@@ -320,6 +321,9 @@ __global__ __launch_bounds__(256) void vq_attn_split_kernel(VqAttn p) {
     __shared__ float s_q[QB][D];
     __shared__ float4 s_w4[kVqSplit][SLOTS];  // [key][query]: logits, then weights
     __shared__ float2 s_vc[256];
+    // value records of the split, vwords each (+1: a funnel shift reads one word past the last block)
+    __shared__ uint32_t s_vrec[kVqSplit * (D / 2 * 8 / 32) + 1];
+    __shared__ float s_vn[kVqSplit];
     __shared__ float s_m[QB], s_l[QB];
     float4* s_lut = s_u4;  // [SLOTS][NB][NK]
     float* s_acc = reinterpret_cast<float*>(s_u4);  // [KS][QB][D]
@@ -366,6 +370,8 @@ __global__ __launch_bounds__(256) void vq_attn_split_kernel(VqAttn p) {
             uint32_t w[KW];
             load_words<KW>(p.kcodes + rec * KW, w);
             const float f = p.knorm[rec] * p.scale;
+            for (int u = 0; u < p.vwords; ++u) s_vrec[i * p.vwords + u] = p.vcodes[rec * p.vwords + u];
+            s_vn[i] = p.vnorm[rec];
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
                 const uint32_t idx = index_at<KB, KW>(w, j);
@@ -412,7 +418,7 @@ __global__ __launch_bounds__(256) void vq_attn_split_kernel(VqAttn p) {
     }
     __syncthreads();
     for (int i = threadIdx.x; i < cnt; i += blockDim.x) {
-        const float nv = p.vnorm[vq_record(p, bk, b, kh, t0 + i)];
+        const float nv = s_vn[i];
 #pragma unroll
         for (int sl4 = 0; sl4 < SLOTS; ++sl4) {
             float4 w = s_w4[i][sl4];
@@ -428,17 +434,17 @@ __global__ __launch_bounds__(256) void vq_attn_split_kernel(VqAttn p) {
     // pass 2: lane j of stream st accumulates value block j
     const int j = threadIdx.x % NB, st = threadIdx.x / NB;
     const int o = j * p.vbits, wi = o >> 5, sh = o & 31;
-    const bool straddle = sh + p.vbits > 32;
     const uint32_t vmask = (1u << p.vbits) - 1u;
     float a0[QB], a1[QB];
 #pragma unroll
     for (int g = 0; g < QB; ++g) a0[g] = a1[g] = 0.0f;
-#pragma unroll 4
+#pragma unroll 8
     for (int i = st; i < cnt; i += KS) {
-        const uint32_t* vw = p.vcodes + vq_record(p, bk, b, kh, t0 + i) * p.vwords;
-        uint32_t idx = vw[wi] >> sh;
-        if (straddle) idx |= vw[wi + 1] << (32 - sh);
-        const float2 c = s_vc[idx & vmask];
+        // the index's bits from the word pair (a funnel shift: no branch for
+        // indices that straddle two words)
+        const uint32_t* vw = s_vrec + i * p.vwords + wi;
+        const uint32_t idx = __builtin_amdgcn_alignbit(vw[1], vw[0], sh) & vmask;
+        const float2 c = s_vc[idx];
 #pragma unroll
         for (int sl4 = 0; sl4 < SLOTS; ++sl4) {
             const float4 w = s_w4[i][sl4];
