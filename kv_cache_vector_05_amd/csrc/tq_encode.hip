@@ -27,9 +27,11 @@
 // Vector codebooks (FibQuant summary, sections 2.1-2.3; MODE 3): after the
 // rotation each lane holds 32 (d = 128) or 16 (d = 64) whole blocks of two
 // coordinates (registers r, r + 1 for even r), so the nearest codeword - the
-// largest <y, c> - |c|^2 / 2, ties to the smaller index - is a search over
-// the shared codebook (registers for N <= 16, LDS broadcast above) with no
-// data exchange; the indices are packed LSB first, lane half 1's moved up
+// largest <y, c> - |c|^2 / 2, ties to the smaller index - needs no data
+// exchange.  Codebooks of up to 64 codewords look the block's cell up in a
+// candidate grid (built by the host, in LDS) and score its four candidates;
+// cells with more candidates, blocks off the grid and larger codebooks score
+// every codeword.  The indices are packed LSB first, lane half 1's moved up
 // by two blocks, and the pair's words merged.
 // Blocks are persistent (one resident round, grid-stride over tiles) so each
 // block stages its tables in LDS once; tiles run token block, then sequence,
@@ -76,6 +78,8 @@ struct EncK {
     const float* levels;
     const float* thresholds;
     const float* sketch_mfma;
+    const uint32_t* vq_grid;  // vector codebooks: candidate grid (tq_internal.h), or nullptr
+    float vq_inv_cell;
     float* norm;
     float* rnorm;
     uint32_t* codes;
@@ -245,21 +249,26 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
     __shared__ uint4 s_had[NOROT ? 1 : (NEG_LDS ? 2 : 1) * NKB * 64];
     // scaled levels, indexed by code (3 and 4 bits: looked up by K/2 + c')
     __shared__ float s_lvl[16];
-    // vector codebook, scaled: {c0, c1, -|c|^2 / 2} (LDS above 16 codewords)
+    // vector codebook, scaled: {c0, c1, -|c|^2 / 2}; codebooks of up to 64
+    // codewords search the candidates of their grid cell
     constexpr int NV = VQ ? 1 << BITS : 1;
-    constexpr bool VQREG = VQ && NV <= 16;
-    __shared__ float4 s_vq[VQ && !VQREG ? NV : 1];
+    constexpr bool VQGRID = VQ && NV <= kVqGridMaxN;
+    __shared__ float4 s_vq[NV];
+    __shared__ uint32_t s_grid[VQGRID ? kVqGrid * kVqGrid : 1];
 
     if constexpr (SKETCH) {
         const half8* src = reinterpret_cast<const half8*>(p.sketch_mfma);
         for (int i = threadIdx.x; i < SKN; i += blockDim.x) s_sk[i] = src[i];
     }
     if (!VQ && threadIdx.x < 16) s_lvl[threadIdx.x] = threadIdx.x < 2 * KH ? p.levels[threadIdx.x] * ESCALE : 0.0f;
-    if constexpr (VQ && !VQREG) {
+    if constexpr (VQ) {
         for (int i = threadIdx.x; i < NV; i += blockDim.x) {
             const float c0 = p.levels[2 * i] * ESCALE, c1 = p.levels[2 * i + 1] * ESCALE;
             s_vq[i] = make_float4(c0, c1, -0.5f * (c0 * c0 + c1 * c1), 0.0f);
         }
+    }
+    if constexpr (VQGRID) {
+        for (int i = threadIdx.x; i < kVqGrid * kVqGrid; i += blockDim.x) s_grid[i] = p.vq_grid[i];
     }
     for (int i = threadIdx.x; i < (NOROT ? 0 : NKB * 64); i += blockDim.x) {
         const int kb = i >> 6, row = i & 31, hh = (i >> 5) & 1;
@@ -299,18 +308,8 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
 #pragma unroll
         for (int k = 0; k < KH; ++k) pl[k] = p.levels[KH + k] * ESCALE;
     }
-    // small vector codebooks in registers, scaled: the coordinates in scalar
-    // registers (one scalar operand per FMA), -|c|^2 / 2 in vector registers
-    float vc0[VQREG ? NV : 1], vc1[VQREG ? NV : 1], vnh[VQREG ? NV : 1];
-    if constexpr (VQREG) {
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const float c0 = p.levels[2 * i] * ESCALE, c1 = p.levels[2 * i + 1] * ESCALE;
-            vc0[i] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, c0)));
-            vc1[i] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, c1)));
-            vnh[i] = -0.5f * (c0 * c0 + c1 * c1);
-        }
-    }
+    // grid coordinates of a scaled block: cell = floor(y * inv_cell / 2^8 + kVqGrid / 2)
+    const float vq_gscale = p.vq_inv_cell * (1.0f / ESCALE);
     const float yscale = ESCALE / sqrtf((float)D);
 
     // RoPE rows of the block's 32 tokens, staged in LDS when the block's four
@@ -648,27 +647,41 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
             uint32_t cw[CW];
 #pragma unroll
             for (int w = 0; w < CW; ++w) cw[w] = 0u;
+            // (pairs one at a time: batching the cells' grid reads costs
+            // registers and occupancy, which the values' encoder needs more)
 #pragma unroll
             for (int ob = 0; ob < NOB; ++ob)
 #pragma unroll
                 for (int r = 0; r < 16; r += 2) {
                     const float y0 = EXACT ? fmaf(acc[ob][r], scale, 0.0f) : acc[ob][r];
                     const float y1 = EXACT ? fmaf(acc[ob][r + 1], scale, 0.0f) : acc[ob][r + 1];
-                    float bs;
+                    // the nearest codeword: the first maximum of <y, c> - |c|^2 / 2
+                    // over the cell's candidates, or over the whole codebook
+                    float bs = -INFINITY;
                     uint32_t bi = 0u;
-                    if constexpr (VQREG) {
-                        bs = fmaf(vc0[0], y0, fmaf(vc1[0], y1, vnh[0]));
+                    bool full = true;
+                    if constexpr (VQGRID) {
+                        const int ix = (int)floorf(fmaf(y0, vq_gscale, 0.5f * kVqGrid));
+                        const int iy = (int)floorf(fmaf(y1, vq_gscale, 0.5f * kVqGrid));
+                        const bool in = ((ix | iy) & ~(kVqGrid - 1)) == 0;
+                        const uint32_t cw0 = s_grid[in ? (iy << kVqGridLog) | ix : 0];
+                        // a flagged cell (byte 0 = 0xFF) searches everything;
+                        // its candidate reads stay at codeword 0
+                        full = !in || (cw0 & 0xFFu) == 0xFFu;
+                        const uint32_t cand = full ? 0u : cw0;
 #pragma unroll
-                        for (int c = 1; c < NV; ++c) {
-                            const float sc = fmaf(vc0[c], y0, fmaf(vc1[c], y1, vnh[c]));
+                        for (int q = 0; q < 4; ++q) {
+                            const uint32_t c = (cand >> (8 * q)) & 0xFFu;
+                            const float4 cv = s_vq[c];
+                            const float sc = fmaf(cv.x, y0, fmaf(cv.y, y1, cv.z));
                             if (sc > bs) {
                                 bs = sc;
-                                bi = (uint32_t)c;
+                                bi = c;
                             }
                         }
-                    } else {
+                    }
+                    if (full) {
                         bs = -INFINITY;
-#pragma unroll 2
                         for (int c = 0; c < NV; ++c) {
                             const float4 cv = s_vq[c];
                             const float sc = fmaf(cv.x, y0, fmaf(cv.y, y1, cv.z));
@@ -1247,6 +1260,8 @@ hipError_t launch_encode(const tq_codebook* cb, const EncodeArgs& a, hipStream_t
         p.levels = cb->dev.levels;
         p.thresholds = cb->dev.thresholds;
         p.sketch_mfma = cb->dev.sketch_mfma;
+        p.vq_grid = cb->dev.vq_grid;
+        p.vq_inv_cell = cb->vq_inv_cell;
         p.norm = a.out.norm;
         p.rnorm = a.out.rnorm;
         p.codes = a.out.codes;

@@ -570,6 +570,52 @@ float f16_to_f32(uint16_t h) {
 }
 
 // Builds every host table of a codebook.
+// Candidate grid of a two-coordinate codebook for the encoder's nearest-codeword
+// search (layout in tq_internal.h).  Cells cover |y_i| < 5 / sqrt(d): a
+// rotated unit vector's coordinate has standard deviation 1 / sqrt(d), so
+// blocks outside are rare (they fall back to the full search).  Codeword n
+// is a candidate for the cell of centre m when
+//   |m - c_n| <= min_k |m - c_k| + 2 rho + eps,
+// rho the cell's half-diagonal with 2e-4 of slack for the float32 cell
+// assignment, eps = 3e-4.  For any point p of the cell a codeword outside the
+// list is then farther than the best candidate by more than eps, so its
+// squared distance exceeds the best one's by more than eps^2 - far above the
+// float32 rounding of the scores - and the first maximum over the candidates
+// (ascending) is the first maximum over the whole codebook.
+static void vq_candidate_grid(const std::vector<float>& code, int N, int d, std::vector<uint32_t>* grid,
+                              float* inv_cell) {
+    const double R = 5.0 / std::sqrt((double)d);
+    *inv_cell = (float)(kVqGrid / (2.0 * R));
+    const double cell = 1.0 / (double)*inv_cell;
+    const double rho = cell * std::sqrt(0.5) * (1.0 + 2e-4), eps = 3e-4;
+    grid->assign((size_t)kVqGrid * kVqGrid, 0u);
+    std::vector<double> dist(N);
+    for (int iy = 0; iy < kVqGrid; ++iy)
+        for (int ix = 0; ix < kVqGrid; ++ix) {
+            const double mx = (ix - kVqGrid / 2 + 0.5) * cell, my = (iy - kVqGrid / 2 + 0.5) * cell;
+            double best = INFINITY;
+            for (int n = 0; n < N; ++n) {
+                const double dx = mx - code[2 * n], dy = my - code[2 * n + 1];
+                dist[n] = std::sqrt(dx * dx + dy * dy);
+                best = std::min(best, dist[n]);
+            }
+            uint32_t w = 0;
+            int cnt = 0, last = 0;
+            for (int n = 0; n < N && cnt <= 4; ++n)
+                if (dist[n] <= best + 2.0 * rho + eps) {
+                    if (cnt < 4) w |= (uint32_t)n << (8 * cnt);
+                    last = n;
+                    ++cnt;
+                }
+            if (cnt > 4) {
+                w = 0xFFu;
+            } else {
+                for (int q = cnt; q < 4; ++q) w |= (uint32_t)last << (8 * q);
+            }
+            (*grid)[(size_t)iy * kVqGrid + ix] = w;
+        }
+}
+
 static tq_status build_tables(const tq_spec& s, const tq_draws* dr, bool dense,
                               std::vector<float>* levels, std::vector<float>* thr,
                               std::vector<float>* rot, std::vector<float>* sk) {
@@ -731,6 +777,8 @@ static tq_status codebook_create(const tq_spec* spec, const tq_draws* draws, con
     }
     if (cb->K <= 8 && !vq) level_digits(cb->levels, cb->lvl_digits, &cb->lvl_shift);
     const int d = spec->d, m = spec->m;
+    if (vq && spec->block == 2 && !dense && cb->K <= kVqGridMaxN)
+        vq_candidate_grid(cb->levels, cb->K, d, &cb->vq_grid, &cb->vq_inv_cell);
     // the encode kernel's sketch operand (Hadamard form): S split into fp16
     // hi + lo parts in the A-operand order of v_mfma_f32_32x32x16_f16, the
     // columns in the order the kernel's Hadamard MFMAs leave the residual in:
@@ -753,13 +801,14 @@ static tq_status codebook_create(const tq_spec* spec, const tq_draws* draws, con
                         out[base + 64 * 8] = lo;
                     }
     }
-    // one device block: levels[16] | thresholds[16] | sigma[d] or rot[d*d] | sketch | sketch_mfma | mu
-    // (the sign correction's S = I is never read on the device)
+    // one device block: levels[16] | thresholds[16] | sigma[d] or rot[d*d] | sketch | sketch_mfma | mu |
+    // candidate grid (the sign correction's S = I is never read on the device)
     const size_t n_lv = vq ? std::max<size_t>(16, cb->levels.size()) : 16, n_th = 16;
     const size_t n_rot = dense ? (size_t)d * d : (size_t)d;
     const size_t n_sk = sign ? 0 : (size_t)m * d;
     const size_t n_mu_dev = cb->mu.size();
-    const size_t total = n_lv + n_th + n_rot + 2 * n_sk + n_mu_dev;
+    const size_t n_grid = cb->vq_grid.size();
+    const size_t total = n_lv + n_th + n_rot + 2 * n_sk + n_mu_dev + n_grid;
     std::vector<float> host(total, 0.0f);
     std::memcpy(host.data(), cb->levels.data(), cb->levels.size() * 4);
     std::memcpy(host.data() + n_lv, cb->thresholds.data(), cb->thresholds.size() * 4);
@@ -769,6 +818,7 @@ static tq_status codebook_create(const tq_spec* spec, const tq_draws* draws, con
         std::memcpy(host.data() + n_lv + n_th + n_rot + n_sk, sk_mfma.data(), n_sk * 4);
     }
     if (n_mu_dev) std::memcpy(host.data() + n_lv + n_th + n_rot + 2 * n_sk, cb->mu.data(), n_mu_dev * 4);
+    if (n_grid) std::memcpy(host.data() + n_lv + n_th + n_rot + 2 * n_sk + n_mu_dev, cb->vq_grid.data(), n_grid * 4);
     if (const char* f = std::getenv("TQ_TEST_FAIL_ALLOC"); f && std::atoi(f) == 1) {
         delete cb;
         return fail(TQ_ENOMEM, "allocation failure forced by TQ_TEST_FAIL_ALLOC");
@@ -795,6 +845,7 @@ static tq_status codebook_create(const tq_spec* spec, const tq_draws* draws, con
         cb->dev.sketch_mfma = base + n_lv + n_th + n_rot + n_sk;
     }
     if (n_mu_dev) cb->dev.mu = base + n_lv + n_th + n_rot + 2 * n_sk;
+    if (n_grid) cb->dev.vq_grid = reinterpret_cast<uint32_t*>(base + n_lv + n_th + n_rot + 2 * n_sk + n_mu_dev);
     hipStream_t s = (hipStream_t)stream;
     e = hipMemcpyAsync(cb->block, host.data(), total * sizeof(float), hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);  // host staging buffer is local

@@ -22,7 +22,17 @@ struct DeviceTables {
     float* sketch = nullptr;      // [m*d]  S, row-major
     float* sketch_mfma = nullptr; // [m*d]  S as fp16 hi/lo pairs in the encode kernel's MFMA operand order
     float* mu = nullptr;          // [n_mu] mean residual magnitudes (sign correction)
+    uint32_t* vq_grid = nullptr;  // [kVqGrid^2] candidate codewords per cell (vector codebooks, N <= 64)
 };
+
+// Candidate grid of a two-coordinate vector codebook: kVqGrid^2 cells of side
+// 1 / inv_cell over |y_i| < kVqGrid / (2 inv_cell); cell (ix, iy) holds, in
+// bytes 0..3 of word iy * kVqGrid + ix, the ascending indices of the only
+// codewords that can be nearest to a point of the cell (the last repeated),
+// or 0xFF in byte 0 when more than four can be.
+constexpr int kVqGridLog = 6;
+constexpr int kVqGrid = 1 << kVqGridLog;
+constexpr int kVqGridMaxN = 64;
 
 }  // namespace tq
 
@@ -40,6 +50,9 @@ struct tq_codebook {
     // of codes 0..3, word 2b+1 of codes 4..7 (byte tables for v_perm)
     uint32_t lvl_digits[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     int lvl_shift = 0;
+    // vector codebooks (block 2, N <= 64): the encoder's candidate grid
+    std::vector<uint32_t> vq_grid;
+    float vq_inv_cell = 0.0f;
 };
 
 namespace tq {

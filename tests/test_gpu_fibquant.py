@@ -68,13 +68,18 @@ def test_vq_encode(d, bits, dtype, rope, H):
     X = g.standard_normal((B, T, H, d)).astype(np.float32)
     X[:, :, :, 3] *= np.float32(30.0)
     X[0, 4] = 0.0
+    o, gc = books(d, bits, 13)
+    if not rope:
+        # rows of the rotation: the rotated unit vector is a basis vector, so
+        # one block lies far outside the encoder's candidate grid
+        for h in range(H):
+            X[1, 5, h] = (o.pi[(7 * h + 1) % d] * 3.0).astype(np.float32)
     if dtype == "bf16":
         xb = synth.bf16_round_bits(X)
         X = synth.bf16_bits_to_f32(xb)
         x_dev = bf16_tensor(xb)
     else:
         x_dev = torch.from_numpy(X).cuda()
-    o, gc = books(d, bits, 13)
     rope_g = tq.rope_table(1e4, d, L) if rope else None
     rope_o = orope.rope_table(1e4, d, L) if rope else None
     kp = tq.Packed(gc, B * H * L)
