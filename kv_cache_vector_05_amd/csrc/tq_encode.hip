@@ -219,7 +219,10 @@ __device__ __forceinline__ void rope_stage_store(f32x4* lds, const int (&tab)[NQ
 // 1: Hadamard rotation, sign of each residual coordinate; 2: no rotation,
 // sign of each residual coordinate; 3: Hadamard rotation, nearest codeword
 // of every two-coordinate block in a vector codebook of 2^BITS codewords.
-template <int D, int BITS, int M, bool BF16, bool ROPE, int MODE>
+// GEN: general addressing (appends at per-sequence slots, page tables);
+// bulk encodes into contiguous records take the kernel without it, which
+// keeps the page-table and slot arguments out of its scalar registers.
+template <int D, int BITS, int M, bool BF16, bool ROPE, int MODE, bool GEN>
 __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
     constexpr bool SGN = MODE == 1 || MODE == 2;
     constexpr bool NOROT = MODE == 2;
@@ -341,7 +344,7 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
     // last token read the last token instead (an MFMA column only feeds its
     // own vector, and these vectors are not stored)
     auto input_offset = [&](int64_t t) -> int64_t {
-        if (p.append) {
+        if (GEN && p.append) {
             const int64_t idx = min(t * 32 + v, (int64_t)p.n_seq * p.h_kv - 1);
             const uint32_t b = p.div_h.div((uint32_t)idx);
             return (int64_t)b * p.s_seq + (int64_t)((uint32_t)idx - b * (uint32_t)p.h_kv) * p.s_head;
@@ -357,7 +360,7 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
     // cache (or behind a page-table entry outside the pool): such a vector is
     // encoded but not stored
     auto record_of = [&](int b, int hd, int64_t t) -> int64_t {
-        if (p.pages) {
+        if (GEN && p.pages) {
             if (t < 0 || t >= (int64_t)p.max_pages * p.page_size) return -1;
             const uint32_t j = p.div_page.div((uint32_t)t);
             const int32_t pg = p.pages[(int64_t)b * p.max_pages + j];
@@ -388,31 +391,50 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
       const bool prefetch = stage && base + blk_stride < p.n_tiles;
       if (tile >= p.n_tiles && prefetch) rope_stage_load<HALF, NQ>(p, base + blk_stride, st_table, st_row, st_c4, pre);
       if (tile < p.n_tiles) {
-        int head, seq;
-        int64_t slot;  // cache slot of the lane's vector
-        int rpos;      // its RoPE row (a valid table row for every lane)
-        bool valid;
-        if (p.append) {
-            const int64_t idx = tile * 32 + v;
-            const int64_t nv = (int64_t)p.n_seq * p.h_kv;
-            const uint32_t bq = p.div_h.div((uint32_t)min(idx, nv - 1));
-            seq = (int)bq;
-            head = (int)((uint32_t)min(idx, nv - 1) - bq * (uint32_t)p.h_kv);
-            slot = p.pos[seq];
-            valid = idx < nv;
-            rpos = (int)min(max(slot, (int64_t)0), (int64_t)max(p.rope_npos - 1, 0));
-        } else {
-            const uint32_t r = p.div_h.div((uint32_t)tile);
-            head = (int)((uint32_t)tile - r * (uint32_t)p.h_kv);
-            const uint32_t tbq = p.div_seq.div(r);
-            seq = (int)(r - tbq * (uint32_t)p.n_seq);
-            const int token = (int)tbq * 32 + v;
-            valid = token < p.n_tok;
-            slot = (int64_t)p.tok_offset + token;
-            rpos = p.tok_offset + (valid ? token : 0);
-        }
-        const int64_t n = record_of(seq, head, slot);
-        valid = valid && n >= 0;
+        // the lane's vector: sequence, head, cache slot, RoPE row (a valid
+        // table row for every lane) and whether it is stored.  Computed at
+        // the start for the RoPE row, and again from the lane's index at the
+        // stores, so the record address holds no registers in between.
+        struct Loc {
+            int seq, head, rpos;
+            int64_t slot;
+            bool valid;
+        };
+        auto locate = [&](int vl) -> Loc {
+            Loc L;
+            if (GEN && p.append) {
+                const int64_t idx = tile * 32 + vl;
+                const int64_t nv = (int64_t)p.n_seq * p.h_kv;
+                const uint32_t bq = p.div_h.div((uint32_t)min(idx, nv - 1));
+                L.seq = (int)bq;
+                L.head = (int)((uint32_t)min(idx, nv - 1) - bq * (uint32_t)p.h_kv);
+                L.slot = p.pos[L.seq];
+                L.valid = idx < nv;
+                L.rpos = (int)min(max(L.slot, (int64_t)0), (int64_t)max(p.rope_npos - 1, 0));
+            } else {
+                const uint32_t r = p.div_h.div((uint32_t)tile);
+                L.head = (int)((uint32_t)tile - r * (uint32_t)p.h_kv);
+                const uint32_t tbq = p.div_seq.div(r);
+                L.seq = (int)(r - tbq * (uint32_t)p.n_seq);
+                const int token = (int)tbq * 32 + vl;
+                L.valid = token < p.n_tok;
+                L.slot = (int64_t)p.tok_offset + token;
+                L.rpos = p.tok_offset + (L.valid ? token : 0);
+            }
+            return L;
+        };
+        // record index and store flag, at the stores (the lane index passes
+        // through an empty asm so that the address is recomputed there, not
+        // carried from the start)
+        auto record = [&](int64_t* n_out) -> bool {
+            int vl = v;
+            asm volatile("" : "+v"(vl));
+            const Loc L = locate(vl);
+            const int64_t rec = record_of(L.seq, L.head, L.slot);
+            *n_out = rec;
+            return L.valid && rec >= 0;
+        };
+        const int rpos = locate(v).rpos;
 
         floatx16 acc[NOB];
         float nu, scale;
@@ -708,6 +730,8 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
                 const Swap sw = swap32(__uint_as_float(cw[w]));
                 cw[w] = __float_as_uint(sw.r0) | __float_as_uint(sw.r1);
             }
+            int64_t n;
+            const bool valid = record(&n);
             if (valid) {
                 uint32_t* dst = p.codes + n * CW;
                 if constexpr (CW % 8 == 0) {
@@ -872,6 +896,8 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
                 cw[k] = __float_as_uint(a) | __float_as_uint(b);
             }
 
+            int64_t n;
+            const bool valid = record(&n);
             if (valid) {
                 uint32_t* dst = p.codes + n * CW + h * (CW / 2);
     #pragma unroll
@@ -1140,63 +1166,71 @@ int64_t dense_chunk(int64_t nvec) { return nvec < 65536 ? nvec : 65536; }
 
 using EncFn = void (*)(EncK);
 
+template <int D, int BITS, int M, int MODE, bool GEN>
+EncFn pick_dtype_g(bool bf16, bool rope) {
+    if (rope) return bf16 ? encode_had_kernel<D, BITS, M, true, true, MODE, GEN>
+                          : encode_had_kernel<D, BITS, M, false, true, MODE, GEN>;
+    return bf16 ? encode_had_kernel<D, BITS, M, true, false, MODE, GEN>
+                : encode_had_kernel<D, BITS, M, false, false, MODE, GEN>;
+}
+
+// gen: the general-addressing kernel (appends, page tables)
 template <int D, int BITS, int M, int MODE>
-EncFn pick_dtype(bool bf16, bool rope) {
-    if (rope) return bf16 ? encode_had_kernel<D, BITS, M, true, true, MODE> : encode_had_kernel<D, BITS, M, false, true, MODE>;
-    return bf16 ? encode_had_kernel<D, BITS, M, true, false, MODE> : encode_had_kernel<D, BITS, M, false, false, MODE>;
+EncFn pick_dtype(bool bf16, bool rope, bool gen) {
+    return gen ? pick_dtype_g<D, BITS, M, MODE, true>(bf16, rope) : pick_dtype_g<D, BITS, M, MODE, false>(bf16, rope);
 }
 
 template <int D, int BITS>
-EncFn pick_m(int m, bool bf16, bool rope, int mode) {
+EncFn pick_m(int m, bool bf16, bool rope, int mode, bool gen) {
     if (mode != 0) {
         if constexpr (BITS <= 3) {
             if (m != D) return nullptr;
-            return mode == 1 ? pick_dtype<D, BITS, D, 1>(bf16, rope) : pick_dtype<D, BITS, D, 2>(bf16, rope);
+            return mode == 1 ? pick_dtype<D, BITS, D, 1>(bf16, rope, gen) : pick_dtype<D, BITS, D, 2>(bf16, rope, gen);
         }
         return nullptr;
     }
-    if (m == 0) return pick_dtype<D, BITS, 0, 0>(bf16, rope);
-    if (m == D / 2) return pick_dtype<D, BITS, D / 2, 0>(bf16, rope);
-    if (m == D) return pick_dtype<D, BITS, D, 0>(bf16, rope);
+    if (m == 0) return pick_dtype<D, BITS, 0, 0>(bf16, rope, gen);
+    if (m == D / 2) return pick_dtype<D, BITS, D / 2, 0>(bf16, rope, gen);
+    if (m == D) return pick_dtype<D, BITS, D, 0>(bf16, rope, gen);
     return nullptr;
 }
 
 template <int D>
-EncFn pick_bits(int bits, int m, bool bf16, bool rope, int mode) {
+EncFn pick_bits(int bits, int m, bool bf16, bool rope, int mode, bool gen) {
     switch (bits) {
-        case 1: return pick_m<D, 1>(m, bf16, rope, mode);
-        case 2: return pick_m<D, 2>(m, bf16, rope, mode);
-        case 3: return pick_m<D, 3>(m, bf16, rope, mode);
-        case 4: return pick_m<D, 4>(m, bf16, rope, mode);
+        case 1: return pick_m<D, 1>(m, bf16, rope, mode, gen);
+        case 2: return pick_m<D, 2>(m, bf16, rope, mode, gen);
+        case 3: return pick_m<D, 3>(m, bf16, rope, mode, gen);
+        case 4: return pick_m<D, 4>(m, bf16, rope, mode, gen);
     }
     return nullptr;
 }
 
 template <int D>
-EncFn pick_vq_bits(int bits, bool bf16, bool rope) {
+EncFn pick_vq_bits(int bits, bool bf16, bool rope, bool gen) {
     switch (bits) {
-        case 1: return pick_dtype<D, 1, 0, 3>(bf16, rope);
-        case 2: return pick_dtype<D, 2, 0, 3>(bf16, rope);
-        case 3: return pick_dtype<D, 3, 0, 3>(bf16, rope);
-        case 4: return pick_dtype<D, 4, 0, 3>(bf16, rope);
-        case 5: return pick_dtype<D, 5, 0, 3>(bf16, rope);
-        case 6: return pick_dtype<D, 6, 0, 3>(bf16, rope);
-        case 7: return pick_dtype<D, 7, 0, 3>(bf16, rope);
-        case 8: return pick_dtype<D, 8, 0, 3>(bf16, rope);
+        case 1: return pick_dtype<D, 1, 0, 3>(bf16, rope, gen);
+        case 2: return pick_dtype<D, 2, 0, 3>(bf16, rope, gen);
+        case 3: return pick_dtype<D, 3, 0, 3>(bf16, rope, gen);
+        case 4: return pick_dtype<D, 4, 0, 3>(bf16, rope, gen);
+        case 5: return pick_dtype<D, 5, 0, 3>(bf16, rope, gen);
+        case 6: return pick_dtype<D, 6, 0, 3>(bf16, rope, gen);
+        case 7: return pick_dtype<D, 7, 0, 3>(bf16, rope, gen);
+        case 8: return pick_dtype<D, 8, 0, 3>(bf16, rope, gen);
     }
     return nullptr;
 }
 
 // mode: 0 QJL sketch, 1 sign correction, 2 sign correction without rotation,
 // 3 vector codebook (bits = log2 of the codebook size)
-EncFn pick_encode(int d, int bits, int m, bool bf16, bool rope, int mode) {
+EncFn pick_encode(int d, int bits, int m, bool bf16, bool rope, int mode, bool gen) {
     if (mode == 3) {
-        if (d == 64) return pick_vq_bits<64>(bits, bf16, rope);
-        if (d == 128) return pick_vq_bits<128>(bits, bf16, rope);
+        if (d == 64) return pick_vq_bits<64>(bits, bf16, rope, gen);
+        if (d == 128) return pick_vq_bits<128>(bits, bf16, rope, gen);
         return nullptr;
     }
-    if (d == 64) return pick_bits<64>(bits, m, bf16, rope, mode);
-    if (d == 128) return pick_bits<128>(bits, m, bf16, rope, mode);
+    if (d == 64) return pick_bits<64>(bits, m, bf16, rope, mode, gen);
+    if (d == 128) return pick_bits<128>(bits, m, bf16, rope, mode, gen);
     return nullptr;
 }
 
@@ -1240,7 +1274,8 @@ hipError_t launch_encode(const tq_codebook* cb, const EncodeArgs& a, hipStream_t
         const int mode = cb->spec.block >= 2                    ? 3
                          : cb->spec.correction == TQ_CORR_SIGN ? (cb->spec.rotation == TQ_ROT_NONE ? 2 : 1)
                                                                : 0;
-        EncFn fn = pick_encode(d, bits, m, a.bf16 != 0, a.rope_cos != nullptr, mode);
+        const bool gen = a.append != 0 || a.pages.table != nullptr;
+        EncFn fn = pick_encode(d, bits, m, a.bf16 != 0, a.rope_cos != nullptr, mode, gen);
         if (!fn) return hipErrorInvalidValue;
         EncK p{};
         p.x = a.x;
