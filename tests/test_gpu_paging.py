@@ -217,3 +217,41 @@ def test_contiguous_appends_and_out_of_range_slots():
         others[pos[b]] = False
         assert np.all(nrm[b][:, others] == -2.0)
     assert np.all(nrm[2:] == -2.0)
+
+
+@pytest.mark.parametrize("kind,d,dtype", [("qjl", 128, "bf16"), ("sign", 128, "bf16"), ("vq", 128, "bf16"),
+                                          ("qjl", 64, "f32"), ("vq", 64, "f32")])
+def test_appends_match_bulk_encode_bitwise(kind, d, dtype):
+    """Token-by-token appends (the general-addressing encoder) write exactly
+    the records one bulk encode (the contiguous encoder) writes: every plane
+    bit for bit, keys with RoPE and values."""
+    B, H, T, L, bits = 2, 4, 40, 64, 3
+    if kind == "vq":
+        gck = tq.Codebook(d, 4, 0, "hadamard", seed=7, block=2)
+        gcv = tq.Codebook(d, 4, 0, "hadamard", seed=8, block=2)
+    else:
+        _, gck, _, gcv = make_codebooks(kind, d, bits)
+    g = synth.rng(400 + d)
+    K = g.standard_normal((B, T, H, d)).astype(np.float32) * np.float32(2.0)
+    V = g.standard_normal((B, T, H, d)).astype(np.float32)
+    K[1, 3] = 0.0
+    if dtype == "bf16":
+        kd, vd = bf16_tensor(synth.bf16_round_bits(K)), bf16_tensor(synth.bf16_round_bits(V))
+    else:
+        kd, vd = torch.from_numpy(K).cuda(), torch.from_numpy(V).cuda()
+    rope = tq.rope_table(5e5, d, L + 1)
+    bulk_k, bulk_v = tq.Packed(gck, B * H * L), tq.Packed(gcv, B * H * L)
+    app_k, app_v = tq.Packed(gck, B * H * L), tq.Packed(gcv, B * H * L)
+    tq.encode_kv(gck, gcv, kd, vd, bulk_k, bulk_v, L_cap=L, rope=rope)
+    for t in range(T):
+        pos = torch.full((B,), t, dtype=torch.int32, device="cuda")
+        tq.append_kv(gck, gcv, kd[:, t], vd[:, t], app_k, app_v, pos, L_cap=L, rope=rope)
+    torch.cuda.synchronize()
+    written = (np.arange(B * H * L) % L) < T
+    for name, a, b in (("k", bulk_k, app_k), ("v", bulk_v, app_v)):
+        for plane, x, y in zip(("norm", "rnorm", "codes", "signs"), a.numpy(), b.numpy()):
+            x, y = np.asarray(x), np.asarray(y)
+            if x.size == 0:
+                continue
+            np.testing.assert_array_equal(x.view(np.uint32)[written], y.view(np.uint32)[written],
+                                          err_msg=f"{kind} d{d} {dtype} {name} {plane}")
