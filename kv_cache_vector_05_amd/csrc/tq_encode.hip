@@ -372,7 +372,10 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
     };
     // RoPE keys run at two waves per SIMD whatever their register count, so
     // their next tile's bf16 inputs are loaded while this tile is quantised
-    constexpr bool PREFETCH = ROPE && BF16 && D == 128 && !NOROT;
+    // (vector codebooks keep neither prefetch: their search needs the
+    // registers, and a third wave per SIMD hides the loads instead)
+    constexpr bool PREFETCH = ROPE && BF16 && D == 128 && !NOROT && !VQ;
+    constexpr bool ROW_PREFETCH = !VQ;  // next step's RoPE rows in registers during the tile
     uint4 nxt[PREFETCH ? NKB : 1];
     if constexpr (PREFETCH) {
         const int64_t t0 = base + (threadIdx.x >> 6);
@@ -388,7 +391,7 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
       // the next step's rows, in flight during this step's quantiser (loaded
       // once this tile's own input registers are free)
       f32x4 pre[NQ];
-      const bool prefetch = stage && base + blk_stride < p.n_tiles;
+      const bool prefetch = ROW_PREFETCH && stage && base + blk_stride < p.n_tiles;
       if (tile >= p.n_tiles && prefetch) rope_stage_load<HALF, NQ>(p, base + blk_stride, st_table, st_row, st_c4, pre);
       if (tile < p.n_tiles) {
         // the lane's vector: sequence, head, cache slot, RoPE row (a valid
@@ -946,7 +949,10 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
       }
       if (stage) {
           __syncthreads();  // every wave is done with the current rows
-          if (base + blk_stride < p.n_tiles) rope_stage_store<RS, NQ>(s_rope4, st_table, st_row, st_c4, pre);
+          if (base + blk_stride < p.n_tiles) {
+              if constexpr (!ROW_PREFETCH) rope_stage_load<HALF, NQ>(p, base + blk_stride, st_table, st_row, st_c4, pre);
+              rope_stage_store<RS, NQ>(s_rope4, st_table, st_row, st_c4, pre);
+          }
           __syncthreads();
       }
     }
