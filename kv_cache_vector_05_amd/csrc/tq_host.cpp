@@ -569,7 +569,6 @@ float f16_to_f32(uint16_t h) {
     return v;
 }
 
-// Builds every host table of a codebook.
 // Candidate grid of a two-coordinate codebook for the encoder's nearest-codeword
 // search (layout in tq_internal.h).  Cells cover |y_i| < 5 / sqrt(d): a
 // rotated unit vector's coordinate has standard deviation 1 / sqrt(d), so
@@ -616,6 +615,7 @@ static void vq_candidate_grid(const std::vector<float>& code, int N, int d, std:
         }
 }
 
+// Builds every host table of a codebook.
 static tq_status build_tables(const tq_spec& s, const tq_draws* dr, bool dense,
                               std::vector<float>* levels, std::vector<float>* thr,
                               std::vector<float>* rot, std::vector<float>* sk) {

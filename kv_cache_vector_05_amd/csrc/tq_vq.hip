@@ -585,7 +585,8 @@ VqLogFn pick_vq_logits(int bits, int slots) {
     return nullptr;
 }
 
-int vq_grid(int64_t waves_needed) {
+// blocks of 256 threads for a grid-stride launch needing `waves_needed` waves
+int vq_blocks(int64_t waves_needed) {
     static int cus = 0;
     if (!cus) {
         int dev = 0;
@@ -729,7 +730,7 @@ hipError_t launch_vq_decode(const tq_codebook* cb, const tq_packed& k, int64_t f
     p.count = count;
     p.out = out;
     const int vpw = 128 / d;
-    const int grid = vq_grid((count + vpw - 1) / vpw);
+    const int grid = vq_blocks((count + vpw - 1) / vpw);
     if (count == 0) return hipSuccess;
     if (d == 64) hipLaunchKernelGGL(vq_decode_kernel<64>, dim3(grid), dim3(256), 0, stream, p);
     else hipLaunchKernelGGL(vq_decode_kernel<128>, dim3(grid), dim3(256), 0, stream, p);
