@@ -375,6 +375,12 @@ tq_status tq_attn_logits(const tq_codebook* ck, const void* q, int32_t q_dtype, 
  * a TQ_CORR_SIGN value codebook takes mu_kv z^v_t as the correction term
  * (and Pi_v = I for TQ_ROT_NONE).  Key and value codebooks need the same d,
  * bits and m; TQ_CORR_SIGN codebooks are served for bits <= 3 only.
+ * Vector codebooks (FibQuant summary, sections 2.3 and 5) are served for
+ * keys and values together - block 2, Hadamard, d = 64 or 128, at most 5
+ * key index bits at d = 128 (6 at d = 64), values of any size - with
+ * out = sum_t p_t nu^v_t Pi_v^T (c_v[idx^v_t(0)], c_v[idx^v_t(1)], ...) and the
+ * logit nu^k_t <q', concatenated key codewords>; mixing scalar and vector
+ * codebooks, or more than 65535 splits of 256 keys, is TQ_EUNSUPPORTED.
  * Split over the key axis with an online softmax and a log-sum-exp merge.
  *   scale         0 means 1/sqrt(d)
  *   out           device float [B][Hq][d]; zeros where seq_len[b] == 0
@@ -391,8 +397,8 @@ tq_status tq_attn_decode(const tq_codebook* ck, const tq_codebook* cv, const voi
  * Paged forms of tq_attn_logits and tq_attn_decode: keys (and values) are
  * read through the page table; the logical capacity max_pages * page_size
  * takes the place of L_cap (logit rows are [max_pages * page_size] wide,
- * workspaces are sized with it).  Bits <= 3 Hadamard or unrotated codebooks
- * (TQ_EUNSUPPORTED otherwise).
+ * workspaces are sized with it).  Bits <= 3 Hadamard or unrotated scalar
+ * codebooks, or Hadamard vector codebooks (TQ_EUNSUPPORTED otherwise).
  */
 tq_status tq_attn_logits_paged(const tq_codebook* ck, const void* q, int32_t q_dtype, const tq_packed* k, int32_t B,
                                int32_t Hq, int32_t h_kv, const int32_t* seq_len, const tq_pages* pages,
@@ -408,8 +414,9 @@ tq_status tq_attn_decode_paged(const tq_codebook* ck, const tq_codebook* cv, con
  * tq_decode_vectors: the FibQuant decoder (FibQuant summary, section 2.3):
  * records [first, first + count) of a vector-coded tensor rebuilt as
  * out[i] = nu Pi^T (c[idx_0], c[idx_1], ...) (device float [count][d]).
- * Vector codebooks with kernels only (TQ_EUNSUPPORTED otherwise).  The fused
- * decode (tq_attn_decode) takes scalar codebooks.
+ * Vector codebooks with kernels only (TQ_EUNSUPPORTED otherwise).  Values
+ * the fused decode (tq_attn_decode) does not serve - a dense rotation, or
+ * scalar keys with vector-coded values - are rebuilt here.
  */
 tq_status tq_decode_vectors(const tq_codebook* cb, const tq_packed* packed, int64_t first, int64_t count, float* out,
                             void* stream);

@@ -1213,6 +1213,11 @@ static tq_status decode_common(const tq_codebook* ck, const tq_codebook* cv, con
         return fail(TQ_EUNSUPPORTED, "the fused decode takes vector codebooks for keys and values together (block 2, "
                                      "Hadamard, d = 64 or 128, at most 5 key index bits at d = 128 and 6 at d = 64); "
                                      "rebuild other vector-coded values with tq_decode_vectors");
+    if (vq) {
+        int nsplit = 1, split_len = 0;
+        vq_attn_plan(L_cap, &nsplit, &split_len);
+        if (nsplit > 65535) return fail(TQ_EUNSUPPORTED, "the vector-codebook decode takes at most 65535 splits of keys");
+    }
     st = check_packed(ck, k, cap_records, "k");
     if (st) return st;
     st = check_packed(cv, v, cap_records, "v");

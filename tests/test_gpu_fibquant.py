@@ -353,5 +353,8 @@ def test_vq_rejections():
         tq.attn_decode(scalar, gc, q, sp, kp, 1, 64, sl)  # scalar keys with vector-coded values
     assert ei.value.code == -2
     with pytest.raises(tq.TQError) as ei:
+        tq.attn_decode(gc, gc, q, kp, kp, 1, 256 * 65536, sl)  # more than 65535 splits of 256 keys
+    assert ei.value.code == -2
+    with pytest.raises(tq.TQError) as ei:
         tq.decode_vectors(gc, kp, first=10, count=60)
     assert ei.value.code == -1
