@@ -148,7 +148,9 @@ class Codebook:
     GPU.  Draws default to the library's seeded generator; pass sigma /
     rot_gauss / sketch (host arrays) to supply them.  correction="sign" makes
     a TurboESM-style codebook (m must equal d); levels / mu give a calibrated
-    table and per-head mean residual magnitudes (see calibrate)."""
+    table and per-head mean residual magnitudes (see calibrate).  block=2 or 3
+    makes a FibQuant vector codebook of 2^bits codewords per block of that
+    many rotated coordinates (m must be 0)."""
 
     def __init__(self, d, bits, m, rotation="auto", seed=0, sigma=None, rot_gauss=None, sketch=None,
                  correction="qjl", levels=None, mu=None, block=0):
