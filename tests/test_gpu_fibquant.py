@@ -358,3 +358,35 @@ def test_vq_rejections():
     with pytest.raises(tq.TQError) as ei:
         tq.decode_vectors(gc, kp, first=10, count=60)
     assert ei.value.code == -1
+
+
+def test_vq_lengths_above_capacity_are_clamped():
+    """A seq_len above L_cap reads L_cap keys and takes L_cap as the query's
+    position, in the logit scan and in the fused decode; a seq_len of 0
+    writes no logits and decodes to zeros."""
+    d, B, H, Hq, L = 128, 3, 2, 8, 300
+    g, (ok, gk, ek), (ov, gv, ev), rope_o = fused_case(d, 4, 5, B, H, L, 140)
+    z = np.zeros((B * H * L, 0))
+    kp = tq.Packed.from_arrays(gk, ek.norm.astype(np.float32), np.zeros(0), ek.codes, z)
+    vp = tq.Packed.from_arrays(gv, ev.norm.astype(np.float32), np.zeros(0), ev.codes, z)
+    Q = g.standard_normal((B, Hq, d)).astype(np.float32)
+    qt = torch.from_numpy(Q).cuda()
+    lens = np.array([5000, 0, 301], np.int32)
+    eff = np.minimum(lens, L)
+    sl = torch.from_numpy(lens).cuda()
+    rope_g = tq.rope_table(5e5, d, L + 1)
+    cont = lambda b, h, t: (b * H + h) * L + t
+    out = tq.attn_decode(gk, gv, qt, kp, vp, H, L, sl, rope=rope_g).cpu().numpy()
+    parity.assert_close(out, fused_reference(ok, ov, ek, ev, Q, eff, H, L, rope_o, cont), "vq clamped decode")
+    assert not np.any(out[1])
+    lg = tq.attn_logits(gk, qt, kp, H, L, sl, rope=rope_g,
+                        out=torch.full((B, Hq, L), float("nan"), device="cuda")).cpu().numpy()
+    kn = ek.norm.astype(np.float32).astype(np.float64)
+    G = Hq // H
+    for b in range(B):
+        qp, _ = estimator.prep_query(o_as_scalar(ok), Q[b], int(eff[b]), rope_o)
+        for h in range(H):
+            r = cont(b, h, np.arange(eff[b]))
+            gs = slice(h * G, (h + 1) * G)
+            parity.assert_close(lg[b, gs, :eff[b]], F.logits(ok, qp[gs], kn[r], ek.codes[r]), f"vq clamped logits b={b}")
+            assert np.all(np.isnan(lg[b, gs, eff[b]:]))

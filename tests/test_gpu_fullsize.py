@@ -21,7 +21,7 @@ import numpy as np
 import pytest
 
 import synth
-from oracle import codec, estimator, rope as orope
+from oracle import codec, estimator, fibquant as F, rng as orng, rope as orope
 
 import parity
 
@@ -129,6 +129,60 @@ def test_llama8b_turboesm_full_size():
     """The Llama-3.1-8B-shaped layer with TurboESM-style records: calibrated
     key (rotated) and value (unrotated) tables, one mu per KV head."""
     check_llama("llama8b", variant="turboesm")
+
+
+@pytest.mark.timeout(900)
+def test_llama8b_fib_full_size():
+    """The Llama-3.1-8B-shaped layer with FibQuant vector codebooks (blocks of
+    two coordinates, 16 codewords): sampled key (RoPE) and value encodes,
+    sampled logits, and whole query groups of the fused decode, from the GPU's
+    own records."""
+    from test_gpu_fibquant import compare, o_as_scalar
+    st = bench.setup_fib(torch, tq, synth)
+    bench.run_calls(st, bench.NoTimer())
+    torch.cuda.synchronize()
+    B, Hq, H, L, d, bits = (st[k] for k in ("B", "Hq", "H", "L", "d", "bits"))
+    G = Hq // H
+    K, V, Q = st["host"]
+    rope_o = orope.rope_table(st["rope_base"], d, L + 1)
+    # the codebooks' signs as the seeded codec draws them (its counter-based stream)
+    ock = F.make_vq_codebook(d, 2, 1 << bits, orng.signs(synth.K_SEED, d))
+    ocv = F.make_vq_codebook(d, 2, 1 << bits, orng.signs(synth.V_SEED, d), code=ock.code32)
+    for o, c in ((ock, st["ck"]), (ocv, st["cv"])):
+        np.testing.assert_allclose(c.export()["levels"], o.code32, rtol=0, atol=1e-7)
+    kn, _, kc, _ = st["kp"].numpy()
+    vn, _, vc, _ = st["vp"].numpy()
+    g = np.random.default_rng(4321)
+
+    # encode: sampled vectors (record n = (b*H + kh)*L + t)
+    n_enc = 256
+    b_s, kh_s = g.integers(0, B, n_enc), g.integers(0, H, n_enc)
+    t_s = np.concatenate([g.integers(0, L, n_enc - 2), [0, L - 1]])
+    n_s = (b_s * H + kh_s) * L + t_s
+    ek = F.encode(ock, synth.bf16_bits_to_f32(K[b_s, t_s, kh_s]), pos=t_s, rope=rope_o)
+    ev = F.encode(ocv, synth.bf16_bits_to_f32(V[b_s, t_s, kh_s]))
+    compare(ock, ek, kn[n_s], kc[n_s], "fib K (full size, sampled)")
+    compare(ocv, ev, vn[n_s], vc[n_s], "fib V (full size, sampled)")
+
+    # logits: sampled (b, h, t) entries, query at position L
+    qf = synth.bf16_bits_to_f32(Q)
+    qp = {b: estimator.prep_query(o_as_scalar(ock), qf[b], L, rope_o)[0] for b in range(B)}
+    lg = st["logits"].cpu().numpy()
+    b_l, h_l, t_l = g.integers(0, B, 1024), g.integers(0, Hq, 1024), g.integers(0, L, 1024)
+    n_l = (b_l * H + h_l // G) * L + t_l
+    ref = np.array([F.logits(ock, qp[b_l[i]][h_l[i]:h_l[i] + 1], kn[n_l[i]:n_l[i] + 1].astype(np.float64),
+                             kc[n_l[i]:n_l[i] + 1])[0, 0] for i in range(len(n_l))])
+    parity.assert_close(lg[b_l, h_l, t_l], ref, "fib logits (full size, sampled)")
+
+    # fused decode: whole query groups of sampled KV heads
+    out = st["out"].cpu().numpy()
+    for _ in range(2):
+        b, kh = int(g.integers(0, B)), int(g.integers(0, H))
+        idx = np.arange((b * H + kh) * L, (b * H + kh + 1) * L)
+        gs = slice(kh * G, (kh + 1) * G)
+        ref_o = F.attention(ock, ocv, qp[b][gs], kn[idx].astype(np.float64), kc[idx], vn[idx].astype(np.float64),
+                            vc[idx], 1.0 / np.sqrt(d))
+        parity.assert_close(out[b, gs], ref_o, f"fib decode b={b} kh={kh} (full size)")
 
 
 @pytest.mark.timeout(900)
