@@ -81,7 +81,7 @@ typedef int32_t tq_status;
 enum {
     TQ_OK = 0,
     TQ_EINVAL = -1,        /* bad argument (null pointer, size, stride, alignment) */
-    TQ_EUNSUPPORTED = -2,  /* valid spec this build has no kernel for */
+    TQ_EUNSUPPORTED = -2,  /* valid spec the library has no kernel for */
     TQ_ENOMEM = -3,        /* device allocation failed (codebook init only) */
     TQ_EHIP = -4           /* a HIP runtime call or kernel launch failed */
 };
