@@ -177,3 +177,18 @@ def test_paged_and_append_calls_reject_bad_arguments_without_a_gpu():
                           None) == _lib.TQ_EINVAL
     assert L.tq_append_kv(None, None, None, None, 0, 1, 1, None, None, C.c_void_p(16), None, 0, None, None, 0, None,
                           None, None) == _lib.TQ_EINVAL
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """Without the built library every call raises: the binding has no other
+    path to fall back on."""
+    import sys
+    code = ("import kv_cache_vector_05_amd as tq\n"
+            "try:\n"
+            "    tq.Codebook(64, 2, 0, 'hadamard', seed=1)\n"
+            "except ImportError as e:\n"
+            "    print('RAISED', e)\n")
+    env = dict(os.environ, TQ_LIBRARY=str(tmp_path / "absent" / "libtq.so"))
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr
+    assert "RAISED" in r.stdout and "not built" in r.stdout, r.stdout
