@@ -390,3 +390,27 @@ def test_vq_lengths_above_capacity_are_clamped():
             gs = slice(h * G, (h + 1) * G)
             parity.assert_close(lg[b, gs, :eff[b]], F.logits(ok, qp[gs], kn[r], ek.codes[r]), f"vq clamped logits b={b}")
             assert np.all(np.isnan(lg[b, gs, eff[b]:]))
+
+
+def test_vq_runs_are_deterministic():
+    """Two runs of the encoders, the scan and the fused decode over the same
+    inputs give bit-identical records, logits and outputs."""
+    d, H, Hq, L = 128, 2, 8, 3000
+    gk = books(d, 4, 31)[1]
+    gv = books(d, 5, 32)[1]
+    g = synth.rng(33)
+    K = torch.from_numpy(g.standard_normal((1, L, H, d)).astype(np.float32)).cuda()
+    V = torch.from_numpy(g.standard_normal((1, L, H, d)).astype(np.float32)).cuda()
+    Q = torch.from_numpy(g.standard_normal((1, Hq, d)).astype(np.float32)).cuda()
+    sl = torch.tensor([L], dtype=torch.int32, device="cuda")
+    rope = tq.rope_table(5e5, d, L + 1)
+    res = []
+    for _ in range(2):
+        kp, vp = tq.Packed(gk, H * L), tq.Packed(gv, H * L)
+        tq.encode_kv(gk, gv, K, V, kp, vp, L_cap=L, rope=rope)
+        lg = tq.attn_logits(gk, Q, kp, H, L, sl, rope=rope)
+        out = tq.attn_decode(gk, gv, Q, kp, vp, H, L, sl, rope=rope)
+        torch.cuda.synchronize()
+        res.append([t.cpu().numpy() for t in (kp.codes, kp.norm, vp.codes, vp.norm, lg, out)])
+    for a, b in zip(*res):
+        assert np.array_equal(a, b)
