@@ -10,9 +10,12 @@ by the angle pos * base^(-2i/d).  Angles and their cosines and sines are
 computed in float64 and stored as a float32 table [pos][d/2]; every consumer
 rotates with the float32 table values.
 
-Pinned by tests: rotation by position 0 is the identity; norms are kept;
-<R_a q, R_b k> = <q, R_{b-a} k>; RoPE then Pi keeps logits exactly while Pi
-then RoPE does not.
+Pinned by tests: the frequencies against closed-form cases of the RoFormer
+definition (Su et al., 2021: a geometric sequence from 1 rad per position down
+towards 1/base; at d = 8, base 1e4 the angles per position are exactly 1, 0.1,
+0.01 and 0.001, and pair d/4 always turns by base^(-1/2)); rotation by
+position 0 is the identity; norms are kept; <R_a q, R_b k> = <q, R_{b-a} k>;
+RoPE then Pi keeps logits exactly while Pi then RoPE does not.
 """
 from __future__ import annotations
 

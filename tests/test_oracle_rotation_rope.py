@@ -87,3 +87,27 @@ def test_rope_before_rotation_keeps_scores_rotation_before_rope_does_not():
     bad = rope.apply_rope(q @ pi.T, [pq], c, s) @ rope.apply_rope(k @ pi.T, [pk], c, s).T
     np.testing.assert_allclose(good, ref, rtol=1e-12)
     assert abs(bad - ref).item() > 1e-3
+
+
+def _angle_per_position(c, s):
+    """Angle of each pair at position 1, from the table's cos and sin."""
+    return np.arctan2(s[1].astype(np.float64), c[1].astype(np.float64))
+
+
+def test_rope_frequencies_closed_form_cases():
+    """RoFormer's frequencies are a geometric sequence starting at 1 rad per
+    position with ratio base^(-2/d).  At d = 8 and base 1e4 the angles per
+    position are exactly 1, 0.1, 0.01 and 0.001; at d = 4, base 1e4 they are
+    1 and 0.01; for any d, pair d/4 turns by base^(-1/2) (1/100 at base 1e4,
+    1/sqrt(5e5) = 1.41421356e-3 at base 5e5)."""
+    c, s = rope.rope_table(10000.0, 8, 4)
+    np.testing.assert_allclose(_angle_per_position(c, s), [1.0, 0.1, 0.01, 0.001], rtol=1e-6)
+    c, s = rope.rope_table(10000.0, 4, 4)
+    np.testing.assert_allclose(_angle_per_position(c, s), [1.0, 0.01], rtol=1e-6)
+    for base, want in ((10000.0, 0.01), (500000.0, 1.41421356e-3)):
+        c, s = rope.rope_table(base, 128, 2)
+        np.testing.assert_allclose(_angle_per_position(c, s)[32], want, rtol=1e-6)
+    # position p turns pair 0 by exactly p radians (cos(3) = -0.9899924966)
+    c, s = rope.rope_table(500000.0, 128, 8)
+    assert abs(float(c[3, 0]) - (-0.9899924966)) < 1e-7
+    assert abs(float(s[3, 0]) - 0.1411200081) < 1e-7
