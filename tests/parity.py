@@ -65,3 +65,33 @@ def assert_close(gpu, ref, label=""):
         i = np.unravel_index(np.argmax(err - lim), err.shape)
         raise AssertionError(f"{label}: {bad.sum()} of {bad.size} outside tolerance; worst at {i}: "
                              f"gpu {gpu[i]!r} ref {ref[i]!r}")
+
+
+def check_topk(vals, idx, ref_scores, k, label=""):
+    """A GPU top-k against the oracle's scores of the same rows.
+
+    vals, idx: [rows, k] from the GPU; ref_scores: [rows, n] oracle scores of
+    every candidate.  Per row: the min(k, n) leading indices are distinct and
+    in range, the values descend (equal values by ascending index), each value
+    matches the oracle's score at its index, and each returned index scores no
+    worse than the oracle's k-th best less the tolerance (near-ties at the
+    cut may pick either key, and both answers are correct).  Slots past n
+    hold index -1 and value -inf."""
+    vals = np.asarray(vals)
+    idx = np.asarray(idx)
+    ref_scores = np.asarray(ref_scores, np.float64)
+    n = ref_scores.shape[1]
+    kk = min(k, n)
+    for g in range(len(vals)):
+        ii = idx[g, :kk]
+        assert len(set(ii.tolist())) == kk, f"{label} row {g}: repeated indices {ii}"
+        assert ii.min() >= 0 and ii.max() < n, f"{label} row {g}: index out of range {ii}"
+        v = vals[g, :kk]
+        assert np.all(np.diff(v) <= 0), f"{label} row {g}: values not descending {v}"
+        tie = np.diff(v) == 0
+        assert np.all(np.diff(ii)[tie] > 0), f"{label} row {g}: equal values not in index order"
+        assert_close(v, ref_scores[g, ii], f"{label} top-k values row {g}")
+        kth = np.partition(ref_scores[g], n - kk)[n - kk]
+        assert np.all(ref_scores[g, ii] >= kth - (ATOL + RTOL * abs(kth))), f"{label} row {g}: below the k-th best"
+        if kk < k:
+            assert np.all(idx[g, kk:] == -1) and np.all(np.isneginf(vals[g, kk:])), f"{label} row {g}: padding"

@@ -9,9 +9,10 @@ on a seeded sample it can compute one by one:
   records (both sides read the same cache);
 * decode: whole query groups of sampled KV heads, over every record of the
   head;
-* top-10 (vector search): returned scores equal the oracle's scores of the
-  returned rows, and no sampled other row beats the 10th score by more than
-  the tolerance.
+* top-10 (vector search): for 32 sampled queries the oracle scores all 10^6
+  rows from the GPU's records, and the returned sets are checked completely
+  (distinct, descending, scores equal to the oracle's, none below the
+  oracle's 10th best less the tolerance).
 """
 import math
 import os
@@ -237,15 +238,15 @@ def test_vector_search_full_size():
     rows_i = np.concatenate([ra, rb])
     X = np.concatenate([first[ra], last[rb - last0]])
     parity.compare_encoded(ock, codec.encode(ock, X), pick(planes, rows_i), "vsearch index (sampled)")
-    # top-10 of sampled queries
-    others = g.choice(n, 20000, replace=False)
-    for qi in g.choice(st["nq"], 6, replace=False):
-        qp, s = estimator.prep_query(ock, st["Qh"][qi:qi + 1])
-        assert len(set(idx[qi].tolist())) == 10 and np.all(np.diff(vals[qi]) <= 0)
-        ref_top = estimator.logits(ock, qp, s, records(planes, idx[qi]))[0]
-        parity.assert_close(vals[qi], ref_top, f"vsearch top-10 values, query {qi}")
-        ref_oth = estimator.logits(ock, qp, s, records(planes, others))[0]
-        kth = vals[qi, -1]
-        mask = ~np.isin(others, idx[qi])
-        assert np.all(ref_oth[mask] <= kth + parity.ATOL + parity.RTOL * abs(kth)), \
-            f"vsearch query {qi}: a sampled row beats the returned 10th score"
+    # top-10 of 32 sampled queries against every one of the 10^6 rows: the
+    # oracle scores the GPU's records chunk by chunk (any record decodes on
+    # its own), so the returned sets are checked completely
+    qs = np.sort(g.choice(st["nq"], 32, replace=False))
+    qp, s = estimator.prep_query(ock, st["Qh"][qs])
+    ref = np.empty((len(qs), n))
+    step = 65536
+    for r0 in range(0, n, step):
+        rr = np.arange(r0, min(n, r0 + step))
+        ref[:, rr] = estimator.logits(ock, qp, s, records(planes, rr))
+        print(f"vsearch oracle scores: rows {rr[-1] + 1} of {n}", flush=True)
+    parity.check_topk(vals[qs], idx[qs], ref, 10, "vsearch top-10")
