@@ -363,6 +363,8 @@ def setup_serve(torch, tq, synth):
     tq.encode_kv(st["ck"], st["cv"], Kd[:, :L - 1], Vd[:, :L - 1], st["kp"], st["vp"], rope=st["rope"],
                  pages=st["pages"])
     st["K1"], st["V1"] = Kd[:, L - 1].contiguous(), Vd[:, L - 1].contiguous()
+    # the new token sits at slot L - 1: its query attends to slots 0..L-1 at
+    # position L - 1, like its own key
     st["pos"] = torch.full((B,), L - 1, dtype=torch.int32, device="cuda")
     st["sl"] = torch.full((B,), L, dtype=torch.int32, device="cuda")
     st["Q"] = bf16_dev(torch, Q)
@@ -373,7 +375,8 @@ def setup_serve(torch, tq, synth):
         ("append", tq.append_kv(st["ck"], st["cv"], st["K1"], st["V1"], st["kp"], st["vp"], st["pos"],
                                 pages=st["pages"], rope=st["rope"], prepare=True)),
         ("decode", tq.attn_decode(st["ck"], st["cv"], st["Q"], st["kp"], st["vp"], H, None, st["sl"], rope=st["rope"],
-                                  out=st["out"], workspace=st["ws_d"], prepare=True, pages=st["pages"])[0]),
+                                  out=st["out"], workspace=st["ws_d"], prepare=True, pages=st["pages"],
+                                  q_pos=st["pos"])[0]),
     ]
     return st
 
@@ -426,7 +429,7 @@ def cpu_baseline_serve(st, budget_s=8.0):
             nv = codec.encode(ocv, vx[L - 1:])
             cat = lambda e, n: codec.Encoded(np.concatenate([e.norm, n.norm]), np.concatenate([e.rnorm, n.rnorm]),
                                              np.concatenate([e.codes, n.codes]), np.concatenate([e.signs, n.signs]))
-            qp, s = estimator.prep_query(ock, q, L, rope)
+            qp, s = estimator.prep_query(ock, q, L - 1, rope)
             estimator.attention(ock, ocv, qp, s, cat(ek, nk), cat(ev, nv), L, 1 / math.sqrt(d))
             dt += time.perf_counter() - t1
             done += L

@@ -349,8 +349,13 @@ tq_status tq_append_kv(const tq_codebook* ck, const tq_codebook* cv, const void*
  *   k             packed keys, capacity >= B*h_kv*L_cap
  *   B, Hq, h_kv   Hq a multiple of h_kv; query head h reads KV head h/(Hq/h_kv)
  *   seq_len       device int32 [B]; keys t < seq_len[b] are scored (values
- *                 above L_cap are clamped to L_cap); also the query's RoPE
- *                 position
+ *                 above L_cap are clamped to L_cap)
+ *   q_pos         device int32 [B]: the RoPE position of sequence b's query,
+ *                 or NULL for seq_len[b] (a query whose own key is not yet in
+ *                 the cache).  A decode step that appended its token's key at
+ *                 slot p before scoring passes q_pos = p with seq_len = p + 1,
+ *                 so that the query and its own key share a position.
+ *                 Clamped to [0, L_cap] like seq_len.
  *   rope_*        as tq_encode_kv (rope_npos > L_cap) or NULL
  *   top_k = 0     out = device float [B][Hq][L_cap]; entries t >= seq_len[b]
  *                 are left untouched
@@ -362,7 +367,7 @@ tq_status tq_append_kv(const tq_codebook* ck, const tq_codebook* cv, const void*
  */
 tq_status tq_attn_logits(const tq_codebook* ck, const void* q, int32_t q_dtype, const tq_packed* k,
                          int32_t B, int32_t Hq, int32_t h_kv, int32_t L_cap, const int32_t* seq_len,
-                         const float* rope_cos, const float* rope_sin, int32_t rope_npos,
+                         const int32_t* q_pos, const float* rope_cos, const float* rope_sin, int32_t rope_npos,
                          int32_t top_k, float* out, int32_t* topk_idx, void* ws, size_t ws_bytes,
                          void* stream);
 
@@ -373,8 +378,9 @@ tq_status tq_attn_logits(const tq_codebook* ck, const void* q, int32_t q_dtype, 
  *   out[b][h] = sum_t p_t nu^v_t Pi_v^T (t_v[c^v_t] + sqrt(pi/2)/m_v gamma^v_t S_v^T z^v_t),
  *   p = softmax over t < seq_len[b] of scale * logit[b][h][t];
  * a TQ_CORR_SIGN value codebook takes mu_kv z^v_t as the correction term
- * (and Pi_v = I for TQ_ROT_NONE).  Key and value codebooks need the same d,
- * bits and m; TQ_CORR_SIGN codebooks are served for bits <= 3 only.
+ * (and Pi_v = I for TQ_ROT_NONE).  Scalar key and value codebooks need the
+ * same d, bits and m and a Hadamard or no rotation (TQ_EUNSUPPORTED before
+ * any launch otherwise); TQ_CORR_SIGN codebooks are served for bits <= 3 only.
  * Vector codebooks (FibQuant summary, sections 2.3 and 5) are served for
  * keys and values together - block 2, Hadamard, d = 64 or 128, at most 5
  * key index bits at d = 128 (6 at d = 64), values of any size - with
@@ -389,7 +395,7 @@ tq_status tq_attn_logits(const tq_codebook* ck, const void* q, int32_t q_dtype, 
  */
 tq_status tq_attn_decode(const tq_codebook* ck, const tq_codebook* cv, const void* q, int32_t q_dtype,
                          const tq_packed* k, const tq_packed* v, int32_t B, int32_t Hq, int32_t h_kv,
-                         int32_t L_cap, const int32_t* seq_len, const float* rope_cos,
+                         int32_t L_cap, const int32_t* seq_len, const int32_t* q_pos, const float* rope_cos,
                          const float* rope_sin, int32_t rope_npos, float scale, float* out,
                          void* ws, size_t ws_bytes, void* stream);
 
@@ -401,14 +407,14 @@ tq_status tq_attn_decode(const tq_codebook* ck, const tq_codebook* cv, const voi
  * codebooks, or Hadamard vector codebooks (TQ_EUNSUPPORTED otherwise).
  */
 tq_status tq_attn_logits_paged(const tq_codebook* ck, const void* q, int32_t q_dtype, const tq_packed* k, int32_t B,
-                               int32_t Hq, int32_t h_kv, const int32_t* seq_len, const tq_pages* pages,
-                               const float* rope_cos, const float* rope_sin, int32_t rope_npos, int32_t top_k,
-                               float* out, int32_t* topk_idx, void* ws, size_t ws_bytes, void* stream);
+                               int32_t Hq, int32_t h_kv, const int32_t* seq_len, const int32_t* q_pos,
+                               const tq_pages* pages, const float* rope_cos, const float* rope_sin, int32_t rope_npos,
+                               int32_t top_k, float* out, int32_t* topk_idx, void* ws, size_t ws_bytes, void* stream);
 tq_status tq_attn_decode_paged(const tq_codebook* ck, const tq_codebook* cv, const void* q, int32_t q_dtype,
                                const tq_packed* k, const tq_packed* v, int32_t B, int32_t Hq, int32_t h_kv,
-                               const int32_t* seq_len, const tq_pages* pages, const float* rope_cos,
-                               const float* rope_sin, int32_t rope_npos, float scale, float* out, void* ws,
-                               size_t ws_bytes, void* stream);
+                               const int32_t* seq_len, const int32_t* q_pos, const tq_pages* pages,
+                               const float* rope_cos, const float* rope_sin, int32_t rope_npos, float scale,
+                               float* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * tq_decode_vectors: the FibQuant decoder (FibQuant summary, section 2.3):

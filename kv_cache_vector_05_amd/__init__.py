@@ -411,10 +411,11 @@ def append_kv(ck, cv, k, v, kout, vout, pos, pages=None, L_cap=None, rope=None, 
 
 
 def attn_logits(ck, q, kp, h_kv, L_cap, seq_len, rope=None, top_k=0, out=None, workspace=None, prepare=False,
-                pages=None):
+                pages=None, q_pos=None):
     """Logits [B, Hq, L_cap] (top_k = 0) or (values, indices) [B, Hq, top_k]
     for queries q [B, Hq, d] against packed keys.  seq_len: int32 [B] on the
-    GPU.  With pages (a Pages), keys are read through the page table and
+    GPU; q_pos: int32 [B] on the GPU, the queries' RoPE positions (None:
+    seq_len).  With pages (a Pages), keys are read through the page table and
     L_cap is its capacity.  prepare=True returns (Launch, outputs) without
     running."""
     torch = _torch()
@@ -436,21 +437,22 @@ def attn_logits(ck, q, kp, h_kv, L_cap, seq_len, rope=None, top_k=0, out=None, w
     kst = kp.struct()
     if pages is not None:
         pst = pages.struct()
-        args = [ck.handle, _ptr(q), _dtype_code(q), C.byref(kst), B, Hq, int(h_kv), _ptr(seq_len), C.byref(pst),
-                _ptr(cos), _ptr(sin), npos, int(top_k), _ptr(out), _ptr(idx), _ptr(ws), wsb, _stream()]
+        args = [ck.handle, _ptr(q), _dtype_code(q), C.byref(kst), B, Hq, int(h_kv), _ptr(seq_len), _ptr(q_pos),
+                C.byref(pst), _ptr(cos), _ptr(sin), npos, int(top_k), _ptr(out), _ptr(idx), _ptr(ws), wsb, _stream()]
         launch = _run(lib().tq_attn_logits_paged, args, (kst, pst, ws, out, idx), prepare)
     else:
         args = [ck.handle, _ptr(q), _dtype_code(q), C.byref(kst), B, Hq, int(h_kv), int(L_cap), _ptr(seq_len),
-                _ptr(cos), _ptr(sin), npos, int(top_k), _ptr(out), _ptr(idx), _ptr(ws), wsb, _stream()]
+                _ptr(q_pos), _ptr(cos), _ptr(sin), npos, int(top_k), _ptr(out), _ptr(idx), _ptr(ws), wsb, _stream()]
         launch = _run(lib().tq_attn_logits, args, (kst, ws, out, idx), prepare)
     res = (out, idx) if top_k else out
     return (launch, res) if prepare else res
 
 
 def attn_decode(ck, cv, q, kp, vp, h_kv, L_cap, seq_len, rope=None, scale=0.0, out=None, workspace=None,
-                prepare=False, pages=None):
+                prepare=False, pages=None, q_pos=None):
     """Decode attention output [B, Hq, d] float32 over packed K and V (read
     through the page table when pages is given; L_cap is then its capacity).
+    q_pos: the queries' RoPE positions (int32 [B] on the GPU; None: seq_len).
     prepare=True returns (Launch, out) without running."""
     torch = _torch()
     B, Hq, d = q.shape
@@ -468,12 +470,12 @@ def attn_decode(ck, cv, q, kp, vp, h_kv, L_cap, seq_len, rope=None, scale=0.0, o
     if pages is not None:
         pst = pages.struct()
         args = [ck.handle, cv.handle, _ptr(q), _dtype_code(q), C.byref(kst), C.byref(vst), B, Hq, int(h_kv),
-                _ptr(seq_len), C.byref(pst), _ptr(cos), _ptr(sin), npos, float(scale), _ptr(out), _ptr(ws), wsb,
-                _stream()]
+                _ptr(seq_len), _ptr(q_pos), C.byref(pst), _ptr(cos), _ptr(sin), npos, float(scale), _ptr(out),
+                _ptr(ws), wsb, _stream()]
         launch = _run(lib().tq_attn_decode_paged, args, (kst, vst, pst, ws, out), prepare)
     else:
         args = [ck.handle, cv.handle, _ptr(q), _dtype_code(q), C.byref(kst), C.byref(vst), B, Hq, int(h_kv),
-                int(L_cap), _ptr(seq_len), _ptr(cos), _ptr(sin), npos, float(scale), _ptr(out), _ptr(ws), wsb,
-                _stream()]
+                int(L_cap), _ptr(seq_len), _ptr(q_pos), _ptr(cos), _ptr(sin), npos, float(scale), _ptr(out),
+                _ptr(ws), wsb, _stream()]
         launch = _run(lib().tq_attn_decode, args, (kst, vst, ws, out), prepare)
     return (launch, out) if prepare else out

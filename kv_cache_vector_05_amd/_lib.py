@@ -64,20 +64,20 @@ SIGNATURES = {
                                  C.c_int32, C.c_void_p, C.c_void_p, C.c_int32, C.POINTER(tq_packed),
                                  C.POINTER(tq_packed), C.c_void_p]),
     "tq_attn_logits_paged": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_int32, C.POINTER(tq_packed), C.c_int32,
-                                         C.c_int32, C.c_int32, C.c_void_p, C.POINTER(tq_pages), C.c_void_p,
+                                         C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.POINTER(tq_pages), C.c_void_p,
                                          C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
                                          C.c_size_t, C.c_void_p]),
     "tq_attn_decode_paged": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.POINTER(tq_packed),
                                          C.POINTER(tq_packed), C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
-                                         C.POINTER(tq_pages), C.c_void_p, C.c_void_p, C.c_int32, C.c_float,
+                                         C.c_void_p, C.POINTER(tq_pages), C.c_void_p, C.c_void_p, C.c_int32, C.c_float,
                                          C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "tq_attn_logits": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_int32, C.POINTER(tq_packed), C.c_int32,
-                                   C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
+                                   C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                    C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
                                    C.c_void_p]),
     "tq_attn_decode": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.POINTER(tq_packed),
                                    C.POINTER(tq_packed), C.c_int32, C.c_int32, C.c_int32, C.c_int32,
-                                   C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_float, C.c_void_p,
+                                   C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_float, C.c_void_p,
                                    C.c_void_p, C.c_size_t, C.c_void_p]),
     "tq_workspace_bytes": (C.c_size_t, [C.c_void_p, C.c_void_p, C.c_int32, C.c_int64, C.c_int32, C.c_int32,
                                         C.c_int32, C.c_int32]),

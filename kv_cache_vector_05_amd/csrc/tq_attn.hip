@@ -60,6 +60,7 @@ struct QPrep {
     const void* q;
     int32_t bf16, Hq, L_cap, d, m;
     const int32_t* seq_len;
+    const int32_t* q_pos;
     const float* rope_cos;
     const float* rope_sin;
     const float* sigma;
@@ -78,7 +79,7 @@ __global__ __launch_bounds__(256) void qprep_rht_kernel(QPrep p) {
     if (t < D) xs[t] = load_q(p.q, p.bf16, bh * D + t);
     __syncthreads();
     if (p.rope_cos) {
-        const int pos = clamp_len(p.seq_len, b, p.L_cap);
+        const int pos = dev::query_pos(p.q_pos, p.seq_len, b, p.L_cap);
         float lo = 0.f, hi = 0.f;
         if (t < D / 2) {
             const float c = p.rope_cos[(int64_t)pos * (D / 2) + t];
@@ -128,7 +129,7 @@ __global__ __launch_bounds__(256) void qrope_kernel(QPrep p, float* out) {
         float a = load_q(p.q, p.bf16, bh * p.d + i);
         float bb = load_q(p.q, p.bf16, bh * p.d + i + half);
         if (p.rope_cos) {
-            const int pos = clamp_len(p.seq_len, b, p.L_cap);
+            const int pos = dev::query_pos(p.q_pos, p.seq_len, b, p.L_cap);
             const float c = p.rope_cos[(int64_t)pos * half + i];
             const float sn = p.rope_sin[(int64_t)pos * half + i];
             const float a2 = a * c - bb * sn;
@@ -805,6 +806,7 @@ QPrep make_qprep(const tq_codebook* ck, const AttnArgs& a, float* qp, float* s) 
     q.d = ck->spec.d;
     q.m = ck->spec.m;
     q.seq_len = a.seq_len;
+    q.q_pos = a.q_pos;
     q.rope_cos = a.rope_cos;
     q.rope_sin = a.rope_sin;
     q.sigma = ck->dev.sigma;

@@ -29,6 +29,13 @@ __device__ __forceinline__ int clamp_len(const int32_t* seq_len, int b, int L_ca
     return s < 0 ? 0 : (s > L_cap ? L_cap : s);
 }
 
+// RoPE position of sequence b's query: q_pos[b] when a position array is
+// given, else seq_len[b] (the token after the cached ones); clamped to [0, L_cap]
+__device__ __forceinline__ int query_pos(const int32_t* q_pos, const int32_t* seq_len, int b, int L_cap) {
+    int s = q_pos ? q_pos[b] : seq_len[b];
+    return s < 0 ? 0 : (s > L_cap ? L_cap : s);
+}
+
 // Division by a run-time constant d >= 1 for dividends below 2^31, by a
 // multiply-high and a shift (Granlund and Montgomery, PLDI 1994): with
 // s = ceil(log2 d) and m = floor(2^32 (2^s - d) / d) + 1,

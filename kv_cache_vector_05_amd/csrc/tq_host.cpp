@@ -1156,9 +1156,9 @@ static tq_status check_attn(const tq_codebook* ck, const void* q, int32_t q_dtyp
 }
 
 static tq_status logits_common(const tq_codebook* ck, const void* q, int32_t q_dtype, const tq_packed* k, int32_t B,
-                               int32_t Hq, int32_t h_kv, int32_t L_cap, const int32_t* seq_len, const PageRef& pg,
-                               int64_t cap_records, const float* rope_cos, const float* rope_sin, int32_t rope_npos,
-                               int32_t top_k, float* out, int32_t* topk_idx, void* ws, size_t ws_bytes, void* stream) {
+                               int32_t Hq, int32_t h_kv, int32_t L_cap, const int32_t* seq_len, const int32_t* q_pos,
+                               const PageRef& pg, int64_t cap_records, const float* rope_cos, const float* rope_sin,
+                               int32_t rope_npos, int32_t top_k, float* out, int32_t* topk_idx, void* ws, size_t ws_bytes, void* stream) {
     tq_status st = check_attn(ck, q, q_dtype, B, Hq, h_kv, L_cap, seq_len, rope_cos, rope_sin, rope_npos);
     if (st) return st;
     if (top_k < 0 || top_k > 16) return fail(TQ_EINVAL, "top_k must be 0..16");
@@ -1185,6 +1185,7 @@ static tq_status logits_common(const tq_codebook* ck, const void* q, int32_t q_d
     a.h_kv = h_kv;
     a.L_cap = L_cap;
     a.seq_len = seq_len;
+    a.q_pos = q_pos;
     a.rope_cos = rope_cos;
     a.rope_sin = rope_sin;
     a.top_k = top_k;
@@ -1199,8 +1200,9 @@ static tq_status logits_common(const tq_codebook* ck, const void* q, int32_t q_d
 
 static tq_status decode_common(const tq_codebook* ck, const tq_codebook* cv, const void* q, int32_t q_dtype,
                                const tq_packed* k, const tq_packed* v, int32_t B, int32_t Hq, int32_t h_kv,
-                               int32_t L_cap, const int32_t* seq_len, const PageRef& pg, int64_t cap_records,
-                               const float* rope_cos, const float* rope_sin, int32_t rope_npos, float scale,
+                               int32_t L_cap, const int32_t* seq_len, const int32_t* q_pos, const PageRef& pg,
+                               int64_t cap_records, const float* rope_cos, const float* rope_sin, int32_t rope_npos,
+                               float scale,
                                float* out, void* ws, size_t ws_bytes, void* stream) {
     tq_status st = check_attn(ck, q, q_dtype, B, Hq, h_kv, L_cap, seq_len, rope_cos, rope_sin, rope_npos);
     if (st) return st;
@@ -1226,6 +1228,11 @@ static tq_status decode_common(const tq_codebook* ck, const tq_codebook* cv, con
     if (st) return st;
     st = check_mu(cv, h_kv);
     if (st) return st;
+    if (!vq && (ck->dense || cv->dense))
+        return fail(TQ_EUNSUPPORTED, "the fused decode serves Hadamard or unrotated scalar codebooks; a dense "
+                                     "rotation is served by tq_attn_logits only");
+    if (!vq && (ck->spec.bits != cv->spec.bits || ck->spec.m != cv->spec.m))
+        return fail(TQ_EUNSUPPORTED, "the fused decode needs key and value codebooks of equal bits and m");
     if (!vq && (sign_corr(ck) || sign_corr(cv) || pg.table) && !decode_mfma_supported(ck, cv))
         return fail(TQ_EUNSUPPORTED, "paged and sign-corrected decodes need key and value tables of equal d, bits "
                                      "and m (bits <= 3)");
@@ -1240,6 +1247,7 @@ static tq_status decode_common(const tq_codebook* ck, const tq_codebook* cv, con
     a.h_kv = h_kv;
     a.L_cap = L_cap;
     a.seq_len = seq_len;
+    a.q_pos = q_pos;
     a.rope_cos = rope_cos;
     a.rope_sin = rope_sin;
     a.scale = scale > 0 ? scale : 1.0f / std::sqrt((float)ck->spec.d);
@@ -1303,43 +1311,44 @@ tq_status tq_append_kv(const tq_codebook* ck, const tq_codebook* cv, const void*
 
 tq_status tq_attn_logits(const tq_codebook* ck, const void* q, int32_t q_dtype, const tq_packed* k,
                          int32_t B, int32_t Hq, int32_t h_kv, int32_t L_cap, const int32_t* seq_len,
-                         const float* rope_cos, const float* rope_sin, int32_t rope_npos,
+                         const int32_t* q_pos, const float* rope_cos, const float* rope_sin, int32_t rope_npos,
                          int32_t top_k, float* out, int32_t* topk_idx, void* ws, size_t ws_bytes,
                          void* stream) {
-    return logits_common(ck, q, q_dtype, k, B, Hq, h_kv, L_cap, seq_len, PageRef{}, (int64_t)B * h_kv * L_cap,
+    return logits_common(ck, q, q_dtype, k, B, Hq, h_kv, L_cap, seq_len, q_pos, PageRef{}, (int64_t)B * h_kv * L_cap,
                          rope_cos, rope_sin, rope_npos, top_k, out, topk_idx, ws, ws_bytes, stream);
 }
 
 tq_status tq_attn_logits_paged(const tq_codebook* ck, const void* q, int32_t q_dtype, const tq_packed* k, int32_t B,
-                               int32_t Hq, int32_t h_kv, const int32_t* seq_len, const tq_pages* pages,
-                               const float* rope_cos, const float* rope_sin, int32_t rope_npos, int32_t top_k,
-                               float* out, int32_t* topk_idx, void* ws, size_t ws_bytes, void* stream) {
+                               int32_t Hq, int32_t h_kv, const int32_t* seq_len, const int32_t* q_pos,
+                               const tq_pages* pages, const float* rope_cos, const float* rope_sin, int32_t rope_npos,
+                               int32_t top_k, float* out, int32_t* topk_idx, void* ws, size_t ws_bytes, void* stream) {
     PageRef pg;
     tq_status st = check_pages(pages, &pg);
     if (st) return st;
-    return logits_common(ck, q, q_dtype, k, B, Hq, h_kv, pg.max_pages * pg.size, seq_len, pg,
+    return logits_common(ck, q, q_dtype, k, B, Hq, h_kv, pg.max_pages * pg.size, seq_len, q_pos, pg,
                          pg.n_pages * h_kv * (int64_t)pg.size, rope_cos, rope_sin, rope_npos, top_k, out, topk_idx, ws,
                          ws_bytes, stream);
 }
 
 tq_status tq_attn_decode(const tq_codebook* ck, const tq_codebook* cv, const void* q, int32_t q_dtype,
                          const tq_packed* k, const tq_packed* v, int32_t B, int32_t Hq, int32_t h_kv,
-                         int32_t L_cap, const int32_t* seq_len, const float* rope_cos,
+                         int32_t L_cap, const int32_t* seq_len, const int32_t* q_pos, const float* rope_cos,
                          const float* rope_sin, int32_t rope_npos, float scale, float* out,
                          void* ws, size_t ws_bytes, void* stream) {
-    return decode_common(ck, cv, q, q_dtype, k, v, B, Hq, h_kv, L_cap, seq_len, PageRef{}, (int64_t)B * h_kv * L_cap,
+    return decode_common(ck, cv, q, q_dtype, k, v, B, Hq, h_kv, L_cap, seq_len, q_pos, PageRef{},
+                         (int64_t)B * h_kv * L_cap,
                          rope_cos, rope_sin, rope_npos, scale, out, ws, ws_bytes, stream);
 }
 
 tq_status tq_attn_decode_paged(const tq_codebook* ck, const tq_codebook* cv, const void* q, int32_t q_dtype,
                                const tq_packed* k, const tq_packed* v, int32_t B, int32_t Hq, int32_t h_kv,
-                               const int32_t* seq_len, const tq_pages* pages, const float* rope_cos,
-                               const float* rope_sin, int32_t rope_npos, float scale, float* out, void* ws,
-                               size_t ws_bytes, void* stream) {
+                               const int32_t* seq_len, const int32_t* q_pos, const tq_pages* pages,
+                               const float* rope_cos, const float* rope_sin, int32_t rope_npos, float scale,
+                               float* out, void* ws, size_t ws_bytes, void* stream) {
     PageRef pg;
     tq_status st = check_pages(pages, &pg);
     if (st) return st;
-    return decode_common(ck, cv, q, q_dtype, k, v, B, Hq, h_kv, pg.max_pages * pg.size, seq_len, pg,
+    return decode_common(ck, cv, q, q_dtype, k, v, B, Hq, h_kv, pg.max_pages * pg.size, seq_len, q_pos, pg,
                          pg.n_pages * h_kv * (int64_t)pg.size, rope_cos, rope_sin, rope_npos, scale, out, ws, ws_bytes,
                          stream);
 }

@@ -129,6 +129,7 @@ struct AttnArgs {
     int32_t bf16;
     int32_t B, Hq, h_kv, L_cap;
     const int32_t* seq_len;
+    const int32_t* q_pos;  // RoPE position of each sequence's query (nullptr: seq_len)
     const float* rope_cos;
     const float* rope_sin;
     float scale;

@@ -83,6 +83,7 @@ struct QDig {
     int32_t norot;    // Pi = I: q' = RoPE(q)
     int32_t s_ident;  // S = I (sign correction): s = q'
     const int32_t* seq_len;
+    const int32_t* q_pos;
     const float* rope_cos;
     const float* rope_sin;
     const float* sigma;
@@ -110,7 +111,7 @@ __global__ __launch_bounds__(256) void qprep_digits_kernel(QDig p) {
     }
     __syncthreads();
     if (p.rope_cos) {
-        const int pos = clamp_len2(p.seq_len, b, p.L_cap);
+        const int pos = dev::query_pos(p.q_pos, p.seq_len, b, p.L_cap);
         float lo = 0.f, hi = 0.f;
         if (t < D / 2) {
             const float c = p.rope_cos[(int64_t)pos * (D / 2) + t];
@@ -436,6 +437,7 @@ hipError_t launch_qdigits(const tq_codebook* ck, const AttnArgs& a, const QDigit
     p.sdw = q.sdw;
     p.ncs = q.ncs;
     p.seq_len = a.seq_len;
+    p.q_pos = a.q_pos;
     p.rope_cos = a.rope_cos;
     p.rope_sin = a.rope_sin;
     p.sigma = ck->dev.sigma;

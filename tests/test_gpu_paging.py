@@ -159,13 +159,17 @@ def test_autoregressive_appends_through_pages(kind):
             paging.append(ock, kpool, kf[b:b + 1], pos[b:b + 1], lambda bb, h, t: index_of(bb + b, h, t), rope=rope_o)
             paging.append(ocv, vpool, vf[b:b + 1], pos[b:b + 1], lambda bb, h, t: index_of(bb + b, h, t))
         if (s + 1) % 30 == 0:
+            # the step's token was appended at slot pos: its query attends to
+            # slots 0..pos and sits at position pos, like its own key
             lens = np.maximum(pos + 1, 0)
+            qpos = np.maximum(pos, 0).astype(np.int32)
             out = tq.attn_decode(gck, gcv, torch.from_numpy(Q).cuda(), kp, vp, H, None,
-                                 torch.from_numpy(lens.astype(np.int32)).cuda(), rope=rope_g, pages=pg).cpu().numpy()
+                                 torch.from_numpy(lens.astype(np.int32)).cuda(), rope=rope_g, pages=pg,
+                                 q_pos=torch.from_numpy(qpos).cuda()).cpu().numpy()
             # the decode reads the GPU's own records; compare with the oracle over them
             gk, gv = kp.numpy(), vp.numpy()
             for b in range(B):
-                qp, sq = estimator.prep_query(ock, Q[b], int(lens[b]), rope_o)
+                qp, sq = estimator.prep_query(ock, Q[b], int(qpos[b]), rope_o)
                 for h in range(H):
                     idx = index_of(b, h, np.arange(lens[b]))
                     ek = codec.Encoded(gk[0][idx].astype(np.float64), gk[1][idx].astype(np.float64) if len(gk[1]) else

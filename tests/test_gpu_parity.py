@@ -321,6 +321,17 @@ def test_api_rejects_bad_calls_on_gpu():
         tq.encode_kv(gck, None, torch.zeros((1, 64, 1, d), device="cuda"), None, kp, None, tok_offset=10, L_cap=64)
     # empty input is a no-op
     tq.encode_kv(gck, None, torch.zeros((1, 0, 1, d), device="cuda"), None, kp, None, L_cap=64)
+    # the fused decode needs equal bits and m for keys and values, and no
+    # dense rotation: refused before any launch with TQ_EUNSUPPORTED
+    for cv_bad in (codebooks(d, 2, 64, False, 1)[1], codebooks(d, 3, 128, False, 1)[1],
+                   codebooks(d, 3, 64, True, 1)[1]):
+        with pytest.raises(tq.TQError) as ei:
+            tq.attn_decode(gck, cv_bad, Q, kp, tq.Packed(cv_bad, H * L), H, L, sl)
+        assert ei.value.code == -2 and "decode" in str(ei.value)
+    gck_dense = codebooks(d, 3, 64, True, 0)[1]
+    with pytest.raises(tq.TQError) as ei:
+        tq.attn_decode(gck_dense, gcv, Q, tq.Packed(gck_dense, H * L), vp, H, L, sl)
+    assert ei.value.code == -2
 
 
 def test_prepared_launches_match_eager_calls():
@@ -352,3 +363,51 @@ def test_prepared_launches_match_eager_calls():
         for a, b in [(kp.codes, kp2.codes), (kp.signs, kp2.signs), (kp.norm, kp2.norm), (vp.codes, vp2.codes),
                      (lg[..., :L - 3], lg2[..., :L - 3]), (out, out2)]:
             assert torch.equal(a, b)
+
+
+def test_explicit_query_positions():
+    """q_pos sets each sequence's query RoPE position (a decode step whose own
+    key is already cached passes q_pos = seq_len - 1); positions below 0 and
+    above L_cap are clamped like seq_len.  Logits, top-k and the fused decode
+    all take it, for the contiguous and the paged forms."""
+    d, H, Hq, L, B = 128, 2, 8, 257, 4
+    ock, gck = codebooks(d, 3, 64, False, 0)
+    ocv, gcv = codebooks(d, 3, 64, False, 1)
+    g = synth.rng(21)
+    K = g.standard_normal((B, L, H, d)).astype(np.float32)
+    V = g.standard_normal((B, L, H, d)).astype(np.float32)
+    Q = g.standard_normal((B, Hq, d)).astype(np.float32)
+    rope_o = orope.rope_table(5e5, d, L + 1)
+    rope_g = tq.rope_table(5e5, d, L + 1)
+    kp, vp = tq.Packed(gck, B * H * L), tq.Packed(gcv, B * H * L)
+    tq.encode_kv(gck, gcv, torch.from_numpy(K).cuda(), torch.from_numpy(V).cuda(), kp, vp, L_cap=L, rope=rope_g)
+    lens = np.array([L, 130, 1, L], np.int32)
+    qpos = np.array([L - 1, 7, -5, 10 ** 6], np.int32)
+    sl = torch.from_numpy(lens).cuda()
+    qp_dev = torch.from_numpy(qpos).cuda()
+    qd = torch.from_numpy(Q).cuda()
+    lg = tq.attn_logits(gck, qd, kp, H, L, sl, rope=rope_g, q_pos=qp_dev).cpu().numpy()
+    vals, idx = tq.attn_logits(gck, qd, kp, H, L, sl, rope=rope_g, q_pos=qp_dev, top_k=4)
+    out = tq.attn_decode(gck, gcv, qd, kp, vp, H, L, sl, rope=rope_g, q_pos=qp_dev).cpu().numpy()
+    lg_default = tq.attn_logits(gck, qd, kp, H, L, sl, rope=rope_g).cpu().numpy()
+    torch.cuda.synchronize()
+    vals, idx = vals.cpu().numpy(), idx.cpu().numpy()
+    gk, gv = kp.numpy(), vp.numpy()
+    ek = codec.Encoded(gk[0].astype(np.float64), gk[1].astype(np.float64), gk[2], gk[3])
+    ev = codec.Encoded(gv[0].astype(np.float64), gv[1].astype(np.float64), gv[2], gv[3])
+    G = Hq // H
+    for b in range(B):
+        p = int(min(max(qpos[b], 0), L))
+        qp, s = estimator.prep_query(ock, Q[b], p, rope_o)
+        qd0, sd0 = estimator.prep_query(ock, Q[b], int(lens[b]), rope_o)
+        for h in range(H):
+            gs = slice(h * G, (h + 1) * G)
+            r = rows(ek, (b * H + h) * L, (b * H + h) * L + lens[b])
+            rv = rows(ev, (b * H + h) * L, (b * H + h) * L + lens[b])
+            ref = estimator.logits(ock, qp[gs], s[gs], r)
+            parity.assert_close(lg[b, gs, :lens[b]], ref, f"q_pos logits b={b} h={h}")
+            parity.check_topk(vals[b, gs], idx[b, gs], ref, 4, f"q_pos top-k b={b} h={h}")
+            parity.assert_close(out[b, gs], estimator.attention(ock, ocv, qp[gs], s[gs], r, rv, int(lens[b]),
+                                                                1 / math.sqrt(d), h), f"q_pos decode b={b} h={h}")
+            parity.assert_close(lg_default[b, gs, :lens[b]], estimator.logits(ock, qd0[gs], sd0[gs], r),
+                                f"default position logits b={b} h={h}")

@@ -142,10 +142,10 @@ def test_null_arguments_are_rejected_without_a_gpu():
     assert L.tq_codebook_destroy(None) == _lib.TQ_OK
     assert L.tq_encode_kv(None, None, None, None, 0, 1, 1, 1, None, None, 0, 1, None, None, 0, None, None, None,
                           0, None) == _lib.TQ_EINVAL
-    assert L.tq_attn_logits(None, None, 0, None, 1, 1, 1, 1, None, None, None, 0, 0, None, None, None, 0,
+    assert L.tq_attn_logits(None, None, 0, None, 1, 1, 1, 1, None, None, None, None, 0, 0, None, None, None, 0,
                             None) == _lib.TQ_EINVAL
-    assert L.tq_attn_decode(None, None, None, 0, None, None, 1, 1, 1, 1, None, None, None, 0, 0.0, None, None, 0,
-                            None) == _lib.TQ_EINVAL
+    assert L.tq_attn_decode(None, None, None, 0, None, None, 1, 1, 1, 1, None, None, None, None, 0, 0.0, None, None,
+                            0, None) == _lib.TQ_EINVAL
     assert L.tq_rope_table(10000.0, 63, 4, None, None) == _lib.TQ_EINVAL
     assert L.tq_workspace_bytes(None, None, 0, 10, 1, 1, 1, 0) == 0
     assert L.tq_version().decode().startswith("libtq")
@@ -165,11 +165,11 @@ def test_paged_and_append_calls_reject_bad_arguments_without_a_gpu():
     sp = _lib.tq_spec(64, 2, 32, 0, 0)
     for size, maxp, npg in [(48, 4, 8), (0, 4, 8), (64, 0, 8), (64, 4, 0), (64, 1 << 25, 8)]:
         pg = _lib.tq_pages(1, size, maxp, npg)
-        assert L.tq_attn_logits_paged(None, None, 0, None, 1, 1, 1, None, C.byref(pg), None, None, 0, 0, None,
-                                      None, None, 0, None) == _lib.TQ_EINVAL
+        assert L.tq_attn_logits_paged(None, None, 0, None, 1, 1, 1, None, None, C.byref(pg), None, None, 0, 0,
+                                      None, None, None, 0, None) == _lib.TQ_EINVAL
     pg = _lib.tq_pages(None, 64, 4, 8)
-    assert L.tq_attn_decode_paged(None, None, None, 0, None, None, 1, 1, 1, None, C.byref(pg), None, None, 0, 0.0,
-                                  None, None, 0, None) == _lib.TQ_EINVAL
+    assert L.tq_attn_decode_paged(None, None, None, 0, None, None, 1, 1, 1, None, None, C.byref(pg), None, None, 0,
+                                  0.0, None, None, 0, None) == _lib.TQ_EINVAL
     assert L.tq_encode_kv_paged(None, None, None, None, 0, 1, 1, 1, None, None, 0, None, None, None, 0, None, None,
                                 None) == _lib.TQ_EINVAL
     # append: no positions, or no page table and no capacity

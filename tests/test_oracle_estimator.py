@@ -131,3 +131,25 @@ def test_topk_order_and_ties():
     g = np.random.default_rng(0).standard_normal((5, 1000))
     idx, val = estimator.topk(g, 10)
     np.testing.assert_array_equal(val, -np.sort(-g, axis=1)[:, :10])
+
+
+def test_query_and_key_at_one_position_score_their_plain_product():
+    """A query RoPE'd at position p against a key RoPE'd at the same p: the
+    rotated query q' = Pi RoPE(q, p) and the rotated key Pi RoPE(k, p) have the
+    inner product <q, k> of the un-rotated vectors (relative offset 0; TurboESM
+    summary, technical section 2: RoPE, then Pi), at any p."""
+    from oracle import rope as orope
+    d = 128
+    cb = codec.make_codebook(d, 3, 64, False, seed=0)
+    rope = orope.rope_table(5e5, d, 4096)
+    g = np.random.default_rng(12)
+    q, k = g.standard_normal((2, d))
+    for p in (0, 1, 777, 4095):
+        qp, _ = estimator.prep_query(cb, q[None], p, rope)
+        kr = orope.apply_rope(k[None], np.array([p]), rope[0], rope[1]) @ cb.pi.T
+        # (the float32 RoPE table and rotation keep norms to about 1e-8)
+        assert abs(float(qp[0] @ kr[0]) - float(q @ k)) < 1e-6 * (1 + abs(float(q @ k)))
+    # a query one position after its key does not
+    qp, _ = estimator.prep_query(cb, q[None], 778, rope)
+    kr = orope.apply_rope(k[None], np.array([777]), rope[0], rope[1]) @ cb.pi.T
+    assert abs(float(qp[0] @ kr[0]) - float(q @ k)) > 1e-3
