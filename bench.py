@@ -1,6 +1,8 @@
 """Benchmark of the KV codec's hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama8b]
+                    [--copies 4] [--reps 5] [--cache-state rotate|hot|flushed]
+    python bench.py --copy-calibrate          # a device copy of known size
 
 A step is one pass of the whole hot path over one batch of synthetic input
 that is already resident in HBM: encode K and V into packed records, score
@@ -10,11 +12,29 @@ Llama-3.1-8B-shaped layer: batch 8, 32 query heads over 8 KV heads, head dim
 128, context 32768, bf16 K/V with one percent of channels scaled x100, RoPE
 base 5e5, 3-bit Lloyd-Max codes plus a 64-row QJL sketch.
 
-Printed: one JSON line.  `value` is whole-step key throughput (cached keys
-encoded, scored and attended per second); per-kernel times come from HIP
-events on the launch stream inside the timed region, and `roofline` relates
-the dominant kernel's algorithmic bytes per launch to its measured duration.
-`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+Timing.
+* Steps: W untimed warmup steps, then K steps timed by the host clock
+  between two device synchronisations (ms_per_step).  Every buffer the step
+  touches exists in --copies copies (inputs, records, outputs) and step i uses
+  copy i mod copies, so no step finds the previous step's data in the 256 MB
+  memory-side cache.
+* Calls: each call of the step (encode K, encode V, logits, decode) is then
+  timed alone as N back-to-back launches between one pair of HIP events on
+  the launch stream, N cycling through the buffer copies (about 3 ms per
+  repeat); the figure is the median over --reps repeats of the per-launch
+  time.  With --cache-state hot the same copy is relaunched (its data stays
+  cached); with flushed every launch is timed alone after a 1 GiB read that
+  evicts the cache.
+* Device bandwidth: a 1 GiB device copy, fill and read (sum) are timed in the
+  same run, and the kernels' rates are also given as a fraction of them.
+
+Printed: one JSON line.  `value` is the logit scan's key throughput (keys of
+the cached context scored per second for all their query heads) for the
+decode workloads, encode tokens/s for the ESM-2 prefill encode, database
+vectors scanned per second for vector search.  `roofline` relates the
+dominant call's algorithmic bytes (or flops) per launch to its measured
+duration; `cpu_baseline` times the CPU oracle on a bounded sample of the same
+workload, and the tiny configuration on one and on all host threads.
 """
 from __future__ import annotations
 
@@ -33,7 +53,9 @@ if ROOT not in sys.path:
 
 METRIC = "decode attn-logit keys/sec + % of HBM peak; KV encode tokens/sec (1 MI355X)"
 HBM_PEAK_GBS = 8000.0
+FP32_PEAK_TFLOPS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+REPEAT_MS = 3.0  # device time per timed repeat of a call
 
 
 def device_code_digest() -> str:
@@ -56,10 +78,9 @@ def measured_traffic(workload: str, call: str):
     """HBM bytes per call from rocprofv3 FETCH_SIZE / WRITE_SIZE passes
     (profiles/hbm_traffic.json), or None when absent or taken for other
     device code."""
-    import json as _json
     try:
         with open(TRAFFIC_FILE) as fh:
-            t = _json.load(fh)
+            t = json.load(fh)
     except (OSError, ValueError):
         return None
     if t.get("device_code_sha256") != device_code_digest():
@@ -67,24 +88,43 @@ def measured_traffic(workload: str, call: str):
     return t.get("calls", {}).get(workload, {}).get(call, {}).get("traffic_bytes")
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=None,
-                    help="untimed warmup steps (default: as many as fill about 0.3 s, at least 3: the "
-                         "GPU's clocks take some 100 ms of load to settle)")
+                    help="untimed warmup steps (default: as many as fill about 0.3 s, at least one per buffer "
+                         "copy: the GPU's clocks take some 100 ms of load to settle)")
     ap.add_argument("--workload", default="llama8b",
                     choices=["llama8b", "llama70b", "esm650m", "vsearch", "llama8b-turboesm", "esm650m-turboesm",
                              "llama8b-serve", "llama8b-fib", "tiny"])
+    ap.add_argument("--copies", type=int, default=4, help="buffer copies the steps and timed calls rotate over")
+    ap.add_argument("--reps", type=int, default=5, help="timed repeats per call (the median is reported)")
+    ap.add_argument("--cache-state", default="rotate", choices=["rotate", "hot", "flushed"])
+    ap.add_argument("--bits", type=int, default=None, help="llama workloads: Lloyd-Max bits (default 3)")
+    ap.add_argument("--qjl-rows", type=int, default=None,
+                    help="llama workloads: QJL sketch rows m (default 64 for llama8b, 128 for llama70b)")
+    ap.add_argument("--copy-calibrate", action="store_true",
+                    help="only run a 1 GiB device copy, fill and read (counter calibration) and print their rates")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="keys in the oracle's sample (0: default)")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
-class Timer:
-    """HIP events on the launch stream around individual API calls (events
-    created up front, so that recording them costs the host little)."""
+def host_cores():
+    """Host CPUs this process may run on, and the oracle's BLAS thread count."""
+    cores = len(os.sched_getaffinity(0))
+    try:
+        import threadpoolctl
+        blas = max(p["num_threads"] for p in threadpoolctl.threadpool_info()) or 1
+    except Exception:
+        blas = cores
+    return cores, blas
+
+
+class StepTimer:
+    """HIP events on the launch stream around the calls of the timed steps
+    (created up front, so that recording them costs the host little)."""
 
     def __init__(self, torch, events=0):
         self.torch = torch
@@ -106,9 +146,9 @@ class Timer:
         e.record(self.stream)
         self.spans.setdefault(name, []).append((s, e))
 
-    def mean_ms(self, name):
-        v = [s.elapsed_time(e) for s, e in self.spans[name]]
-        return float(np.mean(v)), len(v)
+    def mean_us(self, name):
+        v = [s.elapsed_time(e) for s, e in self.spans.get(name, [])]
+        return float(np.mean(v)) * 1e3 if v else None
 
 
 class NoTimer:
@@ -118,8 +158,118 @@ class NoTimer:
         fn()
 
 
+def run_step(st, timer, i=0):
+    """Step i: the calls of buffer copy i mod copies."""
+    for name, launch in st["rot"][i % len(st["rot"])]:
+        timer.call(name, launch)
+
+
+def run_calls(st, timer):
+    """One step over buffer copy 0."""
+    run_step(st, timer, 0)
+
+
+def call_names(st):
+    names = []
+    for n, _ in st["rot"][0]:
+        if n not in names:
+            names.append(n)
+    return names
+
+
+def time_calls(torch, st, state, reps):
+    """Per-launch device time (us) of each call, as the median over `reps`
+    repeats of N back-to-back launches between one event pair on the launch
+    stream.  rotate: the launches cycle through the buffer copies (and, for a
+    call made several times per step, its instances); hot: one instance
+    relaunched; flushed: each launch timed alone after a 1 GiB read."""
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda") if state == "flushed" else None
+    out = {}
+    for name in call_names(st):
+        seq = [launch for rot in st["rot"] for n, launch in rot if n == name]
+        if state == "hot":
+            seq = seq[:1]
+        if state == "flushed":
+            ts = []
+            for j in range(3 + 8 * reps):
+                flush.sum()
+                s, e = ev(), ev()
+                s.record(stream)
+                seq[j % len(seq)]()
+                e.record(stream)
+                torch.cuda.synchronize()
+                ts.append(s.elapsed_time(e) * 1e3)
+            ts = np.array(ts[3:])
+            out[name] = {"us": float(np.median(ts)), "us_min": float(ts.min()), "us_max": float(ts.max()),
+                         "launches": len(ts), "timing": "each launch alone after a 1 GiB read"}
+            continue
+        s, e = ev(), ev()
+        s.record(stream)
+        for f in seq:
+            f()
+        e.record(stream)
+        torch.cuda.synchronize()
+        t_seq = s.elapsed_time(e)
+        n = len(seq) * max(2, int(math.ceil(REPEAT_MS / max(t_seq, 1e-3))))
+        per = []
+        for _ in range(reps):
+            s, e = ev(), ev()
+            s.record(stream)
+            for j in range(n):
+                seq[j % len(seq)]()
+            e.record(stream)
+            torch.cuda.synchronize()
+            per.append(s.elapsed_time(e) * 1e3 / n)
+        per = np.array(per)
+        out[name] = {"us": float(np.median(per)), "us_min": float(per.min()), "us_max": float(per.max()),
+                     "launches_per_repeat": n, "repeats": reps, "instances": len(seq),
+                     "timing": "back-to-back launches, one event pair per repeat"}
+    return out
+
+
+def device_rates(torch, mib=1024, reps=5):
+    """GB/s of a device copy (read + write), a fill (write) and a sum (read)
+    of `mib` MiB, each the median of `reps` event-timed repeats of three
+    back-to-back launches."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    nbytes = n * 4
+    res = {}
+    for label, fn, moved in (("copy", lambda: dst.copy_(src), 2 * nbytes),
+                             ("fill", lambda: dst.fill_(2.0), nbytes),
+                             ("read", lambda: src.sum(), nbytes)):
+        fn()
+        torch.cuda.synchronize()
+        v = []
+        for _ in range(reps):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for _ in range(3):
+                fn()
+            e.record()
+            torch.cuda.synchronize()
+            v.append(3 * moved / (s.elapsed_time(e) * 1e-3) / 1e9)
+        res[label + "_GBps"] = float(np.median(v))
+    del src, dst
+    torch.cuda.empty_cache()
+    return res
+
+
 def bf16_dev(torch, bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def _copies(t, n):
+    return [t] + [t.clone() for _ in range(n - 1)]
+
+
+def _rate(k):
+    k["GBps"] = k["alg_bytes"] / (k["us"] * 1e-6) / 1e9
+    k["hbm_frac"] = k["GBps"] / HBM_PEAK_GBS
+    return k
 
 
 # ------------------------------------------------------------ TurboESM tables
@@ -138,18 +288,19 @@ def turboesm_codebooks(tq, synth, d, bits, k_sample, v_sample, rope_host):
 
 
 # ------------------------------------------------------------ llama-shaped
-def setup_llama(torch, tq, synth, kind, variant="qjl"):
+def setup_llama(torch, tq, synth, kind, variant="qjl", copies=1, bits=None, m=None):
     if kind == "llama8b":
-        B, Hq, H, L, d, bits, m, rope_base = 8, 32, 8, 32768, 128, 3, 64, 5e5
+        B, Hq, H, L, d, b0, m0, rope_base = 8, 32, 8, 32768, 128, 3, 64, 5e5
     else:
-        B, Hq, H, L, d, bits, m, rope_base = 1, 64, 8, 131072, 128, 3, 128, 0.0
-    if variant == "turboesm":
-        m = d
+        B, Hq, H, L, d, b0, m0, rope_base = 1, 64, 8, 131072, 128, 3, 128, 0.0
+    bits = b0 if bits is None else bits
+    m = (d if variant == "turboesm" else m0) if m is None else m
     K, V = synth.llama_kv_inputs(kind, seed=0, batch=B, ctx=L, hkv=H, d=d)
     Q = synth.llama_q_inputs(seed=100, batch=B, hq=Hq, d=d)
     st = {"B": B, "Hq": Hq, "H": H, "L": L, "d": d, "bits": bits, "m": m, "rope_base": rope_base,
-          "variant": variant}
-    st["K"], st["V"], st["Q"] = bf16_dev(torch, K), bf16_dev(torch, V), bf16_dev(torch, Q)
+          "variant": variant, "kind": kind}
+    Kd, Vd = bf16_dev(torch, K), bf16_dev(torch, V)
+    st["Q"] = bf16_dev(torch, Q)
     st["host"] = (K, V, Q)
     if variant == "turboesm":
         rope_host = tq.rope_table(rope_base, d, L + 1, device=None) if rope_base else None
@@ -159,64 +310,61 @@ def setup_llama(torch, tq, synth, kind, variant="qjl"):
     else:
         st["ck"] = tq.Codebook(d, bits, m, "hadamard", seed=synth.K_SEED)
         st["cv"] = tq.Codebook(d, bits, m, "hadamard", seed=synth.V_SEED)
-    st["kp"] = tq.Packed(st["ck"], B * H * L)
-    st["vp"] = tq.Packed(st["cv"], B * H * L)
     st["rope"] = tq.rope_table(rope_base, d, L + 1) if rope_base else None
     st["sl"] = torch.full((B,), L, dtype=torch.int32, device="cuda")
-    st["logits"] = torch.empty((B, Hq, L), dtype=torch.float32, device="cuda")
-    st["out"] = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
     st["ws_l"] = torch.empty(max(1, tq.workspace_bytes(st["ck"], None, tq.TQ_OP_LOGITS, B, Hq, H, L, 0)),
                              dtype=torch.uint8, device="cuda")
     st["ws_d"] = torch.empty(max(1, tq.workspace_bytes(st["ck"], st["cv"], tq.TQ_OP_DECODE, B, Hq, H, L, 0)),
                              dtype=torch.uint8, device="cuda")
-    # every call of the step with its arguments marshalled once
-    st["calls"] = [
-        ("encode_k", tq.encode_kv(st["ck"], None, st["K"], None, st["kp"], None, L_cap=L, rope=st["rope"],
-                                  prepare=True)),
-        ("encode_v", tq.encode_kv(None, st["cv"], None, st["V"], None, st["vp"], L_cap=L, prepare=True)),
-        ("logits", tq.attn_logits(st["ck"], st["Q"], st["kp"], H, L, st["sl"], rope=st["rope"], out=st["logits"],
-                                  workspace=st["ws_l"], prepare=True)[0]),
-        ("decode", tq.attn_decode(st["ck"], st["cv"], st["Q"], st["kp"], st["vp"], H, L, st["sl"], rope=st["rope"],
-                                  out=st["out"], workspace=st["ws_d"], prepare=True)[0]),
-    ]
+    Ks, Vs = _copies(Kd, copies), _copies(Vd, copies)
+    st["rot"] = []
+    for c in range(copies):
+        kp, vp = tq.Packed(st["ck"], B * H * L), tq.Packed(st["cv"], B * H * L)
+        lg = torch.empty((B, Hq, L), dtype=torch.float32, device="cuda")
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+        if c == 0:
+            st["K"], st["V"], st["kp"], st["vp"], st["logits"], st["out"] = Ks[0], Vs[0], kp, vp, lg, out
+        # every call of the step with its arguments marshalled once
+        st["rot"].append([
+            ("encode_k", tq.encode_kv(st["ck"], None, Ks[c], None, kp, None, L_cap=L, rope=st["rope"],
+                                      prepare=True)),
+            ("encode_v", tq.encode_kv(None, st["cv"], None, Vs[c], None, vp, L_cap=L, prepare=True)),
+            ("logits", tq.attn_logits(st["ck"], st["Q"], kp, H, L, st["sl"], rope=st["rope"], out=lg,
+                                      workspace=st["ws_l"], prepare=True)[0]),
+            ("decode", tq.attn_decode(st["ck"], st["cv"], st["Q"], kp, vp, H, L, st["sl"], rope=st["rope"],
+                                      out=out, workspace=st["ws_d"], prepare=True)[0]),
+        ])
+    st["calls"] = st["rot"][0]
     return st
 
 
-def run_calls(st, timer):
-    for name, launch in st["calls"]:
-        timer.call(name, launch)
-
-
-def llama_report(st, timer, ms_step):
+def llama_report(st, ct, ms_step):
     B, Hq, H, L, d, bits, m = (st[k] for k in ("B", "Hq", "H", "L", "d", "bits", "m"))
     G = Hq // H
     keys = B * H * L
     sign = st["variant"] == "turboesm"
     rec = 4 + (4 if m and not sign else 0) + bits * d // 8 + m // 8
     in_bytes = 2 * d  # bf16
-    enc_ms, n_enc = timer.mean_ms("encode_k")
-    encv_ms, _ = timer.mean_ms("encode_v")
-    log_ms, _ = timer.mean_ms("logits")
-    dec_ms, _ = timer.mean_ms("decode")
     kern = {
-        "encode_k": {"ms": enc_ms, "launches": n_enc, "alg_bytes": keys * (in_bytes + rec),
-                     "unit": "vectors", "units": keys},
-        "encode_v": {"ms": encv_ms, "alg_bytes": keys * (in_bytes + rec), "units": keys},
-        "logits": {"ms": log_ms, "alg_bytes": keys * (rec + 4 * G), "units": keys},
-        "decode": {"ms": dec_ms, "alg_bytes": keys * 2 * rec, "units": keys},
+        "encode_k": {"alg_bytes": keys * (in_bytes + rec), "units": keys, "unit": "vectors"},
+        "encode_v": {"alg_bytes": keys * (in_bytes + rec), "units": keys, "unit": "vectors"},
+        "logits": {"alg_bytes": keys * (rec + 4 * G), "units": keys, "unit": "keys"},
+        "decode": {"alg_bytes": keys * 2 * rec, "units": keys, "unit": "keys"},
     }
-    for k in kern.values():
-        k["GBps"] = k["alg_bytes"] / (k["ms"] * 1e-3) / 1e9
-        k["hbm_frac"] = k["GBps"] / HBM_PEAK_GBS
-    dom = max(("encode_k", "encode_v", "logits", "decode"), key=lambda k: kern[k]["ms"])
+    for name, k in kern.items():
+        k.update(ct[name])
+        _rate(k)
+    t = {n: kern[n]["us"] * 1e-6 for n in kern}
     extra = {
-        "logit_keys_per_s": keys / (log_ms * 1e-3),
+        "logit_keys_per_s": keys / t["logits"],
+        "logits_per_s": keys * G / t["logits"],
         "logit_hbm_frac": kern["logits"]["hbm_frac"],
-        "decode_keys_per_s": keys / (dec_ms * 1e-3),
-        "encode_tokens_per_s": B * L / ((enc_ms + encv_ms) * 1e-3),
-        "encode_vectors_per_s": 2 * keys / ((enc_ms + encv_ms) * 1e-3),
+        "decode_keys_per_s": keys / t["decode"],
+        "encode_tokens_per_s": B * L / (t["encode_k"] + t["encode_v"]),
+        "encode_vectors_per_s": 2 * keys / (t["encode_k"] + t["encode_v"]),
+        "step_keys_per_s": keys / (ms_step * 1e-3),
     }
-    name = f"{'Llama-3.1-8B' if L == 32768 else 'Llama-70B'}-shaped decode layer"
+    name = f"{'Llama-3.1-8B' if st['kind'] == 'llama8b' else 'Llama-70B'}-shaped decode layer"
     cfg = {"workload": name + (", TurboESM-style records" if sign else ""), "batch": B,
            "q_heads": Hq, "kv_heads": H, "head_dim": d, "context": L, "bits": bits,
            "input_dtype": "bf16", "rope_base": st["rope_base"], "record_bytes": rec}
@@ -225,14 +373,14 @@ def llama_report(st, timer, ms_step):
                     "value_table": "calibrated, original coordinates", "calibration_tokens": CALIB_TOKENS})
     else:
         cfg["qjl_rows"] = m
-    return keys / (ms_step * 1e-3), "keys/s", kern, dom, extra, cfg
+    return extra["logit_keys_per_s"], "keys/s", kern, extra, cfg
 
 
 # ------------------------------------------------------------ FibQuant codebooks
 FIB_BITS = 4  # 16 codewords per 2-coordinate block: 2 bits per coordinate
 
 
-def setup_fib(torch, tq, synth):
+def setup_fib(torch, tq, synth, copies=1):
     """The Llama-3.1-8B-shaped layer with FibQuant vector codebooks for keys
     and values (k = 2, N = 16): encode K (RoPE), encode V, the logit scan of
     the 32 query heads over every cached key, and the fused decode."""
@@ -240,55 +388,58 @@ def setup_fib(torch, tq, synth):
     K, V = synth.llama_kv_inputs("llama8b", seed=0, batch=B, ctx=L, hkv=H, d=d)
     Q = synth.llama_q_inputs(seed=100, batch=B, hq=Hq, d=d)
     st = {"B": B, "Hq": Hq, "H": H, "L": L, "d": d, "bits": FIB_BITS, "rope_base": 5e5, "host": (K, V, Q)}
-    st["K"], st["V"], st["Q"] = bf16_dev(torch, K), bf16_dev(torch, V), bf16_dev(torch, Q)
+    Kd, Vd = bf16_dev(torch, K), bf16_dev(torch, V)
+    st["Q"] = bf16_dev(torch, Q)
     st["ck"] = tq.Codebook(d, FIB_BITS, 0, "hadamard", seed=synth.K_SEED, block=2)
     st["cv"] = tq.Codebook(d, FIB_BITS, 0, "hadamard", seed=synth.V_SEED, block=2)
-    st["kp"], st["vp"] = tq.Packed(st["ck"], B * H * L), tq.Packed(st["cv"], B * H * L)
     st["rope"] = tq.rope_table(5e5, d, L + 1)
     st["sl"] = torch.full((B,), L, dtype=torch.int32, device="cuda")
-    st["logits"] = torch.empty((B, Hq, L), dtype=torch.float32, device="cuda")
     st["ws_l"] = torch.empty(max(1, tq.workspace_bytes(st["ck"], None, tq.TQ_OP_LOGITS, B, Hq, H, L, 0)),
                              dtype=torch.uint8, device="cuda")
-    st["out"] = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
     st["ws_d"] = torch.empty(max(1, tq.workspace_bytes(st["ck"], st["cv"], tq.TQ_OP_DECODE, B, Hq, H, L, 0)),
                              dtype=torch.uint8, device="cuda")
-    st["calls"] = [
-        ("encode_k", tq.encode_kv(st["ck"], None, st["K"], None, st["kp"], None, L_cap=L, rope=st["rope"],
-                                  prepare=True)),
-        ("encode_v", tq.encode_kv(None, st["cv"], None, st["V"], None, st["vp"], L_cap=L, prepare=True)),
-        ("logits", tq.attn_logits(st["ck"], st["Q"], st["kp"], H, L, st["sl"], rope=st["rope"], out=st["logits"],
-                                  workspace=st["ws_l"], prepare=True)[0]),
-        ("decode", tq.attn_decode(st["ck"], st["cv"], st["Q"], st["kp"], st["vp"], H, L, st["sl"], rope=st["rope"],
-                                  out=st["out"], workspace=st["ws_d"], prepare=True)[0]),
-    ]
+    Ks, Vs = _copies(Kd, copies), _copies(Vd, copies)
+    st["rot"] = []
+    for c in range(copies):
+        kp, vp = tq.Packed(st["ck"], B * H * L), tq.Packed(st["cv"], B * H * L)
+        lg = torch.empty((B, Hq, L), dtype=torch.float32, device="cuda")
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+        if c == 0:
+            st["K"], st["V"], st["kp"], st["vp"], st["logits"], st["out"] = Ks[0], Vs[0], kp, vp, lg, out
+        st["rot"].append([
+            ("encode_k", tq.encode_kv(st["ck"], None, Ks[c], None, kp, None, L_cap=L, rope=st["rope"],
+                                      prepare=True)),
+            ("encode_v", tq.encode_kv(None, st["cv"], None, Vs[c], None, vp, L_cap=L, prepare=True)),
+            ("logits", tq.attn_logits(st["ck"], st["Q"], kp, H, L, st["sl"], rope=st["rope"], out=lg,
+                                      workspace=st["ws_l"], prepare=True)[0]),
+            ("decode", tq.attn_decode(st["ck"], st["cv"], st["Q"], kp, vp, H, L, st["sl"], rope=st["rope"],
+                                      out=out, workspace=st["ws_d"], prepare=True)[0]),
+        ])
+    st["calls"] = st["rot"][0]
     return st
 
 
-def fib_report(st, timer, ms_step):
+def fib_report(st, ct, ms_step):
     B, Hq, H, L, d, bits = (st[k] for k in ("B", "Hq", "H", "L", "d", "bits"))
     keys = B * H * L
     rec = 4 + 4 * ((d // 2 * bits + 31) // 32)
-    enc_ms, n = timer.mean_ms("encode_k")
-    encv_ms, _ = timer.mean_ms("encode_v")
-    log_ms, _ = timer.mean_ms("logits")
-    dec_ms, _ = timer.mean_ms("decode")
-    kern = {"encode_k": {"ms": enc_ms, "launches": n, "alg_bytes": keys * (2 * d + rec), "units": keys},
-            "encode_v": {"ms": encv_ms, "alg_bytes": keys * (2 * d + rec), "units": keys},
-            "logits": {"ms": log_ms, "alg_bytes": keys * (rec + 4 * Hq // H), "units": keys},
-            "decode": {"ms": dec_ms, "alg_bytes": keys * 2 * rec, "units": keys}}
-    for k in kern.values():
-        k["GBps"] = k["alg_bytes"] / (k["ms"] * 1e-3) / 1e9
-        k["hbm_frac"] = k["GBps"] / HBM_PEAK_GBS
-    dom = max(kern, key=lambda x: kern[x]["ms"])
-    extra = {"logit_keys_per_s": keys / (log_ms * 1e-3), "logit_hbm_frac": kern["logits"]["hbm_frac"],
-             "decode_keys_per_s": keys / (dec_ms * 1e-3),
-             "encode_vectors_per_s": 2 * keys / ((enc_ms + encv_ms) * 1e-3)}
+    kern = {"encode_k": {"alg_bytes": keys * (2 * d + rec), "units": keys, "unit": "vectors"},
+            "encode_v": {"alg_bytes": keys * (2 * d + rec), "units": keys, "unit": "vectors"},
+            "logits": {"alg_bytes": keys * (rec + 4 * Hq // H), "units": keys, "unit": "keys"},
+            "decode": {"alg_bytes": keys * 2 * rec, "units": keys, "unit": "keys"}}
+    for name, k in kern.items():
+        k.update(ct[name])
+        _rate(k)
+    t = {n: kern[n]["us"] * 1e-6 for n in kern}
+    extra = {"logit_keys_per_s": keys / t["logits"], "logit_hbm_frac": kern["logits"]["hbm_frac"],
+             "decode_keys_per_s": keys / t["decode"],
+             "encode_vectors_per_s": 2 * keys / (t["encode_k"] + t["encode_v"]),
+             "step_keys_per_s": keys / (ms_step * 1e-3)}
     cfg = {"workload": "Llama-3.1-8B-shaped layer with FibQuant vector codebooks (encode K, V; logits; decode)",
-           "batch": B,
-           "q_heads": Hq, "kv_heads": H, "head_dim": d, "context": L, "block": 2, "codewords": 1 << bits,
-           "bits_per_coordinate": bits / 2, "input_dtype": "bf16", "rope_base": st["rope_base"],
-           "record_bytes": rec}
-    return keys / (ms_step * 1e-3), "keys/s", kern, dom, extra, cfg
+           "batch": B, "q_heads": Hq, "kv_heads": H, "head_dim": d, "context": L, "block": 2,
+           "codewords": 1 << bits, "bits_per_coordinate": bits / 2, "input_dtype": "bf16",
+           "rope_base": st["rope_base"], "record_bytes": rec}
+    return extra["logit_keys_per_s"], "keys/s", kern, extra, cfg
 
 
 def cpu_baseline_fib(st, budget_s=10.0):
@@ -324,26 +475,22 @@ def cpu_baseline_fib(st, budget_s=10.0):
             dt += time.perf_counter() - t1
             done += n
             pairs += 1
-    try:
-        import threadpoolctl
-        threads = max(p["num_threads"] for p in threadpoolctl.threadpool_info()) or 1
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
-    return {"value": done / dt, "unit": "keys/s", "cores": threads, "kind": "oracle",
+    return {"value": done / dt, "unit": "keys/s", "kind": "oracle",
             "sample": f"{pairs} (sequence, KV head) pairs, the first {n} keys and values of each encoded, scored "
-                      f"and attended for {G} query heads by the oracle, {dt:.1f} s on the host (codebook built beforehand, "
-                      f"{t_setup:.1f} s)"}
+                      f"and attended for {G} query heads by the oracle, {dt:.1f} s on the host (codebook built "
+                      f"beforehand, {t_setup:.1f} s)"}
 
 
 # ------------------------------------------------------------ serving step
 PAGE = 256  # slots per page of the paged cache
 
 
-def setup_serve(torch, tq, synth):
+def setup_serve(torch, tq, synth, copies=1):
     """One autoregressive step of the Llama-3.1-8B-shaped layer over a paged
     cache: the cache holds L - 1 tokens per sequence, spread over a shuffled
     pool of pages; a step appends token L - 1 (keys and values of every
-    (sequence, KV head)) and runs the fused decode over the L tokens."""
+    (sequence, KV head)) and runs the fused decode over the L tokens, the
+    query at position L - 1 like its own key."""
     B, Hq, H, L, d, bits, m, rope_base = 8, 32, 8, 32768, 128, 3, 64, 5e5
     K, V = synth.llama_kv_inputs("llama8b", seed=0, batch=B, ctx=L, hkv=H, d=d)
     Q = synth.llama_q_inputs(seed=100, batch=B, hq=Hq, d=d)
@@ -355,50 +502,50 @@ def setup_serve(torch, tq, synth):
     st["pages"] = tq.Pages(torch.from_numpy(table).cuda(), PAGE, n_pages)
     st["ck"] = tq.Codebook(d, bits, m, "hadamard", seed=synth.K_SEED)
     st["cv"] = tq.Codebook(d, bits, m, "hadamard", seed=synth.V_SEED)
-    st["kp"] = tq.Packed(st["ck"], st["pages"].records(H))
-    st["vp"] = tq.Packed(st["cv"], st["pages"].records(H))
     st["rope"] = tq.rope_table(rope_base, d, L + 1)
     Kd, Vd = bf16_dev(torch, K), bf16_dev(torch, V)
-    # prefill: the first L - 1 tokens
-    tq.encode_kv(st["ck"], st["cv"], Kd[:, :L - 1], Vd[:, :L - 1], st["kp"], st["vp"], rope=st["rope"],
-                 pages=st["pages"])
     st["K1"], st["V1"] = Kd[:, L - 1].contiguous(), Vd[:, L - 1].contiguous()
-    # the new token sits at slot L - 1: its query attends to slots 0..L-1 at
-    # position L - 1, like its own key
     st["pos"] = torch.full((B,), L - 1, dtype=torch.int32, device="cuda")
     st["sl"] = torch.full((B,), L, dtype=torch.int32, device="cuda")
     st["Q"] = bf16_dev(torch, Q)
-    st["out"] = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
     st["ws_d"] = torch.empty(max(1, tq.workspace_bytes(st["ck"], st["cv"], tq.TQ_OP_DECODE, B, Hq, H, L, 0)),
                              dtype=torch.uint8, device="cuda")
-    st["calls"] = [
-        ("append", tq.append_kv(st["ck"], st["cv"], st["K1"], st["V1"], st["kp"], st["vp"], st["pos"],
-                                pages=st["pages"], rope=st["rope"], prepare=True)),
-        ("decode", tq.attn_decode(st["ck"], st["cv"], st["Q"], st["kp"], st["vp"], H, None, st["sl"], rope=st["rope"],
-                                  out=st["out"], workspace=st["ws_d"], prepare=True, pages=st["pages"],
-                                  q_pos=st["pos"])[0]),
-    ]
+    st["rot"] = []
+    for c in range(copies):
+        kp, vp = tq.Packed(st["ck"], st["pages"].records(H)), tq.Packed(st["cv"], st["pages"].records(H))
+        # prefill: the first L - 1 tokens
+        tq.encode_kv(st["ck"], st["cv"], Kd[:, :L - 1], Vd[:, :L - 1], kp, vp, rope=st["rope"], pages=st["pages"])
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+        if c == 0:
+            st["kp"], st["vp"], st["out"] = kp, vp, out
+        st["rot"].append([
+            ("append", tq.append_kv(st["ck"], st["cv"], st["K1"], st["V1"], kp, vp, st["pos"], pages=st["pages"],
+                                    rope=st["rope"], prepare=True)),
+            ("decode", tq.attn_decode(st["ck"], st["cv"], st["Q"], kp, vp, H, None, st["sl"], rope=st["rope"],
+                                      out=out, workspace=st["ws_d"], prepare=True, pages=st["pages"],
+                                      q_pos=st["pos"])[0]),
+        ])
+    del Kd, Vd
+    st["calls"] = st["rot"][0]
     return st
 
 
-def serve_report(st, timer, ms_step):
+def serve_report(st, ct, ms_step):
     B, Hq, H, L, d, bits, m = (st[k] for k in ("B", "Hq", "H", "L", "d", "bits", "m"))
     keys = B * H * L
     rec = 8 + bits * d // 8 + m // 8
-    app_ms, n = timer.mean_ms("append")
-    dec_ms, _ = timer.mean_ms("decode")
-    kern = {"append": {"ms": app_ms, "launches": n, "alg_bytes": 2 * B * H * (2 * d + rec), "units": 2 * B * H},
-            "decode": {"ms": dec_ms, "alg_bytes": keys * 2 * rec, "units": keys}}
-    for k in kern.values():
-        k["GBps"] = k["alg_bytes"] / (k["ms"] * 1e-3) / 1e9
-        k["hbm_frac"] = k["GBps"] / HBM_PEAK_GBS
-    extra = {"decode_keys_per_s": keys / (dec_ms * 1e-3), "append_us": app_ms * 1e3, "decode_us": dec_ms * 1e3,
-             "tokens_per_s": B / (ms_step * 1e-3)}
+    kern = {"append": {"alg_bytes": 2 * B * H * (2 * d + rec), "units": 2 * B * H, "unit": "vectors"},
+            "decode": {"alg_bytes": keys * 2 * rec, "units": keys, "unit": "keys"}}
+    for name, k in kern.items():
+        k.update(ct[name])
+        _rate(k)
+    extra = {"decode_keys_per_s": keys / (kern["decode"]["us"] * 1e-6), "append_us": kern["append"]["us"],
+             "decode_us": kern["decode"]["us"], "tokens_per_s": B / (ms_step * 1e-3)}
     cfg = {"workload": "Llama-3.1-8B-shaped decode step over a paged cache (append + fused decode)", "batch": B,
            "q_heads": Hq, "kv_heads": H, "head_dim": d, "context": L, "bits": bits, "qjl_rows": m,
            "input_dtype": "bf16", "rope_base": st["rope_base"], "record_bytes": rec, "page_size": PAGE,
-           "pages": B * (L // PAGE), "page_order": "shuffled"}
-    return keys / (ms_step * 1e-3), "keys/s", kern, "decode", extra, cfg
+           "pages": B * (L // PAGE), "page_order": "shuffled", "query_position": L - 1}
+    return extra["decode_keys_per_s"], "keys/s", kern, extra, cfg
 
 
 def cpu_baseline_serve(st, budget_s=8.0):
@@ -434,12 +581,7 @@ def cpu_baseline_serve(st, budget_s=8.0):
             dt += time.perf_counter() - t1
             done += L
             pairs += 1
-    try:
-        import threadpoolctl
-        threads = max(p["num_threads"] for p in threadpoolctl.threadpool_info()) or 1
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
-    return {"value": done / dt, "unit": "keys/s", "cores": threads, "kind": "oracle",
+    return {"value": done / dt, "unit": "keys/s", "kind": "oracle",
             "sample": f"{pairs} (sequence, KV head) pairs: the append of one key and value and the decode of "
                       f"{G} query heads over {L} cached keys each, {dt:.1f} s on the host (the caches encoded "
                       f"beforehand, untimed)"}
@@ -449,7 +591,9 @@ def cpu_baseline_llama(st, sample_keys, budget_s=12.0):
     """The oracle on a bounded sample: (sequence, KV head) pairs in order,
     each fully encoded (keys with RoPE, values), scored for its G query heads
     and decoded, until about budget_s seconds of host time or sample_keys
-    keys."""
+    keys.  `value` is the oracle's logit rate (keys scored per second for
+    their G query heads, query preparation included), the GPU's `value`
+    quantity; step_keys_per_s covers encode, logits and decode."""
     import synth
     from oracle import codec, estimator, rope as orope
     K, V, Q = st["host"]
@@ -464,7 +608,7 @@ def cpu_baseline_llama(st, sample_keys, budget_s=12.0):
         ock = codec.make_codebook(d, bits, m, False, seed=synth.K_SEED)
         ocv = codec.make_codebook(d, bits, m, False, seed=synth.V_SEED)
     t_setup = time.perf_counter() - t0
-    done, pairs, dt = 0, 0, 0.0
+    done, pairs, dt, dt_log = 0, 0, 0.0, 0.0
     for b in range(B):
         for kh in range(H):
             if done >= sample_keys or dt >= budget_s:
@@ -476,21 +620,20 @@ def cpu_baseline_llama(st, sample_keys, budget_s=12.0):
             t1 = time.perf_counter()
             ek = codec.encode(ock, kx, pos=np.arange(n), rope=rope)
             ev = codec.encode(ocv, vx)
+            t2 = time.perf_counter()
             qp, s = estimator.prep_query(ock, q, n, rope)
             estimator.logits(ock, qp, s, ek, kh)
+            t3 = time.perf_counter()
             estimator.attention(ock, ocv, qp, s, ek, ev, n, 1 / math.sqrt(d), kh)
             dt += time.perf_counter() - t1
+            dt_log += t3 - t2
             done += n
             pairs += 1
-    try:
-        import threadpoolctl
-        threads = max(p["num_threads"] for p in threadpoolctl.threadpool_info()) or 1
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
-    return {"value": done / dt, "unit": "keys/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} keys+values: the first {pairs} (sequence, KV head) pairs, each encoded "
-                      f"(keys with RoPE), scored for its {G} query heads and decoded by the oracle; "
-                      f"{dt:.1f} s on the host (codebook tables built once beforehand, {t_setup:.1f} s)"}
+    return {"value": done / dt_log, "unit": "keys/s", "kind": "oracle", "step_keys_per_s": done / dt,
+            "sample": f"{done} keys: the first {pairs} (sequence, KV head) pairs, each encoded (keys with RoPE, and "
+                      f"values), scored for its {G} query heads and decoded by the oracle in {dt:.1f} s on the host; "
+                      f"value counts the {dt_log:.1f} s of query preparation and logits (codebook tables built once "
+                      f"beforehand, {t_setup:.1f} s)"}
 
 
 def oracle_turboesm_codebooks(synth, d, bits, k_sample, v_sample, rope):
@@ -504,8 +647,31 @@ def oracle_turboesm_codebooks(synth, d, bits, k_sample, v_sample, rope):
             codec.make_sign_codebook(d, bits, "none", levels=lv, mu=mv))
 
 
+def cpu_tiny(threads):
+    """The oracle on the tiny configuration (4096 fp32 keys, d = 128, 2-bit
+    codes + 128-row sketch, 16 queries): encode every key, then score it for
+    every query, with the BLAS pool limited to `threads`."""
+    import threadpoolctl
+    import synth
+    from oracle import codec, estimator
+    K, Q, _ = synth.tiny_inputs(0)
+    ock = codec.make_codebook(128, 2, 128, False, seed=synth.K_SEED)
+    ts = []
+    with threadpoolctl.threadpool_limits(threads):
+        for _ in range(5):
+            t0 = time.perf_counter()
+            enc = codec.encode(ock, K)
+            qp, s = estimator.prep_query(ock, Q)
+            estimator.logits(ock, qp, s, enc)
+            ts.append(time.perf_counter() - t0)
+    dt = float(np.median(ts))
+    return {"keys_per_s": len(K) / dt, "threads": threads, "seconds_median_of_5": dt}
+
+
 # ------------------------------------------------------------ ESM-2 prefill
-def setup_esm(torch, tq, synth, variant="qjl"):
+def setup_esm(torch, tq, synth, variant="qjl", copies=1):
+    """33 layers of K and V: the step's own layer buffers already rotate (one
+    encode of each layer per step), so one copy serves."""
     S, T, H, d, layers, bits, m = 32, 1024, 20, 64, 33, 3, 64
     tok_h = synth.esm_tokens(0, S, T)
     tok = torch.from_numpy(tok_h).cuda()
@@ -531,12 +697,14 @@ def setup_esm(torch, tq, synth, variant="qjl"):
     st["kp"] = [tq.Packed(cks[i], S * H * T) for i in range(layers)]
     st["vp"] = [tq.Packed(cvs[i], S * H * T) for i in range(layers)]
     st["rope"] = tq.rope_table(1e4, d, T)
-    st["calls"] = []
+    calls = []
     for layer in range(layers):
-        st["calls"].append(("encode_k", tq.encode_kv(cks[layer], None, Ks[layer], None, st["kp"][layer], None,
-                                                     L_cap=T, rope=st["rope"], prepare=True)))
-        st["calls"].append(("encode_v", tq.encode_kv(None, cvs[layer], None, Vs[layer], None, st["vp"][layer],
-                                                     L_cap=T, prepare=True)))
+        calls.append(("encode_k", tq.encode_kv(cks[layer], None, Ks[layer], None, st["kp"][layer], None,
+                                               L_cap=T, rope=st["rope"], prepare=True)))
+        calls.append(("encode_v", tq.encode_kv(None, cvs[layer], None, Vs[layer], None, st["vp"][layer],
+                                               L_cap=T, prepare=True)))
+    st["rot"] = [calls]
+    st["calls"] = calls
     return st
 
 
@@ -570,31 +738,27 @@ def cpu_baseline_esm(st, budget_s=12.0):
             codec.encode(ocv, vx)
             dt += time.perf_counter() - t1
             done += T
-    try:
-        import threadpoolctl
-        threads = max(p["num_threads"] for p in threadpoolctl.threadpool_info()) or 1
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
     # `done` key+value vector pairs of one layer; a token needs layers * H of them
-    return {"value": done / dt / (layers * H), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": done / dt / (layers * H), "unit": "tokens/s", "kind": "oracle",
             "sample": f"{done} key+value vector pairs of layer 0 ({done // T} (sequence, head) pairs of {T} tokens) "
                       f"encoded by the oracle in {dt:.1f} s on the host, scaled to tokens of the {layers}-layer, "
                       f"{H}-head encode (codebook tables built once beforehand, {t_setup:.1f} s)"}
 
 
-def esm_report(st, timer, ms_step):
+def esm_report(st, ct, ms_step):
     S, T, H, d, layers, bits, m = (st[k] for k in ("S", "T", "H", "d", "layers", "bits", "m"))
     vec = S * T * H
     sign = st["variant"] == "turboesm"
     rec = 4 + (0 if sign else 4) + bits * d // 8 + m // 8
-    enc_ms, n = timer.mean_ms("encode_k")
-    encv_ms, _ = timer.mean_ms("encode_v")
-    kern = {"encode_k": {"ms": enc_ms, "launches": n, "alg_bytes": vec * (4 * d + rec), "units": vec},
-            "encode_v": {"ms": encv_ms, "alg_bytes": vec * (4 * d + rec), "units": vec}}
-    for k in kern.values():
-        k["GBps"] = k["alg_bytes"] / (k["ms"] * 1e-3) / 1e9
-        k["hbm_frac"] = k["GBps"] / HBM_PEAK_GBS
-    extra = {"encode_tokens_per_s": S * T / (ms_step * 1e-3), "encode_vectors_per_s": 2 * layers * vec / (ms_step * 1e-3),
+    kern = {"encode_k": {"alg_bytes": vec * (4 * d + rec), "units": vec, "unit": "vectors"},
+            "encode_v": {"alg_bytes": vec * (4 * d + rec), "units": vec, "unit": "vectors"}}
+    for name, k in kern.items():
+        k.update(ct[name])
+        _rate(k)
+    t_layer = (kern["encode_k"]["us"] + kern["encode_v"]["us"]) * 1e-6
+    extra = {"encode_tokens_per_s": S * T / (layers * t_layer),
+             "encode_vectors_per_s": 2 * vec / t_layer,
+             "step_tokens_per_s": S * T / (ms_step * 1e-3),
              "kv_bytes_fp32_per_sequence": 2 * layers * T * H * d * 4,
              "kv_bytes_packed_per_sequence": 2 * layers * T * H * rec,
              "kv_reduction_vs_fp32": (4 * d) / rec}
@@ -606,11 +770,11 @@ def esm_report(st, timer, ms_step):
                     "value_table": "calibrated per layer, original coordinates", "calibration_tokens": CALIB_TOKENS})
     else:
         cfg["qjl_rows"] = m
-    return S * T / (ms_step * 1e-3), "tokens/s", kern, "encode_k", extra, cfg
+    return extra["encode_tokens_per_s"], "tokens/s", kern, extra, cfg
 
 
 # ------------------------------------------------------------ vector search
-def setup_vsearch(torch, tq, synth):
+def setup_vsearch(torch, tq, synth, copies=1):
     n, nq, d, bits, m = 1_000_000, 1024, 1536, 2, 1536
     X = torch.empty((n, d), dtype=torch.float32, device="cuda")
     step = 65536
@@ -618,128 +782,173 @@ def setup_vsearch(torch, tq, synth):
         c = min(step, n - s0)
         X[s0:s0 + c] = torch.from_numpy(synth.vsearch_rows(0, s0, c)).cuda()
     Qh = synth.vsearch_rows(1, 0, nq)
-    st = {"n": n, "nq": nq, "d": d, "bits": bits, "m": m, "X": X.view(1, n, 1, d),
-          "Q": torch.from_numpy(Qh).cuda()[None], "Qh": Qh}
+    st = {"n": n, "nq": nq, "d": d, "bits": bits, "m": m, "Q": torch.from_numpy(Qh).cuda()[None], "Qh": Qh}
     st["ck"] = tq.Codebook(d, bits, m, "dense", seed=synth.K_SEED)
-    st["kp"] = tq.Packed(st["ck"], n)
     st["ws_e"] = torch.empty(tq.workspace_bytes(st["ck"], None, tq.TQ_OP_ENCODE, n), dtype=torch.uint8, device="cuda")
     st["ws_l"] = torch.empty(tq.workspace_bytes(st["ck"], None, tq.TQ_OP_LOGITS, 1, nq, 1, n, 10), dtype=torch.uint8,
                              device="cuda")
     st["sl"] = torch.tensor([n], dtype=torch.int32, device="cuda")
-    st["calls"] = [
-        ("encode_k", tq.encode_kv(st["ck"], None, st["X"], None, st["kp"], None, L_cap=n, workspace=st["ws_e"],
-                                  prepare=True)),
-        ("scan_topk", tq.attn_logits(st["ck"], st["Q"], st["kp"], 1, n, st["sl"], top_k=10, workspace=st["ws_l"],
-                                     prepare=True)[0]),
-    ]
+    Xs = _copies(X, copies)
+    st["rot"] = []
+    for c in range(copies):
+        kp = tq.Packed(st["ck"], n)
+        vals = torch.empty((1, nq, 10), dtype=torch.float32, device="cuda")
+        if c == 0:
+            st["X"], st["kp"] = Xs[0].view(1, n, 1, d), kp
+        st["rot"].append([
+            ("encode_k", tq.encode_kv(st["ck"], None, Xs[c].view(1, n, 1, d), None, kp, None, L_cap=n,
+                                      workspace=st["ws_e"], prepare=True)),
+            ("scan_topk", tq.attn_logits(st["ck"], st["Q"], kp, 1, n, st["sl"], top_k=10, out=vals,
+                                         workspace=st["ws_l"], prepare=True)[0]),
+        ])
+    st["calls"] = st["rot"][0]
     return st
 
 
-def vsearch_report(st, timer, ms_step):
+def vsearch_report(st, ct, ms_step):
     n, nq, d, bits, m = (st[k] for k in ("n", "nq", "d", "bits", "m"))
     rec = 8 + bits * d // 8 + m // 8
-    enc_ms, k = timer.mean_ms("encode_k")
-    scan_ms, _ = timer.mean_ms("scan_topk")
-    kern = {"encode_k": {"ms": enc_ms, "launches": k, "alg_bytes": n * (4 * d + rec), "units": n,
+    kern = {"encode_k": {"alg_bytes": n * (4 * d + rec), "units": n, "unit": "vectors",
                          "alg_tflop": 2.0 * n * d * (d + m) / 1e12},
-            "scan_topk": {"ms": scan_ms, "alg_bytes": n * rec, "units": n * nq,
+            "scan_topk": {"alg_bytes": n * rec, "units": n * nq, "unit": "scores",
                           "alg_tflop": 2.0 * n * nq * (d + m) / 1e12}}
-    for kk in kern.values():
-        kk["GBps"] = kk["alg_bytes"] / (kk["ms"] * 1e-3) / 1e9
-        kk["hbm_frac"] = kk["GBps"] / HBM_PEAK_GBS
-        kk["TFLOPs"] = kk["alg_tflop"] / (kk["ms"] * 1e-3)
-    extra = {"scan_scores_per_s": n * nq / (scan_ms * 1e-3), "index_vectors_per_s": n / (enc_ms * 1e-3)}
+    for name, k in kern.items():
+        k.update(ct[name])
+        _rate(k)
+        k["TFLOPs"] = k["alg_tflop"] / (k["us"] * 1e-6)
+    extra = {"scan_vectors_per_s": n / (kern["scan_topk"]["us"] * 1e-6),
+             "scan_scores_per_s": n * nq / (kern["scan_topk"]["us"] * 1e-6),
+             "index_vectors_per_s": n / (kern["encode_k"]["us"] * 1e-6),
+             "step_vectors_per_s": n / (ms_step * 1e-3)}
     cfg = {"workload": "vector search, 1e6 x 1536 unit vectors, 1024 queries, top-10", "bits": bits, "qjl_rows": m,
            "rotation": "dense Haar", "record_bytes": rec}
-    return n / (ms_step * 1e-3), "vectors/s", kern, max(kern, key=lambda x: kern[x]["ms"]), extra, cfg
+    return extra["scan_vectors_per_s"], "vectors/s", kern, extra, cfg
 
 
-def main():
-    args = parse()
+# ------------------------------------------------------------ main
+def roofline_of(name, k, rates):
+    if "TFLOPs" in k and name == "scan_topk":
+        r = {"bound": "mfma", "achieved": k["TFLOPs"], "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+             "frac": k["TFLOPs"] / FP32_PEAK_TFLOPS}
+    else:
+        r = {"bound": "hbm", "achieved": k["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": k["GBps"] / HBM_PEAK_GBS, "frac_of_measured_copy": k["GBps"] / rates["copy_GBps"],
+             "frac_of_measured_read": k["GBps"] / rates["read_GBps"]}
+    r["traffic"] = k.get("traffic_bytes")
+    r["kernel"] = name
+    r["launch_us"] = k["us"]
+    return r
+
+
+def main(argv=None):
+    args = parse(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         return 2
     import torch
-    import kv_cache_vector_05_amd as tq
-    import synth
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     torch.cuda.set_device(0)
+    if args.copy_calibrate:
+        # a device copy of known size: FETCH_SIZE / WRITE_SIZE of this run calibrate the counters
+        r = device_rates(torch, 1024, 3)
+        print(json.dumps({"device_copy_MiB": 1024, **r}), flush=True)
+        return 0
+    import kv_cache_vector_05_amd as tq
+    import synth
     wl = args.workload
-    print(f"[bench] setting up {wl}", file=sys.stderr, flush=True)
+    copies = max(1, args.copies) if args.cache_state != "hot" else 1
+    print(f"[bench] setting up {wl} ({copies} buffer copies)", file=sys.stderr, flush=True)
     if wl in ("llama8b", "llama70b", "llama8b-turboesm"):
-        st = setup_llama(torch, tq, synth, wl.split("-")[0], "turboesm" if wl.endswith("turboesm") else "qjl")
-        report = lambda t, ms: llama_report(st, t, ms)
+        st = setup_llama(torch, tq, synth, wl.split("-")[0], "turboesm" if wl.endswith("turboesm") else "qjl",
+                         copies, args.bits, args.qjl_rows)
+        report = llama_report
     elif wl in ("esm650m", "esm650m-turboesm"):
         st = setup_esm(torch, tq, synth, "turboesm" if wl.endswith("turboesm") else "qjl")
-        report = lambda t, ms: esm_report(st, t, ms)
+        report = esm_report
     elif wl == "vsearch":
-        st = setup_vsearch(torch, tq, synth)
-        report = lambda t, ms: vsearch_report(st, t, ms)
+        st = setup_vsearch(torch, tq, synth, copies)
+        report = vsearch_report
     elif wl == "llama8b-serve":
-        st = setup_serve(torch, tq, synth)
-        report = lambda t, ms: serve_report(st, t, ms)
+        st = setup_serve(torch, tq, synth, copies)
+        report = serve_report
     elif wl == "llama8b-fib":
-        st = setup_fib(torch, tq, synth)
-        report = lambda t, ms: fib_report(st, t, ms)
+        st = setup_fib(torch, tq, synth, copies)
+        report = fib_report
     else:
         raise SystemExit("tiny is a parity case, not a benchmark workload")
-    step = lambda t: run_calls(st, t)
+    nrot = len(st["rot"])
+    torch.cuda.synchronize()
+    # every buffer copy once (fills all records), then enough steps for the clock ramp
+    for i in range(nrot):
+        run_step(st, NoTimer(), i)
     torch.cuda.synchronize()
     if args.warmup is None:
-        # enough steps to cover the clock ramp under load (~0.3 s), at least 3,
-        # sized from the second step (the first carries one-time set-up)
-        step(NoTimer())
-        torch.cuda.synchronize()
         t0 = time.perf_counter()
-        step(NoTimer())
+        run_step(st, NoTimer(), 0)
         torch.cuda.synchronize()
         one = time.perf_counter() - t0
-        args.warmup = max(3, min(2000, int(0.3 / max(one, 1e-6))))
-        warm = args.warmup - 2
+        args.warmup = max(nrot + 1, min(2000, int(0.3 / max(one, 1e-6))))
+        warm = args.warmup - nrot - 1
     else:
-        warm = args.warmup
+        warm = max(0, args.warmup - nrot)
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(warm):
-        step(NoTimer())
+    for i in range(warm):
+        run_step(st, NoTimer(), i)
     torch.cuda.synchronize()
-    timer = Timer(torch, events=args.steps * len(st["calls"]))
+    timer = StepTimer(torch, events=args.steps * len(st["rot"][0]))
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(timer)
+    for i in range(args.steps):
+        run_step(st, timer, i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    value, unit, kern, dom, extra, cfg = report(timer, ms_step)
-    dk = kern[dom]
+    print(f"[bench] timing each call ({args.cache_state}, {args.reps} repeats)", file=sys.stderr, flush=True)
+    ct = time_calls(torch, st, args.cache_state, args.reps)
+    for name in ct:
+        ct[name]["in_step_us"] = timer.mean_us(name)
+    print("[bench] device copy, fill and read rates", file=sys.stderr, flush=True)
+    rates = device_rates(torch)
+    value, unit, kern, extra, cfg = report(st, ct, ms_step)
     for name, k in kern.items():
         k["traffic_bytes"] = measured_traffic(wl, name)
-    if "TFLOPs" in dk and dom == "scan_topk":
-        roof = {"bound": "mfma", "achieved": dk["TFLOPs"], "peak": 157.3, "unit": "TFLOP/s",
-                "frac": dk["TFLOPs"] / 157.3, "traffic": dk["traffic_bytes"], "kernel": dom}
-    else:
-        roof = {"bound": "hbm", "achieved": dk["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": dk["GBps"] / HBM_PEAK_GBS, "traffic": dk["traffic_bytes"], "kernel": dom}
+        k["frac_of_measured_copy"] = k["GBps"] / rates["copy_GBps"]
+    dom = max(kern, key=lambda x: kern[x]["us"])
+    roof = roofline_of(dom, kern[dom], rates)
+    cores, blas = host_cores()
     line = {"metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
-            "vs_baseline": None, "dtype": "f32", "data": "synthetic", "config": cfg, "roofline": roof,
-            "kernels": kern, **extra}
-    if not args.no_cpu_baseline and wl == "llama8b-fib":
+            "vs_baseline": None, "dtype": "f32", "data": "synthetic", "config": cfg, "roofline": roof}
+    if "logits" in kern:
+        line["logits_roofline"] = roofline_of("logits", kern["logits"], rates)
+    line.update({"timing": {"cache_state": args.cache_state, "buffer_copies": nrot, "repeats": args.reps,
+                            "per_call": "median over repeats of back-to-back launches per event pair",
+                            "step": "host clock over the timed steps between device synchronisations"},
+                 "device_rates": rates, "kernels": kern, **extra})
+    if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle on a sample)", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline_fib(st)
-    elif not args.no_cpu_baseline and wl == "llama8b-serve":
-        print("[bench] cpu baseline (oracle on a sample)", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline_serve(st)
-    elif not args.no_cpu_baseline and wl in ("llama8b", "llama70b", "llama8b-turboesm"):
-        print("[bench] cpu baseline (oracle on a sample)", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline_llama(st, args.cpu_sample or 1 << 22)
-    elif not args.no_cpu_baseline and wl in ("esm650m", "esm650m-turboesm"):
-        print("[bench] cpu baseline (oracle on a sample)", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline_esm(st)
+        if wl == "llama8b-fib":
+            cb = cpu_baseline_fib(st)
+        elif wl == "llama8b-serve":
+            cb = cpu_baseline_serve(st)
+        elif wl in ("esm650m", "esm650m-turboesm"):
+            cb = cpu_baseline_esm(st)
+        elif wl == "vsearch":
+            cb = None
+        else:
+            cb = cpu_baseline_llama(st, args.cpu_sample or 1 << 22)
+        if cb is not None:
+            cb["cores"] = blas
+            cb["affinity_cores"] = cores
+            cb["blas_threads"] = blas
+            print("[bench] cpu baseline: tiny configuration on 1 and on all threads", file=sys.stderr, flush=True)
+            cb["tiny_one_thread"] = cpu_tiny(1)
+            cb["tiny_all_threads"] = cpu_tiny(blas)
+            line["cpu_baseline"] = cb
     print(json.dumps(line), flush=True)
     return 0
 
