@@ -25,7 +25,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libtq.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["tq_host.cpp", "tq_gemm.hip", "tq_encode.hip", "tq_attn.hip", "tq_logits.hip", "tq_decode.hip",
+SOURCES = ["tq_host.cpp", "tq_gemm.hip", "tq_encode.hip", "tq_attn.hip", "tq_qprep.hip", "tq_scan.hip", "tq_decode.hip",
            "tq_vq.hip"]
 ARCH = "gfx950"
 
@@ -48,7 +48,7 @@ def _compile(src: str, verbose: bool) -> str:
     cmd = [hipcc()] + common_flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd += ["-ffp-contract=off"]
-    if src in ("tq_logits.hip", "tq_encode.hip", "tq_decode.hip"):
+    if src in ("tq_qprep.hip", "tq_scan.hip", "tq_encode.hip", "tq_decode.hip"):
         # keep MFMA accumulators in architectural VGPRs (no AGPR copies in the loop)
         cmd += ["-mllvm", "--amdgpu-mfma-vgpr-form"]
     if verbose:

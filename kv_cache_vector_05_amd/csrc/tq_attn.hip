@@ -859,8 +859,8 @@ size_t logits_workspace_bytes(const tq_codebook* ck, int64_t B, int Hq, int h_kv
         return bytes;
     }
     if (!ck->dense) {
-        size_t bytes = logits_mfma_supported(ck) ? align256(qdigits_workspace_bytes(ck, (int64_t)rows))
-                                                 : align256(rows * (d + m) * 4);
+        size_t bytes = scan_supported(ck) ? align256(qdigits_workspace_bytes(ck, (int64_t)rows))
+                                          : align256(rows * (d + m) * 4);
         if (top_k) bytes += align256(rows * chunk * 4);
         return bytes;
     }
@@ -920,15 +920,15 @@ hipError_t launch_logits(const tq_codebook* ck, const tq_packed& k, const AttnAr
         }
         return hipSuccess;
     }
-    if (!ck->dense && logits_mfma_supported(ck)) {
+    if (!ck->dense && scan_supported(ck)) {
         const QDigits qd = carve_qdigits(ck, ws, rows);
         float* scores = reinterpret_cast<float*>(ws + align256(qdigits_workspace_bytes(ck, rows)));
         hipError_t e = launch_qdigits(ck, a, qd, stream);
         if (e != hipSuccess) return e;
-        if (a.top_k == 0) return launch_logits_mfma(ck, k, a, qd, 0, a.L_cap, a.out, a.L_cap, 0, stream);
+        if (a.top_k == 0) return launch_scan(ck, k, a, qd, 0, a.L_cap, a.out, a.L_cap, 0, stream);
         for (int k0 = 0; k0 < a.L_cap; k0 += chunk) {
             const int cnt = std::min(chunk, a.L_cap - k0);
-            e = launch_logits_mfma(ck, k, a, qd, k0, cnt, scores, chunk, k0, stream);
+            e = launch_scan(ck, k, a, qd, k0, cnt, scores, chunk, k0, stream);
             if (e != hipSuccess) return e;
             TopK tk{};
             tk.scores = scores;

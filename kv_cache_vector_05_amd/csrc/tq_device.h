@@ -1,4 +1,4 @@
-// Device-side building blocks shared by the logit scan (tq_logits.hip) and
+// Device-side building blocks shared by the logit scan (tq_scan.hip) and
 // the fused decode (tq_decode.hip): code unpacking into v_perm selectors,
 // level-digit lookup, sign-bit spreading, and the integer-MFMA logit of one
 // 16-key tile.

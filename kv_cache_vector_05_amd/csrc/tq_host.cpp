@@ -801,14 +801,14 @@ static tq_status codebook_create(const tq_spec* spec, const tq_draws* draws, con
                         out[base + 64 * 8] = lo;
                     }
     }
-    // one device block: levels[16] | thresholds[16] | sigma[d] or rot[d*d] | sketch | sketch_mfma | mu |
-    // candidate grid (the sign correction's S = I is never read on the device)
+    // one device block: levels[16] | thresholds[16] | sigma[d] or rot[d*d] | sketch | sketch_mfma |
+    // sketch transposed | mu | candidate grid (the sign correction's S = I is never read on the device)
     const size_t n_lv = vq ? std::max<size_t>(16, cb->levels.size()) : 16, n_th = 16;
     const size_t n_rot = dense ? (size_t)d * d : (size_t)d;
     const size_t n_sk = sign ? 0 : (size_t)m * d;
     const size_t n_mu_dev = cb->mu.size();
     const size_t n_grid = cb->vq_grid.size();
-    const size_t total = n_lv + n_th + n_rot + 2 * n_sk + n_mu_dev + n_grid;
+    const size_t total = n_lv + n_th + n_rot + 3 * n_sk + n_mu_dev + n_grid;
     std::vector<float> host(total, 0.0f);
     std::memcpy(host.data(), cb->levels.data(), cb->levels.size() * 4);
     std::memcpy(host.data() + n_lv, cb->thresholds.data(), cb->thresholds.size() * 4);
@@ -816,9 +816,12 @@ static tq_status codebook_create(const tq_spec* spec, const tq_draws* draws, con
     if (n_sk) {
         std::memcpy(host.data() + n_lv + n_th + n_rot, cb->sketch.data(), n_sk * 4);
         std::memcpy(host.data() + n_lv + n_th + n_rot + n_sk, sk_mfma.data(), n_sk * 4);
+        float* skt = host.data() + n_lv + n_th + n_rot + 2 * n_sk;
+        for (int l = 0; l < m; ++l)
+            for (int i = 0; i < d; ++i) skt[(size_t)i * m + l] = cb->sketch[(size_t)l * d + i];
     }
-    if (n_mu_dev) std::memcpy(host.data() + n_lv + n_th + n_rot + 2 * n_sk, cb->mu.data(), n_mu_dev * 4);
-    if (n_grid) std::memcpy(host.data() + n_lv + n_th + n_rot + 2 * n_sk + n_mu_dev, cb->vq_grid.data(), n_grid * 4);
+    if (n_mu_dev) std::memcpy(host.data() + n_lv + n_th + n_rot + 3 * n_sk, cb->mu.data(), n_mu_dev * 4);
+    if (n_grid) std::memcpy(host.data() + n_lv + n_th + n_rot + 3 * n_sk + n_mu_dev, cb->vq_grid.data(), n_grid * 4);
     if (const char* f = std::getenv("TQ_TEST_FAIL_ALLOC"); f && std::atoi(f) == 1) {
         delete cb;
         return fail(TQ_ENOMEM, "allocation failure forced by TQ_TEST_FAIL_ALLOC");
@@ -843,9 +846,10 @@ static tq_status codebook_create(const tq_spec* spec, const tq_draws* draws, con
     if (n_sk) {
         cb->dev.sketch = base + n_lv + n_th + n_rot;
         cb->dev.sketch_mfma = base + n_lv + n_th + n_rot + n_sk;
+        cb->dev.sketch_t = base + n_lv + n_th + n_rot + 2 * n_sk;
     }
-    if (n_mu_dev) cb->dev.mu = base + n_lv + n_th + n_rot + 2 * n_sk;
-    if (n_grid) cb->dev.vq_grid = reinterpret_cast<uint32_t*>(base + n_lv + n_th + n_rot + 2 * n_sk + n_mu_dev);
+    if (n_mu_dev) cb->dev.mu = base + n_lv + n_th + n_rot + 3 * n_sk;
+    if (n_grid) cb->dev.vq_grid = reinterpret_cast<uint32_t*>(base + n_lv + n_th + n_rot + 3 * n_sk + n_mu_dev);
     hipStream_t s = (hipStream_t)stream;
     e = hipMemcpyAsync(cb->block, host.data(), total * sizeof(float), hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);  // host staging buffer is local

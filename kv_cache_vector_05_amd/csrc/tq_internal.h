@@ -21,6 +21,7 @@ struct DeviceTables {
     float* rot = nullptr;         // [d*d]  dense Pi, row-major (y = Pi u)
     float* sketch = nullptr;      // [m*d]  S, row-major
     float* sketch_mfma = nullptr; // [m*d]  S as fp16 hi/lo pairs in the encode kernel's MFMA operand order
+    float* sketch_t = nullptr;    // [d*m]  S transposed (column l of S^T is row l of S)
     float* mu = nullptr;          // [n_mu] mean residual magnitudes (sign correction)
     uint32_t* vq_grid = nullptr;  // [kVqGrid^2] candidate codewords per cell (vector codebooks, N <= 64)
 };
@@ -149,7 +150,7 @@ size_t logits_workspace_bytes(const tq_codebook* ck, int64_t B, int Hq, int h_kv
 size_t decode_workspace_bytes(const tq_codebook* ck, const tq_codebook* cv, int64_t B, int Hq,
                               int h_kv, int L_cap);
 
-// Fixed-point digit form of prepared queries (tq_logits.hip).
+// Fixed-point digit form of prepared queries (tq_qprep.hip).
 struct QDigits {
     float* qp;      // [rows][d]   q' = Pi RoPE(q)
     float* s;       // [rows][m]   s = S q'
@@ -162,9 +163,10 @@ bool logits_mfma_supported(const tq_codebook* ck);
 size_t qdigits_workspace_bytes(const tq_codebook* ck, int64_t rows);
 QDigits carve_qdigits(const tq_codebook* ck, void* ws, int64_t rows);
 hipError_t launch_qdigits(const tq_codebook* ck, const AttnArgs& a, const QDigits& q, hipStream_t stream);
-hipError_t launch_logits_mfma(const tq_codebook* ck, const tq_packed& k, const AttnArgs& a, const QDigits& q,
-                              int k0, int klen, float* out, int64_t ld, int col0, hipStream_t stream);
-
+// the integer-MFMA logit scan (tq_scan.hip) over queries prepared by launch_qdigits
+bool scan_supported(const tq_codebook* ck);
+hipError_t launch_scan(const tq_codebook* ck, const tq_packed& k, const AttnArgs& a, const QDigits& q, int k0,
+                       int klen, float* out, int64_t ld, int col0, hipStream_t stream);
 // Fused decode on the integer matrix cores (tq_decode.hip): partials of
 // [B*Hq][nsplit][2 + d + m] floats (max, sum, A_y, A_z) for the merge kernel.
 bool decode_mfma_supported(const tq_codebook* ck, const tq_codebook* cv);

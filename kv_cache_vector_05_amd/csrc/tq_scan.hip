@@ -1,0 +1,434 @@
+// Attention-logit scan from packed keys on the integer matrix cores
+// (tambur post: logits straight from quantised keys; iaemfoco post,
+// "TurboQuant: Uma Nova Abordagem" and itstec post, "Por dentro do processo de
+// compressao KV": the one-bit QJL correction):
+//     logit = nu ( <q', t[c]> + sqrt(pi/2)/m * gamma * <s, z> ),  q' = Pi RoPE(q), s = S q',
+// or, with the sign correction (TurboESM summary, technical section 2),
+//     logit = nu ( <q', t[c]> + mu_head <q', z> )  (S = I, so s = q').
+//
+// Exact integer arithmetic on v_mfma_i32_16x16x64_i8: rows = (query, digit
+// of q'), columns = 16 keys, K = 64 coordinates.  The queries arrive prepared
+// (tq_qprep.hip: q' and s as four balanced base-128 digits with one scale per
+// query); the levels' three base-256 digits come from the packed codes by one
+// v_perm per four coordinates; the sign bits become 0/1 bytes through a
+// 256-entry LDS table.  The digit sums are combined exactly in int32 pairs
+// and fp64, and only the logit is rounded to fp32.  Lane l owns key l % 16
+// and coordinate quarter l / 16, and holds the logit of (query l / 16, key
+// l % 16) of each four-query row tile.
+//
+// One workgroup (four waves) serves one KV head of one sequence, up to 4 NRT
+// of its query heads and a contiguous run of keys, sized so that the whole
+// grid is resident at once.  Records are read with buffer loads whose
+// per-tile advance is a scalar offset (no vector instructions on addresses);
+// every load is unconditional, so each wave keeps its next four tiles of
+// records in flight behind the one it computes.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+
+#include "tq_device.h"
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+using dev::intx4;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+
+constexpr int kRsrcWord3 = 0x00020000;  // buffer resource word 3 for gfx9: 32-bit elements, no swizzle
+
+// buffer resource over [base, base + bytes); loads past the end return 0
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0xFFFFFFFFll ? 0xFFFFFFFFu : (uint32_t)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, kRsrcWord3);
+}
+
+struct ScanArgs {
+    const int8_t* qd;       // prepared queries (tq_qprep.hip): digit rows of q'
+    const int8_t* sd;       // digit rows of s in MFMA slot order
+    const float* scale;     // per query: shift(q'), shift(s), sum of the fixed-point s
+    int32_t sdw;
+    const int32_t* seq_len;
+    const float* norm;
+    const float* rnorm;
+    const uint32_t* codes;
+    const uint32_t* signs;
+    int64_t cap;            // records in each plane
+    int32_t Hq, h_kv, L_cap, m, ngroups, tiles_per_wave, k0, klen;
+    float* out;
+    int64_t ld;
+    int32_t col0;
+    uint32_t tdig[8];
+    int32_t lvl_shift;
+    double cq;              // scale of the correction term
+    const float* mu;        // sign correction: mu per KV head (stride mu_stride)
+    int32_t mu_stride;
+    const int32_t* pages;   // paged records: [B][max_pages], pages of page_size slots
+    int32_t page_size, max_pages;
+    int64_t n_pages;
+    dev::FastDiv div_page;
+};
+
+template <int D, int BITS, int NRT, int NCS, bool PAGED>
+__global__ __launch_bounds__(256) void scan_kernel(ScanArgs p) {
+    using Q = dev::Quarter<D, BITS>;
+    constexpr int R = 4 * NRT;       // query rows of the workgroup
+    constexpr int NC = Q::LPG / 16;  // K = 64 chunks over the lane's coordinates
+    __shared__ u32x2 stab[256];      // bits of a byte -> eight 0/1 bytes
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform: scalar addresses
+    const int n = lane & 15;
+    const int qk = lane >> 4;
+    const int grp = blockIdx.x % p.ngroups;
+    const int64_t bk = blockIdx.x / p.ngroups;
+    const int b = (int)(bk / p.h_kv);
+    const int kh = (int)(bk % p.h_kv);
+    const int G = p.Hq / p.h_kv;
+    const int64_t rowbase = (int64_t)b * p.Hq + (int64_t)kh * G;
+    const int gq0 = grp * R;
+
+    const int sl = dev::clamp_len(p.seq_len, b, p.L_cap);
+    const int kend = min(sl, p.k0 + p.klen);
+    // a workgroup without keys leaves at once (before any barrier)
+    if (p.k0 + (int)blockIdx.y * 4 * p.tiles_per_wave * 16 >= kend) return;
+    const int kbeg = p.k0 + ((int)blockIdx.y * 4 + wave) * p.tiles_per_wave * 16;
+    const int ntile = __builtin_amdgcn_readfirstlane(max(0, min(p.tiles_per_wave, (kend - kbeg + 15) / 16)));
+    const int nfull = __builtin_amdgcn_readfirstlane(max(0, min(p.tiles_per_wave, (kend - kbeg) / 16)));
+    const int mw = p.m >> 5;
+    const int per = p.m >> 2;  // sketch rows per lane group: 8, 16 or 32
+
+    // ---- record loads (per lane: its key's quarter of the code words, the
+    // sign word holding its sketch rows, nu, gamma)
+    constexpr int CW = Q::CW;
+    const uint32_t vo_c = (uint32_t)(n * CW + Q::word0(qk)) * 4u;
+    const uint32_t vo_s = (uint32_t)(n * mw + ((qk * per) >> 5)) * 4u;
+    const uint32_t vo_n = (uint32_t)n * 4u;
+    const bool g_per_key = p.mu == nullptr;
+    const float g_head = g_per_key ? 0.0f : p.mu[kh * p.mu_stride];
+    const int64_t rec_w = bk * p.L_cap + kbeg;  // contiguous records: the wave's first key
+    __amdgpu_buffer_rsrc_t rc, rs_, rn, rg;
+    if constexpr (!PAGED) {
+        rc = make_rsrc(p.codes + rec_w * CW, (p.cap - rec_w) * CW * 4);
+        rs_ = make_rsrc(p.signs + rec_w * mw, (p.cap - rec_w) * mw * 4);
+        rn = make_rsrc(p.norm + rec_w, (p.cap - rec_w) * 4);
+        rg = make_rsrc(p.rnorm + rec_w, (p.cap - rec_w) * 4);
+    }
+    struct Raw {
+        uint32_t W[Q::NW];
+        uint32_t sg;
+        float nu, gm;
+        int64_t rec;  // paged: the tile's first record
+    };
+    // code and sign words of a tile (and, for paged records, its page)
+    auto fetch_codes = [&](int tile, Raw& r) {
+        uint32_t so_c, so_s;
+        if constexpr (PAGED) {
+            // a 16-key tile lies in one page (pages hold a multiple of 64 slots)
+            const int key0 = kbeg + tile * 16;
+            const uint32_t j = p.div_page.div((uint32_t)key0);
+            int64_t pg = p.pages[(int64_t)b * p.max_pages + j];
+            pg = pg < 0 ? 0 : (pg >= p.n_pages ? p.n_pages - 1 : pg);
+            r.rec = (pg * p.h_kv + kh) * p.page_size + (key0 - (int64_t)j * p.page_size);
+            rc = make_rsrc(p.codes + r.rec * CW, (p.cap - r.rec) * CW * 4);
+            rs_ = make_rsrc(p.signs + r.rec * mw, (p.cap - r.rec) * mw * 4);
+            so_c = so_s = 0;
+        } else {
+            so_c = (uint32_t)tile * 16u * CW * 4u;
+            so_s = (uint32_t)tile * 16u * (uint32_t)mw * 4u;
+        }
+        if constexpr (Q::NW == 3) {
+            const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(rc, vo_c, so_c, 0);
+            r.W[0] = v.x;
+            r.W[1] = v.y;
+            r.W[2] = v.z;
+        } else if constexpr (Q::NW == 2 && Q::ALIGNED) {
+            const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rc, vo_c, so_c, 0);
+            r.W[0] = v.x;
+            r.W[1] = v.y;
+        } else if constexpr (Q::ALIGNED) {
+#pragma unroll
+            for (int i = 0; i < Q::NW; ++i) r.W[i] = __builtin_amdgcn_raw_buffer_load_b32(rc, vo_c + 4u * i, so_c, 0);
+        } else {
+            // the quarter straddles words: NW words from word0, the last clamped
+            // into the record, shifted into place
+            const int w0 = Q::word0(qk);
+#pragma unroll
+            for (int i = 0; i < Q::NW; ++i)
+                r.W[i] = __builtin_amdgcn_raw_buffer_load_b32(rc, (uint32_t)(n * CW + w0 + min(i, CW - 1 - w0)) * 4u,
+                                                              so_c, 0);
+            const int sh = (Q::BPG * qk) & 31;
+#pragma unroll
+            for (int i = 0; i + 1 < Q::NW; ++i) r.W[i] = __builtin_amdgcn_alignbit(r.W[i + 1], r.W[i], sh);
+        }
+        r.sg = NCS > 0 ? __builtin_amdgcn_raw_buffer_load_b32(rs_, vo_s, so_s, 0) : 0u;
+    };
+    // nu and gamma of a tile (loaded after the tile's slot has been combined)
+    auto fetch_scalars = [&](int tile, Raw& r) {
+        uint32_t so_n;
+        if constexpr (PAGED) {
+            rn = make_rsrc(p.norm + r.rec, (p.cap - r.rec) * 4);
+            rg = make_rsrc(p.rnorm + r.rec, (p.cap - r.rec) * 4);
+            so_n = 0;
+        } else {
+            so_n = (uint32_t)tile * 64u;
+        }
+        r.nu = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rn, vo_n, so_n, 0));
+        if (NCS > 0 && g_per_key) r.gm = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, vo_n, so_n, 0));
+        else r.gm = g_head;
+    };
+    // ---- the prepared queries: A rows (query 4rt + (lane&15)/4, digit
+    // lane&3; a row past the group repeats the last query and is never
+    // stored) and the scales of the lane's output query 4rt + qk.  Loaded
+    // before the first records: loads complete in order, so waiting for
+    // these leaves the records in flight.
+    intx4 aq[NRT][NC];
+    intx4 as[NRT][NCS > 0 ? NCS : 1];
+    float sc[NRT][3];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+        const int64_t drow = (rowbase + min(gq0 + 4 * rt + ((lane & 15) >> 2), G - 1)) * 4 + (lane & 3);
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            aq[rt][c] = *reinterpret_cast<const intx4*>(p.qd + drow * D + qk * Q::LPG + 16 * c);
+#pragma unroll
+        for (int cs = 0; cs < NCS; ++cs)
+            as[rt][cs] = *reinterpret_cast<const intx4*>(p.sd + drow * p.sdw + (qk * NCS + cs) * 16);
+        const int64_t orow = rowbase + min(gq0 + 4 * rt + qk, G - 1);
+#pragma unroll
+        for (int k = 0; k < 3; ++k) sc[rt][k] = p.scale[orow * 3 + k];
+    }
+    // Every record fetch is unconditional: a tile past the wave's last
+    // reloads the last one (a cache hit), so each loop step issues the same
+    // loads and the waits for a tile's data leave the later tiles' in flight.
+    const auto clampt = [&](int tile) { return max(0, min(tile, ntile - 1)); };
+    Raw raw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        fetch_codes(clampt(i), raw[i]);
+        fetch_scalars(clampt(i), raw[i]);
+    }
+    {
+        const uint32_t v = (uint32_t)t;  // 256 threads: one table entry each
+        stab[t] = u32x2{dev::spread4(v), dev::spread4(v >> 4)};
+    }
+    __syncthreads();
+    double qscale[NRT], zk[NRT], zc[NRT];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+        qscale[rt] = ldexp(1.0, -p.lvl_shift - (int)sc[rt][0]);
+        const double c = NCS > 0 ? p.cq : 0.0;
+        zk[rt] = 2.0 * c * ldexp(1.0, -(int)sc[rt][1]);
+        zc[rt] = c * (double)sc[rt][2];
+    }
+    uint32_t tdig[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tdig[i] = p.tdig[i];
+
+    // ---- output: row (rowbase + gq0 + 4rt + qk), column key - col0
+    const int g_lane = gq0 + qk;
+    __amdgpu_buffer_rsrc_t ro = make_rsrc(p.out + (rowbase + gq0) * p.ld + (kbeg - p.col0), (int64_t)0xFFFFFFFF);
+    const bool rows_full = gq0 + R <= G;
+
+    struct Acc {
+        intx4 y[NRT][3];
+        intx4 z[NRT];
+    };
+    auto mma = [&](const Raw& r, Acc& A) {
+        intx4 bd[NC][3];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+#pragma unroll
+            for (int sg = 0; sg < 4; ++sg) {
+                const uint32_t sel = Q::sel(r.W, 4 * c + sg, qk);
+#pragma unroll
+                for (int bb = 0; bb < 3; ++bb) bd[c][bb][sg] = (int)dev::lut4(tdig, bb, sel);
+            }
+        }
+        intx4 bz[NCS > 0 ? NCS : 1];
+        if constexpr (NCS > 0) {
+#pragma unroll
+            for (int cs = 0; cs < NCS; ++cs) {
+                uint32_t x = r.sg >> ((qk * per + 16 * cs) & 31);
+                if (per - 16 * cs < 16) x &= (1u << (per - 16 * cs)) - 1u;  // 8 rows: one byte
+                const u32x2 lo = stab[x & 0xFFu];
+                const u32x2 hi = stab[(x >> 8) & 0xFFu];
+                bz[cs] = intx4{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
+            }
+        }
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+#pragma unroll
+            for (int bb = 0; bb < 3; ++bb) A.y[rt][bb] = intx4{0, 0, 0, 0};
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+#pragma unroll
+                for (int bb = 0; bb < 3; ++bb)
+                    A.y[rt][bb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[rt][c], bd[c][bb], A.y[rt][bb], 0, 0, 0);
+            A.z[rt] = intx4{0, 0, 0, 0};
+#pragma unroll
+            for (int cs = 0; cs < NCS; ++cs)
+                A.z[rt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(as[rt][cs], bz[cs], A.z[rt], 0, 0, 0);
+        }
+    };
+    // logit of (query 4rt + qk, key n) from its digit sums: y[b][a] is digit a
+    // of q' (weight 128^(3-a)) times digit b of the level (weight 256^(2-b));
+    // pairs of q' digits combine exactly in int32 (|y| <= 2^20)
+    auto finish = [&](const Acc& A, float nu, float gm, int tile) {
+        const bool key_ok = tile < nfull || kbeg + tile * 16 + n < kend;
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+            double V = 0.0;
+#pragma unroll
+            for (int bb = 0; bb < 3; ++bb) {
+                const intx4& y = A.y[rt][bb];
+                const double h = (double)(y[0] * 128 + y[1]);
+                const double l = (double)(y[2] * 128 + y[3]);
+                V = fma(V, 256.0, fma(h, 16384.0, l));
+            }
+            double lg = V * qscale[rt];
+            if constexpr (NCS > 0) {
+                // sum_l s_l z_l = 2 sum_l s_l bit_l - sum_l s_l
+                const intx4& z = A.z[rt];
+                const double Z = fma((double)(z[0] * 128 + z[1]), 16384.0, (double)(z[2] * 128 + z[3]));
+                lg = fma((double)gm, fma(Z, zk[rt], -zc[rt]), lg);
+            }
+            const float v = (float)lg * nu;
+            if ((rows_full && tile < nfull) || (key_ok && g_lane + 4 * rt < G))
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ro,
+                                                      (uint32_t)(((int64_t)(qk + 4 * rt) * p.ld + n) * 4),
+                                                      (uint32_t)tile * 64u, 0);
+        }
+    };
+    // One tile per step: its MFMAs, then its slot refilled with the tile
+    // four ahead (code and sign words first, as soon as the MFMAs have read
+    // them; nu and gamma once the tile is combined).  A tile past the
+    // wave's last computes on a reloaded tile and stores nothing (the launch
+    // gives waves multiples of four tiles, so only the last wave of a row
+    // does this).
+    auto step = [&](int tile, int s0) {
+        Acc a0;
+        mma(raw[s0], a0);
+        fetch_codes(clampt(tile + 4), raw[s0]);
+        finish(a0, raw[s0].nu, raw[s0].gm, tile);
+        fetch_scalars(clampt(tile + 4), raw[s0]);
+    };
+    for (int tile = 0; tile < ntile; tile += 4) {
+        step(tile, 0);
+        step(tile + 1, 1);
+        step(tile + 2, 2);
+        step(tile + 3, 3);
+    }
+}
+
+using ScanFn = void (*)(ScanArgs);
+
+template <int D, int BITS, int NRT, bool PG>
+ScanFn pick_ncs(int m) {
+    switch (m) {
+        case 0: return scan_kernel<D, BITS, NRT, 0, PG>;
+        case 32:
+        case 64: return scan_kernel<D, BITS, NRT, 1, PG>;
+        case 128: return scan_kernel<D, BITS, NRT, 2, PG>;
+    }
+    return nullptr;
+}
+template <int D, int BITS, bool PG>
+ScanFn pick_nrt(int nrt, int m) {
+    if (nrt == 1) return pick_ncs<D, BITS, 1, PG>(m);
+    if (nrt == 2) return pick_ncs<D, BITS, 2, PG>(m);
+    if (nrt == 4) return pick_ncs<D, BITS, 4, PG>(m);
+    return nullptr;
+}
+template <int D, bool PG>
+ScanFn pick_bits(int bits, int nrt, int m) {
+    switch (bits) {
+        case 1: return pick_nrt<D, 1, PG>(nrt, m);
+        case 2: return pick_nrt<D, 2, PG>(nrt, m);
+        case 3: return pick_nrt<D, 3, PG>(nrt, m);
+    }
+    return nullptr;
+}
+
+int64_t resident_blocks(const void* fn) {
+    static thread_local const void* last_fn = nullptr;
+    static thread_local int64_t last = 0;
+    if (fn == last_fn) return last;
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, 0) != hipSuccess || per_cu < 1)
+        return 1024;
+    last_fn = fn;
+    last = (int64_t)cus * per_cu;
+    return last;
+}
+
+}  // namespace
+
+bool scan_supported(const tq_codebook* ck) {
+    const int m = ck->spec.m;
+    return !ck->dense && ck->spec.block < 2 && ck->spec.bits <= 3 && (ck->spec.d == 64 || ck->spec.d == 128) &&
+           (m == 0 || m == 32 || m == 64 || m == 128);
+}
+
+hipError_t launch_scan(const tq_codebook* ck, const tq_packed& k, const AttnArgs& a, const QDigits& q, int k0,
+                       int klen, float* out, int64_t ld, int col0, hipStream_t stream) {
+    const int G = a.Hq / a.h_kv;
+    const int nrt = G <= 4 ? 1 : (G <= 8 ? 2 : 4);
+    const int ngroups = (G + 4 * nrt - 1) / (4 * nrt);
+    const bool paged = a.pages.table != nullptr;
+    const int d = ck->spec.d, bits = ck->spec.bits, m = ck->spec.m;
+    ScanFn fn = nullptr;
+    if (d == 64) fn = paged ? pick_bits<64, true>(bits, nrt, m) : pick_bits<64, false>(bits, nrt, m);
+    else if (d == 128) fn = paged ? pick_bits<128, true>(bits, nrt, m) : pick_bits<128, false>(bits, nrt, m);
+    if (!fn) return hipErrorInvalidValue;
+    ScanArgs p{};
+    p.qd = q.qd;
+    p.sd = q.sd;
+    p.scale = q.scale;
+    p.sdw = q.sdw;
+    p.seq_len = a.seq_len;
+    p.norm = k.norm;
+    p.rnorm = k.rnorm;
+    p.codes = k.codes;
+    p.signs = k.signs;
+    p.cap = paged ? a.pages.n_pages * a.h_kv * (int64_t)a.pages.size : (int64_t)a.B * a.h_kv * a.L_cap;
+    p.Hq = a.Hq;
+    p.h_kv = a.h_kv;
+    p.L_cap = a.L_cap;
+    p.m = m;
+    p.ngroups = ngroups;
+    p.k0 = k0;
+    p.klen = klen;
+    p.out = out;
+    p.ld = ld;
+    p.col0 = col0;
+    for (int i = 0; i < 8; ++i) p.tdig[i] = ck->lvl_digits[i];
+    p.lvl_shift = ck->lvl_shift;
+    p.cq = corr_scale(ck);
+    const MuRef mr = mu_ref(ck);
+    p.mu = mr.ptr;
+    p.mu_stride = mr.stride;
+    p.pages = a.pages.table;
+    p.page_size = a.pages.size;
+    p.max_pages = a.pages.max_pages;
+    p.n_pages = a.pages.n_pages;
+    p.div_page = dev::FastDiv((uint32_t)(a.pages.size > 0 ? a.pages.size : 1));
+    // work per wave sized so that the whole grid is resident at once
+    const int64_t gx = (int64_t)a.B * a.h_kv * ngroups;
+    const int64_t tiles_row = (klen + 15) / 16;
+    if (gx == 0 || tiles_row == 0) return hipSuccess;
+    const int64_t resident = resident_blocks((const void*)fn);
+    const int64_t gy_want = std::max<int64_t>(1, (resident + gx - 1) / gx);
+    // a multiple of four tiles per wave (the loop's step)
+    p.tiles_per_wave = (int)(((tiles_row + 4 * gy_want - 1) / (4 * gy_want) + 3) / 4 * 4);
+    const int64_t gy = (tiles_row + 4 * (int64_t)p.tiles_per_wave - 1) / (4 * (int64_t)p.tiles_per_wave);
+    hipLaunchKernelGGL(fn, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace tq
