@@ -693,6 +693,123 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeK p) {
     }
 }
 
+// The same merge for m in {0, 32, 64, 128}, arranged for latency (one
+// workgroup per query row, few rows, so the loads' round trips dominate):
+// every load that does not depend on another is issued at once - the
+// thread's share of S (thread (kh, c) sums rows [kh m/(256/d), ...) of
+// column c), the split maxima, and per 64 splits the thread's column of the
+// partials - and the inverse Walsh-Hadamard transform runs in wave 0's
+// registers (lane l holds coordinates l + 64 v) instead of through barriers.
+template <int D, int M>
+__global__ __launch_bounds__(256) void decode_merge_fast_kernel(MergeK p) {
+    constexpr int VPL = D / 64;
+    constexpr int KP = 256 / D;                  // threads per output column for S^T A_z
+    constexpr int NK = M > 0 ? M / KP : 1;       // sketch rows per thread
+    constexpr int W = 2 + D + M;
+    __shared__ float fw[64];
+    __shared__ float red[8];
+    __shared__ float az[M > 0 ? M : 1];
+    __shared__ float cpart[M > 0 ? 256 : 1];
+    __shared__ float w[D];
+    const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
+    const int64_t row = blockIdx.x;
+    const float* base = p.part + row * p.nsplit * (int64_t)W;
+    const bool col = t < D + M;
+    const bool skt = M > 0 && !p.s_ident;
+    // S rows of this thread's share (independent of everything else)
+    float sk[NK];
+    if (skt) {
+        const int c = t % D, kh = t / D;
+#pragma unroll
+        for (int k = 0; k < NK; ++k) sk[k] = p.sketch[(int64_t)(kh * NK + k) * D + c];
+    }
+    // split maxima
+    float mx = -INFINITY;
+    for (int s = t; s < p.nsplit; s += 256) mx = fmaxf(mx, base[(int64_t)s * W]);
+    mx = wave_max(mx);
+    if (lane == 0) red[wave] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float l = 0.0f, acc = 0.0f;
+    for (int s0 = 0; s0 < p.nsplit; s0 += 64) {
+        const int cnt = min(64, p.nsplit - s0);
+        // the column's 64 partials (past the last split: a clamped reload, weight 0)
+        float v[64];
+        if (col) {
+#pragma unroll
+            for (int u = 0; u < 64; ++u) v[u] = base[(int64_t)min(s0 + u, p.nsplit - 1) * W + 2 + t];
+        }
+        __syncthreads();  // the previous chunk's weights have been used
+        if (wave == 0) {
+            const int64_t sr = (int64_t)min(s0 + lane, p.nsplit - 1) * W;
+            const float ms = base[sr], ls = base[sr + 1];
+            const float f = (lane >= cnt || ms == -INFINITY || mx == -INFINITY) ? 0.0f : expf(ms - mx);
+            fw[lane] = f;
+            const float lw = wave_sum(f * ls);
+            if (lane == 0) red[4] = lw;
+        }
+        __syncthreads();
+        l += red[4];
+        if (col) {
+#pragma unroll
+            for (int u = 0; u < 64; ++u) acc = fmaf(fw[u], v[u], acc);
+        }
+    }
+    // (empty splits have weight 0 and all-zero columns, written by the split kernels)
+    if constexpr (M > 0) {
+        if (t >= D && col) az[t - D] = acc;
+        __syncthreads();
+        if (skt) {
+            const int kh = t / D;
+            float cr = 0.0f;
+#pragma unroll
+            for (int k = 0; k < NK; ++k) cr = fmaf(sk[k], az[kh * NK + k], cr);
+            cpart[t] = cr;
+        }
+        __syncthreads();
+        if (t < D) {
+            float corr = 0.0f;
+            if (skt) {
+#pragma unroll
+                for (int kk = 0; kk < KP; ++kk) corr += cpart[kk * D + t];
+            } else {
+                corr = az[t];
+            }
+            acc += p.corr * corr;
+        }
+    }
+    if (t < D) w[t] = acc;
+    __syncthreads();
+    if (wave != 0) return;
+    float x[VPL];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) x[v] = w[lane + 64 * v];
+    if (!p.norot) {
+        // H_d in Sylvester order, then the sign flips and 1/sqrt(d)
+#pragma unroll
+        for (int sp = 1; sp < 64; sp <<= 1) {
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) {
+                const float o = __shfl_xor(x[v], sp);
+                x[v] = (lane & sp) ? o - x[v] : x[v] + o;
+            }
+        }
+        if constexpr (VPL == 2) {
+            const float a0 = x[0], a1 = x[1];
+            x[0] = a0 + a1;
+            x[1] = a0 - a1;
+        }
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) x[v] = (l > 0.0f) ? p.sigma[lane + 64 * v] * x[v] / (sqrtf((float)D) * l) : 0.0f;
+    } else {
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) x[v] = (l > 0.0f) ? x[v] / l : 0.0f;
+    }
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) p.out[row * D + lane + 64 * v] = x[v];
+}
+
 // First merge stage for many splits: workgroup (row, g) combines splits
 // [32 g, 32 g + 32) of the row by log-sum-exp into one partial of the same
 // form (max, sum, A_y, A_z), so the final merge reads few partials.
@@ -1107,8 +1224,17 @@ hipError_t launch_decode(const tq_codebook* ck, const tq_codebook* cv, const tq_
             mk.part = part2;
             mk.nsplit = ngroup;
         }
-        if (d == 64) hipLaunchKernelGGL(decode_merge_kernel<64>, dim3((unsigned)rows), dim3(256), 0, stream, mk);
-        else hipLaunchKernelGGL(decode_merge_kernel<128>, dim3((unsigned)rows), dim3(256), 0, stream, mk);
+        using MFn = void (*)(MergeK);
+        MFn fn = nullptr;
+        const bool d64 = d == 64;
+        switch (mk.m) {
+            case 0: fn = d64 ? decode_merge_fast_kernel<64, 0> : decode_merge_fast_kernel<128, 0>; break;
+            case 32: fn = d64 ? decode_merge_fast_kernel<64, 32> : decode_merge_fast_kernel<128, 32>; break;
+            case 64: fn = d64 ? decode_merge_fast_kernel<64, 64> : decode_merge_fast_kernel<128, 64>; break;
+            case 128: fn = d64 ? decode_merge_fast_kernel<64, 128> : decode_merge_fast_kernel<128, 128>; break;
+            default: fn = d64 ? decode_merge_kernel<64> : decode_merge_kernel<128>; break;
+        }
+        hipLaunchKernelGGL(fn, dim3((unsigned)rows), dim3(256), 0, stream, mk);
         return hipGetLastError();
     };
     if (ck->spec.block >= 2) {

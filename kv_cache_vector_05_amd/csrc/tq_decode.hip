@@ -39,6 +39,7 @@ namespace {
 
 using dev::intx2;
 using dev::intx4;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct DecM {
     const int8_t* qd;
@@ -74,9 +75,11 @@ struct DecM {
     float* part;  // [B*Hq][nsplit][2 + D + M]
 };
 
+// keys per split at most: the logits and weight digits of a split stay in
+// LDS (24 KB per row tile of four queries at 512 keys)
 template <int NRT>
 constexpr int split_max() {
-    return 512;
+    return NRT == 1 ? 512 : 256;
 }
 
 typedef __attribute__((address_space(3))) intx2* lds_intx2_ptr;
@@ -117,6 +120,11 @@ __device__ __forceinline__ float max64(float v) {
     for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
     return v;
 }
+__device__ __forceinline__ float sum64(float v) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
+    return v;
+}
 
 template <int D, int BITS, int NRT, int M, bool PAGED>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
@@ -124,22 +132,29 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
     using TL = dev::TileLogit<D, BITS, NRT, NCS>;
     using Q = typename TL::Q;
     constexpr int SMAX = split_max<NRT>();
-    constexpr int NCH = SMAX / 64;     // 64-key chunks per split at most
-    constexpr int NCB = D / 16;        // 16-coordinate column blocks of A_y
-    constexpr int CBW = NCB / 4;       // ... per wave (= per coordinate quarter)
-    constexpr int NZB = M / 16;        // 16-row column blocks of A_z
-    constexpr int ZBW = (NZB + 3) / 4; // ... per wave at most
-    constexpr int PER = M / 4;         // sketch rows per coordinate quarter
-    constexpr int MW = M / 32;         // sign words per record
+    constexpr int NCH = SMAX / 64;        // 64-key chunks per split at most
+    constexpr int KPT = SMAX / 256;       // keys per thread in the weight pass
+    constexpr int CBW = D / 64;           // 16-coordinate column blocks of A_y per coordinate quarter
+    constexpr int PER = M / 4;            // sketch rows per coordinate quarter
+    constexpr int ZBW = (PER + 15) / 16;  // 16-row column blocks of A_z per quarter
+    constexpr int MW = M / 32;            // sign words per record
+    constexpr int NWO = M > 0 ? 2 : 1;    // weight operands: w (and w * gamma)
+    static_assert(ZBW <= CBW, "the operand buffer holds CBW blocks");
+    // record loads run this many 64-key chunks ahead of their use
+    constexpr int KDEPTH = 4, VDEPTH = 4;
 
-    __shared__ float lgs[4 * NCH * NRT * 64];                    // pass-1 logits (scaled)
-    __shared__ __attribute__((aligned(16))) int8_t vy[3 * NCB * 64 * 16];  // [digit][cb][key][16]
-    __shared__ __attribute__((aligned(16))) int8_t vz[(NZB > 0 ? NZB : 1) * 64 * 16];  // [cs][key][16]
-    __shared__ __attribute__((aligned(16))) int8_t wd[2 * NRT * 64 * 16];  // [w | w*gamma][rt][key][16]
-    __shared__ float red[16 * NRT + 8];
+    // logits of the split [rt][chunk][key][query of the row tile]
+    __shared__ f32x4 lgs[NRT * NCH * 64];
+    // weight digits of the split: A-operand rows [w | w gamma][rt][chunk][key][16]
+    __shared__ __attribute__((aligned(16))) int8_t wdig[NWO * NRT * NCH * 1024];
+    // per wave: one B-operand buffer [block][key][16] that the level digits
+    // and the sign bytes pass through in turn
+    __shared__ __attribute__((aligned(16))) int8_t bpool[4 * CBW * 1024];
+    __shared__ float red[32 * NRT + 8];
 
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = t >> 6;
     const int n = lane & 15;
     const int qk = lane >> 4;
     const int grp = blockIdx.x % p.ngroups;
@@ -156,7 +171,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
     const int c0 = split * p.split_len;
     const int c1 = min(c0 + p.split_len, sl);
     if (c0 >= c1) {  // empty split: weight 0 in the merge, all-zero columns
-        for (int i = threadIdx.x; i < 4 * NRT * width; i += blockDim.x) {
+        for (int i = t; i < 4 * NRT * width; i += blockDim.x) {
             const int g = gq0 + i / width, c = i % width;
             if (g < G) p.part[((rowbase + g) * p.nsplit + split) * width + c] = c == 0 ? -INFINITY : 0.f;
         }
@@ -175,60 +190,97 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
         }
         return rec_base + c0 + 64 * c + r;
     };
+    // record of row r of chunk c; chunks past the split's last one, and rows
+    // past its last key, reload the last key's record (unused), so the loads
+    // need no branch and can all be in flight together
+    auto rec_of = [&](int c, int r) -> int64_t {
+        const int cc = min(c, nch - 1);
+        return record(cc, min(r, c1 - 1 - c0 - 64 * cc));
+    };
     // correction weights: gamma per record (QJL sketch) or the KV head's mu
     const float k_head = p.k_mu ? p.k_mu[kh * p.k_mu_stride] : 0.f;
     const float v_head = p.v_mu ? p.v_mu[kh * p.v_mu_stride] : 0.f;
 
+    // the value norms of the keys this thread weighs (key t + 256 i of the split)
+    float vnw[KPT], vgw[KPT];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        const int kk = t + 256 * i;
+        const int64_t rec = rec_of(kk >> 6, kk & 63);
+        vnw[i] = p.v_norm[rec];
+        vgw[i] = M > 0 ? (p.v_mu ? v_head : p.v_rnorm[rec]) : 0.f;
+    }
+
     // ---------------- pass 1: logits, split max, value-norm bounds
+    // lane (qk, n) of wave w scores key 16 w + n of every chunk for query qk
+    // of each row tile; the key records run KDEPTH chunks ahead
+    const int row1 = 16 * wave + n;
     float mx[NRT];
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) mx[rt] = -INFINITY;
-    float numax = 0.f, ngmax = 0.f;
     {
         TL tl;
         tl.init(p.qd, p.sd, p.qscale, p.sdw, p.cq_k, rowbase, gq0, G, p.tdig_k, p.shift_k, lane);
-        // the key record (and the value norms) of the next chunk's tile are
-        // loaded before the current tile computes
         struct Rec1 {
             typename TL::Raw raw;
-            float nu, gm, vn, vg;
-        } cur, nxt;
-        auto fetch1 = [&](int c, Rec1& r) {
-            const int64_t rec = record(c, min(16 * wave + n, c1 - 1 - c0 - 64 * c));
-            TL::load(p.k_codes + rec * Q::CW + Q::word0(qk), p.k_signs + rec * MW, PER, lane, r.raw);
-            r.nu = p.k_norm[rec];
-            r.gm = M > 0 ? (p.k_mu ? k_head : p.k_rnorm[rec]) : 0.f;
-            r.vn = p.v_norm[rec];
-            r.vg = M > 0 ? (p.v_mu ? v_head : p.v_rnorm[rec]) : 0.f;
+            float nu, gm;
+        } kr[NCH];
+        auto fetch1 = [&](int c) {
+            const int64_t rec = rec_of(c, row1);
+            TL::load(p.k_codes + rec * Q::CW + Q::word0(qk), p.k_signs + rec * MW, PER, lane, kr[c].raw);
+            kr[c].nu = p.k_norm[rec];
+            kr[c].gm = M > 0 ? (p.k_mu ? k_head : p.k_rnorm[rec]) : 0.f;
         };
-        if (c0 + 16 * wave < c1) fetch1(0, cur);
-        for (int c = 0; c < nch; ++c) {
+#pragma unroll
+        for (int c = 0; c < KDEPTH && c < NCH; ++c) fetch1(c);
+        float* lgf = reinterpret_cast<float*>(lgs);
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
             const int key0 = c0 + 64 * c + 16 * wave;
-            if (key0 + 64 < c1) fetch1(c + 1, nxt);  // the same for the whole wave
             float a[NRT];
             if (key0 < c1) {  // the same for the whole wave
                 const bool valid = key0 + n < c1;
                 double lg[NRT];
-                tl.compute(cur.raw, cur.gm, PER, lane, lg);
+                tl.compute(kr[c].raw, kr[c].gm, PER, lane, lg);
 #pragma unroll
                 for (int rt = 0; rt < NRT; ++rt)
-                    a[rt] = valid ? (float)((double)p.scale * (double)cur.nu * lg[rt]) : -INFINITY;
-                if (valid) {
-                    numax = fmaxf(numax, cur.vn);
-                    ngmax = fmaxf(ngmax, cur.vn * cur.vg);
-                }
+                    a[rt] = valid ? (float)((double)p.scale * (double)kr[c].nu * lg[rt]) : -INFINITY;
             } else {
 #pragma unroll
                 for (int rt = 0; rt < NRT; ++rt) a[rt] = -INFINITY;
             }
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt) {
-                lgs[((wave * NCH + c) * NRT + rt) * 64 + lane] = a[rt];
+                lgf[((rt * NCH + c) * 64 + row1) * 4 + qk] = a[rt];
                 mx[rt] = fmaxf(mx[rt], a[rt]);
             }
-            cur = nxt;
+            if (c + KDEPTH < NCH) fetch1(c + KDEPTH);
         }
     }
+    float numax = 0.f, ngmax = 0.f;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        if (c0 + t + 256 * i < c1) {
+            numax = fmaxf(numax, vnw[i]);
+            ngmax = fmaxf(ngmax, vnw[i] * vgw[i]);
+        }
+    }
+
+    // value records for pass 2: lane l of every wave takes key l of each
+    // chunk, wave w the code words of coordinate quarter w and the sign word
+    // of its sketch rows
+    struct Rec2 {
+        uint32_t W[Q::NW];
+        uint32_t sg;
+    } vr[NCH];
+    auto fetch2 = [&](int c) {
+        const int64_t rec = rec_of(c, lane);
+        Q::load(p.v_codes + rec * Q::CW + Q::word0(wave), wave, vr[c].W);
+        vr[c].sg = M > 0 ? p.v_signs[rec * MW + ((wave * PER) >> 5)] : 0u;
+    };
+#pragma unroll
+    for (int c = 0; c < VDEPTH && c < NCH; ++c) fetch2(c);
+
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
         mx[rt] = max16(mx[rt]);
@@ -237,19 +289,22 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
     numax = max64(numax);
     ngmax = max64(ngmax);
     if (lane == 0) {
-        red[16 * NRT + wave] = numax;
-        red[16 * NRT + 4 + wave] = ngmax;
+        red[32 * NRT + wave] = numax;
+        red[32 * NRT + 4 + wave] = ngmax;
     }
     __syncthreads();
+    float mq[NRT][4];  // the split max of every query of the row tiles
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-        float v = red[rt * 4 + qk];
+    for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-        for (int w = 1; w < 4; ++w) v = fmaxf(v, red[(w * NRT + rt) * 4 + qk]);
-        mx[rt] = v;
-    }
-    numax = fmaxf(fmaxf(red[16 * NRT], red[16 * NRT + 1]), fmaxf(red[16 * NRT + 2], red[16 * NRT + 3]));
-    ngmax = fmaxf(fmaxf(red[16 * NRT + 4], red[16 * NRT + 5]), fmaxf(red[16 * NRT + 6], red[16 * NRT + 7]));
+        for (int qq = 0; qq < 4; ++qq) {
+            float v = red[rt * 4 + qq];
+#pragma unroll
+            for (int w = 1; w < 4; ++w) v = fmaxf(v, red[(w * NRT + rt) * 4 + qq]);
+            mq[rt][qq] = v;
+        }
+    numax = fmaxf(fmaxf(red[32 * NRT], red[32 * NRT + 1]), fmaxf(red[32 * NRT + 2], red[32 * NRT + 3]));
+    ngmax = fmaxf(fmaxf(red[32 * NRT + 4], red[32 * NRT + 5]), fmaxf(red[32 * NRT + 6], red[32 * NRT + 7]));
     // weights: w = p nu <= max nu, w gamma <= max nu gamma (p <= 1)
     const int sw = dev::fixed_shift(numax);
     const int sz = dev::fixed_shift(ngmax);
@@ -257,13 +312,60 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
     const float wscale = ldexpf(1.0f, min(sw, 126));
     const float zscale = ldexpf(1.0f, min(sz, 126));
 
+    // ---------------- weights, once per (query, key) of the split
+    // thread t weighs keys t + 256 i for the four queries of each row tile:
+    // w = exp(a - M) nu (and w gamma) in fixed point, the base-128 digits of
+    // query qq in bytes 4 qq .. 4 qq + 3 of the key's row (A-operand rows
+    // 4 qq + digit); exp(-inf) = 0 past the end
+    {
+        float ls[NRT][4];
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) ls[rt][qq] = 0.f;
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int kk = t + 256 * i;
+            const int c = kk >> 6, r = kk & 63;
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt) {
+                const f32x4 a = lgs[(rt * NCH + c) * 64 + r];
+                uint32_t dw[4], dz[4];
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    const float pj = __expf(a[qq] - mq[rt][qq]);
+                    ls[rt][qq] += pj;
+                    const float w = pj * vnw[i];
+                    dw[qq] = digits4_unsigned((uint32_t)rintf(w * wscale));
+                    dz[qq] = M > 0 ? digits4_unsigned((uint32_t)rintf((w * vgw[i]) * zscale)) : 0u;
+                }
+                *reinterpret_cast<intx4*>(wdig + ((0 * NRT + rt) * NCH + c) * 1024 + 16 * r) =
+                    intx4{(int)dw[0], (int)dw[1], (int)dw[2], (int)dw[3]};
+                if constexpr (M > 0)
+                    *reinterpret_cast<intx4*>(wdig + ((1 * NRT + rt) * NCH + c) * 1024 + 16 * r) =
+                        intx4{(int)dz[0], (int)dz[1], (int)dz[2], (int)dz[3]};
+            }
+        }
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const float s = sum64(ls[rt][qq]);
+                if (lane == 0) red[16 * NRT + (wave * NRT + rt) * 4 + qq] = s;
+            }
+    }
+    __syncthreads();
+
     // ---------------- pass 2: weighted value sums on the matrix cores
-    float lsum[NRT];
+    // Each wave sums its coordinate quarter over every key of the split,
+    // passing its B operands through a region of LDS of its own (written and
+    // read back transposed by the same wave, whose LDS accesses are served in
+    // order): no workgroup barrier.
+    int8_t* bbuf = bpool + wave * CBW * 1024;
     intx4 accy[NRT][CBW][3];
     intx4 accz[NRT][ZBW > 0 ? ZBW : 1];
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
-        lsum[rt] = 0.f;
 #pragma unroll
         for (int j = 0; j < CBW; ++j)
 #pragma unroll
@@ -274,119 +376,64 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
     uint32_t tdv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) tdv[i] = p.tdig_v[i];
-    const int row = 16 * wave + n;  // this lane's key row within a 64-key chunk
 
-    // value record of the lane's key (a clamped, valid record past the end;
-    // its weight is zero), loaded one chunk ahead
-    struct Rec2 {
-        uint32_t W[Q::NW];
-        uint32_t sg;  // the sign word holding sketch rows [qk*PER, (qk+1)*PER)
-        float vn, vg;
-    } vcur, vnxt;
-    auto fetch2 = [&](int c, Rec2& r) {
-        const int64_t rec = record(c, min(row, c1 - 1 - c0 - 64 * c));
-        Q::load(p.v_codes + rec * Q::CW + Q::word0(qk), qk, r.W);
-        r.sg = M > 0 ? p.v_signs[rec * MW + ((qk * PER) >> 5)] : 0u;
-        r.vn = p.v_norm[rec];
-        r.vg = M > 0 ? (p.v_mu ? v_head : p.v_rnorm[rec]) : 0.f;
-    };
-    fetch2(0, vcur);
-    for (int c = 0; c < nch; ++c) {
-        if (c + 1 < nch) fetch2(c + 1, vnxt);
-        const uint32_t* W = vcur.W;
-        const float vn = vcur.vn;
-        const float vg = vcur.vg;
-        // weights in fixed point, digits in the A-operand rows 4 qk + digit
 #pragma unroll
-        for (int rt = 0; rt < NRT; ++rt) {
-            const float a = lgs[((wave * NCH + c) * NRT + rt) * 64 + lane];
-            const float pj = __expf(a - mx[rt]);  // exp(-inf) = 0 past the end
-            lsum[rt] += pj;
-            const float w = pj * vn;
-            const uint32_t Wi = (uint32_t)rintf(w * wscale);
-            *reinterpret_cast<uint32_t*>(wd + ((0 * NRT + rt) * 64 + row) * 16 + 4 * qk) = digits4_unsigned(Wi);
-            if constexpr (M > 0) {
-                const uint32_t Zi = (uint32_t)rintf((w * vg) * zscale);
-                *reinterpret_cast<uint32_t*>(wd + ((1 * NRT + rt) * 64 + row) * 16 + 4 * qk) = digits4_unsigned(Zi);
-            }
-        }
-        // level digits of the lane's coordinate quarter: column blocks qk*CBW + j
-#pragma unroll
-        for (int j = 0; j < CBW; ++j) {
-            uint32_t sel[4];
-#pragma unroll
-            for (int sg = 0; sg < 4; ++sg) sel[sg] = Q::sel(W, 4 * j + sg, qk);
-#pragma unroll
-            for (int bb = 0; bb < 3; ++bb) {
-                intx4 v;
-#pragma unroll
-                for (int sg = 0; sg < 4; ++sg) v[sg] = (int)dev::lut4(tdv, bb, sel[sg]);
-                *reinterpret_cast<intx4*>(vy + ((bb * NCB + qk * CBW + j) * 64 + row) * 16) = v;
-            }
-        }
-        // sign bits of sketch rows [qk*PER, (qk+1)*PER) as +-1 bytes
-        if constexpr (M > 0) {
-            if constexpr (PER >= 16) {
-#pragma unroll
-                for (int k = 0; k < PER / 16; ++k) {
-                    const int bit0 = qk * PER + 16 * k;
-                    const uint32_t x = vcur.sg >> (bit0 & 31);
-                    intx4 v;
-#pragma unroll
-                    for (int s4 = 0; s4 < 4; ++s4) v[s4] = (int)dev::spread4_pm(x >> (4 * s4));
-                    *reinterpret_cast<intx4*>(vz + ((bit0 >> 4) * 64 + row) * 16) = v;
-                }
-            } else {
-                const int bit0 = qk * PER;
-                const uint32_t x = vcur.sg >> (bit0 & 31);
-                intx2 v;
-                v[0] = (int)dev::spread4_pm(x);
-                v[1] = (int)dev::spread4_pm(x >> 4);
-                *reinterpret_cast<intx2*>(vz + ((bit0 >> 4) * 64 + row) * 16 + (bit0 & 15)) = v;
-            }
-        }
-        __syncthreads();
+    for (int c = 0; c < NCH; ++c) {
+        if (c >= nch) break;  // the same for the whole workgroup
+        if (c + VDEPTH < NCH) fetch2(c + VDEPTH);
+        const Rec2& r = vr[c];
         intx4 aw[NRT], az[NRT];
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
-            aw[rt] = tr_operand(wd + (0 * NRT + rt) * 1024, lane);
-            if constexpr (M > 0) az[rt] = tr_operand(wd + (1 * NRT + rt) * 1024, lane);
+            aw[rt] = tr_operand(wdig + ((0 * NRT + rt) * NCH + c) * 1024, lane);
+            if constexpr (M > 0) az[rt] = tr_operand(wdig + ((1 * NRT + rt) * NCH + c) * 1024, lane);
         }
+        // level digits of quarter `wave`, one digit plane at a time:
+        // coordinates 16 j + 4 sg .. + 3 of the quarter in bytes 4 sg .. of block j
+        uint32_t sel[CBW][4];
 #pragma unroll
-        for (int j = 0; j < CBW; ++j) {
-            const int cb = wave * CBW + j;
+        for (int j = 0; j < CBW; ++j)
 #pragma unroll
-            for (int bb = 0; bb < 3; ++bb) {
-                const intx4 bv = tr_operand(vy + (bb * NCB + cb) * 1024, lane);
+            for (int sg = 0; sg < 4; ++sg) sel[j][sg] = Q::sel(r.W, 4 * j + sg, wave);
+#pragma unroll
+        for (int bb = 0; bb < 3; ++bb) {
+#pragma unroll
+            for (int j = 0; j < CBW; ++j) {
+                intx4 v;
+#pragma unroll
+                for (int sg = 0; sg < 4; ++sg) v[sg] = (int)dev::lut4(tdv, bb, sel[j][sg]);
+                *reinterpret_cast<intx4*>(bbuf + j * 1024 + 16 * lane) = v;
+            }
+#pragma unroll
+            for (int j = 0; j < CBW; ++j) {
+                const intx4 bv = tr_operand(bbuf + j * 1024, lane);
 #pragma unroll
                 for (int rt = 0; rt < NRT; ++rt)
                     accy[rt][j][bb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aw[rt], bv, accy[rt][j][bb], 0, 0, 0);
             }
         }
+        // sign bits of sketch rows wave*PER + 16 zb .. as +-1 bytes (rows past
+        // PER, when PER < 16, are zero bytes)
         if constexpr (M > 0) {
 #pragma unroll
-            for (int j = 0; j < ZBW; ++j) {
-                const int cs = wave + 4 * j;
-                if (cs < NZB) {
-                    const intx4 bz = tr_operand(vz + cs * 1024, lane);
+            for (int zb = 0; zb < ZBW; ++zb) {
+                const uint32_t x = r.sg >> ((wave * PER + 16 * zb) & 31);
+                intx4 v;
 #pragma unroll
-                    for (int rt = 0; rt < NRT; ++rt)
-                        accz[rt][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(az[rt], bz, accz[rt][j], 0, 0, 0);
-                }
+                for (int s4 = 0; s4 < 4; ++s4) v[s4] = 4 * s4 < PER - 16 * zb ? (int)dev::spread4_pm(x >> (4 * s4)) : 0;
+                *reinterpret_cast<intx4*>(bbuf + zb * 1024 + 16 * lane) = v;
+            }
+#pragma unroll
+            for (int zb = 0; zb < ZBW; ++zb) {
+                const intx4 bz = tr_operand(bbuf + zb * 1024, lane);
+#pragma unroll
+                for (int rt = 0; rt < NRT; ++rt)
+                    accz[rt][zb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(az[rt], bz, accz[rt][zb], 0, 0, 0);
             }
         }
-        __syncthreads();
-        vcur = vnxt;
     }
 
     // ---------------- partial results of the split
-    // l per query: lanes of one query hold disjoint keys; then across waves
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-        lsum[rt] = sum16(lsum[rt]);
-        if (n == 0) red[(wave * NRT + rt) * 4 + qk] = lsum[rt];
-    }
-    __syncthreads();
     const double yscale = ldexp(1.0, -(sw + p.shift_v));
     const double zs = ldexp(1.0, -sz);
 #pragma unroll
@@ -395,8 +442,12 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
         if (g >= G) continue;
         float* dst = p.part + ((rowbase + g) * p.nsplit + split) * width;
         if (wave == 0 && n == 0) {
-            dst[0] = mx[rt];
-            dst[1] = (red[rt * 4 + qk] + red[(NRT + rt) * 4 + qk]) + (red[(2 * NRT + rt) * 4 + qk] + red[(3 * NRT + rt) * 4 + qk]);
+            float mxq = mq[rt][0];
+#pragma unroll
+            for (int qq = 1; qq < 4; ++qq) mxq = qk == qq ? mq[rt][qq] : mxq;
+            const float* lr = red + 16 * NRT;
+            dst[0] = mxq;
+            dst[1] = (lr[rt * 4 + qk] + lr[(NRT + rt) * 4 + qk]) + (lr[(2 * NRT + rt) * 4 + qk] + lr[(3 * NRT + rt) * 4 + qk]);
         }
 #pragma unroll
         for (int j = 0; j < CBW; ++j) {
@@ -407,10 +458,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
         }
         if constexpr (M > 0) {
 #pragma unroll
-            for (int j = 0; j < ZBW; ++j) {
-                const int cs = wave + 4 * j;
-                if (cs < NZB) dst[2 + D + 16 * cs + n] = (float)(digit_rows(accz[rt][j]) * zs);
-            }
+            for (int zb = 0; zb < ZBW; ++zb)
+                if (16 * zb + n < PER) dst[2 + D + wave * PER + 16 * zb + n] = (float)(digit_rows(accz[rt][zb]) * zs);
         }
     }
 }
