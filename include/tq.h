@@ -400,6 +400,24 @@ tq_status tq_attn_decode(const tq_codebook* ck, const tq_codebook* cv, const voi
                          void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * tq_attn_decode_noalloc: tq_attn_decode for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments and result as tq_attn_decode without ws and
+ * ws_bytes: the workspace is a static device array of the library, 32 MiB
+ * on every GPU the library runs on, held until the process ends.  The call
+ * allocates nothing.  A decode whose tq_workspace_bytes(ck, cv,
+ * TQ_OP_DECODE, ...) exceeds the array is refused with TQ_EINVAL before any
+ * launch.  Every call on one GPU shares that GPU's array (it keeps the last
+ * call's contents; the decode writes every scratch byte it reads), so calls
+ * that overlap on one GPU - on two streams at once - race.
+ */
+tq_status tq_attn_decode_noalloc(const tq_codebook* ck, const tq_codebook* cv, const void* q, int32_t q_dtype,
+                                 const tq_packed* k, const tq_packed* v, int32_t B, int32_t Hq, int32_t h_kv,
+                                 int32_t L_cap, const int32_t* seq_len, const int32_t* q_pos,
+                                 const float* rope_cos, const float* rope_sin, int32_t rope_npos, float scale,
+                                 float* out, void* stream);
+
+/*
  * Paged forms of tq_attn_logits and tq_attn_decode: keys (and values) are
  * read through the page table; the logical capacity max_pages * page_size
  * takes the place of L_cap (logit rows are [max_pages * page_size] wide,

@@ -33,7 +33,7 @@ from ._lib import (TQError, TQ_F32, TQ_BF16, TQ_ROT_AUTO, TQ_ROT_HADAMARD, TQ_RO
                    TQ_CORR_QJL, TQ_CORR_SIGN, TQ_OP_ENCODE, TQ_OP_LOGITS, TQ_OP_DECODE, check, lib, tq_draws,
                    tq_packed, tq_pages, tq_spec)
 
-__all__ = ["Codebook", "Packed", "Pages", "Launch", "encode_kv", "append_kv", "attn_logits", "attn_decode",
+__all__ = ["Codebook", "Packed", "Pages", "Launch", "encode_kv", "append_kv", "attn_logits", "attn_decode", "attn_decode_noalloc",
            "decode_vectors", "rope_table", "codebook_tables", "plane_words", "workspace_bytes", "calibrate",
            "TQError", "lib"]
 
@@ -478,4 +478,24 @@ def attn_decode(ck, cv, q, kp, vp, h_kv, L_cap, seq_len, rope=None, scale=0.0, o
                 int(L_cap), _ptr(seq_len), _ptr(q_pos), _ptr(cos), _ptr(sin), npos, float(scale), _ptr(out),
                 _ptr(ws), wsb, _stream()]
         launch = _run(lib().tq_attn_decode, args, (kst, vst, ws, out), prepare)
+    return (launch, out) if prepare else out
+
+
+def attn_decode_noalloc(ck, cv, q, kp, vp, h_kv, L_cap, seq_len, rope=None, scale=0.0, out=None, prepare=False,
+                        q_pos=None):
+    """attn_decode with the library's static device scratch as its workspace
+    (the library allocates nothing; out is allocated here when not given).
+    Calls that overlap on one GPU race on that scratch."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    cos, sin = (None, None) if rope is None else rope
+    npos = 0 if rope is None else int(cos.shape[0])
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    kst, vst = kp.struct(), vp.struct()
+    args = [ck.handle, cv.handle, _ptr(q), _dtype_code(q), C.byref(kst), C.byref(vst), B, Hq, int(h_kv),
+            int(L_cap), _ptr(seq_len), _ptr(q_pos), _ptr(cos), _ptr(sin), npos, float(scale), _ptr(out), _stream()]
+    launch = _run(lib().tq_attn_decode_noalloc, args, (kst, vst, out), prepare)
     return (launch, out) if prepare else out

@@ -79,6 +79,10 @@ SIGNATURES = {
                                    C.POINTER(tq_packed), C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                    C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_float, C.c_void_p,
                                    C.c_void_p, C.c_size_t, C.c_void_p]),
+    "tq_attn_decode_noalloc": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.POINTER(tq_packed),
+                                           C.POINTER(tq_packed), C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                           C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_float,
+                                           C.c_void_p, C.c_void_p]),
     "tq_workspace_bytes": (C.c_size_t, [C.c_void_p, C.c_void_p, C.c_int32, C.c_int64, C.c_int32, C.c_int32,
                                         C.c_int32, C.c_int32]),
     "tq_plane_words": (C.c_int64, [C.POINTER(tq_spec), C.c_int32]),

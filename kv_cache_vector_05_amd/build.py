@@ -26,7 +26,7 @@ OUT = os.path.join(PKG, "libtq.so")
 BUILD = os.path.join(ROOT, "_build")
 
 SOURCES = ["tq_host.cpp", "tq_gemm.hip", "tq_encode.hip", "tq_attn.hip", "tq_qprep.hip", "tq_scan.hip", "tq_decode.hip",
-           "tq_vq.hip"]
+           "tq_vq.hip", "tq_noalloc.hip"]
 ARCH = "gfx950"
 
 
