@@ -421,7 +421,7 @@ tq_status tq_attn_decode_noalloc(const tq_codebook* ck, const tq_codebook* cv, c
  * Paged forms of tq_attn_logits and tq_attn_decode: keys (and values) are
  * read through the page table; the logical capacity max_pages * page_size
  * takes the place of L_cap (logit rows are [max_pages * page_size] wide,
- * workspaces are sized with it).  Bits <= 3 Hadamard or unrotated scalar
+ * workspaces are sized with it).  Bits <= 4 Hadamard or unrotated scalar
  * codebooks, or Hadamard vector codebooks (TQ_EUNSUPPORTED otherwise).
  */
 tq_status tq_attn_logits_paged(const tq_codebook* ck, const void* q, int32_t q_dtype, const tq_packed* k, int32_t B,

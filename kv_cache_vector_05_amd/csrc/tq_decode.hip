@@ -57,9 +57,9 @@ struct DecM {
     const int32_t* seq_len;
     int32_t Hq, h_kv, L_cap, ngroups, nsplit, split_len;
     float scale;
-    uint32_t tdig_k[8];
+    uint32_t tdig_k[16];
     int32_t shift_k;
-    uint32_t tdig_v[8];
+    uint32_t tdig_v[16];
     int32_t shift_v;
     double cq_k;                  // scale of the key correction term
     const float* k_mu;            // sign correction: mu per KV head, else nullptr (gamma per key)
@@ -373,9 +373,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
 #pragma unroll
         for (int j = 0; j < (ZBW > 0 ? ZBW : 1); ++j) accz[rt][j] = intx4{0, 0, 0, 0};
     }
-    uint32_t tdv[8];
+    uint32_t tdv[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) tdv[i] = p.tdig_v[i];
+    for (int i = 0; i < (BITS == 4 ? 16 : 8); ++i) tdv[i] = p.tdig_v[i];
 
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -401,7 +401,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
             for (int j = 0; j < CBW; ++j) {
                 intx4 v;
 #pragma unroll
-                for (int sg = 0; sg < 4; ++sg) v[sg] = (int)dev::lut4(tdv, bb, sel[j][sg]);
+                for (int sg = 0; sg < 4; ++sg) v[sg] = (int)dev::lut<BITS>(tdv, bb, sel[j][sg]);
                 *reinterpret_cast<intx4*>(bbuf + j * 1024 + 16 * lane) = v;
             }
 #pragma unroll
@@ -493,6 +493,7 @@ DecMFn pick_bits(int bits, int nrt, int m) {
         case 1: return pick_nrt<D, 1, PG>(nrt, m);
         case 2: return pick_nrt<D, 2, PG>(nrt, m);
         case 3: return pick_nrt<D, 3, PG>(nrt, m);
+        case 4: return pick_nrt<D, 4, PG>(nrt, m);
     }
     return nullptr;
 }
@@ -554,7 +555,7 @@ hipError_t launch_decode_mfma(const tq_codebook* ck, const tq_codebook* cv, cons
     p.nsplit = nsplit;
     p.split_len = split_len;
     p.scale = a.scale;
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 16; ++i) {
         p.tdig_k[i] = ck->lvl_digits[i];
         p.tdig_v[i] = cv->lvl_digits[i];
     }

@@ -51,9 +51,22 @@ struct FastDiv {
     __device__ uint32_t div(uint32_t n) const { return (__umulhi(n, m) + n) >> s; }
 };
 
-// digit b of the levels of the 4 codes in the bytes of sel
-__device__ __forceinline__ uint32_t lut4(const uint32_t* tdig, int b, uint32_t sel) {
-    return __builtin_amdgcn_perm(tdig[2 * b + 1], tdig[2 * b], sel);
+// digit b of the levels of the 4 codes in the bytes of sel.  tdig holds the
+// digits of levels 0-7 in words 2b, 2b + 1 and of levels 8-15 in words
+// 8 + 2b, 8 + 2b + 1 (byte c % 4 of word c / 4 of its half).  Up to 8
+// levels: one v_perm; 16 levels: one per half and a byte select on bit 3 of
+// each code (v_perm selectors 8-15 would not index bytes).
+template <int BITS>
+__device__ __forceinline__ uint32_t lut(const uint32_t* tdig, int b, uint32_t sel) {
+    if constexpr (BITS <= 3) {
+        return __builtin_amdgcn_perm(tdig[2 * b + 1], tdig[2 * b], sel);
+    } else {
+        const uint32_t s7 = sel & 0x07070707u;
+        const uint32_t lo = __builtin_amdgcn_perm(tdig[2 * b + 1], tdig[2 * b], s7);
+        const uint32_t hi = __builtin_amdgcn_perm(tdig[8 + 2 * b + 1], tdig[8 + 2 * b], s7);
+        const uint32_t mask = ((sel >> 3) & 0x01010101u) * 0xFFu;
+        return (hi & mask) | (lo & ~mask);
+    }
 }
 
 // v_perm selector for the 4 codes in the low 4*BITS bits of w: byte k = code k
@@ -63,6 +76,10 @@ __device__ __forceinline__ uint32_t code_sel(uint32_t w) {
         // even codes (bits 0-2, 6-8) and odd codes (3-5, 9-11) spread by
         // multiplication; the partial products never overlap
         return (((w & 0x1C7u) * 0x401u) & 0x70007u) | (((w & 0xE38u) * 0x8020u) & 0x7000700u);
+    } else if constexpr (BITS == 4) {
+        // nibbles 0, 1 to bytes 0, 1 and nibbles 2, 3 to bytes 2, 3
+        const uint32_t t = __builtin_amdgcn_perm(0u, w, 0x0C010C00u);  // bytes: w0, 0, w1, 0
+        return (t & 0x000F000Fu) | ((t & 0x00F000F0u) << 4);
     } else if constexpr (BITS == 2) {
         return (((w & 0x33u) * 0x1001u) & 0x30003u) | (((w & 0xCCu) * 0x40040u) & 0x3000300u);
     } else {
@@ -218,7 +235,7 @@ struct TileLogit {
     intx4 as[NRT][NCS > 0 ? NCS : 1];
     // logit / nu = V qscale + gamma (Z zk - zc), Z the sign-digit sum
     double qscale[NRT], zk[NRT], zc[NRT];
-    uint32_t tdig[8];
+    uint32_t tdig[16];
 
     // qd/sd/scale: the prepared query digits; cq: scale of the correction
     // term (sqrt(pi/2)/m for the QJL sketch, 1 for the sign correction);
@@ -256,7 +273,7 @@ struct TileLogit {
             zc[rt] = c * (double)scale[row * 3 + 2];
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) tdig[i] = lvl_digits[i];
+        for (int i = 0; i < (BITS == 4 ? 16 : 8); ++i) tdig[i] = lvl_digits[i];
     }
 
     // The lane's share of one key record, loaded ahead of its use so that a
@@ -289,7 +306,7 @@ struct TileLogit {
             for (int sg = 0; sg < 4; ++sg) {
                 const uint32_t sel = Q::sel(r.W, 4 * c + sg, qk);
 #pragma unroll
-                for (int bb = 0; bb < 3; ++bb) bd[c][bb][sg] = (int)lut4(tdig, bb, sel);
+                for (int bb = 0; bb < 3; ++bb) bd[c][bb][sg] = (int)lut<BITS>(tdig, bb, sel);
             }
         }
         intx4 bz[NCS > 0 ? NCS : 1];

@@ -506,7 +506,9 @@ void haar_from_gaussians(int d, const double* g, std::vector<double>* qout) {
 // Levels as 24-bit fixed-point integers T_k ~= t_k * 2^shift split into three
 // balanced base-256 digits, each in [-128, 127]: T = e0*2^16 + e1*2^8 + e2.
 // The shift puts max|T| just under 127.5 * 2^16 so the top digit fits.
-void level_digits(const std::vector<float>& levels, uint32_t words[8], int* shift) {
+// Digit b of level c sits in byte c % 4 of word 8 (c / 8) + 2 b + (c % 8) / 4
+// (levels 8-15 of a 4-bit table in the upper half).
+void level_digits(const std::vector<float>& levels, uint32_t words[16], int* shift) {
     double mx = 0.0;
     for (float v : levels) mx = std::max(mx, (double)std::fabs(v));
     int e = 0;
@@ -514,8 +516,8 @@ void level_digits(const std::vector<float>& levels, uint32_t words[8], int* shif
     int sh = 23 - e;
     if (std::ldexp(mx, sh) > 127.0 * 65536.0) --sh;
     *shift = sh;
-    for (int w = 0; w < 8; ++w) words[w] = 0u;
-    for (size_t c = 0; c < levels.size() && c < 8; ++c) {
+    for (int w = 0; w < 16; ++w) words[w] = 0u;
+    for (size_t c = 0; c < levels.size() && c < 16; ++c) {
         long long T = std::llround(std::ldexp((double)levels[c], sh));
         int dig[3];
         for (int k = 2; k >= 1; --k) {
@@ -526,7 +528,7 @@ void level_digits(const std::vector<float>& levels, uint32_t words[8], int* shif
         dig[0] = (int)T;
         for (int b = 0; b < 3; ++b) {
             const uint32_t byte = (uint32_t)(uint8_t)(int8_t)dig[b];
-            words[2 * b + (c >> 2)] |= byte << (8 * (c & 3));
+            words[8 * (c >> 3) + 2 * b + ((c & 7) >> 2)] |= byte << (8 * (c & 3));
         }
     }
 }
@@ -775,7 +777,7 @@ static tq_status codebook_create(const tq_spec* spec, const tq_draws* draws, con
         if (mu) cb->mu.assign(mu, mu + n_mu);
         else cb->mu.assign(1, (float)beta_mean_abs_error(spec->d, cb->levels, cb->thresholds));
     }
-    if (cb->K <= 8 && !vq) level_digits(cb->levels, cb->lvl_digits, &cb->lvl_shift);
+    if (cb->K <= 16 && !vq) level_digits(cb->levels, cb->lvl_digits, &cb->lvl_shift);
     const int d = spec->d, m = spec->m;
     if (vq && spec->block == 2 && !dense && cb->K <= kVqGridMaxN)
         vq_candidate_grid(cb->levels, cb->K, d, &cb->vq_grid, &cb->vq_inv_cell);
@@ -1176,7 +1178,7 @@ static tq_status logits_common(const tq_codebook* ck, const void* q, int32_t q_d
         if (ck->dense && pg.table) return fail(TQ_EUNSUPPORTED, "paged scans are served for Hadamard codebooks");
     } else if ((sign_corr(ck) || pg.table) && !logits_mfma_supported(ck)) {
         return fail(TQ_EUNSUPPORTED, "no logit kernel for this codebook (paged and sign-corrected scans need "
-                                     "a Hadamard or unrotated codebook with bits <= 3 and m <= 128)");
+                                     "a Hadamard or unrotated codebook with bits <= 4 and m <= 128)");
     }
     if ((int64_t)B * Hq == 0 || (L_cap == 0 && top_k == 0)) return TQ_OK;
     const size_t need = logits_workspace_bytes(ck, B, Hq, h_kv, L_cap, top_k);
@@ -1239,7 +1241,7 @@ static tq_status decode_common(const tq_codebook* ck, const tq_codebook* cv, con
         return fail(TQ_EUNSUPPORTED, "the fused decode needs key and value codebooks of equal bits and m");
     if (!vq && (sign_corr(ck) || sign_corr(cv) || pg.table) && !decode_mfma_supported(ck, cv))
         return fail(TQ_EUNSUPPORTED, "paged and sign-corrected decodes need key and value tables of equal d, bits "
-                                     "and m (bits <= 3)");
+                                     "and m (bits <= 4)");
     if ((int64_t)B * Hq == 0) return TQ_OK;
     const size_t need = decode_workspace_bytes(ck, cv, B, Hq, h_kv, L_cap);
     if (ws_bytes < need || (need && !ws)) return fail(TQ_EINVAL, "workspace too small");

@@ -49,7 +49,7 @@ struct tq_codebook {
     // levels in 24-bit fixed point, t_k ~= T_k * 2^-lvl_shift, as three balanced
     // base-256 int8 digits (digit 0 most significant); word 2b holds digit b
     // of codes 0..3, word 2b+1 of codes 4..7 (byte tables for v_perm)
-    uint32_t lvl_digits[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    uint32_t lvl_digits[16] = {};
     int lvl_shift = 0;
     // vector codebooks (block 2, N <= 64): the encoder's candidate grid
     std::vector<uint32_t> vq_grid;
@@ -95,7 +95,7 @@ void fibquant_codebook(int d, int k, int N, std::vector<double>* code);  // [N][
 void splitmix_gaussians(uint64_t seed, int purpose, size_t n, double* out);
 void splitmix_signs(uint64_t seed, size_t n, int8_t* out);
 void haar_from_gaussians(int d, const double* g, std::vector<double>* q);  // row-major
-void level_digits(const std::vector<float>& levels, uint32_t words[8], int* shift);
+void level_digits(const std::vector<float>& levels, uint32_t words[16], int* shift);
 uint16_t f32_to_f16(float f);
 float f16_to_f32(uint16_t h);
 

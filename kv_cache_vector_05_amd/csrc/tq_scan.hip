@@ -36,6 +36,7 @@ namespace {
 using dev::intx4;
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRsrcWord3 = 0x00020000;  // buffer resource word 3 for gfx9: 32-bit elements, no swizzle
 
@@ -60,7 +61,7 @@ struct ScanArgs {
     float* out;
     int64_t ld;
     int32_t col0;
-    uint32_t tdig[8];
+    uint32_t tdig[16];
     int32_t lvl_shift;
     double cq;              // scale of the correction term
     const float* mu;        // sign correction: mu per KV head (stride mu_stride)
@@ -145,6 +146,12 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs p) {
             r.W[0] = v.x;
             r.W[1] = v.y;
             r.W[2] = v.z;
+        } else if constexpr (Q::NW == 4 && Q::ALIGNED) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rc, vo_c, so_c, 0);
+            r.W[0] = v.x;
+            r.W[1] = v.y;
+            r.W[2] = v.z;
+            r.W[3] = v.w;
         } else if constexpr (Q::NW == 2 && Q::ALIGNED) {
             const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rc, vo_c, so_c, 0);
             r.W[0] = v.x;
@@ -224,9 +231,9 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs p) {
         zk[rt] = 2.0 * c * ldexp(1.0, -(int)sc[rt][1]);
         zc[rt] = c * (double)sc[rt][2];
     }
-    uint32_t tdig[8];
+    uint32_t tdig[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) tdig[i] = p.tdig[i];
+    for (int i = 0; i < (BITS == 4 ? 16 : 8); ++i) tdig[i] = p.tdig[i];
 
     // ---- output: row (rowbase + gq0 + 4rt + qk), column key - col0
     const int g_lane = gq0 + qk;
@@ -245,7 +252,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs p) {
             for (int sg = 0; sg < 4; ++sg) {
                 const uint32_t sel = Q::sel(r.W, 4 * c + sg, qk);
 #pragma unroll
-                for (int bb = 0; bb < 3; ++bb) bd[c][bb][sg] = (int)dev::lut4(tdig, bb, sel);
+                for (int bb = 0; bb < 3; ++bb) bd[c][bb][sg] = (int)dev::lut<BITS>(tdig, bb, sel);
             }
         }
         intx4 bz[NCS > 0 ? NCS : 1];
@@ -349,6 +356,7 @@ ScanFn pick_bits(int bits, int nrt, int m) {
         case 1: return pick_nrt<D, 1, PG>(nrt, m);
         case 2: return pick_nrt<D, 2, PG>(nrt, m);
         case 3: return pick_nrt<D, 3, PG>(nrt, m);
+        case 4: return pick_nrt<D, 4, PG>(nrt, m);
     }
     return nullptr;
 }
@@ -371,7 +379,7 @@ int64_t resident_blocks(const void* fn) {
 
 bool scan_supported(const tq_codebook* ck) {
     const int m = ck->spec.m;
-    return !ck->dense && ck->spec.block < 2 && ck->spec.bits <= 3 && (ck->spec.d == 64 || ck->spec.d == 128) &&
+    return !ck->dense && ck->spec.block < 2 && ck->spec.bits <= 4 && (ck->spec.d == 64 || ck->spec.d == 128) &&
            (m == 0 || m == 32 || m == 64 || m == 128);
 }
 
@@ -407,7 +415,7 @@ hipError_t launch_scan(const tq_codebook* ck, const tq_packed& k, const AttnArgs
     p.out = out;
     p.ld = ld;
     p.col0 = col0;
-    for (int i = 0; i < 8; ++i) p.tdig[i] = ck->lvl_digits[i];
+    for (int i = 0; i < 16; ++i) p.tdig[i] = ck->lvl_digits[i];
     p.lvl_shift = ck->lvl_shift;
     p.cq = corr_scale(ck);
     const MuRef mr = mu_ref(ck);

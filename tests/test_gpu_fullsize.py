@@ -55,8 +55,8 @@ def pick(planes, idx):
     return tuple(p[idx] if len(p) else p for p in planes)
 
 
-def check_llama(kind, n_enc=192, n_logit=1024, n_decode_heads=2, variant="qjl"):
-    st = bench.setup_llama(torch, tq, synth, kind, variant)
+def check_llama(kind, n_enc=192, n_logit=1024, n_decode_heads=2, variant="qjl", bits=None, m=None):
+    st = bench.setup_llama(torch, tq, synth, kind, variant, bits=bits, m=m)
     bench.run_calls(st, bench.NoTimer())
     torch.cuda.synchronize()
     B, Hq, H, L, d, bits, m = (st[k] for k in ("B", "Hq", "H", "L", "d", "bits", "m"))
@@ -123,6 +123,12 @@ def test_llama8b_full_size():
 def test_llama70b_full_size():
     """Batch 1, 64/8 heads, context 131072, Student-t(3) channel scales, b=3 + m=128."""
     check_llama("llama70b", n_decode_heads=1)
+
+
+@pytest.mark.timeout(900)
+def test_llama70b_4bit_full_size():
+    """The Llama-70B-shaped decode with 4-bit codes and no sketch (b=4, m=0)."""
+    check_llama("llama70b", n_decode_heads=1, bits=4, m=0)
 
 
 @pytest.mark.timeout(900)
