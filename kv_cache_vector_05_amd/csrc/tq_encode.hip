@@ -195,6 +195,30 @@ __device__ __forceinline__ void split_f16(const float* x, half8& hi, half8& lo) 
 // RoPE rows of the 32 tokens of the tile step at `base` (table entries of
 // this thread's staging slots), and their store into the LDS buffer
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// buffer resource over [base, base + bytes) (gfx9 word 3: 32-bit elements, no
+// swizzle); stores at or past the end are dropped by the hardware
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    const uint32_t n = bytes <= 0 ? 0u : (uint32_t)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
+}
+// a byte offset past every tile's resource: the store is dropped
+constexpr uint32_t kDrop = 0x40000000u;
+// N consecutive words at byte offset vo (16-, 8- and 4-byte stores)
+template <int N>
+__device__ __forceinline__ void store_words(__amdgpu_buffer_rsrc_t r, uint32_t vo, const uint32_t* w) {
+    int k = 0;
+#pragma unroll
+    for (; k + 4 <= N; k += 4)
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{w[k], w[k + 1], w[k + 2], w[k + 3]}, r, vo + 4u * k, 0, 0);
+    if constexpr (N % 4 >= 2) {
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[k], w[k + 1]}, r, vo + 4u * k, 0, 0);
+        k += 2;
+    }
+    if constexpr (N % 2 == 1) __builtin_amdgcn_raw_buffer_store_b32(w[k], r, vo + 4u * k, 0, 0);
+}
 
 template <int HALF, int NQ>
 __device__ __forceinline__ void rope_stage_load(const EncK& p, int64_t base, const int (&tab)[NQ],
@@ -322,7 +346,10 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
     constexpr int RS = HALF + 4;                   // padded row stride (floats)
     constexpr int NQ = 2 * 32 * (HALF / 4) / 256;  // float4 per thread per stage (cos and sin)
     extern __shared__ f32x4 s_rope4[];             // [cos, sin][32 tokens][RS / 4]
-    const bool stage = ROPE && p.rope_stage;
+    // bulk encodes (!GEN) with RoPE always stage the rows (the launcher sends
+    // other head counts to the general kernel), so their loop has no
+    // per-lane RoPE loads
+    const bool stage = ROPE && (!GEN || p.rope_stage != 0);
     int st_table[NQ], st_row[NQ], st_c4[NQ];
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
@@ -334,12 +361,7 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
     }
     const int64_t blk_stride = (int64_t)gridDim.x * 4;
     int64_t base = (int64_t)blockIdx.x * 4;
-    if (stage && base < p.n_tiles) {
-        f32x4 pre[NQ];
-        rope_stage_load<HALF, NQ>(p, base, st_table, st_row, st_c4, pre);
-        rope_stage_store<RS, NQ>(s_rope4, st_table, st_row, st_c4, pre);
-    }
-    __syncthreads();
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // wave (scalar)
     // element offset of this lane's input vector in tile t; lanes past the
     // last token read the last token instead (an MFMA column only feeds its
     // own vector, and these vectors are not stored)
@@ -378,22 +400,42 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
     constexpr bool ROW_PREFETCH = !VQ;  // next step's RoPE rows in registers during the tile
     uint4 nxt[PREFETCH ? NKB : 1];
     if constexpr (PREFETCH) {
-        const int64_t t0 = base + (threadIdx.x >> 6);
-        if (t0 < p.n_tiles) {
+        // bulk encodes load a tile past the last as the last (unused), so the
+        // load is unconditional
+        const int64_t t0 = GEN ? base + wv : min(base + wv, p.n_tiles - 1);
+        if (!GEN || t0 < p.n_tiles) {
             const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.x) + input_offset(t0));
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) nxt[kb] = src[2 * kb + h];
         }
     }
+    // the first step's RoPE rows (after the first inputs are requested: the
+    // rows' wait then covers them, and the loop starts with nothing in
+    // flight, as each iteration ends with only its prefetches and stores)
+    if (stage && base < p.n_tiles) {
+        f32x4 pre[NQ];
+        rope_stage_load<HALF, NQ>(p, base, st_table, st_row, st_c4, pre);
+        rope_stage_store<RS, NQ>(s_rope4, st_table, st_row, st_c4, pre);
+    }
+    __syncthreads();
     // the loop bound is the same for the whole block (barriers inside)
     for (; base < p.n_tiles; base += blk_stride) {
-      const int64_t tile = base + (threadIdx.x >> 6);
+      const int64_t tile = base + wv;
+      const bool live = tile < p.n_tiles;
+      // Bulk encodes run every wave through the tile body - a wave past the
+      // last tile computes on the last and stores nothing - and issue their
+      // loads and stores unconditionally: with no memory operation behind a
+      // branch, the compiler's in-order count of outstanding operations stays
+      // exact and a wait for the prefetched inputs waits for nothing else.
+      const int64_t ctile = GEN ? tile : min(tile, p.n_tiles - 1);
       // the next step's rows, in flight during this step's quantiser (loaded
-      // once this tile's own input registers are free)
+      // once this tile's own input registers are free; bulk encodes reload
+      // the last step's rows at the last step)
       f32x4 pre[NQ];
-      const bool prefetch = ROW_PREFETCH && stage && base + blk_stride < p.n_tiles;
-      if (tile >= p.n_tiles && prefetch) rope_stage_load<HALF, NQ>(p, base + blk_stride, st_table, st_row, st_c4, pre);
-      if (tile < p.n_tiles) {
+      const bool prefetch = ROW_PREFETCH && stage && (!GEN || base + blk_stride < p.n_tiles);
+      const int64_t pbase = GEN ? base + blk_stride : min(base + blk_stride, p.n_tiles - 1);
+      if (GEN && !live && prefetch) rope_stage_load<HALF, NQ>(p, pbase, st_table, st_row, st_c4, pre);
+      if (!GEN || live) {
         // the lane's vector: sequence, head, cache slot, RoPE row (a valid
         // table row for every lane) and whether it is stored.  Computed at
         // the start for the RoPE row, and again from the lane's index at the
@@ -406,7 +448,7 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
         auto locate = [&](int vl) -> Loc {
             Loc L;
             if (GEN && p.append) {
-                const int64_t idx = tile * 32 + vl;
+                const int64_t idx = ctile * 32 + vl;
                 const int64_t nv = (int64_t)p.n_seq * p.h_kv;
                 const uint32_t bq = p.div_h.div((uint32_t)min(idx, nv - 1));
                 L.seq = (int)bq;
@@ -415,8 +457,8 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
                 L.valid = idx < nv;
                 L.rpos = (int)min(max(L.slot, (int64_t)0), (int64_t)max(p.rope_npos - 1, 0));
             } else {
-                const uint32_t r = p.div_h.div((uint32_t)tile);
-                L.head = (int)((uint32_t)tile - r * (uint32_t)p.h_kv);
+                const uint32_t r = p.div_h.div((uint32_t)ctile);
+                L.head = (int)((uint32_t)ctile - r * (uint32_t)p.h_kv);
                 const uint32_t tbq = p.div_seq.div(r);
                 L.seq = (int)(r - tbq * (uint32_t)p.n_seq);
                 const int token = (int)tbq * 32 + vl;
@@ -438,6 +480,25 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
             return L.valid && rec >= 0;
         };
         const int rpos = locate(v).rpos;
+        // bulk encodes: the tile's vectors are 32 consecutive slots of one
+        // (sequence, head), so one buffer resource per plane spans the records
+        // the tile stores (none for a tile past the last); stores of vectors
+        // past the last token, and of the other lane half's words, fall
+        // outside it or go to kDrop
+        __amdgpu_buffer_rsrc_t o_codes = make_rsrc(nullptr, 0), o_norm = o_codes, o_rnorm = o_codes, o_signs = o_codes;
+        if constexpr (!GEN) {
+            const uint32_t r = p.div_h.div((uint32_t)ctile);
+            const int hd = (int)((uint32_t)ctile - r * (uint32_t)p.h_kv);
+            const uint32_t tbq = p.div_seq.div(r);
+            const int sq = (int)(r - tbq * (uint32_t)p.n_seq);
+            const int tok0 = (int)tbq * 32;
+            const int64_t cnt = live ? min(32, p.n_tok - tok0) : 0;
+            const int64_t rec0 = ((int64_t)sq * p.h_kv + hd) * p.L_cap + p.tok_offset + tok0;
+            o_codes = make_rsrc(p.codes + rec0 * CW, cnt * CW * 4);
+            o_norm = make_rsrc(p.norm + rec0, cnt * 4);
+            if constexpr (M > 0 && !SGN) o_rnorm = make_rsrc(p.rnorm + rec0, cnt * 4);
+            if constexpr (M > 0) o_signs = make_rsrc(p.signs + rec0 * (M / 32), cnt * (M / 32) * 4);
+        }
 
         floatx16 acc[NOB];
         float nu, scale;
@@ -446,7 +507,7 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
             // (the layout the Hadamard MFMAs leave): four contiguous inputs per
             // (ob, r/4), loaded as they are
             float xs[NOB][16];
-            const int64_t off = input_offset(tile);
+            const int64_t off = input_offset(ctile);
 #pragma unroll
             for (int ob = 0; ob < NOB; ++ob)
 #pragma unroll
@@ -517,7 +578,7 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) raw[kb] = nxt[kb];
             } else {
-                const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.x) + input_offset(tile));
+                const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.x) + input_offset(ctile));
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) raw[kb] = src[2 * kb + h];
             }
@@ -534,7 +595,7 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
                                                      __builtin_bit_cast(bf16x2, raw[kb].w), ss, false);
             }
         } else {
-            const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(p.x) + input_offset(tile));
+            const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(p.x) + input_offset(ctile));
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 const f32x4 a = src[4 * kb + 2 * h];
@@ -656,10 +717,10 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
         }
         }  // rotation
         __builtin_amdgcn_sched_barrier(0);
-        if (prefetch) rope_stage_load<HALF, NQ>(p, base + blk_stride, st_table, st_row, st_c4, pre);
+        if (prefetch) rope_stage_load<HALF, NQ>(p, pbase, st_table, st_row, st_c4, pre);
         if constexpr (PREFETCH) {
-            const int64_t tn = tile + blk_stride;
-            if (tn < p.n_tiles) {
+            const int64_t tn = GEN ? tile + blk_stride : min(tile + blk_stride, p.n_tiles - 1);
+            if (!GEN || tn < p.n_tiles) {
                 const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.x) + input_offset(tn));
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) nxt[kb] = src[2 * kb + h];
@@ -733,6 +794,17 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
                 const Swap sw = swap32(__uint_as_float(cw[w]));
                 cw[w] = __float_as_uint(sw.r0) | __float_as_uint(sw.r1);
             }
+            if constexpr (!GEN) {
+                const uint32_t vo = (uint32_t)(v * CW) * 4u;
+                if constexpr (CW % 8 == 0) {
+                    store_words<HW>(o_codes, vo + 4u * (h * HW), cw + h * HW);
+                } else {
+#pragma unroll
+                    for (int w = 0; w < CW; ++w)
+                        __builtin_amdgcn_raw_buffer_store_b32(cw[w], o_codes, (w >= HW) == (h == 1) ? vo + 4u * w : kDrop, 0, 0);
+                }
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(nu), o_norm, h == 0 ? 4u * v : kDrop, 0, 0);
+            } else {
             int64_t n;
             const bool valid = record(&n);
             if (valid) {
@@ -749,6 +821,7 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
                         if ((w >= HW) == (h == 1)) dst[w] = cw[w];
                 }
                 if (h == 0) p.norm[n] = nu;
+            }
             }
         } else {
             // per 8-value chunk pc (block pc/2, registers 8(pc%2)..+7): quantise,
@@ -899,14 +972,22 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
                 cw[k] = __float_as_uint(a) | __float_as_uint(b);
             }
 
-            int64_t n;
-            const bool valid = record(&n);
-            if (valid) {
-                uint32_t* dst = p.codes + n * CW + h * (CW / 2);
+            int64_t n = 0;
+            bool valid = false;
+            if constexpr (!GEN) {
+                store_words<CW / 2>(o_codes, (uint32_t)(v * CW + h * (CW / 2)) * 4u, cw);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(nu), o_norm, h == 0 ? 4u * v : kDrop, 0, 0);
+                if constexpr (SKETCH)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gamma), o_rnorm, h == 1 ? 4u * v : kDrop, 0, 0);
+            } else {
+                valid = record(&n);
+                if (valid) {
+                    uint32_t* dst = p.codes + n * CW + h * (CW / 2);
     #pragma unroll
-                for (int k = 0; k < CW / 2; ++k) dst[k] = cw[k];
-                if (h == 0) p.norm[n] = nu;
-                else if (SKETCH) p.rnorm[n] = gamma;
+                    for (int k = 0; k < CW / 2; ++k) dst[k] = cw[k];
+                    if (h == 0) p.norm[n] = nu;
+                    else if (SKETCH) p.rnorm[n] = gamma;
+                }
             }
 
             if constexpr (SGN) {
@@ -918,7 +999,10 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
                     uint32_t wb = (~wsg[ob] & 0x0F0F0F0Fu) << (4 * h);
                     const Swap sw = swap32(__uint_as_float(wb));
                     wb = __float_as_uint(sw.r0) | __float_as_uint(sw.r1);
-                    if (valid && (ob & 1) == h) p.signs[n * NOB + ob] = wb;
+                    if constexpr (!GEN)
+                        __builtin_amdgcn_raw_buffer_store_b32(wb, o_signs, (ob & 1) == h ? 4u * (v * NOB + ob) : kDrop, 0, 0);
+                    else if (valid && (ob & 1) == h)
+                        p.signs[n * NOB + ob] = wb;
                 }
             }
             if constexpr (SKETCH) {
@@ -942,7 +1026,10 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
                     wb = (~wb & 0x0F0F0F0Fu) << (4 * h);
                     const Swap sw = swap32(__uint_as_float(wb));
                     wb = __float_as_uint(sw.r0) | __float_as_uint(sw.r1);
-                    if (valid && (rb & 1) == h) p.signs[n * NRB + rb] = wb;
+                    if constexpr (!GEN)
+                        __builtin_amdgcn_raw_buffer_store_b32(wb, o_signs, (rb & 1) == h ? 4u * (v * NRB + rb) : kDrop, 0, 0);
+                    else if (valid && (rb & 1) == h)
+                        p.signs[n * NRB + rb] = wb;
                 }
             }
         }
@@ -950,7 +1037,7 @@ __global__ __launch_bounds__(256) void encode_had_kernel(EncK p) {
       if (stage) {
           __syncthreads();  // every wave is done with the current rows
           if (base + blk_stride < p.n_tiles) {
-              if constexpr (!ROW_PREFETCH) rope_stage_load<HALF, NQ>(p, base + blk_stride, st_table, st_row, st_c4, pre);
+              if constexpr (!ROW_PREFETCH) rope_stage_load<HALF, NQ>(p, pbase, st_table, st_row, st_c4, pre);
               rope_stage_store<RS, NQ>(s_rope4, st_table, st_row, st_c4, pre);
           }
           __syncthreads();
@@ -1280,7 +1367,9 @@ hipError_t launch_encode(const tq_codebook* cb, const EncodeArgs& a, hipStream_t
         const int mode = cb->spec.block >= 2                    ? 3
                          : cb->spec.correction == TQ_CORR_SIGN ? (cb->spec.rotation == TQ_ROT_NONE ? 2 : 1)
                                                                : 0;
-        const bool gen = a.append != 0 || a.pages.table != nullptr;
+        // the bulk kernel stages RoPE rows per block of four heads; other head
+        // counts take the general kernel (per-lane rows)
+        const bool gen = a.append != 0 || a.pages.table != nullptr || (a.rope_cos != nullptr && a.h_kv % 4 != 0);
         EncFn fn = pick_encode(d, bits, m, a.bf16 != 0, a.rope_cos != nullptr, mode, gen);
         if (!fn) return hipErrorInvalidValue;
         EncK p{};
