@@ -914,8 +914,10 @@ def main(argv=None):
     print("[bench] device copy, fill and read rates", file=sys.stderr, flush=True)
     rates = device_rates(torch)
     value, unit, kern, extra, cfg = report(st, ct, ms_step)
+    # counter figures are kept per workload; a bit-width override is a workload of its own
+    tkey = wl if (args.bits is None and args.qjl_rows is None) else f"{wl}-b{st['bits']}m{st['m']}"
     for name, k in kern.items():
-        k["traffic_bytes"] = measured_traffic(wl, name)
+        k["traffic_bytes"] = measured_traffic(tkey, name)
         k["frac_of_measured_copy"] = k["GBps"] / rates["copy_GBps"]
     dom = max(kern, key=lambda x: kern[x]["us"])
     roof = roofline_of(dom, kern[dom], rates)

@@ -976,8 +976,11 @@ size_t logits_workspace_bytes(const tq_codebook* ck, int64_t B, int Hq, int h_kv
         return bytes;
     }
     if (!ck->dense) {
-        size_t bytes = scan_supported(ck) ? align256(qdigits_workspace_bytes(ck, (int64_t)rows))
-                                          : align256(rows * (d + m) * 4);
+        // one row tile per KV head: the scan prepares its queries in LDS
+        const int G = h_kv > 0 ? Hq / h_kv : 1;
+        size_t bytes = !scan_supported(ck)         ? align256(rows * (d + m) * 4)
+                       : scan_row_tiles(G) == 1 ? 0
+                                                : align256(qdigits_workspace_bytes(ck, (int64_t)rows));
         if (top_k) bytes += align256(rows * chunk * 4);
         return bytes;
     }
@@ -1038,14 +1041,21 @@ hipError_t launch_logits(const tq_codebook* ck, const tq_packed& k, const AttnAr
         return hipSuccess;
     }
     if (!ck->dense && scan_supported(ck)) {
-        const QDigits qd = carve_qdigits(ck, ws, rows);
-        float* scores = reinterpret_cast<float*>(ws + align256(qdigits_workspace_bytes(ck, rows)));
-        hipError_t e = launch_qdigits(ck, a, qd, stream);
-        if (e != hipSuccess) return e;
-        if (a.top_k == 0) return launch_scan(ck, k, a, qd, 0, a.L_cap, a.out, a.L_cap, 0, stream);
+        const bool fused = scan_row_tiles(G) == 1;
+        QDigits qd{};
+        char* wsc = ws;
+        if (!fused) {
+            qd = carve_qdigits(ck, ws, rows);
+            wsc = ws + align256(qdigits_workspace_bytes(ck, rows));
+            const hipError_t e = launch_qdigits(ck, a, qd, stream);
+            if (e != hipSuccess) return e;
+        }
+        const QDigits* qp = fused ? nullptr : &qd;
+        float* scores = reinterpret_cast<float*>(wsc);
+        if (a.top_k == 0) return launch_scan(ck, k, a, qp, 0, a.L_cap, a.out, a.L_cap, 0, stream);
         for (int k0 = 0; k0 < a.L_cap; k0 += chunk) {
             const int cnt = std::min(chunk, a.L_cap - k0);
-            e = launch_scan(ck, k, a, qd, k0, cnt, scores, chunk, k0, stream);
+            hipError_t e = launch_scan(ck, k, a, qp, k0, cnt, scores, chunk, k0, stream);
             if (e != hipSuccess) return e;
             TopK tk{};
             tk.scores = scores;

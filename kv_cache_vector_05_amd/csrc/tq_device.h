@@ -367,5 +367,225 @@ struct TileLogit {
     }
 };
 
+// ---------------------------------------------------------------- query preparation
+// q' = Pi RoPE(q) and s = S q' (s = q' with the sign correction of the
+// TurboESM summary, technical section 2), as fixed-point integers with one
+// power-of-two scale per query (|X| <= 2^26) split into four balanced
+// base-128 int8 digits: the A operands of the integer-MFMA logit tile (tambur
+// post: logits straight from quantised keys; iaemfoco post, "TurboQuant: Uma
+// Nova Abordagem": the QJL correction), with the scale and the exact sum of
+// the fixed-point s values beside them.
+
+__device__ __forceinline__ long long to_fixed(float x, int sh) { return llrint(ldexp((double)x, sh)); }
+// four balanced base-128 digits of X (most significant first)
+__device__ __forceinline__ void digits4(long long X, int8_t d[4]) {
+#pragma unroll
+    for (int k = 3; k >= 1; --k) {
+        long long r = ((X + 64) & 127) - 64;
+        d[k] = (int8_t)r;
+        X = (X - r) >> 7;
+    }
+    d[0] = (int8_t)X;
+}
+__device__ __forceinline__ float wave_max64(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+__device__ __forceinline__ double wave_sum64(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+struct PrepIn {
+    const void* q;            // [rows][d] float32 or bfloat16
+    int32_t bf16, L_cap;
+    int32_t norot;            // Pi = I: q' = RoPE(q)
+    int32_t s_ident;          // S = I (sign correction): s = q'
+    const float* rope_cos;    // [n_pos][d/2] or nullptr
+    const float* rope_sin;
+    const float* sigma;       // Hadamard signs
+    const float* sketch_t;    // S^T [d][m]
+};
+
+// LDS of the preparation of R query rows
+template <int D, int M, int R>
+struct alignas(16) PrepLds {
+    static constexpr int NCS = M == 0 ? 0 : (M >= 64 ? M / 64 : 1);  // 64-row sketch chunks of the MFMA
+    static constexpr int SDW = 64 * (NCS > 0 ? NCS : 1);             // bytes per digit row of s
+    float qp[R][D];               // q'
+    float part[M > 0 ? R : 1][256];  // partial sums of s (one per thread)
+    float s[R][M > 0 ? M : 1];
+    int8_t qd[R][4][D];           // digit rows of q'
+    int8_t sd[R][4][SDW];         // digit rows of s in MFMA slot order
+    float scl[R][3];              // shift(q'), shift(s), sum of the fixed-point s values
+};
+
+// Preparation of R query rows by the 256 threads of a workgroup, in two
+// stages so that a caller can put other loads in flight behind the
+// preparation's own: load() issues every load, compute() waits for them and
+// fills the LDS (ending with a barrier).  Row r is query row
+// row_of(min(r, R - 1)); wave w prepares rows w, w + 4, ...  Thread (part,
+// l) of the sketch sums row l of S over one of 256/m coordinate ranges, so
+// each entry of S is read once and a wave's loads are contiguous.
+template <int D, int M, int R>
+struct Prep {
+    static constexpr int VPL = D / 64;
+    static constexpr int NT = M > 0 ? 256 / M : 1;  // parts per sketch row
+    static constexpr int NI = D / NT;               // S^T entries per thread
+    static constexpr int RW = (R + 3) / 4;          // rows per wave
+    float sk[M > 0 ? NI : 1];
+    float x[RW][VPL];
+    float sg[VPL];
+    float c = 1.0f, sn = 0.0f;
+
+    // pos: the queries' RoPE position (one sequence per workgroup)
+    template <typename RowOf>
+    __device__ void load(const PrepIn& in, RowOf row_of, int pos) {
+        const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+        if constexpr (M > 0) {
+            if (!in.s_ident) {
+                const int l = t % M, prt = t / M;
+#pragma unroll
+                for (int k = 0; k < NI; ++k) sk[k] = in.sketch_t[(int64_t)(prt * NI + k) * M + l];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < RW; ++j) {
+            const int64_t row = row_of(min(wave + 4 * j, R - 1));
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) {
+                const int64_t e = row * D + lane + 64 * v;
+                x[j][v] = in.bf16 ? __uint_as_float((uint32_t) static_cast<const uint16_t*>(in.q)[e] << 16)
+                                  : static_cast<const float*>(in.q)[e];
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) sg[v] = in.norot ? 1.0f : in.sigma[lane + 64 * v];
+        if (in.rope_cos) {
+            c = in.rope_cos[(int64_t)pos * (D / 2) + lane % (D / 2)];
+            sn = in.rope_sin[(int64_t)pos * (D / 2) + lane % (D / 2)];
+        }
+    }
+
+    __device__ void compute(const PrepIn& in, PrepLds<D, M, R>& L) {
+        const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+#pragma unroll
+        for (int j = 0; j < RW; ++j) {
+            const int r = wave + 4 * j;
+            if (r >= R) break;  // the same for the whole wave
+            float xv[VPL];
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) xv[v] = x[j][v];
+            if (in.rope_cos) {
+                // RoPE: pair (i, i + d/2) in one lane (d = 128) or lanes l, l ^ 32 (d = 64)
+                if constexpr (VPL == 2) {
+                    const float lo = xv[0], hi = xv[1];
+                    xv[0] = lo * c - hi * sn;
+                    xv[1] = hi * c + lo * sn;
+                } else {
+                    const float own = xv[0], other = __shfl_xor(own, 32);
+                    xv[0] = lane < 32 ? own * c - other * sn : own * c + other * sn;
+                }
+            }
+            if (!in.norot) {
+#pragma unroll
+                for (int v = 0; v < VPL; ++v) xv[v] *= sg[v];
+                // H_d in Sylvester order: butterflies over every index bit
+#pragma unroll
+                for (int sp = 1; sp < 64; sp <<= 1) {
+#pragma unroll
+                    for (int v = 0; v < VPL; ++v) {
+                        const float o = __shfl_xor(xv[v], sp);
+                        xv[v] = (lane & sp) ? o - xv[v] : xv[v] + o;
+                    }
+                }
+                if constexpr (VPL == 2) {
+                    const float a0 = xv[0], a1 = xv[1];
+                    xv[0] = a0 + a1;
+                    xv[1] = a0 - a1;
+                }
+                const float inv = 1.0f / sqrtf((float)D);
+#pragma unroll
+                for (int v = 0; v < VPL; ++v) xv[v] *= inv;
+            }
+            float amax = 0.0f;
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) amax = fmaxf(amax, fabsf(xv[v]));
+            const int shq = fixed_shift(wave_max64(amax));
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) {
+                const int i = lane + 64 * v;
+                L.qp[r][i] = xv[v];
+                int8_t d[4];
+                digits4(to_fixed(xv[v], shq), d);
+#pragma unroll
+                for (int a = 0; a < 4; ++a) L.qd[r][a][i] = d[a];
+            }
+            if (lane == 0) {
+                L.scl[r][0] = (float)shq;  // shifts are small integers, exact in fp32
+                L.scl[r][1] = 0.0f;
+                L.scl[r][2] = 0.0f;
+            }
+        }
+        if constexpr (M > 0) {
+            const bool sketch = !in.s_ident;
+            __syncthreads();
+            // partial sums of s = S q' (or s = q')
+            if (sketch) {
+                const int prt = t / M;
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int k = 0; k < NI; ++k) acc = fmaf(sk[k], L.qp[r][prt * NI + k], acc);
+                    L.part[r][t] = acc;
+                }
+            }
+            __syncthreads();
+            for (int idx = t; idx < R * M; idx += 256) {
+                const int r = idx / M, l = idx % M;
+                float sv = 0.0f;
+                if (sketch) {
+#pragma unroll
+                    for (int k = 0; k < NT; ++k) sv += L.part[r][k * M + l];
+                } else {
+                    sv = L.qp[r][l];
+                }
+                L.s[r][l] = sv;
+            }
+            __syncthreads();
+            // scale, exact sum and digits of s; digit byte (qk*ncs + cs)*16 + j
+            // holds sketch row qk*(m/4) + 16*cs + j (zero where that slot is past m/4)
+            constexpr int NCS = PrepLds<D, M, R>::NCS, SDW = PrepLds<D, M, R>::SDW;
+#pragma unroll
+            for (int j = 0; j < RW; ++j) {
+                const int r = wave + 4 * j;
+                if (r >= R) break;
+                float smax = 0.0f;
+                double sf = 0.0;
+                for (int li = lane; li < M; li += 64) smax = fmaxf(smax, fabsf(L.s[r][li]));
+                const int shs = fixed_shift(wave_max64(smax));
+                for (int li = lane; li < M; li += 64) sf += (double)to_fixed(L.s[r][li], shs);
+                sf = wave_sum64(sf);
+                for (int off = lane; off < SDW; off += 64) {
+                    const int qk = off / (16 * NCS), rem = off % (16 * NCS);
+                    const int cs = rem / 16, jj = rem % 16;
+                    int8_t d[4] = {0, 0, 0, 0};
+                    if (16 * cs + jj < M / 4) digits4(to_fixed(L.s[r][qk * (M / 4) + 16 * cs + jj], shs), d);
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) L.sd[r][a][off] = d[a];
+                }
+                if (lane == 0) {
+                    L.scl[r][1] = (float)shs;
+                    L.scl[r][2] = (float)ldexp(sf, -shs);
+                }
+            }
+        }
+        __syncthreads();
+    }
+};
+
 }  // namespace dev
 }  // namespace tq

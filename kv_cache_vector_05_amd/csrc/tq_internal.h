@@ -163,9 +163,12 @@ bool logits_mfma_supported(const tq_codebook* ck);
 size_t qdigits_workspace_bytes(const tq_codebook* ck, int64_t rows);
 QDigits carve_qdigits(const tq_codebook* ck, void* ws, int64_t rows);
 hipError_t launch_qdigits(const tq_codebook* ck, const AttnArgs& a, const QDigits& q, hipStream_t stream);
-// the integer-MFMA logit scan (tq_scan.hip) over queries prepared by launch_qdigits
+// the integer-MFMA logit scan (tq_scan.hip): query rows in tiles of four;
+// with one tile per KV head (q == nullptr) each workgroup prepares its own
+// queries, with more it reads those launch_qdigits prepared
 bool scan_supported(const tq_codebook* ck);
-hipError_t launch_scan(const tq_codebook* ck, const tq_packed& k, const AttnArgs& a, const QDigits& q, int k0,
+int scan_row_tiles(int G);
+hipError_t launch_scan(const tq_codebook* ck, const tq_packed& k, const AttnArgs& a, const QDigits* q, int k0,
                        int klen, float* out, int64_t ld, int col0, hipStream_t stream);
 // Fused decode on the integer matrix cores (tq_decode.hip): partials of
 // [B*Hq][nsplit][2 + d + m] floats (max, sum, A_y, A_z) for the merge kernel.

@@ -24,6 +24,8 @@
 // records in flight behind the one it computes.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include <algorithm>
 #include <cmath>
 
@@ -47,7 +49,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 }
 
 struct ScanArgs {
-    const int8_t* qd;       // prepared queries (tq_qprep.hip): digit rows of q'
+    dev::PrepIn prep;       // one row tile: the queries and the tables their preparation reads
+    const int32_t* q_pos;   // queries' RoPE positions (nullptr: seq_len)
+    const int8_t* qd;       // several row tiles: queries prepared by tq_qprep.hip (digit rows of q')
     const int8_t* sd;       // digit rows of s in MFMA slot order
     const float* scale;     // per query: shift(q'), shift(s), sum of the fixed-point s
     int32_t sdw;
@@ -72,12 +76,19 @@ struct ScanArgs {
     dev::FastDiv div_page;
 };
 
-template <int D, int BITS, int NRT, int NCS, bool PAGED>
+template <int D, int BITS, int NRT, int M, bool PAGED>
 __global__ __launch_bounds__(256) void scan_kernel(ScanArgs p) {
     using Q = dev::Quarter<D, BITS>;
     constexpr int R = 4 * NRT;       // query rows of the workgroup
     constexpr int NC = Q::LPG / 16;  // K = 64 chunks over the lane's coordinates
+    using PL = dev::PrepLds<D, M, R>;
+    constexpr int NCS = PL::NCS;     // K = 64 chunks of the sketch product
+    // One row tile: the workgroup prepares its four queries itself.  More
+    // tiles read the queries prepared beforehand (their preparation would
+    // cost the kernel a wave per SIMD).
+    constexpr bool FUSE = NRT == 1;
     __shared__ u32x2 stab[256];      // bits of a byte -> eight 0/1 bytes
+    __shared__ std::conditional_t<FUSE, PL, char> prep;  // the workgroup's prepared queries
 
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -187,26 +198,35 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs p) {
         if (NCS > 0 && g_per_key) r.gm = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, vo_n, so_n, 0));
         else r.gm = g_head;
     };
-    // ---- the prepared queries: A rows (query 4rt + (lane&15)/4, digit
-    // lane&3; a row past the group repeats the last query and is never
-    // stored) and the scales of the lane's output query 4rt + qk.  Loaded
-    // before the first records: loads complete in order, so waiting for
-    // these leaves the records in flight.
+    // ---- query preparation: every workgroup of a (sequence, KV head) row
+    // tile prepares its rows itself (rows past the group repeat the last
+    // query and are never stored).  Its loads go first, then the record
+    // prefetch: loads complete in order, so the preparation waits for its own
+    // loads only and computes while the first records are in flight.
+    dev::Prep<D, M, FUSE ? R : 1> pr;
     intx4 aq[NRT][NC];
     intx4 as[NRT][NCS > 0 ? NCS : 1];
     float sc[NRT][3];
+    if constexpr (FUSE) {
+        pr.load(p.prep, [&](int r) { return rowbase + min(gq0 + r, G - 1); },
+                dev::query_pos(p.q_pos, p.seq_len, b, p.L_cap));
+    } else {
+        // A rows (query 4rt + (lane&15)/4, digit lane&3; a row past the
+        // group repeats the last query and is never stored) and the scales of
+        // the lane's output query 4rt + qk
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-        const int64_t drow = (rowbase + min(gq0 + 4 * rt + ((lane & 15) >> 2), G - 1)) * 4 + (lane & 3);
+        for (int rt = 0; rt < NRT; ++rt) {
+            const int64_t drow = (rowbase + min(gq0 + 4 * rt + ((lane & 15) >> 2), G - 1)) * 4 + (lane & 3);
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
-            aq[rt][c] = *reinterpret_cast<const intx4*>(p.qd + drow * D + qk * Q::LPG + 16 * c);
+            for (int c = 0; c < NC; ++c)
+                aq[rt][c] = *reinterpret_cast<const intx4*>(p.qd + drow * D + qk * Q::LPG + 16 * c);
 #pragma unroll
-        for (int cs = 0; cs < NCS; ++cs)
-            as[rt][cs] = *reinterpret_cast<const intx4*>(p.sd + drow * p.sdw + (qk * NCS + cs) * 16);
-        const int64_t orow = rowbase + min(gq0 + 4 * rt + qk, G - 1);
+            for (int cs = 0; cs < NCS; ++cs)
+                as[rt][cs] = *reinterpret_cast<const intx4*>(p.sd + drow * p.sdw + (qk * NCS + cs) * 16);
+            const int64_t orow = rowbase + min(gq0 + 4 * rt + qk, G - 1);
 #pragma unroll
-        for (int k = 0; k < 3; ++k) sc[rt][k] = p.scale[orow * 3 + k];
+            for (int k = 0; k < 3; ++k) sc[rt][k] = p.scale[orow * 3 + k];
+        }
     }
     // Every record fetch is unconditional: a tile past the wave's last
     // reloads the last one (a cache hit), so each loop step issues the same
@@ -222,7 +242,20 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs p) {
         const uint32_t v = (uint32_t)t;  // 256 threads: one table entry each
         stab[t] = u32x2{dev::spread4(v), dev::spread4(v >> 4)};
     }
-    __syncthreads();
+    if constexpr (FUSE) {
+        pr.compute(p.prep, prep);  // ends with a barrier (the sign table is ready too)
+        // A rows (query (lane&15)/4, digit lane&3) and the scales of the
+        // lane's output query qk
+        const int r = (lane & 15) >> 2, a = lane & 3;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) aq[0][c] = *reinterpret_cast<const intx4*>(&prep.qd[r][a][qk * Q::LPG + 16 * c]);
+#pragma unroll
+        for (int cs = 0; cs < NCS; ++cs) as[0][cs] = *reinterpret_cast<const intx4*>(&prep.sd[r][a][(qk * NCS + cs) * 16]);
+#pragma unroll
+        for (int k = 0; k < 3; ++k) sc[0][k] = prep.scl[qk][k];
+    } else {
+        __syncthreads();
+    }
     double qscale[NRT], zk[NRT], zc[NRT];
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
@@ -337,9 +370,9 @@ template <int D, int BITS, int NRT, bool PG>
 ScanFn pick_ncs(int m) {
     switch (m) {
         case 0: return scan_kernel<D, BITS, NRT, 0, PG>;
-        case 32:
-        case 64: return scan_kernel<D, BITS, NRT, 1, PG>;
-        case 128: return scan_kernel<D, BITS, NRT, 2, PG>;
+        case 32: return scan_kernel<D, BITS, NRT, 32, PG>;
+        case 64: return scan_kernel<D, BITS, NRT, 64, PG>;
+        case 128: return scan_kernel<D, BITS, NRT, 128, PG>;
     }
     return nullptr;
 }
@@ -383,10 +416,13 @@ bool scan_supported(const tq_codebook* ck) {
            (m == 0 || m == 32 || m == 64 || m == 128);
 }
 
-hipError_t launch_scan(const tq_codebook* ck, const tq_packed& k, const AttnArgs& a, const QDigits& q, int k0,
+int scan_row_tiles(int G) { return G <= 4 ? 1 : (G <= 8 ? 2 : 4); }
+
+hipError_t launch_scan(const tq_codebook* ck, const tq_packed& k, const AttnArgs& a, const QDigits* q, int k0,
                        int klen, float* out, int64_t ld, int col0, hipStream_t stream) {
     const int G = a.Hq / a.h_kv;
-    const int nrt = G <= 4 ? 1 : (G <= 8 ? 2 : 4);
+    const int nrt = scan_row_tiles(G);
+    if ((nrt > 1) != (q != nullptr)) return hipErrorInvalidValue;
     const int ngroups = (G + 4 * nrt - 1) / (4 * nrt);
     const bool paged = a.pages.table != nullptr;
     const int d = ck->spec.d, bits = ck->spec.bits, m = ck->spec.m;
@@ -395,10 +431,22 @@ hipError_t launch_scan(const tq_codebook* ck, const tq_packed& k, const AttnArgs
     else if (d == 128) fn = paged ? pick_bits<128, true>(bits, nrt, m) : pick_bits<128, false>(bits, nrt, m);
     if (!fn) return hipErrorInvalidValue;
     ScanArgs p{};
-    p.qd = q.qd;
-    p.sd = q.sd;
-    p.scale = q.scale;
-    p.sdw = q.sdw;
+    p.prep.q = a.q;
+    p.prep.bf16 = a.bf16;
+    p.prep.L_cap = a.L_cap;
+    p.prep.norot = no_rotation(ck) ? 1 : 0;
+    p.prep.s_ident = sign_corr(ck) ? 1 : 0;
+    p.prep.rope_cos = a.rope_cos;
+    p.prep.rope_sin = a.rope_sin;
+    p.prep.sigma = ck->dev.sigma;
+    p.prep.sketch_t = ck->dev.sketch_t;
+    p.q_pos = a.q_pos;
+    if (q) {
+        p.qd = q->qd;
+        p.sd = q->sd;
+        p.scale = q->scale;
+        p.sdw = q->sdw;
+    }
     p.seq_len = a.seq_len;
     p.norm = k.norm;
     p.rnorm = k.rnorm;
