@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama8b]
                     [--copies 4] [--reps 5] [--cache-state rotate|hot|flushed]
+                    [--bits B] [--qjl-rows M] [--context L]
     python bench.py --copy-calibrate          # a device copy of known size
 
 A step is one pass of the whole hot path over one batch of synthetic input
@@ -102,6 +103,8 @@ def parse(argv=None):
     ap.add_argument("--reps", type=int, default=5, help="timed repeats per call (the median is reported)")
     ap.add_argument("--cache-state", default="rotate", choices=["rotate", "hot", "flushed"])
     ap.add_argument("--bits", type=int, default=None, help="llama workloads: Lloyd-Max bits (default 3)")
+    ap.add_argument("--context", type=int, default=None,
+                    help="llama workloads: tokens per sequence (default 32768 for llama8b, 131072 for llama70b)")
     ap.add_argument("--qjl-rows", type=int, default=None,
                     help="llama workloads: QJL sketch rows m (default 64 for llama8b, 128 for llama70b)")
     ap.add_argument("--copy-calibrate", action="store_true",
@@ -288,11 +291,12 @@ def turboesm_codebooks(tq, synth, d, bits, k_sample, v_sample, rope_host):
 
 
 # ------------------------------------------------------------ llama-shaped
-def setup_llama(torch, tq, synth, kind, variant="qjl", copies=1, bits=None, m=None):
+def setup_llama(torch, tq, synth, kind, variant="qjl", copies=1, bits=None, m=None, ctx=None):
     if kind == "llama8b":
         B, Hq, H, L, d, b0, m0, rope_base = 8, 32, 8, 32768, 128, 3, 64, 5e5
     else:
         B, Hq, H, L, d, b0, m0, rope_base = 1, 64, 8, 131072, 128, 3, 128, 0.0
+    L = L if ctx is None else ctx
     bits = b0 if bits is None else bits
     m = (d if variant == "turboesm" else m0) if m is None else m
     K, V = synth.llama_kv_inputs(kind, seed=0, batch=B, ctx=L, hkv=H, d=d)
@@ -827,7 +831,7 @@ def vsearch_report(st, ct, ms_step):
 
 # ------------------------------------------------------------ main
 def roofline_of(name, k, rates):
-    if "TFLOPs" in k and name == "scan_topk":
+    if "TFLOPs" in k:
         r = {"bound": "mfma", "achieved": k["TFLOPs"], "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
              "frac": k["TFLOPs"] / FP32_PEAK_TFLOPS}
     else:
@@ -863,7 +867,7 @@ def main(argv=None):
     print(f"[bench] setting up {wl} ({copies} buffer copies)", file=sys.stderr, flush=True)
     if wl in ("llama8b", "llama70b", "llama8b-turboesm"):
         st = setup_llama(torch, tq, synth, wl.split("-")[0], "turboesm" if wl.endswith("turboesm") else "qjl",
-                         copies, args.bits, args.qjl_rows)
+                         copies, args.bits, args.qjl_rows, args.context)
         report = llama_report
     elif wl in ("esm650m", "esm650m-turboesm"):
         st = setup_esm(torch, tq, synth, "turboesm" if wl.endswith("turboesm") else "qjl")
@@ -916,6 +920,8 @@ def main(argv=None):
     value, unit, kern, extra, cfg = report(st, ct, ms_step)
     # counter figures are kept per workload; a bit-width override is a workload of its own
     tkey = wl if (args.bits is None and args.qjl_rows is None) else f"{wl}-b{st['bits']}m{st['m']}"
+    if args.context is not None:
+        tkey += f"-L{args.context}"
     for name, k in kern.items():
         k["traffic_bytes"] = measured_traffic(tkey, name)
         k["frac_of_measured_copy"] = k["GBps"] / rates["copy_GBps"]

@@ -200,15 +200,40 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
     // correction weights: gamma per record (QJL sketch) or the KV head's mu
     const float k_head = p.k_mu ? p.k_mu[kh * p.k_mu_stride] : 0.f;
     const float v_head = p.v_mu ? p.v_mu[kh * p.v_mu_stride] : 0.f;
+    // contiguous records: one buffer resource per plane over the split's
+    // records, so that every load is a fixed lane offset plus a scalar one
+    // (keys past the split read zeros, which no output uses)
+    const int64_t recs = rec_base + c0;
+    const int64_t nkeys = c1 - c0;
+    constexpr int CW = Q::CW;
+    __amdgpu_buffer_rsrc_t kc = dev::buf_rsrc(nullptr, 0), ks = kc, kn = kc, kg = kc, vc = kc, vs = kc, vn = kc, vg = kc;
+    if constexpr (!PAGED) {
+        kc = dev::buf_rsrc(p.k_codes + recs * CW, nkeys * CW * 4);
+        kn = dev::buf_rsrc(p.k_norm + recs, nkeys * 4);
+        vc = dev::buf_rsrc(p.v_codes + recs * CW, nkeys * CW * 4);
+        vn = dev::buf_rsrc(p.v_norm + recs, nkeys * 4);
+        if constexpr (M > 0) {
+            ks = dev::buf_rsrc(p.k_signs + recs * MW, nkeys * MW * 4);
+            vs = dev::buf_rsrc(p.v_signs + recs * MW, nkeys * MW * 4);
+            if (!p.k_mu) kg = dev::buf_rsrc(p.k_rnorm + recs, nkeys * 4);
+            if (!p.v_mu) vg = dev::buf_rsrc(p.v_rnorm + recs, nkeys * 4);
+        }
+    }
 
     // the value norms of the keys this thread weighs (key t + 256 i of the split)
     float vnw[KPT], vgw[KPT];
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
         const int kk = t + 256 * i;
-        const int64_t rec = rec_of(kk >> 6, kk & 63);
-        vnw[i] = p.v_norm[rec];
-        vgw[i] = M > 0 ? (p.v_mu ? v_head : p.v_rnorm[rec]) : 0.f;
+        if constexpr (PAGED) {
+            const int64_t rec = rec_of(kk >> 6, kk & 63);
+            vnw[i] = p.v_norm[rec];
+            vgw[i] = M > 0 ? (p.v_mu ? v_head : p.v_rnorm[rec]) : 0.f;
+        } else {
+            vnw[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vn, 4u * kk, 0, 0));
+            vgw[i] = M > 0 ? (p.v_mu ? v_head : __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vg, 4u * kk, 0, 0)))
+                           : 0.f;
+        }
     }
 
     // ---------------- pass 1: logits, split max, value-norm bounds
@@ -226,10 +251,23 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
             float nu, gm;
         } kr[NCH];
         auto fetch1 = [&](int c) {
-            const int64_t rec = rec_of(c, row1);
-            TL::load(p.k_codes + rec * Q::CW + Q::word0(qk), p.k_signs + rec * MW, PER, lane, kr[c].raw);
-            kr[c].nu = p.k_norm[rec];
-            kr[c].gm = M > 0 ? (p.k_mu ? k_head : p.k_rnorm[rec]) : 0.f;
+            if constexpr (PAGED) {
+                const int64_t rec = rec_of(c, row1);
+                TL::load(p.k_codes + rec * Q::CW + Q::word0(qk), p.k_signs + rec * MW, PER, lane, kr[c].raw);
+                kr[c].nu = p.k_norm[rec];
+                kr[c].gm = M > 0 ? (p.k_mu ? k_head : p.k_rnorm[rec]) : 0.f;
+            } else {
+                const uint32_t key = (uint32_t)(64 * c);  // scalar: the chunk's first key
+                dev::quarter_load_buf<D, BITS>(kc, (uint32_t)(row1 * CW + Q::word0(qk)) * 4u, key * CW * 4u, qk,
+                                               kr[c].raw.W);
+                kr[c].raw.sg = M > 0 ? __builtin_amdgcn_raw_buffer_load_b32(ks, (uint32_t)(row1 * MW + ((qk * PER) >> 5)) * 4u,
+                                                                             key * MW * 4u, 0)
+                                     : 0u;
+                kr[c].nu = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(kn, 4u * row1, 4u * key, 0));
+                kr[c].gm = M > 0 ? (p.k_mu ? k_head
+                                           : __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(kg, 4u * row1, 4u * key, 0)))
+                                 : 0.f;
+            }
         };
 #pragma unroll
         for (int c = 0; c < KDEPTH && c < NCH; ++c) fetch1(c);
@@ -274,9 +312,17 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
         uint32_t sg;
     } vr[NCH];
     auto fetch2 = [&](int c) {
-        const int64_t rec = rec_of(c, lane);
-        Q::load(p.v_codes + rec * Q::CW + Q::word0(wave), wave, vr[c].W);
-        vr[c].sg = M > 0 ? p.v_signs[rec * MW + ((wave * PER) >> 5)] : 0u;
+        if constexpr (PAGED) {
+            const int64_t rec = rec_of(c, lane);
+            Q::load(p.v_codes + rec * Q::CW + Q::word0(wave), wave, vr[c].W);
+            vr[c].sg = M > 0 ? p.v_signs[rec * MW + ((wave * PER) >> 5)] : 0u;
+        } else {
+            const uint32_t key = (uint32_t)(64 * c);
+            dev::quarter_load_buf<D, BITS>(vc, (uint32_t)(lane * CW + Q::word0(wave)) * 4u, key * CW * 4u, wave, vr[c].W);
+            vr[c].sg = M > 0 ? __builtin_amdgcn_raw_buffer_load_b32(vs, (uint32_t)(lane * MW + ((wave * PER) >> 5)) * 4u,
+                                                                     key * MW * 4u, 0)
+                             : 0u;
+        }
     };
 #pragma unroll
     for (int c = 0; c < VDEPTH && c < NCH; ++c) fetch2(c);

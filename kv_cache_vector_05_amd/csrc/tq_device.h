@@ -189,6 +189,55 @@ struct Quarter {
     }
 };
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// buffer resource over [base, base + bytes) (gfx9 word 3: 32-bit elements, no
+// swizzle); loads past the end return 0
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int64_t bytes) {
+    const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0xFFFFFFFFll ? 0xFFFFFFFFu : (uint32_t)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
+}
+
+// Quarter<D, BITS>::load through a buffer resource: voff is the byte offset of
+// the lane's record word word0(qk), soff a scalar byte offset; no vector
+// address arithmetic
+template <int D, int BITS>
+__device__ __forceinline__ void quarter_load_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, int qk,
+                                                 uint32_t* W) {
+    using Q = Quarter<D, BITS>;
+    if constexpr (Q::NW == 3) {
+        const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, 0);
+        W[0] = v.x;
+        W[1] = v.y;
+        W[2] = v.z;
+    } else if constexpr (Q::NW == 4 && Q::ALIGNED) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+        W[0] = v.x;
+        W[1] = v.y;
+        W[2] = v.z;
+        W[3] = v.w;
+    } else if constexpr (Q::NW == 2 && Q::ALIGNED) {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+        W[0] = v.x;
+        W[1] = v.y;
+    } else if constexpr (Q::ALIGNED) {
+#pragma unroll
+        for (int i = 0; i < Q::NW; ++i) W[i] = __builtin_amdgcn_raw_buffer_load_b32(r, voff + 4u * i, soff, 0);
+    } else {
+        // the quarter straddles words: NW words from word0, the last clamped
+        // into the record, shifted into place
+        const int w0 = Q::word0(qk);
+#pragma unroll
+        for (int i = 0; i < Q::NW; ++i)
+            W[i] = __builtin_amdgcn_raw_buffer_load_b32(r, voff + 4u * (uint32_t)min(i, Q::CW - 1 - w0), soff, 0);
+        const int sh = (Q::BPG * qk) & 31;
+#pragma unroll
+        for (int i = 0; i + 1 < Q::NW; ++i) W[i] = __builtin_amdgcn_alignbit(W[i + 1], W[i], sh);
+    }
+}
+
 // Fixed point with four balanced base-128 digits: x ~= X * 2^-sh, |X| <= 2^26.
 __device__ __forceinline__ int fixed_shift(float amax) {
     if (!(amax > 0.0f)) return 0;
