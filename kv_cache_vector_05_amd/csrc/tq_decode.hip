@@ -197,9 +197,15 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
         const int cc = min(c, nch - 1);
         return record(cc, min(r, c1 - 1 - c0 - 64 * cc));
     };
-    // correction weights: gamma per record (QJL sketch) or the KV head's mu
-    const float k_head = p.k_mu ? p.k_mu[kh * p.k_mu_stride] : 0.f;
-    const float v_head = p.v_mu ? p.v_mu[kh * p.v_mu_stride] : 0.f;
+    // correction weights: gamma per record (QJL sketch) or the KV head's mu.
+    // Loads are unconditional (a resource of size zero reads zeros where a
+    // plane is absent) and a weight is the sum of the two readings, so no
+    // load sits behind a branch and every wait counts exactly.
+    const int64_t kmu = (int64_t)kh * p.k_mu_stride, vmu = (int64_t)kh * p.v_mu_stride;
+    const float k_head = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(dev::buf_rsrc(p.k_mu ? p.k_mu + kmu : nullptr, p.k_mu ? 4 : 0), 0, 0, 0));
+    const float v_head = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(dev::buf_rsrc(p.v_mu ? p.v_mu + vmu : nullptr, p.v_mu ? 4 : 0), 0, 0, 0));
     // contiguous records: one buffer resource per plane over the split's
     // records, so that every load is a fixed lane offset plus a scalar one
     // (keys past the split read zeros, which no output uses)
@@ -231,8 +237,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
             vgw[i] = M > 0 ? (p.v_mu ? v_head : p.v_rnorm[rec]) : 0.f;
         } else {
             vnw[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vn, 4u * kk, 0, 0));
-            vgw[i] = M > 0 ? (p.v_mu ? v_head : __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vg, 4u * kk, 0, 0)))
-                           : 0.f;
+            vgw[i] = M > 0 ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vg, 4u * kk, 0, 0)) + v_head : 0.f;
         }
     }
 
@@ -264,8 +269,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
                                                                              key * MW * 4u, 0)
                                      : 0u;
                 kr[c].nu = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(kn, 4u * row1, 4u * key, 0));
-                kr[c].gm = M > 0 ? (p.k_mu ? k_head
-                                           : __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(kg, 4u * row1, 4u * key, 0)))
+                kr[c].gm = M > 0 ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(kg, 4u * row1, 4u * key, 0)) + k_head
                                  : 0.f;
             }
         };
@@ -274,18 +278,20 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
         float* lgf = reinterpret_cast<float*>(lgs);
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
+            // every wave scores its keys of every chunk, also past the split's
+            // end (zeros, never used): with no branch around the tile, the
+            // records' loads are not moved behind one, where the wait for a
+            // chunk would also wait for the chunks fetched after it
             const int key0 = c0 + 64 * c + 16 * wave;
             float a[NRT];
-            if (key0 < c1) {  // the same for the whole wave
-                const bool valid = key0 + n < c1;
+            {
+                // keys past the end: + -inf (an add, not a select, so that the
+                // compiler does not put the norm loads behind a branch either)
+                const float off = key0 + n < c1 ? 0.0f : -INFINITY;
                 double lg[NRT];
                 tl.compute(kr[c].raw, kr[c].gm, PER, lane, lg);
 #pragma unroll
-                for (int rt = 0; rt < NRT; ++rt)
-                    a[rt] = valid ? (float)((double)p.scale * (double)kr[c].nu * lg[rt]) : -INFINITY;
-            } else {
-#pragma unroll
-                for (int rt = 0; rt < NRT; ++rt) a[rt] = -INFINITY;
+                for (int rt = 0; rt < NRT; ++rt) a[rt] = (float)((double)p.scale * (double)kr[c].nu * lg[rt]) + off;
             }
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt) {

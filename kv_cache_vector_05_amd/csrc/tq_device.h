@@ -474,47 +474,59 @@ struct alignas(16) PrepLds {
 // Preparation of R query rows by the 256 threads of a workgroup, in two
 // stages so that a caller can put other loads in flight behind the
 // preparation's own: load() issues every load, compute() waits for them and
-// fills the LDS (ending with a barrier).  Row r is query row
+// fills the LDS (ending with a barrier).  Every load is unconditional, through
+// a buffer resource (one of size zero reads zeros where an input is absent),
+// and the query rows go first: with no load behind a branch the in-order
+// count of outstanding loads stays exact, so compute() waits for the operand
+// it needs next and the loads issued after it (the sketch, the caller's
+// record prefetch) stay in flight.  Row r is query row
 // row_of(min(r, R - 1)); wave w prepares rows w, w + 4, ...  Thread (part,
 // l) of the sketch sums row l of S over one of 256/m coordinate ranges, so
-// each entry of S is read once and a wave's loads are contiguous.
+// each entry of S is read once and a wave's loads are contiguous.  The
+// work runs on the first four waves; a wider workgroup's other waves only
+// pass the barriers (their sketch loads fall past S and read nothing).
 template <int D, int M, int R>
 struct Prep {
     static constexpr int VPL = D / 64;
     static constexpr int NT = M > 0 ? 256 / M : 1;  // parts per sketch row
     static constexpr int NI = D / NT;               // S^T entries per thread
     static constexpr int RW = (R + 3) / 4;          // rows per wave
-    float sk[M > 0 ? NI : 1];
-    float x[RW][VPL];
-    float sg[VPL];
-    float c = 1.0f, sn = 0.0f;
+    // raw words as loaded; compute() converts them
+    uint32_t sk[M > 0 ? NI : 1];
+    uint32_t xw[RW][VPL];  // fp32, or the aligned word holding the bf16 element
+    uint32_t sgw[VPL];
+    uint32_t cw = 0u, snw = 0u;
 
     // pos: the queries' RoPE position (one sequence per workgroup)
     template <typename RowOf>
     __device__ void load(const PrepIn& in, RowOf row_of, int pos) {
         const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-        if constexpr (M > 0) {
-            if (!in.s_ident) {
-                const int l = t % M, prt = t / M;
-#pragma unroll
-                for (int k = 0; k < NI; ++k) sk[k] = in.sketch_t[(int64_t)(prt * NI + k) * M + l];
-            }
-        }
+        // query element e: word e (fp32) or the word holding bf16 element e
+        // (the other half is its neighbour; rows have an even length)
+        const __amdgpu_buffer_rsrc_t rq = buf_rsrc(in.q, 0xFFFFFFFFll);
 #pragma unroll
         for (int j = 0; j < RW; ++j) {
             const int64_t row = row_of(min(wave + 4 * j, R - 1));
 #pragma unroll
             for (int v = 0; v < VPL; ++v) {
-                const int64_t e = row * D + lane + 64 * v;
-                x[j][v] = in.bf16 ? __uint_as_float((uint32_t) static_cast<const uint16_t*>(in.q)[e] << 16)
-                                  : static_cast<const float*>(in.q)[e];
+                const uint32_t e = (uint32_t)(row * D + lane + 64 * v);
+                xw[j][v] = __builtin_amdgcn_raw_buffer_load_b32(rq, in.bf16 ? (2u * e) & ~3u : 4u * e, 0, 0);
             }
         }
+        const __amdgpu_buffer_rsrc_t rsg = buf_rsrc(in.sigma, in.norot ? 0 : D * 4);
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) sg[v] = in.norot ? 1.0f : in.sigma[lane + 64 * v];
-        if (in.rope_cos) {
-            c = in.rope_cos[(int64_t)pos * (D / 2) + lane % (D / 2)];
-            sn = in.rope_sin[(int64_t)pos * (D / 2) + lane % (D / 2)];
+        for (int v = 0; v < VPL; ++v) sgw[v] = __builtin_amdgcn_raw_buffer_load_b32(rsg, 4u * (lane + 64 * v), 0, 0);
+        const int64_t rope_bytes = in.rope_cos ? ((int64_t)in.L_cap + 1) * (D / 2) * 4 : 0;
+        const __amdgpu_buffer_rsrc_t rc = buf_rsrc(in.rope_cos, rope_bytes), rsn = buf_rsrc(in.rope_sin, rope_bytes);
+        const uint32_t ro = 4u * (uint32_t)(pos * (D / 2) + lane % (D / 2));
+        cw = __builtin_amdgcn_raw_buffer_load_b32(rc, ro, 0, 0);
+        snw = __builtin_amdgcn_raw_buffer_load_b32(rsn, ro, 0, 0);
+        if constexpr (M > 0) {
+            const __amdgpu_buffer_rsrc_t rsk = buf_rsrc(in.sketch_t, in.s_ident ? 0 : D * M * 4);
+            const int l = t % M, prt = t / M;
+#pragma unroll
+            for (int k = 0; k < NI; ++k)
+                sk[k] = __builtin_amdgcn_raw_buffer_load_b32(rsk, 4u * (uint32_t)((prt * NI + k) * M + l), 0, 0);
         }
     }
 
@@ -526,7 +538,11 @@ struct Prep {
             if (r >= R) break;  // the same for the whole wave
             float xv[VPL];
 #pragma unroll
-            for (int v = 0; v < VPL; ++v) xv[v] = x[j][v];
+            for (int v = 0; v < VPL; ++v) {
+                const uint32_t w = xw[j][v];
+                xv[v] = __uint_as_float(in.bf16 ? ((lane & 1) ? w & 0xFFFF0000u : w << 16) : w);
+            }
+            const float c = __uint_as_float(cw), sn = __uint_as_float(snw);
             if (in.rope_cos) {
                 // RoPE: pair (i, i + d/2) in one lane (d = 128) or lanes l, l ^ 32 (d = 64)
                 if constexpr (VPL == 2) {
@@ -540,7 +556,7 @@ struct Prep {
             }
             if (!in.norot) {
 #pragma unroll
-                for (int v = 0; v < VPL; ++v) xv[v] *= sg[v];
+                for (int v = 0; v < VPL; ++v) xv[v] *= __uint_as_float(sgw[v]);
                 // H_d in Sylvester order: butterflies over every index bit
 #pragma unroll
                 for (int sp = 1; sp < 64; sp <<= 1) {
@@ -582,18 +598,18 @@ struct Prep {
             const bool sketch = !in.s_ident;
             __syncthreads();
             // partial sums of s = S q' (or s = q')
-            if (sketch) {
+            if (sketch && t < 256) {
                 const int prt = t / M;
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     float acc = 0.0f;
 #pragma unroll
-                    for (int k = 0; k < NI; ++k) acc = fmaf(sk[k], L.qp[r][prt * NI + k], acc);
+                    for (int k = 0; k < NI; ++k) acc = fmaf(__uint_as_float(sk[k]), L.qp[r][prt * NI + k], acc);
                     L.part[r][t] = acc;
                 }
             }
             __syncthreads();
-            for (int idx = t; idx < R * M; idx += 256) {
+            for (int idx = t; t < 256 && idx < R * M; idx += 256) {
                 const int r = idx / M, l = idx % M;
                 float sv = 0.0f;
                 if (sketch) {

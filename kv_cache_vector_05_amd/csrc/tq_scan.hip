@@ -16,12 +16,15 @@
 // and coordinate quarter l / 16, and holds the logit of (query l / 16, key
 // l % 16) of each four-query row tile.
 //
-// One workgroup (four waves) serves one KV head of one sequence, up to 4 NRT
-// of its query heads and a contiguous run of keys, sized so that the whole
-// grid is resident at once.  Records are read with buffer loads whose
-// per-tile advance is a scalar offset (no vector instructions on addresses);
-// every load is unconditional, so each wave keeps its next four tiles of
-// records in flight behind the one it computes.
+// One workgroup serves one KV head of one sequence, up to 4 NRT of its query
+// heads and a contiguous run of keys, sized so that the whole grid is
+// resident at once: sixteen waves when it prepares its four queries itself
+// (one row tile; the preparation runs once per workgroup, on four of the
+// waves), four waves reading prepared queries otherwise.  Records are read
+// with buffer loads whose per-tile advance is a scalar offset (no vector
+// instructions on addresses); every load is unconditional, so each wave keeps
+// its next eight (four) tiles of records in flight behind the one it
+// computes.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -76,8 +79,25 @@ struct ScanArgs {
     dev::FastDiv div_page;
 };
 
+// waves per workgroup: a single row tile prepares its queries in the kernel,
+// on four of the waves, so the workgroup is as wide as the CU takes (the
+// preparation is repeated once per workgroup); more row tiles read prepared
+// queries and keep four waves
+constexpr int kFusedWaves = 16;
+template <int NRT>
+constexpr int scan_waves() {
+    return NRT == 1 ? kFusedWaves : 4;
+}
+// tiles of records each wave keeps in flight behind the one it computes: the
+// wide workgroup runs at four waves per SIMD whatever its register count, so
+// it takes twice the depth (the bytes in flight set the streaming rate)
+template <int NRT>
+constexpr int scan_depth() {
+    return NRT == 1 ? 8 : 4;
+}
+
 template <int D, int BITS, int NRT, int M, bool PAGED>
-__global__ __launch_bounds__(256) void scan_kernel(ScanArgs p) {
+__global__ __launch_bounds__(64 * scan_waves<NRT>()) void scan_kernel(ScanArgs p) {
     using Q = dev::Quarter<D, BITS>;
     constexpr int R = 4 * NRT;       // query rows of the workgroup
     constexpr int NC = Q::LPG / 16;  // K = 64 chunks over the lane's coordinates
@@ -106,8 +126,9 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs p) {
     const int sl = dev::clamp_len(p.seq_len, b, p.L_cap);
     const int kend = min(sl, p.k0 + p.klen);
     // a workgroup without keys leaves at once (before any barrier)
-    if (p.k0 + (int)blockIdx.y * 4 * p.tiles_per_wave * 16 >= kend) return;
-    const int kbeg = p.k0 + ((int)blockIdx.y * 4 + wave) * p.tiles_per_wave * 16;
+    constexpr int NWV = scan_waves<NRT>();
+    if (p.k0 + (int)blockIdx.y * NWV * p.tiles_per_wave * 16 >= kend) return;
+    const int kbeg = p.k0 + ((int)blockIdx.y * NWV + wave) * p.tiles_per_wave * 16;
     const int ntile = __builtin_amdgcn_readfirstlane(max(0, min(p.tiles_per_wave, (kend - kbeg + 15) / 16)));
     const int nfull = __builtin_amdgcn_readfirstlane(max(0, min(p.tiles_per_wave, (kend - kbeg) / 16)));
     const int mw = p.m >> 5;
@@ -127,7 +148,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs p) {
         rc = make_rsrc(p.codes + rec_w * CW, (p.cap - rec_w) * CW * 4);
         rs_ = make_rsrc(p.signs + rec_w * mw, (p.cap - rec_w) * mw * 4);
         rn = make_rsrc(p.norm + rec_w, (p.cap - rec_w) * 4);
-        rg = make_rsrc(p.rnorm + rec_w, (p.cap - rec_w) * 4);
+        rg = make_rsrc(g_per_key ? p.rnorm + rec_w : nullptr, g_per_key ? (p.cap - rec_w) * 4 : 0);
     }
     struct Raw {
         uint32_t W[Q::NW];
@@ -189,20 +210,25 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs p) {
         uint32_t so_n;
         if constexpr (PAGED) {
             rn = make_rsrc(p.norm + r.rec, (p.cap - r.rec) * 4);
-            rg = make_rsrc(p.rnorm + r.rec, (p.cap - r.rec) * 4);
+            rg = make_rsrc(g_per_key ? p.rnorm + r.rec : nullptr, g_per_key ? (p.cap - r.rec) * 4 : 0);
             so_n = 0;
         } else {
             so_n = (uint32_t)tile * 64u;
         }
         r.nu = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rn, vo_n, so_n, 0));
-        if (NCS > 0 && g_per_key) r.gm = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, vo_n, so_n, 0));
-        else r.gm = g_head;
+        // gamma per key, or the head's mu (the load then reads zeros)
+        if constexpr (NCS > 0) {
+            // an add rather than a select keeps the load unconditional
+            r.gm = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, vo_n, so_n, 0)) + g_head;
+        } else {
+            r.gm = g_head;
+        }
     };
     // ---- query preparation: every workgroup of a (sequence, KV head) row
     // tile prepares its rows itself (rows past the group repeat the last
-    // query and are never stored).  Its loads go first, then the record
-    // prefetch: loads complete in order, so the preparation waits for its own
-    // loads only and computes while the first records are in flight.
+    // query and are never stored).  Its loads go first, then the first
+    // records: loads complete in order, so the preparation waits for its own
+    // loads only and computes while those records are in flight.
     dev::Prep<D, M, FUSE ? R : 1> pr;
     intx4 aq[NRT][NC];
     intx4 as[NRT][NCS > 0 ? NCS : 1];
@@ -232,14 +258,18 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs p) {
     // reloads the last one (a cache hit), so each loop step issues the same
     // loads and the waits for a tile's data leave the later tiles' in flight.
     const auto clampt = [&](int tile) { return max(0, min(tile, ntile - 1)); };
-    Raw raw[4];
+    // the first half of the tiles in flight are requested before the
+    // preparation, the rest after it (all of them in flight across it would
+    // raise the register peak)
+    constexpr int PF = scan_depth<NRT>();
+    Raw raw[PF];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < PF / 2; ++i) {
         fetch_codes(clampt(i), raw[i]);
         fetch_scalars(clampt(i), raw[i]);
     }
-    {
-        const uint32_t v = (uint32_t)t;  // 256 threads: one table entry each
+    if (t < 256) {
+        const uint32_t v = (uint32_t)t;  // one table entry per thread of the first four waves
         stab[t] = u32x2{dev::spread4(v), dev::spread4(v >> 4)};
     }
     if constexpr (FUSE) {
@@ -255,6 +285,11 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs p) {
         for (int k = 0; k < 3; ++k) sc[0][k] = prep.scl[qk][k];
     } else {
         __syncthreads();
+    }
+#pragma unroll
+    for (int i = PF / 2; i < PF; ++i) {
+        fetch_codes(clampt(i), raw[i]);
+        fetch_scalars(clampt(i), raw[i]);
     }
     double qscale[NRT], zk[NRT], zc[NRT];
 #pragma unroll
@@ -344,23 +379,21 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs p) {
         }
     };
     // One tile per step: its MFMAs, then its slot refilled with the tile
-    // four ahead (code and sign words first, as soon as the MFMAs have read
+    // PF ahead (code and sign words first, as soon as the MFMAs have read
     // them; nu and gamma once the tile is combined).  A tile past the
     // wave's last computes on a reloaded tile and stores nothing (the launch
-    // gives waves multiples of four tiles, so only the last wave of a row
+    // gives waves multiples of PF tiles, so only the last wave of a row
     // does this).
     auto step = [&](int tile, int s0) {
         Acc a0;
         mma(raw[s0], a0);
-        fetch_codes(clampt(tile + 4), raw[s0]);
+        fetch_codes(clampt(tile + PF), raw[s0]);
         finish(a0, raw[s0].nu, raw[s0].gm, tile);
-        fetch_scalars(clampt(tile + 4), raw[s0]);
+        fetch_scalars(clampt(tile + PF), raw[s0]);
     };
-    for (int tile = 0; tile < ntile; tile += 4) {
-        step(tile, 0);
-        step(tile + 1, 1);
-        step(tile + 2, 2);
-        step(tile + 3, 3);
+    for (int tile = 0; tile < ntile; tile += PF) {
+#pragma unroll
+        for (int i = 0; i < PF; ++i) step(tile + i, i);
     }
 }
 
@@ -394,15 +427,15 @@ ScanFn pick_bits(int bits, int nrt, int m) {
     return nullptr;
 }
 
-int64_t resident_blocks(const void* fn) {
+int64_t resident_blocks(const void* fn, int threads) {
     static thread_local const void* last_fn = nullptr;
     static thread_local int64_t last = 0;
     if (fn == last_fn) return last;
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, 0) != hipSuccess || per_cu < 1)
-        return 1024;
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, 0) != hipSuccess || per_cu < 1)
+        return 1024 * 4 / (threads / 64);
     last_fn = fn;
     last = (int64_t)cus * per_cu;
     return last;
@@ -478,12 +511,14 @@ hipError_t launch_scan(const tq_codebook* ck, const tq_packed& k, const AttnArgs
     const int64_t gx = (int64_t)a.B * a.h_kv * ngroups;
     const int64_t tiles_row = (klen + 15) / 16;
     if (gx == 0 || tiles_row == 0) return hipSuccess;
-    const int64_t resident = resident_blocks((const void*)fn);
+    const int nwv = nrt == 1 ? scan_waves<1>() : scan_waves<2>();
+    const int64_t resident = resident_blocks((const void*)fn, 64 * nwv);
     const int64_t gy_want = std::max<int64_t>(1, (resident + gx - 1) / gx);
-    // a multiple of four tiles per wave (the loop's step)
-    p.tiles_per_wave = (int)(((tiles_row + 4 * gy_want - 1) / (4 * gy_want) + 3) / 4 * 4);
-    const int64_t gy = (tiles_row + 4 * (int64_t)p.tiles_per_wave - 1) / (4 * (int64_t)p.tiles_per_wave);
-    hipLaunchKernelGGL(fn, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, stream, p);
+    // a multiple of the prefetch depth per wave (the loop's step)
+    const int pf = nrt == 1 ? scan_depth<1>() : scan_depth<2>();
+    p.tiles_per_wave = (int)(((tiles_row + nwv * gy_want - 1) / (nwv * gy_want) + pf - 1) / pf * pf);
+    const int64_t gy = (tiles_row + nwv * (int64_t)p.tiles_per_wave - 1) / (nwv * (int64_t)p.tiles_per_wave);
+    hipLaunchKernelGGL(fn, dim3((unsigned)gx, (unsigned)gy), dim3(64 * nwv), 0, stream, p);
     return hipGetLastError();
 }
 
