@@ -1,14 +1,26 @@
-// Plain fp32 GEMM on CDNA MFMA: C[M][N] = A[M][K] * B[N][K]^T, row-major
-// operands with the K index contiguous.  Used by the dense (Haar) rotation
-// path: rotating unit vectors by Pi, sketching residuals by S, preparing
-// queries, and scoring a dense-rotation index.
+// fp32 GEMM on the bf16 matrix cores: C[M][N] = A[M][K] * B[N][K]^T,
+// row-major operands with the K index contiguous.  Used by the dense (Haar)
+// rotation path: rotating unit vectors by Pi, sketching residuals by S,
+// preparing queries, and scoring a dense-rotation index.
+//
+// Each fp32 operand is split into three bf16 pieces, x = h + m + l (each the
+// remainder of the previous, rounded to nearest: |x - h - m - l| <= 2^-27 |x|
+// with bf16's 8-bit significands and fp32's exponent range, so no scaling is
+// needed).  A product keeps the six piece products down to the 2^-16 level,
+//     a b ~ ah bh + ah bm + am bh + ah bl + al bh + am bm,
+// and leaves out am bl, al bm, al bl (each below 2^-24 |a b|, the rounding of
+// an fp32 product).  Six v_mfma_f32_32x32x16_bf16 per 16 K-steps against the
+// 64 K-steps of eight v_mfma_f32_32x32x2_f32: about 2.7 times the fp32
+// matrix rate, with fp32 accumulation as before.
 //
 // Tiling: 256 threads (4 wave64s) own a 128 x 128 tile of C; each wave owns a
-// 64 x 64 quarter as 2 x 2 blocks of v_mfma_f32_32x32x2f32.  K advances in
-// steps of 32 through LDS tiles padded to 33 floats per row so that the 32
-// rows an MFMA operand reads fall in distinct banks.  The next step's operands
-// are loaded into registers (float4 where rows are 16-byte aligned) while the
-// current step multiplies, so global latency overlaps the matrix work.
+// 64 x 64 quarter as 2 x 2 blocks of 32 x 32.  K advances in steps of 32: the
+// step's operands are loaded as fp32 through buffer resources over the tile's
+// rows (float4 where rows are 16-byte aligned; columns past K read zeros),
+// split while they are written to LDS (rows padded to 40 bf16, so that the
+// 16-byte reads of an MFMA operand fall in distinct banks), and the operands
+// of the step two ahead are loaded into registers while the current one
+// multiplies.
 #include <hip/hip_runtime.h>
 
 #include "tq_internal.h"
@@ -17,52 +29,84 @@ namespace tq {
 namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 128;
 constexpr int kKt = 32;
-constexpr int kLd = kKt + 1;
+constexpr int kRow = kKt + 8;                  // bf16 per LDS row
+constexpr int kPiece = kTile * kRow;           // bf16 per piece plane
 constexpr int kLoads = kTile * kKt / 4 / 256;  // float4 slots per thread per operand and step
 
-// rows m0 + idx/8 of X, columns k0 + 4 (idx % 8) .. + 3 for the thread's slots
+// buffer resource over the tile's rows [r0, r0 + 128) of X (fewer at the
+// last tile); loads past it return zeros
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const float* X, int64_t ldx, int64_t r0, int rows) {
+    const int64_t n = rows - r0 < kTile ? rows - r0 : kTile;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(X + r0 * ldx), (short)0, (int)(n * ldx * 4), 0x00020000);
+}
+
+// rows idx/8 of the tile, columns k0 + 4 (idx % 8) .. + 3 for the thread's
+// slots.  Every load is issued (columns past K read at an offset past the
+// tile, which returns zeros), so no load sits behind a branch and the waits
+// for one step leave the next step's loads in flight.
 template <bool VEC>
-__device__ __forceinline__ void load_step(const float* __restrict__ X, int64_t ldx, int64_t r0, int rows, int k0,
-                                          int K, int tid, float4 (&v)[kLoads]) {
+__device__ __forceinline__ void load_step(__amdgpu_buffer_rsrc_t X, int64_t ldx, int k0, int K, int tid,
+                                          float4 (&v)[kLoads]) {
+    constexpr uint32_t kOut = 0x80000000u;  // beyond any tile
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
         const int idx = tid + 256 * i;
-        const int64_t r = r0 + (idx >> 3);
         const int k = k0 + 4 * (idx & 7);
+        const uint32_t o = (uint32_t)(((idx >> 3) * ldx + k) * 4);
         if constexpr (VEC) {
-            v[i] = (r < rows && k < K) ? *reinterpret_cast<const float4*>(X + r * ldx + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+            v[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(X, k < K ? o : kOut, 0, 0));
         } else {
-            const bool ok = r < rows;
-            v[i].x = ok && k < K ? X[r * ldx + k] : 0.f;
-            v[i].y = ok && k + 1 < K ? X[r * ldx + k + 1] : 0.f;
-            v[i].z = ok && k + 2 < K ? X[r * ldx + k + 2] : 0.f;
-            v[i].w = ok && k + 3 < K ? X[r * ldx + k + 3] : 0.f;
+            v[i].x = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(X, k < K ? o : kOut, 0, 0));
+            v[i].y = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(X, k + 1 < K ? o + 4 : kOut, 0, 0));
+            v[i].z = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(X, k + 2 < K ? o + 8 : kOut, 0, 0));
+            v[i].w = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(X, k + 3 < K ? o + 12 : kOut, 0, 0));
         }
     }
 }
 
-__device__ __forceinline__ void store_step(float* S, int tid, const float4 (&v)[kLoads]) {
+// the three bf16 pieces of a pair of floats, packed two to a word
+__device__ __forceinline__ void split3(float a, float b, uint32_t& h, uint32_t& m, uint32_t& l) {
+    h = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a, (__bf16)b});
+    const float ra = a - __uint_as_float(h << 16), rb = b - __uint_as_float(h & 0xFFFF0000u);
+    m = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)ra, (__bf16)rb});
+    const float sa = ra - __uint_as_float(m << 16), sb = rb - __uint_as_float(m & 0xFFFF0000u);
+    l = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)sa, (__bf16)sb});
+}
+
+// the thread's slots split into the three piece planes of S
+__device__ __forceinline__ void store_step(__bf16* S, int tid, const float4 (&v)[kLoads]) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
         const int idx = tid + 256 * i;
-        float* d = S + (idx >> 3) * kLd + 4 * (idx & 7);
-        d[0] = v[i].x;
-        d[1] = v[i].y;
-        d[2] = v[i].z;
-        d[3] = v[i].w;
+        const int o = (idx >> 3) * kRow + 4 * (idx & 7);
+        uint32_t h0, m0, l0, h1, m1, l1;
+        split3(v[i].x, v[i].y, h0, m0, l0);
+        split3(v[i].z, v[i].w, h1, m1, l1);
+        *reinterpret_cast<u32x2*>(S + o) = u32x2{h0, h1};
+        *reinterpret_cast<u32x2*>(S + kPiece + o) = u32x2{m0, m1};
+        *reinterpret_cast<u32x2*>(S + 2 * kPiece + o) = u32x2{l0, l1};
     }
 }
 
+// MFMA operand: row `row` of the tile, K slots 8 (lane / 32) .. + 7 of the
+// 16-wide sub-step kk, from piece plane p
+__device__ __forceinline__ bf16x8 operand(const __bf16* S, int p, int row, int kk, int lane) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(S + p * kPiece + row * kRow + 16 * kk + 8 * (lane >> 5)));
+}
+
 template <bool VEC>
-__global__ __launch_bounds__(256) void gemm_nt_f32(const float* __restrict__ A, int64_t lda,
-                                                   const float* __restrict__ B, int64_t ldb,
-                                                   float* __restrict__ C, int64_t ldc, int M, int N,
-                                                   int K) {
-    __shared__ float As[kTile * kLd];
-    __shared__ float Bs[kTile * kLd];
+__global__ __launch_bounds__(256) void gemm_nt_bf16x3(const float* __restrict__ A, int64_t lda,
+                                                      const float* __restrict__ B, int64_t ldb,
+                                                      float* __restrict__ C, int64_t ldc, int M, int N, int K) {
+    __shared__ __attribute__((aligned(16))) __bf16 As[3 * kPiece];
+    __shared__ __attribute__((aligned(16))) __bf16 Bs[3 * kPiece];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -72,37 +116,69 @@ __global__ __launch_bounds__(256) void gemm_nt_f32(const float* __restrict__ A, 
     const int wn = (wave & 1) * 64;
 
     floatx16 acc[2][2];
+#pragma unroll
     for (int i = 0; i < 2; ++i)
+#pragma unroll
         for (int j = 0; j < 2; ++j)
+#pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    float4 va[kLoads], vb[kLoads];
-    load_step<VEC>(A, lda, m0, M, 0, K, tid, va);
-    load_step<VEC>(B, ldb, n0, N, 0, K, tid, vb);
-    for (int k0 = 0; k0 < K; k0 += kKt) {
-        store_step(As, tid, va);
-        store_step(Bs, tid, vb);
-        __syncthreads();
-        if (k0 + kKt < K) {  // the next step's operands, in flight during this step
-            load_step<VEC>(A, lda, m0, M, k0 + kKt, K, tid, va);
-            load_step<VEC>(B, ldb, n0, N, k0 + kKt, K, tid, vb);
-        }
+    // operands of two steps in flight: step s + 2 is requested once step s
+    // is in LDS, so each load has two steps of matrix work to arrive in
+    const __amdgpu_buffer_rsrc_t ra = tile_rsrc(A, lda, m0, M), rb = tile_rsrc(B, ldb, n0, N);
+    float4 va[2][kLoads], vb[2][kLoads];
 #pragma unroll
-        for (int kk = 0; kk < kKt; kk += 2) {
-            const int kidx = kk + (lane >> 5);
-            float a[2], b[2];
-            for (int i = 0; i < 2; ++i) a[i] = As[(wm + 32 * i + (lane & 31)) * kLd + kidx];
-            for (int j = 0; j < 2; ++j) b[j] = Bs[(wn + 32 * j + (lane & 31)) * kLd + kidx];
-            for (int i = 0; i < 2; ++i)
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
+    for (int s = 0; s < 2; ++s) {
+        load_step<VEC>(ra, lda, s * kKt, K, tid, va[s]);
+        load_step<VEC>(rb, ldb, s * kKt, K, tid, vb[s]);
+    }
+    // K-steps in pairs, one per register buffer: the buffered operands split
+    // into LDS, the step two ahead requested into the same registers, then
+    // the step's MFMAs.  Steps past K (at most one, when their count is odd,
+    // and the requests ahead) read zeros and add nothing.
+    for (int k0 = 0; k0 < K; k0 += 2 * kKt) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            store_step(As, tid, va[h]);
+            store_step(Bs, tid, vb[h]);
+            __syncthreads();
+            load_step<VEC>(ra, lda, k0 + (h + 2) * kKt, K, tid, va[h]);
+            load_step<VEC>(rb, ldb, k0 + (h + 2) * kKt, K, tid, vb[h]);
+#pragma unroll
+            for (int kk = 0; kk < kKt / 16; ++kk) {
+                bf16x8 a[2][3], b[2][3];
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int p = 0; p < 3; ++p) {
+                        a[i][p] = operand(As, p, wm + 32 * i + (lane & 31), kk, lane);
+                        b[i][p] = operand(Bs, p, wn + 32 * i + (lane & 31), kk, lane);
+                    }
+                // smallest terms first: each enters the fp32 sum before the larger ones
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        floatx16 c = acc[i][j];
+                        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i][1], b[j][1], c, 0, 0, 0);
+                        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i][0], b[j][2], c, 0, 0, 0);
+                        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i][2], b[j][0], c, 0, 0, 0);
+                        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i][0], b[j][1], c, 0, 0, 0);
+                        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i][1], b[j][0], c, 0, 0, 0);
+                        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i][0], b[j][0], c, 0, 0, 0);
+                        acc[i][j] = c;
+                    }
+            }
+            __syncthreads();
         }
-        __syncthreads();
     }
     // D[i][j] of a 32x32 block: column j = lane % 32, row 8*(r/4) + 4*(lane/32) + r%4
+#pragma unroll
     for (int i = 0; i < 2; ++i)
+#pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int64_t col = n0 + wn + 32 * j + (lane & 31);
+#pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                 if (row < M && col < N) C[row * ldc + col] = acc[i][j][r];
@@ -118,8 +194,8 @@ hipError_t launch_gemm_nt(const float* A, int64_t lda, const float* B, int64_t l
     dim3 grid((N + kTile - 1) / kTile, (M + kTile - 1) / kTile);
     // float4 loads need 16-byte aligned rows
     const bool vec = ((lda | ldb) & 3) == 0 && ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & 15) == 0;
-    if (vec) hipLaunchKernelGGL(gemm_nt_f32<true>, grid, dim3(256), 0, stream, A, lda, B, ldb, C, ldc, M, N, K);
-    else hipLaunchKernelGGL(gemm_nt_f32<false>, grid, dim3(256), 0, stream, A, lda, B, ldb, C, ldc, M, N, K);
+    if (vec) hipLaunchKernelGGL(gemm_nt_bf16x3<true>, grid, dim3(256), 0, stream, A, lda, B, ldb, C, ldc, M, N, K);
+    else hipLaunchKernelGGL(gemm_nt_bf16x3<false>, grid, dim3(256), 0, stream, A, lda, B, ldb, C, ldc, M, N, K);
     return hipGetLastError();
 }
 
