@@ -101,17 +101,30 @@ __device__ __forceinline__ bf16x8 operand(const __bf16* S, int p, int row, int k
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(S + p * kPiece + row * kRow + 16 * kk + 8 * (lane >> 5)));
 }
 
+// Tile order: workgroup w of a one-dimensional grid takes tile (f, s) of a
+// "fast" axis with nf tiles (the one with fewer) and a "slow" axis, as
+// w = s % 8 + 8 (f + nf (s / 8)).  Workgroups are dealt to the eight XCDs in
+// turn, so every tile sharing the slow index s runs on one XCD, together:
+// that operand's 128 rows are read from HBM once and served from that XCD's
+// L2 to the others (for the index scan, the dequantised keys against the
+// few query tiles).
 template <bool VEC>
 __global__ __launch_bounds__(256) void gemm_nt_bf16x3(const float* __restrict__ A, int64_t lda,
                                                       const float* __restrict__ B, int64_t ldb,
-                                                      float* __restrict__ C, int64_t ldc, int M, int N, int K) {
+                                                      float* __restrict__ C, int64_t ldc, int M, int N, int K,
+                                                      int m_fast) {
     __shared__ __attribute__((aligned(16))) __bf16 As[3 * kPiece];
     __shared__ __attribute__((aligned(16))) __bf16 Bs[3 * kPiece];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int64_t m0 = (int64_t)blockIdx.y * kTile;
-    const int64_t n0 = (int64_t)blockIdx.x * kTile;
+    const int tm = (M + kTile - 1) / kTile, tn = (N + kTile - 1) / kTile;
+    const int nf = m_fast ? tm : tn, ns = m_fast ? tn : tm;
+    const int w = blockIdx.x, r = w >> 3;
+    const int f = r % nf, sl = (r / nf) * 8 + (w & 7);
+    if (sl >= ns) return;  // the last group's padding
+    const int64_t m0 = (int64_t)(m_fast ? f : sl) * kTile;
+    const int64_t n0 = (int64_t)(m_fast ? sl : f) * kTile;
     const int wm = (wave >> 1) * 64;  // wave's row offset inside the tile
     const int wn = (wave & 1) * 64;
 
@@ -191,11 +204,19 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16x3(const float* __restrict__ 
 hipError_t launch_gemm_nt(const float* A, int64_t lda, const float* B, int64_t ldb, float* C,
                           int64_t ldc, int M, int N, int K, hipStream_t stream) {
     if (M <= 0 || N <= 0) return hipSuccess;
-    dim3 grid((N + kTile - 1) / kTile, (M + kTile - 1) / kTile);
+    const int64_t tm = (M + kTile - 1) / kTile, tn = (N + kTile - 1) / kTile;
+    const int m_fast = tm <= tn ? 1 : 0;
+    const int64_t nf = m_fast ? tm : tn, ns = m_fast ? tn : tm;
+    const int64_t blocks = nf * ((ns + 7) / 8) * 8;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     // float4 loads need 16-byte aligned rows
     const bool vec = ((lda | ldb) & 3) == 0 && ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & 15) == 0;
-    if (vec) hipLaunchKernelGGL(gemm_nt_bf16x3<true>, grid, dim3(256), 0, stream, A, lda, B, ldb, C, ldc, M, N, K);
-    else hipLaunchKernelGGL(gemm_nt_bf16x3<false>, grid, dim3(256), 0, stream, A, lda, B, ldb, C, ldc, M, N, K);
+    if (vec)
+        hipLaunchKernelGGL(gemm_nt_bf16x3<true>, dim3((unsigned)blocks), dim3(256), 0, stream, A, lda, B, ldb, C, ldc, M, N,
+                           K, m_fast);
+    else
+        hipLaunchKernelGGL(gemm_nt_bf16x3<false>, dim3((unsigned)blocks), dim3(256), 0, stream, A, lda, B, ldb, C, ldc, M,
+                           N, K, m_fast);
     return hipGetLastError();
 }
 
