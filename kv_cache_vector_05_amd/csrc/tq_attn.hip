@@ -812,9 +812,11 @@ __global__ __launch_bounds__(256) void decode_merge_fast_kernel(MergeK p) {
 
 // First merge stage for many splits: workgroup (row, g) combines splits
 // [32 g, 32 g + 32) of the row by log-sum-exp into one partial of the same
-// form (max, sum, A_y, A_z), so the final merge reads few partials.
+// form (max, sum, A_y, A_z), so the final merge reads few partials.  The
+// launch gives a thread per column (up to 512), so every column's 32 loads
+// are in flight at once.
 constexpr int kMergeGroup = 32;
-__global__ __launch_bounds__(256) void decode_merge_group_kernel(const float* part, int nsplit, int width,
+__global__ __launch_bounds__(512) void decode_merge_group_kernel(const float* part, int nsplit, int width,
                                                                  float* out, int ngroup) {
     __shared__ float fw[kMergeGroup];
     __shared__ float red[2];
@@ -976,11 +978,11 @@ size_t logits_workspace_bytes(const tq_codebook* ck, int64_t B, int Hq, int h_kv
         return bytes;
     }
     if (!ck->dense) {
-        // one row tile per KV head: the scan prepares its queries in LDS
+        // the scan prepares its queries in LDS (one row tile per KV head, or two without a sketch)
         const int G = h_kv > 0 ? Hq / h_kv : 1;
-        size_t bytes = !scan_supported(ck)         ? align256(rows * (d + m) * 4)
-                       : scan_row_tiles(G) == 1 ? 0
-                                                : align256(qdigits_workspace_bytes(ck, (int64_t)rows));
+        size_t bytes = !scan_supported(ck)           ? align256(rows * (d + m) * 4)
+                       : scan_prepares_queries(ck, G) ? 0
+                                                  : align256(qdigits_workspace_bytes(ck, (int64_t)rows));
         if (top_k) bytes += align256(rows * chunk * 4);
         return bytes;
     }
@@ -1041,7 +1043,7 @@ hipError_t launch_logits(const tq_codebook* ck, const tq_packed& k, const AttnAr
         return hipSuccess;
     }
     if (!ck->dense && scan_supported(ck)) {
-        const bool fused = scan_row_tiles(G) == 1;
+        const bool fused = scan_prepares_queries(ck, G);
         QDigits qd{};
         char* wsc = ws;
         if (!fused) {
@@ -1227,7 +1229,8 @@ hipError_t launch_decode(const tq_codebook* ck, const tq_codebook* cv, const tq_
         if (nsplit > 2 * kMergeGroup) {
             const int ngroup = (nsplit + kMergeGroup - 1) / kMergeGroup;
             float* part2 = part + align256(rows * nsplit * width * 4) / 4;
-            hipLaunchKernelGGL(decode_merge_group_kernel, dim3((unsigned)rows, (unsigned)ngroup), dim3(256), 0, stream,
+            const unsigned threads = (unsigned)std::min(512, (width + 63) / 64 * 64);
+            hipLaunchKernelGGL(decode_merge_group_kernel, dim3((unsigned)rows, (unsigned)ngroup), dim3(threads), 0, stream,
                                part, nsplit, width, part2, ngroup);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;

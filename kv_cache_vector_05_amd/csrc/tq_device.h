@@ -458,21 +458,21 @@ struct PrepIn {
     const float* sketch_t;    // S^T [d][m]
 };
 
-// LDS of the preparation of R query rows
-template <int D, int M, int R>
+// LDS of the preparation of R query rows (ST threads sum the sketch)
+template <int D, int M, int R, int ST = 256>
 struct alignas(16) PrepLds {
     static constexpr int NCS = M == 0 ? 0 : (M >= 64 ? M / 64 : 1);  // 64-row sketch chunks of the MFMA
     static constexpr int SDW = 64 * (NCS > 0 ? NCS : 1);             // bytes per digit row of s
     float qp[R][D];               // q'
-    float part[M > 0 ? R : 1][256];  // partial sums of s (one per thread)
+    float part[M > 0 ? R : 1][ST];  // partial sums of s (one per thread)
     float s[R][M > 0 ? M : 1];
     int8_t qd[R][4][D];           // digit rows of q'
     int8_t sd[R][4][SDW];         // digit rows of s in MFMA slot order
     float scl[R][3];              // shift(q'), shift(s), sum of the fixed-point s values
 };
 
-// Preparation of R query rows by the 256 threads of a workgroup, in two
-// stages so that a caller can put other loads in flight behind the
+// Preparation of R query rows by the first four waves of a workgroup (the
+// sketch product by its first ST threads), in two stages so that a caller can put other loads in flight behind the
 // preparation's own: load() issues every load, compute() waits for them and
 // fills the LDS (ending with a barrier).  Every load is unconditional, through
 // a buffer resource (one of size zero reads zeros where an input is absent),
@@ -480,15 +480,16 @@ struct alignas(16) PrepLds {
 // count of outstanding loads stays exact, so compute() waits for the operand
 // it needs next and the loads issued after it (the sketch, the caller's
 // record prefetch) stay in flight.  Row r is query row
-// row_of(min(r, R - 1)); wave w prepares rows w, w + 4, ...  Thread (part,
-// l) of the sketch sums row l of S over one of 256/m coordinate ranges, so
-// each entry of S is read once and a wave's loads are contiguous.  The
-// work runs on the first four waves; a wider workgroup's other waves only
-// pass the barriers (their sketch loads fall past S and read nothing).
-template <int D, int M, int R>
+// row_of(min(r, R - 1)); waves 0-3 prepare rows w, w + 4, ...  Thread
+// (part, l) of the first ST sums row l of S over one of ST/m coordinate
+// ranges, so each entry of S is read once and a wave's loads are
+// contiguous; a wider workgroup's other waves only pass the barriers (their
+// sketch loads fall past S and read nothing).
+template <int D, int M, int R, int ST = 256>
 struct Prep {
+    static_assert(ST >= 256 && ST % 256 == 0, "the sketch takes whole groups of four waves");
     static constexpr int VPL = D / 64;
-    static constexpr int NT = M > 0 ? 256 / M : 1;  // parts per sketch row
+    static constexpr int NT = M > 0 ? ST / M : 1;  // parts per sketch row
     static constexpr int NI = D / NT;               // S^T entries per thread
     static constexpr int RW = (R + 3) / 4;          // rows per wave
     // raw words as loaded; compute() converts them
@@ -530,12 +531,12 @@ struct Prep {
         }
     }
 
-    __device__ void compute(const PrepIn& in, PrepLds<D, M, R>& L) {
+    __device__ void compute(const PrepIn& in, PrepLds<D, M, R, ST>& L) {
         const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
 #pragma unroll
         for (int j = 0; j < RW; ++j) {
             const int r = wave + 4 * j;
-            if (r >= R) break;  // the same for the whole wave
+            if (r >= R || wave >= 4) break;  // the same for the whole wave
             float xv[VPL];
 #pragma unroll
             for (int v = 0; v < VPL; ++v) {
@@ -598,7 +599,7 @@ struct Prep {
             const bool sketch = !in.s_ident;
             __syncthreads();
             // partial sums of s = S q' (or s = q')
-            if (sketch && t < 256) {
+            if (sketch && t < ST) {
                 const int prt = t / M;
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
@@ -623,11 +624,11 @@ struct Prep {
             __syncthreads();
             // scale, exact sum and digits of s; digit byte (qk*ncs + cs)*16 + j
             // holds sketch row qk*(m/4) + 16*cs + j (zero where that slot is past m/4)
-            constexpr int NCS = PrepLds<D, M, R>::NCS, SDW = PrepLds<D, M, R>::SDW;
+            constexpr int NCS = PrepLds<D, M, R, ST>::NCS, SDW = PrepLds<D, M, R, ST>::SDW;
 #pragma unroll
             for (int j = 0; j < RW; ++j) {
                 const int r = wave + 4 * j;
-                if (r >= R) break;
+                if (r >= R || wave >= 4) break;
                 float smax = 0.0f;
                 double sf = 0.0;
                 for (int li = lane; li < M; li += 64) smax = fmaxf(smax, fabsf(L.s[r][li]));

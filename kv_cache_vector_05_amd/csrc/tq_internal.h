@@ -164,10 +164,11 @@ size_t qdigits_workspace_bytes(const tq_codebook* ck, int64_t rows);
 QDigits carve_qdigits(const tq_codebook* ck, void* ws, int64_t rows);
 hipError_t launch_qdigits(const tq_codebook* ck, const AttnArgs& a, const QDigits& q, hipStream_t stream);
 // the integer-MFMA logit scan (tq_scan.hip): query rows in tiles of four;
-// with one tile per KV head (q == nullptr) each workgroup prepares its own
-// queries, with more it reads those launch_qdigits prepared
+// where scan_prepares_queries (q == nullptr) each workgroup prepares its own
+// queries, elsewhere it reads those launch_qdigits prepared
 bool scan_supported(const tq_codebook* ck);
 int scan_row_tiles(int G);
+bool scan_prepares_queries(const tq_codebook* ck, int G);  // the scan prepares the queries itself (no query workspace)
 hipError_t launch_scan(const tq_codebook* ck, const tq_packed& k, const AttnArgs& a, const QDigits* q, int k0,
                        int klen, float* out, int64_t ld, int col0, hipStream_t stream);
 // Fused decode on the integer matrix cores (tq_decode.hip): partials of

@@ -84,29 +84,31 @@ struct ScanArgs {
 // preparation is repeated once per workgroup); more row tiles read prepared
 // queries and keep four waves
 constexpr int kFusedWaves = 16;
-template <int NRT>
+// one row tile always; two without a sketch (with one, the eight rows'
+// sketch product and the second tile's operands cost more than the separate
+// preparation they save)
+constexpr bool scan_fused(int nrt, int m) { return nrt == 1 || (nrt == 2 && m == 0); }
+template <int NRT, int M>
 constexpr int scan_waves() {
-    return NRT == 1 ? kFusedWaves : 4;
+    return scan_fused(NRT, M) ? kFusedWaves : 4;
 }
 // tiles of records each wave keeps in flight behind the one it computes: the
 // wide workgroup runs at four waves per SIMD whatever its register count, so
-// it takes twice the depth (the bytes in flight set the streaming rate)
-template <int NRT>
-constexpr int scan_depth() {
-    return NRT == 1 ? 8 : 4;
-}
+// one row tile takes twice the depth (the bytes in flight set the streaming
+// rate); two row tiles, and paged 4-bit records, need the registers
+constexpr int scan_depth(int nrt, int bits, bool paged) { return nrt == 1 && !(paged && bits == 4) ? 8 : 4; }
 
 template <int D, int BITS, int NRT, int M, bool PAGED>
-__global__ __launch_bounds__(64 * scan_waves<NRT>()) void scan_kernel(ScanArgs p) {
+__global__ __launch_bounds__((64 * scan_waves<NRT, M>())) void scan_kernel(ScanArgs p) {
     using Q = dev::Quarter<D, BITS>;
     constexpr int R = 4 * NRT;       // query rows of the workgroup
     constexpr int NC = Q::LPG / 16;  // K = 64 chunks over the lane's coordinates
-    using PL = dev::PrepLds<D, M, R>;
+    constexpr bool FUSE = scan_fused(NRT, M);
+    constexpr int ST = FUSE ? 512 : 256;  // threads of the sketch product
+    using PL = dev::PrepLds<D, M, R, ST>;
     constexpr int NCS = PL::NCS;     // K = 64 chunks of the sketch product
-    // One row tile: the workgroup prepares its four queries itself.  More
-    // tiles read the queries prepared beforehand (their preparation would
-    // cost the kernel a wave per SIMD).
-    constexpr bool FUSE = NRT == 1;
+    // The workgroup prepares its queries itself (one row tile, or two
+    // without a sketch); otherwise it reads the queries prepared beforehand.
     __shared__ u32x2 stab[256];      // bits of a byte -> eight 0/1 bytes
     __shared__ std::conditional_t<FUSE, PL, char> prep;  // the workgroup's prepared queries
 
@@ -126,7 +128,7 @@ __global__ __launch_bounds__(64 * scan_waves<NRT>()) void scan_kernel(ScanArgs p
     const int sl = dev::clamp_len(p.seq_len, b, p.L_cap);
     const int kend = min(sl, p.k0 + p.klen);
     // a workgroup without keys leaves at once (before any barrier)
-    constexpr int NWV = scan_waves<NRT>();
+    constexpr int NWV = scan_waves<NRT, M>();
     if (p.k0 + (int)blockIdx.y * NWV * p.tiles_per_wave * 16 >= kend) return;
     const int kbeg = p.k0 + ((int)blockIdx.y * NWV + wave) * p.tiles_per_wave * 16;
     const int ntile = __builtin_amdgcn_readfirstlane(max(0, min(p.tiles_per_wave, (kend - kbeg + 15) / 16)));
@@ -229,7 +231,7 @@ __global__ __launch_bounds__(64 * scan_waves<NRT>()) void scan_kernel(ScanArgs p
     // query and are never stored).  Its loads go first, then the first
     // records: loads complete in order, so the preparation waits for its own
     // loads only and computes while those records are in flight.
-    dev::Prep<D, M, FUSE ? R : 1> pr;
+    dev::Prep<D, M, FUSE ? R : 1, ST> pr;
     intx4 aq[NRT][NC];
     intx4 as[NRT][NCS > 0 ? NCS : 1];
     float sc[NRT][3];
@@ -261,7 +263,7 @@ __global__ __launch_bounds__(64 * scan_waves<NRT>()) void scan_kernel(ScanArgs p
     // the first half of the tiles in flight are requested before the
     // preparation, the rest after it (all of them in flight across it would
     // raise the register peak)
-    constexpr int PF = scan_depth<NRT>();
+    constexpr int PF = scan_depth(NRT, BITS, PAGED);
     Raw raw[PF];
 #pragma unroll
     for (int i = 0; i < PF / 2; ++i) {
@@ -278,11 +280,16 @@ __global__ __launch_bounds__(64 * scan_waves<NRT>()) void scan_kernel(ScanArgs p
         // lane's output query qk
         const int r = (lane & 15) >> 2, a = lane & 3;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) aq[0][c] = *reinterpret_cast<const intx4*>(&prep.qd[r][a][qk * Q::LPG + 16 * c]);
+        for (int rt = 0; rt < NRT; ++rt) {
 #pragma unroll
-        for (int cs = 0; cs < NCS; ++cs) as[0][cs] = *reinterpret_cast<const intx4*>(&prep.sd[r][a][(qk * NCS + cs) * 16]);
+            for (int c = 0; c < NC; ++c)
+                aq[rt][c] = *reinterpret_cast<const intx4*>(&prep.qd[4 * rt + r][a][qk * Q::LPG + 16 * c]);
 #pragma unroll
-        for (int k = 0; k < 3; ++k) sc[0][k] = prep.scl[qk][k];
+            for (int cs = 0; cs < NCS; ++cs)
+                as[rt][cs] = *reinterpret_cast<const intx4*>(&prep.sd[4 * rt + r][a][(qk * NCS + cs) * 16]);
+#pragma unroll
+            for (int k = 0; k < 3; ++k) sc[rt][k] = prep.scl[4 * rt + qk][k];
+        }
     } else {
         __syncthreads();
     }
@@ -450,12 +457,14 @@ bool scan_supported(const tq_codebook* ck) {
 }
 
 int scan_row_tiles(int G) { return G <= 4 ? 1 : (G <= 8 ? 2 : 4); }
+bool scan_prepares_queries(const tq_codebook* ck, int G) { return scan_fused(scan_row_tiles(G), ck->spec.m); }
 
 hipError_t launch_scan(const tq_codebook* ck, const tq_packed& k, const AttnArgs& a, const QDigits* q, int k0,
                        int klen, float* out, int64_t ld, int col0, hipStream_t stream) {
     const int G = a.Hq / a.h_kv;
     const int nrt = scan_row_tiles(G);
-    if ((nrt > 1) != (q != nullptr)) return hipErrorInvalidValue;
+    const bool fused = scan_fused(nrt, ck->spec.m);
+    if (fused != (q == nullptr)) return hipErrorInvalidValue;
     const int ngroups = (G + 4 * nrt - 1) / (4 * nrt);
     const bool paged = a.pages.table != nullptr;
     const int d = ck->spec.d, bits = ck->spec.bits, m = ck->spec.m;
@@ -511,11 +520,11 @@ hipError_t launch_scan(const tq_codebook* ck, const tq_packed& k, const AttnArgs
     const int64_t gx = (int64_t)a.B * a.h_kv * ngroups;
     const int64_t tiles_row = (klen + 15) / 16;
     if (gx == 0 || tiles_row == 0) return hipSuccess;
-    const int nwv = nrt == 1 ? scan_waves<1>() : scan_waves<2>();
+    const int nwv = fused ? kFusedWaves : 4;
     const int64_t resident = resident_blocks((const void*)fn, 64 * nwv);
     const int64_t gy_want = std::max<int64_t>(1, (resident + gx - 1) / gx);
     // a multiple of the prefetch depth per wave (the loop's step)
-    const int pf = nrt == 1 ? scan_depth<1>() : scan_depth<2>();
+    const int pf = scan_depth(nrt, bits, paged);
     p.tiles_per_wave = (int)(((tiles_row + nwv * gy_want - 1) / (nwv * gy_want) + pf - 1) / pf * pf);
     const int64_t gy = (tiles_row + nwv * (int64_t)p.tiles_per_wave - 1) / (nwv * (int64_t)p.tiles_per_wave);
     hipLaunchKernelGGL(fn, dim3((unsigned)gx, (unsigned)gy), dim3(64 * nwv), 0, stream, p);
