@@ -1175,16 +1175,23 @@ hipError_t launch_logits(const tq_codebook* ck, const tq_packed& k, const AttnAr
                 ds.k0 = k0;
                 ds.cnt = cnt;
                 ds.aug = aug;
-                if (ck->spec.block >= 2)
-                    hipLaunchKernelGGL(dense_vq_dequant_kernel, dim3((unsigned)std::min(cnt, 8192)), dim3(256), 0,
-                                       stream, ds);
-                else
-                    hipLaunchKernelGGL(dense_dequant_kernel, dim3((unsigned)std::min(cnt, 8192)), dim3(256), 0, stream,
-                                       ds);
-                e = hipGetLastError();
-                if (e != hipSuccess) return e;
-                e = launch_gemm_nt(qaug + row0 * (d + m), d + m, aug, d + m, scores, chunk, G, cnt, d + m, stream);
-                if (e != hipSuccess) return e;
+                if (ck->spec.block < 2 && d % 32 == 0 && m % 32 == 0 && (bits == 1 || bits == 2 || bits == 4)) {
+                    // the score GEMM forms the keys' estimates from their records while it loads them
+                    const RecB rb{k.codes, k.signs, k.rnorm, ck->dev.levels, rec0 + k0, d, m, bits};
+                    e = launch_gemm_records(qaug + row0 * (d + m), d + m, rb, scores, chunk, G, cnt, stream);
+                    if (e != hipSuccess) return e;
+                } else {
+                    if (ck->spec.block >= 2)
+                        hipLaunchKernelGGL(dense_vq_dequant_kernel, dim3((unsigned)std::min(cnt, 8192)), dim3(256), 0,
+                                           stream, ds);
+                    else
+                        hipLaunchKernelGGL(dense_dequant_kernel, dim3((unsigned)std::min(cnt, 8192)), dim3(256), 0,
+                                           stream, ds);
+                    e = hipGetLastError();
+                    if (e != hipSuccess) return e;
+                    e = launch_gemm_nt(qaug + row0 * (d + m), d + m, aug, d + m, scores, chunk, G, cnt, d + m, stream);
+                    if (e != hipSuccess) return e;
+                }
                 const int64_t tot = (int64_t)G * cnt;
                 const unsigned sg = (unsigned)std::min<int64_t>((tot + 255) / 256, 65536);
                 hipLaunchKernelGGL(finalize_scores_kernel, dim3(sg), dim3(256), 0, stream, scores, (int64_t)chunk, G,

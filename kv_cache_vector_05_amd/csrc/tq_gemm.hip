@@ -23,6 +23,7 @@
 // multiplies.
 #include <hip/hip_runtime.h>
 
+#include "tq_device.h"
 #include "tq_internal.h"
 
 namespace tq {
@@ -39,6 +40,7 @@ constexpr int kKt = 32;
 constexpr int kRow = kKt + 8;                  // bf16 per LDS row
 constexpr int kPiece = kTile * kRow;           // bf16 per piece plane
 constexpr int kLoads = kTile * kKt / 4 / 256;  // float4 slots per thread per operand and step
+constexpr float kQjlF = 1.2533141373155003f;   // sqrt(pi / 2)
 
 // buffer resource over the tile's rows [r0, r0 + 128) of X (fewer at the
 // last tile); loads past it return zeros
@@ -68,6 +70,45 @@ __device__ __forceinline__ void load_step(__amdgpu_buffer_rsrc_t X, int64_t ldx,
             v[i].z = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(X, k + 2 < K ? o + 8 : kOut, 0, 0));
             v[i].w = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(X, k + 3 < K ? o + 12 : kOut, 0, 0));
         }
+    }
+}
+
+// B rows from packed scalar records (the index scan): row n of B is key
+// n0 + n's estimate in the rotated domain, t[c_i] for i < d and then
+// sqrt(pi/2)/m gamma z_l (+-) for l < m; the same values a dequantisation
+// pass would write (QJL estimator, iaemfoco post, "TurboQuant: Uma Nova
+// Abordagem"), formed while the step is loaded.  d and m are multiples of
+// 32, so a step lies in one part; BITS is 1, 2 or 4 (four codes in one
+// word).  The resources span the tile's records: keys past the last read
+// zeros, which only feed columns that are never stored.
+struct RecTile {
+    __amdgpu_buffer_rsrc_t codes, signs, rnorm;
+    int cw, mw, d, m, K;
+    float cq;
+};
+template <int BITS>
+__device__ __forceinline__ void load_step_rec(const RecTile& R, const float* lv, int k0, int tid,
+                                              float4 (&v)[kLoads]) {
+    constexpr uint32_t mask = (1u << BITS) - 1u;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+        const int idx = tid + 256 * i;
+        const int kl = idx >> 3;
+        const int k = k0 + 4 * (idx & 7);
+        float x[4] = {0.f, 0.f, 0.f, 0.f};
+        if (k0 < R.d) {  // the same for the whole workgroup
+            const int bp = BITS * k;
+            const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(R.codes, (uint32_t)(kl * R.cw + (bp >> 5)) * 4u, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[j] = lv[(w >> ((bp & 31) + BITS * j)) & mask];
+        } else if (k0 < R.K) {
+            const int l = k - R.d;
+            const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(R.signs, (uint32_t)(kl * R.mw + (l >> 5)) * 4u, 0, 0);
+            const float g = R.cq * __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(R.rnorm, (uint32_t)kl * 4u, 0, 0));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[j] = ((w >> ((l + j) & 31)) & 1u) ? g : -g;
+        }
+        v[i] = make_float4(x[0], x[1], x[2], x[3]);
     }
 }
 
@@ -108,13 +149,16 @@ __device__ __forceinline__ bf16x8 operand(const __bf16* S, int p, int row, int k
 // that operand's 128 rows are read from HBM once and served from that XCD's
 // L2 to the others (for the index scan, the dequantised keys against the
 // few query tiles).
-template <bool VEC>
+// BITS = 0: B is an fp32 matrix; 1, 2, 4: B is formed from packed records
+template <bool VEC, int BITS>
 __global__ __launch_bounds__(256) void gemm_nt_bf16x3(const float* __restrict__ A, int64_t lda,
                                                       const float* __restrict__ B, int64_t ldb,
                                                       float* __restrict__ C, int64_t ldc, int M, int N, int K,
-                                                      int m_fast) {
+                                                      int m_fast, RecB rec) {
     __shared__ __attribute__((aligned(16))) __bf16 As[3 * kPiece];
     __shared__ __attribute__((aligned(16))) __bf16 Bs[3 * kPiece];
+    constexpr bool REC = BITS > 0;
+    __shared__ float lvs[REC ? 16 : 1];  // record B: the level table
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -125,6 +169,24 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16x3(const float* __restrict__ 
     if (sl >= ns) return;  // the last group's padding
     const int64_t m0 = (int64_t)(m_fast ? f : sl) * kTile;
     const int64_t n0 = (int64_t)(m_fast ? sl : f) * kTile;
+    RecTile rt{};
+    if constexpr (REC) {
+        if (tid < (1 << BITS)) lvs[tid] = rec.levels[tid];
+        rt.cw = BITS * rec.d / 32;
+        rt.mw = rec.m / 32;
+        rt.d = rec.d;
+        rt.m = rec.m;
+        rt.K = rec.d + rec.m;
+        rt.cq = rec.m ? kQjlF / (float)rec.m : 0.f;
+        const int64_t nk = N - n0 < kTile ? N - n0 : kTile, r0 = rec.rec0 + n0;
+        rt.codes = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(rec.codes + r0 * rt.cw), (short)0,
+                                                      (int)(nk * rt.cw * 4), 0x00020000);
+        rt.signs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(rec.m ? rec.signs + r0 * rt.mw : nullptr),
+                                                      (short)0, (int)(rec.m ? nk * rt.mw * 4 : 0), 0x00020000);
+        rt.rnorm = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(rec.m ? rec.rnorm + r0 : nullptr), (short)0,
+                                                      (int)(rec.m ? nk * 4 : 0), 0x00020000);
+        __syncthreads();
+    }
     const int wm = (wave >> 1) * 64;  // wave's row offset inside the tile
     const int wn = (wave & 1) * 64;
 
@@ -143,7 +205,8 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16x3(const float* __restrict__ 
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
         load_step<VEC>(ra, lda, s * kKt, K, tid, va[s]);
-        load_step<VEC>(rb, ldb, s * kKt, K, tid, vb[s]);
+        if constexpr (REC) load_step_rec<BITS>(rt, lvs, s * kKt, tid, vb[s]);
+        else load_step<VEC>(rb, ldb, s * kKt, K, tid, vb[s]);
     }
     // K-steps in pairs, one per register buffer: the buffered operands split
     // into LDS, the step two ahead requested into the same registers, then
@@ -156,7 +219,8 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16x3(const float* __restrict__ 
             store_step(Bs, tid, vb[h]);
             __syncthreads();
             load_step<VEC>(ra, lda, k0 + (h + 2) * kKt, K, tid, va[h]);
-            load_step<VEC>(rb, ldb, k0 + (h + 2) * kKt, K, tid, vb[h]);
+            if constexpr (REC) load_step_rec<BITS>(rt, lvs, k0 + (h + 2) * kKt, tid, vb[h]);
+            else load_step<VEC>(rb, ldb, k0 + (h + 2) * kKt, K, tid, vb[h]);
 #pragma unroll
             for (int kk = 0; kk < kKt / 16; ++kk) {
                 bf16x8 a[2][3], b[2][3];
@@ -201,8 +265,16 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16x3(const float* __restrict__ 
 
 }  // namespace
 
-hipError_t launch_gemm_nt(const float* A, int64_t lda, const float* B, int64_t ldb, float* C,
-                          int64_t ldc, int M, int N, int K, hipStream_t stream) {
+namespace {
+template <int BITS>
+void launch_kernel(bool vec, dim3 grid, hipStream_t stream, const float* A, int64_t lda, const float* B, int64_t ldb,
+                   float* C, int64_t ldc, int M, int N, int K, int m_fast, const RecB& r) {
+    if (vec) hipLaunchKernelGGL((gemm_nt_bf16x3<true, BITS>), grid, dim3(256), 0, stream, A, lda, B, ldb, C, ldc, M, N, K, m_fast, r);
+    else hipLaunchKernelGGL((gemm_nt_bf16x3<false, BITS>), grid, dim3(256), 0, stream, A, lda, B, ldb, C, ldc, M, N, K, m_fast, r);
+}
+
+hipError_t launch_gemm(const float* A, int64_t lda, const float* B, int64_t ldb, const RecB* rec, float* C,
+                       int64_t ldc, int M, int N, int K, hipStream_t stream) {
     if (M <= 0 || N <= 0) return hipSuccess;
     const int64_t tm = (M + kTile - 1) / kTile, tn = (N + kTile - 1) / kTile;
     const int m_fast = tm <= tn ? 1 : 0;
@@ -210,14 +282,31 @@ hipError_t launch_gemm_nt(const float* A, int64_t lda, const float* B, int64_t l
     const int64_t blocks = nf * ((ns + 7) / 8) * 8;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     // float4 loads need 16-byte aligned rows
-    const bool vec = ((lda | ldb) & 3) == 0 && ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & 15) == 0;
-    if (vec)
-        hipLaunchKernelGGL(gemm_nt_bf16x3<true>, dim3((unsigned)blocks), dim3(256), 0, stream, A, lda, B, ldb, C, ldc, M, N,
-                           K, m_fast);
-    else
-        hipLaunchKernelGGL(gemm_nt_bf16x3<false>, dim3((unsigned)blocks), dim3(256), 0, stream, A, lda, B, ldb, C, ldc, M,
-                           N, K, m_fast);
+    const bool vec = ((lda | (rec ? 0 : ldb)) & 3) == 0 &&
+                     ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(rec ? nullptr : B)) & 15) == 0;
+    const RecB r = rec ? *rec : RecB{};
+    const dim3 grid((unsigned)blocks);
+    switch (rec ? rec->bits : 0) {
+        case 0: launch_kernel<0>(vec, grid, stream, A, lda, B, ldb, C, ldc, M, N, K, m_fast, r); break;
+        case 1: launch_kernel<1>(vec, grid, stream, A, lda, B, ldb, C, ldc, M, N, K, m_fast, r); break;
+        case 2: launch_kernel<2>(vec, grid, stream, A, lda, B, ldb, C, ldc, M, N, K, m_fast, r); break;
+        case 4: launch_kernel<4>(vec, grid, stream, A, lda, B, ldb, C, ldc, M, N, K, m_fast, r); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_gemm_nt(const float* A, int64_t lda, const float* B, int64_t ldb, float* C,
+                          int64_t ldc, int M, int N, int K, hipStream_t stream) {
+    return launch_gemm(A, lda, B, ldb, nullptr, C, ldc, M, N, K, stream);
+}
+
+hipError_t launch_gemm_records(const float* A, int64_t lda, const RecB& rec, float* C, int64_t ldc, int M, int N,
+                               hipStream_t stream) {
+    if (rec.d % 32 != 0 || rec.m % 32 != 0 || !(rec.bits == 1 || rec.bits == 2 || rec.bits == 4))
+        return hipErrorInvalidValue;
+    return launch_gemm(A, lda, nullptr, 0, &rec, C, ldc, M, N, rec.d + rec.m, stream);
 }
 
 }  // namespace tq

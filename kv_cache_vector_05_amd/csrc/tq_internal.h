@@ -196,9 +196,22 @@ hipError_t launch_qprep_rht(const tq_codebook* ck, const AttnArgs& a, float* qp,
 hipError_t launch_topk(const AttnArgs& a, const float* scores, int64_t ld, int64_t row0, int col0, int cnt,
                        bool first, hipStream_t stream);
 
-// C[M][N] = A[M][K] * B[N][K]^T (+ per-column scale if col_scale != nullptr),
-// fp32, row-major with leading dimensions lda/ldb/ldc (elements).
+// C[M][N] = A[M][K] * B[N][K]^T, fp32, row-major with leading dimensions
+// lda/ldb/ldc (elements).
 hipError_t launch_gemm_nt(const float* A, int64_t lda, const float* B, int64_t ldb, float* C,
                           int64_t ldc, int M, int N, int K, hipStream_t stream);
+// The same with B formed from packed scalar records: row n is key rec0 + n's
+// rotated-domain estimate [t[c_0..c_{d-1}], sqrt(pi/2)/m gamma (+-1)_0..m-1]
+// (d and m multiples of 32, K = d + m).
+struct RecB {
+    const uint32_t* codes;
+    const uint32_t* signs;
+    const float* rnorm;
+    const float* levels;
+    int64_t rec0;
+    int32_t d, m, bits;
+};
+hipError_t launch_gemm_records(const float* A, int64_t lda, const RecB& rec, float* C, int64_t ldc, int M, int N,
+                               hipStream_t stream);
 
 }  // namespace tq

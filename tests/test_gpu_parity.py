@@ -170,6 +170,24 @@ def test_vector_search_shaped_small():
     check_topk(vals, idx, ref, rval)
 
 
+@pytest.mark.parametrize("bits,m", [(1, 64), (3, 64), (4, 32), (2, 0)])
+def test_dense_logits_bit_widths(bits, m):
+    """Dense Haar rotation at d = 128: logits from records the oracle wrote,
+    for the widths the score GEMM decodes from the records itself (1, 2, 4
+    bits) and for 3 bits (dequantised first); a ragged key count."""
+    n, nq, d = 700, 8, 128
+    X = synth.vsearch_rows(2, 0, n, d=d)
+    Q = synth.vsearch_rows(3, 0, nq, d=d)
+    ock, gck = codebooks(d, bits, m, True, 11 + bits)
+    st = stored(codec.encode(ock, X))
+    kpo = upload(gck, st)
+    qt = torch.from_numpy(Q).cuda()[None]
+    sl = torch.tensor([n], dtype=torch.int32, device="cuda")
+    lg = tq.attn_logits(gck, qt, kpo, 1, n, sl).cpu().numpy()[0]
+    qp, s_ = estimator.prep_query(ock, Q)
+    parity.assert_close(lg, estimator.logits(ock, qp, s_, st), f"dense logits b{bits} m{m}")
+
+
 def check_topk(vals, idx, ref_scores, ref_vals, k=10):
     """Top-k sets agree up to near-ties (tests/parity.py::check_topk)."""
     parity.check_topk(vals, idx, ref_scores, k)
