@@ -57,7 +57,8 @@ HBM_PEAK_GBS = 8000.0
 FP32_PEAK_TFLOPS = 157.3
 BF16_PEAK_TFLOPS = 2500.0
 # the dense-rotation GEMMs run fp32 operands as three bf16 pieces each and
-# issue six bf16 matrix products per fp32 multiply-add
+# issue six bf16 matrix products per fp32 multiply-add; the index scan's
+# sketch part multiplies by exact +-1 (three products)
 BF16_PRODUCTS_PER_FP32_MAC = 6
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 REPEAT_MS = 3.0  # device time per timed repeat of a call
@@ -820,11 +821,14 @@ def vsearch_report(st, ct, ms_step):
                          "alg_tflop": 2.0 * n * d * (d + m) / 1e12},
             "scan_topk": {"alg_bytes": n * rec, "units": n * nq, "unit": "scores",
                           "alg_tflop": 2.0 * n * nq * (d + m) / 1e12}}
+    products = {"encode_k": BF16_PRODUCTS_PER_FP32_MAC,
+                "scan_topk": (BF16_PRODUCTS_PER_FP32_MAC * d + 3 * m) / (d + m)}
     for name, k in kern.items():
         k.update(ct[name])
         _rate(k)
         k["TFLOPs"] = k["alg_tflop"] / (k["us"] * 1e-6)  # fp32 multiply-adds as the method counts them
-        k["bf16_TFLOPs"] = BF16_PRODUCTS_PER_FP32_MAC * k["TFLOPs"]  # what the matrix cores execute
+        k["bf16_products_per_fp32_mac"] = products[name]
+        k["bf16_TFLOPs"] = products[name] * k["TFLOPs"]  # what the matrix cores execute
     extra = {"scan_vectors_per_s": n / (kern["scan_topk"]["us"] * 1e-6),
              "scan_scores_per_s": n * nq / (kern["scan_topk"]["us"] * 1e-6),
              "index_vectors_per_s": n / (kern["encode_k"]["us"] * 1e-6),
@@ -839,7 +843,7 @@ def roofline_of(name, k, rates):
     if "bf16_TFLOPs" in k:
         r = {"bound": "mfma", "achieved": k["bf16_TFLOPs"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
              "frac": k["bf16_TFLOPs"] / BF16_PEAK_TFLOPS, "dtype": "bf16 (three-piece fp32)",
-             "bf16_products_per_fp32_mac": BF16_PRODUCTS_PER_FP32_MAC, "fp32_equivalent_TFLOPs": k["TFLOPs"],
+             "bf16_products_per_fp32_mac": k["bf16_products_per_fp32_mac"], "fp32_equivalent_TFLOPs": k["TFLOPs"],
              "frac_of_fp32_peak": k["TFLOPs"] / FP32_PEAK_TFLOPS}
     else:
         r = {"bound": "hbm", "achieved": k["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",

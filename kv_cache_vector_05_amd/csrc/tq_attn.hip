@@ -988,7 +988,10 @@ size_t logits_workspace_bytes(const tq_codebook* ck, int64_t B, int Hq, int h_kv
     }
     const int G = h_kv > 0 ? Hq / h_kv : 0;
     size_t bytes = align256(rows * d * 4) + align256(rows * (d + m) * 4);  // rope'd q, [q' | s]
-    bytes += align256(chunk * (d + m) * 4);                                // dequantised keys
+    if (ck->spec.block < 2 && gemm_records_supported(d, m, ck->spec.bits))
+        bytes += align256(gemm_records_split_bytes((int64_t)rows, d, m));  // [q' | s] in bf16 pieces
+    else
+        bytes += align256(chunk * (d + m) * 4);                            // dequantised keys
     bytes += align256((size_t)G * chunk * 4);                              // scores
     (void)top_k;
     return bytes;
@@ -1139,12 +1142,16 @@ hipError_t launch_logits(const tq_codebook* ck, const tq_packed& k, const AttnAr
         }
         return hipSuccess;
     }
-    // dense rotation: q' and s by GEMM, keys dequantised per chunk, scores by GEMM
+    // dense rotation: q' and s by GEMM, keys dequantised per chunk (or formed inside the score GEMM), scores by GEMM
     float* qr = reinterpret_cast<float*>(ws);
     float* qaug = reinterpret_cast<float*>(ws + align256(rows * d * 4));
     float* aug = reinterpret_cast<float*>(ws + align256(rows * d * 4) + align256(rows * (d + m) * 4));
+    // scalar codes of 1, 2 or 4 bits: [q' | s] split once into bf16 pieces
+    // (in the dequantisation buffer's place) for the record-forming score GEMM
+    const bool records = ck->spec.block < 2 && gemm_records_supported(d, m, bits);
+    const size_t aug_bytes = records ? gemm_records_split_bytes((int64_t)rows, d, m) : (size_t)chunk * (d + m) * 4;
     float* scores = reinterpret_cast<float*>(ws + align256(rows * d * 4) + align256(rows * (d + m) * 4) +
-                                             align256((size_t)chunk * (d + m) * 4));
+                                             align256(aug_bytes));
     QPrep q = make_qprep(ck, a, nullptr, nullptr);
     hipLaunchKernelGGL(qrope_kernel, dim3((unsigned)rows), dim3(256), 0, stream, q, qr);
     hipError_t e = hipGetLastError();
@@ -1153,6 +1160,10 @@ hipError_t launch_logits(const tq_codebook* ck, const tq_packed& k, const AttnAr
     if (e != hipSuccess) return e;
     if (m) {
         e = launch_gemm_nt(qaug, d + m, ck->dev.sketch, d, qaug + d, d + m, (int)rows, m, d, stream);
+        if (e != hipSuccess) return e;
+    }
+    if (records) {
+        e = launch_split_rows(qaug, d + m, (int)rows, d + m, aug, stream);
         if (e != hipSuccess) return e;
     }
     for (int b = 0; b < a.B; ++b)
@@ -1175,10 +1186,11 @@ hipError_t launch_logits(const tq_codebook* ck, const tq_packed& k, const AttnAr
                 ds.k0 = k0;
                 ds.cnt = cnt;
                 ds.aug = aug;
-                if (ck->spec.block < 2 && d % 32 == 0 && m % 32 == 0 && (bits == 1 || bits == 2 || bits == 4)) {
+                if (records) {
                     // the score GEMM forms the keys' estimates from their records while it loads them
                     const RecB rb{k.codes, k.signs, k.rnorm, ck->dev.levels, rec0 + k0, d, m, bits};
-                    e = launch_gemm_records(qaug + row0 * (d + m), d + m, rb, scores, chunk, G, cnt, stream);
+                    e = launch_gemm_records(reinterpret_cast<const uint16_t*>(aug) + row0 * (d + m),
+                                            (int64_t)rows * (d + m), G, rb, scores, chunk, cnt, stream);
                     if (e != hipSuccess) return e;
                 } else {
                     if (ck->spec.block >= 2)

@@ -200,9 +200,10 @@ hipError_t launch_topk(const AttnArgs& a, const float* scores, int64_t ld, int64
 // lda/ldb/ldc (elements).
 hipError_t launch_gemm_nt(const float* A, int64_t lda, const float* B, int64_t ldb, float* C,
                           int64_t ldc, int M, int N, int K, hipStream_t stream);
-// The same with B formed from packed scalar records: row n is key rec0 + n's
-// rotated-domain estimate [t[c_0..c_{d-1}], sqrt(pi/2)/m gamma (+-1)_0..m-1]
-// (d and m multiples of 32, K = d + m).
+// Index-scan scores against packed scalar records: row n of B is key
+// rec0 + n's rotated-domain estimate [t[c_0..c_{d-1}], sqrt(pi/2)/m gamma
+// (+-1)_0..m-1] (d and m multiples of 32, 1, 2 or 4 bits), A = [q' | s] split
+// beforehand by launch_split_rows into three bf16 piece planes [3][rows][d + m].
 struct RecB {
     const uint32_t* codes;
     const uint32_t* signs;
@@ -211,7 +212,11 @@ struct RecB {
     int64_t rec0;
     int32_t d, m, bits;
 };
-hipError_t launch_gemm_records(const float* A, int64_t lda, const RecB& rec, float* C, int64_t ldc, int M, int N,
-                               hipStream_t stream);
+bool gemm_records_supported(int d, int m, int bits);
+size_t gemm_records_split_bytes(int64_t M, int d, int m);
+hipError_t launch_split_rows(const float* A, int64_t lda, int M, int K, void* planes, hipStream_t stream);
+// planes: the M rows' first piece (`plane` elements between pieces)
+hipError_t launch_gemm_records(const void* planes, int64_t plane, int M, const RecB& rec, float* C, int64_t ldc,
+                               int N, hipStream_t stream);
 
 }  // namespace tq
