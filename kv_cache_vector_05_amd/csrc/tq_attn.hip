@@ -246,94 +246,73 @@ __device__ __forceinline__ bool better(float a, int ia, float b, int ib) {
     return a > b || (a == b && ia < ib);
 }
 
-// one workgroup per row: thread-local sorted lists, then k rounds of a
-// block-wide argmax; the running list of earlier chunks seeds thread 0
+// One workgroup per row.  Each wave keeps its best k in lanes 0..k-1 (sorted
+// by `better`) and the k-th as a threshold: a batch of 64 scores costs one
+// compare and a ballot, and only the few that beat the threshold are
+// inserted, one at a time (a shift of the lanes behind the insertion
+// point).  Wave 0 then takes in the other waves' lists, and the running list
+// of earlier chunks first.
 __global__ __launch_bounds__(256) void topk_merge_kernel(TopK p) {
-    __shared__ float rv[4];
-    __shared__ int ri[4];
-    __shared__ int rt[4];
-    __shared__ int winner;
+    __shared__ float lv[4][kTopKMax];
+    __shared__ int li[4][kTopKMax];
     const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
     const int64_t rel = blockIdx.x;
     const int64_t row = p.row0 + rel;
     const int b = (int)(row / p.Hq);
     const int sl = clamp_len(p.seq_len, b, p.L_cap);
-    float vals[kTopKMax];
-    int idx[kTopKMax];
-#pragma unroll
-    for (int s = 0; s < kTopKMax; ++s) {
-        vals[s] = -INFINITY;
-        idx[s] = 0x7fffffff;
-    }
-    auto insert = [&](float x, int id) {
-        if (!(x == x)) return;  // NaN is never kept
-#pragma unroll
-        for (int s = 0; s < kTopKMax; ++s) {
-            if (s < p.k && better(x, id, vals[s], idx[s])) {
-                const float tv = vals[s];
-                const int ti = idx[s];
-                vals[s] = x;
-                idx[s] = id;
-                x = tv;
-                id = ti;
+    const int k = p.k;
+    float kv = -INFINITY, thv = -INFINITY;
+    int ki = 0x7fffffff, thi = 0x7fffffff;
+    // every lane offers (x, id) when `valid`; NaN is never kept
+    auto offer = [&](float x, int id, bool valid) {
+        unsigned long long mask = __ballot(valid && x == x && better(x, id, thv, thi));
+        while (mask) {
+            const int l = __ffsll(mask) - 1;
+            mask &= mask - 1;
+            const float cv = __shfl(x, l);
+            const int ci = __shfl(id, l);
+            if (!better(cv, ci, thv, thi)) continue;  // the threshold rose meanwhile
+            const int pos = __popcll(__ballot(lane < k && better(kv, ki, cv, ci)));
+            const float uv = __shfl_up(kv, 1);
+            const int ui = __shfl_up(ki, 1);
+            if (lane < k && lane > pos) {
+                kv = uv;
+                ki = ui;
             }
+            if (lane == pos) {
+                kv = cv;
+                ki = ci;
+            }
+            thv = __shfl(kv, k - 1);
+            thi = __shfl(ki, k - 1);
         }
     };
-    if (t == 0 && !p.first) {
-        for (int s = 0; s < p.k; ++s) {
-            const int id = p.out_idx[row * p.k + s];
-            if (id >= 0) insert(p.out_val[row * p.k + s], id);
-        }
+    if (wave == 0 && !p.first) {
+        const int id = lane < k ? p.out_idx[row * k + lane] : -1;
+        offer(lane < k ? p.out_val[row * k + lane] : -INFINITY, id, lane < k && id >= 0);
     }
     const int hi = min(p.col0 + p.cnt, sl);
-    for (int key = p.col0 + t; key < hi; key += 256) insert(p.scores[rel * p.ld + (key - p.col0)], key);
-    int head = 0;
-    for (int r = 0; r < p.k; ++r) {
-        float bv = -INFINITY;
-        int bi = 0x7fffffff;
-        if (head < p.k) {
-#pragma unroll
-            for (int s = 0; s < kTopKMax; ++s)
-                if (s == head) {
-                    bv = vals[s];
-                    bi = idx[s];
-                }
-        }
-        int bt = t;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            const float ov = __shfl_xor(bv, o);
-            const int oi = __shfl_xor(bi, o);
-            const int ot = __shfl_xor(bt, o);
-            if (better(ov, oi, bv, bi)) {
-                bv = ov;
-                bi = oi;
-                bt = ot;
-            }
-        }
-        if ((t & 63) == 0) {
-            rv[t >> 6] = bv;
-            ri[t >> 6] = bi;
-            rt[t >> 6] = bt;
-        }
-        __syncthreads();
-        if (t == 0) {
-            float v = rv[0];
-            int i = ri[0], w = rt[0];
-            for (int q = 1; q < 4; ++q)
-                if (better(rv[q], ri[q], v, i)) {
-                    v = rv[q];
-                    i = ri[q];
-                    w = rt[q];
-                }
-            const bool ok = i != 0x7fffffff;
-            p.out_val[row * p.k + r] = ok ? v : -INFINITY;
-            p.out_idx[row * p.k + r] = ok ? i : -1;
-            winner = ok ? w : -1;
-        }
-        __syncthreads();
-        if (t == winner) ++head;
-        __syncthreads();
+    for (int key0 = p.col0 + 64 * wave; key0 < hi; key0 += 256) {  // the same for the whole wave
+        const int key = key0 + lane;
+        const bool ok = key < hi;
+        offer(ok ? p.scores[rel * p.ld + (key - p.col0)] : -INFINITY, key, ok);
+    }
+    if (lane < k) {
+        lv[wave][lane] = kv;
+        li[wave][lane] = ki;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    for (int w = 1; w < 4; ++w) {
+        const float x = lane < k ? lv[w][lane] : -INFINITY;
+        const int id = lane < k ? li[w][lane] : 0x7fffffff;
+        offer(x, id, lane < k && id != 0x7fffffff);
+    }
+    if (lane < k) {
+        const bool ok = ki != 0x7fffffff;
+        p.out_val[row * k + lane] = ok ? kv : -INFINITY;
+        p.out_idx[row * k + lane] = ok ? ki : -1;
     }
 }
 
