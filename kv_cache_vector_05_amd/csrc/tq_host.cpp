@@ -721,9 +721,12 @@ tq_status tq_codebook_tables(const tq_spec* spec, const tq_draws* draws, float* 
     std::vector<float> lv, th, rot, sk;
     st = build_tables(*spec, draws, dense, &lv, &th, &rot, &sk);
     if (st) return st;
-    if (levels) std::memcpy(levels, lv.data(), lv.size() * sizeof(float));
-    if (thresholds) std::memcpy(thresholds, th.data(), th.size() * sizeof(float));
-    if (rotation && spec->rotation != TQ_ROT_NONE) std::memcpy(rotation, rot.data(), rot.size() * sizeof(float));
+    // (an empty table, such as a vector codebook's thresholds, copies nothing:
+    // memcpy from the null data() of an empty vector is undefined)
+    if (levels && !lv.empty()) std::memcpy(levels, lv.data(), lv.size() * sizeof(float));
+    if (thresholds && !th.empty()) std::memcpy(thresholds, th.data(), th.size() * sizeof(float));
+    if (rotation && spec->rotation != TQ_ROT_NONE && !rot.empty())
+        std::memcpy(rotation, rot.data(), rot.size() * sizeof(float));
     if (sketch && !sk.empty()) std::memcpy(sketch, sk.data(), sk.size() * sizeof(float));
     return TQ_OK;
 }
@@ -812,9 +815,9 @@ static tq_status codebook_create(const tq_spec* spec, const tq_draws* draws, con
     const size_t n_grid = cb->vq_grid.size();
     const size_t total = n_lv + n_th + n_rot + 3 * n_sk + n_mu_dev + n_grid;
     std::vector<float> host(total, 0.0f);
-    std::memcpy(host.data(), cb->levels.data(), cb->levels.size() * 4);
-    std::memcpy(host.data() + n_lv, cb->thresholds.data(), cb->thresholds.size() * 4);
-    std::memcpy(host.data() + n_lv + n_th, cb->rotation.data(), n_rot * 4);
+    if (!cb->levels.empty()) std::memcpy(host.data(), cb->levels.data(), cb->levels.size() * 4);
+    if (!cb->thresholds.empty()) std::memcpy(host.data() + n_lv, cb->thresholds.data(), cb->thresholds.size() * 4);
+    if (n_rot) std::memcpy(host.data() + n_lv + n_th, cb->rotation.data(), n_rot * 4);
     if (n_sk) {
         std::memcpy(host.data() + n_lv + n_th + n_rot, cb->sketch.data(), n_sk * 4);
         std::memcpy(host.data() + n_lv + n_th + n_rot + n_sk, sk_mfma.data(), n_sk * 4);
@@ -1029,8 +1032,9 @@ tq_status tq_codebook_get_spec(const tq_codebook* cb, tq_spec* out) {
 tq_status tq_codebook_export(const tq_codebook* cb, float* levels, float* thresholds,
                              float* rotation, float* sketch) {
     if (!cb) return fail(TQ_EINVAL, "null codebook");
-    if (levels) std::memcpy(levels, cb->levels.data(), cb->levels.size() * 4);
-    if (thresholds) std::memcpy(thresholds, cb->thresholds.data(), cb->thresholds.size() * 4);
+    if (levels && !cb->levels.empty()) std::memcpy(levels, cb->levels.data(), cb->levels.size() * 4);
+    if (thresholds && !cb->thresholds.empty())
+        std::memcpy(thresholds, cb->thresholds.data(), cb->thresholds.size() * 4);
     if (rotation && !no_rotation(cb)) std::memcpy(rotation, cb->rotation.data(), cb->rotation.size() * 4);
     if (sketch && !cb->sketch.empty()) std::memcpy(sketch, cb->sketch.data(), cb->sketch.size() * 4);
     return TQ_OK;
