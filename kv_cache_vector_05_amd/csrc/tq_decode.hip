@@ -288,10 +288,11 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
                 // keys past the end: + -inf (an add, not a select, so that the
                 // compiler does not put the norm loads behind a branch either)
                 const float off = key0 + n < c1 ? 0.0f : -INFINITY;
-                double lg[NRT];
+                float lg[NRT];
                 tl.compute(kr[c].raw, kr[c].gm, PER, lane, lg);
+                const float snu = p.scale * kr[c].nu;
 #pragma unroll
-                for (int rt = 0; rt < NRT; ++rt) a[rt] = (float)((double)p.scale * (double)kr[c].nu * lg[rt]) + off;
+                for (int rt = 0; rt < NRT; ++rt) a[rt] = snu * lg[rt] + off;
             }
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt) {

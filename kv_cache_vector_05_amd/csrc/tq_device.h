@@ -260,10 +260,11 @@ __device__ __forceinline__ uint32_t digits4_packed(int X) {
 }
 
 // value of an MFMA result whose four rows are the base-128 digits of one operand
-__device__ __forceinline__ double digits4_value(const intx4& a) {
-    const double h = (double)(a[0] * 128 + a[1]);  // |a| <= 2^25 per row: exact in int32
-    const double l = (double)(a[2] * 128 + a[3]);
-    return h * 16384.0 + l;
+// value of four digit rows (base 128, most significant first) as a float:
+// the row pairs combine exactly in int32 (|a| <= 2^20 per row), and the pair
+// sum rounds once
+__device__ __forceinline__ float digits4_f32(const intx4& a) {
+    return fmaf((float)(a[0] * 128 + a[1]), 16384.0f, (float)(a[2] * 128 + a[3]));
 }
 
 // Exact logit of one 16-key tile on the int8 matrix cores.
@@ -282,8 +283,10 @@ struct TileLogit {
 
     intx4 aq[NRT][NC];
     intx4 as[NRT][NCS > 0 ? NCS : 1];
-    // logit / nu = V qscale + gamma (Z zk - zc), Z the sign-digit sum
-    double qscale[NRT], zk[NRT], zc[NRT];
+    // logit / nu = V 2^qe + gamma (Z 2^ze c2 - zc), Z the sign-digit sum (the
+    // powers of two are applied by ldexp, so no scale leaves the fp32 range)
+    int qe[NRT], ze[NRT];
+    float c2[NRT], zc[NRT];
     uint32_t tdig[16];
 
     // qd/sd/scale: the prepared query digits; cq: scale of the correction
@@ -310,16 +313,16 @@ struct TileLogit {
                 as[rt][cs] = ok ? v : intx4{0, 0, 0, 0};
             }
         }
-        const double tscale = ldexp(1.0, -lvl_shift);
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
             const int g = gq0 + 4 * rt + qk;
             const int64_t row = rowbase + (g < G ? g : 0);
-            qscale[rt] = ldexp(tscale, -(int)scale[row * 3 + 0]);
+            qe[rt] = -lvl_shift - (int)scale[row * 3 + 0];
             // cq <s, z> with z = 2 bit - 1: (2 Z 2^-shift(s) - sum s) cq
             const double c = NCS > 0 ? cq : 0.0;
-            zk[rt] = 2.0 * c * ldexp(1.0, -(int)scale[row * 3 + 1]);
-            zc[rt] = c * (double)scale[row * 3 + 2];
+            ze[rt] = -(int)scale[row * 3 + 1];
+            c2[rt] = (float)(2.0 * c);
+            zc[rt] = (float)(c * (double)scale[row * 3 + 2]);
         }
 #pragma unroll
         for (int i = 0; i < (BITS == 4 ? 16 : 8); ++i) tdig[i] = lvl_digits[i];
@@ -388,28 +391,30 @@ struct TileLogit {
     }
 
     // out[rt] = <q', t[c]> + cq gm <s, z>  (not yet times nu); gm is gamma
-    // for the QJL sketch, the KV head's mu for the sign correction
-    __device__ void finish(const Acc& A, float gm, double out[NRT]) const {
+    // for the QJL sketch, the KV head's mu for the sign correction.  The digit
+    // sums are exact; their combination runs in fp32, whose roundings stay
+    // near 2^-22 of max(|logit|, 2^-7 sum_i |q'_i t_i|) (the top digits carry
+    // the sum to within that fraction), far inside the logits' tolerance.
+    __device__ void finish(const Acc& A, float gm, float out[NRT]) const {
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
             // y[b][a]: digit a of q' (weight 2^(7(3-a))) times digit b of t
             // (weight 2^(8(2-b))); |y| <= 128 * 64 * 128 = 2^20
-            double V = 0.0;
+            float V = 0.0f;
 #pragma unroll
-            for (int bb = 0; bb < 3; ++bb) V = V * 256.0 + digits4_value(A.y[rt][bb]);
-            double logit = V * qscale[rt];
+            for (int bb = 0; bb < 3; ++bb) V = fmaf(V, 256.0f, digits4_f32(A.y[rt][bb]));
+            float logit = ldexpf(V, qe[rt]);
             if constexpr (NCS > 0) {
                 // sum_l s_l z_l = 2 sum_l s_l bit_l - sum_l s_l; the digit rows
                 // are paired in int32 (|z| <= 64 * 64 per row)
-                const intx4& z = A.z[rt];
-                const double Z = digits4_value(z);
-                logit = fma((double)gm, fma(Z, zk[rt], -zc[rt]), logit);
+                const float Z = ldexpf(digits4_f32(A.z[rt]), ze[rt]);
+                logit = fmaf(gm, fmaf(Z, c2[rt], -zc[rt]), logit);
             }
             out[rt] = logit;
         }
     }
 
-    __device__ void compute(const Raw& r, float gm, int per, int lane, double out[NRT]) const {
+    __device__ void compute(const Raw& r, float gm, int per, int lane, float out[NRT]) const {
         Acc A;
         mma(r, per, lane, A);
         finish(A, gm, out);

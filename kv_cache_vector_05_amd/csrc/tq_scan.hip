@@ -11,14 +11,14 @@
 // (tq_qprep.hip: q' and s as four balanced base-128 digits with one scale per
 // query); the levels' three base-256 digits come from the packed codes by one
 // v_perm per four coordinates; the sign bits become 0/1 bytes through a
-// 256-entry LDS table.  The digit sums are combined exactly in int32 pairs
-// and fp64, and only the logit is rounded to fp32.  Lane l owns key l % 16
-// and coordinate quarter l / 16, and holds the logit of (query l / 16, key
-// l % 16) of each four-query row tile.
+// 256-entry LDS table.  The digit sums are exact; the digit rows pair
+// exactly in int32 and the rest of the combination runs in fp32.  Lane l
+// owns key l % 16 and coordinate quarter l / 16, and holds the logit of
+// (query l / 16, key l % 16) of each four-query row tile.
 //
 // One workgroup serves one KV head of one sequence, up to 4 NRT of its query
 // heads and a contiguous run of keys, sized so that the whole grid is
-// resident at once: sixteen waves when it prepares its four queries itself
+// resident at once: eight waves when it prepares its four queries itself
 // (one row tile; the preparation runs once per workgroup, on four of the
 // waves), four waves reading prepared queries otherwise.  Records are read
 // with buffer loads whose per-tile advance is a scalar offset (no vector
@@ -44,6 +44,10 @@ typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRsrcWord3 = 0x00020000;  // buffer resource word 3 for gfx9: 32-bit elements, no swizzle
+// cache policy of the record loads and logit stores of one-row-tile scans:
+// nt (streaming; each record and logit is touched once).  Scans of several
+// row tiles keep the default policy, which measured faster for them.
+constexpr int kStream = 2;
 
 // buffer resource over [base, base + bytes); loads past the end return 0
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
@@ -80,10 +84,11 @@ struct ScanArgs {
 };
 
 // waves per workgroup: a single row tile prepares its queries in the kernel,
-// on four of the waves, so the workgroup is as wide as the CU takes (the
-// preparation is repeated once per workgroup); more row tiles read prepared
-// queries and keep four waves
-constexpr int kFusedWaves = 16;
+// on four of the waves, so the workgroup is wider than four waves (the
+// preparation is repeated once per workgroup); eight waves, two workgroups
+// per CU, measured faster than one sixteen-wave workgroup.  More row tiles
+// read prepared queries and keep four waves.
+constexpr int kFusedWaves = 8;
 // one row tile always; two without a sketch (with one, the eight rows'
 // sketch product and the second tile's operands cost more than the separate
 // preparation they save)
@@ -104,9 +109,10 @@ __global__ __launch_bounds__((64 * scan_waves<NRT, M>())) void scan_kernel(ScanA
     constexpr int R = 4 * NRT;       // query rows of the workgroup
     constexpr int NC = Q::LPG / 16;  // K = 64 chunks over the lane's coordinates
     constexpr bool FUSE = scan_fused(NRT, M);
-    constexpr int ST = FUSE ? 512 : 256;  // threads of the sketch product
+    constexpr int ST = FUSE && scan_waves<NRT, M>() >= 8 ? 512 : 256;  // threads of the sketch product
     using PL = dev::PrepLds<D, M, R, ST>;
     constexpr int NCS = PL::NCS;     // K = 64 chunks of the sketch product
+    constexpr int CP = FUSE && NRT == 1 ? kStream : 0;  // cache policy of the record stream
     // The workgroup prepares its queries itself (one row tile, or two
     // without a sketch); otherwise it reads the queries prepared beforehand.
     __shared__ u32x2 stab[256];      // bits of a byte -> eight 0/1 bytes
@@ -176,23 +182,23 @@ __global__ __launch_bounds__((64 * scan_waves<NRT, M>())) void scan_kernel(ScanA
             so_s = (uint32_t)tile * 16u * (uint32_t)mw * 4u;
         }
         if constexpr (Q::NW == 3) {
-            const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(rc, vo_c, so_c, 0);
+            const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(rc, vo_c, so_c, CP);
             r.W[0] = v.x;
             r.W[1] = v.y;
             r.W[2] = v.z;
         } else if constexpr (Q::NW == 4 && Q::ALIGNED) {
-            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rc, vo_c, so_c, 0);
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rc, vo_c, so_c, CP);
             r.W[0] = v.x;
             r.W[1] = v.y;
             r.W[2] = v.z;
             r.W[3] = v.w;
         } else if constexpr (Q::NW == 2 && Q::ALIGNED) {
-            const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rc, vo_c, so_c, 0);
+            const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rc, vo_c, so_c, CP);
             r.W[0] = v.x;
             r.W[1] = v.y;
         } else if constexpr (Q::ALIGNED) {
 #pragma unroll
-            for (int i = 0; i < Q::NW; ++i) r.W[i] = __builtin_amdgcn_raw_buffer_load_b32(rc, vo_c + 4u * i, so_c, 0);
+            for (int i = 0; i < Q::NW; ++i) r.W[i] = __builtin_amdgcn_raw_buffer_load_b32(rc, vo_c + 4u * i, so_c, CP);
         } else {
             // the quarter straddles words: NW words from word0, the last clamped
             // into the record, shifted into place
@@ -200,12 +206,12 @@ __global__ __launch_bounds__((64 * scan_waves<NRT, M>())) void scan_kernel(ScanA
 #pragma unroll
             for (int i = 0; i < Q::NW; ++i)
                 r.W[i] = __builtin_amdgcn_raw_buffer_load_b32(rc, (uint32_t)(n * CW + w0 + min(i, CW - 1 - w0)) * 4u,
-                                                              so_c, 0);
+                                                              so_c, CP);
             const int sh = (Q::BPG * qk) & 31;
 #pragma unroll
             for (int i = 0; i + 1 < Q::NW; ++i) r.W[i] = __builtin_amdgcn_alignbit(r.W[i + 1], r.W[i], sh);
         }
-        r.sg = NCS > 0 ? __builtin_amdgcn_raw_buffer_load_b32(rs_, vo_s, so_s, 0) : 0u;
+        r.sg = NCS > 0 ? __builtin_amdgcn_raw_buffer_load_b32(rs_, vo_s, so_s, CP) : 0u;
     };
     // nu and gamma of a tile (loaded after the tile's slot has been combined)
     auto fetch_scalars = [&](int tile, Raw& r) {
@@ -217,11 +223,11 @@ __global__ __launch_bounds__((64 * scan_waves<NRT, M>())) void scan_kernel(ScanA
         } else {
             so_n = (uint32_t)tile * 64u;
         }
-        r.nu = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rn, vo_n, so_n, 0));
+        r.nu = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rn, vo_n, so_n, CP));
         // gamma per key, or the head's mu (the load then reads zeros)
         if constexpr (NCS > 0) {
             // an add rather than a select keeps the load unconditional
-            r.gm = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, vo_n, so_n, 0)) + g_head;
+            r.gm = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, vo_n, so_n, CP)) + g_head;
         } else {
             r.gm = g_head;
         }
@@ -298,13 +304,17 @@ __global__ __launch_bounds__((64 * scan_waves<NRT, M>())) void scan_kernel(ScanA
         fetch_codes(clampt(i), raw[i]);
         fetch_scalars(clampt(i), raw[i]);
     }
-    double qscale[NRT], zk[NRT], zc[NRT];
+    // logit / nu = V 2^qe + gamma (Z 2^ze c2 - zc) (powers of two by ldexp,
+    // so no scale leaves the fp32 range)
+    int qe[NRT], ze[NRT];
+    float c2[NRT], zc[NRT];
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
-        qscale[rt] = ldexp(1.0, -p.lvl_shift - (int)sc[rt][0]);
+        qe[rt] = -p.lvl_shift - (int)sc[rt][0];
         const double c = NCS > 0 ? p.cq : 0.0;
-        zk[rt] = 2.0 * c * ldexp(1.0, -(int)sc[rt][1]);
-        zc[rt] = c * (double)sc[rt][2];
+        ze[rt] = -(int)sc[rt][1];
+        c2[rt] = (float)(2.0 * c);
+        zc[rt] = (float)(c * (double)sc[rt][2]);
     }
     uint32_t tdig[16];
 #pragma unroll
@@ -363,26 +373,19 @@ __global__ __launch_bounds__((64 * scan_waves<NRT, M>())) void scan_kernel(ScanA
         const bool key_ok = tile < nfull || kbeg + tile * 16 + n < kend;
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
-            double V = 0.0;
+            float V = 0.0f;
 #pragma unroll
-            for (int bb = 0; bb < 3; ++bb) {
-                const intx4& y = A.y[rt][bb];
-                const double h = (double)(y[0] * 128 + y[1]);
-                const double l = (double)(y[2] * 128 + y[3]);
-                V = fma(V, 256.0, fma(h, 16384.0, l));
-            }
-            double lg = V * qscale[rt];
+            for (int bb = 0; bb < 3; ++bb) V = fmaf(V, 256.0f, dev::digits4_f32(A.y[rt][bb]));
+            float lg = ldexpf(V, qe[rt]);
             if constexpr (NCS > 0) {
                 // sum_l s_l z_l = 2 sum_l s_l bit_l - sum_l s_l
-                const intx4& z = A.z[rt];
-                const double Z = fma((double)(z[0] * 128 + z[1]), 16384.0, (double)(z[2] * 128 + z[3]));
-                lg = fma((double)gm, fma(Z, zk[rt], -zc[rt]), lg);
+                lg = fmaf(gm, fmaf(ldexpf(dev::digits4_f32(A.z[rt]), ze[rt]), c2[rt], -zc[rt]), lg);
             }
-            const float v = (float)lg * nu;
+            const float v = lg * nu;
             if ((rows_full && tile < nfull) || (key_ok && g_lane + 4 * rt < G))
                 __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ro,
                                                       (uint32_t)(((int64_t)(qk + 4 * rt) * p.ld + n) * 4),
-                                                      (uint32_t)tile * 64u, 0);
+                                                      (uint32_t)tile * 64u, CP);
         }
     };
     // One tile per step: its MFMAs, then its slot refilled with the tile
@@ -433,6 +436,9 @@ ScanFn pick_bits(int bits, int nrt, int m) {
     }
     return nullptr;
 }
+
+// rounds of resident workgroups the launch is cut into
+constexpr int kScanRounds = 1;
 
 int64_t resident_blocks(const void* fn, int threads) {
     static thread_local const void* last_fn = nullptr;
@@ -522,7 +528,7 @@ hipError_t launch_scan(const tq_codebook* ck, const tq_packed& k, const AttnArgs
     if (gx == 0 || tiles_row == 0) return hipSuccess;
     const int nwv = fused ? kFusedWaves : 4;
     const int64_t resident = resident_blocks((const void*)fn, 64 * nwv);
-    const int64_t gy_want = std::max<int64_t>(1, (resident + gx - 1) / gx);
+    const int64_t gy_want = std::max<int64_t>(1, (kScanRounds * resident + gx - 1) / gx);
     // a multiple of the prefetch depth per wave (the loop's step)
     const int pf = scan_depth(nrt, bits, paged);
     p.tiles_per_wave = (int)(((tiles_row + nwv * gy_want - 1) / (nwv * gy_want) + pf - 1) / pf * pf);
