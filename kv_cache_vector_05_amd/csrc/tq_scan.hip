@@ -44,9 +44,9 @@ typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRsrcWord3 = 0x00020000;  // buffer resource word 3 for gfx9: 32-bit elements, no swizzle
-// cache policy of the record loads and logit stores of one-row-tile scans:
-// nt (streaming; each record and logit is touched once).  Scans of several
-// row tiles keep the default policy, which measured faster for them.
+// cache policy of the logit stores: nt (streaming; each logit is written
+// once).  The record loads keep the default policy: streaming loads measured
+// slower.
 constexpr int kStream = 2;
 
 // buffer resource over [base, base + bytes); loads past the end return 0
@@ -112,7 +112,6 @@ __global__ __launch_bounds__((64 * scan_waves<NRT, M>())) void scan_kernel(ScanA
     constexpr int ST = FUSE && scan_waves<NRT, M>() >= 8 ? 512 : 256;  // threads of the sketch product
     using PL = dev::PrepLds<D, M, R, ST>;
     constexpr int NCS = PL::NCS;     // K = 64 chunks of the sketch product
-    constexpr int CP = FUSE && NRT == 1 ? kStream : 0;  // cache policy of the record stream
     // The workgroup prepares its queries itself (one row tile, or two
     // without a sketch); otherwise it reads the queries prepared beforehand.
     __shared__ u32x2 stab[256];      // bits of a byte -> eight 0/1 bytes
@@ -182,23 +181,23 @@ __global__ __launch_bounds__((64 * scan_waves<NRT, M>())) void scan_kernel(ScanA
             so_s = (uint32_t)tile * 16u * (uint32_t)mw * 4u;
         }
         if constexpr (Q::NW == 3) {
-            const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(rc, vo_c, so_c, CP);
+            const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(rc, vo_c, so_c, 0);
             r.W[0] = v.x;
             r.W[1] = v.y;
             r.W[2] = v.z;
         } else if constexpr (Q::NW == 4 && Q::ALIGNED) {
-            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rc, vo_c, so_c, CP);
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rc, vo_c, so_c, 0);
             r.W[0] = v.x;
             r.W[1] = v.y;
             r.W[2] = v.z;
             r.W[3] = v.w;
         } else if constexpr (Q::NW == 2 && Q::ALIGNED) {
-            const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rc, vo_c, so_c, CP);
+            const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rc, vo_c, so_c, 0);
             r.W[0] = v.x;
             r.W[1] = v.y;
         } else if constexpr (Q::ALIGNED) {
 #pragma unroll
-            for (int i = 0; i < Q::NW; ++i) r.W[i] = __builtin_amdgcn_raw_buffer_load_b32(rc, vo_c + 4u * i, so_c, CP);
+            for (int i = 0; i < Q::NW; ++i) r.W[i] = __builtin_amdgcn_raw_buffer_load_b32(rc, vo_c + 4u * i, so_c, 0);
         } else {
             // the quarter straddles words: NW words from word0, the last clamped
             // into the record, shifted into place
@@ -206,12 +205,12 @@ __global__ __launch_bounds__((64 * scan_waves<NRT, M>())) void scan_kernel(ScanA
 #pragma unroll
             for (int i = 0; i < Q::NW; ++i)
                 r.W[i] = __builtin_amdgcn_raw_buffer_load_b32(rc, (uint32_t)(n * CW + w0 + min(i, CW - 1 - w0)) * 4u,
-                                                              so_c, CP);
+                                                              so_c, 0);
             const int sh = (Q::BPG * qk) & 31;
 #pragma unroll
             for (int i = 0; i + 1 < Q::NW; ++i) r.W[i] = __builtin_amdgcn_alignbit(r.W[i + 1], r.W[i], sh);
         }
-        r.sg = NCS > 0 ? __builtin_amdgcn_raw_buffer_load_b32(rs_, vo_s, so_s, CP) : 0u;
+        r.sg = NCS > 0 ? __builtin_amdgcn_raw_buffer_load_b32(rs_, vo_s, so_s, 0) : 0u;
     };
     // nu and gamma of a tile (loaded after the tile's slot has been combined)
     auto fetch_scalars = [&](int tile, Raw& r) {
@@ -223,11 +222,11 @@ __global__ __launch_bounds__((64 * scan_waves<NRT, M>())) void scan_kernel(ScanA
         } else {
             so_n = (uint32_t)tile * 64u;
         }
-        r.nu = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rn, vo_n, so_n, CP));
+        r.nu = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rn, vo_n, so_n, 0));
         // gamma per key, or the head's mu (the load then reads zeros)
         if constexpr (NCS > 0) {
             // an add rather than a select keeps the load unconditional
-            r.gm = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, vo_n, so_n, CP)) + g_head;
+            r.gm = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, vo_n, so_n, 0)) + g_head;
         } else {
             r.gm = g_head;
         }
@@ -385,7 +384,7 @@ __global__ __launch_bounds__((64 * scan_waves<NRT, M>())) void scan_kernel(ScanA
             if ((rows_full && tile < nfull) || (key_ok && g_lane + 4 * rt < G))
                 __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ro,
                                                       (uint32_t)(((int64_t)(qk + 4 * rt) * p.ld + n) * 4),
-                                                      (uint32_t)tile * 64u, CP);
+                                                      (uint32_t)tile * 64u, kStream);
         }
     };
     // One tile per step: its MFMAs, then its slot refilled with the tile
