@@ -127,7 +127,12 @@ __device__ __forceinline__ float sum64(float v) {
 }
 
 template <int D, int BITS, int NRT, int M, bool PAGED>
-__global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
+// One row tile runs five waves per SIMD: with one operand block per wave's
+// buffer (28 KB of LDS) and at most 96 VGPRs, five four-wave workgroups share
+// a CU (measured 3 % faster than four).  Two row tiles hold 132 VGPRs and
+// keep three.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NRT == 1 ? 5 : 3))) void decode_mfma_kernel(
+    DecM p) {
     constexpr int NCS = M == 0 ? 0 : (M >= 64 ? M / 64 : 1);  // K=64 sketch chunks of the logit
     using TL = dev::TileLogit<D, BITS, NRT, NCS>;
     using Q = typename TL::Q;
@@ -140,6 +145,10 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
     constexpr int MW = M / 32;            // sign words per record
     constexpr int NWO = M > 0 ? 2 : 1;    // weight operands: w (and w * gamma)
     static_assert(ZBW <= CBW, "the operand buffer holds CBW blocks");
+    // operand blocks per wave's B buffer: one row tile passes its blocks
+    // through one block in turn (less LDS, a fifth workgroup per CU); two
+    // row tiles write all CBW blocks before reading them back
+    constexpr int NBB = NRT == 1 ? 1 : CBW;
     // record loads run this many 64-key chunks ahead of their use
     constexpr int KDEPTH = 4, VDEPTH = 4;
 
@@ -149,7 +158,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
     __shared__ __attribute__((aligned(16))) int8_t wdig[NWO * NRT * NCH * 1024];
     // per wave: one B-operand buffer [block][key][16] that the level digits
     // and the sign bytes pass through in turn
-    __shared__ __attribute__((aligned(16))) int8_t bpool[4 * CBW * 1024];
+    __shared__ __attribute__((aligned(16))) int8_t bpool[4 * NBB * 1024];
     __shared__ float red[32 * NRT + 8];
 
     const int t = threadIdx.x;
@@ -414,7 +423,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
     // passing its B operands through a region of LDS of its own (written and
     // read back transposed by the same wave, whose LDS accesses are served in
     // order): no workgroup barrier.
-    int8_t* bbuf = bpool + wave * CBW * 1024;
+    int8_t* bbuf = bpool + wave * NBB * 1024;
     intx4 accy[NRT][CBW][3];
     intx4 accz[NRT][ZBW > 0 ? ZBW : 1];
 #pragma unroll
@@ -455,14 +464,24 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
                 intx4 v;
 #pragma unroll
                 for (int sg = 0; sg < 4; ++sg) v[sg] = (int)dev::lut<BITS>(tdv, bb, sel[j][sg]);
-                *reinterpret_cast<intx4*>(bbuf + j * 1024 + 16 * lane) = v;
+                *reinterpret_cast<intx4*>(bbuf + (j % NBB) * 1024 + 16 * lane) = v;
+                if constexpr (NBB == 1) {
+                    // the wave's LDS accesses are served in order: the block is
+                    // read back before the next one overwrites it
+                    const intx4 bv = tr_operand(bbuf, lane);
+#pragma unroll
+                    for (int rt = 0; rt < NRT; ++rt)
+                        accy[rt][j][bb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aw[rt], bv, accy[rt][j][bb], 0, 0, 0);
+                }
             }
+            if constexpr (NBB > 1) {
 #pragma unroll
-            for (int j = 0; j < CBW; ++j) {
-                const intx4 bv = tr_operand(bbuf + j * 1024, lane);
+                for (int j = 0; j < CBW; ++j) {
+                    const intx4 bv = tr_operand(bbuf + j * 1024, lane);
 #pragma unroll
-                for (int rt = 0; rt < NRT; ++rt)
-                    accy[rt][j][bb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aw[rt], bv, accy[rt][j][bb], 0, 0, 0);
+                    for (int rt = 0; rt < NRT; ++rt)
+                        accy[rt][j][bb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aw[rt], bv, accy[rt][j][bb], 0, 0, 0);
+                }
             }
         }
         // sign bits of sketch rows wave*PER + 16 zb .. as +-1 bytes (rows past
@@ -474,14 +493,22 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecM p) {
                 intx4 v;
 #pragma unroll
                 for (int s4 = 0; s4 < 4; ++s4) v[s4] = 4 * s4 < PER - 16 * zb ? (int)dev::spread4_pm(x >> (4 * s4)) : 0;
-                *reinterpret_cast<intx4*>(bbuf + zb * 1024 + 16 * lane) = v;
+                *reinterpret_cast<intx4*>(bbuf + (zb % NBB) * 1024 + 16 * lane) = v;
+                if constexpr (NBB == 1) {
+                    const intx4 bz = tr_operand(bbuf, lane);
+#pragma unroll
+                    for (int rt = 0; rt < NRT; ++rt)
+                        accz[rt][zb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(az[rt], bz, accz[rt][zb], 0, 0, 0);
+                }
             }
+            if constexpr (NBB > 1) {
 #pragma unroll
-            for (int zb = 0; zb < ZBW; ++zb) {
-                const intx4 bz = tr_operand(bbuf + zb * 1024, lane);
+                for (int zb = 0; zb < ZBW; ++zb) {
+                    const intx4 bz = tr_operand(bbuf + zb * 1024, lane);
 #pragma unroll
-                for (int rt = 0; rt < NRT; ++rt)
-                    accz[rt][zb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(az[rt], bz, accz[rt][zb], 0, 0, 0);
+                    for (int rt = 0; rt < NRT; ++rt)
+                        accz[rt][zb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(az[rt], bz, accz[rt][zb], 0, 0, 0);
+                }
             }
         }
     }
