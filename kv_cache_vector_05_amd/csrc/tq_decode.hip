@@ -129,9 +129,10 @@ __device__ __forceinline__ float sum64(float v) {
 template <int D, int BITS, int NRT, int M, bool PAGED>
 // One row tile runs five waves per SIMD: with one operand block per wave's
 // buffer (28 KB of LDS) and at most 96 VGPRs, five four-wave workgroups share
-// a CU (measured 3 % faster than four).  Two row tiles hold 132 VGPRs and
-// keep three.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NRT == 1 ? 5 : 3))) void decode_mfma_kernel(
+// a CU (measured 3 % faster than four).  Two row tiles (33 KB of LDS) run
+// four, held to 128 VGPRs (measured 2 % faster than the three their 138
+// VGPRs would give).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NRT == 1 ? 5 : 4))) void decode_mfma_kernel(
     DecM p) {
     constexpr int NCS = M == 0 ? 0 : (M >= 64 ? M / 64 : 1);  // K=64 sketch chunks of the logit
     using TL = dev::TileLogit<D, BITS, NRT, NCS>;
